@@ -1,0 +1,152 @@
+"""Seeded synthetic inputs for the Muir operator.
+
+This module is shared by the HIP library's tests/benchmark and by the oracle
+checks, so it holds no arithmetic of the operator itself: it only draws
+random tensors with the shapes and value distributions of the workloads
+(arXiv 2611.08376: head size d_k = d_v = 128, 16 heads at d = 2,048, 4K
+training length, 32K throughput context, streaming decode) and casts them
+once to the working dtype.  The caller passes the drawn values to both
+sides; neither side draws anything itself.
+
+Recipe (numpy PCG64, one generator per call, fixed draw order):
+  q, k   : x ~ N(0,1)^{d_k}; s = silu(x); q = s / ||s||_2 per (b, t, h)
+           (the pages' q/k pathway ends in SiLU then unit normalisation)
+  v      : N(0, 1)
+  log_a  : "uniform"      -> U[-3, -1e-3] i.i.d. per element
+           "channel"      -> per (h, j) rate r = exp(U[ln 1e-4, ln 3]),
+                             log_a = -r for every b, t
+           "channel_slow" -> as "channel", plus round(0.1 d_k) channels per
+                             head (seeded choice) with r ~ U[1e-6, 1e-4]
+           "zero"         -> 0 (no decay)
+  erase, write : sigmoid(N(0,1));  gamma : 2 sigmoid(N(0,1))
+  dO     : N(0, 1) (only when asked for)
+  S0     : S0_scale * N(0, 1) in fp32 (zeros when S0_scale == 0)
+Draw order: q, k, v, log_a, erase, write, gamma, dO, S0.  Values are drawn in
+float32, transformed in float32, then rounded once (round-to-nearest-even)
+to the requested dtype.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+_DT = {"bf16": torch.bfloat16, "f32": torch.float32, "fp32": torch.float32}
+
+
+def _silu_unit(x: np.ndarray) -> np.ndarray:
+    s = x / (1.0 + np.exp(-x))
+    n = np.sqrt(np.sum(s * s, axis=-1, keepdims=True))
+    return s / np.maximum(n, np.float32(1e-12))
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def _decay_rates(rng: np.random.Generator, H: int, dk: int, mode: str) -> np.ndarray:
+    """Per-(head, channel) positive rates for the 'channel' modes, shape [H, dk]."""
+    lo, hi = math.log(1e-4), math.log(3.0)
+    r = np.exp(rng.uniform(lo, hi, size=(H, dk))).astype(np.float32)
+    if mode == "channel_slow":
+        nslow = int(round(0.1 * dk))
+        for h in range(H):
+            idx = rng.choice(dk, size=nslow, replace=False)
+            r[h, idx] = rng.uniform(1e-6, 1e-4, size=nslow).astype(np.float32)
+    return r
+
+
+def _cast(x: np.ndarray, dtype: str) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(_DT[dtype])
+
+
+def seq_inputs(B: int, T: int, H: int, dk: int, dv: int, *, dtype: str = "bf16",
+               decay: str = "uniform", seed: int = 0, with_dO: bool = False,
+               S0_scale: float = 0.0, with_dST: bool = False) -> Dict[str, torch.Tensor]:
+    """Inputs of one chunkwise call, as CPU tensors in ``dtype`` ([B, T, H, D] layout).
+
+    Keys: q, k, v, log_a, erase, write, gamma (dtype); dO (dtype, if asked);
+    S0 (fp32 [B, H, dk, dv] or None); dS_T (fp32 or None).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    f32 = np.float32
+    q = _silu_unit(rng.standard_normal((B, T, H, dk), dtype=f32))
+    k = _silu_unit(rng.standard_normal((B, T, H, dk), dtype=f32))
+    v = rng.standard_normal((B, T, H, dv), dtype=f32)
+    if decay == "uniform":
+        log_a = rng.uniform(-3.0, -1e-3, size=(B, T, H, dk)).astype(f32)
+    elif decay in ("channel", "channel_slow"):
+        r = _decay_rates(rng, H, dk, decay)
+        log_a = np.broadcast_to(-r[None, None, :, :], (B, T, H, dk)).astype(f32)
+    elif decay == "zero":
+        log_a = np.zeros((B, T, H, dk), dtype=f32)
+    else:
+        raise ValueError(f"unknown decay mode {decay!r}")
+    erase = _sigmoid(rng.standard_normal((B, T, H, dk), dtype=f32))
+    write = _sigmoid(rng.standard_normal((B, T, H, dv), dtype=f32))
+    gamma = 2.0 * _sigmoid(rng.standard_normal((B, T, H, dk), dtype=f32))
+    out = {n: _cast(a, dtype) for n, a in
+           (("q", q), ("k", k), ("v", v), ("log_a", log_a), ("erase", erase), ("write", write), ("gamma", gamma))}
+    out["dO"] = _cast(rng.standard_normal((B, T, H, dv), dtype=f32), dtype) if with_dO else None
+    if S0_scale:
+        out["S0"] = torch.from_numpy(S0_scale * rng.standard_normal((B, H, dk, dv), dtype=f32))
+    else:
+        out["S0"] = None
+    out["dS_T"] = torch.from_numpy(rng.standard_normal((B, H, dk, dv), dtype=f32)) if with_dST else None
+    return out
+
+
+def step_rates(H: int, dk: int, seed: int = 0, mode: str = "channel") -> np.ndarray:
+    """Per-(head, channel) decay rates for a decode stream, fixed over steps, [H, dk] fp32."""
+    rng = np.random.Generator(np.random.PCG64([seed, 1 << 20]))
+    return _decay_rates(rng, H, dk, mode)
+
+
+def step_inputs(N: int, H: int, dk: int, dv: int, step: int, *, rates: np.ndarray,
+                dtype: str = "bf16", seed: int = 0) -> Dict[str, torch.Tensor]:
+    """Inputs of decode step ``step`` for N streams ([N, H, D] layout, CPU tensors).
+
+    Each step has its own PCG64 stream keyed by (seed, step), so any subset
+    of steps can be regenerated independently.  log_a = -rates for every step.
+    """
+    rng = np.random.Generator(np.random.PCG64([seed, step]))
+    f32 = np.float32
+    q = _silu_unit(rng.standard_normal((N, H, dk), dtype=f32))
+    k = _silu_unit(rng.standard_normal((N, H, dk), dtype=f32))
+    v = rng.standard_normal((N, H, dv), dtype=f32)
+    log_a = np.broadcast_to(-rates[None, :, :], (N, H, dk)).astype(f32)
+    erase = _sigmoid(rng.standard_normal((N, H, dk), dtype=f32))
+    write = _sigmoid(rng.standard_normal((N, H, dv), dtype=f32))
+    gamma = 2.0 * _sigmoid(rng.standard_normal((N, H, dk), dtype=f32))
+    return {n: _cast(a, dtype) for n, a in
+            (("q", q), ("k", k), ("v", v), ("log_a", log_a), ("erase", erase), ("write", write), ("gamma", gamma))}
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One workload: a name, its sizes and its input recipe."""
+    name: str
+    B: int
+    T: int
+    H: int
+    dk: int
+    dv: int
+    chunk: int
+    dtype: str
+    decay: str
+    backward: bool = False
+    extra: dict = field(default_factory=dict)
+
+
+WORKLOADS = {
+    "tiny_f32": Workload("tiny_f32", 1, 256, 2, 64, 64, 64, "f32", "uniform"),
+    "layer_fwd_4k": Workload("layer_fwd_4k", 8, 4096, 16, 128, 128, 64, "bf16", "channel"),
+    "layer_fwdbwd_4k": Workload("layer_fwdbwd_4k", 8, 4096, 16, 128, 128, 64, "bf16", "channel", backward=True),
+    "long_32k_c128": Workload("long_32k_c128", 1, 32768, 16, 128, 128, 128, "bf16", "channel_slow", backward=True),
+    "long_32k_c256": Workload("long_32k_c256", 1, 32768, 16, 128, 128, 256, "bf16", "channel_slow", backward=True),
+    "decode_64x16": Workload("decode_64x16", 64, 4096, 16, 128, 128, 1, "bf16", "channel",
+                             extra={"steps": 4096}),
+}
