@@ -1,0 +1,219 @@
+"""Muir gated delta-rule operator on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over ``libmuir.so`` (declared in ``include/muir.h``).
+Every step of the operator runs in the library's HIP kernels; this module
+only checks tensor arguments, allocates outputs and workspaces with torch
+(device memory plumbing) and passes raw pointers plus the current HIP stream.
+If the library has not been built, importing works but every call raises.
+
+Operator (arXiv 2611.08376, abstract and Methodology): per head, a state
+S (dk x dv) is decayed row-wise by exp(log_a_t), the prediction of the
+erase-gated key is erased, the gated value write_t*v_t is written along k_t,
+and the output reads S_t through gamma_t*q_t.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["muir_chunk_fwd", "muir_chunk_bwd", "muir_step", "muir_chunk_fwd_workspace",
+           "muir_chunk_bwd_workspace", "lib", "library_path", "MuirError", "STATUS"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libmuir.so")
+
+MUIR_F32, MUIR_BF16 = 0, 1
+STATUS = {0: "MUIR_OK", 1: "MUIR_ERR_NULL", 2: "MUIR_ERR_SHAPE", 3: "MUIR_ERR_DTYPE",
+          4: "MUIR_ERR_WORKSPACE", 5: "MUIR_ERR_ALIGN", 6: "MUIR_ERR_HIP"}
+
+
+class MuirError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {STATUS.get(code, code)} ({_status_text(code)})")
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded ``libmuir.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: run __graft_entry__.build() "
+                               "(or python -m gated_delta_rule_muir_amd._build) first")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        D = ctypes.POINTER(_Dims)
+        L.muir_abi_version.restype = I32
+        L.muir_status_string.argtypes = [ctypes.c_int]
+        L.muir_status_string.restype = ctypes.c_char_p
+        L.muir_chunk_fwd_workspace.argtypes = [D]
+        L.muir_chunk_fwd_workspace.restype = SZ
+        L.muir_chunk_bwd_workspace.argtypes = [D]
+        L.muir_chunk_bwd_workspace.restype = SZ
+        L.muir_chunk_fwd.argtypes = [D] + [P] * 7 + [P, P, P, P] + [P, SZ, P]
+        L.muir_chunk_fwd.restype = ctypes.c_int
+        L.muir_chunk_bwd.argtypes = [D] + [P] * 7 + [P, P, P, P] + [P] * 8 + [P, SZ, P]
+        L.muir_chunk_bwd.restype = ctypes.c_int
+        L.muir_step.argtypes = [I32] * 5 + [P] * 7 + [P, P, P]
+        L.muir_step.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _status_text(code: int) -> str:
+    try:
+        return lib().muir_status_string(code).decode()
+    except Exception:  # library missing while formatting an error
+        return STATUS.get(code, str(code))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MUIR_BF16
+    if t.dtype == torch.float32:
+        return MUIR_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_io(name: str, t: torch.Tensor, shape, dtype, device) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dims(B, T, H, dk, dv, chunk, dtype) -> _Dims:
+    return _Dims(B, T, H, dk, dv, chunk, dtype)
+
+
+def muir_chunk_fwd_workspace(B, T, H, dk, dv, chunk, dtype=MUIR_BF16) -> int:
+    d = _dims(B, T, H, dk, dv, chunk, dtype)
+    return int(lib().muir_chunk_fwd_workspace(ctypes.byref(d)))
+
+
+def muir_chunk_bwd_workspace(B, T, H, dk, dv, chunk, dtype=MUIR_BF16) -> int:
+    d = _dims(B, T, H, dk, dv, chunk, dtype)
+    return int(lib().muir_chunk_bwd_workspace(ctypes.byref(d)))
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def muir_chunk_fwd(q, k, v, log_a, erase, write, gamma, S0=None, *, chunk: int = 64,
+                   save_states: bool = False, final_state: bool = True,
+                   workspace: Optional[torch.Tensor] = None, out=None
+                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
+    """Chunkwise forward.  Inputs [B, T, H, D] (bf16 or fp32, on one GPU).
+
+    Returns (o [B,T,H,dv] in the input dtype, S_T [B,H,dk,dv] fp32 or None,
+    S_chunks [B,H,T/chunk,dk,dv] fp32 or None).
+    """
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for n, t in (("q", q), ("k", k), ("log_a", log_a), ("erase", erase), ("gamma", gamma)):
+        _check_io(n, t, (B, T, H, dk), dt, dev)
+    for n, t in (("v", v), ("write", write)):
+        _check_io(n, t, (B, T, H, dv), dt, dev)
+    if S0 is not None:
+        _check_io("S0", S0, (B, H, dk, dv), torch.float32, dev)
+    o = out if out is not None else torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if final_state else None
+    S_chunks = (torch.empty((B, H, T // chunk if chunk else 0, dk, dv), dtype=torch.float32, device=dev)
+                if save_states else None)
+    d = _dims(B, T, H, dk, dv, chunk, code)
+    nbytes = int(lib().muir_chunk_fwd_workspace(ctypes.byref(d)))
+    ws = _workspace(nbytes, dev, workspace)
+    rc = lib().muir_chunk_fwd(ctypes.byref(d), *(_ptr(t) for t in (q, k, v, log_a, erase, write, gamma)),
+                              _ptr(S0), _ptr(o), _ptr(S_T), _ptr(S_chunks),
+                              _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
+    if rc != 0:
+        raise MuirError(rc, "muir_chunk_fwd")
+    return o, S_T, S_chunks
+
+
+def muir_chunk_bwd(q, k, v, log_a, erase, write, gamma, dO, S0=None, S_chunks=None, dS_T=None, *,
+                   chunk: int = 64, workspace: Optional[torch.Tensor] = None, want_dS0: bool = True):
+    """Chunkwise backward.  Returns a dict of fp32 gradients
+    (dq, dk, dv, dlog_a, derase, dwrite, dgamma, dS0)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for n, t in (("q", q), ("k", k), ("log_a", log_a), ("erase", erase), ("gamma", gamma)):
+        _check_io(n, t, (B, T, H, dk), dt, dev)
+    for n, t in (("v", v), ("write", write), ("dO", dO)):
+        _check_io(n, t, (B, T, H, dv), dt, dev)
+    if S0 is not None:
+        _check_io("S0", S0, (B, H, dk, dv), torch.float32, dev)
+    if dS_T is not None:
+        _check_io("dS_T", dS_T, (B, H, dk, dv), torch.float32, dev)
+    if S_chunks is not None:
+        _check_io("S_chunks", S_chunks, (B, H, T // chunk, dk, dv), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {n: torch.empty((B, T, H, dk), **f32) for n in ("dq", "dk", "dlog_a", "derase", "dgamma")}
+    g.update({n: torch.empty((B, T, H, dv), **f32) for n in ("dv", "dwrite")})
+    g["dS0"] = torch.empty((B, H, dk, dv), **f32) if want_dS0 else None
+    d = _dims(B, T, H, dk, dv, chunk, code)
+    nbytes = int(lib().muir_chunk_bwd_workspace(ctypes.byref(d)))
+    ws = _workspace(nbytes, dev, workspace)
+    rc = lib().muir_chunk_bwd(ctypes.byref(d), *(_ptr(t) for t in (q, k, v, log_a, erase, write, gamma)),
+                              _ptr(S0), _ptr(S_chunks), _ptr(dO), _ptr(dS_T),
+                              *(_ptr(g[n]) for n in ("dq", "dk", "dv", "dlog_a", "derase", "dwrite",
+                                                     "dgamma", "dS0")),
+                              _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
+    if rc != 0:
+        raise MuirError(rc, "muir_chunk_bwd")
+    return g
+
+
+def muir_step(q, k, v, log_a, erase, write, gamma, S, *, out=None) -> torch.Tensor:
+    """One decode step for [N, H, D] inputs; S [N, H, dk, dv] fp32 is updated in place.
+    Returns o [N, H, dv] in the input dtype."""
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for n, t in (("q", q), ("k", k), ("log_a", log_a), ("erase", erase), ("gamma", gamma)):
+        _check_io(n, t, (N, H, dk), dt, dev)
+    for n, t in (("v", v), ("write", write)):
+        _check_io(n, t, (N, H, dv), dt, dev)
+    _check_io("S", S, (N, H, dk, dv), torch.float32, dev)
+    o = out if out is not None else torch.empty((N, H, dv), dtype=dt, device=dev)
+    rc = lib().muir_step(N, H, dk, dv, code, *(_ptr(t) for t in (q, k, v, log_a, erase, write, gamma)),
+                         _ptr(S), _ptr(o), _stream(dev))
+    if rc != 0:
+        raise MuirError(rc, "muir_step")
+    return o

@@ -1,0 +1,116 @@
+// Device-side helpers shared by the Muir HIP kernels (gfx950 only).
+//
+// MFMA lane layouts used throughout (wave64; checked on hardware):
+//   v_mfma_f32_16x16x16_bf16  A: lane l holds row (l%16), k = 4*(l/16)+i, i<4
+//                             B: lane l holds col (l%16), k = 4*(l/16)+i, i<4
+//                             D: lane l holds row 4*(l/16)+i, col (l%16), i<4
+//   v_mfma_f32_16x16x4_f32    A: lane l holds row (l%16), k = l/16
+//                             B: lane l holds col (l%16), k = l/16
+//                             D: as above.
+// The accumulator layout of a 16x16 tile (4 consecutive rows per lane) is the
+// operand layout of a 16x16x16 product whose contraction runs over those rows,
+// which lets results feed the next product without a shuffle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muir {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// ---- bf16 storage helpers (raw 16-bit patterns) ------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (finite inputs; NaN is kept a NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return static_cast<uint16_t>((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+// Element loads from an input tensor of either dtype.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+  static __device__ __forceinline__ void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// Load 4 consecutive elements (16-byte aligned for fp32, 8-byte for bf16).
+__device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 load4(const uint16_t* p) {
+  uint2 r = *reinterpret_cast<const uint2*>(p);
+  f32x4 o;
+  o[0] = __uint_as_float(r.x << 16);
+  o[1] = __uint_as_float(r.x & 0xffff0000u);
+  o[2] = __uint_as_float(r.y << 16);
+  o[3] = __uint_as_float(r.y & 0xffff0000u);
+  return o;
+}
+__device__ __forceinline__ void store4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void store4(uint16_t* p, f32x4 v) {
+  uint2 r;
+  r.x = pack_bf16x2(v[0], v[1]);
+  r.y = pack_bf16x2(v[2], v[3]);
+  *reinterpret_cast<uint2*>(p) = r;
+}
+
+// ---- MFMA wrappers -----------------------------------------------------------
+
+// acc += A(16x16 bf16) * B(16x16 bf16); operands packed as 4 bf16 per lane.
+__device__ __forceinline__ f32x4 mma16_bf16(i16x4 a, i16x4 b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+}
+
+// acc += A(16x4 f32) * B(4x16 f32); one value per lane.
+__device__ __forceinline__ f32x4 mma4_f32(float a, float b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ i16x4 pack4(f32x4 v) {
+  uint32_t lo = pack_bf16x2(v[0], v[1]);
+  uint32_t hi = pack_bf16x2(v[2], v[3]);
+  i16x4 r;
+  r[0] = static_cast<short>(lo & 0xffffu);
+  r[1] = static_cast<short>(lo >> 16);
+  r[2] = static_cast<short>(hi & 0xffffu);
+  r[3] = static_cast<short>(hi >> 16);
+  return r;
+}
+
+__device__ __forceinline__ i16x4 load_bf16x4(const uint16_t* p) {
+  uint2 r = *reinterpret_cast<const uint2*>(p);
+  i16x4 o;
+  o[0] = static_cast<short>(r.x & 0xffffu);
+  o[1] = static_cast<short>(r.x >> 16);
+  o[2] = static_cast<short>(r.y & 0xffffu);
+  o[3] = static_cast<short>(r.y >> 16);
+  return o;
+}
+
+__device__ __forceinline__ f32x4 zero4() {
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return z;
+}
+
+// Reductions over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace muir

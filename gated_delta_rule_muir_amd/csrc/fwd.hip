@@ -1,0 +1,460 @@
+// Chunkwise forward of the Muir gated delta rule (gfx950).
+//
+// arXiv 2611.08376, Methodology and the fig:kernel caption: each chunk is a
+// triangular system; cumulative log-decay is split at interval boundaries so
+// every exponential factor lies in (0, 1]; the per-chunk systems are inverted
+// without division (block-Neumann products at the leaves).
+//
+// Notation for one chunk of C tokens (b, h fixed), Lam_r = sum_{s<=r} log_a_s
+// (chunk-local), u_r = write_r*v_r, ek_r = erase_r*k_r, qt_r = gamma_r*q_r:
+//   A_ri = sum_j ek_rj k_ij exp(Lam_rj - Lam_ij)   (i < r)      erase system
+//   P_ri = sum_j qt_rj k_ij exp(Lam_rj - Lam_ij)   (i <= r)     readout kernel
+//   [U~ | W] = (I + A)^-1 [U | exp(Lam) * ek]
+//   Q' = exp(Lam) * qt - P W ,  O~ = P U~ ,  Kbar_i = exp(Lam_C - Lam_i) * k_i
+// so that with S the state at the chunk start
+//   o = O~ + Q' S ,  Delta = U~ - W S ,  S_next = diag(exp(Lam_C)) S + Kbar^T Delta.
+//
+// Kernel 1 (fwd_prep, one workgroup per chunk) computes the chunk summary
+// (W, Q', Kbar, U~, O~, exp(Lam_C)).  It never forms the C x C matrices:
+// the chunk is walked in 16-token blocks with an inner state
+//   H_I = sum_{i < 16 I} (k_i exp(B_I - Lam_i)) (x) [U~_i | W_i]     (dk x (dv+dk))
+// pivoted at the block boundary B_I = Lam_{16 I - 1}, so that for block I
+//   [U~|W]_I = T_II ([U|K~]_I - X_I H_I),   X_r = ek_r exp(Lam_r - B_I)
+//   [O~|P W]_I = Y_I H_I + P_II [U~|W]_I,   Y_r = qt_r exp(Lam_r - B_I)
+//   H_{I+1} = diag(exp(B_{I+1} - B_I)) H_I + Ke_I^T [U~|W]_I,  Ke_i = k_i exp(B_{I+1} - Lam_i)
+// All factors are exponentials of non-positive numbers.  The 16 x 16 leaf
+// blocks A_II, P_II are formed directly from per-pair factors
+// exp(Lam_r - Lam_i), r >= i, and T_II = (I + A_II)^-1 is the exact Neumann
+// product (I - A)(I + A^2)(I + A^4)(I + A^8) (A_II^16 = 0).
+//
+// Kernel 2 (fwd_scan) walks the chunks of one (b, h) in order; each wave owns
+// 16 value columns of S (fp32, held in MFMA accumulators) and applies the
+// three products above per chunk.
+#include "kernels.h"
+#include "mma.h"
+
+namespace muir {
+
+namespace {
+
+constexpr int PREP_THREADS = 256;
+
+template <typename TC>
+struct SummaryView {
+  TC* W;     // [C][DK]
+  TC* Qp;    // [C][DK]
+  TC* KbT;   // [DK][C]
+  TC* UtT;   // [DV][C]
+  TC* OtT;   // [DV][C]
+  float* gC; // [DK]
+  __device__ SummaryView(char* base, int C, int DK, int DV) {
+    W = reinterpret_cast<TC*>(base);
+    Qp = W + static_cast<size_t>(C) * DK;
+    KbT = Qp + static_cast<size_t>(C) * DK;
+    UtT = KbT + static_cast<size_t>(C) * DK;
+    OtT = UtT + static_cast<size_t>(C) * DV;
+    gC = reinterpret_cast<float*>(OtT + static_cast<size_t>(C) * DV);
+  }
+};
+
+template <typename Tin, int DK>
+__global__ __launch_bounds__(PREP_THREADS) void fwd_prep_kernel(
+    int T, int H, int C, const Tin* __restrict__ q, const Tin* __restrict__ k,
+    const Tin* __restrict__ v, const Tin* __restrict__ log_a, const Tin* __restrict__ erase,
+    const Tin* __restrict__ write, const Tin* __restrict__ gamma, char* __restrict__ summ,
+    size_t summ_bytes) {
+  typedef Tin TC;
+  typedef MM<TC> M;
+  typedef typename M::frag frag;
+  constexpr int DV = DK;
+  constexpr int NH = DV + DK;   // columns of the inner state: [U~ | W]
+  constexpr int CW = NH / 4;    // columns per wave
+  constexpr int NT = CW / 16;   // column tiles per wave
+  constexpr int RT = DK / 16;   // row tiles of the inner state
+  constexpr int PAD = DK + 1;   // fp32 row stride of the [16][DK] leaf tiles
+  constexpr int PT = DK + 4;    // row stride of the [16][DK] operand tiles
+
+  const int NC = T / C;
+  const int NB = C / 16;
+  const int chunk = blockIdx.x;
+  const int bh = chunk / NC;
+  const int c = chunk - bh * NC;
+  const int b = bh / H;
+  const int h = bh - b * H;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+
+  SummaryView<TC> out(summ + static_cast<size_t>(chunk) * summ_bytes, C, DK, DV);
+  // element (t, j) of a [B, T, H, D] tensor for chunk-local token t
+  const size_t rowbase = (static_cast<size_t>(b) * T + static_cast<size_t>(c) * C) * H + h;
+  auto gidx = [&](int t, int j) -> size_t { return (rowbase + static_cast<size_t>(t) * H) * DK + j; };
+
+  __shared__ __attribute__((aligned(16))) float sB[17][DK];          // block-boundary cumulative log-decay B_0..B_NB
+  __shared__ float sL[16][PAD];         // Lam of the block's tokens
+  __shared__ float sBK[16][PAD];        // ek
+  __shared__ float sQT[16][PAD];        // qt
+  __shared__ float sK[16][PAD];         // k
+  __shared__ __attribute__((aligned(16))) TC sX[16][PT];             // X rows (operand)
+  __shared__ __attribute__((aligned(16))) TC sY[16][PT];             // Y rows (operand)
+  __shared__ __attribute__((aligned(16))) TC sKe[DK][20];            // Ke^T (operand, rows = key channels)
+  __shared__ float sR[NH][16];          // [U | K~]^T of the block
+  __shared__ float sQh[DK][16];         // Q^^T of the block (exp(Lam) * qt)
+  __shared__ float sWa[16][17];         // A_II, then powers of A_II
+  __shared__ float sWt[16][17];         // running Neumann product
+  __shared__ __attribute__((aligned(16))) TC sT[16][20];             // T_II (operand)
+  __shared__ __attribute__((aligned(16))) TC sP[16][20];             // P_II (operand)
+  __shared__ float sG[DK];              // exp(B_{I+1} - B_I)
+  __shared__ __attribute__((aligned(16))) TC sStage[16][2 * DK + 8]; // W and Q' rows of the block, for row-layout stores
+
+  // ---- boundaries of the cumulative log-decay, and exp(Lam_C) ----
+  if (tid < DK) {
+    float L = 0.f;
+    sB[0][tid] = 0.f;
+    for (int t = 0; t < C; ++t) {
+      L += Elem<Tin>::load(log_a, gidx(t, tid));
+      if ((t & 15) == 15) sB[(t >> 4) + 1][tid] = L;
+    }
+    out.gC[tid] = __expf(L);
+  }
+
+  f32x4 Hs[RT][NT];
+#pragma unroll
+  for (int s = 0; s < RT; ++s)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) Hs[s][n] = zero4();
+  __syncthreads();
+
+  for (int I = 0; I < NB; ++I) {
+    const int r0 = 16 * I;
+    // ---- within-block cumulative log-decay ----
+    if (tid < DK) {
+      float L = sB[I][tid];
+#pragma unroll 4
+      for (int r = 0; r < 16; ++r) {
+        L += Elem<Tin>::load(log_a, gidx(r0 + r, tid));
+        sL[r][tid] = L;
+      }
+      sG[tid] = __expf(sB[I + 1][tid] - sB[I][tid]);
+    }
+    __syncthreads();
+
+    // ---- elementwise operand tiles ----
+    for (int idx = tid; idx < 16 * DK; idx += PREP_THREADS) {
+      const int r = idx / DK;
+      const int j = idx - r * DK;
+      const size_t gi = gidx(r0 + r, j);
+      const float kj = Elem<Tin>::load(k, gi);
+      const float ek = Elem<Tin>::load(erase, gi) * kj;
+      const float qt = Elem<Tin>::load(gamma, gi) * Elem<Tin>::load(q, gi);
+      const float u = Elem<Tin>::load(write, gi) * Elem<Tin>::load(v, gi);
+      const float L = sL[r][j];
+      const float fs = __expf(L - sB[I][j]);   // exp(Lam_r - B_I) in (0, 1]
+      const float GL = __expf(L);              // exp(Lam_r) in (0, 1]
+      sBK[r][j] = ek;
+      sQT[r][j] = qt;
+      sK[r][j] = kj;
+      sX[r][j] = M::cvt(ek * fs);
+      sY[r][j] = M::cvt(qt * fs);
+      sKe[j][r] = M::cvt(kj * __expf(sB[I + 1][j] - L));
+      sR[j][r] = u;
+      sR[DV + j][r] = ek * GL;
+      sQh[j][r] = qt * GL;
+      out.KbT[static_cast<size_t>(j) * C + r0 + r] = M::cvt(kj * __expf(sB[NB][j] - L));
+    }
+    __syncthreads();
+
+    // ---- leaf block: A_II (strictly lower), P_II (lower), start of the Neumann product ----
+    {
+      const int r = tid >> 4;
+      const int i = tid & 15;
+      float a = 0.f, p = 0.f;
+      if (i <= r) {
+        for (int j = 0; j < DK; ++j) {
+          const float kk = sK[i][j] * __expf(sL[r][j] - sL[i][j]);
+          a += sBK[r][j] * kk;
+          p += sQT[r][j] * kk;
+        }
+      }
+      if (i >= r) a = 0.f;
+      sP[r][i] = M::cvt(p);
+      sWa[r][i] = a;
+      sWt[r][i] = (r == i ? 1.f : 0.f) - a;
+    }
+    __syncthreads();
+    // T_II = (I - A)(I + A^2)(I + A^4)(I + A^8)
+    {
+      const int r = tid >> 4;
+      const int cc = tid & 15;
+#pragma unroll 1
+      for (int step = 0; step < 3; ++step) {
+        float sq = 0.f;
+#pragma unroll
+        for (int x = 0; x < 16; ++x) sq += sWa[r][x] * sWa[x][cc];
+        __syncthreads();
+        sWa[r][cc] = sq;
+        __syncthreads();
+        float t2 = sWt[r][cc];
+#pragma unroll
+        for (int x = 0; x < 16; ++x) t2 += sWt[r][x] * sWa[x][cc];
+        __syncthreads();
+        sWt[r][cc] = t2;
+        __syncthreads();
+      }
+      sT[r][cc] = M::cvt(sWt[r][cc]);
+    }
+    __syncthreads();
+
+    // ---- per-wave products over this wave's columns of [U~ | W] ----
+    const int col0 = wave * CW;
+    f32x4 XH[NT], YH[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      XH[n] = zero4();
+      YH[n] = zero4();
+    }
+    if (I > 0) {
+#pragma unroll
+      for (int s = 0; s < RT; ++s) {
+        const frag xa = M::load(&sX[c16][16 * s + 4 * g]);
+        const frag ya = M::load(&sY[c16][16 * s + 4 * g]);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const frag hb = M::from_f32(Hs[s][n]);
+          XH[n] = M::mma(xa, hb, XH[n]);
+          YH[n] = M::mma(ya, hb, YH[n]);
+        }
+      }
+    }
+    const frag ta = M::load(&sT[c16][4 * g]);
+    const frag pa = M::load(&sP[c16][4 * g]);
+    f32x4 UW[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int colg = col0 + 16 * n + c16;
+      f32x4 rhs;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rhs[i] = sR[colg][4 * g + i] - XH[n][i];
+      const f32x4 uw = M::mma(ta, M::from_f32(rhs), zero4());
+      const f32x4 op = M::mma(pa, M::from_f32(uw), YH[n]);
+      UW[n] = uw;
+      if (colg < DV) {
+        store4(out.UtT + static_cast<size_t>(colg) * C + r0 + 4 * g, uw);
+        store4(out.OtT + static_cast<size_t>(colg) * C + r0 + 4 * g, op);
+      } else {
+        const int j = colg - DV;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sStage[4 * g + i][j] = M::cvt(uw[i]);
+          sStage[4 * g + i][DK + j] = M::cvt(sQh[j][4 * g + i] - op[i]);
+        }
+      }
+    }
+    // ---- advance the inner state to the next block boundary ----
+    if (I + 1 < NB) {
+#pragma unroll
+      for (int s = 0; s < RT; ++s) {
+        const frag ka = M::load(&sKe[16 * s + c16][4 * g]);
+        f32x4 gs;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gs[i] = sG[16 * s + 4 * g + i];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) Hs[s][n] = M::mma(ka, M::from_f32(UW[n]), Hs[s][n] * gs);
+      }
+    }
+    __syncthreads();
+    // ---- W and Q' rows of the block (row layout, 4 elements per store) ----
+    for (int idx = tid; idx < 16 * DK / 4; idx += PREP_THREADS) {
+      const int r = idx / (DK / 4);
+      const int j4 = (idx - r * (DK / 4)) * 4;
+      f32x4 wv, qv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wv[i] = M::to_f32(sStage[r][j4 + i]);
+        qv[i] = M::to_f32(sStage[r][DK + j4 + i]);
+      }
+      store4(out.W + static_cast<size_t>(r0 + r) * DK + j4, wv);
+      store4(out.Qp + static_cast<size_t>(r0 + r) * DK + j4, qv);
+    }
+    __syncthreads();
+  }
+}
+
+constexpr int SCAN_SB = 64;  // tokens staged per step of the scan
+
+template <typename Tin, int DK, int NW>
+__global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
+    int T, int H, int C, const char* __restrict__ summ, size_t summ_bytes,
+    const float* __restrict__ S0, Tin* __restrict__ o, float* __restrict__ S_chunks,
+    float* __restrict__ S_T) {
+  typedef Tin TC;
+  typedef MM<TC> M;
+  typedef typename M::frag frag;
+  constexpr int DV = DK;
+  constexpr int RT = DK / 16;
+  constexpr int NV = 16 * NW;
+  constexpr int PW = DK + 4;
+  constexpr int PK = SCAN_SB + 4;
+
+  const int NC = T / C;
+  const int nvb = DV / NV;
+  const int bh = blockIdx.x / nvb;
+  const int vb = blockIdx.x - bh * nvb;
+  const int b = bh / H;
+  const int h = bh - b * H;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+  const int colg = vb * NV + 16 * wave + c16;
+
+  __shared__ __attribute__((aligned(16))) TC sW[SCAN_SB][PW];
+  __shared__ __attribute__((aligned(16))) TC sQ[SCAN_SB][PW];
+  __shared__ __attribute__((aligned(16))) TC sKb[DK][PK];
+  __shared__ float sgC[DK];
+
+  const size_t sbase = static_cast<size_t>(bh) * DK * DV;
+  f32x4 S[RT];
+#pragma unroll
+  for (int s = 0; s < RT; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      S[s][i] = S0 ? S0[sbase + static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] : 0.f;
+
+  for (int c = 0; c < NC; ++c) {
+    char* base = const_cast<char*>(summ) + (static_cast<size_t>(bh) * NC + c) * summ_bytes;
+    SummaryView<TC> sv(base, C, DK, DV);
+    if (S_chunks) {
+      float* dst = S_chunks + (static_cast<size_t>(bh) * NC + c) * DK * DV;
+#pragma unroll
+      for (int s = 0; s < RT; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] = S[s][i];
+    }
+    frag Sf[RT];
+#pragma unroll
+    for (int s = 0; s < RT; ++s) Sf[s] = M::from_f32(S[s]);
+    f32x4 dS[RT];
+#pragma unroll
+    for (int s = 0; s < RT; ++s) dS[s] = zero4();
+
+    for (int sb = 0; sb < C; sb += SCAN_SB) {
+      __syncthreads();
+      for (int idx = tid; idx < SCAN_SB * DK / 4; idx += 64 * NW) {
+        const int r = idx / (DK / 4);
+        const int j4 = (idx - r * (DK / 4)) * 4;
+        const f32x4 wv = load4(sv.W + static_cast<size_t>(sb + r) * DK + j4);
+        const f32x4 qv = load4(sv.Qp + static_cast<size_t>(sb + r) * DK + j4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sW[r][j4 + i] = M::cvt(wv[i]);
+          sQ[r][j4 + i] = M::cvt(qv[i]);
+        }
+      }
+      for (int idx = tid; idx < DK * SCAN_SB / 4; idx += 64 * NW) {
+        const int j = idx / (SCAN_SB / 4);
+        const int r4 = (idx - j * (SCAN_SB / 4)) * 4;
+        const f32x4 kv = load4(sv.KbT + static_cast<size_t>(j) * C + sb + r4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sKb[j][r4 + i] = M::cvt(kv[i]);
+      }
+      if (sb == 0)
+        for (int j = tid; j < DK; j += 64 * NW) sgC[j] = sv.gC[j];
+      __syncthreads();
+#pragma unroll 1
+      for (int m = 0; m < SCAN_SB / 16; ++m) {
+        f32x4 Oa = zero4(), Da = zero4();
+#pragma unroll
+        for (int s = 0; s < RT; ++s) {
+          const frag qa = M::load(&sQ[16 * m + c16][16 * s + 4 * g]);
+          const frag wa = M::load(&sW[16 * m + c16][16 * s + 4 * g]);
+          Oa = M::mma(qa, Sf[s], Oa);
+          Da = M::mma(wa, Sf[s], Da);
+        }
+        const int tok = sb + 16 * m + 4 * g;  // chunk-local token of element i = 0
+        const f32x4 ot = load4(sv.OtT + static_cast<size_t>(colg) * C + tok);
+        const f32x4 ut = load4(sv.UtT + static_cast<size_t>(colg) * C + tok);
+        if (o) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const size_t oi =
+                ((static_cast<size_t>(b) * T + static_cast<size_t>(c) * C + tok + i) * H + h) * DV + colg;
+            Elem<Tin>::store(o, oi, Oa[i] + ot[i]);
+          }
+        }
+        const frag df = M::from_f32(ut - Da);
+#pragma unroll
+        for (int s = 0; s < RT; ++s) {
+          const frag ka = M::load(&sKb[16 * s + c16][16 * m + 4 * g]);
+          dS[s] = M::mma(ka, df, dS[s]);
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < RT; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[s][i] = sgC[16 * s + 4 * g + i] * S[s][i] + dS[s][i];
+  }
+  if (S_T) {
+#pragma unroll
+    for (int s = 0; s < RT; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S_T[sbase + static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] = S[s][i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_prep(const ChunkShape& s, const void* q, const void* k, const void* v,
+                           const void* log_a, const void* erase, const void* write,
+                           const void* gamma, void* summ, hipStream_t stream) {
+  const unsigned grid = static_cast<unsigned>(s.nchunks());
+  if (grid == 0) return hipSuccess;
+#define MUIR_PREP(TT, DD)                                                                          \
+  hipLaunchKernelGGL((fwd_prep_kernel<TT, DD>), dim3(grid), dim3(PREP_THREADS), 0, stream, s.T,     \
+                     s.H, s.C, (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a,           \
+                     (const TT*)erase, (const TT*)write, (const TT*)gamma, (char*)summ,              \
+                     s.summary_bytes())
+  if (s.bf16) {
+    if (s.DK == 128) MUIR_PREP(uint16_t, 128);
+    else MUIR_PREP(uint16_t, 64);
+  } else {
+    if (s.DK == 128) MUIR_PREP(float, 128);
+    else MUIR_PREP(float, 64);
+  }
+#undef MUIR_PREP
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S0, void* o,
+                           float* S_chunks, float* S_T, hipStream_t stream) {
+  const int heads = s.B * s.H;
+  if (heads == 0) return hipSuccess;
+  // Four waves (64 columns) per workgroup when that still fills the chip,
+  // else one wave (16 columns) per workgroup for more independent chains.
+  const bool wide = static_cast<long long>(heads) * (s.DV / 64) >= 256;
+#define MUIR_SCAN(TT, DD, NW)                                                                      \
+  hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, NW>), dim3(heads * (s.DV / (16 * NW))),              \
+                     dim3(64 * NW), 0, stream, s.T, s.H, s.C, (const char*)summ, s.summary_bytes(), \
+                     S0, (TT*)o, S_chunks, S_T)
+  if (s.bf16) {
+    if (s.DK == 128) {
+      if (wide) MUIR_SCAN(uint16_t, 128, 4); else MUIR_SCAN(uint16_t, 128, 1);
+    } else {
+      if (wide) MUIR_SCAN(uint16_t, 64, 4); else MUIR_SCAN(uint16_t, 64, 1);
+    }
+  } else {
+    if (s.DK == 128) {
+      if (wide) MUIR_SCAN(float, 128, 4); else MUIR_SCAN(float, 128, 1);
+    } else {
+      if (wide) MUIR_SCAN(float, 64, 4); else MUIR_SCAN(float, 64, 1);
+    }
+  }
+#undef MUIR_SCAN
+  return hipGetLastError();
+}
+
+}  // namespace muir

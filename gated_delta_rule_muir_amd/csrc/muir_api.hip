@@ -1,0 +1,188 @@
+// C ABI of the Muir operator: argument validation, workspace sizing and
+// kernel dispatch.  Every entry point checks its arguments before launching
+// anything and never allocates, frees or synchronises.
+#include <muir.h>
+
+#include "kernels.h"
+
+using muir::ChunkShape;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+muir_status_t check_dims(const muir_dims_t* d, ChunkShape* s) {
+  if (!d) return MUIR_ERR_NULL;
+  if (d->dtype != MUIR_F32 && d->dtype != MUIR_BF16) return MUIR_ERR_DTYPE;
+  if (d->B < 0 || d->T < 0 || d->H < 0) return MUIR_ERR_SHAPE;
+  if (d->dk != d->dv || (d->dk != 64 && d->dk != 128)) return MUIR_ERR_SHAPE;
+  if (d->chunk != 64 && d->chunk != 128 && d->chunk != 256) return MUIR_ERR_SHAPE;
+  if (d->T % d->chunk != 0) return MUIR_ERR_SHAPE;
+  // keep every flat index inside 32-bit chunk counts and 64-bit element counts
+  if (static_cast<long long>(d->B) * d->H * (d->T / d->chunk) > (1LL << 30)) return MUIR_ERR_SHAPE;
+  s->B = d->B;
+  s->T = d->T;
+  s->H = d->H;
+  s->DK = d->dk;
+  s->DV = d->dv;
+  s->C = d->chunk;
+  s->bf16 = d->dtype == MUIR_BF16;
+  return MUIR_OK;
+}
+
+size_t fwd_ws(const ChunkShape& s) { return s.nchunks() * s.summary_bytes(); }
+
+// Backward workspace: chunk summaries, recomputed chunk states (only used when
+// the caller passes no S_chunks; always reserved so the size does not depend
+// on a pointer), and the chunk-end state gradients.
+size_t bwd_ws(const ChunkShape& s) {
+  return s.nchunks() * s.summary_bytes() + 2 * s.nchunks() * s.state_bytes();
+}
+
+muir_status_t need(const void* p) { return p ? MUIR_OK : MUIR_ERR_NULL; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t muir_abi_version(void) { return 1; }
+
+const char* muir_status_string(muir_status_t st) {
+  switch (st) {
+    case MUIR_OK: return "ok";
+    case MUIR_ERR_NULL: return "a required pointer is NULL";
+    case MUIR_ERR_SHAPE: return "unsupported or inconsistent sizes";
+    case MUIR_ERR_DTYPE: return "unknown dtype code";
+    case MUIR_ERR_WORKSPACE: return "workspace missing or too small";
+    case MUIR_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MUIR_ERR_HIP: return "a HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+size_t muir_chunk_fwd_workspace(const muir_dims_t* dims) {
+  ChunkShape s;
+  if (check_dims(dims, &s) != MUIR_OK) return 0;
+  return fwd_ws(s);
+}
+
+size_t muir_chunk_bwd_workspace(const muir_dims_t* dims) {
+  ChunkShape s;
+  if (check_dims(dims, &s) != MUIR_OK) return 0;
+  return bwd_ws(s);
+}
+
+muir_status_t muir_chunk_fwd(const muir_dims_t* dims, const void* q, const void* k,
+                             const void* v, const void* log_a, const void* erase,
+                             const void* write, const void* gamma, const float* S0, void* o,
+                             float* S_T, float* S_chunks, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  ChunkShape s;
+  muir_status_t st = check_dims(dims, &s);
+  if (st != MUIR_OK) return st;
+  const bool empty = s.nchunks() == 0;
+  if (!empty) {
+    const void* req[] = {q, k, v, log_a, erase, write, gamma, o};
+    for (const void* p : req)
+      if (!p) return MUIR_ERR_NULL;
+    for (const void* p : req)
+      if (!aligned16(p)) return MUIR_ERR_ALIGN;
+    if (!workspace || workspace_bytes < fwd_ws(s)) return MUIR_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MUIR_ERR_ALIGN;
+  }
+  const void* opt[] = {S0, S_T, S_chunks};
+  for (const void* p : opt)
+    if (p && !aligned16(p)) return MUIR_ERR_ALIGN;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (empty) {
+    // T == 0: the final state is the initial state
+    if (S_T && s.B * s.H > 0) {
+      size_t n = static_cast<size_t>(s.B) * s.H * s.state_bytes();
+      hipError_t e = S0 ? hipMemcpyAsync(S_T, S0, n, hipMemcpyDeviceToDevice, hs)
+                        : hipMemsetAsync(S_T, 0, n, hs);
+      if (e != hipSuccess) return MUIR_ERR_HIP;
+    }
+    return MUIR_OK;
+  }
+  if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, workspace, hs) != hipSuccess)
+    return MUIR_ERR_HIP;
+  if (muir::launch_fwd_scan(s, workspace, S0, o, S_chunks, S_T, hs) != hipSuccess)
+    return MUIR_ERR_HIP;
+  return MUIR_OK;
+}
+
+muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void* k,
+                             const void* v, const void* log_a, const void* erase,
+                             const void* write, const void* gamma, const float* S0,
+                             const float* S_chunks, const void* dO, const float* dS_T,
+                             float* dq, float* dk, float* dv, float* dlog_a, float* derase,
+                             float* dwrite, float* dgamma, float* dS0, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  ChunkShape s;
+  muir_status_t st = check_dims(dims, &s);
+  if (st != MUIR_OK) return st;
+  const bool empty = s.nchunks() == 0;
+  if (!empty) {
+    const void* req[] = {q, k, v, log_a, erase, write, gamma, dO,
+                         dq, dk, dv, dlog_a, derase, dwrite, dgamma};
+    for (const void* p : req)
+      if (!p) return MUIR_ERR_NULL;
+    for (const void* p : req)
+      if (!aligned16(p)) return MUIR_ERR_ALIGN;
+    if (!workspace || workspace_bytes < bwd_ws(s)) return MUIR_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MUIR_ERR_ALIGN;
+  }
+  const void* opt[] = {S0, S_chunks, dS_T, dS0};
+  for (const void* p : opt)
+    if (p && !aligned16(p)) return MUIR_ERR_ALIGN;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (empty) {
+    if (dS0 && s.B * s.H > 0) {
+      size_t n = static_cast<size_t>(s.B) * s.H * s.state_bytes();
+      hipError_t e = dS_T ? hipMemcpyAsync(dS0, dS_T, n, hipMemcpyDeviceToDevice, hs)
+                          : hipMemsetAsync(dS0, 0, n, hs);
+      if (e != hipSuccess) return MUIR_ERR_HIP;
+    }
+    return MUIR_OK;
+  }
+  char* ws = static_cast<char*>(workspace);
+  void* summ = ws;
+  float* S_rec = reinterpret_cast<float*>(ws + s.nchunks() * s.summary_bytes());
+  float* dS_chunks = S_rec + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
+  if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, summ, hs) != hipSuccess)
+    return MUIR_ERR_HIP;
+  const float* Sc = S_chunks;
+  if (!Sc) {
+    if (muir::launch_fwd_scan(s, summ, S0, nullptr, S_rec, nullptr, hs) != hipSuccess)
+      return MUIR_ERR_HIP;
+    Sc = S_rec;
+  }
+  if (muir::launch_bwd_scan(s, summ, dO, dS_T, dS_chunks, dS0, hs) != hipSuccess)
+    return MUIR_ERR_HIP;
+  if (muir::launch_bwd_chunk(s, q, k, v, log_a, erase, write, gamma, Sc, dS_chunks, dO, dq, dk,
+                             dv, dlog_a, derase, dwrite, dgamma, hs) != hipSuccess)
+    return MUIR_ERR_HIP;
+  return MUIR_OK;
+}
+
+muir_status_t muir_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtype,
+                        const void* q, const void* k, const void* v, const void* log_a,
+                        const void* erase, const void* write, const void* gamma, float* S,
+                        void* o, void* stream) {
+  if (dtype != MUIR_F32 && dtype != MUIR_BF16) return MUIR_ERR_DTYPE;
+  if (N < 0 || H < 0 || (dk != 64 && dk != 128) || dv <= 0 || dv % 64 != 0 || dv > 4096)
+    return MUIR_ERR_SHAPE;
+  if (static_cast<long long>(N) * H * (dv / 64) > (1LL << 30)) return MUIR_ERR_SHAPE;
+  if (static_cast<long long>(N) * H == 0) return MUIR_OK;
+  const void* req[] = {q, k, v, log_a, erase, write, gamma, S, o};
+  for (const void* p : req)
+    if (!p) return MUIR_ERR_NULL;
+  for (const void* p : req)
+    if (!aligned16(p)) return MUIR_ERR_ALIGN;
+  if (muir::launch_step(N, H, dk, dv, dtype == MUIR_BF16, q, k, v, log_a, erase, write, gamma, S,
+                        o, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return MUIR_ERR_HIP;
+  return MUIR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,155 @@
+/*
+ * muir.h -- C ABI of the Muir gated delta-rule operator on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operator (arXiv 2611.08376, "Muir: Linear Attention with
+ * Sensitivity-Allocated Gating and Matched-Filter Readout"; abstract and the
+ * Methodology section of the wolonglab summary page) keeps, per batch row b
+ * and head h, a state S in R^{dk x dv} (rows = key channels) and for every
+ * token t:
+ *
+ *   S'_t = diag(exp(log_a_t)) S_{t-1}                      row-wise decay
+ *   d_t  = write_t * v_t - S'_t^T (erase_t * k_t)          erase the key's prediction
+ *   S_t  = S'_t + k_t d_t^T                                gated write
+ *   o_t  = S_t^T (gamma_t * q_t)                           readout gate on the query
+ *
+ * q and k are expected unit-normalised by the caller (the pages normalise
+ * them before the operator); the library does not normalise.
+ *
+ * Training runs the recurrence chunkwise: each chunk of `chunk` tokens is a
+ * triangular system whose cumulative log-decay is split at interval
+ * boundaries so every exponential factor lies in (0, 1] (Methodology;
+ * fig:kernel caption).  Decode is the single-token recurrence.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every tensor pointer is a DEVICE pointer to dense, contiguous memory,
+ *    aligned to 16 bytes.  Inputs and o/dO use the element type `dtype`
+ *    (MUIR_F32 or MUIR_BF16); states, workspaces and gradients are fp32
+ *    (except the workspace, whose content is opaque).
+ *  - Sequence tensors are [B, T, H, D] with D contiguous; states are
+ *    [B, H, dk, dv] row-major (dv contiguous).
+ *  - The caller owns every buffer, including the workspace; the library
+ *    never allocates, frees or synchronises, and keeps no state between
+ *    calls.  Calls are asynchronous on `stream` (a hipStream_t; NULL is the
+ *    default stream).  Calls on different streams with disjoint buffers may
+ *    run concurrently.
+ *  - Outputs must not alias inputs (muir_step's S is updated in place by
+ *    design).
+ *  - Argument errors are detected before any launch and returned as a
+ *    status; nothing is launched then.  A launch failure returns
+ *    MUIR_ERR_HIP.  On error, outputs are undefined.  No C++ exception
+ *    crosses this interface.
+ *  - log_a must be finite and <= 0.  "No decay" is log_a = 0; "full decay"
+ *    is a large negative value (e.g. -1e4), for which exp() is 0.
+ *  - Supported sizes: dk == dv, dk in {64, 128}; chunk in {64, 128, 256};
+ *    T % chunk == 0.  Sizes B, T, H may be 0 (nothing is launched).
+ */
+#ifndef MUIR_H_
+#define MUIR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MUIR_OK = 0,
+  MUIR_ERR_NULL = 1,      /* a required pointer is NULL */
+  MUIR_ERR_SHAPE = 2,     /* unsupported or inconsistent sizes */
+  MUIR_ERR_DTYPE = 3,     /* unknown dtype code */
+  MUIR_ERR_WORKSPACE = 4, /* workspace pointer NULL or smaller than required */
+  MUIR_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned */
+  MUIR_ERR_HIP = 6        /* a kernel launch failed */
+} muir_status_t;
+
+typedef enum { MUIR_F32 = 0, MUIR_BF16 = 1 } muir_dtype_t;
+
+/* Sizes of a chunkwise call. */
+typedef struct {
+  int32_t B, T, H;   /* batch, tokens, heads */
+  int32_t dk, dv;    /* key / value head size */
+  int32_t chunk;     /* tokens per triangular system */
+  int32_t dtype;     /* muir_dtype_t of q, k, v, gates, o, dO */
+} muir_dims_t;
+
+/* Version of this interface (bumped on any signature change). */
+int32_t muir_abi_version(void);
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* muir_status_string(muir_status_t status);
+
+/* Bytes of workspace muir_chunk_fwd needs for `dims` (0 if dims are invalid). */
+size_t muir_chunk_fwd_workspace(const muir_dims_t* dims);
+
+/*
+ * Chunkwise forward over T tokens (Methodology: each chunk is a triangular
+ * system with boundary-split cumulative log-decay).
+ *
+ *   q, k, log_a, erase, gamma : [B, T, H, dk]  dtype
+ *   v, write                  : [B, T, H, dv]  dtype
+ *   S0       : [B, H, dk, dv] fp32 initial state, or NULL for zeros
+ *   o        : [B, T, H, dv]  dtype, output
+ *   S_T      : [B, H, dk, dv] fp32 final state, or NULL to skip
+ *   S_chunks : [B, H, T/chunk, dk, dv] fp32 state at the START of every
+ *              chunk (kept for muir_chunk_bwd), or NULL to skip
+ *   workspace: device scratch of at least muir_chunk_fwd_workspace(dims)
+ *              bytes; contents are clobbered.
+ */
+muir_status_t muir_chunk_fwd(const muir_dims_t* dims,
+                             const void* q, const void* k, const void* v,
+                             const void* log_a, const void* erase,
+                             const void* write, const void* gamma,
+                             const float* S0, void* o, float* S_T, float* S_chunks,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace muir_chunk_bwd needs for `dims` (0 if dims are invalid). */
+size_t muir_chunk_bwd_workspace(const muir_dims_t* dims);
+
+/*
+ * Chunkwise backward: gradients of sum(dO * o) + sum(dS_T * S_T) with
+ * respect to every input of muir_chunk_fwd (the pages state only that a
+ * custom backward pass is used; this is the adjoint of the recurrence above).
+ *
+ *   inputs as in muir_chunk_fwd, plus
+ *   S_chunks : [B, H, T/chunk, dk, dv] fp32 from muir_chunk_fwd, or NULL
+ *              (then recomputed inside, in the workspace)
+ *   dO       : [B, T, H, dv] dtype upstream gradient of o
+ *   dS_T     : [B, H, dk, dv] fp32 upstream gradient of S_T, or NULL for 0
+ *   dq, dk, dlog_a, derase, dgamma : [B, T, H, dk] fp32 outputs
+ *   dv, dwrite                     : [B, T, H, dv] fp32 outputs
+ *   dS0      : [B, H, dk, dv] fp32 output, or NULL to skip
+ */
+muir_status_t muir_chunk_bwd(const muir_dims_t* dims,
+                             const void* q, const void* k, const void* v,
+                             const void* log_a, const void* erase,
+                             const void* write, const void* gamma,
+                             const float* S0, const float* S_chunks,
+                             const void* dO, const float* dS_T,
+                             float* dq, float* dk, float* dv, float* dlog_a,
+                             float* derase, float* dwrite, float* dgamma, float* dS0,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step of the recurrence for N independent streams (abstract:
+ * constant-memory inference; the state stays fp32).
+ *
+ *   q, k, log_a, erase, gamma : [N, H, dk] dtype
+ *   v, write                  : [N, H, dv] dtype
+ *   S : [N, H, dk, dv] fp32, read and updated in place (S_{t-1} -> S_t)
+ *   o : [N, H, dv] dtype, output o_t
+ * Supported sizes: dk in {64, 128}, dv a multiple of 64.
+ */
+muir_status_t muir_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtype,
+                        const void* q, const void* k, const void* v,
+                        const void* log_a, const void* erase,
+                        const void* write, const void* gamma,
+                        float* S, void* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUIR_H_ */

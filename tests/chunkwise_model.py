@@ -46,3 +46,29 @@ def chunkwise_fwd(q, k, v, log_a, erase, write, gamma, S0, C):
                 S = np.exp(L[-1])[:, None] * S + (np.exp(L[-1][None, :] - L) * kk).T @ D
             S_T[b, h] = S
     return o, S_T
+
+
+def chunk_summary(q, k, v, log_a, erase, write, gamma, C):
+    """Per-chunk quantities of the chunkwise form, for one (b, h) sequence
+    given as [T, D] arrays: returns a list of dicts with
+      W = (I+A)^-1 (exp(L) * ek), U~ = (I+A)^-1 (write*v), Q' = exp(L)*qt - P W,
+      O~ = P U~, Kbar = exp(L_C - L) * k, gC = exp(L_C)
+    (test-only; used to inspect the GPU path's intermediate workspace)."""
+    q, k, v, la, er, wr, ga = (np.asarray(x, dtype=np.float64) for x in (q, k, v, log_a, erase, write, gamma))
+    T = q.shape[0]
+    out = []
+    for c0 in range(0, T, C):
+        kk, qq, vv = k[c0:c0 + C], q[c0:c0 + C], v[c0:c0 + C]
+        n = kk.shape[0]
+        L = np.cumsum(la[c0:c0 + C], axis=0)
+        dec = np.exp(L[:, None, :] - L[None, :, :])
+        ek = er[c0:c0 + C] * kk
+        qt = ga[c0:c0 + C] * qq
+        A = np.einsum("rj,ij,rij->ri", ek, kk, dec) * np.tril(np.ones((n, n)), -1)
+        P = np.einsum("rj,ij,rij->ri", qt, kk, dec) * np.tril(np.ones((n, n)), 0)
+        Tm = np.linalg.inv(np.eye(n) + A)
+        W = Tm @ (np.exp(L) * ek)
+        Ut = Tm @ (wr[c0:c0 + C] * vv)
+        out.append(dict(W=W, Ut=Ut, Qp=np.exp(L) * qt - P @ W, Ot=P @ Ut,
+                        Kb=np.exp(L[-1][None, :] - L) * kk, gC=np.exp(L[-1])))
+    return out

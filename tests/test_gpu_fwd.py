@@ -1,0 +1,141 @@
+"""GPU parity of the chunkwise forward and the decode step against the fp64 oracle.
+
+Tolerances (max |gpu - oracle| / max |oracle| per output tensor): 1e-4 for
+fp32 inputs, 2e-2 for bf16 inputs with fp32 state and accumulation.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import muir_inputs
+import oracle
+from gpu_util import NAMES, TOL, oracle_fwd, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import gated_delta_rule_muir_amd as m
+    m.lib()
+    return m
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("dtype,dk", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
+def test_step_matches_oracle(dtype, dk):
+    m = _lib()
+    N, H, steps = 3, 2, 6
+    _say(f"step dtype={dtype} dk={dk}")
+    rates = muir_inputs.step_rates(H, dk, seed=1)
+    S_gpu = torch.zeros((N, H, dk, dk), dtype=torch.float32, device="cuda")
+    S_ref = np.zeros((N, H, dk, dk))
+    for s in range(steps):
+        inp = muir_inputs.step_inputs(N, H, dk, dk, s, rates=rates, dtype=dtype, seed=1)
+        d = to_dev(inp)
+        o = m.muir_step(*(d[n] for n in NAMES), S_gpu)
+        o_ref, S_ref = oracle.step(*(inp[n] for n in NAMES), S_ref)
+        torch.cuda.synchronize()
+        assert rel_err(o, o_ref) <= TOL[dtype], (s, rel_err(o, o_ref))
+    assert rel_err(S_gpu, S_ref) <= TOL[dtype]
+
+
+CASES = [
+    # name, B, T, H, d, C, dtype, decay, S0 scale
+    ("tiny_f32_c64", 1, 256, 2, 64, 64, "f32", "uniform", 0.0),
+    ("f32_d128_c64_S0", 1, 128, 2, 128, 64, "f32", "uniform", 0.1),
+    ("bf16_d128_c64", 2, 256, 2, 128, 64, "bf16", "channel", 0.0),
+    ("bf16_d128_c128_S0", 1, 256, 2, 128, 128, "bf16", "channel_slow", 0.1),
+    ("bf16_d128_c256", 1, 512, 2, 128, 256, "bf16", "channel_slow", 0.0),
+    ("bf16_d64_c64_uniform", 2, 192, 3, 64, 64, "bf16", "uniform", 0.1),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_chunk_fwd_matches_oracle(case):
+    name, B, T, H, d, C, dtype, decay, s0 = case
+    m = _lib()
+    _say(f"chunk_fwd case={name}")
+    inp = muir_inputs.seq_inputs(B, T, H, d, d, dtype=dtype, decay=decay, seed=3, S0_scale=s0)
+    dv = to_dev(inp)
+    o, S_T, S_chunks = m.muir_chunk_fwd(*(dv[n] for n in NAMES), dv["S0"], chunk=C, save_states=True)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_fwd(inp)
+    eo, es = rel_err(o, o_ref), rel_err(S_T, S_ref)
+    _say(f"  err o={eo:.3e} S_T={es:.3e}")
+    assert eo <= TOL[dtype]
+    assert es <= TOL[dtype]
+    # chunk-start states: the state after c*C tokens
+    for c in range(T // C):
+        if c == 0:
+            ref = np.zeros((B, H, d, d)) if inp["S0"] is None else inp["S0"].double().numpy()
+        else:
+            pre = {n: inp[n][:, : c * C] for n in NAMES}
+            pre["S0"] = inp["S0"]
+            ref = oracle_fwd(pre)[1]
+        assert rel_err(S_chunks[:, :, c], ref) <= TOL[dtype] or np.abs(ref).max() == 0
+
+
+def test_chunk_sizes_agree():
+    """C = 64, 128 and 256 give the same result (same triangular systems, grouped differently)."""
+    m = _lib()
+    inp = muir_inputs.seq_inputs(1, 512, 2, 128, 128, dtype="bf16", decay="channel", seed=4)
+    dv = to_dev(inp)
+    outs = [m.muir_chunk_fwd(*(dv[n] for n in NAMES), chunk=C)[0].float() for C in (64, 128, 256)]
+    torch.cuda.synchronize()
+    assert rel_err(outs[1], outs[0]) <= 1e-2
+    assert rel_err(outs[2], outs[0]) <= 1e-2
+
+
+def test_steps_equal_chunk_fwd():
+    """T decode steps reproduce one chunkwise call (the recurrence at chunk size 1)."""
+    m = _lib()
+    B, T, H, d = 2, 64, 2, 128
+    inp = muir_inputs.seq_inputs(B, T, H, d, d, dtype="f32", decay="channel", seed=5)
+    dv = to_dev(inp)
+    o, S_T, _ = m.muir_chunk_fwd(*(dv[n] for n in NAMES), chunk=64)
+    S = torch.zeros((B, H, d, d), dtype=torch.float32, device="cuda")
+    outs = []
+    for t in range(T):
+        outs.append(m.muir_step(*(dv[n][:, t].contiguous() for n in NAMES), S))
+    torch.cuda.synchronize()
+    assert rel_err(torch.stack(outs, 1), o) <= 1e-4
+    assert rel_err(S, S_T) <= 1e-4
+
+
+def test_fwd_summary_intermediates():
+    """The chunk summary in the workspace equals the plain chunkwise quantities
+    (fp32 path, one head): W, U~, Q', O~, Kbar and exp(L_C)."""
+    from chunkwise_model import chunk_summary
+    m = _lib()
+    B, T, H, d, C = 1, 128, 1, 64, 64
+    inp = muir_inputs.seq_inputs(B, T, H, d, d, dtype="f32", decay="uniform", seed=6)
+    dv = to_dev(inp)
+    nbytes = m.muir_chunk_fwd_workspace(B, T, H, d, d, C, m.MUIR_F32)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    m.muir_chunk_fwd(*(dv[n] for n in NAMES), chunk=C, workspace=ws)
+    torch.cuda.synchronize()
+    per = nbytes // (T // C)
+    ref = chunk_summary(*(inp[n][0, :, 0].double().numpy() for n in NAMES), C)
+    for c in range(T // C):
+        blk = ws[c * per:(c + 1) * per].view(torch.float32).cpu().double().numpy()
+        W = blk[: C * d].reshape(C, d)
+        Qp = blk[C * d: 2 * C * d].reshape(C, d)
+        KbT = blk[2 * C * d: 3 * C * d].reshape(d, C)
+        UtT = blk[3 * C * d: 4 * C * d].reshape(d, C)
+        OtT = blk[4 * C * d: 5 * C * d].reshape(d, C)
+        gC = blk[5 * C * d: 5 * C * d + d]
+        r = ref[c]
+        # exp(L_C) of fast channels sits in the fp32 denormal range, where the
+        # device exponential flushes to zero: compare it with an absolute floor.
+        np.testing.assert_allclose(gC, r["gC"], rtol=1e-4, atol=1e-36)
+        for nm, got, want in (("W", W, r["W"]), ("Ut", UtT.T, r["Ut"]), ("Qp", Qp, r["Qp"]),
+                              ("Ot", OtT.T, r["Ot"]), ("Kb", KbT.T, r["Kb"])):
+            e = rel_err(got, want)
+            _say(f"  chunk {c} {nm}: {e:.3e}")
+            assert e <= 1e-4, (c, nm, e)
