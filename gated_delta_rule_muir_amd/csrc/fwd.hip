@@ -57,7 +57,9 @@ struct SummaryView {
   }
 };
 
-template <typename Tin, int DK>
+// BWDL selects the summary layout the backward scan reads: W and Q' as
+// [DK][C] (token-contiguous), Kbar as [C][DK]; U~ and O~ are not written.
+template <typename Tin, int DK, bool BWDL>
 __global__ __launch_bounds__(PREP_THREADS) void fwd_prep_kernel(
     int T, int H, int C, const Tin* __restrict__ q, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ log_a, const Tin* __restrict__ erase,
@@ -162,7 +164,11 @@ __global__ __launch_bounds__(PREP_THREADS) void fwd_prep_kernel(
       sR[j][r] = u;
       sR[DV + j][r] = ek * GL;
       sQh[j][r] = qt * GL;
-      out.KbT[static_cast<size_t>(j) * C + r0 + r] = M::cvt(kj * __expf(sB[NB][j] - L));
+      const TC kb = M::cvt(kj * __expf(sB[NB][j] - L));
+      if (BWDL)
+        out.KbT[static_cast<size_t>(r0 + r) * DK + j] = kb;
+      else
+        out.KbT[static_cast<size_t>(j) * C + r0 + r] = kb;
     }
     __syncthreads();
 
@@ -241,8 +247,17 @@ __global__ __launch_bounds__(PREP_THREADS) void fwd_prep_kernel(
       const f32x4 op = M::mma(pa, M::from_f32(uw), YH[n]);
       UW[n] = uw;
       if (colg < DV) {
-        store4(out.UtT + static_cast<size_t>(colg) * C + r0 + 4 * g, uw);
-        store4(out.OtT + static_cast<size_t>(colg) * C + r0 + 4 * g, op);
+        if (!BWDL) {
+          store4(out.UtT + static_cast<size_t>(colg) * C + r0 + 4 * g, uw);
+          store4(out.OtT + static_cast<size_t>(colg) * C + r0 + 4 * g, op);
+        }
+      } else if (BWDL) {
+        const int j = colg - DV;
+        f32x4 qv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qv[i] = sQh[j][4 * g + i] - op[i];
+        store4(out.W + static_cast<size_t>(j) * C + r0 + 4 * g, uw);
+        store4(out.Qp + static_cast<size_t>(j) * C + r0 + 4 * g, qv);
       } else {
         const int j = colg - DV;
 #pragma unroll
@@ -266,6 +281,7 @@ __global__ __launch_bounds__(PREP_THREADS) void fwd_prep_kernel(
     }
     __syncthreads();
     // ---- W and Q' rows of the block (row layout, 4 elements per store) ----
+    if (!BWDL)
     for (int idx = tid; idx < 16 * DK / 4; idx += PREP_THREADS) {
       const int r = idx / (DK / 4);
       const int j4 = (idx - r * (DK / 4)) * 4;
@@ -410,14 +426,19 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
 
 hipError_t launch_fwd_prep(const ChunkShape& s, const void* q, const void* k, const void* v,
                            const void* log_a, const void* erase, const void* write,
-                           const void* gamma, void* summ, hipStream_t stream) {
+                           const void* gamma, void* summ, bool bwd_layout, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(s.nchunks());
   if (grid == 0) return hipSuccess;
-#define MUIR_PREP(TT, DD)                                                                          \
-  hipLaunchKernelGGL((fwd_prep_kernel<TT, DD>), dim3(grid), dim3(PREP_THREADS), 0, stream, s.T,     \
+#define MUIR_PREP1(TT, DD, BL)                                                                     \
+  hipLaunchKernelGGL((fwd_prep_kernel<TT, DD, BL>), dim3(grid), dim3(PREP_THREADS), 0, stream, s.T, \
                      s.H, s.C, (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a,           \
                      (const TT*)erase, (const TT*)write, (const TT*)gamma, (char*)summ,              \
                      s.summary_bytes())
+#define MUIR_PREP(TT, DD)                 \
+  do {                                    \
+    if (bwd_layout) MUIR_PREP1(TT, DD, true); \
+    else MUIR_PREP1(TT, DD, false);        \
+  } while (0)
   if (s.bf16) {
     if (s.DK == 128) MUIR_PREP(uint16_t, 128);
     else MUIR_PREP(uint16_t, 64);
@@ -426,6 +447,7 @@ hipError_t launch_fwd_prep(const ChunkShape& s, const void* q, const void* k, co
     else MUIR_PREP(float, 64);
   }
 #undef MUIR_PREP
+#undef MUIR_PREP1
   return hipGetLastError();
 }
 

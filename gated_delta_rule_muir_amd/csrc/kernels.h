@@ -30,9 +30,11 @@ hipError_t launch_step(int N, int H, int dk, int dv, bool bf16, const void* q, c
                        const void* gamma, float* S, void* o, hipStream_t stream);
 
 // Chunk-parallel: per chunk summary (W, Q', Kbar, U~, O~, Gamma_C) into `summ`.
+// bwd_layout: W, Q' token-contiguous and Kbar channel-contiguous (what the
+// backward scan reads); U~ and O~ are then not written.
 hipError_t launch_fwd_prep(const ChunkShape& s, const void* q, const void* k, const void* v,
                            const void* log_a, const void* erase, const void* write,
-                           const void* gamma, void* summ, hipStream_t stream);
+                           const void* gamma, void* summ, bool bwd_layout, hipStream_t stream);
 
 // Sequential over chunks: o (may be NULL), S_chunks (may be NULL), S_T (may be NULL).
 hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S0, void* o,
@@ -43,11 +45,13 @@ hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S
 hipError_t launch_bwd_scan(const ChunkShape& s, const void* summ, const void* dO,
                            const float* dS_T, float* dS_chunks, float* dS0, hipStream_t stream);
 
-// Chunk-parallel: all input gradients of every chunk.
+// Chunk-parallel: all input gradients of every chunk.  `scratch` holds
+// 2 * C * DV floats per chunk (the chunk's deltas and their gradients).
 hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, const void* v,
                             const void* log_a, const void* erase, const void* write,
                             const void* gamma, const float* S_chunks, const float* dS_chunks,
                             const void* dO, float* dq, float* dk, float* dv, float* dlog_a,
-                            float* derase, float* dwrite, float* dgamma, hipStream_t stream);
+                            float* derase, float* dwrite, float* dgamma, float* scratch,
+                            hipStream_t stream);
 
 }  // namespace muir

@@ -34,9 +34,13 @@ size_t fwd_ws(const ChunkShape& s) { return s.nchunks() * s.summary_bytes(); }
 
 // Backward workspace: chunk summaries, recomputed chunk states (only used when
 // the caller passes no S_chunks; always reserved so the size does not depend
-// on a pointer), and the chunk-end state gradients.
+// on a pointer), the chunk-end state gradients, and per-chunk scratch for the
+// deltas and their gradients (2 * C * dv fp32).
+size_t bwd_scratch_bytes(const ChunkShape& s) {
+  return static_cast<size_t>(2) * s.C * s.DV * 4;
+}
 size_t bwd_ws(const ChunkShape& s) {
-  return s.nchunks() * s.summary_bytes() + 2 * s.nchunks() * s.state_bytes();
+  return s.nchunks() * (s.summary_bytes() + 2 * s.state_bytes() + bwd_scratch_bytes(s));
 }
 
 muir_status_t need(const void* p) { return p ? MUIR_OK : MUIR_ERR_NULL; }
@@ -104,7 +108,8 @@ muir_status_t muir_chunk_fwd(const muir_dims_t* dims, const void* q, const void*
     }
     return MUIR_OK;
   }
-  if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, workspace, hs) != hipSuccess)
+  if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, workspace, false, hs) !=
+      hipSuccess)
     return MUIR_ERR_HIP;
   if (muir::launch_fwd_scan(s, workspace, S0, o, S_chunks, S_T, hs) != hipSuccess)
     return MUIR_ERR_HIP;
@@ -149,18 +154,23 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void*
   void* summ = ws;
   float* S_rec = reinterpret_cast<float*>(ws + s.nchunks() * s.summary_bytes());
   float* dS_chunks = S_rec + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
-  if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, summ, hs) != hipSuccess)
-    return MUIR_ERR_HIP;
+  float* scratch = dS_chunks + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
   const float* Sc = S_chunks;
   if (!Sc) {
+    // chunk-start states are not given: run the forward summaries and scan first
+    if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, summ, false, hs) !=
+        hipSuccess)
+      return MUIR_ERR_HIP;
     if (muir::launch_fwd_scan(s, summ, S0, nullptr, S_rec, nullptr, hs) != hipSuccess)
       return MUIR_ERR_HIP;
     Sc = S_rec;
   }
+  if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, summ, true, hs) != hipSuccess)
+    return MUIR_ERR_HIP;
   if (muir::launch_bwd_scan(s, summ, dO, dS_T, dS_chunks, dS0, hs) != hipSuccess)
     return MUIR_ERR_HIP;
   if (muir::launch_bwd_chunk(s, q, k, v, log_a, erase, write, gamma, Sc, dS_chunks, dO, dq, dk,
-                             dv, dlog_a, derase, dwrite, dgamma, hs) != hipSuccess)
+                             dv, dlog_a, derase, dwrite, dgamma, scratch, hs) != hipSuccess)
     return MUIR_ERR_HIP;
   return MUIR_OK;
 }
