@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the Muir gated delta-rule operator on one MI355X.
+
+One timed step = one chunkwise forward (saving chunk states) plus one
+chunkwise backward over the headline workload: B=8, T=4096, H=16,
+dk=dv=128, chunk 64, bf16 inputs, fp32 state/gradients, synthetic seeded
+inputs already resident in HBM.  `value` is tokens/s (B*T per step time).
+
+Beside it the line carries:
+  roofline      the dominant kernel's algorithmic bytes per launch over its
+                average duration (HIP events recorded by the library between
+                its own launches, on the launch stream, inside the timed loop)
+  kernels       the same for every kernel of the step
+  cpu_baseline  the fp64 sequential oracle on the host cores, on a bounded
+                sample of the same workload (4 batch rows: 64 heads x 4096)
+  secondary     long-context fwd+bwd (T=32768, chunk 128 and 256) and the
+                streaming decode step (64 streams x 16 heads, 4096 steps)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "fwd+bwd tokens/s & MFMA util, H=16 d=128 T=4K/32K; decode tok/s & HBM GB/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# Algorithmic bytes per token-head of each kernel (d = head size, C = chunk,
+# bf16 inputs of 2 bytes, fp32 states and gradients): the bytes the kernel must
+# read and write by construction -- its inputs and outputs, not its re-reads.
+def kernel_bytes(d: int, C: int, e: int = 2):
+    st = 4 * d * d / C  # one fp32 state per chunk, per token
+    return {
+        "fwd_prep": 7 * d * e + 5 * d * e,              # 7 inputs -> W, Q', Kbar, U~, O~
+        "fwd_scan": 5 * d * e + d * e + st,             # summary -> o, chunk states
+        "bwd_prep": 7 * d * e + 3 * d * e,              # 7 inputs -> W, Q', Kbar
+        "bwd_scan": 3 * d * e + d * e + st,             # summary, dO -> chunk-end state grads
+        "bwd_chunk": 7 * d * e + d * e + 2 * st + 7 * d * 4,  # inputs, dO, S, dS -> 7 fp32 grads
+    }
+
+
+def step_flops(d: int, C: int):
+    """Algorithmic flops per token-head: forward and backward (incl. recompute)."""
+    fwd = 5 * C * d + C * C / 3 + 6 * d * d
+    bwd = 12 * C * d + C * C / 3 + 14 * d * d
+    return fwd, bwd
+
+
+def gen_seq(B, T, H, d, dtype, decay, seed, torch, muir_inputs):
+    inp = muir_inputs.seq_inputs(B, T, H, d, d, dtype=dtype, decay=decay, seed=seed, with_dO=True)
+    return {n: (t.to("cuda") if t is not None else None) for n, t in inp.items()}, inp
+
+
+def time_fwdbwd(m, dv, C, steps, warmup, torch, hiprt, names, profile=True):
+    """Run warmup + timed fwd+bwd steps; returns (ms_per_step, per-kernel avg ms)."""
+    B, T, H, d = dv["q"].shape
+    dev = dv["q"].device
+    fws = torch.empty(m.muir_chunk_fwd_workspace(B, T, H, d, d, C), dtype=torch.uint8, device=dev)
+    bws = torch.empty(m.muir_chunk_bwd_workspace(B, T, H, d, d, C), dtype=torch.uint8, device=dev)
+    args = [dv[n] for n in names]
+
+    def step():
+        o, S_T, Sc = m.muir_chunk_fwd(*args, chunk=C, save_states=True, workspace=fws)
+        g = m.muir_chunk_bwd(*args, dv["dO"], S_chunks=Sc, chunk=C, workspace=bws)
+        return o, g
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    per_step = 3 + 4  # events: fwd (before, prep, scan), bwd (before, prep, bscan, bchunk)
+    pool = hiprt.EventPool(per_step * steps) if profile else None
+    if pool is not None:
+        m.muir_set_profile_events(pool.arr, pool.n)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern = None
+    if pool is not None:
+        rec = m.muir_profile_events_recorded()
+        m.muir_set_profile_events(None)
+        if rec != per_step * steps:
+            raise RuntimeError(f"expected {per_step * steps} profile events, got {rec}")
+        names_k = ["fwd_prep", "fwd_scan", None, "bwd_prep", "bwd_scan", "bwd_chunk"]
+        acc = {k: 0.0 for k in names_k if k}
+        for s in range(steps):
+            base = s * per_step
+            for i, kn in enumerate(names_k):
+                if kn is None:
+                    continue
+                acc[kn] += pool.elapsed_ms(base + i, base + i + 1)
+        kern = {k: v / steps for k, v in acc.items()}
+        pool.close()
+    return (t1 - t0) * 1e3 / steps, kern
+
+
+def cpu_baseline(inp_cpu, names, torch):
+    """The oracle (fwd + bwd) on a bounded sample of the workload (the first
+    `rows` batch rows, all heads, full length), all host cores."""
+    import oracle
+    rows = 4
+    sl = {n: (inp_cpu[n][:rows] if inp_cpu[n] is not None else None) for n in list(names) + ["dO"]}
+    B, T, H, d = sl["q"].shape
+    nproc = os.cpu_count() or 1
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except Exception:
+        pass
+    threads = min(nproc, B * H)
+    args = [sl[n].float().numpy() for n in names]
+    dO = sl["dO"].float().numpy()
+    t0 = time.perf_counter()
+    oracle.fwd(*args, nthreads=threads)
+    oracle.bwd(*args, dO, nthreads=threads)
+    t = time.perf_counter() - t0
+    return {"value": B * T / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fwd+bwd of batch rows 0..{B - 1} of the workload (B={B}, T={T}, H={H}, d={d}), fp64, "
+                      f"{t:.2f} s wall on {threads} threads"}
+
+
+def decode_bench(m, torch, hiprt, N=64, H=16, d=128, steps=4096, seed=0):
+    """Streaming decode: `steps` consecutive muir_step calls on an fp32 state."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    dev = "cuda"
+
+    def unit(x):
+        s = torch.nn.functional.silu(x)
+        return s / s.norm(dim=-1, keepdim=True).clamp_min(1e-12)
+
+    bf = torch.bfloat16
+    shp = (steps, N, H, d)
+    q = unit(torch.randn(shp, generator=g, device=dev)).to(bf)
+    k = unit(torch.randn(shp, generator=g, device=dev)).to(bf)
+    v = torch.randn(shp, generator=g, device=dev).to(bf)
+    rates = torch.exp(torch.empty((H, d), device=dev).uniform_(-9.2103, 1.0986, generator=g))
+    log_a = (-rates).to(bf).expand(N, H, d).contiguous()
+    erase = torch.sigmoid(torch.randn(shp, generator=g, device=dev)).to(bf)
+    write = torch.sigmoid(torch.randn(shp, generator=g, device=dev)).to(bf)
+    gamma = (2 * torch.sigmoid(torch.randn(shp, generator=g, device=dev))).to(bf)
+    S = torch.zeros((N, H, d, d), dtype=torch.float32, device=dev)
+    o = torch.empty((N, H, d), dtype=bf, device=dev)
+    for t in range(8):  # warmup
+        m.muir_step(q[t], k[t], v[t], log_a, erase[t], write[t], gamma[t], S, out=o)
+    S.zero_()
+    torch.cuda.synchronize()
+    pool = hiprt.EventPool(2 * steps)
+    m.muir_set_profile_events(pool.arr, pool.n)
+    t0 = time.perf_counter()
+    for t in range(steps):
+        m.muir_step(q[t], k[t], v[t], log_a, erase[t], write[t], gamma[t], S, out=o)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    m.muir_set_profile_events(None)
+    kt = sum(pool.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps)) / steps
+    pool.close()
+    wall = (t1 - t0) * 1e3 / steps
+    state_bytes = 2 * N * H * d * d * 4
+    in_bytes = N * H * d * 2 * 7 + N * H * d * 2
+    del q, k, v, erase, write, gamma
+    torch.cuda.empty_cache()
+    return {"workload": f"decode N={N} H={H} d={d} fp32 state, {steps} steps",
+            "tokens_per_s": N / (wall * 1e-3), "wall_us_per_step": wall * 1e3,
+            "kernel_us_per_step": kt * 1e3,
+            "hbm_GBs_at_kernel_time": (state_bytes + in_bytes) / (kt * 1e-3) / 1e9,
+            "bytes_per_step": state_bytes + in_bytes,
+            "note": "state (%d MiB) may be served partly from the 256 MB Infinity Cache" % (N * H * d * d * 4 >> 20)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=4096)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the operator runs on one MI355X); --gpus {args.gpus} "
+              "is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import muir_inputs
+    import gated_delta_rule_muir_amd as m
+    from gated_delta_rule_muir_amd import hiprt
+    m.lib()  # fails loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    names = ("q", "k", "v", "log_a", "erase", "write", "gamma")
+
+    wl = muir_inputs.WORKLOADS["layer_fwdbwd_4k"]
+    B, T, H, d, C = wl.B, wl.T, wl.H, wl.dk, wl.chunk
+    log(f"[bench] generating {wl.name} inputs B={B} T={T} H={H} d={d} C={C} {wl.dtype}")
+    dv, inp_cpu = gen_seq(B, T, H, d, wl.dtype, wl.decay, 0, torch, muir_inputs)
+    log(f"[bench] timing fwd+bwd: warmup={args.warmup} steps={args.steps}")
+    ms, kern = time_fwdbwd(m, dv, C, args.steps, args.warmup, torch, hiprt, names)
+    ntok = B * T
+    nth = B * T * H
+    log(f"[bench] {ms:.3f} ms/step -> {ntok / (ms * 1e-3):.4g} tokens/s")
+
+    kb = kernel_bytes(d, C)
+    kernels = {}
+    for kn, t in kern.items():
+        byt = kb[kn] * nth
+        kernels[kn] = {"avg_us": t * 1e3, "alg_bytes": byt, "GBs": byt / (t * 1e-3) / 1e9,
+                       "hbm_frac": byt / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    dom = max(kern, key=lambda k: kern[k])
+    fwd_f, bwd_f = step_flops(d, C)
+    step_bytes = (kb["fwd_prep"] + kb["fwd_scan"] + kb["bwd_prep"] + kb["bwd_scan"] + kb["bwd_chunk"]) * nth
+    traffic = None
+    roof = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GBs"], "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": kernels[dom]["GBs"] / HBM_PEAK_GBS, "traffic": traffic,
+            "alg_bytes_per_launch": kb[dom] * nth, "avg_launch_us": kernels[dom]["avg_us"]}
+    result = {
+        "metric": METRIC, "value": ntok / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "T": T, "H": H, "dk": d, "dv": d, "chunk": C,
+                   "inputs": "bf16, seeded (muir_inputs), per-channel decay rates 1e-4..3",
+                   "step": "muir_chunk_fwd (saving chunk states) + muir_chunk_bwd"},
+        "roofline": roof,
+        "kernels": kernels,
+        "step_model": {"alg_bytes": step_bytes, "alg_GBs": step_bytes / (ms * 1e-3) / 1e9,
+                       "alg_flops": (fwd_f + bwd_f) * nth,
+                       "mfma_util_alg": (fwd_f + bwd_f) * nth / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) on one batch row ...")
+        result["cpu_baseline"] = cpu_baseline(inp_cpu, names, torch)
+        log(f"[bench] cpu baseline {result['cpu_baseline']['value']:.4g} tokens/s")
+    del inp_cpu
+    if not args.no_secondary:
+        sec = {}
+        del dv
+        torch.cuda.empty_cache()
+        for name in ("long_32k_c128", "long_32k_c256"):
+            w = muir_inputs.WORKLOADS[name]
+            log(f"[bench] secondary {name}")
+            dv2, _ = gen_seq(w.B, w.T, w.H, w.dk, w.dtype, w.decay, 0, torch, muir_inputs)
+            ms2, k2 = time_fwdbwd(m, dv2, w.chunk, 5, 2, torch, hiprt, names)
+            fwd_f2, bwd_f2 = step_flops(w.dk, w.chunk)
+            nth2 = w.B * w.T * w.H
+            sec[name] = {"tokens_per_s": w.B * w.T / (ms2 * 1e-3), "ms_per_step": ms2,
+                         "kernels_us": {k: v * 1e3 for k, v in k2.items()},
+                         "mfma_util_alg": (fwd_f2 + bwd_f2) * nth2 / (ms2 * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)}
+            log(f"[bench]   {sec[name]['tokens_per_s']:.4g} tokens/s")
+            del dv2
+            torch.cuda.empty_cache()
+        log(f"[bench] secondary decode ({args.decode_steps} steps)")
+        sec["decode_64x16"] = decode_bench(m, torch, hiprt, steps=args.decode_steps)
+        log(f"[bench]   {sec['decode_64x16']['kernel_us_per_step']:.2f} us/step kernel")
+        result["secondary"] = sec
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

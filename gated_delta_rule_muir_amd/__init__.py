@@ -20,7 +20,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["muir_chunk_fwd", "muir_chunk_bwd", "muir_step", "muir_chunk_fwd_workspace",
-           "muir_chunk_bwd_workspace", "lib", "library_path", "MuirError", "STATUS"]
+           "muir_chunk_bwd_workspace", "muir_set_profile_events", "muir_profile_events_recorded",
+           "lib", "library_path", "MuirError", "STATUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libmuir.so")
@@ -72,6 +73,9 @@ def lib():
         L.muir_chunk_bwd.restype = ctypes.c_int
         L.muir_step.argtypes = [I32] * 5 + [P] * 7 + [P, P, P]
         L.muir_step.restype = ctypes.c_int
+        L.muir_set_profile_events.argtypes = [P, I32]
+        L.muir_set_profile_events.restype = I32
+        L.muir_profile_events_recorded.restype = I32
         _lib = L
     return _lib
 
@@ -217,3 +221,15 @@ def muir_step(q, k, v, log_a, erase, write, gamma, S, *, out=None) -> torch.Tens
     if rc != 0:
         raise MuirError(rc, "muir_step")
     return o
+
+
+def muir_set_profile_events(events=None, count: int = 0) -> None:
+    """Register a ctypes array of hipEvent_t handles for per-kernel timing
+    (see include/muir.h); ``None`` turns it off."""
+    rc = lib().muir_set_profile_events(events, int(count) if events is not None else 0)
+    if rc != 0:
+        raise MuirError(rc, "muir_set_profile_events")
+
+
+def muir_profile_events_recorded() -> int:
+    return int(lib().muir_profile_events_recorded())

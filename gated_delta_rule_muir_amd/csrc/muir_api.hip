@@ -43,13 +43,33 @@ size_t bwd_ws(const ChunkShape& s) {
   return s.nchunks() * (s.summary_bytes() + 2 * s.state_bytes() + bwd_scratch_bytes(s));
 }
 
-muir_status_t need(const void* p) { return p ? MUIR_OK : MUIR_ERR_NULL; }
+// Optional per-kernel timing: when the caller registers an array of HIP
+// events, each entry point records the next event before its first kernel
+// and after every kernel it launches, on the caller's stream, until the array
+// is used up.  No work is skipped or reordered.
+thread_local hipEvent_t* g_events = nullptr;
+thread_local int g_nevents = 0;
+thread_local int g_cursor = 0;
+
+inline void mark(hipStream_t s) {
+  if (g_events && g_cursor < g_nevents) hipEventRecord(g_events[g_cursor++], s);
+}
 
 }  // namespace
 
 extern "C" {
 
 int32_t muir_abi_version(void) { return 1; }
+
+int32_t muir_set_profile_events(void** events, int32_t count) {
+  if (count < 0 || (count > 0 && !events)) return MUIR_ERR_NULL;
+  g_events = reinterpret_cast<hipEvent_t*>(events);
+  g_nevents = events ? count : 0;
+  g_cursor = 0;
+  return MUIR_OK;
+}
+
+int32_t muir_profile_events_recorded(void) { return g_cursor; }
 
 const char* muir_status_string(muir_status_t st) {
   switch (st) {
@@ -108,11 +128,14 @@ muir_status_t muir_chunk_fwd(const muir_dims_t* dims, const void* q, const void*
     }
     return MUIR_OK;
   }
+  mark(hs);
   if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, workspace, false, hs) !=
       hipSuccess)
     return MUIR_ERR_HIP;
+  mark(hs);
   if (muir::launch_fwd_scan(s, workspace, S0, o, S_chunks, S_T, hs) != hipSuccess)
     return MUIR_ERR_HIP;
+  mark(hs);
   return MUIR_OK;
 }
 
@@ -156,22 +179,28 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void*
   float* dS_chunks = S_rec + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
   float* scratch = dS_chunks + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
   const float* Sc = S_chunks;
+  mark(hs);
   if (!Sc) {
     // chunk-start states are not given: run the forward summaries and scan first
     if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, summ, false, hs) !=
         hipSuccess)
       return MUIR_ERR_HIP;
+    mark(hs);
     if (muir::launch_fwd_scan(s, summ, S0, nullptr, S_rec, nullptr, hs) != hipSuccess)
       return MUIR_ERR_HIP;
+    mark(hs);
     Sc = S_rec;
   }
   if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, summ, true, hs) != hipSuccess)
     return MUIR_ERR_HIP;
+  mark(hs);
   if (muir::launch_bwd_scan(s, summ, dO, dS_T, dS_chunks, dS0, hs) != hipSuccess)
     return MUIR_ERR_HIP;
+  mark(hs);
   if (muir::launch_bwd_chunk(s, q, k, v, log_a, erase, write, gamma, Sc, dS_chunks, dO, dq, dk,
                              dv, dlog_a, derase, dwrite, dgamma, scratch, hs) != hipSuccess)
     return MUIR_ERR_HIP;
+  mark(hs);
   return MUIR_OK;
 }
 
@@ -189,9 +218,12 @@ muir_status_t muir_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dt
     if (!p) return MUIR_ERR_NULL;
   for (const void* p : req)
     if (!aligned16(p)) return MUIR_ERR_ALIGN;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  mark(hs);
   if (muir::launch_step(N, H, dk, dv, dtype == MUIR_BF16, q, k, v, log_a, erase, write, gamma, S,
-                        o, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+                        o, hs) != hipSuccess)
     return MUIR_ERR_HIP;
+  mark(hs);
   return MUIR_OK;
 }
 

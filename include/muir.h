@@ -78,6 +78,20 @@ typedef struct {
 /* Version of this interface (bumped on any signature change). */
 int32_t muir_abi_version(void);
 
+/*
+ * Per-kernel timing for profilers and benchmarks.  `events` points to
+ * `count` hipEvent_t handles created by the caller (hipEventCreate).  After
+ * registration, each entry point records the next unused event on its
+ * stream before its first kernel and after each kernel it launches, until
+ * all `count` events are used.  Registering (NULL, 0) turns this off.  The
+ * registration is per host thread; the events stay owned by the caller.
+ * Returns MUIR_OK, or MUIR_ERR_NULL for (NULL, count > 0).
+ */
+int32_t muir_set_profile_events(void** events, int32_t count);
+
+/* Events recorded since the last muir_set_profile_events on this thread. */
+int32_t muir_profile_events_recorded(void);
+
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* muir_status_string(muir_status_t status);
 
