@@ -30,14 +30,13 @@
 // Kernel 2 (fwd_scan) walks the chunks of one (b, h) in order; each wave owns
 // 16 value columns of S (fp32, held in MFMA accumulators) and applies the
 // three products above per chunk.
+#include "chunk_common.h"
 #include "kernels.h"
 #include "mma.h"
 
 namespace muir {
 
 namespace {
-
-constexpr int PREP_THREADS = 256;
 
 template <typename TC>
 struct SummaryView {
@@ -59,9 +58,13 @@ struct SummaryView {
 
 // BWDL selects the summary layout the backward scan reads: W and Q' as
 // [DK][C] (token-contiguous), Kbar as [C][DK]; U~ and O~ are not written.
-template <typename Tin, int DK, bool BWDL>
-__global__ __launch_bounds__(PREP_THREADS) void fwd_prep_kernel(
-    int T, int H, int C, const Tin* __restrict__ q, const Tin* __restrict__ k,
+//
+// Work split: NW = (DK + DV) / 32 waves; wave w owns columns [32w, 32w + 32)
+// of the inner state [U~ | W].  For the elementwise work each thread owns one
+// key channel and 4 consecutive tokens of the current block.
+template <typename Tin, int DK, int C, bool BWDL>
+__global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
+    int T, int H, const Tin* __restrict__ q, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ log_a, const Tin* __restrict__ erase,
     const Tin* __restrict__ write, const Tin* __restrict__ gamma, char* __restrict__ summ,
     size_t summ_bytes) {
@@ -69,15 +72,17 @@ __global__ __launch_bounds__(PREP_THREADS) void fwd_prep_kernel(
   typedef MM<TC> M;
   typedef typename M::frag frag;
   constexpr int DV = DK;
-  constexpr int NH = DV + DK;   // columns of the inner state: [U~ | W]
-  constexpr int CW = NH / 4;    // columns per wave
-  constexpr int NT = CW / 16;   // column tiles per wave
-  constexpr int RT = DK / 16;   // row tiles of the inner state
-  constexpr int PAD = DK + 1;   // fp32 row stride of the [16][DK] leaf tiles
-  constexpr int PT = DK + 4;    // row stride of the [16][DK] operand tiles
+  constexpr int NH = DV + DK;    // columns of the inner state: [U~ | W]
+  constexpr int NW = NH / 32;    // waves
+  constexpr int NTH = 64 * NW;
+  constexpr int NT = 2;          // column tiles per wave
+  constexpr int RT = DK / 16;    // row tiles of the inner state
+  constexpr int TPC = NTH / DK;  // threads per key channel in the elementwise phase
+  constexpr int NB = C / 16;     // 16-token blocks per chunk
+  constexpr int PT = DK + 4;     // row stride of [16][DK] operand tiles
+  static_assert(TPC == 4, "each thread owns 4 tokens of a block");
 
   const int NC = T / C;
-  const int NB = C / 16;
   const int chunk = blockIdx.x;
   const int bh = chunk / NC;
   const int c = chunk - bh * NC;
@@ -88,133 +93,144 @@ __global__ __launch_bounds__(PREP_THREADS) void fwd_prep_kernel(
   const int wave = tid >> 6;
   const int g = lane >> 4;
   const int c16 = lane & 15;
+  const int ej = tid % DK;       // elementwise: key channel
+  const int part = tid / DK;     // elementwise: tokens 4*part .. 4*part+3 of the block
 
   SummaryView<TC> out(summ + static_cast<size_t>(chunk) * summ_bytes, C, DK, DV);
-  // element (t, j) of a [B, T, H, D] tensor for chunk-local token t
   const size_t rowbase = (static_cast<size_t>(b) * T + static_cast<size_t>(c) * C) * H + h;
   auto gidx = [&](int t, int j) -> size_t { return (rowbase + static_cast<size_t>(t) * H) * DK + j; };
 
-  __shared__ __attribute__((aligned(16))) float sB[17][DK];          // block-boundary cumulative log-decay B_0..B_NB
-  __shared__ float sL[16][PAD];         // Lam of the block's tokens
-  __shared__ float sBK[16][PAD];        // ek
-  __shared__ float sQT[16][PAD];        // qt
-  __shared__ float sK[16][PAD];         // k
-  __shared__ __attribute__((aligned(16))) TC sX[16][PT];             // X rows (operand)
-  __shared__ __attribute__((aligned(16))) TC sY[16][PT];             // Y rows (operand)
-  __shared__ __attribute__((aligned(16))) TC sKe[DK][20];            // Ke^T (operand, rows = key channels)
-  __shared__ float sR[NH][16];          // [U | K~]^T of the block
-  __shared__ float sQh[DK][16];         // Q^^T of the block (exp(Lam) * qt)
-  __shared__ float sWa[16][17];         // A_II, then powers of A_II
-  __shared__ float sWt[16][17];         // running Neumann product
-  __shared__ __attribute__((aligned(16))) TC sT[16][20];             // T_II (operand)
-  __shared__ __attribute__((aligned(16))) TC sP[16][20];             // P_II (operand)
-  __shared__ float sG[DK];              // exp(B_{I+1} - B_I)
-  __shared__ __attribute__((aligned(16))) TC sStage[16][2 * DK + 8]; // W and Q' rows of the block, for row-layout stores
+  __shared__ float sB[NB + 1][DK];     // B_I = Lam at the end of block I-1 (B_0 = 0)
+  __shared__ float sBsum[NB][DK];      // sum of log_a over block I  (= B_{I+1} - B_I)
+  __shared__ float sBsuf[NB][DK];      // sum of log_a over blocks >= I  (= B_NB - B_I)
+  __shared__ float sTmp[TPC][DK];
+  __shared__ float sL[16][DK + 1];     // log_a of the block's tokens (per-pair fallback)
+  __shared__ __attribute__((aligned(16))) TC sX[16][PT];   // ek * exp(Lam - B_I)
+  __shared__ __attribute__((aligned(16))) TC sY[16][PT];   // qt * exp(Lam - B_I)
+  __shared__ __attribute__((aligned(16))) TC sZ[16][PT];   // k * exp(B_I - Lam)   (leaf only)
+  __shared__ __attribute__((aligned(16))) TC sKe[DK][20];  // (k * exp(B_{I+1} - Lam))^T
+  __shared__ __attribute__((aligned(16))) TC sR[NH][20];   // [U | K~]^T
+  __shared__ __attribute__((aligned(16))) TC sQh[DK][20];  // (qt * exp(Lam))^T
+  __shared__ float sAw[16][17];
+  __shared__ float sPw[16][17];
+  __shared__ float sTw[16][17];
+  __shared__ float sPf[16][17];
+  __shared__ __attribute__((aligned(16))) TC sT[16][20];
+  __shared__ __attribute__((aligned(16))) TC sP[16][20];
+  __shared__ float sG[DK];
+  __shared__ __attribute__((aligned(16))) TC sStage[BWDL ? 1 : 16][2 * DK + 8];
 
-  // ---- boundaries of the cumulative log-decay, and exp(Lam_C) ----
-  if (tid < DK) {
-    float L = 0.f;
-    sB[0][tid] = 0.f;
-    for (int t = 0; t < C; ++t) {
-      L += Elem<Tin>::load(log_a, gidx(t, tid));
-      if ((t & 15) == 15) sB[(t >> 4) + 1][tid] = L;
-    }
-    out.gC[tid] = __expf(L);
+  // ---- block sums of the log-decay and their prefix/suffix sums ----
+#pragma unroll
+  for (int I = part; I < NB; I += TPC) {
+    float sacc = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) sacc += Elem<Tin>::load(log_a, gidx(16 * I + rr, ej));
+    sBsum[I][ej] = sacc;
   }
+  __syncthreads();
+  if (tid < DK) {
+    float acc = 0.f;
+    sB[0][tid] = 0.f;
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      acc += sBsum[I][tid];
+      sB[I + 1][tid] = acc;
+    }
+    float suf = 0.f;
+#pragma unroll
+    for (int I = NB - 1; I >= 0; --I) {
+      suf += sBsum[I][tid];
+      sBsuf[I][tid] = suf;
+    }
+    out.gC[tid] = __expf(acc);
+  }
+  __syncthreads();
 
   f32x4 Hs[RT][NT];
 #pragma unroll
   for (int s = 0; s < RT; ++s)
 #pragma unroll
     for (int n = 0; n < NT; ++n) Hs[s][n] = zero4();
-  __syncthreads();
 
+#pragma unroll 1
   for (int I = 0; I < NB; ++I) {
     const int r0 = 16 * I;
-    // ---- within-block cumulative log-decay ----
-    if (tid < DK) {
-      float L = sB[I][tid];
-#pragma unroll 4
-      for (int r = 0; r < 16; ++r) {
-        L += Elem<Tin>::load(log_a, gidx(r0 + r, tid));
-        sL[r][tid] = L;
-      }
-      sG[tid] = __expf(sB[I + 1][tid] - sB[I][tid]);
-    }
-    __syncthreads();
-
-    // ---- elementwise operand tiles ----
-    for (int idx = tid; idx < 16 * DK; idx += PREP_THREADS) {
-      const int r = idx / DK;
-      const int j = idx - r * DK;
-      const size_t gi = gidx(r0 + r, j);
-      const float kj = Elem<Tin>::load(k, gi);
-      const float ek = Elem<Tin>::load(erase, gi) * kj;
-      const float qt = Elem<Tin>::load(gamma, gi) * Elem<Tin>::load(q, gi);
-      const float u = Elem<Tin>::load(write, gi) * Elem<Tin>::load(v, gi);
-      const float L = sL[r][j];
-      const float fs = __expf(L - sB[I][j]);   // exp(Lam_r - B_I) in (0, 1]
-      const float GL = __expf(L);              // exp(Lam_r) in (0, 1]
-      sBK[r][j] = ek;
-      sQT[r][j] = qt;
-      sK[r][j] = kj;
-      sX[r][j] = M::cvt(ek * fs);
-      sY[r][j] = M::cvt(qt * fs);
-      sKe[j][r] = M::cvt(kj * __expf(sB[I + 1][j] - L));
-      sR[j][r] = u;
-      sR[DV + j][r] = ek * GL;
-      sQh[j][r] = qt * GL;
-      const TC kb = M::cvt(kj * __expf(sB[NB][j] - L));
-      if (BWDL)
-        out.KbT[static_cast<size_t>(r0 + r) * DK + j] = kb;
-      else
-        out.KbT[static_cast<size_t>(j) * C + r0 + r] = kb;
-    }
-    __syncthreads();
-
-    // ---- leaf block: A_II (strictly lower), P_II (lower), start of the Neumann product ----
-    {
-      const int r = tid >> 4;
-      const int i = tid & 15;
-      float a = 0.f, p = 0.f;
-      if (i <= r) {
-        for (int j = 0; j < DK; ++j) {
-          const float kk = sK[i][j] * __expf(sL[r][j] - sL[i][j]);
-          a += sBK[r][j] * kk;
-          p += sQT[r][j] * kk;
-        }
-      }
-      if (i >= r) a = 0.f;
-      sP[r][i] = M::cvt(p);
-      sWa[r][i] = a;
-      sWt[r][i] = (r == i ? 1.f : 0.f) - a;
-    }
-    __syncthreads();
-    // T_II = (I - A)(I + A^2)(I + A^4)(I + A^8)
-    {
-      const int r = tid >> 4;
-      const int cc = tid & 15;
-#pragma unroll 1
-      for (int step = 0; step < 3; ++step) {
-        float sq = 0.f;
+    // ---- elementwise: 4 tokens of channel ej ----
+    float kv[4], ev[4], qv[4], gv[4], vv[4], wv[4], lv[4];
 #pragma unroll
-        for (int x = 0; x < 16; ++x) sq += sWa[r][x] * sWa[x][cc];
-        __syncthreads();
-        sWa[r][cc] = sq;
-        __syncthreads();
-        float t2 = sWt[r][cc];
+    for (int rr = 0; rr < 4; ++rr) {
+      const size_t gi = gidx(r0 + 4 * part + rr, ej);
+      kv[rr] = Elem<Tin>::load(k, gi);
+      ev[rr] = Elem<Tin>::load(erase, gi);
+      qv[rr] = Elem<Tin>::load(q, gi);
+      gv[rr] = Elem<Tin>::load(gamma, gi);
+      vv[rr] = Elem<Tin>::load(v, gi);
+      wv[rr] = Elem<Tin>::load(write, gi);
+      lv[rr] = Elem<Tin>::load(log_a, gi);
+    }
+    // direct partial sums (never differences of cumulative sums): prefix of
+    // the block up to and including each token, and suffix after it
+    float cs[4], sf[4];
+    {
+      float run = 0.f;
 #pragma unroll
-        for (int x = 0; x < 16; ++x) t2 += sWt[r][x] * sWa[x][cc];
-        __syncthreads();
-        sWt[r][cc] = t2;
-        __syncthreads();
+      for (int rr = 0; rr < 4; ++rr) {
+        run += lv[rr];
+        cs[rr] = run;
       }
-      sT[r][cc] = M::cvt(sWt[r][cc]);
+      sTmp[part][ej] = run;
+      sf[3] = 0.f;
+      sf[2] = lv[3];
+      sf[1] = lv[3] + lv[2];
+      sf[0] = lv[3] + lv[2] + lv[1];
+    }
+    const float BI = sB[I][ej];
+    const float bsum = sBsum[I][ej];
+    const float bsuf1 = I + 1 < NB ? sBsuf[I + 1][ej] : 0.f;
+    const int safe = __syncthreads_and(-bsum <= LEAF_SAFE_RANGE);
+    float excl = 0.f, exsuf = 0.f;
+    for (int p = 0; p < TPC; ++p) {
+      if (p < part) excl += sTmp[p][ej];
+      if (p > part) exsuf += sTmp[p][ej];
+    }
+    if (part == 0) sG[ej] = __expf(bsum);
+    f32x4 keT, uT, ktT, qhT, kbT;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = 4 * part + rr;
+      const float loc = excl + cs[rr];         // Lam_r - B_I        (<= 0)
+      const float suf = sf[rr] + exsuf;        // B_{I+1} - Lam_r    (<= 0)
+      const float fs = __expf(loc);            // exp(Lam_r - B_I)
+      const float GL = __expf(BI + loc);       // exp(Lam_r)
+      const float fe = __expf(suf);            // exp(B_{I+1} - Lam_r)
+      const float kb = __expf(suf + bsuf1);    // exp(Lam_C - Lam_r)
+      const float ek = ev[rr] * kv[rr];
+      const float qt = gv[rr] * qv[rr];
+      sL[r][ej] = lv[rr];
+      sX[r][ej] = M::cvt(ek * fs);
+      sY[r][ej] = M::cvt(qt * fs);
+      sZ[r][ej] = M::cvt(safe ? kv[rr] * __expf(-loc) : 0.f);
+      keT[rr] = kv[rr] * fe;
+      uT[rr] = wv[rr] * vv[rr];
+      ktT[rr] = ek * GL;
+      qhT[rr] = qt * GL;
+      kbT[rr] = kv[rr] * kb;
+    }
+    store4(&sKe[ej][4 * part], keT);
+    store4(&sR[ej][4 * part], uT);
+    store4(&sR[DV + ej][4 * part], ktT);
+    store4(&sQh[ej][4 * part], qhT);
+    if (BWDL) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        out.KbT[static_cast<size_t>(r0 + 4 * part + rr) * DK + ej] = M::cvt(kbT[rr]);
+    } else {
+      store4(out.KbT + static_cast<size_t>(ej) * C + r0 + 4 * part, kbT);
     }
     __syncthreads();
 
-    // ---- per-wave products over this wave's columns of [U~ | W] ----
-    const int col0 = wave * CW;
+    // ---- X H and Y H for this wave's columns ----
     f32x4 XH[NT], YH[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
@@ -234,15 +250,62 @@ __global__ __launch_bounds__(PREP_THREADS) void fwd_prep_kernel(
         }
       }
     }
+    // ---- leaf: A_II, P_II, T_II ----
+    if (safe) {
+      if (wave == 0) {
+        f32x4 a = zero4(), p = zero4();
+#pragma unroll
+        for (int s = 0; s < RT; ++s) {
+          const frag zb = M::load(&sZ[c16][16 * s + 4 * g]);
+          a = M::mma(M::load(&sX[c16][16 * s + 4 * g]), zb, a);
+          p = M::mma(M::load(&sY[c16][16 * s + 4 * g]), zb, p);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g + i;
+          sAw[r][c16] = c16 < r ? a[i] : 0.f;
+          sPf[r][c16] = c16 <= r ? p[i] : 0.f;
+        }
+      }
+    } else {
+      // per-pair factors exp(Lam_r - Lam_i) = exp(sum of log_a over (i, r]) in (0, 1]
+      for (int pr = tid; pr < 256; pr += NTH) {
+        const int r = pr >> 4;
+        const int i = pr & 15;
+        float a = 0.f, p = 0.f;
+        if (i <= r) {
+          for (int j = 0; j < DK; ++j) {
+            const size_t gr = gidx(r0 + r, j), gq = gidx(r0 + i, j);
+            float ls = 0.f;
+            for (int x = i + 1; x <= r; ++x) ls += sL[x][j];
+            const float kk = Elem<Tin>::load(k, gq) * __expf(ls);
+            a += Elem<Tin>::load(erase, gr) * Elem<Tin>::load(k, gr) * kk;
+            p += Elem<Tin>::load(gamma, gr) * Elem<Tin>::load(q, gr) * kk;
+          }
+        }
+        sAw[r][i] = i < r ? a : 0.f;
+        sPf[r][i] = p;
+      }
+      __syncthreads();
+    }
+    if (wave == 0) {
+      const f32x4 t = neumann16(sAw, sPw, sTw);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sT[4 * g + i][c16] = M::cvt(t[i]);
+        sP[4 * g + i][c16] = M::cvt(sPf[4 * g + i][c16]);
+      }
+    }
+    __syncthreads();
+
+    // ---- [U~|W]_I = T_II (R_I - X_I H_I);  [O~|PW]_I = Y_I H_I + P_II [U~|W]_I ----
     const frag ta = M::load(&sT[c16][4 * g]);
     const frag pa = M::load(&sP[c16][4 * g]);
     f32x4 UW[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      const int colg = col0 + 16 * n + c16;
-      f32x4 rhs;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rhs[i] = sR[colg][4 * g + i] - XH[n][i];
+      const int colg = wave * 32 + 16 * n + c16;
+      const f32x4 rhs = load4(&sR[colg][4 * g]) - XH[n];
       const f32x4 uw = M::mma(ta, M::from_f32(rhs), zero4());
       const f32x4 op = M::mma(pa, M::from_f32(uw), YH[n]);
       UW[n] = uw;
@@ -251,19 +314,18 @@ __global__ __launch_bounds__(PREP_THREADS) void fwd_prep_kernel(
           store4(out.UtT + static_cast<size_t>(colg) * C + r0 + 4 * g, uw);
           store4(out.OtT + static_cast<size_t>(colg) * C + r0 + 4 * g, op);
         }
-      } else if (BWDL) {
-        const int j = colg - DV;
-        f32x4 qv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) qv[i] = sQh[j][4 * g + i] - op[i];
-        store4(out.W + static_cast<size_t>(j) * C + r0 + 4 * g, uw);
-        store4(out.Qp + static_cast<size_t>(j) * C + r0 + 4 * g, qv);
       } else {
         const int j = colg - DV;
+        const f32x4 qv = load4(&sQh[j][4 * g]) - op;
+        if (BWDL) {
+          store4(out.W + static_cast<size_t>(j) * C + r0 + 4 * g, uw);
+          store4(out.Qp + static_cast<size_t>(j) * C + r0 + 4 * g, qv);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sStage[4 * g + i][j] = M::cvt(uw[i]);
-          sStage[4 * g + i][DK + j] = M::cvt(sQh[j][4 * g + i] - op[i]);
+          for (int i = 0; i < 4; ++i) {
+            sStage[4 * g + i][j] = M::cvt(uw[i]);
+            sStage[4 * g + i][DK + j] = M::cvt(qv[i]);
+          }
         }
       }
     }
@@ -280,21 +342,22 @@ __global__ __launch_bounds__(PREP_THREADS) void fwd_prep_kernel(
       }
     }
     __syncthreads();
-    // ---- W and Q' rows of the block (row layout, 4 elements per store) ----
-    if (!BWDL)
-    for (int idx = tid; idx < 16 * DK / 4; idx += PREP_THREADS) {
-      const int r = idx / (DK / 4);
-      const int j4 = (idx - r * (DK / 4)) * 4;
-      f32x4 wv, qv;
+    if (!BWDL) {
+      // W and Q' rows of the block, 4 elements per store
+      for (int idx = tid; idx < 16 * DK / 4; idx += NTH) {
+        const int r = idx / (DK / 4);
+        const int j4 = (idx - r * (DK / 4)) * 4;
+        f32x4 wq, qq;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wv[i] = M::to_f32(sStage[r][j4 + i]);
-        qv[i] = M::to_f32(sStage[r][DK + j4 + i]);
+        for (int i = 0; i < 4; ++i) {
+          wq[i] = M::to_f32(sStage[r][j4 + i]);
+          qq[i] = M::to_f32(sStage[r][DK + j4 + i]);
+        }
+        store4(out.W + static_cast<size_t>(r0 + r) * DK + j4, wq);
+        store4(out.Qp + static_cast<size_t>(r0 + r) * DK + j4, qq);
       }
-      store4(out.W + static_cast<size_t>(r0 + r) * DK + j4, wv);
-      store4(out.Qp + static_cast<size_t>(r0 + r) * DK + j4, qv);
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
@@ -429,15 +492,21 @@ hipError_t launch_fwd_prep(const ChunkShape& s, const void* q, const void* k, co
                            const void* gamma, void* summ, bool bwd_layout, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(s.nchunks());
   if (grid == 0) return hipSuccess;
-#define MUIR_PREP1(TT, DD, BL)                                                                     \
-  hipLaunchKernelGGL((fwd_prep_kernel<TT, DD, BL>), dim3(grid), dim3(PREP_THREADS), 0, stream, s.T, \
-                     s.H, s.C, (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a,           \
-                     (const TT*)erase, (const TT*)write, (const TT*)gamma, (char*)summ,              \
+#define MUIR_PREP1(TT, DD, CC, BL)                                                                 \
+  hipLaunchKernelGGL((fwd_prep_kernel<TT, DD, CC, BL>), dim3(grid), dim3((2 * DD / 32) * 64), 0,     \
+                     stream, s.T, s.H, (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, \
+                     (const TT*)erase, (const TT*)write, (const TT*)gamma, (char*)summ,            \
                      s.summary_bytes())
-#define MUIR_PREP(TT, DD)                 \
-  do {                                    \
-    if (bwd_layout) MUIR_PREP1(TT, DD, true); \
-    else MUIR_PREP1(TT, DD, false);        \
+#define MUIR_PREP2(TT, DD, CC)                   \
+  do {                                           \
+    if (bwd_layout) MUIR_PREP1(TT, DD, CC, true); \
+    else MUIR_PREP1(TT, DD, CC, false);           \
+  } while (0)
+#define MUIR_PREP(TT, DD)                               \
+  do {                                                  \
+    if (s.C == 64) MUIR_PREP2(TT, DD, 64);              \
+    else if (s.C == 128) MUIR_PREP2(TT, DD, 128);       \
+    else MUIR_PREP2(TT, DD, 256);                       \
   } while (0)
   if (s.bf16) {
     if (s.DK == 128) MUIR_PREP(uint16_t, 128);
@@ -448,6 +517,7 @@ hipError_t launch_fwd_prep(const ChunkShape& s, const void* q, const void* k, co
   }
 #undef MUIR_PREP
 #undef MUIR_PREP1
+#undef MUIR_PREP2
   return hipGetLastError();
 }
 

@@ -46,7 +46,9 @@ hipError_t launch_bwd_scan(const ChunkShape& s, const void* summ, const void* dO
                            const float* dS_T, float* dS_chunks, float* dS0, hipStream_t stream);
 
 // Chunk-parallel: all input gradients of every chunk.  `scratch` holds
-// 2 * C * DV floats per chunk (the chunk's deltas and their gradients).
+// bwd_chunk_scratch_bytes(s) per chunk (the chunk's deltas, their gradients
+// and its leaf inverses).
+size_t bwd_chunk_scratch_bytes(const ChunkShape& s);
 hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, const void* v,
                             const void* log_a, const void* erase, const void* write,
                             const void* gamma, const float* S_chunks, const float* dS_chunks,

@@ -37,7 +37,7 @@ size_t fwd_ws(const ChunkShape& s) { return s.nchunks() * s.summary_bytes(); }
 // on a pointer), the chunk-end state gradients, and per-chunk scratch for the
 // deltas and their gradients (2 * C * dv fp32).
 size_t bwd_scratch_bytes(const ChunkShape& s) {
-  return static_cast<size_t>(2) * s.C * s.DV * 4;
+  return (muir::bwd_chunk_scratch_bytes(s) + 255) & ~static_cast<size_t>(255);
 }
 size_t bwd_ws(const ChunkShape& s) {
   return s.nchunks() * (s.summary_bytes() + 2 * s.state_bytes() + bwd_scratch_bytes(s));

@@ -18,6 +18,10 @@ Recipe (numpy PCG64, one generator per call, fixed draw order):
            "channel_slow" -> as "channel", plus round(0.1 d_k) channels per
                              head (seeded choice) with r ~ U[1e-6, 1e-4]
            "zero"         -> 0 (no decay)
+           "steep"        -> U[-12, -1e-3] i.i.d. per element (fast rows whose
+                             16-token decay exceeds what a single leaf factor spans)
+           "spiky"        -> "channel", plus log_a = -1e4 (state wiped: exp = 0)
+                             on a seeded 2% of the elements
   erase, write : sigmoid(N(0,1));  gamma : 2 sigmoid(N(0,1))
   dO     : N(0, 1) (only when asked for)
   S0     : S0_scale * N(0, 1) in fp32 (zeros when S0_scale == 0)
@@ -83,6 +87,12 @@ def seq_inputs(B: int, T: int, H: int, dk: int, dv: int, *, dtype: str = "bf16",
         log_a = np.broadcast_to(-r[None, None, :, :], (B, T, H, dk)).astype(f32)
     elif decay == "zero":
         log_a = np.zeros((B, T, H, dk), dtype=f32)
+    elif decay == "steep":
+        log_a = rng.uniform(-12.0, -1e-3, size=(B, T, H, dk)).astype(f32)
+    elif decay == "spiky":
+        r = _decay_rates(rng, H, dk, "channel")
+        log_a = np.broadcast_to(-r[None, None, :, :], (B, T, H, dk)).astype(f32).copy()
+        log_a[rng.random((B, T, H, dk)) < 0.02] = -1e4
     else:
         raise ValueError(f"unknown decay mode {decay!r}")
     erase = _sigmoid(rng.standard_normal((B, T, H, dk), dtype=f32))

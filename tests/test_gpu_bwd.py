@@ -37,6 +37,10 @@ CASES = [
     ("bf16_d128_c128_S0", 1, 256, 2, 128, 128, "bf16", "channel_slow", 0.1, True),
     ("bf16_d128_c256", 1, 512, 2, 128, 256, "bf16", "channel_slow", 0.0, False),
     ("bf16_d64_c64_uniform", 1, 192, 3, 64, 64, "bf16", "uniform", 0.1, True),
+    ("f32_d64_c64_steep", 1, 128, 2, 64, 64, "f32", "steep", 0.1, True),
+    ("bf16_d128_c128_steep", 1, 256, 2, 128, 128, "bf16", "steep", 0.0, False),
+    ("f32_d128_c64_spiky", 1, 128, 2, 128, 64, "f32", "spiky", 0.1, True),
+    ("bf16_d128_c64_spiky", 1, 256, 2, 128, 64, "bf16", "spiky", 0.0, True),
 ]
 
 

@@ -53,6 +53,11 @@ CASES = [
     ("bf16_d128_c128_S0", 1, 256, 2, 128, 128, "bf16", "channel_slow", 0.1),
     ("bf16_d128_c256", 1, 512, 2, 128, 256, "bf16", "channel_slow", 0.0),
     ("bf16_d64_c64_uniform", 2, 192, 3, 64, 64, "bf16", "uniform", 0.1),
+    # leaves whose decay range needs the per-pair factors
+    ("f32_d64_c64_steep", 1, 128, 2, 64, 64, "f32", "steep", 0.1),
+    ("bf16_d128_c128_steep", 1, 256, 2, 128, 128, "bf16", "steep", 0.0),
+    ("f32_d128_c64_spiky", 1, 128, 2, 128, 64, "f32", "spiky", 0.1),
+    ("bf16_d128_c256_spiky", 1, 512, 2, 128, 256, "bf16", "spiky", 0.1),
 ]
 
 
