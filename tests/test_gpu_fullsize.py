@@ -1,0 +1,105 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py
+times, on outputs the oracle can compute one (batch, head) at a time.
+
+  layer 4K  : B=8, T=4096, H=16, d=128, chunk 64, bf16   (forward and backward)
+  long 32K  : B=1, T=32768, H=16, d=128, chunk 128 / 256  (forward and backward)
+  decode    : 64 streams x 16 heads x d=128, 4096 steps  (every step's output)
+
+Tolerance: max |gpu - oracle| / max |oracle| per tensor on the sampled slice <= 2e-2.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import muir_inputs
+import oracle
+from gpu_util import NAMES, rel_err
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+GRADS = ("dq", "dk", "dv", "dlog_a", "derase", "dwrite", "dgamma")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _lib():
+    import gated_delta_rule_muir_amd as m
+    m.lib()
+    return m
+
+
+def _check_heads(name, inp, o, S_T, g, heads, with_bwd=True):
+    for (b, h) in heads:
+        sl = {n: inp[n][b:b + 1, :, h:h + 1] for n in NAMES}
+        dO = inp["dO"][b:b + 1, :, h:h + 1]
+        o_ref, S_ref = oracle.fwd(*(sl[n] for n in NAMES))
+        errs = {"o": rel_err(o[b:b + 1, :, h:h + 1], o_ref), "S_T": rel_err(S_T[b:b + 1, h:h + 1], S_ref)}
+        if with_bwd:
+            gr = oracle.bwd(*(sl[n] for n in NAMES), dO)
+            for n in GRADS:
+                errs[n] = rel_err(g[n][b:b + 1, :, h:h + 1], gr[n])
+            errs["dS0"] = rel_err(g["dS0"][b:b + 1, h:h + 1], gr["dS0"])
+        _say(f"  {name} b={b} h={h}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+        for k_, v_ in errs.items():
+            assert v_ <= TOL, (name, b, h, k_, v_)
+
+
+def _run(m, inp, C):
+    dv = {n: (t.to("cuda") if t is not None else None) for n, t in inp.items()}
+    o, S_T, Sc = m.muir_chunk_fwd(*(dv[n] for n in NAMES), chunk=C, save_states=True)
+    g = m.muir_chunk_bwd(*(dv[n] for n in NAMES), dv["dO"], S_chunks=Sc, chunk=C)
+    torch.cuda.synchronize()
+    out = (o.cpu(), S_T.cpu(), {n: t.cpu() for n, t in g.items()})
+    del dv, o, S_T, Sc, g
+    torch.cuda.empty_cache()
+    return out
+
+
+def test_layer_4k_fwd_bwd_sampled_heads():
+    m = _lib()
+    w = muir_inputs.WORKLOADS["layer_fwdbwd_4k"]
+    _say(f"layer_4k: generating B={w.B} T={w.T} H={w.H} d={w.dk}")
+    inp = muir_inputs.seq_inputs(w.B, w.T, w.H, w.dk, w.dv, dtype=w.dtype, decay=w.decay, seed=0, with_dO=True)
+    o, S_T, g = _run(m, inp, w.chunk)
+    _check_heads("layer_4k", inp, o, S_T, g, [(0, 0), (3, 7), (7, 15)])
+
+
+@pytest.mark.parametrize("name", ["long_32k_c128", "long_32k_c256"])
+def test_long_32k_fwd_bwd_sampled_heads(name):
+    m = _lib()
+    w = muir_inputs.WORKLOADS[name]
+    _say(f"{name}: generating B={w.B} T={w.T} H={w.H} d={w.dk} C={w.chunk}")
+    inp = muir_inputs.seq_inputs(w.B, w.T, w.H, w.dk, w.dv, dtype=w.dtype, decay=w.decay, seed=0, with_dO=True)
+    o, S_T, g = _run(m, inp, w.chunk)
+    _check_heads(name, inp, o, S_T, g, [(0, 0), (0, 11)])
+
+
+def test_decode_4096_steps_sampled_streams():
+    """64 streams x 16 heads for 4096 steps; streams 0 and 63 are replayed by the
+    oracle (a decode stream is the recurrence over its steps) and compared at
+    every step and on the final state."""
+    m = _lib()
+    N, H, d, steps = 64, 16, 128, 4096
+    _say("decode: generating inputs on the device")
+    inp = muir_inputs.step_inputs_torch(N, H, d, d, steps, device="cuda", seed=5)
+    S = torch.zeros((N, H, d, d), dtype=torch.float32, device="cuda")
+    picks = [0, N - 1]
+    outs = torch.empty((steps, len(picks), H, d), dtype=torch.bfloat16, device="cuda")
+    for t in range(steps):
+        o = m.muir_step(inp["q"][t], inp["k"][t], inp["v"][t], inp["log_a"], inp["erase"][t],
+                        inp["write"][t], inp["gamma"][t], S)
+        outs[t] = o[picks]
+    torch.cuda.synchronize()
+    _say("decode: oracle on the sampled streams")
+    seq = {n: inp[n][:, picks].transpose(0, 1).cpu() for n in ("q", "k", "v", "erase", "write", "gamma")}
+    seq["log_a"] = inp["log_a"][picks].unsqueeze(1).expand(len(picks), steps, H, d).cpu()
+    o_ref, S_ref = oracle.fwd(*(seq[n] for n in NAMES))
+    e_o = rel_err(outs.transpose(0, 1).cpu(), o_ref)
+    e_s = rel_err(S[picks].cpu(), S_ref)
+    _say(f"  decode o={e_o:.2e} S={e_s:.2e}")
+    assert e_o <= TOL and e_s <= TOL
