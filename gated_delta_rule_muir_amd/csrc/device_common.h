@@ -18,7 +18,10 @@
 namespace muir {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---- bf16 storage helpers (raw 16-bit patterns) ------------------------------
 
@@ -26,16 +29,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
   return __uint_as_float(static_cast<uint32_t>(x) << 16);
 }
 
-// Round-to-nearest-even fp32 -> bf16 (finite inputs; NaN is kept a NaN).
+// Round-to-nearest-even fp32 -> bf16 (gfx950 converts in hardware,
+// v_cvt_pk_bf16_f32, two values per instruction).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return static_cast<uint16_t>((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Element loads from an input tensor of either dtype.
@@ -48,6 +50,10 @@ template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ float load(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
   static __device__ __forceinline__ void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 };
+
+__device__ __forceinline__ i16x4 pack4(f32x4 v) {
+  return __builtin_bit_cast(i16x4, __builtin_convertvector(v, bf16x4));
+}
 
 // Load 4 consecutive elements (16-byte aligned for fp32, 8-byte for bf16).
 __device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
@@ -62,10 +68,7 @@ __device__ __forceinline__ f32x4 load4(const uint16_t* p) {
 }
 __device__ __forceinline__ void store4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 __device__ __forceinline__ void store4(uint16_t* p, f32x4 v) {
-  uint2 r;
-  r.x = pack_bf16x2(v[0], v[1]);
-  r.y = pack_bf16x2(v[2], v[3]);
-  *reinterpret_cast<uint2*>(p) = r;
+  *reinterpret_cast<i16x4*>(p) = pack4(v);
 }
 
 // ---- MFMA wrappers -----------------------------------------------------------
@@ -80,25 +83,8 @@ __device__ __forceinline__ f32x4 mma4_f32(float a, float b, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
 
-__device__ __forceinline__ i16x4 pack4(f32x4 v) {
-  uint32_t lo = pack_bf16x2(v[0], v[1]);
-  uint32_t hi = pack_bf16x2(v[2], v[3]);
-  i16x4 r;
-  r[0] = static_cast<short>(lo & 0xffffu);
-  r[1] = static_cast<short>(lo >> 16);
-  r[2] = static_cast<short>(hi & 0xffffu);
-  r[3] = static_cast<short>(hi >> 16);
-  return r;
-}
-
 __device__ __forceinline__ i16x4 load_bf16x4(const uint16_t* p) {
-  uint2 r = *reinterpret_cast<const uint2*>(p);
-  i16x4 o;
-  o[0] = static_cast<short>(r.x & 0xffffu);
-  o[1] = static_cast<short>(r.x >> 16);
-  o[2] = static_cast<short>(r.y & 0xffffu);
-  o[3] = static_cast<short>(r.y >> 16);
-  return o;
+  return *reinterpret_cast<const i16x4*>(p);
 }
 
 __device__ __forceinline__ f32x4 zero4() {

@@ -53,7 +53,7 @@ hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, c
                             const void* log_a, const void* erase, const void* write,
                             const void* gamma, const float* S_chunks, const float* dS_chunks,
                             const void* dO, float* dq, float* dk, float* dv, float* dlog_a,
-                            float* derase, float* dwrite, float* dgamma, float* scratch,
+                            float* derase, float* dwrite, float* dgamma, void* scratch,
                             hipStream_t stream);
 
 }  // namespace muir
