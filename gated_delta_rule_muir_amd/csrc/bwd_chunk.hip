@@ -45,8 +45,12 @@ __host__ __device__ constexpr size_t bwd_scratch_bytes_tc(int C, int DV) {
   return (static_cast<size_t>(2) * C * DV + static_cast<size_t>(C / 16) * 512) * sizeof(TC);
 }
 
-template <typename Tin, int DK, int C>
-__global__ __launch_bounds__((2 * DK / 32) * 64) void bwd_chunk_kernel(
+// LDS row padding (elements) that keeps 16 lanes reading 4 consecutive
+// elements of 16 different rows on distinct banks.
+template <typename TC> constexpr int row_pad() { return sizeof(TC) == 2 ? 8 : 4; }
+
+template <typename Tin, int DK, int C, int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     int T, int H, const Tin* __restrict__ q, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ log_a, const Tin* __restrict__ erase,
     const Tin* __restrict__ write, const Tin* __restrict__ gamma,
@@ -58,20 +62,27 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void bwd_chunk_kernel(
   typedef MM<TC> M;
   typedef typename M::frag frag;
   constexpr int DV = DK;
-  constexpr int NW = 2 * DK / 32;    // wave w owns state column / gradient channel 16w + lane%16
   constexpr int NTH = 64 * NW;
+  constexpr int NT = DV / (16 * NW);  // 16-column tiles per wave (state columns, gradient channels)
   constexpr int RT = DK / 16;
-  constexpr int TPC = NTH / DK;      // elementwise: 4 threads per key channel, 4 tokens each
+  constexpr int TPC = NTH / DK;       // elementwise: threads per key channel
+  constexpr int RPT = 16 / TPC;       // elementwise: consecutive tokens per thread
   constexpr int NB = C / 16;
   constexpr int NSTEP = 3 * NB;
-  constexpr bool LEAN = sizeof(TC) == 4 && DK == 128;  // q, gamma re-read from global (LDS budget)
-  constexpr int SPLIT = LEAN ? 4 : 2;                  // staged state in column passes
+  constexpr int SPLIT = (sizeof(TC) == 4 && DK == 128) ? 4 : 1;  // staged state in column passes
   constexpr int SW = DV / SPLIT;
-  constexpr int PT = DK + 4;
-  constexpr int PV = DV + 4;
-  constexpr int PS = SW + 4;
-  constexpr int RC = DV / 4;         // threads per row of a [16][DV] tile
-  static_assert(NW * 16 == DV && TPC == 4 && NTH == 16 * RC, "thread layout");
+  constexpr int PT = DK + row_pad<TC>();
+  constexpr int PV = DV + row_pad<TC>();
+  constexpr int PS = SW + row_pad<TC>();
+  constexpr int TP = sizeof(TC) == 2 ? 24 : 20;  // row length of the [.][16] transposed tiles
+  constexpr int EPT = 16 * DV / NTH;  // row-tile elements per thread
+  constexpr int RC = DV / EPT;        // threads per row of a [16][DV] tile
+  constexpr int EPW = 8 / static_cast<int>(sizeof(TC));  // elements per 8-byte word
+  constexpr int RW = EPT / EPW;       // 8-byte words per thread of a row tile
+  constexpr int TPW = 512 / EPW;      // threads that move a block's T_II, P_II words
+  static_assert(NT >= 1 && NW * NT * 16 == DV && TPC * RPT == 16 && RPT % 4 == 0 && RW >= 1 &&
+                    EPT % EPW == 0 && TPW <= NTH,
+                "thread layout");
 
   const int NC = T / C;
   const int chunk = blockIdx.x;
@@ -84,35 +95,50 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void bwd_chunk_kernel(
   const int wave = tid >> 6;
   const int g = lane >> 4;
   const int c16 = lane & 15;
-  const int colv = 16 * wave + c16;  // MFMA-output mapping: state column / gradient channel
-  const int ej = tid % DK;           // elementwise mapping: channel, tokens 4*part..+3
+  // MFMA-output mapping: lane's state column / gradient channel of tile n
+  auto colv = [&](int n) -> int { return 16 * (NT * wave + n) + c16; };
+  const int ej = tid % DK;            // elementwise mapping: channel, tokens RPT*part..+RPT-1
   const int part = tid / DK;
-  const int prow = tid / RC;         // row-tile mapping: row, columns 4*pc..+3
-  const int pc4 = (tid % RC) * 4;
+  const int prow = tid / RC;          // row-tile mapping: row, columns pc0..pc0+EPT-1
+  const int pc0 = (tid % RC) * EPT;
 
-  const size_t rowbase = (static_cast<size_t>(b) * T + static_cast<size_t>(c) * C) * H + h;
-  auto gidx = [&](int t, int j) -> size_t { return (rowbase + static_cast<size_t>(t) * H) * DK + j; };
+  // Workgroup-uniform bases of the chunk; element (t, j) of a [B, T, H, D]
+  // tensor is at index t * HD + j from them.
+  const size_t ebase = ((static_cast<size_t>(b) * T + static_cast<size_t>(c) * C) * H + h) * DK;
+  const uint32_t HD = static_cast<uint32_t>(H) * DK;
+  const Tin* qb = q + ebase;
+  const Tin* kb = k + ebase;
+  const Tin* vb = v + ebase;
+  const Tin* lb = log_a + ebase;
+  const Tin* eb = erase + ebase;
+  const Tin* wb = write + ebase;
+  const Tin* gb = gamma + ebase;
+  const Tin* dOb = dO + ebase;
+  float* dqb = dq + ebase;
+  float* dkb = dk + ebase;
+  float* dvb = dv + ebase;
+  float* dlb = dlog_a + ebase;
+  float* deb = derase + ebase;
+  float* dwb = dwrite + ebase;
+  float* dgb = dgamma + ebase;
+  auto gi = [&](int t, int j) -> uint32_t { return static_cast<uint32_t>(t) * HD + static_cast<uint32_t>(j); };
   TC* gDel = reinterpret_cast<TC*>(scratch + static_cast<size_t>(chunk) * bwd_scratch_bytes_tc<TC>(C, DV));
   TC* gdR = gDel + static_cast<size_t>(C) * DV;
   TC* gTP = gdR + static_cast<size_t>(C) * DV;  // [NB][2][16][16]
   const float* S0c = S_chunks + static_cast<size_t>(chunk) * DK * DV;
   const float* dSC = dS_chunks + static_cast<size_t>(chunk) * DK * DV;
 
-  constexpr int UNI = 16 * PT > DK * 20 ? 16 * PT : DK * 20;
-  constexpr int UNU = DV * 20 > 16 * PV ? DV * 20 : 16 * PV;
+  constexpr int UNI = 16 * PT > DK * TP ? 16 * PT : DK * TP;
+  constexpr int UNU = DV * TP > 16 * PV ? DV * TP : 16 * PV;
   __shared__ float sBsum[NB][DK];                            // sum of log_a over block I
   __shared__ float sTmp[TPC][DK];
   __shared__ float sF[16][DK + 1];                           // per-element factor of the sweep
-  __shared__ float sLam[16][DK + 1];                         // log_a of the block (per-pair leaves)
-  __shared__ __attribute__((aligned(16))) TC sK[16][PT];     // raw k of the block
-  __shared__ __attribute__((aligned(16))) TC sE[16][PT];     // raw erase
-  __shared__ __attribute__((aligned(16))) TC sQ[LEAN ? 1 : 16][PT];   // raw q
-  __shared__ __attribute__((aligned(16))) TC sGm[LEAN ? 1 : 16][PT];  // raw gamma
+  __shared__ float sLam[16][DK + 1];                         // log_a of a steep block (per-pair leaves)
   __shared__ __attribute__((aligned(16))) TC sRowA[16][PT];  // F1: X rows   R: Ke rows
   __shared__ __attribute__((aligned(16))) TC sUn1[UNI];      // F1: Y rows   R: Y^T
   __shared__ __attribute__((aligned(16))) TC sUn2[UNI];      // F1: Z rows   R: Yhat^T
-  __shared__ __attribute__((aligned(16))) TC sTA[DK][20];    // F1, F2: Ke^T   R: X^T
-  __shared__ __attribute__((aligned(16))) TC sTZ[DK][20];    // F1, F2: Z^T    R: Xhat^T
+  __shared__ __attribute__((aligned(16))) TC sTA[DK][TP];    // F1, F2: Ke^T   R: X^T
+  __shared__ __attribute__((aligned(16))) TC sTZ[DK][TP];    // F1, F2: Z^T    R: Xhat^T
   __shared__ __attribute__((aligned(16))) TC sUnU[UNU];      // F1: (write*v)^T   R, F2: dR rows
   __shared__ __attribute__((aligned(16))) TC sDO[16][PV];    // dO rows of the block
   __shared__ __attribute__((aligned(16))) TC sDL[16][PV];    // delta rows of the block
@@ -120,8 +146,8 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void bwd_chunk_kernel(
   __shared__ float sPw[16][17];
   __shared__ float sTw[16][17];
   __shared__ float sPf[16][17];
-  __shared__ __attribute__((aligned(16))) TC sT[16][20];     // T_II of the block
-  __shared__ __attribute__((aligned(16))) TC sP[16][20];     // P_II of the block
+  __shared__ __attribute__((aligned(16))) TC sT[16][TP];     // T_II of the block
+  __shared__ __attribute__((aligned(16))) TC sP[16][TP];     // P_II of the block
   __shared__ __attribute__((aligned(16))) TC sSD[DK][PS];    // staged S or D columns, [dk][dv]
   __shared__ float sLf[2][16][17];                           // leaf gradient matrices
   __shared__ float sG[DK];
@@ -129,30 +155,41 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void bwd_chunk_kernel(
   __shared__ float sTot[DK];
   TC (*sRowB)[PT] = reinterpret_cast<TC (*)[PT]>(sUn1);
   TC (*sRowZ)[PT] = reinterpret_cast<TC (*)[PT]>(sUn2);
-  TC (*sTB)[20] = reinterpret_cast<TC (*)[20]>(sUn1);
-  TC (*sTY)[20] = reinterpret_cast<TC (*)[20]>(sUn2);
-  TC (*sU)[20] = reinterpret_cast<TC (*)[20]>(sUnU);
+  TC (*sTB)[TP] = reinterpret_cast<TC (*)[TP]>(sUn1);
+  TC (*sTY)[TP] = reinterpret_cast<TC (*)[TP]>(sUn2);
+  TC (*sU)[TP] = reinterpret_cast<TC (*)[TP]>(sUnU);
   TC (*sDR)[PV] = reinterpret_cast<TC (*)[PV]>(sUnU);
+
+  // identity operand: a 16x16 product with it moves a tile's rows onto lanes
+  frag ident;
+  {
+    f32x4 idv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) idv[i] = (4 * g + i == c16) ? 1.f : 0.f;
+    ident = M::from_f32(idv);
+  }
 
   // ---- block sums of the log-decay ----
 #pragma unroll
   for (int I = part; I < NB; I += TPC) {
     float sacc = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) sacc += Elem<Tin>::load(log_a, gidx(16 * I + rr, ej));
+    for (int rr = 0; rr < 16; ++rr) sacc += ldv(lb, gi(16 * I + rr, ej));
     sBsum[I][ej] = sacc;
   }
 
   auto step_sweep = [](int s) { return s / NB; };
   auto step_block = [](int s) { return (s / NB) == 1 ? NB - 1 - (s - NB) : s % NB; };
 
-  // ---- prefetch registers ----
-  float pk[4], pe[4], pq[4], pg[4], pl[4], pu[4];  // inputs of channel ej, tokens 4*part..+3
-  f32x4 pdo, pdl, pdr;                             // row tiles: row prow, columns pc4..+3
-  float ptp[512 / NTH];                            // T_II, P_II elements
-  float pvv[4], pww[4];                            // R: v, write at (token 4g+i, column colv)
-  float pdk[4], pdla[4];                           // F2: partial d(k), partial dLam at the same
-  float pq2[4], pg2[4];                            // LEAN F1: q, gamma at the same
+  // ---- prefetch slots, all assigned by every prefetch (unused ones to 0) ----
+  // elementwise (channel ej, tokens RPT*part + rr): log_a, k, erase, q, gamma, write, v
+  float xl[RPT], xk[RPT], xe[RPT], xq[RPT], xg[RPT], xw[RPT], xv[RPT];
+  // row tiles (row prow, columns pc0..): dO, deltas, their gradients (raw words)
+  u32x2 rdo[RW], rdl[RW], rdr[RW];
+  u32x2 rtp;  // one word of the block's T_II, P_II (threads < TPW)
+  // MFMA-output mapping (token 4g+i, column colv(n)):
+  //   F1: q, gamma   R: v, write   F2: k, erase, partial d(k), partial dLam
+  float oa[NT][4], ob[NT][4], oc[NT][4], od[NT][4];
 
   auto prefetch = [&](int s) {
     if (s >= NSTEP) return;
@@ -160,41 +197,51 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void bwd_chunk_kernel(
     const int I = step_block(s);
     const int r0 = 16 * I;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const size_t gi = gidx(r0 + 4 * part + rr, ej);
-      pk[rr] = Elem<Tin>::load(k, gi);
-      pe[rr] = Elem<Tin>::load(erase, gi);
-      pq[rr] = Elem<Tin>::load(q, gi);
-      pg[rr] = Elem<Tin>::load(gamma, gi);
-      pl[rr] = Elem<Tin>::load(log_a, gi);
-      pu[rr] = sw == 0 ? Elem<Tin>::load(write, gi) * Elem<Tin>::load(v, gi) : 0.f;
+    for (int rr = 0; rr < RPT; ++rr) {
+      const uint32_t o = gi(r0 + RPT * part + rr, ej);
+      xl[rr] = ldv(lb, o);
+      xk[rr] = ldv(kb, o);
+      xe[rr] = sw != 2 ? ldv(eb, o) : 0.f;
+      xq[rr] = sw != 2 ? ldv(qb, o) : 0.f;
+      xg[rr] = sw != 2 ? ldv(gb, o) : 0.f;
+      xw[rr] = sw == 0 ? ldv(wb, o) : 0.f;
+      xv[rr] = sw == 0 ? ldv(vb, o) : 0.f;
     }
-    if (sw != 2) pdo = load4(dO + gidx(r0 + prow, pc4));
-    // deltas: not for F1; for R's first block and F2's first block they are
-    // still in LDS from the step before (which computed or loaded them)
-    if ((sw == 1 && I != NB - 1) || (sw == 2 && I != 0))
-      pdl = load4(gDel + static_cast<size_t>(r0 + prow) * DV + pc4);
-    if (sw == 2 && I != 0) pdr = load4(gdR + static_cast<size_t>(r0 + prow) * DV + pc4);
-    if (sw == 1 && I != NB - 1) {
+    const bool ldl = (sw == 1 && I != NB - 1) || (sw == 2 && I != 0);
+    const bool ldr = sw == 2 && I != 0;
+    const u32x2 zw = {0u, 0u};
 #pragma unroll
-      for (int e = 0; e < 512 / NTH; ++e) ptp[e] = M::to_f32(gTP[static_cast<size_t>(I) * 512 + tid + e * NTH]);
+    for (int e = 0; e < RW; ++e) {
+      const int col = pc0 + e * EPW;
+      const uint32_t so = static_cast<uint32_t>(r0 + prow) * DV + col;
+      rdo[e] = sw != 2 ? *reinterpret_cast<const u32x2*>(at(dOb, gi(r0 + prow, col))) : zw;
+      // deltas: not for F1; R's first block and F2's first block find them in
+      // LDS, left by the step before
+      rdl[e] = ldl ? *reinterpret_cast<const u32x2*>(at(gDel, so)) : zw;
+      rdr[e] = ldr ? *reinterpret_cast<const u32x2*>(at(gdR, so)) : zw;
     }
+    rtp = (sw == 1 && I != NB - 1 && tid < TPW)
+              ? *reinterpret_cast<const u32x2*>(at(gTP, static_cast<uint32_t>(I * 512 + tid * EPW)))
+              : zw;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const size_t go = gidx(r0 + 4 * g + ii, colv);
-      if (sw == 1) {
-        pvv[ii] = Elem<Tin>::load(v, go);
-        pww[ii] = Elem<Tin>::load(write, go);
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const uint32_t o = gi(r0 + 4 * g + ii, colv(n));
+        if (sw == 0) {
+          oa[n][ii] = ldv(qb, o);
+          ob[n][ii] = ldv(gb, o);
+        } else if (sw == 1) {
+          oa[n][ii] = ldv(vb, o);
+          ob[n][ii] = ldv(wb, o);
+        } else {
+          oa[n][ii] = ldv(kb, o);
+          ob[n][ii] = ldv(eb, o);
+        }
+        // F2's block 0: the partial d(k) is still in registers from R's last step
+        oc[n][ii] = (sw == 2 && I != 0) ? *at(dkb, o) : 0.f;
+        od[n][ii] = sw == 2 ? *at(dlb, o) : 0.f;
       }
-      if (sw == 2) {
-        pdla[ii] = dlog_a[go];
-        if (I != 0) pdk[ii] = dk[go];  // F2's block 0: kept from R's last step
-      }
-      if (LEAN && sw == 0) {
-        pq2[ii] = Elem<Tin>::load(q, go);
-        pg2[ii] = Elem<Tin>::load(gamma, go);
-      }
-    }
   };
 
   // Commit the prefetched step into LDS and form the block's factor tiles.
@@ -207,19 +254,21 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void bwd_chunk_kernel(
   auto commit = [&](int s) -> int {
     const int sw = step_sweep(s);
     const int I = step_block(s);
-    float cs[4], sf[4];
+    float cs[RPT], sf[RPT];
     {
       float run = 0.f;
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        run += pl[rr];
+      for (int rr = 0; rr < RPT; ++rr) {
+        run += xl[rr];
         cs[rr] = run;
       }
       sTmp[part][ej] = run;
-      sf[3] = 0.f;
-      sf[2] = pl[3];
-      sf[1] = pl[3] + pl[2];
-      sf[0] = pl[3] + pl[2] + pl[1];
+      float suf = 0.f;
+#pragma unroll
+      for (int rr = RPT - 1; rr >= 0; --rr) {
+        sf[rr] = suf;
+        suf += xl[rr];
+      }
     }
     const float bsum = sBsum[I][ej];
     const int safe = __syncthreads_and(-bsum <= LEAF_SAFE_RANGE);
@@ -230,83 +279,75 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void bwd_chunk_kernel(
       if (p > part) exsuf += sTmp[p][ej];
     }
     if (part == 0) sG[ej] = __expf(bsum);
-    f32x4 tA, tZ, tB, tY;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int r = 4 * part + rr;
-      const float loc = excl + cs[rr];   // Lam_r - B_I
-      const float suf = sf[rr] + exsuf;  // B_{I+1} - Lam_r
-      const float fs = __expf(loc);
-      const float fe = __expf(suf);
-      const float ek = pe[rr] * pk[rr];
-      const float qt = pg[rr] * pq[rr];
-      sLam[r][ej] = pl[rr];
-      sK[r][ej] = M::cvt(pk[rr]);
-      sE[r][ej] = M::cvt(pe[rr]);
-      if (!LEAN) {
-        sQ[r][ej] = M::cvt(pq[rr]);
-        sGm[r][ej] = M::cvt(pg[rr]);
+    for (int h4 = 0; h4 < RPT / 4; ++h4) {
+      f32x4 tA, tZ, tB, tY;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int rr = 4 * h4 + q4;
+        const int r = RPT * part + rr;
+        const float loc = excl + cs[rr];   // Lam_r - B_I
+        const float suf = sf[rr] + exsuf;  // B_{I+1} - Lam_r
+        const float fs = __expf(loc);
+        const float fe = __expf(suf);
+        const float ek = xe[rr] * xk[rr];
+        const float qt = xg[rr] * xq[rr];
+        if (!safe) sLam[r][ej] = xl[rr];
+        if (sw == 0) {
+          const float z = safe ? xk[rr] * __expf(-loc) : 0.f;
+          sF[r][ej] = fs;
+          sRowA[r][ej] = M::cvt(ek * fs);
+          sRowB[r][ej] = M::cvt(qt * fs);
+          sRowZ[r][ej] = M::cvt(z);
+          tA[q4] = xk[rr] * fe;
+          tZ[q4] = z;
+          tB[q4] = xw[rr] * xv[rr];
+        } else if (sw == 1) {
+          const float ie = safe ? __expf(-suf) : 0.f;
+          sF[r][ej] = fe;
+          sRowA[r][ej] = M::cvt(xk[rr] * fe);
+          tA[q4] = ek * fs;
+          tB[q4] = qt * fs;
+          tZ[q4] = ek * ie;
+          tY[q4] = qt * ie;
+        } else {
+          sF[r][ej] = fs;
+          tA[q4] = xk[rr] * fe;
+          tZ[q4] = safe ? xk[rr] * __expf(-loc) : 0.f;
+        }
       }
-      if (sw == 0) {
-        const float z = safe ? pk[rr] * __expf(-loc) : 0.f;
-        sF[r][ej] = fs;
-        sRowA[r][ej] = M::cvt(ek * fs);
-        sRowB[r][ej] = M::cvt(qt * fs);
-        sRowZ[r][ej] = M::cvt(z);
-        tA[rr] = pk[rr] * fe;
-        tZ[rr] = z;
-        tB[rr] = pu[rr];
-      } else if (sw == 1) {
-        const float ie = safe ? __expf(-suf) : 0.f;
-        sF[r][ej] = fe;
-        sRowA[r][ej] = M::cvt(pk[rr] * fe);
-        tA[rr] = ek * fs;
-        tB[rr] = qt * fs;
-        tZ[rr] = ek * ie;
-        tY[rr] = qt * ie;
-      } else {
-        sF[r][ej] = fs;
-        tA[rr] = pk[rr] * fe;
-        tZ[rr] = safe ? pk[rr] * __expf(-loc) : 0.f;
+      const int t0 = RPT * part + 4 * h4;
+      store4(&sTA[ej][t0], tA);
+      store4(&sTZ[ej][t0], tZ);
+      if (sw == 0) store4(&sU[ej][t0], tB);
+      if (sw == 1) {
+        store4(&sTB[ej][t0], tB);
+        store4(&sTY[ej][t0], tY);
       }
     }
-    store4(&sTA[ej][4 * part], tA);
-    store4(&sTZ[ej][4 * part], tZ);
-    if (sw == 0) store4(&sU[ej][4 * part], tB);
-    if (sw == 1) {
-      store4(&sTB[ej][4 * part], tB);
-      store4(&sTY[ej][4 * part], tY);
-    }
-    if (sw != 2) store4(&sDO[prow][pc4], pdo);
-    if ((sw == 1 && I != NB - 1) || (sw == 2 && I != 0)) store4(&sDL[prow][pc4], pdl);
-    if (sw == 2 && I != 0) store4(&sDR[prow][pc4], pdr);
-    if (sw == 1 && I != NB - 1) {
 #pragma unroll
-      for (int e = 0; e < 512 / NTH; ++e) {
-        const int idx = tid + e * NTH;
-        if (idx < 256)
-          sT[idx >> 4][idx & 15] = M::cvt(ptp[e]);
-        else
-          sP[(idx - 256) >> 4][idx & 15] = M::cvt(ptp[e]);
-      }
+    for (int e = 0; e < RW; ++e) {
+      const int col = pc0 + e * EPW;
+      if (sw != 2) *reinterpret_cast<u32x2*>(&sDO[prow][col]) = rdo[e];
+      if ((sw == 1 && I != NB - 1) || (sw == 2 && I != 0)) *reinterpret_cast<u32x2*>(&sDL[prow][col]) = rdl[e];
+      if (sw == 2 && I != 0) *reinterpret_cast<u32x2*>(&sDR[prow][col]) = rdr[e];
+    }
+    if (sw == 1 && I != NB - 1 && tid < TPW) {
+      const int e0 = tid * EPW;
+      TC* dst = e0 < 256 ? &sT[e0 >> 4][e0 & 15] : &sP[(e0 - 256) >> 4][e0 & 15];
+      *reinterpret_cast<u32x2*>(dst) = rtp;
     }
     __syncthreads();
     return safe;
   };
 
+  // Steep leaves read the raw inputs from global memory (L2-resident: the
+  // step's own loads brought them in).
   // exp(sum of log_a over tokens (i, r] of the block, channel j), r >= i
   auto pair_factor = [&](int r, int i, int j) -> float {
     float ls = 0.f;
     for (int x = i + 1; x <= r; ++x) ls += sLam[x][j];
     return __expf(ls);
-  };
-  auto in_q = [&](int r0, int r, int j) -> float {
-    if constexpr (LEAN) return Elem<Tin>::load(q, gidx(r0 + r, j));
-    else return M::to_f32(sQ[LEAN ? 0 : r][j]);
-  };
-  auto in_g = [&](int r0, int r, int j) -> float {
-    if constexpr (LEAN) return Elem<Tin>::load(gamma, gidx(r0 + r, j));
-    else return M::to_f32(sGm[LEAN ? 0 : r][j]);
   };
 
   // out[r][i] = A_r . B_i over the DV columns of two row tiles, masked to
@@ -324,53 +365,68 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void bwd_chunk_kernel(
     }
   };
 
-  // stage columns [p*SW, (p+1)*SW) of a state (rows 16s+4g+i, column colv) into sSD
-  auto stage_state = [&](const f32x4* st, int p) {
-    const int col = colv - p * SW;
-    if (col >= 0 && col < SW) {
+  // Store a [16 tokens][16 columns] tile held in MFMA-output layout (tokens
+  // 4g+i, column c16) as rows: one identity product moves the tokens onto
+  // lanes, then each lane writes 4 consecutive columns of its token.
+  auto store_rows = [&](f32x4 tile, TC (*lds)[PV], TC* glob, int col0) {
+    const f32x4 tt = M::mma(M::from_f32(tile), ident, zero4());  // token c16, columns col0+4g+i
+    store4(&lds[c16][col0 + 4 * g], tt);
+    store4(glob + static_cast<size_t>(c16) * DV + col0 + 4 * g, tt);
+  };
+
+  // contraction over dv of a state (rows 16s+4g+i, columns colv(n)) with the
+  // rows of a [16][DV] tile: acc[n][token 4g+i] = sum_c A[token][c] st[channel colv(n)][c].
+  // The state is staged in LDS as [dk][dv] bf16/fp32 rows, moved there by
+  // identity products (4 consecutive columns per lane and store).
+  auto state_rows = [&](const f32x4 (*st)[NT], const TC (*A)[PV], f32x4* acc) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[n] = zero4();
+#pragma unroll
+    for (int p = 0; p < SPLIT; ++p) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const int cb = 16 * (NT * wave + n) - p * SW;
+        if (cb >= 0 && cb < SW) {
+#pragma unroll
+          for (int s = 0; s < RT; ++s) {
+            const f32x4 tt = M::mma(M::from_f32(st[s][n]), ident, zero4());  // row 16s+c16, columns cb+4g+i
+            store4(&sSD[16 * s + c16][cb + 4 * g], tt);
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < SW / 16; ++kk) {
+        const frag af = M::load(&A[c16][p * SW + 16 * kk + 4 * g]);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[n] = M::mma(af, M::load(&sSD[colv(n)][16 * kk + 4 * g]), acc[n]);
+      }
+      if (p + 1 < SPLIT) __syncthreads();
+    }
+  };
+
+  // (the lane offset is made opaque per call so that the addresses are formed
+  // where they are used instead of being kept live across the sweeps)
+  auto load_state = [&](f32x4 (*st)[NT], const float* src) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      uint32_t lo = static_cast<uint32_t>(4 * g * DV + colv(n));
+      asm volatile("" : "+v"(lo));
 #pragma unroll
       for (int s = 0; s < RT; ++s)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sSD[16 * s + 4 * g + i][col] = M::cvt(st[s][i]);
+        for (int i = 0; i < 4; ++i) st[s][n][i] = *at(src, lo + static_cast<uint32_t>((16 * s + i) * DV));
     }
   };
 
-  // acc += A[token c16][staged columns] . sSD[channel colv][staged columns]
-  auto dv_contract = [&](f32x4 acc, const TC (*A)[PV], int p) -> f32x4 {
-#pragma unroll
-    for (int kk = 0; kk < SW / 16; ++kk)
-      acc = M::mma(M::load(&A[c16][p * SW + 16 * kk + 4 * g]), M::load(&sSD[colv][16 * kk + 4 * g]), acc);
-    return acc;
-  };
-
-  // contraction of a state with rows of a [16][DV] tile over dv, all column passes
-  auto state_rows = [&](const f32x4* st, const TC (*A)[PV]) -> f32x4 {
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int p = 0; p < SPLIT; ++p) {
-      stage_state(st, p);
-      __syncthreads();
-      acc = dv_contract(acc, A, p);
-      __syncthreads();
-    }
-    return acc;
-  };
-
-  auto load_state = [&](f32x4* st, const float* src) {
-#pragma unroll
-    for (int s = 0; s < RT; ++s)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st[s][i] = src[static_cast<size_t>(16 * s + 4 * g + i) * DV + colv];
-  };
-
-  auto decay_update = [&](f32x4* st, int s, const frag& a, const frag& bfr) {
+  auto decay_scale = [&](int s) -> f32x4 {
     f32x4 gs;
 #pragma unroll
     for (int i = 0; i < 4; ++i) gs[i] = sG[16 * s + 4 * g + i];
-    st[s] = M::mma(a, bfr, st[s] * gs);
+    return gs;
   };
 
-  f32x4 S[RT];
+  f32x4 S[RT][NT];
   load_state(S, S0c);
   prefetch(0);
   __syncthreads();  // sBsum
@@ -380,12 +436,14 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void bwd_chunk_kernel(
   for (int I = 0; I < NB; ++I) {
     const int r0 = 16 * I;
     const int safe = commit(I);
-    float qcur[4], gcur[4];  // LEAN: this step's q, gamma (prefetch registers are reused next)
+    float qcur[NT][4], gcur[NT][4];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      qcur[ii] = pq2[ii];
-      gcur[ii] = pg2[ii];
-    }
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        qcur[n][ii] = oa[n][ii];
+        gcur[n][ii] = ob[n][ii];
+      }
     prefetch(I + 1);
     // leaf A_II, P_II, T_II (also kept in the scratch for the reverse sweep)
     if (safe) {
@@ -411,9 +469,10 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void bwd_chunk_kernel(
         float a = 0.f, pp = 0.f;
         if (i <= r) {
           for (int j = 0; j < DK; ++j) {
-            const float kk = M::to_f32(sK[i][j]) * pair_factor(r, i, j);
-            a += M::to_f32(sE[r][j]) * M::to_f32(sK[r][j]) * kk;
-            pp += in_g(r0, r, j) * in_q(r0, r, j) * kk;
+            const float kk = ldv(kb, gi(r0 + i, j)) * pair_factor(r, i, j);
+            const uint32_t orj = gi(r0 + r, j);
+            a += ldv(eb, orj) * ldv(kb, orj) * kk;
+            pp += ldv(gb, orj) * ldv(qb, orj) * kk;
           }
         }
         sAw[r][i] = i < r ? a : 0.f;
@@ -437,68 +496,82 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void bwd_chunk_kernel(
     }
     __syncthreads();
     // Delta_I = T_II (U_I - X_I S_I)
-    f32x4 Dl;
+    f32x4 Dl[NT];
     {
-      f32x4 xs = zero4();
+      f32x4 xs[NT];
 #pragma unroll
-      for (int s = 0; s < RT; ++s) xs = M::mma(M::load(&sRowA[c16][16 * s + 4 * g]), M::from_f32(S[s]), xs);
-      f32x4 rhs = load4(&sU[colv][4 * g]);
-      rhs -= xs;
-      Dl = M::mma(M::load(&sT[c16][4 * g]), M::from_f32(rhs), zero4());
+      for (int n = 0; n < NT; ++n) xs[n] = zero4();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const TC dt = M::cvt(Dl[i]);
-        sDL[4 * g + i][colv] = dt;
-        gDel[static_cast<size_t>(r0 + 4 * g + i) * DV + colv] = dt;
+      for (int s = 0; s < RT; ++s) {
+        const frag xa = M::load(&sRowA[c16][16 * s + 4 * g]);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) xs[n] = M::mma(xa, M::from_f32(S[s][n]), xs[n]);
+      }
+      const frag ta = M::load(&sT[c16][4 * g]);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        f32x4 rhs = load4(&sU[colv(n)][4 * g]);
+        rhs -= xs[n];
+        Dl[n] = M::mma(ta, M::from_f32(rhs), zero4());
+        store_rows(Dl[n], sDL, gDel + static_cast<size_t>(r0) * DV, 16 * (NT * wave + n));
       }
     }
     __syncthreads();
     if (wave == 0) leaf_dot(sDO, sDL, false, sLf[0]);  // dO_r . Delta_i, i <= r
     // d(qt)_r = exp(Lam_r - B_I) [ S_I dO_r + sum_{i<=r} (dO_r . Delta_i) Z_i ]
-    f32x4 acc = state_rows(S, sDO);
+    f32x4 acc[NT];
+    state_rows(S, sDO, acc);
     if (safe) {
       f32x4 lf;
 #pragma unroll
       for (int i = 0; i < 4; ++i) lf[i] = sLf[0][c16][4 * g + i];
-      acc = M::mma(M::from_f32(lf), M::load(&sTZ[colv][4 * g]), acc);
+      const frag lff = M::from_f32(lf);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n] = M::mma(lff, M::load(&sTZ[colv(n)][4 * g]), acc[n]);
     }
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int r = 4 * g + ii;
-      const int j = colv;
-      float val = sF[r][j] * acc[ii];
-      if (!safe)
-        for (int i2 = 0; i2 <= r; ++i2) val += sLf[0][r][i2] * pair_factor(r, i2, j) * M::to_f32(sK[i2][j]);
-      const float qq = LEAN ? qcur[ii] : in_q(r0, r, j);
-      const float gg = LEAN ? gcur[ii] : in_g(r0, r, j);
-      const size_t gi = gidx(r0 + r, j);
-      dq[gi] = gg * val;
-      dgamma[gi] = qq * val;
-      dlog_a[gi] = gg * qq * val;
-    }
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int r = 4 * g + ii;
+        const int j = colv(n);
+        float val = sF[r][j] * acc[n][ii];
+        if (!safe)
+          for (int i2 = 0; i2 <= r; ++i2) val += sLf[0][r][i2] * pair_factor(r, i2, j) * ldv(kb, gi(r0 + i2, j));
+        const float qq = qcur[n][ii];
+        const float gg = gcur[n][ii];
+        const uint32_t o = gi(r0 + r, j);
+        *at(dqb, o) = gg * val;
+        *at(dgb, o) = qq * val;
+        *at(dlb, o) = gg * qq * val;
+      }
     // S_{I+1} = diag(exp(B_{I+1} - B_I)) S_I + Ke_I^T Delta_I
-    {
-      const frag df = M::from_f32(Dl);
 #pragma unroll
-      for (int s = 0; s < RT; ++s) decay_update(S, s, M::load(&sTA[16 * s + c16][4 * g]), df);
+    for (int s = 0; s < RT; ++s) {
+      const frag ka = M::load(&sTA[16 * s + c16][4 * g]);
+      const f32x4 gs = decay_scale(s);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) S[s][n] = M::mma(ka, M::from_f32(Dl[n]), S[s][n] * gs);
     }
     __syncthreads();
   }
 
   // ================= R: reverse sweep: dR, d(k) ==================
-  f32x4 D[RT];
+  f32x4 D[RT][NT];
   load_state(D, dSC);
 #pragma unroll 1
   for (int J = NB - 1; J >= 0; --J) {
     const int r0 = 16 * J;
     const int st = NB + (NB - 1 - J);
     const int safe = commit(st);
-    float vcur[4], wcur[4];
+    float vcur[NT][4], wcur[NT][4];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      vcur[ii] = pvv[ii];
-      wcur[ii] = pww[ii];
-    }
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        vcur[n][ii] = oa[n][ii];
+        wcur[n][ii] = ob[n][ii];
+      }
     prefetch(st + 1);
     frag ptf, ttf;
     {
@@ -512,32 +585,45 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void bwd_chunk_kernel(
       ttf = M::from_f32(tv);
     }
     // dR_J = T_JJ^T (Ke_J D + P_JJ^T dO_J)
-    f32x4 acc = zero4();
+    f32x4 dRn[NT];
+    frag dOf[NT];
+    {
+      f32x4 acc[NT];
 #pragma unroll
-    for (int s = 0; s < RT; ++s) acc = M::mma(M::load(&sRowA[c16][16 * s + 4 * g]), M::from_f32(D[s]), acc);
-    f32x4 dov;
+      for (int n = 0; n < NT; ++n) acc[n] = zero4();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dov[i] = M::to_f32(sDO[4 * g + i][colv]);
-    const frag dOf = M::from_f32(dov);
-    acc = M::mma(ptf, dOf, acc);
-    const f32x4 dRn = M::mma(ttf, M::from_f32(acc), zero4());
-    // dR rows replace the delta gradient tile; deltas of this block stay in sDL
-    __syncthreads();  // all waves are done reading sU-overlapping data of the step before
+      for (int s = 0; s < RT; ++s) {
+        const frag ka = M::load(&sRowA[c16][16 * s + 4 * g]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * g + i;
-      const TC dt = M::cvt(dRn[i]);
-      sDR[r][colv] = dt;
-      gdR[static_cast<size_t>(r0 + r) * DV + colv] = dt;
-      const size_t gi = gidx(r0 + r, colv);
-      dwrite[gi] = vcur[i] * dRn[i];
-      dv[gi] = wcur[i] * dRn[i];
+        for (int n = 0; n < NT; ++n) acc[n] = M::mma(ka, M::from_f32(D[s][n]), acc[n]);
+      }
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        f32x4 dov;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dov[i] = M::to_f32(sDO[4 * g + i][colv(n)]);
+        dOf[n] = M::from_f32(dov);
+        acc[n] = M::mma(ptf, dOf[n], acc[n]);
+        dRn[n] = M::mma(ttf, M::from_f32(acc[n]), zero4());
+      }
+    }
+    // dR rows take the place of the step before's (write*v)^T tile
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      store_rows(dRn[n], sDR, gdR + static_cast<size_t>(r0) * DV, 16 * (NT * wave + n));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t o = gi(r0 + 4 * g + i, colv(n));
+        *at(dwb, o) = vcur[n][i] * dRn[n][i];
+        *at(dvb, o) = wcur[n][i] * dRn[n][i];
+      }
     }
     __syncthreads();
     if (wave == 0) leaf_dot(sDO, sDL, false, sLf[0]);      // dO_r . Delta_i, r >= i
     if (wave == 1 % NW) leaf_dot(sDR, sDL, true, sLf[1]);  // dR_r . Delta_i, r > i
     // d(k)_i = exp(B_{J+1} - Lam_i) [ D Delta_i + sum_{r>=i} (dO_r.Delta_i) Yhat_r - sum_{r>i} (dR_r.Delta_i) Xhat_r ]
-    f32x4 acc2 = state_rows(D, sDL);
+    f32x4 acc2[NT];
+    state_rows(D, sDL, acc2);
     if (safe) {
       f32x4 l1, l2;
 #pragma unroll
@@ -545,31 +631,46 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void bwd_chunk_kernel(
         l1[i] = sLf[0][4 * g + i][c16];
         l2[i] = -sLf[1][4 * g + i][c16];
       }
-      acc2 = M::mma(M::from_f32(l1), M::load(&sTY[colv][4 * g]), acc2);
-      acc2 = M::mma(M::from_f32(l2), M::load(&sTZ[colv][4 * g]), acc2);
+      const frag l1f = M::from_f32(l1), l2f = M::from_f32(l2);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        acc2[n] = M::mma(l1f, M::load(&sTY[colv(n)][4 * g]), acc2[n]);
+        acc2[n] = M::mma(l2f, M::load(&sTZ[colv(n)][4 * g]), acc2[n]);
+      }
     }
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int i = 4 * g + ii;
-      const int j = colv;
-      float val = sF[i][j] * acc2[ii];
-      if (!safe)
-        for (int r = i; r < 16; ++r) {
-          const float f = pair_factor(r, i, j);
-          const float qt = in_g(r0, r, j) * in_q(r0, r, j);
-          const float ek = M::to_f32(sE[r][j]) * M::to_f32(sK[r][j]);
-          val += f * (sLf[0][r][i] * qt - sLf[1][r][i] * ek);
-        }
-      dk[gidx(r0 + i, j)] = val;
-      if (J == 0) pdk[ii] = val;  // the next step (F2, block 0) reads it from here
-    }
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = 4 * g + ii;
+        const int j = colv(n);
+        float val = sF[i][j] * acc2[n][ii];
+        if (!safe)
+          for (int r = i; r < 16; ++r) {
+            const float f = pair_factor(r, i, j);
+            const uint32_t orj = gi(r0 + r, j);
+            const float qt = ldv(gb, orj) * ldv(qb, orj);
+            const float ek = ldv(eb, orj) * ldv(kb, orj);
+            val += f * (sLf[0][r][i] * qt - sLf[1][r][i] * ek);
+          }
+        *at(dkb, gi(r0 + i, j)) = val;
+        if (J == 0) oc[n][ii] = val;  // F2's block 0 reads it from here
+      }
     // D <- diag(exp(B_{J+1} - B_J)) D + Y_J^T dO_J - X_J^T dR_J
     {
-      const frag dRf = M::from_f32(-dRn);
+      frag dRf[NT];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) dRf[n] = M::from_f32(-dRn[n]);
 #pragma unroll
       for (int s = 0; s < RT; ++s) {
-        decay_update(D, s, M::load(&sTB[16 * s + c16][4 * g]), dOf);
-        D[s] = M::mma(M::load(&sTA[16 * s + c16][4 * g]), dRf, D[s]);
+        const frag ya = M::load(&sTB[16 * s + c16][4 * g]);
+        const frag xa = M::load(&sTA[16 * s + c16][4 * g]);
+        const f32x4 gs = decay_scale(s);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const f32x4 t = M::mma(ya, dOf[n], D[s][n] * gs);
+          D[s][n] = M::mma(xa, dRf[n], t);
+        }
       }
     }
     __syncthreads();
@@ -577,66 +678,85 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void bwd_chunk_kernel(
 
   // ================= F2: forward sweep: d(ek), totals ==================
   load_state(S, S0c);
-  float prefix = 0.f;  // sum of dLam over the finished blocks, channel colv
+  float prefix[NT];  // sum of dLam over the finished blocks, channel colv(n)
+#pragma unroll
+  for (int n = 0; n < NT; ++n) prefix[n] = 0.f;
 #pragma unroll 1
   for (int I = 0; I < NB; ++I) {
     const int r0 = 16 * I;
     const int st = 2 * NB + I;
     const int safe = commit(st);
-    float dkcur[4], dlcur[4];
+    float kcur[NT][4], ecur[NT][4], dkcur[NT][4], dlcur[NT][4];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      dkcur[ii] = pdk[ii];
-      dlcur[ii] = pdla[ii];
-    }
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        kcur[n][ii] = oa[n][ii];
+        ecur[n][ii] = ob[n][ii];
+        dkcur[n][ii] = oc[n][ii];
+        dlcur[n][ii] = od[n][ii];
+      }
     prefetch(st + 1);
     if (wave == 0) leaf_dot(sDR, sDL, true, sLf[1]);  // dR_r . Delta_i, i < r
-    f32x4 acc = state_rows(S, sDR);
+    f32x4 acc[NT];
+    state_rows(S, sDR, acc);
     if (safe) {
       f32x4 lf;
 #pragma unroll
       for (int i = 0; i < 4; ++i) lf[i] = sLf[1][c16][4 * g + i];
-      acc = M::mma(M::from_f32(lf), M::load(&sTZ[colv][4 * g]), acc);
-    }
-    float dl[4];
+      const frag lff = M::from_f32(lf);
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int r = 4 * g + ii;
-      const int j = colv;
-      float val = sF[r][j] * acc[ii];
-      if (!safe)
-        for (int i2 = 0; i2 < r; ++i2) val += sLf[1][r][i2] * pair_factor(r, i2, j) * M::to_f32(sK[i2][j]);
-      const float dek = -val;  // d(ek)_r = -S'_r dR_r
-      const float kj = M::to_f32(sK[r][j]);
-      const float bj = M::to_f32(sE[r][j]);
-      const size_t gi = gidx(r0 + r, j);
-      derase[gi] = kj * dek;
-      dk[gi] = dkcur[ii] + bj * dek;
-      dl[ii] = dlcur[ii] - kj * dkcur[ii] + bj * kj * dek;
+      for (int n = 0; n < NT; ++n) acc[n] = M::mma(lff, M::load(&sTZ[colv(n)][4 * g]), acc[n]);
     }
-    // exclusive prefix of dLam over the chunk, in token order
-    {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int j = colv(n);
+      float dl[4];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int r = 4 * g + ii;
+        float val = sF[r][j] * acc[n][ii];
+        if (!safe)
+          for (int i2 = 0; i2 < r; ++i2) val += sLf[1][r][i2] * pair_factor(r, i2, j) * ldv(kb, gi(r0 + i2, j));
+        const float dek = -val;  // d(ek)_r = -S'_r dR_r
+        const float kj = kcur[n][ii];
+        const float bj = ecur[n][ii];
+        const uint32_t o = gi(r0 + r, j);
+        *at(deb, o) = kj * dek;
+        *at(dkb, o) = dkcur[n][ii] + bj * dek;
+        dl[ii] = dlcur[n][ii] - kj * dkcur[n][ii] + bj * kj * dek;
+      }
+      // exclusive prefix of dLam over the chunk, in token order
       const float tsum = dl[0] + dl[1] + dl[2] + dl[3];
       const float t0 = __shfl(tsum, c16, 64);
       const float t1 = __shfl(tsum, c16 + 16, 64);
       const float t2 = __shfl(tsum, c16 + 32, 64);
       const float t3 = __shfl(tsum, c16 + 48, 64);
-      float run = prefix + (g > 0 ? t0 : 0.f) + (g > 1 ? t1 : 0.f) + (g > 2 ? t2 : 0.f);
+      float run = prefix[n] + (g > 0 ? t0 : 0.f) + (g > 1 ? t1 : 0.f) + (g > 2 ? t2 : 0.f);
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        dlog_a[gidx(r0 + 4 * g + ii, colv)] = run;
+        *at(dlb, gi(r0 + 4 * g + ii, j)) = run;
         run += dl[ii];
       }
-      prefix += t0 + t1 + t2 + t3;
+      prefix[n] += t0 + t1 + t2 + t3;
     }
     // S_{I+1} = diag(g_I) S_I + Ke_I^T Delta_I
     {
-      f32x4 dlt;
+      frag df[NT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dlt[i] = M::to_f32(sDL[4 * g + i][colv]);
-      const frag df = M::from_f32(dlt);
+      for (int n = 0; n < NT; ++n) {
+        f32x4 dlt;
 #pragma unroll
-      for (int s = 0; s < RT; ++s) decay_update(S, s, M::load(&sTA[16 * s + c16][4 * g]), df);
+        for (int i = 0; i < 4; ++i) dlt[i] = M::to_f32(sDL[4 * g + i][colv(n)]);
+        df[n] = M::from_f32(dlt);
+      }
+#pragma unroll
+      for (int s = 0; s < RT; ++s) {
+        const frag ka = M::load(&sTA[16 * s + c16][4 * g]);
+        const f32x4 gs = decay_scale(s);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) S[s][n] = M::mma(ka, df[n], S[s][n] * gs);
+      }
     }
     __syncthreads();
   }
@@ -646,7 +766,9 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void bwd_chunk_kernel(
   for (int s = 0; s < RT; ++s)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float a = S[s][i] * dSC[static_cast<size_t>(16 * s + 4 * g + i) * DV + colv];
+      float a = 0.f;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) a += S[s][n][i] * *at(dSC, static_cast<uint32_t>((16 * s + 4 * g + i) * DV + colv(n)));
       a += __shfl_xor(a, 1, 64);
       a += __shfl_xor(a, 2, 64);
       a += __shfl_xor(a, 4, 64);
@@ -655,17 +777,20 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void bwd_chunk_kernel(
     }
   __syncthreads();
   if (g == 0) {
-    float tot = prefix;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) tot += sRow[w][colv];
-    sTot[colv] = tot;
+    for (int n = 0; n < NT; ++n) {
+      float tot = prefix[n];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) tot += sRow[w][colv(n)];
+      sTot[colv(n)] = tot;
+    }
   }
   __syncthreads();
   for (int idx = tid; idx < C * DK; idx += NTH) {
     const int r = idx / DK;
     const int j = idx - r * DK;
-    const size_t gi = gidx(r, j);
-    dlog_a[gi] = sTot[j] - dlog_a[gi];
+    const uint32_t o = gi(r, j);
+    *at(dlb, o) = sTot[j] - *at(dlb, o);
   }
 }
 
@@ -683,23 +808,24 @@ hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, c
                             hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(s.nchunks());
   if (grid == 0) return hipSuccess;
-#define MUIR_BCH1(TT, DD, CC)                                                                      \
-  hipLaunchKernelGGL((bwd_chunk_kernel<TT, DD, CC>), dim3(grid), dim3((2 * DD / 32) * 64), 0,      \
-                     stream, s.T, s.H, (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, \
-                     (const TT*)erase, (const TT*)write, (const TT*)gamma, S_chunks, dS_chunks,    \
-                     (const TT*)dO, dq, dk, dv, dlog_a, derase, dwrite, dgamma, (char*)scratch)
-#define MUIR_BCH(TT, DD)                         \
-  do {                                           \
-    if (s.C == 64) MUIR_BCH1(TT, DD, 64);        \
-    else if (s.C == 128) MUIR_BCH1(TT, DD, 128); \
-    else MUIR_BCH1(TT, DD, 256);                 \
+#define MUIR_BCH1(TT, DD, CC, NW)                                                                  \
+  hipLaunchKernelGGL((bwd_chunk_kernel<TT, DD, CC, NW>), dim3(grid), dim3(64 * NW), 0, stream, s.T, s.H, \
+                     (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, (const TT*)erase,      \
+                     (const TT*)write, (const TT*)gamma, S_chunks, dS_chunks, (const TT*)dO, dq, dk,   \
+                     dv, dlog_a, derase, dwrite, dgamma, (char*)scratch)
+#define MUIR_BCH(TT, DD, NW)                         \
+  do {                                               \
+    if (s.C == 64) MUIR_BCH1(TT, DD, 64, NW);        \
+    else if (s.C == 128) MUIR_BCH1(TT, DD, 128, NW); \
+    else MUIR_BCH1(TT, DD, 256, NW);                 \
   } while (0)
+  // one 16-column tile per wave: 8 waves at d = 128, 4 at d = 64
   if (s.bf16) {
-    if (s.DK == 128) MUIR_BCH(uint16_t, 128);
-    else MUIR_BCH(uint16_t, 64);
+    if (s.DK == 128) MUIR_BCH(uint16_t, 128, 8);
+    else MUIR_BCH(uint16_t, 64, 4);
   } else {
-    if (s.DK == 128) MUIR_BCH(float, 128);
-    else MUIR_BCH(float, 64);
+    if (s.DK == 128) MUIR_BCH(float, 128, 8);
+    else MUIR_BCH(float, 64, 4);
   }
 #undef MUIR_BCH
 #undef MUIR_BCH1

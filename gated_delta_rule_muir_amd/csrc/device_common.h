@@ -51,6 +51,22 @@ template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
+// Element access through a workgroup-uniform base pointer and a 32-bit element
+// index: the address is formed as scalar base + 32-bit vector offset, so no
+// per-lane 64-bit address arithmetic is needed.  The caller keeps
+// index * sizeof(T) below 2^32.
+template <typename T> __device__ __forceinline__ const T* at(const T* base, uint32_t i) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + i * static_cast<uint32_t>(sizeof(T)));
+}
+template <typename T> __device__ __forceinline__ T* at(T* base, uint32_t i) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + i * static_cast<uint32_t>(sizeof(T)));
+}
+template <typename T> __device__ __forceinline__ float ldv(const T* base, uint32_t i) {
+  return Elem<T>::load(at(base, i), 0);
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ i16x4 pack4(f32x4 v) {
   return __builtin_bit_cast(i16x4, __builtin_convertvector(v, bf16x4));
 }
