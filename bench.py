@@ -17,10 +17,17 @@ Beside it the line carries:
                 streaming decode step (64 streams x 16 heads, 4096 steps)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+`roofline.traffic` is the dominant kernel's measured HBM bytes per launch,
+read from profiles/traffic_<kernel>_<workload>.json (FETCH_SIZE and WRITE_SIZE
+counter runs, each scaled by the same counter over a copy of known size, see
+--calib-copy); it is null when the library sources have changed since those
+counters were taken (the record holds their SHA-256).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -54,6 +61,47 @@ def step_flops(d: int, C: int):
     fwd = 5 * C * d + C * C / 3 + 6 * d * d
     bwd = 12 * C * d + C * C / 3 + 14 * d * d
     return fwd, bwd
+
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "gated_delta_rule_muir_amd", "csrc")
+
+
+def library_sources_sha256() -> str:
+    """SHA-256 over the HIP library's sources (file names and contents, sorted)."""
+    h = hashlib.sha256()
+    for fn in sorted(os.listdir(CSRC)):
+        if fn.endswith((".hip", ".h")):
+            h.update(fn.encode())
+            with open(os.path.join(CSRC, fn), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """Counter-measured HBM bytes per launch of `kernel`, or None if there is
+    no record or the library changed since it was taken."""
+    path = os.path.join(HERE, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("sources_sha256") != library_sources_sha256():
+        return None
+    return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+
+
+def calib_copy(torch, mib: int = 1024, reps: int = 3):
+    """A plain elementwise copy of known size (reads and writes `mib` MiB per
+    launch) whose counter readings calibrate FETCH_SIZE / WRITE_SIZE."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def gen_seq(B, T, H, d, dtype, decay, seed, torch, muir_inputs):
@@ -187,6 +235,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=4096)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run a 1 GiB elementwise copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the operator runs on one MI355X); --gpus {args.gpus} "
@@ -202,6 +252,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     names = ("q", "k", "v", "log_a", "erase", "write", "gamma")
+    if args.calib_copy:
+        log("[bench] calibration copy: 3 x 1 GiB read + 1 GiB write")
+        calib_copy(torch)
 
     wl = muir_inputs.WORKLOADS["layer_fwdbwd_4k"]
     B, T, H, d, C = wl.B, wl.T, wl.H, wl.dk, wl.chunk
@@ -222,7 +275,7 @@ def main():
     dom = max(kern, key=lambda k: kern[k])
     fwd_f, bwd_f = step_flops(d, C)
     step_bytes = (kb["fwd_prep"] + kb["fwd_scan"] + kb["bwd_prep"] + kb["bwd_scan"] + kb["bwd_chunk"]) * nth
-    traffic = None
+    traffic = measured_traffic(dom, wl.name)
     roof = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GBs"], "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": kernels[dom]["GBs"] / HBM_PEAK_GBS, "traffic": traffic,
             "alg_bytes_per_launch": kb[dom] * nth, "avg_launch_us": kernels[dom]["avg_us"]}
