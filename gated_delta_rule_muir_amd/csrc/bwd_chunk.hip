@@ -190,57 +190,55 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   // MFMA-output mapping (token 4g+i, column colv(n)):
   //   F1: q, gamma   R: v, write   F2: k, erase, partial d(k), partial dLam
   float oa[NT][4], ob[NT][4], oc[NT][4], od[NT][4];
+  float dk0[NT][4];  // partial d(k) of block 0, from R's last step
 
+  // Every slot is loaded on every step, from a sweep-dependent (uniform) base;
+  // slots a sweep does not use re-read k or the scratch.  No load sits under a
+  // branch, so the loads stay in flight until the step that consumes them.
   auto prefetch = [&](int s) {
     if (s >= NSTEP) return;
     const int sw = step_sweep(s);
     const int I = step_block(s);
     const int r0 = 16 * I;
+    const Tin* pe = sw != 2 ? eb : kb;
+    const Tin* pq = sw != 2 ? qb : kb;
+    const Tin* pg = sw != 2 ? gb : kb;
+    const Tin* pw = sw == 0 ? wb : kb;
+    const Tin* pv = sw == 0 ? vb : kb;
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr) {
       const uint32_t o = gi(r0 + RPT * part + rr, ej);
       xl[rr] = ldv(lb, o);
       xk[rr] = ldv(kb, o);
-      xe[rr] = sw != 2 ? ldv(eb, o) : 0.f;
-      xq[rr] = sw != 2 ? ldv(qb, o) : 0.f;
-      xg[rr] = sw != 2 ? ldv(gb, o) : 0.f;
-      xw[rr] = sw == 0 ? ldv(wb, o) : 0.f;
-      xv[rr] = sw == 0 ? ldv(vb, o) : 0.f;
+      xe[rr] = ldv(pe, o);
+      xq[rr] = ldv(pq, o);
+      xg[rr] = ldv(pg, o);
+      xw[rr] = ldv(pw, o);
+      xv[rr] = ldv(pv, o);
     }
-    const bool ldl = (sw == 1 && I != NB - 1) || (sw == 2 && I != 0);
-    const bool ldr = sw == 2 && I != 0;
-    const u32x2 zw = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < RW; ++e) {
       const int col = pc0 + e * EPW;
       const uint32_t so = static_cast<uint32_t>(r0 + prow) * DV + col;
-      rdo[e] = sw != 2 ? *reinterpret_cast<const u32x2*>(at(dOb, gi(r0 + prow, col))) : zw;
-      // deltas: not for F1; R's first block and F2's first block find them in
-      // LDS, left by the step before
-      rdl[e] = ldl ? *reinterpret_cast<const u32x2*>(at(gDel, so)) : zw;
-      rdr[e] = ldr ? *reinterpret_cast<const u32x2*>(at(gdR, so)) : zw;
+      rdo[e] = *reinterpret_cast<const u32x2*>(at(dOb, gi(r0 + prow, col)));
+      // deltas and their gradients: used by R (all but its first block) and
+      // F2 (all but its first block); those find them in LDS
+      rdl[e] = *reinterpret_cast<const u32x2*>(at(gDel, so));
+      rdr[e] = *reinterpret_cast<const u32x2*>(at(gdR, so));
     }
-    rtp = (sw == 1 && I != NB - 1 && tid < TPW)
-              ? *reinterpret_cast<const u32x2*>(at(gTP, static_cast<uint32_t>(I * 512 + tid * EPW)))
-              : zw;
+    rtp = *reinterpret_cast<const u32x2*>(
+        at(gTP, static_cast<uint32_t>(I * 512 + (tid < TPW ? tid : TPW - 1) * EPW)));
+    const Tin* poa = sw == 0 ? qb : (sw == 1 ? vb : kb);
+    const Tin* pob = sw == 0 ? gb : (sw == 1 ? wb : eb);
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const uint32_t o = gi(r0 + 4 * g + ii, colv(n));
-        if (sw == 0) {
-          oa[n][ii] = ldv(qb, o);
-          ob[n][ii] = ldv(gb, o);
-        } else if (sw == 1) {
-          oa[n][ii] = ldv(vb, o);
-          ob[n][ii] = ldv(wb, o);
-        } else {
-          oa[n][ii] = ldv(kb, o);
-          ob[n][ii] = ldv(eb, o);
-        }
-        // F2's block 0: the partial d(k) is still in registers from R's last step
-        oc[n][ii] = (sw == 2 && I != 0) ? *at(dkb, o) : 0.f;
-        od[n][ii] = sw == 2 ? *at(dlb, o) : 0.f;
+        oa[n][ii] = ldv(poa, o);
+        ob[n][ii] = ldv(pob, o);
+        oc[n][ii] = *at(dkb, o);  // F2: partial d(k) (block 0: kept in registers)
+        od[n][ii] = *at(dlb, o);  // F2: partial dLam
       }
   };
 
@@ -559,6 +557,17 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   // ================= R: reverse sweep: dR, d(k) ==================
   f32x4 D[RT][NT];
   load_state(D, dSC);
+  // chunk-end term rowsum(S_C * dS_C): S holds S_C here and D holds dS_C
+#pragma unroll
+  for (int s = 0; s < RT; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float a = 0.f;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) a += S[s][n][i] * D[s][n][i];
+      a = sum16(a);
+      if (c16 == 0) sRow[wave][16 * s + 4 * g + i] = a;
+    }
 #pragma unroll 1
   for (int J = NB - 1; J >= 0; --J) {
     const int r0 = 16 * J;
@@ -654,7 +663,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
             val += f * (sLf[0][r][i] * qt - sLf[1][r][i] * ek);
           }
         *at(dkb, gi(r0 + i, j)) = val;
-        if (J == 0) oc[n][ii] = val;  // F2's block 0 reads it from here
+        if (J == 0) dk0[n][ii] = val;  // F2's block 0 reads it from here
       }
     // D <- diag(exp(B_{J+1} - B_J)) D + Y_J^T dO_J - X_J^T dR_J
     {
@@ -693,7 +702,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       for (int ii = 0; ii < 4; ++ii) {
         kcur[n][ii] = oa[n][ii];
         ecur[n][ii] = ob[n][ii];
-        dkcur[n][ii] = oc[n][ii];
+        dkcur[n][ii] = I != 0 ? oc[n][ii] : dk0[n][ii];
         dlcur[n][ii] = od[n][ii];
       }
     prefetch(st + 1);
@@ -761,21 +770,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     __syncthreads();
   }
 
-  // ---- chunk-end term rowsum(S_C * dS_C); dlog_a_i = total - exclusive prefix ----
-#pragma unroll
-  for (int s = 0; s < RT; ++s)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float a = 0.f;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) a += S[s][n][i] * *at(dSC, static_cast<uint32_t>((16 * s + 4 * g + i) * DV + colv(n)));
-      a += __shfl_xor(a, 1, 64);
-      a += __shfl_xor(a, 2, 64);
-      a += __shfl_xor(a, 4, 64);
-      a += __shfl_xor(a, 8, 64);
-      if (c16 == 0) sRow[wave][16 * s + 4 * g + i] = a;
-    }
-  __syncthreads();
+  // ---- dlog_a_i = total - exclusive prefix (total includes rowsum(S_C * dS_C)) ----
   if (g == 0) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
@@ -786,11 +781,22 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < C * DK; idx += NTH) {
-    const int r = idx / DK;
-    const int j = idx - r * DK;
-    const uint32_t o = gi(r, j);
-    *at(dlb, o) = sTot[j] - *at(dlb, o);
+  constexpr int FPT = C * DK / NTH;  // elements per thread
+  constexpr int FB = FPT < 8 ? FPT : 8;
+  static_assert(FPT % FB == 0, "final pass batches");
+#pragma unroll 1
+  for (int b0 = 0; b0 < FPT; b0 += FB) {
+    float x[FB];
+#pragma unroll
+    for (int u = 0; u < FB; ++u) {
+      const int idx = tid + (b0 + u) * NTH;
+      x[u] = *at(dlb, gi(idx / DK, idx % DK));
+    }
+#pragma unroll
+    for (int u = 0; u < FB; ++u) {
+      const int idx = tid + (b0 + u) * NTH;
+      *at(dlb, gi(idx / DK, idx % DK)) = sTot[idx % DK] - x[u];
+    }
   }
 }
 

@@ -108,6 +108,19 @@ __device__ __forceinline__ f32x4 zero4() {
   return z;
 }
 
+// Sum over each row of 16 lanes (the result in all 16), with DPP moves:
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  return v;
+}
+
 // Reductions over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
