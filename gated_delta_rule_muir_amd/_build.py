@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmuir.so")
-SOURCES = ["muir_api.hip", "step.hip", "fwd.hip", "bwd.hip", "bwd_chunk.hip"]
+SOURCES = ["muir_api.hip", "step.hip", "fwd.hip", "scan.hip", "bwd_chunk.hip"]
 ARCH = "gfx950"
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,

@@ -1,7 +1,7 @@
 // Per-chunk gradients of the Muir gated delta rule (gfx950).
 //
 // One workgroup per chunk gets the chunk's initial state S0 and the gradient
-// dS_C of its end state (from the reverse scan in bwd.hip) and forms every
+// dS_C of its end state (from the reverse scan in scan.hip) and forms every
 // input gradient with three sweeps over the chunk's 16-token blocks, with the
 // block-boundary pivots of the forward (fwd.hip):
 //   F1 (forward): Delta_I = T_II (U_I - X_I S_I), S_{I+1} = g_I S_I + Ke_I^T Delta_I,

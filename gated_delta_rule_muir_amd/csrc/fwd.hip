@@ -27,9 +27,8 @@
 // exp(Lam_r - Lam_i), r >= i, and T_II = (I + A_II)^-1 is the exact Neumann
 // product (I - A)(I + A^2)(I + A^4)(I + A^8) (A_II^16 = 0).
 //
-// Kernel 2 (fwd_scan) walks the chunks of one (b, h) in order; each wave owns
-// 16 value columns of S (fp32, held in MFMA accumulators) and applies the
-// three products above per chunk.
+// The sequential scan over chunks (o and the chunk states from the summary)
+// is in scan.hip.
 #include "chunk_common.h"
 #include "kernels.h"
 #include "mma.h"
@@ -361,130 +360,6 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
   }
 }
 
-constexpr int SCAN_SB = 64;  // tokens staged per step of the scan
-
-template <typename Tin, int DK, int NW>
-__global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
-    int T, int H, int C, const char* __restrict__ summ, size_t summ_bytes,
-    const float* __restrict__ S0, Tin* __restrict__ o, float* __restrict__ S_chunks,
-    float* __restrict__ S_T) {
-  typedef Tin TC;
-  typedef MM<TC> M;
-  typedef typename M::frag frag;
-  constexpr int DV = DK;
-  constexpr int RT = DK / 16;
-  constexpr int NV = 16 * NW;
-  constexpr int PW = DK + 4;
-  constexpr int PK = SCAN_SB + 4;
-
-  const int NC = T / C;
-  const int nvb = DV / NV;
-  const int bh = blockIdx.x / nvb;
-  const int vb = blockIdx.x - bh * nvb;
-  const int b = bh / H;
-  const int h = bh - b * H;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int g = lane >> 4;
-  const int c16 = lane & 15;
-  const int colg = vb * NV + 16 * wave + c16;
-
-  __shared__ __attribute__((aligned(16))) TC sW[SCAN_SB][PW];
-  __shared__ __attribute__((aligned(16))) TC sQ[SCAN_SB][PW];
-  __shared__ __attribute__((aligned(16))) TC sKb[DK][PK];
-  __shared__ float sgC[DK];
-
-  const size_t sbase = static_cast<size_t>(bh) * DK * DV;
-  f32x4 S[RT];
-#pragma unroll
-  for (int s = 0; s < RT; ++s)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      S[s][i] = S0 ? S0[sbase + static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] : 0.f;
-
-  for (int c = 0; c < NC; ++c) {
-    char* base = const_cast<char*>(summ) + (static_cast<size_t>(bh) * NC + c) * summ_bytes;
-    SummaryView<TC> sv(base, C, DK, DV);
-    if (S_chunks) {
-      float* dst = S_chunks + (static_cast<size_t>(bh) * NC + c) * DK * DV;
-#pragma unroll
-      for (int s = 0; s < RT; ++s)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] = S[s][i];
-    }
-    frag Sf[RT];
-#pragma unroll
-    for (int s = 0; s < RT; ++s) Sf[s] = M::from_f32(S[s]);
-    f32x4 dS[RT];
-#pragma unroll
-    for (int s = 0; s < RT; ++s) dS[s] = zero4();
-
-    for (int sb = 0; sb < C; sb += SCAN_SB) {
-      __syncthreads();
-      for (int idx = tid; idx < SCAN_SB * DK / 4; idx += 64 * NW) {
-        const int r = idx / (DK / 4);
-        const int j4 = (idx - r * (DK / 4)) * 4;
-        const f32x4 wv = load4(sv.W + static_cast<size_t>(sb + r) * DK + j4);
-        const f32x4 qv = load4(sv.Qp + static_cast<size_t>(sb + r) * DK + j4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sW[r][j4 + i] = M::cvt(wv[i]);
-          sQ[r][j4 + i] = M::cvt(qv[i]);
-        }
-      }
-      for (int idx = tid; idx < DK * SCAN_SB / 4; idx += 64 * NW) {
-        const int j = idx / (SCAN_SB / 4);
-        const int r4 = (idx - j * (SCAN_SB / 4)) * 4;
-        const f32x4 kv = load4(sv.KbT + static_cast<size_t>(j) * C + sb + r4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sKb[j][r4 + i] = M::cvt(kv[i]);
-      }
-      if (sb == 0)
-        for (int j = tid; j < DK; j += 64 * NW) sgC[j] = sv.gC[j];
-      __syncthreads();
-#pragma unroll 1
-      for (int m = 0; m < SCAN_SB / 16; ++m) {
-        f32x4 Oa = zero4(), Da = zero4();
-#pragma unroll
-        for (int s = 0; s < RT; ++s) {
-          const frag qa = M::load(&sQ[16 * m + c16][16 * s + 4 * g]);
-          const frag wa = M::load(&sW[16 * m + c16][16 * s + 4 * g]);
-          Oa = M::mma(qa, Sf[s], Oa);
-          Da = M::mma(wa, Sf[s], Da);
-        }
-        const int tok = sb + 16 * m + 4 * g;  // chunk-local token of element i = 0
-        const f32x4 ot = load4(sv.OtT + static_cast<size_t>(colg) * C + tok);
-        const f32x4 ut = load4(sv.UtT + static_cast<size_t>(colg) * C + tok);
-        if (o) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const size_t oi =
-                ((static_cast<size_t>(b) * T + static_cast<size_t>(c) * C + tok + i) * H + h) * DV + colg;
-            Elem<Tin>::store(o, oi, Oa[i] + ot[i]);
-          }
-        }
-        const frag df = M::from_f32(ut - Da);
-#pragma unroll
-        for (int s = 0; s < RT; ++s) {
-          const frag ka = M::load(&sKb[16 * s + c16][16 * m + 4 * g]);
-          dS[s] = M::mma(ka, df, dS[s]);
-        }
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < RT; ++s)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[s][i] = sgC[16 * s + 4 * g + i] * S[s][i] + dS[s][i];
-  }
-  if (S_T) {
-#pragma unroll
-    for (int s = 0; s < RT; ++s)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S_T[sbase + static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] = S[s][i];
-  }
-}
-
 }  // namespace
 
 hipError_t launch_fwd_prep(const ChunkShape& s, const void* q, const void* k, const void* v,
@@ -518,34 +393,6 @@ hipError_t launch_fwd_prep(const ChunkShape& s, const void* q, const void* k, co
 #undef MUIR_PREP
 #undef MUIR_PREP1
 #undef MUIR_PREP2
-  return hipGetLastError();
-}
-
-hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S0, void* o,
-                           float* S_chunks, float* S_T, hipStream_t stream) {
-  const int heads = s.B * s.H;
-  if (heads == 0) return hipSuccess;
-  // Four waves (64 columns) per workgroup when that still fills the chip,
-  // else one wave (16 columns) per workgroup for more independent chains.
-  const bool wide = static_cast<long long>(heads) * (s.DV / 64) >= 256;
-#define MUIR_SCAN(TT, DD, NW)                                                                      \
-  hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, NW>), dim3(heads * (s.DV / (16 * NW))),              \
-                     dim3(64 * NW), 0, stream, s.T, s.H, s.C, (const char*)summ, s.summary_bytes(), \
-                     S0, (TT*)o, S_chunks, S_T)
-  if (s.bf16) {
-    if (s.DK == 128) {
-      if (wide) MUIR_SCAN(uint16_t, 128, 4); else MUIR_SCAN(uint16_t, 128, 1);
-    } else {
-      if (wide) MUIR_SCAN(uint16_t, 64, 4); else MUIR_SCAN(uint16_t, 64, 1);
-    }
-  } else {
-    if (s.DK == 128) {
-      if (wide) MUIR_SCAN(float, 128, 4); else MUIR_SCAN(float, 128, 1);
-    } else {
-      if (wide) MUIR_SCAN(float, 64, 4); else MUIR_SCAN(float, 64, 1);
-    }
-  }
-#undef MUIR_SCAN
   return hipGetLastError();
 }
 
