@@ -47,12 +47,12 @@ def log(*a):
 # read and write by construction -- its inputs and outputs, not its re-reads.
 def kernel_bytes(d: int, C: int, e: int = 2):
     st = 4 * d * d / C  # one fp32 state per chunk, per token
+    lf = 2 * 256 * e / 16  # the leaf blocks T_II, P_II (16 x 16 each per 16 tokens)
     return {
-        "fwd_prep": 7 * d * e + 5 * d * e,              # 7 inputs -> W, Q', Kbar, U~, O~
+        "fwd_prep": 7 * d * e + 8 * d * e + lf,         # 7 inputs -> W, Q', Kbar (both ways), U~, O~, leaves
         "fwd_scan": 5 * d * e + d * e + st,             # summary -> o, chunk states
-        "bwd_prep": 7 * d * e + 3 * d * e,              # 7 inputs -> W, Q', Kbar
-        "bwd_scan": 3 * d * e + d * e + st,             # summary, dO -> chunk-end state grads
-        "bwd_chunk": 7 * d * e + d * e + 2 * st + 7 * d * 4,  # inputs, dO, S, dS -> 7 fp32 grads
+        "bwd_scan": 3 * d * e + d * e + st,             # W, Q', Kbar, dO -> chunk-end state grads
+        "bwd_chunk": 7 * d * e + d * e + lf + 2 * st + 7 * d * 4,  # inputs, dO, leaves, S, dS -> 7 fp32 grads
     }
 
 
@@ -119,13 +119,13 @@ def time_fwdbwd(m, dv, C, steps, warmup, torch, hiprt, names, profile=True):
 
     def step():
         o, S_T, Sc = m.muir_chunk_fwd(*args, chunk=C, save_states=True, workspace=fws)
-        g = m.muir_chunk_bwd(*args, dv["dO"], S_chunks=Sc, chunk=C, workspace=bws)
+        g = m.muir_chunk_bwd(*args, dv["dO"], S_chunks=Sc, summaries=fws, chunk=C, workspace=bws)
         return o, g
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    per_step = 3 + 4  # events: fwd (before, prep, scan), bwd (before, prep, bscan, bchunk)
+    per_step = 3 + 3  # events: fwd (before, prep, scan), bwd (before, bscan, bchunk)
     pool = hiprt.EventPool(per_step * steps) if profile else None
     if pool is not None:
         m.muir_set_profile_events(pool.arr, pool.n)
@@ -141,7 +141,7 @@ def time_fwdbwd(m, dv, C, steps, warmup, torch, hiprt, names, profile=True):
         m.muir_set_profile_events(None)
         if rec != per_step * steps:
             raise RuntimeError(f"expected {per_step * steps} profile events, got {rec}")
-        names_k = ["fwd_prep", "fwd_scan", None, "bwd_prep", "bwd_scan", "bwd_chunk"]
+        names_k = ["fwd_prep", "fwd_scan", None, "bwd_scan", "bwd_chunk"]
         acc = {k: 0.0 for k in names_k if k}
         for s in range(steps):
             base = s * per_step
@@ -274,7 +274,7 @@ def main():
                        "hbm_frac": byt / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
     dom = max(kern, key=lambda k: kern[k])
     fwd_f, bwd_f = step_flops(d, C)
-    step_bytes = (kb["fwd_prep"] + kb["fwd_scan"] + kb["bwd_prep"] + kb["bwd_scan"] + kb["bwd_chunk"]) * nth
+    step_bytes = sum(kb.values()) * nth
     traffic = measured_traffic(dom, wl.name)
     roof = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GBs"], "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": kernels[dom]["GBs"] / HBM_PEAK_GBS, "traffic": traffic,
@@ -285,7 +285,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "dk": d, "dv": d, "chunk": C,
                    "inputs": "bf16, seeded (muir_inputs), per-channel decay rates 1e-4..3",
-                   "step": "muir_chunk_fwd (saving chunk states) + muir_chunk_bwd"},
+                   "step": "muir_chunk_fwd (saving chunk states; its workspace keeps the chunk "
+                           "summaries) + muir_chunk_bwd (reusing both)"},
         "roofline": roof,
         "kernels": kernels,
         "step_model": {"alg_bytes": step_bytes, "alg_GBs": step_bytes / (ms * 1e-3) / 1e9,

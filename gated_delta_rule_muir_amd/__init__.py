@@ -69,7 +69,7 @@ def lib():
         L.muir_chunk_bwd_workspace.restype = SZ
         L.muir_chunk_fwd.argtypes = [D] + [P] * 7 + [P, P, P, P] + [P, SZ, P]
         L.muir_chunk_fwd.restype = ctypes.c_int
-        L.muir_chunk_bwd.argtypes = [D] + [P] * 7 + [P, P, P, P] + [P] * 8 + [P, SZ, P]
+        L.muir_chunk_bwd.argtypes = [D] + [P] * 7 + [P, P, P, P, P] + [P] * 8 + [P, SZ, P]
         L.muir_chunk_bwd.restype = ctypes.c_int
         L.muir_step.argtypes = [I32] * 5 + [P] * 7 + [P, P, P]
         L.muir_step.restype = ctypes.c_int
@@ -171,9 +171,14 @@ def muir_chunk_fwd(q, k, v, log_a, erase, write, gamma, S0=None, *, chunk: int =
 
 
 def muir_chunk_bwd(q, k, v, log_a, erase, write, gamma, dO, S0=None, S_chunks=None, dS_T=None, *,
-                   chunk: int = 64, workspace: Optional[torch.Tensor] = None, want_dS0: bool = True):
+                   chunk: int = 64, summaries: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, want_dS0: bool = True):
     """Chunkwise backward.  Returns a dict of fp32 gradients
-    (dq, dk, dv, dlog_a, derase, dwrite, dgamma, dS0)."""
+    (dq, dk, dv, dlog_a, derase, dwrite, dgamma, dS0).
+
+    `S_chunks` (from muir_chunk_fwd(save_states=True)) and `summaries` (the
+    `workspace` tensor of that forward call, left unchanged) are saved forward
+    results; each one that is None is recomputed inside."""
     B, T, H, dk = q.shape
     dv = v.shape[3]
     dev, dt = q.device, q.dtype
@@ -188,6 +193,11 @@ def muir_chunk_bwd(q, k, v, log_a, erase, write, gamma, dO, S0=None, S_chunks=No
         _check_io("dS_T", dS_T, (B, H, dk, dv), torch.float32, dev)
     if S_chunks is not None:
         _check_io("S_chunks", S_chunks, (B, H, T // chunk, dk, dv), torch.float32, dev)
+    if summaries is not None:
+        need = muir_chunk_fwd_workspace(B, T, H, dk, dv, chunk, code)
+        if (not summaries.is_cuda or summaries.device != dev or not summaries.is_contiguous()
+                or summaries.numel() * summaries.element_size() < need):
+            raise ValueError(f"summaries: expected the forward workspace ({need} bytes on {dev})")
     f32 = dict(dtype=torch.float32, device=dev)
     g = {n: torch.empty((B, T, H, dk), **f32) for n in ("dq", "dk", "dlog_a", "derase", "dgamma")}
     g.update({n: torch.empty((B, T, H, dv), **f32) for n in ("dv", "dwrite")})
@@ -196,7 +206,7 @@ def muir_chunk_bwd(q, k, v, log_a, erase, write, gamma, dO, S0=None, S_chunks=No
     nbytes = int(lib().muir_chunk_bwd_workspace(ctypes.byref(d)))
     ws = _workspace(nbytes, dev, workspace)
     rc = lib().muir_chunk_bwd(ctypes.byref(d), *(_ptr(t) for t in (q, k, v, log_a, erase, write, gamma)),
-                              _ptr(S0), _ptr(S_chunks), _ptr(dO), _ptr(dS_T),
+                              _ptr(S0), _ptr(S_chunks), _ptr(summaries), _ptr(dO), _ptr(dS_T),
                               *(_ptr(g[n]) for n in ("dq", "dk", "dv", "dlog_a", "derase", "dwrite",
                                                      "dgamma", "dS0")),
                               _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))

@@ -38,11 +38,11 @@ namespace muir {
 
 namespace {
 
-// Per-chunk scratch: deltas [C][DV] and their gradients [C][DV], then T_II and
-// P_II of every 16-token block as [16][16], all in the compute type.
+// Per-chunk scratch: deltas [C][DV] and their gradients [C][DV], in the
+// compute type.
 template <typename TC>
 __host__ __device__ constexpr size_t bwd_scratch_bytes_tc(int C, int DV) {
-  return (static_cast<size_t>(2) * C * DV + static_cast<size_t>(C / 16) * 512) * sizeof(TC);
+  return static_cast<size_t>(2) * C * DV * sizeof(TC);
 }
 
 // LDS row padding (elements) that keeps 16 lanes reading 4 consecutive
@@ -53,9 +53,10 @@ template <typename Tin, int DK, int C, int NW>
 __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     int T, int H, const Tin* __restrict__ q, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ log_a, const Tin* __restrict__ erase,
-    const Tin* __restrict__ write, const Tin* __restrict__ gamma,
-    const float* __restrict__ S_chunks, const float* __restrict__ dS_chunks,
-    const Tin* __restrict__ dO, float* __restrict__ dq, float* __restrict__ dk,
+    const Tin* __restrict__ write, const Tin* __restrict__ gamma, const char* __restrict__ summ,
+    size_t summ_bytes, size_t tp_offset, const float* __restrict__ S_chunks,
+    const float* __restrict__ dS_chunks, const Tin* __restrict__ dO, float* __restrict__ dq,
+    float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ dlog_a, float* __restrict__ derase,
     float* __restrict__ dwrite, float* __restrict__ dgamma, char* __restrict__ scratch) {
   typedef Tin TC;
@@ -124,28 +125,24 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   auto gi = [&](int t, int j) -> uint32_t { return static_cast<uint32_t>(t) * HD + static_cast<uint32_t>(j); };
   TC* gDel = reinterpret_cast<TC*>(scratch + static_cast<size_t>(chunk) * bwd_scratch_bytes_tc<TC>(C, DV));
   TC* gdR = gDel + static_cast<size_t>(C) * DV;
-  TC* gTP = gdR + static_cast<size_t>(C) * DV;  // [NB][2][16][16]
+  // T_II, P_II of the chunk's blocks, from the chunk summary, [NB][2][16][16]
+  const TC* gTP = reinterpret_cast<const TC*>(summ + static_cast<size_t>(chunk) * summ_bytes + tp_offset);
   const float* S0c = S_chunks + static_cast<size_t>(chunk) * DK * DV;
   const float* dSC = dS_chunks + static_cast<size_t>(chunk) * DK * DV;
 
-  constexpr int UNI = 16 * PT > DK * TP ? 16 * PT : DK * TP;
   constexpr int UNU = DV * TP > 16 * PV ? DV * TP : 16 * PV;
   __shared__ float sBsum[NB][DK];                            // sum of log_a over block I
   __shared__ float sTmp[TPC][DK];
   __shared__ float sF[16][DK + 1];                           // per-element factor of the sweep
   __shared__ float sLam[16][DK + 1];                         // log_a of a steep block (per-pair leaves)
   __shared__ __attribute__((aligned(16))) TC sRowA[16][PT];  // F1: X rows   R: Ke rows
-  __shared__ __attribute__((aligned(16))) TC sUn1[UNI];      // F1: Y rows   R: Y^T
-  __shared__ __attribute__((aligned(16))) TC sUn2[UNI];      // F1: Z rows   R: Yhat^T
+  __shared__ __attribute__((aligned(16))) TC sTB[DK][TP];    // R: Y^T
+  __shared__ __attribute__((aligned(16))) TC sTY[DK][TP];    // R: Yhat^T
   __shared__ __attribute__((aligned(16))) TC sTA[DK][TP];    // F1, F2: Ke^T   R: X^T
   __shared__ __attribute__((aligned(16))) TC sTZ[DK][TP];    // F1, F2: Z^T    R: Xhat^T
   __shared__ __attribute__((aligned(16))) TC sUnU[UNU];      // F1: (write*v)^T   R, F2: dR rows
   __shared__ __attribute__((aligned(16))) TC sDO[16][PV];    // dO rows of the block
   __shared__ __attribute__((aligned(16))) TC sDL[16][PV];    // delta rows of the block
-  __shared__ float sAw[16][17];
-  __shared__ float sPw[16][17];
-  __shared__ float sTw[16][17];
-  __shared__ float sPf[16][17];
   __shared__ __attribute__((aligned(16))) TC sT[16][TP];     // T_II of the block
   __shared__ __attribute__((aligned(16))) TC sP[16][TP];     // P_II of the block
   __shared__ __attribute__((aligned(16))) TC sSD[DK][PS];    // staged S or D columns, [dk][dv]
@@ -153,10 +150,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   __shared__ float sG[DK];
   __shared__ float sRow[NW][DK];
   __shared__ float sTot[DK];
-  TC (*sRowB)[PT] = reinterpret_cast<TC (*)[PT]>(sUn1);
-  TC (*sRowZ)[PT] = reinterpret_cast<TC (*)[PT]>(sUn2);
-  TC (*sTB)[TP] = reinterpret_cast<TC (*)[TP]>(sUn1);
-  TC (*sTY)[TP] = reinterpret_cast<TC (*)[TP]>(sUn2);
   TC (*sU)[TP] = reinterpret_cast<TC (*)[TP]>(sUnU);
   TC (*sDR)[PV] = reinterpret_cast<TC (*)[PV]>(sUnU);
 
@@ -186,7 +179,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   float xl[RPT], xk[RPT], xe[RPT], xq[RPT], xg[RPT], xw[RPT], xv[RPT];
   // row tiles (row prow, columns pc0..): dO, deltas, their gradients (raw words)
   u32x2 rdo[RW], rdl[RW], rdr[RW];
-  u32x2 rtp;  // one word of the block's T_II, P_II (threads < TPW)
+  u32x2 rtp;  // one word of the block's T_II, P_II (threads < TPW; F1 and R)
   // MFMA-output mapping (token 4g+i, column colv(n)):
   //   F1: q, gamma   R: v, write   F2: k, erase, partial d(k), partial dLam
   float oa[NT][4], ob[NT][4], oc[NT][4], od[NT][4];
@@ -243,8 +236,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   };
 
   // Commit the prefetched step into LDS and form the block's factor tiles.
-  // F1: sF = exp(Lam - B_I); X, Y, Z rows; Ke^T, Z^T, U^T
-  // R:  sF = exp(B_{I+1} - Lam); Ke rows; X^T, Y^T, Xhat^T, Yhat^T
+  // F1: sF = exp(Lam - B_I); X rows; Ke^T, Z^T, U^T; T_II, P_II
+  // R:  sF = exp(B_{I+1} - Lam); Ke rows; X^T, Y^T, Xhat^T, Yhat^T; T_II, P_II
   // F2: sF = exp(Lam - B_I); Ke^T, Z^T
   // X = ek exp(Lam - B_I), Y = qt exp(Lam - B_I), Ke = k exp(B_{I+1} - Lam),
   // Z = k exp(B_I - Lam), Xhat = ek exp(Lam - B_{I+1}), Yhat = qt exp(Lam - B_{I+1});
@@ -292,13 +285,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         const float qt = xg[rr] * xq[rr];
         if (!safe) sLam[r][ej] = xl[rr];
         if (sw == 0) {
-          const float z = safe ? xk[rr] * __expf(-loc) : 0.f;
           sF[r][ej] = fs;
           sRowA[r][ej] = M::cvt(ek * fs);
-          sRowB[r][ej] = M::cvt(qt * fs);
-          sRowZ[r][ej] = M::cvt(z);
           tA[q4] = xk[rr] * fe;
-          tZ[q4] = z;
+          tZ[q4] = safe ? xk[rr] * __expf(-loc) : 0.f;
           tB[q4] = xw[rr] * xv[rr];
         } else if (sw == 1) {
           const float ie = safe ? __expf(-suf) : 0.f;
@@ -330,7 +320,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       if ((sw == 1 && I != NB - 1) || (sw == 2 && I != 0)) *reinterpret_cast<u32x2*>(&sDL[prow][col]) = rdl[e];
       if (sw == 2 && I != 0) *reinterpret_cast<u32x2*>(&sDR[prow][col]) = rdr[e];
     }
-    if (sw == 1 && I != NB - 1 && tid < TPW) {
+    if (sw != 2 && tid < TPW) {
       const int e0 = tid * EPW;
       TC* dst = e0 < 256 ? &sT[e0 >> 4][e0 & 15] : &sP[(e0 - 256) >> 4][e0 & 15];
       *reinterpret_cast<u32x2*>(dst) = rtp;
@@ -443,56 +433,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         gcur[n][ii] = ob[n][ii];
       }
     prefetch(I + 1);
-    // leaf A_II, P_II, T_II (also kept in the scratch for the reverse sweep)
-    if (safe) {
-      if (wave == 0) {
-        f32x4 a = zero4(), pp = zero4();
-#pragma unroll
-        for (int s = 0; s < RT; ++s) {
-          const frag zb = M::load(&sRowZ[c16][16 * s + 4 * g]);
-          a = M::mma(M::load(&sRowA[c16][16 * s + 4 * g]), zb, a);
-          pp = M::mma(M::load(&sRowB[c16][16 * s + 4 * g]), zb, pp);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g + i;
-          sAw[r][c16] = c16 < r ? a[i] : 0.f;
-          sPf[r][c16] = c16 <= r ? pp[i] : 0.f;
-        }
-      }
-    } else {
-      for (int pr = tid; pr < 256; pr += NTH) {
-        const int r = pr >> 4;
-        const int i = pr & 15;
-        float a = 0.f, pp = 0.f;
-        if (i <= r) {
-          for (int j = 0; j < DK; ++j) {
-            const float kk = ldv(kb, gi(r0 + i, j)) * pair_factor(r, i, j);
-            const uint32_t orj = gi(r0 + r, j);
-            a += ldv(eb, orj) * ldv(kb, orj) * kk;
-            pp += ldv(gb, orj) * ldv(qb, orj) * kk;
-          }
-        }
-        sAw[r][i] = i < r ? a : 0.f;
-        sPf[r][i] = pp;
-      }
-      __syncthreads();
-    }
-    if (wave == 0) {
-      const f32x4 t = neumann16(sAw, sPw, sTw);
-      TC* tp = gTP + static_cast<size_t>(I) * 512;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g + i;
-        const TC tv = M::cvt(t[i]);
-        const TC pv = M::cvt(sPf[r][c16]);
-        sT[r][c16] = tv;
-        sP[r][c16] = pv;
-        tp[r * 16 + c16] = tv;
-        tp[256 + r * 16 + c16] = pv;
-      }
-    }
-    __syncthreads();
     // Delta_I = T_II (U_I - X_I S_I)
     f32x4 Dl[NT];
     {
@@ -808,8 +748,9 @@ size_t bwd_chunk_scratch_bytes(const ChunkShape& s) {
 
 hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, const void* v,
                             const void* log_a, const void* erase, const void* write,
-                            const void* gamma, const float* S_chunks, const float* dS_chunks,
-                            const void* dO, float* dq, float* dk, float* dv, float* dlog_a,
+                            const void* gamma, const void* summ, const float* S_chunks,
+                            const float* dS_chunks, const void* dO, float* dq, float* dk, float* dv,
+                            float* dlog_a,
                             float* derase, float* dwrite, float* dgamma, void* scratch,
                             hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(s.nchunks());
@@ -817,8 +758,9 @@ hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, c
 #define MUIR_BCH1(TT, DD, CC, NW)                                                                  \
   hipLaunchKernelGGL((bwd_chunk_kernel<TT, DD, CC, NW>), dim3(grid), dim3(64 * NW), 0, stream, s.T, s.H, \
                      (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, (const TT*)erase,      \
-                     (const TT*)write, (const TT*)gamma, S_chunks, dS_chunks, (const TT*)dO, dq, dk,   \
-                     dv, dlog_a, derase, dwrite, dgamma, (char*)scratch)
+                     (const TT*)write, (const TT*)gamma, (const char*)summ, s.summary_bytes(),          \
+                     s.tp_offset(), S_chunks, dS_chunks, (const TT*)dO, dq, dk, dv, dlog_a, derase,     \
+                     dwrite, dgamma, (char*)scratch)
 #define MUIR_BCH(TT, DD, NW)                         \
   do {                                               \
     if (s.C == 64) MUIR_BCH1(TT, DD, 64, NW);        \

@@ -44,24 +44,30 @@ struct SummaryView {
   TC* KbT;   // [DK][C]
   TC* UtT;   // [DV][C]
   TC* OtT;   // [DV][C]
+  TC* Wt;    // [DK][C]
+  TC* Qt;    // [DK][C]
+  TC* Kb;    // [C][DK]
   float* gC; // [DK]
+  TC* TP;    // [C/16][2][16][16]: T_II, P_II of each 16-token block
   __device__ SummaryView(char* base, int C, int DK, int DV) {
-    W = reinterpret_cast<TC*>(base);
-    Qp = W + static_cast<size_t>(C) * DK;
-    KbT = Qp + static_cast<size_t>(C) * DK;
-    UtT = KbT + static_cast<size_t>(C) * DK;
-    OtT = UtT + static_cast<size_t>(C) * DV;
-    gC = reinterpret_cast<float*>(OtT + static_cast<size_t>(C) * DV);
+    TC* b = reinterpret_cast<TC*>(base);
+    W = b + summary_part(SP_W, C, DK, DV);
+    Qp = b + summary_part(SP_QP, C, DK, DV);
+    KbT = b + summary_part(SP_KBT, C, DK, DV);
+    UtT = b + summary_part(SP_UTT, C, DK, DV);
+    OtT = b + summary_part(SP_OTT, C, DK, DV);
+    Wt = b + summary_part(SP_WT, C, DK, DV);
+    Qt = b + summary_part(SP_QT, C, DK, DV);
+    Kb = b + summary_part(SP_KB, C, DK, DV);
+    gC = reinterpret_cast<float*>(b + summary_part(SP_END, C, DK, DV));
+    TP = reinterpret_cast<TC*>(gC + DK);
   }
 };
 
-// BWDL selects the summary layout the backward scan reads: W and Q' as
-// [DK][C] (token-contiguous), Kbar as [C][DK]; U~ and O~ are not written.
-//
 // Work split: NW = (DK + DV) / 32 waves; wave w owns columns [32w, 32w + 32)
 // of the inner state [U~ | W].  For the elementwise work each thread owns one
 // key channel and 4 consecutive tokens of the current block.
-template <typename Tin, int DK, int C, bool BWDL>
+template <typename Tin, int DK, int C>
 __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
     int T, int H, const Tin* __restrict__ q, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ log_a, const Tin* __restrict__ erase,
@@ -96,8 +102,17 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
   const int part = tid / DK;     // elementwise: tokens 4*part .. 4*part+3 of the block
 
   SummaryView<TC> out(summ + static_cast<size_t>(chunk) * summ_bytes, C, DK, DV);
-  const size_t rowbase = (static_cast<size_t>(b) * T + static_cast<size_t>(c) * C) * H + h;
-  auto gidx = [&](int t, int j) -> size_t { return (rowbase + static_cast<size_t>(t) * H) * DK + j; };
+  // workgroup-uniform bases of the chunk; element (t, j) is at t * HD + j
+  const size_t ebase = ((static_cast<size_t>(b) * T + static_cast<size_t>(c) * C) * H + h) * DK;
+  const uint32_t HD = static_cast<uint32_t>(H) * DK;
+  const Tin* qb = q + ebase;
+  const Tin* kb = k + ebase;
+  const Tin* vb = v + ebase;
+  const Tin* lb = log_a + ebase;
+  const Tin* eb = erase + ebase;
+  const Tin* wb = write + ebase;
+  const Tin* gb = gamma + ebase;
+  auto gi = [&](int t, int j) -> uint32_t { return static_cast<uint32_t>(t) * HD + static_cast<uint32_t>(j); };
 
   __shared__ float sB[NB + 1][DK];     // B_I = Lam at the end of block I-1 (B_0 = 0)
   __shared__ float sBsum[NB][DK];      // sum of log_a over block I  (= B_{I+1} - B_I)
@@ -117,14 +132,14 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
   __shared__ __attribute__((aligned(16))) TC sT[16][20];
   __shared__ __attribute__((aligned(16))) TC sP[16][20];
   __shared__ float sG[DK];
-  __shared__ __attribute__((aligned(16))) TC sStage[BWDL ? 1 : 16][2 * DK + 8];
+  __shared__ __attribute__((aligned(16))) TC sStage[16][2 * DK + 8];
 
   // ---- block sums of the log-decay and their prefix/suffix sums ----
 #pragma unroll
   for (int I = part; I < NB; I += TPC) {
     float sacc = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) sacc += Elem<Tin>::load(log_a, gidx(16 * I + rr, ej));
+    for (int rr = 0; rr < 16; ++rr) sacc += ldv(lb, gi(16 * I + rr, ej));
     sBsum[I][ej] = sacc;
   }
   __syncthreads();
@@ -152,6 +167,24 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
 #pragma unroll
     for (int n = 0; n < NT; ++n) Hs[s][n] = zero4();
 
+  // ---- the next block's inputs are loaded one block ahead (4 tokens of
+  // channel ej); no load is under a branch, so they stay in flight ----
+  float pk[4], pe[4], pq[4], pg[4], pv[4], pw[4], pl[4];
+  auto prefetch = [&](int I) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const uint32_t o = gi(16 * I + 4 * part + rr, ej);
+      pk[rr] = ldv(kb, o);
+      pe[rr] = ldv(eb, o);
+      pq[rr] = ldv(qb, o);
+      pg[rr] = ldv(gb, o);
+      pv[rr] = ldv(vb, o);
+      pw[rr] = ldv(wb, o);
+      pl[rr] = ldv(lb, o);
+    }
+  };
+  prefetch(0);
+
 #pragma unroll 1
   for (int I = 0; I < NB; ++I) {
     const int r0 = 16 * I;
@@ -159,15 +192,15 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
     float kv[4], ev[4], qv[4], gv[4], vv[4], wv[4], lv[4];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const size_t gi = gidx(r0 + 4 * part + rr, ej);
-      kv[rr] = Elem<Tin>::load(k, gi);
-      ev[rr] = Elem<Tin>::load(erase, gi);
-      qv[rr] = Elem<Tin>::load(q, gi);
-      gv[rr] = Elem<Tin>::load(gamma, gi);
-      vv[rr] = Elem<Tin>::load(v, gi);
-      wv[rr] = Elem<Tin>::load(write, gi);
-      lv[rr] = Elem<Tin>::load(log_a, gi);
+      kv[rr] = pk[rr];
+      ev[rr] = pe[rr];
+      qv[rr] = pq[rr];
+      gv[rr] = pg[rr];
+      vv[rr] = pv[rr];
+      wv[rr] = pw[rr];
+      lv[rr] = pl[rr];
     }
+    prefetch(I + 1 < NB ? I + 1 : I);
     // direct partial sums (never differences of cumulative sums): prefix of
     // the block up to and including each token, and suffix after it
     float cs[4], sf[4];
@@ -206,7 +239,7 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
       const float kb = __expf(suf + bsuf1);    // exp(Lam_C - Lam_r)
       const float ek = ev[rr] * kv[rr];
       const float qt = gv[rr] * qv[rr];
-      sL[r][ej] = lv[rr];
+      if (!safe) sL[r][ej] = lv[rr];
       sX[r][ej] = M::cvt(ek * fs);
       sY[r][ej] = M::cvt(qt * fs);
       sZ[r][ej] = M::cvt(safe ? kv[rr] * __expf(-loc) : 0.f);
@@ -220,13 +253,9 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
     store4(&sR[ej][4 * part], uT);
     store4(&sR[DV + ej][4 * part], ktT);
     store4(&sQh[ej][4 * part], qhT);
-    if (BWDL) {
+    store4(out.KbT + static_cast<size_t>(ej) * C + r0 + 4 * part, kbT);
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        out.KbT[static_cast<size_t>(r0 + 4 * part + rr) * DK + ej] = M::cvt(kbT[rr]);
-    } else {
-      store4(out.KbT + static_cast<size_t>(ej) * C + r0 + 4 * part, kbT);
-    }
+    for (int rr = 0; rr < 4; ++rr) out.Kb[static_cast<size_t>(r0 + 4 * part + rr) * DK + ej] = M::cvt(kbT[rr]);
     __syncthreads();
 
     // ---- X H and Y H for this wave's columns ----
@@ -274,12 +303,12 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
         float a = 0.f, p = 0.f;
         if (i <= r) {
           for (int j = 0; j < DK; ++j) {
-            const size_t gr = gidx(r0 + r, j), gq = gidx(r0 + i, j);
+            const uint32_t gr = gi(r0 + r, j), gq = gi(r0 + i, j);
             float ls = 0.f;
             for (int x = i + 1; x <= r; ++x) ls += sL[x][j];
-            const float kk = Elem<Tin>::load(k, gq) * __expf(ls);
-            a += Elem<Tin>::load(erase, gr) * Elem<Tin>::load(k, gr) * kk;
-            p += Elem<Tin>::load(gamma, gr) * Elem<Tin>::load(q, gr) * kk;
+            const float kk = ldv(kb, gq) * __expf(ls);
+            a += ldv(eb, gr) * ldv(kb, gr) * kk;
+            p += ldv(gb, gr) * ldv(qb, gr) * kk;
           }
         }
         sAw[r][i] = i < r ? a : 0.f;
@@ -289,10 +318,16 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
     }
     if (wave == 0) {
       const f32x4 t = neumann16(sAw, sPw, sTw);
+      TC* tp = out.TP + static_cast<size_t>(I) * 512;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sT[4 * g + i][c16] = M::cvt(t[i]);
-        sP[4 * g + i][c16] = M::cvt(sPf[4 * g + i][c16]);
+        const int r = 4 * g + i;
+        const TC tv = M::cvt(t[i]);
+        const TC pv = M::cvt(sPf[r][c16]);
+        sT[r][c16] = tv;
+        sP[r][c16] = pv;
+        tp[r * 16 + c16] = tv;  // kept for the backward
+        tp[256 + r * 16 + c16] = pv;
       }
     }
     __syncthreads();
@@ -309,22 +344,17 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
       const f32x4 op = M::mma(pa, M::from_f32(uw), YH[n]);
       UW[n] = uw;
       if (colg < DV) {
-        if (!BWDL) {
-          store4(out.UtT + static_cast<size_t>(colg) * C + r0 + 4 * g, uw);
-          store4(out.OtT + static_cast<size_t>(colg) * C + r0 + 4 * g, op);
-        }
+        store4(out.UtT + static_cast<size_t>(colg) * C + r0 + 4 * g, uw);
+        store4(out.OtT + static_cast<size_t>(colg) * C + r0 + 4 * g, op);
       } else {
         const int j = colg - DV;
         const f32x4 qv = load4(&sQh[j][4 * g]) - op;
-        if (BWDL) {
-          store4(out.W + static_cast<size_t>(j) * C + r0 + 4 * g, uw);
-          store4(out.Qp + static_cast<size_t>(j) * C + r0 + 4 * g, qv);
-        } else {
+        store4(out.Wt + static_cast<size_t>(j) * C + r0 + 4 * g, uw);
+        store4(out.Qt + static_cast<size_t>(j) * C + r0 + 4 * g, qv);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sStage[4 * g + i][j] = M::cvt(uw[i]);
-            sStage[4 * g + i][DK + j] = M::cvt(qv[i]);
-          }
+        for (int i = 0; i < 4; ++i) {
+          sStage[4 * g + i][j] = M::cvt(uw[i]);
+          sStage[4 * g + i][DK + j] = M::cvt(qv[i]);
         }
       }
     }
@@ -341,7 +371,7 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
       }
     }
     __syncthreads();
-    if (!BWDL) {
+    {
       // W and Q' rows of the block, 4 elements per store
       for (int idx = tid; idx < 16 * DK / 4; idx += NTH) {
         const int r = idx / (DK / 4);
@@ -364,24 +394,19 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
 
 hipError_t launch_fwd_prep(const ChunkShape& s, const void* q, const void* k, const void* v,
                            const void* log_a, const void* erase, const void* write,
-                           const void* gamma, void* summ, bool bwd_layout, hipStream_t stream) {
+                           const void* gamma, void* summ, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(s.nchunks());
   if (grid == 0) return hipSuccess;
-#define MUIR_PREP1(TT, DD, CC, BL)                                                                 \
-  hipLaunchKernelGGL((fwd_prep_kernel<TT, DD, CC, BL>), dim3(grid), dim3((2 * DD / 32) * 64), 0,     \
+#define MUIR_PREP1(TT, DD, CC)                                                                     \
+  hipLaunchKernelGGL((fwd_prep_kernel<TT, DD, CC>), dim3(grid), dim3((2 * DD / 32) * 64), 0,         \
                      stream, s.T, s.H, (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, \
                      (const TT*)erase, (const TT*)write, (const TT*)gamma, (char*)summ,            \
                      s.summary_bytes())
-#define MUIR_PREP2(TT, DD, CC)                   \
-  do {                                           \
-    if (bwd_layout) MUIR_PREP1(TT, DD, CC, true); \
-    else MUIR_PREP1(TT, DD, CC, false);           \
-  } while (0)
-#define MUIR_PREP(TT, DD)                               \
-  do {                                                  \
-    if (s.C == 64) MUIR_PREP2(TT, DD, 64);              \
-    else if (s.C == 128) MUIR_PREP2(TT, DD, 128);       \
-    else MUIR_PREP2(TT, DD, 256);                       \
+#define MUIR_PREP(TT, DD)                         \
+  do {                                            \
+    if (s.C == 64) MUIR_PREP1(TT, DD, 64);        \
+    else if (s.C == 128) MUIR_PREP1(TT, DD, 128); \
+    else MUIR_PREP1(TT, DD, 256);                 \
   } while (0)
   if (s.bf16) {
     if (s.DK == 128) MUIR_PREP(uint16_t, 128);
@@ -392,7 +417,6 @@ hipError_t launch_fwd_prep(const ChunkShape& s, const void* q, const void* k, co
   }
 #undef MUIR_PREP
 #undef MUIR_PREP1
-#undef MUIR_PREP2
   return hipGetLastError();
 }
 

@@ -7,6 +7,20 @@
 
 namespace muir {
 
+// Parts of a chunk summary, in order; offsets in compute-type elements.
+//   W [C][DK], Q' [C][DK], Kbar^T [DK][C], U~^T [DV][C], O~^T [DV][C],
+//   W^T [DK][C], Q'^T [DK][C], Kbar [C][DK]
+// (W, Q' and Kbar in both orientations: the forward scan contracts them over
+// key channels, the reverse scan over tokens), then Gamma_C [DK] fp32 and the
+// leaf blocks T_II, P_II [C/16][2][16][16] (compute type).
+enum SummaryPart { SP_W, SP_QP, SP_KBT, SP_UTT, SP_OTT, SP_WT, SP_QT, SP_KB, SP_END };
+__host__ __device__ constexpr size_t summary_part(int part, int C, int DK, int DV) {
+  return part <= SP_UTT ? static_cast<size_t>(part) * C * DK
+         : part <= SP_WT ? static_cast<size_t>(3) * C * DK + static_cast<size_t>(part - SP_UTT) * C * DV
+                         : static_cast<size_t>(3) * C * DK + static_cast<size_t>(2) * C * DV +
+                               static_cast<size_t>(part - SP_WT) * C * DK;
+}
+
 // Sizes and derived quantities of one chunkwise call, validated by the API.
 struct ChunkShape {
   int B, T, H, DK, DV, C;
@@ -14,12 +28,12 @@ struct ChunkShape {
   int NC() const { return T / C; }
   size_t nchunks() const { return static_cast<size_t>(B) * H * NC(); }
   size_t tc_bytes() const { return bf16 ? 2 : 4; }
-  // Per-chunk block of the forward intermediates ("chunk summary"):
-  //   W  [C][DK], Qp [C][DK], Kb^T [DK][C], Ut^T [DV][C], Ot^T [DV][C] (compute type)
-  //   gC [DK] fp32
-  size_t summary_elems() const { return static_cast<size_t>(C) * (3 * DK + 2 * DV); }
+  // Per-chunk block of the forward intermediates ("chunk summary"), see SummaryPart.
+  size_t summary_elems() const { return summary_part(SP_END, C, DK, DV); }
+  size_t gc_offset() const { return summary_elems() * tc_bytes(); }
+  size_t tp_offset() const { return gc_offset() + static_cast<size_t>(DK) * 4; }
   size_t summary_bytes() const {
-    size_t b = summary_elems() * tc_bytes() + static_cast<size_t>(DK) * 4;
+    size_t b = tp_offset() + static_cast<size_t>(C / 16) * 512 * tc_bytes();
     return (b + 255) & ~static_cast<size_t>(255);
   }
   size_t state_bytes() const { return static_cast<size_t>(DK) * DV * 4; }
@@ -29,12 +43,11 @@ hipError_t launch_step(int N, int H, int dk, int dv, bool bf16, const void* q, c
                        const void* v, const void* log_a, const void* erase, const void* write,
                        const void* gamma, float* S, void* o, hipStream_t stream);
 
-// Chunk-parallel: per chunk summary (W, Q', Kbar, U~, O~, Gamma_C) into `summ`.
-// bwd_layout: W, Q' token-contiguous and Kbar channel-contiguous (what the
-// backward scan reads); U~ and O~ are then not written.
+// Chunk-parallel: per chunk summary (W, Q', Kbar, U~, O~, Gamma_C and the
+// 16-token leaf blocks T_II, P_II) into `summ`.
 hipError_t launch_fwd_prep(const ChunkShape& s, const void* q, const void* k, const void* v,
                            const void* log_a, const void* erase, const void* write,
-                           const void* gamma, void* summ, bool bwd_layout, hipStream_t stream);
+                           const void* gamma, void* summ, hipStream_t stream);
 
 // Sequential over chunks: o (may be NULL), S_chunks (may be NULL), S_T (may be NULL).
 hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S0, void* o,
@@ -45,13 +58,14 @@ hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S
 hipError_t launch_bwd_scan(const ChunkShape& s, const void* summ, const void* dO,
                            const float* dS_T, float* dS_chunks, float* dS0, hipStream_t stream);
 
-// Chunk-parallel: all input gradients of every chunk.  `scratch` holds
-// bwd_chunk_scratch_bytes(s) per chunk (the chunk's deltas, their gradients
-// and its leaf inverses).
+// Chunk-parallel: all input gradients of every chunk.  `summ` holds the
+// chunk summaries (their leaf blocks are read); `scratch` holds
+// bwd_chunk_scratch_bytes(s) per chunk (the chunk's deltas and their gradients).
 size_t bwd_chunk_scratch_bytes(const ChunkShape& s);
 hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, const void* v,
                             const void* log_a, const void* erase, const void* write,
-                            const void* gamma, const float* S_chunks, const float* dS_chunks,
+                            const void* gamma, const void* summ, const float* S_chunks,
+                            const float* dS_chunks,
                             const void* dO, float* dq, float* dk, float* dv, float* dlog_a,
                             float* derase, float* dwrite, float* dgamma, void* scratch,
                             hipStream_t stream);

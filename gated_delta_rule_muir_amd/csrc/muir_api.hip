@@ -20,6 +20,8 @@ muir_status_t check_dims(const muir_dims_t* d, ChunkShape* s) {
   if (d->T % d->chunk != 0) return MUIR_ERR_SHAPE;
   // keep every flat index inside 32-bit chunk counts and 64-bit element counts
   if (static_cast<long long>(d->B) * d->H * (d->T / d->chunk) > (1LL << 30)) return MUIR_ERR_SHAPE;
+  // the kernels address one chunk of a [B, T, H, D] tensor with 32-bit offsets
+  if (static_cast<long long>(d->H) * d->dk * d->chunk * 4 >= (1LL << 31)) return MUIR_ERR_SHAPE;
   s->B = d->B;
   s->T = d->T;
   s->H = d->H;
@@ -32,10 +34,11 @@ muir_status_t check_dims(const muir_dims_t* d, ChunkShape* s) {
 
 size_t fwd_ws(const ChunkShape& s) { return s.nchunks() * s.summary_bytes(); }
 
-// Backward workspace: chunk summaries, recomputed chunk states (only used when
-// the caller passes no S_chunks; always reserved so the size does not depend
-// on a pointer), the chunk-end state gradients, and per-chunk scratch for the
-// deltas and their gradients (2 * C * dv fp32).
+// Backward workspace: chunk summaries (used when the caller passes none),
+// recomputed chunk states (used when the caller passes no S_chunks), the
+// chunk-end state gradients, and per-chunk scratch for the deltas and their
+// gradients.  Every part is always reserved, so the size does not depend on
+// which pointers are passed.
 size_t bwd_scratch_bytes(const ChunkShape& s) {
   return (muir::bwd_chunk_scratch_bytes(s) + 255) & ~static_cast<size_t>(255);
 }
@@ -74,7 +77,7 @@ hipError_t copy_or_zero(float* dst, const float* src, size_t n, hipStream_t s) {
 
 extern "C" {
 
-int32_t muir_abi_version(void) { return 1; }
+int32_t muir_abi_version(void) { return 2; }
 
 int32_t muir_set_profile_events(void** events, int32_t count) {
   if (count < 0 || (count > 0 && !events)) return MUIR_ERR_NULL;
@@ -142,8 +145,7 @@ muir_status_t muir_chunk_fwd(const muir_dims_t* dims, const void* q, const void*
     return MUIR_OK;
   }
   mark(hs);
-  if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, workspace, false, hs) !=
-      hipSuccess)
+  if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, workspace, hs) != hipSuccess)
     return MUIR_ERR_HIP;
   mark(hs);
   if (muir::launch_fwd_scan(s, workspace, S0, o, S_chunks, S_T, hs) != hipSuccess)
@@ -155,10 +157,10 @@ muir_status_t muir_chunk_fwd(const muir_dims_t* dims, const void* q, const void*
 muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void* k,
                              const void* v, const void* log_a, const void* erase,
                              const void* write, const void* gamma, const float* S0,
-                             const float* S_chunks, const void* dO, const float* dS_T,
-                             float* dq, float* dk, float* dv, float* dlog_a, float* derase,
-                             float* dwrite, float* dgamma, float* dS0, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+                             const float* S_chunks, const void* summaries, const void* dO,
+                             const float* dS_T, float* dq, float* dk, float* dv, float* dlog_a,
+                             float* derase, float* dwrite, float* dgamma, float* dS0,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   ChunkShape s;
   muir_status_t st = check_dims(dims, &s);
   if (st != MUIR_OK) return st;
@@ -173,7 +175,7 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void*
     if (!workspace || workspace_bytes < bwd_ws(s)) return MUIR_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MUIR_ERR_ALIGN;
   }
-  const void* opt[] = {S0, S_chunks, dS_T, dS0};
+  const void* opt[] = {S0, S_chunks, summaries, dS_T, dS0};
   for (const void* p : opt)
     if (p && !aligned16(p)) return MUIR_ERR_ALIGN;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
@@ -185,31 +187,31 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void*
     return MUIR_OK;
   }
   char* ws = static_cast<char*>(workspace);
-  void* summ = ws;
   float* S_rec = reinterpret_cast<float*>(ws + s.nchunks() * s.summary_bytes());
   float* dS_chunks = S_rec + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
   float* scratch = dS_chunks + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
   const float* Sc = S_chunks;
+  const void* summ = summaries;
   mark(hs);
-  if (!Sc) {
-    // chunk-start states are not given: run the forward summaries and scan first
-    if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, summ, false, hs) !=
-        hipSuccess)
+  if (!summ) {
+    // the forward's chunk summaries are not given: recompute them
+    if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, ws, hs) != hipSuccess)
       return MUIR_ERR_HIP;
     mark(hs);
+    summ = ws;
+  }
+  if (!Sc) {
+    // chunk-start states are not given: rerun the forward scan
     if (muir::launch_fwd_scan(s, summ, S0, nullptr, S_rec, nullptr, hs) != hipSuccess)
       return MUIR_ERR_HIP;
     mark(hs);
     Sc = S_rec;
   }
-  if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, summ, true, hs) != hipSuccess)
-    return MUIR_ERR_HIP;
-  mark(hs);
   if (muir::launch_bwd_scan(s, summ, dO, dS_T, dS_chunks, dS0, hs) != hipSuccess)
     return MUIR_ERR_HIP;
   mark(hs);
-  if (muir::launch_bwd_chunk(s, q, k, v, log_a, erase, write, gamma, Sc, dS_chunks, dO, dq, dk,
-                             dv, dlog_a, derase, dwrite, dgamma, scratch, hs) != hipSuccess)
+  if (muir::launch_bwd_chunk(s, q, k, v, log_a, erase, write, gamma, summ, Sc, dS_chunks, dO, dq,
+                             dk, dv, dlog_a, derase, dwrite, dgamma, scratch, hs) != hipSuccess)
     return MUIR_ERR_HIP;
   mark(hs);
   return MUIR_OK;

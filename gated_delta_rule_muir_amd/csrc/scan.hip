@@ -4,7 +4,8 @@
 //
 // arXiv 2611.08376, Methodology: chunks are processed in order and the state
 // carries the recurrence across chunk boundaries.  With the chunk summary
-// (W, Q', Kbar, U~, O~, Gamma_C) of the chunkwise forward (fwd.hip):
+// (W, Q', Kbar, U~, O~, Gamma_C) of the chunkwise forward (fwd.hip), which
+// both scans read:
 //   forward:  o = O~ + Q' S,  S_next = diag(Gamma_C) S + Kbar^T (U~ - W S)
 //   backward: dS = diag(Gamma_C) dS_next + Q'^T dO - W^T (Kbar dS_next)
 // (the backward is the adjoint of the forward update; the pages state only
@@ -50,8 +51,8 @@ template <typename TC> __device__ __forceinline__ typename MM<TC>::frag identity
 }
 
 // ---------------------------------------------------------------------------
-// Forward.  Summary layout (fwd.hip): W [C][DK], Q' [C][DK], Kbar^T [DK][C],
-// U~^T [DV][C], O~^T [DV][C] in the compute type, then Gamma_C [DK] fp32.
+// Forward.  Reads W [C][DK], Q' [C][DK], Kbar^T [DK][C], U~^T [DV][C],
+// O~^T [DV][C] and Gamma_C of each chunk summary (SummaryPart).
 template <typename Tin, int DK, int NW>
 __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
     int T, int H, int C, const char* __restrict__ summ, size_t summ_bytes,
@@ -108,16 +109,18 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
     const int c = u / NSB;
     const int sb = u - c * NSB;
     const char* base = hsum + static_cast<size_t>(c) * summ_bytes;
-    const uint32_t wofs = static_cast<uint32_t>(sb * SB * LW);
-    const uint32_t kofs = static_cast<uint32_t>(2 * C * LW + sb * LK);
-    const uint32_t uofs = static_cast<uint32_t>(3 * C * LW + vb * NV * C * SZ + sb * LK);
-    const uint32_t oofs = uofs + static_cast<uint32_t>(DV * C * SZ);
-    const uint32_t gofs = static_cast<uint32_t>(C * (3 * DK + 2 * DV) * SZ);
+    auto part = [&](int p) { return static_cast<uint32_t>(summary_part(p, C, DK, DV) * SZ); };
+    const uint32_t wofs = part(SP_W) + static_cast<uint32_t>(sb * SB * LW);
+    const uint32_t qofs = part(SP_QP) + static_cast<uint32_t>(sb * SB * LW);
+    const uint32_t kofs = part(SP_KBT) + static_cast<uint32_t>(sb * LK);
+    const uint32_t uofs = part(SP_UTT) + static_cast<uint32_t>(vb * NV * C * SZ + sb * LK);
+    const uint32_t oofs = part(SP_OTT) + static_cast<uint32_t>(vb * NV * C * SZ + sb * LK);
+    const uint32_t gofs = part(SP_END);
 #pragma unroll
     for (int k = 0; k < PW; ++k) {
       const int w = min(tid + k * NTH, W_WORDS - 1);
       rw[k] = *reinterpret_cast<const u32x4*>(at(base, wofs + 16 * w));
-      rq[k] = *reinterpret_cast<const u32x4*>(at(base, wofs + C * LW + 16 * w));
+      rq[k] = *reinterpret_cast<const u32x4*>(at(base, qofs + 16 * w));
     }
 #pragma unroll
     for (int k = 0; k < PK; ++k) {
@@ -241,9 +244,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Backward.  Summary layout written for it (fwd.hip, backward layout):
-// W^T [DK][C], Q'^T [DK][C], Kbar [C][DK] in the compute type, Gamma_C [DK]
-// fp32 at the same place as in the forward layout.
+// Backward, on the same summaries: reads W^T [DK][C], Q'^T [DK][C] and
+// Kbar [C][DK] (the orientations whose contraction index is contiguous for
+// these products) and Gamma_C.
 template <typename Tin, int DK, int NW>
 __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
     int T, int H, int C, const char* __restrict__ summ, size_t summ_bytes,
@@ -305,9 +308,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
     const int c = unit_c(u);
     const int sb = unit_sb(u);
     const char* base = hsum + static_cast<size_t>(c) * summ_bytes;
-    const uint32_t tofs = static_cast<uint32_t>(sb * LK);
-    const uint32_t kofs = static_cast<uint32_t>(2 * C * LW + sb * SB * LW);
-    const uint32_t gofs = static_cast<uint32_t>(C * (3 * DK + 2 * DV) * SZ);
+    auto part = [&](int p) { return static_cast<uint32_t>(summary_part(p, C, DK, DV) * SZ); };
+    const uint32_t tofs = part(SP_WT) + static_cast<uint32_t>(sb * LK);
+    const uint32_t qofs = part(SP_QT) + static_cast<uint32_t>(sb * LK);
+    const uint32_t kofs = part(SP_KB) + static_cast<uint32_t>(sb * SB * LW);
+    const uint32_t gofs = part(SP_END);
     const char* dob = reinterpret_cast<const char*>(
         dO + ((static_cast<size_t>(b) * T + static_cast<size_t>(c) * C + sb * SB) * H + h) * DV + vb * NV);
 #pragma unroll
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
       const int w = min(tid + k * NTH, T_WORDS - 1);
       const uint32_t r = (w / CK) * C * SZ + 16 * (w % CK);
       rt[k] = *reinterpret_cast<const u32x4*>(at(base, tofs + r));
-      rq[k] = *reinterpret_cast<const u32x4*>(at(base, tofs + C * LW + r));
+      rq[k] = *reinterpret_cast<const u32x4*>(at(base, qofs + r));
     }
 #pragma unroll
     for (int k = 0; k < PK; ++k) {

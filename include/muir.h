@@ -110,7 +110,9 @@ size_t muir_chunk_fwd_workspace(const muir_dims_t* dims);
  *   S_chunks : [B, H, T/chunk, dk, dv] fp32 state at the START of every
  *              chunk (kept for muir_chunk_bwd), or NULL to skip
  *   workspace: device scratch of at least muir_chunk_fwd_workspace(dims)
- *              bytes; contents are clobbered.
+ *              bytes.  On return it holds the chunk summaries (the
+ *              per-chunk solve results); a caller that keeps it unchanged
+ *              may pass it to muir_chunk_bwd as `summaries`.
  */
 muir_status_t muir_chunk_fwd(const muir_dims_t* dims,
                              const void* q, const void* k, const void* v,
@@ -130,17 +132,23 @@ size_t muir_chunk_bwd_workspace(const muir_dims_t* dims);
  *   inputs as in muir_chunk_fwd, plus
  *   S_chunks : [B, H, T/chunk, dk, dv] fp32 from muir_chunk_fwd, or NULL
  *              (then recomputed inside, in the workspace)
+ *   summaries: the workspace of a muir_chunk_fwd call on the same inputs,
+ *              dims and S0, unchanged since (the chunk summaries it left
+ *              there), or NULL (then recomputed inside, in the workspace);
+ *              read only
  *   dO       : [B, T, H, dv] dtype upstream gradient of o
  *   dS_T     : [B, H, dk, dv] fp32 upstream gradient of S_T, or NULL for 0
  *   dq, dk, dlog_a, derase, dgamma : [B, T, H, dk] fp32 outputs
  *   dv, dwrite                     : [B, T, H, dv] fp32 outputs
  *   dS0      : [B, H, dk, dv] fp32 output, or NULL to skip
+ *   workspace: device scratch of at least muir_chunk_bwd_workspace(dims)
+ *              bytes; contents are clobbered.
  */
 muir_status_t muir_chunk_bwd(const muir_dims_t* dims,
                              const void* q, const void* k, const void* v,
                              const void* log_a, const void* erase,
                              const void* write, const void* gamma,
-                             const float* S0, const float* S_chunks,
+                             const float* S0, const float* S_chunks, const void* summaries,
                              const void* dO, const float* dS_T,
                              float* dq, float* dk, float* dv, float* dlog_a,
                              float* derase, float* dwrite, float* dgamma, float* dS0,

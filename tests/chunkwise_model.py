@@ -52,7 +52,7 @@ def chunk_summary(q, k, v, log_a, erase, write, gamma, C):
     """Per-chunk quantities of the chunkwise form, for one (b, h) sequence
     given as [T, D] arrays: returns a list of dicts with
       W = (I+A)^-1 (exp(L) * ek), U~ = (I+A)^-1 (write*v), Q' = exp(L)*qt - P W,
-      O~ = P U~, Kbar = exp(L_C - L) * k, gC = exp(L_C)
+      O~ = P U~, Kbar = exp(L_C - L) * k, gC = exp(L_C), and A, P
     (test-only; used to inspect the GPU path's intermediate workspace)."""
     q, k, v, la, er, wr, ga = (np.asarray(x, dtype=np.float64) for x in (q, k, v, log_a, erase, write, gamma))
     T = q.shape[0]
@@ -70,5 +70,5 @@ def chunk_summary(q, k, v, log_a, erase, write, gamma, C):
         W = Tm @ (np.exp(L) * ek)
         Ut = Tm @ (wr[c0:c0 + C] * vv)
         out.append(dict(W=W, Ut=Ut, Qp=np.exp(L) * qt - P @ W, Ot=P @ Ut,
-                        Kb=np.exp(L[-1][None, :] - L) * kk, gC=np.exp(L[-1])))
+                        Kb=np.exp(L[-1][None, :] - L) * kk, gC=np.exp(L[-1]), A=A, P=P))
     return out

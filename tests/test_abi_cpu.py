@@ -48,7 +48,7 @@ def test_status_strings_cover_every_code():
         seen.add(s)
     assert len(seen) == 7
     assert L.muir_status_string(99).decode() == "unknown status"
-    assert L.muir_abi_version() == 1
+    assert L.muir_abi_version() == 2
 
 
 def _dims(m, B=1, T=128, H=2, dk=64, dv=64, chunk=64, dtype=1):
@@ -100,15 +100,16 @@ def test_bwd_rejects_bad_arguments():
     need = L.muir_chunk_bwd_workspace(ctypes.byref(d))
     assert need > L.muir_chunk_fwd_workspace(ctypes.byref(d))
 
-    def call(dd, grads=None, ws_bytes=1 << 40):
+    def call(dd, grads=None, ws_bytes=1 << 40, summaries=None):
         g = list(FAKE[:7]) if grads is None else grads
-        return L.muir_chunk_bwd(ctypes.byref(dd), *FAKE[:7], None, None, FAKE[8], None, *g, None,
-                                FAKE[12], ctypes.c_size_t(ws_bytes), None)
+        return L.muir_chunk_bwd(ctypes.byref(dd), *FAKE[:7], None, None, summaries, FAKE[8], None, *g,
+                                None, FAKE[12], ctypes.c_size_t(ws_bytes), None)
     assert call(_dims(m, chunk=48)) == ERR_SHAPE
     g = list(FAKE[:7])
     g[5] = None
     assert call(d, grads=g) == ERR_NULL
     assert call(d, ws_bytes=need - 1) == ERR_WORKSPACE
+    assert call(d, summaries=ctypes.c_void_p(FAKE[8].value + 8)) == ERR_ALIGN
 
 
 def test_step_rejects_bad_arguments():

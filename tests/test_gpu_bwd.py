@@ -75,3 +75,25 @@ def test_bwd_with_saved_states_equals_recompute():
     torch.cuda.synchronize()
     for n in GRADS:
         assert torch.equal(g1[n], g2[n]), n
+
+
+def test_bwd_with_saved_summaries_equals_recompute():
+    """Passing the forward's workspace (its chunk summaries) gives the same
+    gradients as letting the backward recompute them, with and without the
+    saved chunk states."""
+    m = _lib()
+    B, T, H, d, C = 2, 256, 2, 128, 64
+    inp = muir_inputs.seq_inputs(B, T, H, d, d, dtype="bf16", decay="channel", seed=9, S0_scale=0.1,
+                                 with_dO=True, with_dST=True)
+    dv = to_dev(inp)
+    ws = torch.empty(m.muir_chunk_fwd_workspace(B, T, H, d, d, C), dtype=torch.uint8, device="cuda")
+    _, _, Sc = m.muir_chunk_fwd(*(dv[n] for n in NAMES), dv["S0"], chunk=C, save_states=True, workspace=ws)
+    ref = m.muir_chunk_bwd(*(dv[n] for n in NAMES), dv["dO"], S0=dv["S0"], dS_T=dv["dS_T"], chunk=C)
+    g1 = m.muir_chunk_bwd(*(dv[n] for n in NAMES), dv["dO"], S0=dv["S0"], S_chunks=Sc, dS_T=dv["dS_T"],
+                          summaries=ws, chunk=C)
+    g2 = m.muir_chunk_bwd(*(dv[n] for n in NAMES), dv["dO"], S0=dv["S0"], dS_T=dv["dS_T"], summaries=ws,
+                          chunk=C)
+    torch.cuda.synchronize()
+    for n in GRADS:
+        assert torch.equal(g1[n], ref[n]), n
+        assert torch.equal(g2[n], ref[n]), n

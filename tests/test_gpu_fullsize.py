@@ -51,11 +51,14 @@ def _check_heads(name, inp, o, S_T, g, heads, with_bwd=True):
 
 def _run(m, inp, C):
     dv = {n: (t.to("cuda") if t is not None else None) for n, t in inp.items()}
-    o, S_T, Sc = m.muir_chunk_fwd(*(dv[n] for n in NAMES), chunk=C, save_states=True)
-    g = m.muir_chunk_bwd(*(dv[n] for n in NAMES), dv["dO"], S_chunks=Sc, chunk=C)
+    # as bench.py runs the step: the backward reuses the forward's chunk states and summaries
+    B, T, H, d = dv["q"].shape
+    ws = torch.empty(m.muir_chunk_fwd_workspace(B, T, H, d, d, C), dtype=torch.uint8, device="cuda")
+    o, S_T, Sc = m.muir_chunk_fwd(*(dv[n] for n in NAMES), chunk=C, save_states=True, workspace=ws)
+    g = m.muir_chunk_bwd(*(dv[n] for n in NAMES), dv["dO"], S_chunks=Sc, summaries=ws, chunk=C)
     torch.cuda.synchronize()
     out = (o.cpu(), S_T.cpu(), {n: t.cpu() for n, t in g.items()})
-    del dv, o, S_T, Sc, g
+    del dv, o, S_T, Sc, g, ws
     torch.cuda.empty_cache()
     return out
 

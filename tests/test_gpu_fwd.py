@@ -115,7 +115,8 @@ def test_steps_equal_chunk_fwd():
 
 def test_fwd_summary_intermediates():
     """The chunk summary in the workspace equals the plain chunkwise quantities
-    (fp32 path, one head): W, U~, Q', O~, Kbar and exp(L_C)."""
+    (fp32 path, one head): W, U~, Q', O~, Kbar (and the transposed copies of
+    W, Q', Kbar), exp(L_C), and each 16-token leaf block's (I + A_II)^-1 and P_II."""
     from chunkwise_model import chunk_summary
     m = _lib()
     B, T, H, d, C = 1, 128, 1, 64, 64
@@ -127,20 +128,33 @@ def test_fwd_summary_intermediates():
     torch.cuda.synchronize()
     per = nbytes // (T // C)
     ref = chunk_summary(*(inp[n][0, :, 0].double().numpy() for n in NAMES), C)
+    n = C * d
     for c in range(T // C):
         blk = ws[c * per:(c + 1) * per].view(torch.float32).cpu().double().numpy()
-        W = blk[: C * d].reshape(C, d)
-        Qp = blk[C * d: 2 * C * d].reshape(C, d)
-        KbT = blk[2 * C * d: 3 * C * d].reshape(d, C)
-        UtT = blk[3 * C * d: 4 * C * d].reshape(d, C)
-        OtT = blk[4 * C * d: 5 * C * d].reshape(d, C)
-        gC = blk[5 * C * d: 5 * C * d + d]
+        W = blk[:n].reshape(C, d)
+        Qp = blk[n: 2 * n].reshape(C, d)
+        KbT = blk[2 * n: 3 * n].reshape(d, C)
+        UtT = blk[3 * n: 4 * n].reshape(d, C)
+        OtT = blk[4 * n: 5 * n].reshape(d, C)
+        Wt = blk[5 * n: 6 * n].reshape(d, C)
+        Qt = blk[6 * n: 7 * n].reshape(d, C)
+        Kb = blk[7 * n: 8 * n].reshape(C, d)
+        gC = blk[8 * n: 8 * n + d]
+        TP = blk[8 * n + d: 8 * n + d + (C // 16) * 512].reshape(C // 16, 2, 16, 16)
         r = ref[c]
         # exp(L_C) of fast channels sits in the fp32 denormal range, where the
         # device exponential flushes to zero: compare it with an absolute floor.
         np.testing.assert_allclose(gC, r["gC"], rtol=1e-4, atol=1e-36)
+        # the second orientations are copies of the same values
+        np.testing.assert_array_equal(Wt, W.T)
+        np.testing.assert_array_equal(Qt, Qp.T)
+        np.testing.assert_array_equal(Kb, KbT.T)
+        leaves_T = np.stack([np.linalg.inv(np.eye(16) + r["A"][16 * i:16 * i + 16, 16 * i:16 * i + 16])
+                             for i in range(C // 16)])
+        leaves_P = np.stack([r["P"][16 * i:16 * i + 16, 16 * i:16 * i + 16] for i in range(C // 16)])
         for nm, got, want in (("W", W, r["W"]), ("Ut", UtT.T, r["Ut"]), ("Qp", Qp, r["Qp"]),
-                              ("Ot", OtT.T, r["Ot"]), ("Kb", KbT.T, r["Kb"])):
+                              ("Ot", OtT.T, r["Ot"]), ("Kb", KbT.T, r["Kb"]),
+                              ("T_II", TP[:, 0], leaves_T), ("P_II", TP[:, 1], leaves_P)):
             e = rel_err(got, want)
             _say(f"  chunk {c} {nm}: {e:.3e}")
             assert e <= 1e-4, (c, nm, e)
