@@ -2,34 +2,36 @@
 //
 // One workgroup per chunk gets the chunk's initial state S0 and the gradient
 // dS_C of its end state (from the reverse scan in scan.hip) and forms every
-// input gradient with three sweeps over the chunk's 16-token blocks, with the
+// input gradient with two sweeps over the chunk's 16-token blocks, with the
 // block-boundary pivots of the forward (fwd.hip):
-//   F1 (forward): Delta_I = T_II (U_I - X_I S_I), S_{I+1} = g_I S_I + Ke_I^T Delta_I,
-//                 d(qt)_r = S_r dO_r                     (S_r: state after token r)
-//   R  (reverse): D, the state gradient at the block's end, from dS_C;
-//                 dR_J = T_JJ^T (Ke_J D + P_JJ^T dO_J)   (gradient of write*v),
-//                 d(k)_i = E_i Delta_i                    (E_i: state gradient at i),
-//                 D <- g_J D + Y_J^T dO_J - X_J^T dR_J
-//   F2 (forward): d(ek)_r = -S'_r dR_r                   (S'_r: decayed state before r)
-// with ek = erase*k, qt = gamma*q, then
-//   dLam_r = ek_r d(ek)_r + qt_r d(qt)_r - k_r d(k)_r (+ rowsum(S_C * dS_C) at the last token),
-//   dlog_a_i = sum_{r >= i in the chunk} dLam_r,
+//   F (forward): Delta_I = T_II (U_I - X_I S_I),  S_{I+1} = g_I S_I + Ke_I^T Delta_I;
+//                the deltas and the block-start states S_I go to the scratch
+//   R (reverse): D, the state gradient at the block's end, starting from dS_C;
+//                dR_J    = T_JJ^T (Ke_J D + P_JJ^T dO_J)   (gradient of write*v)
+//                d(k)_i  = E_i Delta_i                     (E_i: state gradient at token i)
+//                d(qt)_r = S_r dO_r                        (S_r: state after token r)
+//                d(ek)_r = -S'_r dR_r                      (S'_r: decayed state before r's write)
+//                D <- g_J D + Y_J^T dO_J - X_J^T dR_J
+// with ek = erase*k, qt = gamma*q, and
+//   dLam_r   = ek_r d(ek)_r + qt_r d(qt)_r - k_r d(k)_r,
+//   dlog_a_i = sum_{r >= i in the chunk} dLam_r + rowsum(S_C * dS_C),
 //   derase = k d(ek), dk = d(k) + erase d(ek), dq = gamma d(qt), dgamma = q d(qt),
 //   dv = write dR, dwrite = v dR.
-// (arXiv 2611.08376 states only that a custom backward pass is used, in its
-// Methodology section and the fig:kernel caption; this is the adjoint of the
-// chunkwise forward.)
+// Each gradient is written once: the reverse sweep carries the suffix sums of
+// dLam from block to block.  (arXiv 2611.08376 states only that a custom
+// backward pass is used, in its Methodology section and the fig:kernel
+// caption; this is the adjoint of the chunkwise forward.)
 //
-// Each per-token product splits into a boundary part, a tile product with S_I,
+// Each per-token product splits into a boundary part, a tile product with S_J,
 // D or the deltas scaled by exp(.) <= 1, and a 16 x 16 leaf part.  On leaves
 // whose decay stays within LEAF_SAFE_RANGE the leaf part is one more 16-wide
 // MFMA product folded into the same accumulator; steeper leaves use per-pair
 // factors in (0, 1].
 //
 // Latency: every global read a step needs (the block's inputs, dO rows,
-// deltas, their gradients, the leaf inverse, the gradient partials) is issued
-// one step ahead into registers and committed to LDS when the step starts, so
-// a step's compute phase touches only LDS and registers.
+// deltas, the leaf inverse, the block-start state) is issued one step ahead
+// into registers (clamped at the ends of each sweep, so no load sits under a
+// branch) and committed to LDS when the step starts.
 #include "chunk_common.h"
 #include "kernels.h"
 #include "mma.h"
@@ -38,16 +40,24 @@ namespace muir {
 
 namespace {
 
-// Per-chunk scratch: deltas [C][DV] and their gradients [C][DV], in the
-// compute type.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Per-chunk scratch, in the compute type: deltas [C][DV], then the state at
+// the start of every 16-token block [C/16][DK][DV] (row-major, as staged).
 template <typename TC>
-__host__ __device__ constexpr size_t bwd_scratch_bytes_tc(int C, int DV) {
-  return static_cast<size_t>(2) * C * DV * sizeof(TC);
+__host__ __device__ constexpr size_t bwd_scratch_bytes_tc(int C, int DK, int DV) {
+  return (static_cast<size_t>(C) * DV + static_cast<size_t>(C / 16) * DK * DV) * sizeof(TC);
 }
 
 // LDS row padding (elements) that keeps 16 lanes reading 4 consecutive
 // elements of 16 different rows on distinct banks.
 template <typename TC> constexpr int row_pad() { return sizeof(TC) == 2 ? 8 : 4; }
+
+// Column passes for the two staged states ([DK][DV / SPLIT] each), chosen so
+// the kernel's LDS stays within 160 KB.
+template <typename TC, int DK, int C> constexpr int stage_split() {
+  return DK == 64 ? 1 : (sizeof(TC) == 2 ? (C == 64 ? 1 : 2) : (C == 64 ? 4 : 8));
+}
 
 template <typename Tin, int DK, int C, int NW>
 __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
@@ -56,9 +66,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     const Tin* __restrict__ write, const Tin* __restrict__ gamma, const char* __restrict__ summ,
     size_t summ_bytes, size_t tp_offset, const float* __restrict__ S_chunks,
     const float* __restrict__ dS_chunks, const Tin* __restrict__ dO, float* __restrict__ dq,
-    float* __restrict__ dk,
-    float* __restrict__ dv, float* __restrict__ dlog_a, float* __restrict__ derase,
-    float* __restrict__ dwrite, float* __restrict__ dgamma, char* __restrict__ scratch) {
+    float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dlog_a,
+    float* __restrict__ derase, float* __restrict__ dwrite, float* __restrict__ dgamma,
+    char* __restrict__ scratch) {
   typedef Tin TC;
   typedef MM<TC> M;
   typedef typename M::frag frag;
@@ -69,8 +79,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   constexpr int TPC = NTH / DK;       // elementwise: threads per key channel
   constexpr int RPT = 16 / TPC;       // elementwise: consecutive tokens per thread
   constexpr int NB = C / 16;
-  constexpr int NSTEP = 3 * NB;
-  constexpr int SPLIT = (sizeof(TC) == 4 && DK == 128) ? 4 : 1;  // staged state in column passes
+  constexpr int SPLIT = stage_split<TC, DK, C>();
   constexpr int SW = DV / SPLIT;
   constexpr int PT = DK + row_pad<TC>();
   constexpr int PV = DV + row_pad<TC>();
@@ -81,8 +90,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   constexpr int EPW = 8 / static_cast<int>(sizeof(TC));  // elements per 8-byte word
   constexpr int RW = EPT / EPW;       // 8-byte words per thread of a row tile
   constexpr int TPW = 512 / EPW;      // threads that move a block's T_II, P_II words
+  constexpr int SEW = 16 / static_cast<int>(sizeof(TC));  // elements per 16-byte word
+  constexpr int SWR = DV / SEW;       // 16-byte words per state row
+  constexpr int SPT = DK * SWR / NTH; // 16-byte words of a block-start state per thread
   static_assert(NT >= 1 && NW * NT * 16 == DV && TPC * RPT == 16 && RPT % 4 == 0 && RW >= 1 &&
-                    EPT % EPW == 0 && TPW <= NTH,
+                    EPT % EPW == 0 && TPW <= NTH && SPT * NTH == DK * SWR && SW % SEW == 0,
                 "thread layout");
 
   const int NC = T / C;
@@ -98,6 +110,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   const int c16 = lane & 15;
   // MFMA-output mapping: lane's state column / gradient channel of tile n
   auto colv = [&](int n) -> int { return 16 * (NT * wave + n) + c16; };
+  auto col0 = [&](int n) -> int { return 16 * (NT * wave + n); };
   const int ej = tid % DK;            // elementwise mapping: channel, tokens RPT*part..+RPT-1
   const int part = tid / DK;
   const int prow = tid / RC;          // row-tile mapping: row, columns pc0..pc0+EPT-1
@@ -123,35 +136,36 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   float* dwb = dwrite + ebase;
   float* dgb = dgamma + ebase;
   auto gi = [&](int t, int j) -> uint32_t { return static_cast<uint32_t>(t) * HD + static_cast<uint32_t>(j); };
-  TC* gDel = reinterpret_cast<TC*>(scratch + static_cast<size_t>(chunk) * bwd_scratch_bytes_tc<TC>(C, DV));
-  TC* gdR = gDel + static_cast<size_t>(C) * DV;
+  TC* gDel = reinterpret_cast<TC*>(scratch + static_cast<size_t>(chunk) * bwd_scratch_bytes_tc<TC>(C, DK, DV));
+  TC* gS = gDel + static_cast<size_t>(C) * DV;  // [NB][DK][DV]
   // T_II, P_II of the chunk's blocks, from the chunk summary, [NB][2][16][16]
   const TC* gTP = reinterpret_cast<const TC*>(summ + static_cast<size_t>(chunk) * summ_bytes + tp_offset);
   const float* S0c = S_chunks + static_cast<size_t>(chunk) * DK * DV;
   const float* dSC = dS_chunks + static_cast<size_t>(chunk) * DK * DV;
 
-  constexpr int UNU = DV * TP > 16 * PV ? DV * TP : 16 * PV;
-  __shared__ float sBsum[NB][DK];                            // sum of log_a over block I
-  __shared__ float sTmp[TPC][DK];
-  __shared__ float sF[16][DK + 1];                           // per-element factor of the sweep
-  __shared__ float sLam[16][DK + 1];                         // log_a of a steep block (per-pair leaves)
-  __shared__ __attribute__((aligned(16))) TC sRowA[16][PT];  // F1: X rows   R: Ke rows
-  __shared__ __attribute__((aligned(16))) TC sTB[DK][TP];    // R: Y^T
+  __shared__ float sPart[NB][TPC][DK];                       // sum of log_a over each part's RPT tokens
+  __shared__ int sUnsafe;                                    // bit I: block I beyond LEAF_SAFE_RANGE
+  __shared__ float sFs[16][DK + 4];                          // R: exp(Lam - B_J)
+  __shared__ float sFe[16][DK + 4];                          // R: exp(B_{J+1} - Lam)
+  __shared__ __attribute__((aligned(16))) TC sRowA[16][PT];  // F: X rows   R: Ke rows
+  __shared__ __attribute__((aligned(16))) TC sTA[DK][TP];    // F: Ke^T     R: X^T
+  __shared__ __attribute__((aligned(16))) TC sTB[DK][TP];    // F: U^T      R: Y^T
   __shared__ __attribute__((aligned(16))) TC sTY[DK][TP];    // R: Yhat^T
-  __shared__ __attribute__((aligned(16))) TC sTA[DK][TP];    // F1, F2: Ke^T   R: X^T
-  __shared__ __attribute__((aligned(16))) TC sTZ[DK][TP];    // F1, F2: Z^T    R: Xhat^T
-  __shared__ __attribute__((aligned(16))) TC sUnU[UNU];      // F1: (write*v)^T   R, F2: dR rows
+  __shared__ __attribute__((aligned(16))) TC sTX[DK][TP];    // R: Xhat^T
+  __shared__ __attribute__((aligned(16))) TC sTZ[DK][TP];    // R: Z^T
   __shared__ __attribute__((aligned(16))) TC sDO[16][PV];    // dO rows of the block
   __shared__ __attribute__((aligned(16))) TC sDL[16][PV];    // delta rows of the block
+  __shared__ __attribute__((aligned(16))) TC sDR[16][PV];    // dR rows of the block
   __shared__ __attribute__((aligned(16))) TC sT[16][TP];     // T_II of the block
   __shared__ __attribute__((aligned(16))) TC sP[16][TP];     // P_II of the block
-  __shared__ __attribute__((aligned(16))) TC sSD[DK][PS];    // staged S or D columns, [dk][dv]
-  __shared__ float sLf[2][16][17];                           // leaf gradient matrices
+  __shared__ __attribute__((aligned(16))) TC sSD[DK][PS];    // staged D columns, [dk][dv]
+  __shared__ __attribute__((aligned(16))) TC sSS[DK][PS];    // staged S_J columns, [dk][dv]
+  __shared__ float sLf[2][16][17];                           // leaf matrices of steep blocks
   __shared__ float sG[DK];
-  __shared__ float sRow[NW][DK];
-  __shared__ float sTot[DK];
-  TC (*sU)[TP] = reinterpret_cast<TC (*)[TP]>(sUnU);
-  TC (*sDR)[PV] = reinterpret_cast<TC (*)[PV]>(sUnU);
+  // per-wave partial rowsums of S_C * dS_C, used once before the reverse
+  // sweep (which then writes Yhat^T over it)
+  static_assert(NW * DK * sizeof(float) <= sizeof(TC) * DK * TP, "rowsum scratch");
+  float (*sRow)[DK] = reinterpret_cast<float (*)[DK]>(&sTY[0][0]);
 
   // identity operand: a 16x16 product with it moves a tile's rows onto lanes
   frag ident;
@@ -162,189 +176,83 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     ident = M::from_f32(idv);
   }
 
-  // ---- block sums of the log-decay ----
+  // ---- sums of the log-decay over each block and each part of it, and the
+  // blocks whose decay leaves LEAF_SAFE_RANGE (steep leaves) ----
+  if (tid == 0) sUnsafe = 0;
 #pragma unroll
-  for (int I = part; I < NB; I += TPC) {
+  for (int I = 0; I < NB; ++I) {
     float sacc = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) sacc += ldv(lb, gi(16 * I + rr, ej));
-    sBsum[I][ej] = sacc;
+    for (int rr = 0; rr < RPT; ++rr) sacc += ldv(lb, gi(16 * I + RPT * part + rr, ej));
+    sPart[I][part][ej] = sacc;
+  }
+  __syncthreads();
+  if (part == 0) {
+    unsigned mask = 0;
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      float bs = 0.f;
+#pragma unroll
+      for (int p = 0; p < TPC; ++p) bs += sPart[I][p][ej];
+      if (!(-bs <= LEAF_SAFE_RANGE)) mask |= 1u << I;
+    }
+    if (mask) atomicOr(&sUnsafe, static_cast<int>(mask));
   }
 
-  auto step_sweep = [](int s) { return s / NB; };
-  auto step_block = [](int s) { return (s / NB) == 1 ? NB - 1 - (s - NB) : s % NB; };
-
-  // ---- prefetch slots, all assigned by every prefetch (unused ones to 0) ----
-  // elementwise (channel ej, tokens RPT*part + rr): log_a, k, erase, q, gamma, write, v
-  float xl[RPT], xk[RPT], xe[RPT], xq[RPT], xg[RPT], xw[RPT], xv[RPT];
-  // row tiles (row prow, columns pc0..): dO, deltas, their gradients (raw words)
-  u32x2 rdo[RW], rdl[RW], rdr[RW];
-  u32x2 rtp;  // one word of the block's T_II, P_II (threads < TPW; F1 and R)
-  // MFMA-output mapping (token 4g+i, column colv(n)):
-  //   F1: q, gamma   R: v, write   F2: k, erase, partial d(k), partial dLam
-  float oa[NT][4], ob[NT][4], oc[NT][4], od[NT][4];
-  float dk0[NT][4];  // partial d(k) of block 0, from R's last step
-
-  // Every slot is loaded on every step, from a sweep-dependent (uniform) base;
-  // slots a sweep does not use re-read k or the scratch.  No load sits under a
-  // branch, so the loads stay in flight until the step that consumes them.
-  auto prefetch = [&](int s) {
-    if (s >= NSTEP) return;
-    const int sw = step_sweep(s);
-    const int I = step_block(s);
-    const int r0 = 16 * I;
-    const Tin* pe = sw != 2 ? eb : kb;
-    const Tin* pq = sw != 2 ? qb : kb;
-    const Tin* pg = sw != 2 ? gb : kb;
-    const Tin* pw = sw == 0 ? wb : kb;
-    const Tin* pv = sw == 0 ? vb : kb;
-#pragma unroll
-    for (int rr = 0; rr < RPT; ++rr) {
-      const uint32_t o = gi(r0 + RPT * part + rr, ej);
-      xl[rr] = ldv(lb, o);
-      xk[rr] = ldv(kb, o);
-      xe[rr] = ldv(pe, o);
-      xq[rr] = ldv(pq, o);
-      xg[rr] = ldv(pg, o);
-      xw[rr] = ldv(pw, o);
-      xv[rr] = ldv(pv, o);
-    }
-#pragma unroll
-    for (int e = 0; e < RW; ++e) {
-      const int col = pc0 + e * EPW;
-      const uint32_t so = static_cast<uint32_t>(r0 + prow) * DV + col;
-      rdo[e] = *reinterpret_cast<const u32x2*>(at(dOb, gi(r0 + prow, col)));
-      // deltas and their gradients: used by R (all but its first block) and
-      // F2 (all but its first block); those find them in LDS
-      rdl[e] = *reinterpret_cast<const u32x2*>(at(gDel, so));
-      rdr[e] = *reinterpret_cast<const u32x2*>(at(gdR, so));
-    }
-    rtp = *reinterpret_cast<const u32x2*>(
-        at(gTP, static_cast<uint32_t>(I * 512 + (tid < TPW ? tid : TPW - 1) * EPW)));
-    const Tin* poa = sw == 0 ? qb : (sw == 1 ? vb : kb);
-    const Tin* pob = sw == 0 ? gb : (sw == 1 ? wb : eb);
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const uint32_t o = gi(r0 + 4 * g + ii, colv(n));
-        oa[n][ii] = ldv(poa, o);
-        ob[n][ii] = ldv(pob, o);
-        oc[n][ii] = *at(dkb, o);  // F2: partial d(k) (block 0: kept in registers)
-        od[n][ii] = *at(dlb, o);  // F2: partial dLam
-      }
-  };
-
-  // Commit the prefetched step into LDS and form the block's factor tiles.
-  // F1: sF = exp(Lam - B_I); X rows; Ke^T, Z^T, U^T; T_II, P_II
-  // R:  sF = exp(B_{I+1} - Lam); Ke rows; X^T, Y^T, Xhat^T, Yhat^T; T_II, P_II
-  // F2: sF = exp(Lam - B_I); Ke^T, Z^T
-  // X = ek exp(Lam - B_I), Y = qt exp(Lam - B_I), Ke = k exp(B_{I+1} - Lam),
-  // Z = k exp(B_I - Lam), Xhat = ek exp(Lam - B_{I+1}), Yhat = qt exp(Lam - B_{I+1});
-  // Z, Xhat, Yhat (>= 1) only on leaves within LEAF_SAFE_RANGE.  Returns that flag.
-  auto commit = [&](int s) -> int {
-    const int sw = step_sweep(s);
-    const int I = step_block(s);
-    float cs[RPT], sf[RPT];
-    {
-      float run = 0.f;
-#pragma unroll
-      for (int rr = 0; rr < RPT; ++rr) {
-        run += xl[rr];
-        cs[rr] = run;
-      }
-      sTmp[part][ej] = run;
-      float suf = 0.f;
-#pragma unroll
-      for (int rr = RPT - 1; rr >= 0; --rr) {
-        sf[rr] = suf;
-        suf += xl[rr];
-      }
-    }
-    const float bsum = sBsum[I][ej];
-    const int safe = __syncthreads_and(-bsum <= LEAF_SAFE_RANGE);
-    float excl = 0.f, exsuf = 0.f;
+  // within-block prefix (through each token) and suffix (after it) of log_a,
+  // channel ej, tokens RPT*part + rr: loc = Lam_r - B_I, suf = B_{I+1} - Lam_r
+  auto block_sums = [&](int I, const float* xl, float* loc, float* suf) {
+    float excl = 0.f, exsuf = 0.f, bs = 0.f;
 #pragma unroll
     for (int p = 0; p < TPC; ++p) {
-      if (p < part) excl += sTmp[p][ej];
-      if (p > part) exsuf += sTmp[p][ej];
+      const float ps = sPart[I][p][ej];
+      if (p < part) excl += ps;
+      if (p > part) exsuf += ps;
+      bs += ps;
     }
-    if (part == 0) sG[ej] = __expf(bsum);
+    float run = 0.f;
 #pragma unroll
-    for (int h4 = 0; h4 < RPT / 4; ++h4) {
-      f32x4 tA, tZ, tB, tY;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int rr = 4 * h4 + q4;
-        const int r = RPT * part + rr;
-        const float loc = excl + cs[rr];   // Lam_r - B_I
-        const float suf = sf[rr] + exsuf;  // B_{I+1} - Lam_r
-        const float fs = __expf(loc);
-        const float fe = __expf(suf);
-        const float ek = xe[rr] * xk[rr];
-        const float qt = xg[rr] * xq[rr];
-        if (!safe) sLam[r][ej] = xl[rr];
-        if (sw == 0) {
-          sF[r][ej] = fs;
-          sRowA[r][ej] = M::cvt(ek * fs);
-          tA[q4] = xk[rr] * fe;
-          tZ[q4] = safe ? xk[rr] * __expf(-loc) : 0.f;
-          tB[q4] = xw[rr] * xv[rr];
-        } else if (sw == 1) {
-          const float ie = safe ? __expf(-suf) : 0.f;
-          sF[r][ej] = fe;
-          sRowA[r][ej] = M::cvt(xk[rr] * fe);
-          tA[q4] = ek * fs;
-          tB[q4] = qt * fs;
-          tZ[q4] = ek * ie;
-          tY[q4] = qt * ie;
-        } else {
-          sF[r][ej] = fs;
-          tA[q4] = xk[rr] * fe;
-          tZ[q4] = safe ? xk[rr] * __expf(-loc) : 0.f;
-        }
-      }
-      const int t0 = RPT * part + 4 * h4;
-      store4(&sTA[ej][t0], tA);
-      store4(&sTZ[ej][t0], tZ);
-      if (sw == 0) store4(&sU[ej][t0], tB);
-      if (sw == 1) {
-        store4(&sTB[ej][t0], tB);
-        store4(&sTY[ej][t0], tY);
-      }
+    for (int rr = 0; rr < RPT; ++rr) {
+      run += xl[rr];
+      loc[rr] = excl + run;
     }
+    float s2 = 0.f;
 #pragma unroll
-    for (int e = 0; e < RW; ++e) {
-      const int col = pc0 + e * EPW;
-      if (sw != 2) *reinterpret_cast<u32x2*>(&sDO[prow][col]) = rdo[e];
-      if ((sw == 1 && I != NB - 1) || (sw == 2 && I != 0)) *reinterpret_cast<u32x2*>(&sDL[prow][col]) = rdl[e];
-      if (sw == 2 && I != 0) *reinterpret_cast<u32x2*>(&sDR[prow][col]) = rdr[e];
+    for (int rr = RPT - 1; rr >= 0; --rr) {
+      suf[rr] = s2 + exsuf;
+      s2 += xl[rr];
     }
-    if (sw != 2 && tid < TPW) {
+    if (part == 0) sG[ej] = __expf(bs);
+  };
+
+  // T_II, P_II words of block I into sT, sP
+  auto tp_word = [&](int I) -> u32x2 {
+    return *reinterpret_cast<const u32x2*>(
+        at(gTP, static_cast<uint32_t>(I * 512 + (tid < TPW ? tid : TPW - 1) * EPW)));
+  };
+  auto tp_commit = [&](u32x2 w) {
+    if (tid < TPW) {
       const int e0 = tid * EPW;
       TC* dst = e0 < 256 ? &sT[e0 >> 4][e0 & 15] : &sP[(e0 - 256) >> 4][e0 & 15];
-      *reinterpret_cast<u32x2*>(dst) = rtp;
+      *reinterpret_cast<u32x2*>(dst) = w;
     }
-    __syncthreads();
-    return safe;
   };
 
-  // Steep leaves read the raw inputs from global memory (L2-resident: the
-  // step's own loads brought them in).
-  // exp(sum of log_a over tokens (i, r] of the block, channel j), r >= i
-  auto pair_factor = [&](int r, int i, int j) -> float {
-    float ls = 0.f;
-    for (int x = i + 1; x <= r; ++x) ls += sLam[x][j];
-    return __expf(ls);
-  };
-
-  // out[r][i] = A_r . B_i over the DV columns of two row tiles, masked to
-  // i <= r (or i < r when strict)
-  auto leaf_dot = [&](const TC (*A)[PV], const TC (*Bm)[PV], bool strict, float (*dst)[17]) {
+  // (A_m . B_n) over the DV columns of two [16][DV] row tiles, in the
+  // MFMA-output layout: lane (g, c16) holds m = 4g+i, n = c16.  Read as the
+  // left operand of a 16-wide product it is the matrix with n on the rows
+  // and m along the contraction.
+  auto leaf_pair = [&](const TC (*A)[PV], const TC (*Bm)[PV]) -> f32x4 {
     f32x4 acc = zero4();
 #pragma unroll
     for (int kk = 0; kk < DV / 16; ++kk)
       acc = M::mma(M::load(&A[c16][16 * kk + 4 * g]), M::load(&Bm[c16][16 * kk + 4 * g]), acc);
+    return acc;
+  };
+  // dst[r][i] = A_r . B_i, masked to i <= r (or i < r when strict): the leaf
+  // matrices in LDS, for the per-pair sums of steep blocks
+  auto leaf_dot = [&](const TC (*A)[PV], const TC (*Bm)[PV], bool strict, float (*dst)[17]) {
+    const f32x4 acc = leaf_pair(A, Bm);
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int r = 4 * g + ii;
@@ -352,46 +260,19 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       dst[r][c16] = keep ? acc[ii] : 0.f;
     }
   };
-
-  // Store a [16 tokens][16 columns] tile held in MFMA-output layout (tokens
-  // 4g+i, column c16) as rows: one identity product moves the tokens onto
-  // lanes, then each lane writes 4 consecutive columns of its token.
-  auto store_rows = [&](f32x4 tile, TC (*lds)[PV], TC* glob, int col0) {
-    const f32x4 tt = M::mma(M::from_f32(tile), ident, zero4());  // token c16, columns col0+4g+i
-    store4(&lds[c16][col0 + 4 * g], tt);
-    store4(glob + static_cast<size_t>(c16) * DV + col0 + 4 * g, tt);
+  // Steep leaves read the raw inputs from global memory (L2-resident: the
+  // step's own loads brought them in).
+  // exp(sum of log_a over tokens (i, r] of the block at r0, channel j), r >= i
+  auto pair_factor = [&](int r0, int r, int i, int j) -> float {
+    float ls = 0.f;
+    for (int x = i + 1; x <= r; ++x) ls += ldv(lb, gi(r0 + x, j));
+    return __expf(ls);
   };
 
-  // contraction over dv of a state (rows 16s+4g+i, columns colv(n)) with the
-  // rows of a [16][DV] tile: acc[n][token 4g+i] = sum_c A[token][c] st[channel colv(n)][c].
-  // The state is staged in LDS as [dk][dv] bf16/fp32 rows, moved there by
-  // identity products (4 consecutive columns per lane and store).
-  auto state_rows = [&](const f32x4 (*st)[NT], const TC (*A)[PV], f32x4* acc) {
-#pragma unroll
-    for (int n = 0; n < NT; ++n) acc[n] = zero4();
-#pragma unroll
-    for (int p = 0; p < SPLIT; ++p) {
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const int cb = 16 * (NT * wave + n) - p * SW;
-        if (cb >= 0 && cb < SW) {
-#pragma unroll
-          for (int s = 0; s < RT; ++s) {
-            const f32x4 tt = M::mma(M::from_f32(st[s][n]), ident, zero4());  // row 16s+c16, columns cb+4g+i
-            store4(&sSD[16 * s + c16][cb + 4 * g], tt);
-          }
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int kk = 0; kk < SW / 16; ++kk) {
-        const frag af = M::load(&A[c16][p * SW + 16 * kk + 4 * g]);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) acc[n] = M::mma(af, M::load(&sSD[colv(n)][16 * kk + 4 * g]), acc[n]);
-      }
-      if (p + 1 < SPLIT) __syncthreads();
-    }
-  };
+  // a [16][16] tile held in MFMA-output layout (rows 4g+i, column c16), moved
+  // by one identity product so that lane (g, c16) holds row c16, columns
+  // 4g..4g+3
+  auto turn = [&](f32x4 tile) -> f32x4 { return M::mma(M::from_f32(tile), ident, zero4()); };
 
   // (the lane offset is made opaque per call so that the addresses are formed
   // where they are used instead of being kept live across the sweeps)
@@ -414,25 +295,71 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     return gs;
   };
 
+  // =========================== F: forward sweep ===========================
+  // slots: log_a, k, erase, write, v (channel ej, tokens RPT*part + rr), T/P word
+  float fl[RPT], fk[RPT], fe[RPT], fw[RPT], fv[RPT];
+  u32x2 ftp;
+  auto prefetch_f = [&](int I) {
+#pragma unroll
+    for (int rr = 0; rr < RPT; ++rr) {
+      const uint32_t o = gi(16 * I + RPT * part + rr, ej);
+      fl[rr] = ldv(lb, o);
+      fk[rr] = ldv(kb, o);
+      fe[rr] = ldv(eb, o);
+      fw[rr] = ldv(wb, o);
+      fv[rr] = ldv(vb, o);
+    }
+    ftp = tp_word(I);
+  };
+  // X = ek exp(Lam - B_I) rows, Ke = k exp(B_{I+1} - Lam) and U = write*v transposed
+  auto commit_f = [&](int I) {
+    float loc[RPT], suf[RPT];
+    block_sums(I, fl, loc, suf);
+#pragma unroll
+    for (int h4 = 0; h4 < RPT / 4; ++h4) {
+      f32x4 tA, tB;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int rr = 4 * h4 + q4;
+        const int r = RPT * part + rr;
+        sRowA[r][ej] = M::cvt(fe[rr] * fk[rr] * __expf(loc[rr]));
+        tA[q4] = fk[rr] * __expf(suf[rr]);
+        tB[q4] = fw[rr] * fv[rr];
+      }
+      const int t0 = RPT * part + 4 * h4;
+      store4(&sTA[ej][t0], tA);
+      store4(&sTB[ej][t0], tB);
+    }
+    tp_commit(ftp);
+    __syncthreads();
+  };
+
   f32x4 S[RT][NT];
   load_state(S, S0c);
-  prefetch(0);
-  __syncthreads();  // sBsum
+  prefetch_f(0);
+  __syncthreads();  // sPart, sBsum, sUnsafe
 
-  // ================= F1: forward sweep: deltas, d(qt) ==================
 #pragma unroll 1
   for (int I = 0; I < NB; ++I) {
     const int r0 = 16 * I;
-    const int safe = commit(I);
-    float qcur[NT][4], gcur[NT][4];
+    commit_f(I);
+    prefetch_f(I + 1 < NB ? I + 1 : I);
+    frag Sf[RT][NT];
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
+    for (int s = 0; s < RT; ++s)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        qcur[n][ii] = oa[n][ii];
-        gcur[n][ii] = ob[n][ii];
-      }
-    prefetch(I + 1);
+      for (int n = 0; n < NT; ++n) Sf[s][n] = M::from_f32(S[s][n]);
+    // the block-start state, as [dk][dv] rows, for the reverse sweep
+    {
+      TC* dst = gS + static_cast<size_t>(I) * DK * DV;
+#pragma unroll
+      for (int s = 0; s < RT; ++s)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const f32x4 tt = M::mma(Sf[s][n], ident, zero4());  // row 16s+c16, columns col0(n)+4g+i
+          store4(at(dst, static_cast<uint32_t>((16 * s + c16) * DV + col0(n) + 4 * g)), tt);
+        }
+    }
     // Delta_I = T_II (U_I - X_I S_I)
     f32x4 Dl[NT];
     {
@@ -443,46 +370,17 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       for (int s = 0; s < RT; ++s) {
         const frag xa = M::load(&sRowA[c16][16 * s + 4 * g]);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) xs[n] = M::mma(xa, M::from_f32(S[s][n]), xs[n]);
+        for (int n = 0; n < NT; ++n) xs[n] = M::mma(xa, Sf[s][n], xs[n]);
       }
       const frag ta = M::load(&sT[c16][4 * g]);
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        f32x4 rhs = load4(&sU[colv(n)][4 * g]);
+        f32x4 rhs = load4(&sTB[colv(n)][4 * g]);
         rhs -= xs[n];
         Dl[n] = M::mma(ta, M::from_f32(rhs), zero4());
-        store_rows(Dl[n], sDL, gDel + static_cast<size_t>(r0) * DV, 16 * (NT * wave + n));
+        store4(at(gDel, static_cast<uint32_t>((r0 + c16) * DV + col0(n) + 4 * g)), turn(Dl[n]));
       }
     }
-    __syncthreads();
-    if (wave == 0) leaf_dot(sDO, sDL, false, sLf[0]);  // dO_r . Delta_i, i <= r
-    // d(qt)_r = exp(Lam_r - B_I) [ S_I dO_r + sum_{i<=r} (dO_r . Delta_i) Z_i ]
-    f32x4 acc[NT];
-    state_rows(S, sDO, acc);
-    if (safe) {
-      f32x4 lf;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lf[i] = sLf[0][c16][4 * g + i];
-      const frag lff = M::from_f32(lf);
-#pragma unroll
-      for (int n = 0; n < NT; ++n) acc[n] = M::mma(lff, M::load(&sTZ[colv(n)][4 * g]), acc[n]);
-    }
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int r = 4 * g + ii;
-        const int j = colv(n);
-        float val = sF[r][j] * acc[n][ii];
-        if (!safe)
-          for (int i2 = 0; i2 <= r; ++i2) val += sLf[0][r][i2] * pair_factor(r, i2, j) * ldv(kb, gi(r0 + i2, j));
-        const float qq = qcur[n][ii];
-        const float gg = gcur[n][ii];
-        const uint32_t o = gi(r0 + r, j);
-        *at(dqb, o) = gg * val;
-        *at(dgb, o) = qq * val;
-        *at(dlb, o) = gg * qq * val;
-      }
     // S_{I+1} = diag(exp(B_{I+1} - B_I)) S_I + Ke_I^T Delta_I
 #pragma unroll
     for (int s = 0; s < RT; ++s) {
@@ -494,10 +392,119 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     __syncthreads();
   }
 
-  // ================= R: reverse sweep: dR, d(k) ==================
+  // =========================== R: reverse sweep ===========================
+  // slots: log_a, k, erase, q, gamma (channel ej, tokens RPT*part + rr);
+  // dO and delta rows (raw words); T/P word; the block-start state (16-byte
+  // words); q, gamma, v, write, k, erase at (token 4g+i, column colv(n))
+  float xl[RPT], xk[RPT], xe[RPT], xq[RPT], xg[RPT];
+  u32x2 rdo[RW], rdl[RW], rtp;
+  u32x4 rss[SPT];
+  float oq[NT][4], og[NT][4], ov[NT][4], ow[NT][4], ok[NT][4], oe[NT][4];
+  auto prefetch_r = [&](int J) {
+    const int r0 = 16 * J;
+#pragma unroll
+    for (int rr = 0; rr < RPT; ++rr) {
+      const uint32_t o = gi(r0 + RPT * part + rr, ej);
+      xl[rr] = ldv(lb, o);
+      xk[rr] = ldv(kb, o);
+      xe[rr] = ldv(eb, o);
+      xq[rr] = ldv(qb, o);
+      xg[rr] = ldv(gb, o);
+    }
+#pragma unroll
+    for (int e = 0; e < RW; ++e) {
+      const int col = pc0 + e * EPW;
+      rdo[e] = *reinterpret_cast<const u32x2*>(at(dOb, gi(r0 + prow, col)));
+      rdl[e] = *reinterpret_cast<const u32x2*>(at(gDel, static_cast<uint32_t>((r0 + prow) * DV + col)));
+    }
+    rtp = tp_word(J);
+    const TC* sj = gS + static_cast<size_t>(J) * DK * DV;
+#pragma unroll
+    for (int k2 = 0; k2 < SPT; ++k2)
+      rss[k2] = *reinterpret_cast<const u32x4*>(at(sj, static_cast<uint32_t>((tid + k2 * NTH) * SEW)));
+  };
+  // the inputs at the output mapping: issued once the step's outputs are
+  // written (their registers are then free)
+  auto prefetch_r_out = [&](int J) {
+    const int r0 = 16 * J;
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const uint32_t o = gi(r0 + 4 * g + ii, colv(n));
+        oq[n][ii] = ldv(qb, o);
+        og[n][ii] = ldv(gb, o);
+        ov[n][ii] = ldv(vb, o);
+        ow[n][ii] = ldv(wb, o);
+        ok[n][ii] = ldv(kb, o);
+        oe[n][ii] = ldv(eb, o);
+      }
+  };
+  // block-start state words of column pass p into sSS
+  auto commit_state = [&](const u32x4* words, int p) {
+#pragma unroll
+    for (int k2 = 0; k2 < SPT; ++k2) {
+      const int w = tid + k2 * NTH;
+      const int row = w / SWR;
+      const int colw = (w - row * SWR) * SEW;
+      if (colw / SW == p) *reinterpret_cast<u32x4*>(&sSS[row][colw - p * SW]) = words[k2];
+    }
+  };
+  // Ke = k exp(B_{J+1} - Lam) rows; X = ek exp(Lam - B_J), Y = qt exp(Lam - B_J),
+  // Xhat = ek exp(Lam - B_{J+1}), Yhat = qt exp(Lam - B_{J+1}), Z = k exp(B_J - Lam)
+  // transposed; the factors exp(Lam - B_J), exp(B_{J+1} - Lam).  Xhat, Yhat, Z
+  // (>= 1) only on leaves within LEAF_SAFE_RANGE.  Returns that flag.
+  auto commit_r = [&](int J) -> int {
+    const int safe = !((sUnsafe >> J) & 1);
+    float loc[RPT], suf[RPT];
+    block_sums(J, xl, loc, suf);
+#pragma unroll
+    for (int h4 = 0; h4 < RPT / 4; ++h4) {
+      f32x4 tA, tB, tY, tX, tZ;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int rr = 4 * h4 + q4;
+        const int r = RPT * part + rr;
+        const float fs = __expf(loc[rr]);
+        const float fe2 = __expf(suf[rr]);
+        const float ie = safe ? __expf(-suf[rr]) : 0.f;
+        const float zi = safe ? __expf(-loc[rr]) : 0.f;
+        const float ek = xe[rr] * xk[rr];
+        const float qt = xg[rr] * xq[rr];
+        sFs[r][ej] = fs;
+        sFe[r][ej] = fe2;
+        sRowA[r][ej] = M::cvt(xk[rr] * fe2);
+        tA[q4] = ek * fs;
+        tB[q4] = qt * fs;
+        tY[q4] = qt * ie;
+        tX[q4] = ek * ie;
+        tZ[q4] = xk[rr] * zi;
+      }
+      const int t0 = RPT * part + 4 * h4;
+      store4(&sTA[ej][t0], tA);
+      store4(&sTB[ej][t0], tB);
+      store4(&sTY[ej][t0], tY);
+      store4(&sTX[ej][t0], tX);
+      store4(&sTZ[ej][t0], tZ);
+    }
+#pragma unroll
+    for (int e = 0; e < RW; ++e) {
+      const int col = pc0 + e * EPW;
+      *reinterpret_cast<u32x2*>(&sDO[prow][col]) = rdo[e];
+      *reinterpret_cast<u32x2*>(&sDL[prow][col]) = rdl[e];
+    }
+    tp_commit(rtp);
+    commit_state(rss, 0);
+    __syncthreads();
+    return safe;
+  };
+
+  prefetch_r(NB - 1);
+  prefetch_r_out(NB - 1);
   f32x4 D[RT][NT];
   load_state(D, dSC);
-  // chunk-end term rowsum(S_C * dS_C): S holds S_C here and D holds dS_C
+  // chunk-end term rowsum(S_C * dS_C): S holds S_C here and D holds dS_C;
+  // it enters dlog_a on every token of the chunk
 #pragma unroll
   for (int s = 0; s < RT; ++s)
 #pragma unroll
@@ -508,35 +515,42 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       a = sum16(a);
       if (c16 == 0) sRow[wave][16 * s + 4 * g + i] = a;
     }
+  __syncthreads();
+  float carry[NT];  // sum of dLam over the finished (later) tokens, channel colv(n)
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) t += sRow[w][colv(n)];
+    carry[n] = t;
+  }
+  __syncthreads();  // sRow is read before the first commit overwrites it
+
 #pragma unroll 1
   for (int J = NB - 1; J >= 0; --J) {
     const int r0 = 16 * J;
-    const int st = NB + (NB - 1 - J);
-    const int safe = commit(st);
-    float vcur[NT][4], wcur[NT][4];
+    const int safe = commit_r(J);
+    u32x4 css[SPLIT > 1 ? SPT : 1];  // this block's state words for the later column passes
+    if (SPLIT > 1) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        vcur[n][ii] = oa[n][ii];
-        wcur[n][ii] = ob[n][ii];
-      }
-    prefetch(st + 1);
-    frag ptf, ttf;
-    {
-      f32x4 pv, tv;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        tv[i] = M::to_f32(sT[4 * g + i][c16]);
-        pv[i] = M::to_f32(sP[4 * g + i][c16]);
-      }
-      ptf = M::from_f32(pv);
-      ttf = M::from_f32(tv);
+      for (int k2 = 0; k2 < SPT; ++k2) css[k2] = rss[k2];
     }
+    prefetch_r(J > 0 ? J - 1 : 0);
     // dR_J = T_JJ^T (Ke_J D + P_JJ^T dO_J)
     f32x4 dRn[NT];
     frag dOf[NT];
     {
+      frag ptf, ttf;
+      {
+        f32x4 pv, tv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          tv[i] = M::to_f32(sT[4 * g + i][c16]);
+          pv[i] = M::to_f32(sP[4 * g + i][c16]);
+        }
+        ptf = M::from_f32(pv);
+        ttf = M::from_f32(tv);
+      }
       f32x4 acc[NT];
 #pragma unroll
       for (int n = 0; n < NT; ++n) acc[n] = zero4();
@@ -556,55 +570,133 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         dRn[n] = M::mma(ttf, M::from_f32(acc[n]), zero4());
       }
     }
-    // dR rows take the place of the step before's (write*v)^T tile
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      store_rows(dRn[n], sDR, gdR + static_cast<size_t>(r0) * DV, 16 * (NT * wave + n));
+      store4(&sDR[c16][col0(n) + 4 * g], turn(dRn[n]));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t o = gi(r0 + 4 * g + i, colv(n));
-        *at(dwb, o) = vcur[n][i] * dRn[n][i];
-        *at(dvb, o) = wcur[n][i] * dRn[n][i];
+        *at(dwb, o) = ov[n][i] * dRn[n][i];
+        *at(dvb, o) = ow[n][i] * dRn[n][i];
       }
     }
-    __syncthreads();
-    if (wave == 0) leaf_dot(sDO, sDL, false, sLf[0]);      // dO_r . Delta_i, r >= i
-    if (wave == 1 % NW) leaf_dot(sDR, sDL, true, sLf[1]);  // dR_r . Delta_i, r > i
-    // d(k)_i = exp(B_{J+1} - Lam_i) [ D Delta_i + sum_{r>=i} (dO_r.Delta_i) Yhat_r - sum_{r>i} (dR_r.Delta_i) Xhat_r ]
-    f32x4 acc2[NT];
-    state_rows(D, sDL, acc2);
-    if (safe) {
-      f32x4 l1, l2;
+    // Boundary parts, in column passes over dv:
+    //   d(k)_i <- Delta_i . D rows,  d(qt)_r <- dO_r . S_J rows,  d(ek)_r <- dR_r . S_J rows
+    f32x4 acck[NT], accq[NT], acce[NT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        l1[i] = sLf[0][4 * g + i][c16];
-        l2[i] = -sLf[1][4 * g + i][c16];
+    for (int n = 0; n < NT; ++n) {
+      acck[n] = zero4();
+      accq[n] = zero4();
+      acce[n] = zero4();
+    }
+#pragma unroll
+    for (int p = 0; p < SPLIT; ++p) {
+      if (p > 0) {
+        __syncthreads();  // the previous pass's reads of the staging tiles are done
+        commit_state(css, p);
       }
-      const frag l1f = M::from_f32(l1), l2f = M::from_f32(l2);
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        acc2[n] = M::mma(l1f, M::load(&sTY[colv(n)][4 * g]), acc2[n]);
-        acc2[n] = M::mma(l2f, M::load(&sTZ[colv(n)][4 * g]), acc2[n]);
+        const int cb = col0(n) - p * SW;
+        if (cb >= 0 && cb < SW) {
+#pragma unroll
+          for (int s = 0; s < RT; ++s) store4(&sSD[16 * s + c16][cb + 4 * g], turn(D[s][n]));
+        }
+      }
+      __syncthreads();  // also publishes the dR rows
+#pragma unroll
+      for (int kk = 0; kk < SW / 16; ++kk) {
+        const int cc = p * SW + 16 * kk + 4 * g;
+        const frag al = M::load(&sDL[c16][cc]);
+        const frag ao = M::load(&sDO[c16][cc]);
+        const frag ar = M::load(&sDR[c16][cc]);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const frag bd = M::load(&sSD[colv(n)][16 * kk + 4 * g]);
+          const frag bs = M::load(&sSS[colv(n)][16 * kk + 4 * g]);
+          acck[n] = M::mma(al, bd, acck[n]);
+          accq[n] = M::mma(ao, bs, accq[n]);
+          acce[n] = M::mma(ar, bs, acce[n]);
+        }
       }
     }
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
+    // Leaf parts
+    if (safe) {
+      // rows i on lanes, contraction over r:  (dO_r . Delta_i) Yhat_r, r >= i;  -(dR_r . Delta_i) Xhat_r, r > i
+      f32x4 l0 = leaf_pair(sDO, sDL), l1 = leaf_pair(sDR, sDL);
+      // rows r on lanes, contraction over i:  (Delta_i . dO_r) Z_i, i <= r;  (Delta_i . dR_r) Z_i, i < r
+      f32x4 m0 = leaf_pair(sDL, sDO), m1 = leaf_pair(sDL, sDR);
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const int i = 4 * g + ii;
-        const int j = colv(n);
-        float val = sF[i][j] * acc2[n][ii];
-        if (!safe)
-          for (int r = i; r < 16; ++r) {
-            const float f = pair_factor(r, i, j);
+        const int a = 4 * g + ii;
+        l0[ii] = (c16 <= a) ? l0[ii] : 0.f;
+        l1[ii] = (c16 < a) ? -l1[ii] : 0.f;
+        m0[ii] = (a <= c16) ? m0[ii] : 0.f;
+        m1[ii] = (a < c16) ? m1[ii] : 0.f;
+      }
+      const frag l0f = M::from_f32(l0), l1f = M::from_f32(l1), m0f = M::from_f32(m0), m1f = M::from_f32(m1);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        acck[n] = M::mma(l0f, M::load(&sTY[colv(n)][4 * g]), acck[n]);
+        acck[n] = M::mma(l1f, M::load(&sTX[colv(n)][4 * g]), acck[n]);
+        const frag zb = M::load(&sTZ[colv(n)][4 * g]);
+        accq[n] = M::mma(m0f, zb, accq[n]);
+        acce[n] = M::mma(m1f, zb, acce[n]);
+      }
+    } else {
+      if (wave == 0) leaf_dot(sDO, sDL, false, sLf[0]);      // dO_r . Delta_i, i <= r
+      if (wave == 1 % NW) leaf_dot(sDR, sDL, true, sLf[1]);  // dR_r . Delta_i, i < r
+      __syncthreads();
+    }
+    // per-token gradients; dlog_a as the suffix sum of dLam
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int j = colv(n);
+      float dl[4];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int t = 4 * g + ii;  // token of the block
+        float vk = sFe[t][j] * acck[n][ii];  // d(k)_t
+        float vq = sFs[t][j] * accq[n][ii];  // d(qt)_t
+        float ve = sFs[t][j] * acce[n][ii];  // -d(ek)_t
+        if (!safe) {
+          for (int r = t; r < 16; ++r) {
+            const float f = pair_factor(r0, r, t, j);
             const uint32_t orj = gi(r0 + r, j);
             const float qt = ldv(gb, orj) * ldv(qb, orj);
             const float ek = ldv(eb, orj) * ldv(kb, orj);
-            val += f * (sLf[0][r][i] * qt - sLf[1][r][i] * ek);
+            vk += f * (sLf[0][r][t] * qt - sLf[1][r][t] * ek);
           }
-        *at(dkb, gi(r0 + i, j)) = val;
-        if (J == 0) dk0[n][ii] = val;  // F2's block 0 reads it from here
+          for (int i2 = 0; i2 <= t; ++i2) {
+            const float f = pair_factor(r0, t, i2, j) * ldv(kb, gi(r0 + i2, j));
+            vq += sLf[0][t][i2] * f;
+            ve += sLf[1][t][i2] * f;
+          }
+        }
+        const float dek = -ve;
+        const uint32_t o = gi(r0 + t, j);
+        *at(dqb, o) = og[n][ii] * vq;
+        *at(dgb, o) = oq[n][ii] * vq;
+        *at(deb, o) = ok[n][ii] * dek;
+        *at(dkb, o) = vk + oe[n][ii] * dek;
+        dl[ii] = oe[n][ii] * ok[n][ii] * dek + og[n][ii] * oq[n][ii] * vq - ok[n][ii] * vk;
       }
+      // suffix sums over the block's tokens (4g..4g+3 in this lane, the other
+      // token groups in lanes c16 + 16g')
+      const float tsum = dl[0] + dl[1] + dl[2] + dl[3];
+      const float t0 = __shfl(tsum, c16, 64);
+      const float t1 = __shfl(tsum, c16 + 16, 64);
+      const float t2 = __shfl(tsum, c16 + 32, 64);
+      const float t3 = __shfl(tsum, c16 + 48, 64);
+      float run = carry[n] + (g < 3 ? t3 : 0.f) + (g < 2 ? t2 : 0.f) + (g < 1 ? t1 : 0.f);
+#pragma unroll
+      for (int ii = 3; ii >= 0; --ii) {
+        run += dl[ii];
+        *at(dlb, gi(r0 + 4 * g + ii, j)) = run;
+      }
+      carry[n] += t0 + t1 + t2 + t3;
+    }
+    prefetch_r_out(J > 0 ? J - 1 : 0);
     // D <- diag(exp(B_{J+1} - B_J)) D + Y_J^T dO_J - X_J^T dR_J
     {
       frag dRf[NT];
@@ -624,138 +716,23 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     }
     __syncthreads();
   }
-
-  // ================= F2: forward sweep: d(ek), totals ==================
-  load_state(S, S0c);
-  float prefix[NT];  // sum of dLam over the finished blocks, channel colv(n)
-#pragma unroll
-  for (int n = 0; n < NT; ++n) prefix[n] = 0.f;
-#pragma unroll 1
-  for (int I = 0; I < NB; ++I) {
-    const int r0 = 16 * I;
-    const int st = 2 * NB + I;
-    const int safe = commit(st);
-    float kcur[NT][4], ecur[NT][4], dkcur[NT][4], dlcur[NT][4];
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        kcur[n][ii] = oa[n][ii];
-        ecur[n][ii] = ob[n][ii];
-        dkcur[n][ii] = I != 0 ? oc[n][ii] : dk0[n][ii];
-        dlcur[n][ii] = od[n][ii];
-      }
-    prefetch(st + 1);
-    if (wave == 0) leaf_dot(sDR, sDL, true, sLf[1]);  // dR_r . Delta_i, i < r
-    f32x4 acc[NT];
-    state_rows(S, sDR, acc);
-    if (safe) {
-      f32x4 lf;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lf[i] = sLf[1][c16][4 * g + i];
-      const frag lff = M::from_f32(lf);
-#pragma unroll
-      for (int n = 0; n < NT; ++n) acc[n] = M::mma(lff, M::load(&sTZ[colv(n)][4 * g]), acc[n]);
-    }
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const int j = colv(n);
-      float dl[4];
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int r = 4 * g + ii;
-        float val = sF[r][j] * acc[n][ii];
-        if (!safe)
-          for (int i2 = 0; i2 < r; ++i2) val += sLf[1][r][i2] * pair_factor(r, i2, j) * ldv(kb, gi(r0 + i2, j));
-        const float dek = -val;  // d(ek)_r = -S'_r dR_r
-        const float kj = kcur[n][ii];
-        const float bj = ecur[n][ii];
-        const uint32_t o = gi(r0 + r, j);
-        *at(deb, o) = kj * dek;
-        *at(dkb, o) = dkcur[n][ii] + bj * dek;
-        dl[ii] = dlcur[n][ii] - kj * dkcur[n][ii] + bj * kj * dek;
-      }
-      // exclusive prefix of dLam over the chunk, in token order
-      const float tsum = dl[0] + dl[1] + dl[2] + dl[3];
-      const float t0 = __shfl(tsum, c16, 64);
-      const float t1 = __shfl(tsum, c16 + 16, 64);
-      const float t2 = __shfl(tsum, c16 + 32, 64);
-      const float t3 = __shfl(tsum, c16 + 48, 64);
-      float run = prefix[n] + (g > 0 ? t0 : 0.f) + (g > 1 ? t1 : 0.f) + (g > 2 ? t2 : 0.f);
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        *at(dlb, gi(r0 + 4 * g + ii, j)) = run;
-        run += dl[ii];
-      }
-      prefix[n] += t0 + t1 + t2 + t3;
-    }
-    // S_{I+1} = diag(g_I) S_I + Ke_I^T Delta_I
-    {
-      frag df[NT];
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        f32x4 dlt;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dlt[i] = M::to_f32(sDL[4 * g + i][colv(n)]);
-        df[n] = M::from_f32(dlt);
-      }
-#pragma unroll
-      for (int s = 0; s < RT; ++s) {
-        const frag ka = M::load(&sTA[16 * s + c16][4 * g]);
-        const f32x4 gs = decay_scale(s);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) S[s][n] = M::mma(ka, df[n], S[s][n] * gs);
-      }
-    }
-    __syncthreads();
-  }
-
-  // ---- dlog_a_i = total - exclusive prefix (total includes rowsum(S_C * dS_C)) ----
-  if (g == 0) {
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      float tot = prefix[n];
-#pragma unroll
-      for (int w = 0; w < NW; ++w) tot += sRow[w][colv(n)];
-      sTot[colv(n)] = tot;
-    }
-  }
-  __syncthreads();
-  constexpr int FPT = C * DK / NTH;  // elements per thread
-  constexpr int FB = FPT < 8 ? FPT : 8;
-  static_assert(FPT % FB == 0, "final pass batches");
-#pragma unroll 1
-  for (int b0 = 0; b0 < FPT; b0 += FB) {
-    float x[FB];
-#pragma unroll
-    for (int u = 0; u < FB; ++u) {
-      const int idx = tid + (b0 + u) * NTH;
-      x[u] = *at(dlb, gi(idx / DK, idx % DK));
-    }
-#pragma unroll
-    for (int u = 0; u < FB; ++u) {
-      const int idx = tid + (b0 + u) * NTH;
-      *at(dlb, gi(idx / DK, idx % DK)) = sTot[idx % DK] - x[u];
-    }
-  }
 }
 
 }  // namespace
 
 size_t bwd_chunk_scratch_bytes(const ChunkShape& s) {
-  return s.bf16 ? bwd_scratch_bytes_tc<uint16_t>(s.C, s.DV) : bwd_scratch_bytes_tc<float>(s.C, s.DV);
+  return s.bf16 ? bwd_scratch_bytes_tc<uint16_t>(s.C, s.DK, s.DV) : bwd_scratch_bytes_tc<float>(s.C, s.DK, s.DV);
 }
 
 hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, const void* v,
                             const void* log_a, const void* erase, const void* write,
                             const void* gamma, const void* summ, const float* S_chunks,
                             const float* dS_chunks, const void* dO, float* dq, float* dk, float* dv,
-                            float* dlog_a,
-                            float* derase, float* dwrite, float* dgamma, void* scratch,
+                            float* dlog_a, float* derase, float* dwrite, float* dgamma, void* scratch,
                             hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(s.nchunks());
   if (grid == 0) return hipSuccess;
-#define MUIR_BCH1(TT, DD, CC, NW)                                                                  \
+#define MUIR_BCH1(TT, DD, CC, NW)                                                                      \
   hipLaunchKernelGGL((bwd_chunk_kernel<TT, DD, CC, NW>), dim3(grid), dim3(64 * NW), 0, stream, s.T, s.H, \
                      (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, (const TT*)erase,      \
                      (const TT*)write, (const TT*)gamma, (const char*)summ, s.summary_bytes(),          \
