@@ -13,8 +13,10 @@ Beside it the line carries:
   kernels       the same for every kernel of the step
   cpu_baseline  the fp64 sequential oracle on the host cores, on a bounded
                 sample of the same workload (4 batch rows: 64 heads x 4096)
-  secondary     long-context fwd+bwd (T=32768, chunk 128 and 256) and the
-                streaming decode step (64 streams x 16 heads, 4096 steps)
+  secondary     long-context fwd+bwd (T=32768, chunk 128 and 256), one
+                1M-token stream (chunked prefill chained through the state,
+                then decode), and the streaming decode step (64 streams x 16
+                heads, 4096 steps)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -227,6 +229,53 @@ def decode_bench(m, torch, hiprt, N=64, H=16, d=128, steps=4096, seed=0):
             "note": "state (%d MiB) may be served partly from the 256 MB Infinity Cache" % (N * H * d * d * 4 >> 20)}
 
 
+def stream_bench(m, torch, hiprt, T=1 << 20, H=16, d=128, seg=32768, chunk=64, steps=1024, seed=0):
+    """One long stream (B=1): chunked prefill of T tokens in `seg`-token
+    segments chained through the state (S_T -> S0), then `steps` decode tokens
+    from that state.  Inputs are drawn on the GPU (torch generator)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    bf = torch.bfloat16
+
+    def unit(x):
+        s = torch.nn.functional.silu(x)
+        return s / s.norm(dim=-1, keepdim=True).clamp_min(1e-12)
+
+    def draw(n):
+        shp = (1, n, H, d)
+        rates = torch.exp(torch.empty((H, d), device="cuda").uniform_(-9.2103, 1.0986, generator=g))
+        return [unit(torch.randn(shp, generator=g, device="cuda")).to(bf),
+                unit(torch.randn(shp, generator=g, device="cuda")).to(bf),
+                torch.randn(shp, generator=g, device="cuda").to(bf),
+                (-rates).expand(shp).to(bf).contiguous(),
+                torch.sigmoid(torch.randn(shp, generator=g, device="cuda")).to(bf),
+                torch.sigmoid(torch.randn(shp, generator=g, device="cuda")).to(bf),
+                (2 * torch.sigmoid(torch.randn(shp, generator=g, device="cuda"))).to(bf)]
+
+    segs = [draw(seg) for _ in range(T // seg)]
+    dec = [t[0].contiguous() for t in draw(steps)]  # [steps, H, d]
+    ws = torch.empty(m.muir_chunk_fwd_workspace(1, seg, H, d, d, chunk), dtype=torch.uint8, device="cuda")
+    o = torch.empty((1, seg, H, d), dtype=bf, device="cuda")
+    m.muir_chunk_fwd(*segs[0], chunk=chunk, workspace=ws, out=o)  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    S = None
+    for x in segs:
+        _, S, _ = m.muir_chunk_fwd(*x, S, chunk=chunk, workspace=ws, out=o)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    od = torch.empty((1, H, d), dtype=bf, device="cuda")
+    for t in range(steps):
+        m.muir_step(*(x[t:t + 1] for x in dec), S, out=od)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    del segs, dec
+    torch.cuda.empty_cache()
+    return {"workload": f"one stream, H={H} d={d}: prefill {T} tokens in {seg}-token segments "
+                        f"(chunk {chunk}, state chained), then {steps} decode tokens",
+            "prefill_tokens_per_s": T / (t1 - t0), "decode_us_per_token": (t2 - t1) * 1e6 / steps}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -315,6 +364,10 @@ def main():
             log(f"[bench]   {sec[name]['tokens_per_s']:.4g} tokens/s")
             del dv2
             torch.cuda.empty_cache()
+        log("[bench] secondary stream (1M-token prefill, then decode)")
+        sec["stream_1m"] = stream_bench(m, torch, hiprt)
+        log(f"[bench]   prefill {sec['stream_1m']['prefill_tokens_per_s']:.4g} tokens/s, "
+            f"decode {sec['stream_1m']['decode_us_per_token']:.1f} us/token")
         log(f"[bench] secondary decode ({args.decode_steps} steps)")
         sec["decode_64x16"] = decode_bench(m, torch, hiprt, steps=args.decode_steps)
         log(f"[bench]   {sec['decode_64x16']['kernel_us_per_step']:.2f} us/step kernel")
