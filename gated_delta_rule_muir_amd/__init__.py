@@ -178,7 +178,10 @@ def muir_chunk_bwd(q, k, v, log_a, erase, write, gamma, dO, S0=None, S_chunks=No
 
     `S_chunks` (from muir_chunk_fwd(save_states=True)) and `summaries` (the
     `workspace` tensor of that forward call, left unchanged) are saved forward
-    results; each one that is None is recomputed inside."""
+    results; each one that is None is recomputed inside.  For bf16 with
+    chunk 64 they are used only as a pair (the summaries then also hold the
+    chunk deltas that the saving forward kept): both are recomputed when
+    either is None."""
     B, T, H, dk = q.shape
     dv = v.shape[3]
     dev, dt = q.device, q.dtype

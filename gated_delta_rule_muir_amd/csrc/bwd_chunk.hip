@@ -59,12 +59,12 @@ template <typename TC, int DK, int C> constexpr int stage_split() {
   return DK == 64 ? 1 : (sizeof(TC) == 2 ? (C == 64 ? 1 : 2) : (C == 64 ? 4 : 8));
 }
 
-template <typename Tin, int DK, int C, int NW>
+template <typename Tin, int DK, int C, int NW, bool DIRECT>
 __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     int T, int H, const Tin* __restrict__ q, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ log_a, const Tin* __restrict__ erase,
     const Tin* __restrict__ write, const Tin* __restrict__ gamma, const char* __restrict__ summ,
-    size_t summ_bytes, size_t tp_offset, const float* __restrict__ S_chunks,
+    size_t summ_bytes, size_t tp_offset, size_t dl_offset, const float* __restrict__ S_chunks,
     const float* __restrict__ dS_chunks, const Tin* __restrict__ dO, float* __restrict__ dq,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dlog_a,
     float* __restrict__ derase, float* __restrict__ dwrite, float* __restrict__ dgamma,
@@ -96,6 +96,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   static_assert(NT >= 1 && NW * NT * 16 == DV && TPC * RPT == 16 && RPT % 4 == 0 && RW >= 1 &&
                     EPT % EPW == 0 && TPW <= NTH && SPT * NTH == DK * SWR && SW % SEW == 0,
                 "thread layout");
+  static_assert(!DIRECT || SPLIT == 1, "the direct form stages S0 once, whole");
 
   const int NC = T / C;
   const int chunk = blockIdx.x;
@@ -154,14 +155,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   __shared__ __attribute__((aligned(16))) TC sTX[DK][TP];    // R: Xhat^T
   __shared__ __attribute__((aligned(16))) TC sTZ[DK][TP];    // R: Z^T
   __shared__ __attribute__((aligned(16))) TC sDO[16][PV];    // dO rows of the block
-  __shared__ __attribute__((aligned(16))) TC sDL[16][PV];    // delta rows of the block
+  __shared__ __attribute__((aligned(16))) TC sDL[DIRECT ? C : 16][PV];  // delta rows (direct: of the chunk)
   __shared__ __attribute__((aligned(16))) TC sDR[16][PV];    // dR rows of the block
   __shared__ __attribute__((aligned(16))) TC sT[16][TP];     // T_II of the block
   __shared__ __attribute__((aligned(16))) TC sP[16][TP];     // P_II of the block
   __shared__ __attribute__((aligned(16))) TC sSD[DK][PS];    // staged D columns, [dk][dv]
-  __shared__ __attribute__((aligned(16))) TC sSS[DK][PS];    // staged S_J columns, [dk][dv]
+  __shared__ __attribute__((aligned(16))) TC sSS[DK][PS];    // staged S_J (direct: S0) columns, [dk][dv]
   __shared__ float sLf[2][16][17];                           // leaf matrices of steep blocks
   __shared__ float sG[DK];
+  __shared__ float sGH[DIRECT ? NB - 1 : 1][DK];              // direct: block decays exp(B_{I+1} - B_I)
   // per-wave partial rowsums of S_C * dS_C, used once before the reverse
   // sweep (which then writes Yhat^T over it)
   static_assert(NW * DK * sizeof(float) <= sizeof(TC) * DK * TP, "rowsum scratch");
@@ -336,61 +338,147 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
 
   f32x4 S[RT][NT];
   load_state(S, S0c);
-  prefetch_f(0);
-  __syncthreads();  // sPart, sBsum, sUnsafe
-
-#pragma unroll 1
-  for (int I = 0; I < NB; ++I) {
-    const int r0 = 16 * I;
-    commit_f(I);
-    prefetch_f(I + 1 < NB ? I + 1 : I);
-    frag Sf[RT][NT];
+  // Direct form: the operands of the Horner steps below, Ke_I = k exp(B_{I+1} - Lam)
+  // at (token 4g+i of block I, channel colv(n)), and the block decays
+  // exp(B_{I+1} - B_I) in sGH, for every block but the last.
+  frag keH[DIRECT ? NB - 1 : 1][NT];
+  if constexpr (DIRECT) {
+    // the chunk's deltas (kept by the forward scan) into sDL, S0 into sSS
+    {
+      const TC* gD = reinterpret_cast<const TC*>(summ + static_cast<size_t>(chunk) * summ_bytes + dl_offset);
+      constexpr int DWR = DV / SEW;       // 16-byte words per delta row
+      constexpr int DWT = C * DWR / NTH;  // per thread
+      static_assert(DWT * NTH == C * DWR, "delta words");
+      u32x4 dw[DWT];
+#pragma unroll
+      for (int k2 = 0; k2 < DWT; ++k2)
+        dw[k2] = *reinterpret_cast<const u32x4*>(at(gD, static_cast<uint32_t>((tid + k2 * NTH) * SEW)));
+#pragma unroll
+      for (int k2 = 0; k2 < DWT; ++k2) {
+        const int w = tid + k2 * NTH;
+        const int row = w / DWR;
+        *reinterpret_cast<u32x4*>(&sDL[row][(w - row * DWR) * SEW]) = dw[k2];
+      }
+    }
 #pragma unroll
     for (int s = 0; s < RT; ++s)
 #pragma unroll
-      for (int n = 0; n < NT; ++n) Sf[s][n] = M::from_f32(S[s][n]);
-    // the block-start state, as [dk][dv] rows, for the reverse sweep
+      for (int n = 0; n < NT; ++n) store4(&sSS[16 * s + c16][col0(n) + 4 * g], turn(S[s][n]));
+#pragma unroll
+    for (int I = 0; I < NB - 1; ++I)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        float l[4], kk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t o = gi(16 * I + 4 * g + i, colv(n));
+          l[i] = ldv(lb, o);
+          kk[i] = ldv(kb, o);
+        }
+        // log-decay after each token to the block's end: within the lane's
+        // four tokens, plus the token groups of the lanes c16 + 16g' (g' > g)
+        const float s4 = (l[0] + l[1]) + (l[2] + l[3]);
+        const float t1 = __shfl(s4, c16 + 16, 64);
+        const float t2 = __shfl(s4, c16 + 32, 64);
+        const float t3 = __shfl(s4, c16 + 48, 64);
+        const float t0 = __shfl(s4, c16, 64);
+        float later = (g < 3 ? t3 : 0.f) + (g < 2 ? t2 : 0.f) + (g < 1 ? t1 : 0.f);
+        f32x4 kv;
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+          kv[i] = kk[i] * __expf(later);
+          later += l[i];
+        }
+        keH[I][n] = M::from_f32(kv);
+        if (g == 0) sGH[I][colv(n)] = __expf(((t0 + t1) + t2) + t3);
+      }
+    __syncthreads();  // sDL, sSS, sGH, sPart, sUnsafe
+    // S becomes the chunk-end state S_C = diag(Gamma_C) S0 + Kbar^T Delta
+    // (for the rowsum term below), with Kbar^T and Gamma_C of the summary
     {
-      TC* dst = gS + static_cast<size_t>(I) * DK * DV;
+      const char* cs = summ + static_cast<size_t>(chunk) * summ_bytes;
+      const TC* gKT = reinterpret_cast<const TC*>(cs) + summary_part(SP_KBT, C, DK, DV);
+      const float* gGC = reinterpret_cast<const float*>(cs + summary_part(SP_END, C, DK, DV) * sizeof(TC));
+      frag dcol[NB][NT];  // Delta at (token 4g+i of block m, column colv(n))
+#pragma unroll
+      for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          f32x4 t;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) t[i] = M::to_f32(sDL[16 * m + 4 * g + i][colv(n)]);
+          dcol[m][n] = M::from_f32(t);
+        }
+#pragma unroll
+      for (int s = 0; s < RT; ++s) {
+        const f32x4 gc = *reinterpret_cast<const f32x4*>(at(gGC, static_cast<uint32_t>(16 * s + 4 * g)));
+#pragma unroll
+        for (int n = 0; n < NT; ++n) S[s][n] *= gc;
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+          const frag ka = M::load(at(gKT, static_cast<uint32_t>((16 * s + c16) * C + 16 * m + 4 * g)));
+#pragma unroll
+          for (int n = 0; n < NT; ++n) S[s][n] = M::mma(ka, dcol[m][n], S[s][n]);
+        }
+      }
+    }
+  } else {
+    prefetch_f(0);
+    __syncthreads();  // sPart, sUnsafe
+
+#pragma unroll 1
+    for (int I = 0; I < NB; ++I) {
+      const int r0 = 16 * I;
+      commit_f(I);
+      prefetch_f(I + 1 < NB ? I + 1 : I);
+      frag Sf[RT][NT];
 #pragma unroll
       for (int s = 0; s < RT; ++s)
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const f32x4 tt = M::mma(Sf[s][n], ident, zero4());  // row 16s+c16, columns col0(n)+4g+i
-          store4(at(dst, static_cast<uint32_t>((16 * s + c16) * DV + col0(n) + 4 * g)), tt);
-        }
-    }
-    // Delta_I = T_II (U_I - X_I S_I)
-    f32x4 Dl[NT];
-    {
-      f32x4 xs[NT];
+        for (int n = 0; n < NT; ++n) Sf[s][n] = M::from_f32(S[s][n]);
+      // the block-start state, as [dk][dv] rows, for the reverse sweep
+      {
+        TC* dst = gS + static_cast<size_t>(I) * DK * DV;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) xs[n] = zero4();
+        for (int s = 0; s < RT; ++s)
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            const f32x4 tt = M::mma(Sf[s][n], ident, zero4());  // row 16s+c16, columns col0(n)+4g+i
+            store4(at(dst, static_cast<uint32_t>((16 * s + c16) * DV + col0(n) + 4 * g)), tt);
+          }
+      }
+      // Delta_I = T_II (U_I - X_I S_I)
+      f32x4 Dl[NT];
+      {
+        f32x4 xs[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) xs[n] = zero4();
+#pragma unroll
+        for (int s = 0; s < RT; ++s) {
+          const frag xa = M::load(&sRowA[c16][16 * s + 4 * g]);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) xs[n] = M::mma(xa, Sf[s][n], xs[n]);
+        }
+        const frag ta = M::load(&sT[c16][4 * g]);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          f32x4 rhs = load4(&sTB[colv(n)][4 * g]);
+          rhs -= xs[n];
+          Dl[n] = M::mma(ta, M::from_f32(rhs), zero4());
+          store4(at(gDel, static_cast<uint32_t>((r0 + c16) * DV + col0(n) + 4 * g)), turn(Dl[n]));
+        }
+      }
+      // S_{I+1} = diag(exp(B_{I+1} - B_I)) S_I + Ke_I^T Delta_I
 #pragma unroll
       for (int s = 0; s < RT; ++s) {
-        const frag xa = M::load(&sRowA[c16][16 * s + 4 * g]);
+        const frag ka = M::load(&sTA[16 * s + c16][4 * g]);
+        const f32x4 gs = decay_scale(s);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) xs[n] = M::mma(xa, Sf[s][n], xs[n]);
+        for (int n = 0; n < NT; ++n) S[s][n] = M::mma(ka, M::from_f32(Dl[n]), S[s][n] * gs);
       }
-      const frag ta = M::load(&sT[c16][4 * g]);
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        f32x4 rhs = load4(&sTB[colv(n)][4 * g]);
-        rhs -= xs[n];
-        Dl[n] = M::mma(ta, M::from_f32(rhs), zero4());
-        store4(at(gDel, static_cast<uint32_t>((r0 + c16) * DV + col0(n) + 4 * g)), turn(Dl[n]));
-      }
+      __syncthreads();
     }
-    // S_{I+1} = diag(exp(B_{I+1} - B_I)) S_I + Ke_I^T Delta_I
-#pragma unroll
-    for (int s = 0; s < RT; ++s) {
-      const frag ka = M::load(&sTA[16 * s + c16][4 * g]);
-      const f32x4 gs = decay_scale(s);
-#pragma unroll
-      for (int n = 0; n < NT; ++n) S[s][n] = M::mma(ka, M::from_f32(Dl[n]), S[s][n] * gs);
-    }
-    __syncthreads();
-  }
+  }  // F sweep
 
   // =========================== R: reverse sweep ===========================
   // slots: log_a, k, erase, q, gamma (channel ej, tokens RPT*part + rr);
@@ -415,13 +503,16 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     for (int e = 0; e < RW; ++e) {
       const int col = pc0 + e * EPW;
       rdo[e] = *reinterpret_cast<const u32x2*>(at(dOb, gi(r0 + prow, col)));
-      rdl[e] = *reinterpret_cast<const u32x2*>(at(gDel, static_cast<uint32_t>((r0 + prow) * DV + col)));
+      if constexpr (!DIRECT)
+        rdl[e] = *reinterpret_cast<const u32x2*>(at(gDel, static_cast<uint32_t>((r0 + prow) * DV + col)));
     }
     rtp = tp_word(J);
-    const TC* sj = gS + static_cast<size_t>(J) * DK * DV;
+    if constexpr (!DIRECT) {
+      const TC* sj = gS + static_cast<size_t>(J) * DK * DV;
 #pragma unroll
-    for (int k2 = 0; k2 < SPT; ++k2)
-      rss[k2] = *reinterpret_cast<const u32x4*>(at(sj, static_cast<uint32_t>((tid + k2 * NTH) * SEW)));
+      for (int k2 = 0; k2 < SPT; ++k2)
+        rss[k2] = *reinterpret_cast<const u32x4*>(at(sj, static_cast<uint32_t>((tid + k2 * NTH) * SEW)));
+    }
   };
   // the inputs at the output mapping: issued once the step's outputs are
   // written (their registers are then free)
@@ -491,10 +582,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     for (int e = 0; e < RW; ++e) {
       const int col = pc0 + e * EPW;
       *reinterpret_cast<u32x2*>(&sDO[prow][col]) = rdo[e];
-      *reinterpret_cast<u32x2*>(&sDL[prow][col]) = rdl[e];
+      if constexpr (!DIRECT) *reinterpret_cast<u32x2*>(&sDL[prow][col]) = rdl[e];
     }
     tp_commit(rtp);
-    commit_state(rss, 0);
+    if constexpr (!DIRECT) commit_state(rss, 0);
     __syncthreads();
     return safe;
   };
@@ -529,6 +620,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
 #pragma unroll 1
   for (int J = NB - 1; J >= 0; --J) {
     const int r0 = 16 * J;
+    const TC (*dlJ)[PV] = DIRECT ? sDL + r0 : sDL;  // the block's delta rows
     const int safe = commit_r(J);
     u32x4 css[SPLIT > 1 ? SPT : 1];  // this block's state words for the later column passes
     if (SPLIT > 1) {
@@ -607,7 +699,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
 #pragma unroll
       for (int kk = 0; kk < SW / 16; ++kk) {
         const int cc = p * SW + 16 * kk + 4 * g;
-        const frag al = M::load(&sDL[c16][cc]);
+        const frag al = M::load(&dlJ[c16][cc]);
         const frag ao = M::load(&sDO[c16][cc]);
         const frag ar = M::load(&sDR[c16][cc]);
 #pragma unroll
@@ -620,12 +712,32 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         }
       }
     }
+    if constexpr (DIRECT) {
+      // d(qt), d(ek) boundary parts with S_J in place of S0:
+      //   S_J = exp(B_J) S0 + sum_{I<J} diag(exp(B_J - B_{I+1})) Ke_I^T Delta_I,
+      // so each row x of dO_J, dR_J takes, in Horner form over the earlier
+      // blocks I, acc <- exp(B_{I+1} - B_I) acc + (x . Delta_t) Ke_I[t] (every factor <= 1)
+#pragma unroll
+      for (int I = 0; I < NB - 1; ++I) {
+        if (I < J) {
+          // rows r of the block on lanes, contraction over the tokens t of block I
+          const frag mqf = M::from_f32(leaf_pair(sDL + 16 * I, sDO));
+          const frag mef = M::from_f32(leaf_pair(sDL + 16 * I, sDR));
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            const float gb = sGH[I][colv(n)];
+            accq[n] = M::mma(mqf, keH[I][n], accq[n] * gb);
+            acce[n] = M::mma(mef, keH[I][n], acce[n] * gb);
+          }
+        }
+      }
+    }
     // Leaf parts
     if (safe) {
       // rows i on lanes, contraction over r:  (dO_r . Delta_i) Yhat_r, r >= i;  -(dR_r . Delta_i) Xhat_r, r > i
-      f32x4 l0 = leaf_pair(sDO, sDL), l1 = leaf_pair(sDR, sDL);
+      f32x4 l0 = leaf_pair(sDO, dlJ), l1 = leaf_pair(sDR, dlJ);
       // rows r on lanes, contraction over i:  (Delta_i . dO_r) Z_i, i <= r;  (Delta_i . dR_r) Z_i, i < r
-      f32x4 m0 = leaf_pair(sDL, sDO), m1 = leaf_pair(sDL, sDR);
+      f32x4 m0 = leaf_pair(dlJ, sDO), m1 = leaf_pair(dlJ, sDR);
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int a = 4 * g + ii;
@@ -644,8 +756,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         acce[n] = M::mma(m1f, zb, acce[n]);
       }
     } else {
-      if (wave == 0) leaf_dot(sDO, sDL, false, sLf[0]);      // dO_r . Delta_i, i <= r
-      if (wave == 1 % NW) leaf_dot(sDR, sDL, true, sLf[1]);  // dR_r . Delta_i, i < r
+      if (wave == 0) leaf_dot(sDO, dlJ, false, sLf[0]);      // dO_r . Delta_i, i <= r
+      if (wave == 1 % NW) leaf_dot(sDR, dlJ, true, sLf[1]);  // dR_r . Delta_i, i < r
       __syncthreads();
     }
     // per-token gradients; dlog_a as the suffix sum of dLam
@@ -721,6 +833,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
 }  // namespace
 
 size_t bwd_chunk_scratch_bytes(const ChunkShape& s) {
+  if (s.bwd_direct()) return 0;
   return s.bf16 ? bwd_scratch_bytes_tc<uint16_t>(s.C, s.DK, s.DV) : bwd_scratch_bytes_tc<float>(s.C, s.DK, s.DV);
 }
 
@@ -732,25 +845,26 @@ hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, c
                             hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(s.nchunks());
   if (grid == 0) return hipSuccess;
-#define MUIR_BCH1(TT, DD, CC, NW)                                                                      \
-  hipLaunchKernelGGL((bwd_chunk_kernel<TT, DD, CC, NW>), dim3(grid), dim3(64 * NW), 0, stream, s.T, s.H, \
+#define MUIR_BCH1(TT, DD, CC, NW, DIR)                                                                      \
+  hipLaunchKernelGGL((bwd_chunk_kernel<TT, DD, CC, NW, DIR>), dim3(grid), dim3(64 * NW), 0, stream, s.T, s.H, \
                      (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, (const TT*)erase,      \
                      (const TT*)write, (const TT*)gamma, (const char*)summ, s.summary_bytes(),          \
-                     s.tp_offset(), S_chunks, dS_chunks, (const TT*)dO, dq, dk, dv, dlog_a, derase,     \
+                     s.tp_offset(), s.dl_offset(), S_chunks, dS_chunks, (const TT*)dO, dq, dk, dv, dlog_a, derase,     \
                      dwrite, dgamma, (char*)scratch)
-#define MUIR_BCH(TT, DD, NW)                         \
-  do {                                               \
-    if (s.C == 64) MUIR_BCH1(TT, DD, 64, NW);        \
-    else if (s.C == 128) MUIR_BCH1(TT, DD, 128, NW); \
-    else MUIR_BCH1(TT, DD, 256, NW);                 \
+#define MUIR_BCH(TT, DD, NW, DIR64)                         \
+  do {                                                      \
+    if (s.C == 64) MUIR_BCH1(TT, DD, 64, NW, DIR64);        \
+    else if (s.C == 128) MUIR_BCH1(TT, DD, 128, NW, false); \
+    else MUIR_BCH1(TT, DD, 256, NW, false);                 \
   } while (0)
-  // one 16-column tile per wave: 8 waves at d = 128, 4 at d = 64
+  // one 16-column tile per wave: 8 waves at d = 128, 4 at d = 64; the direct
+  // form exactly where ChunkShape::bwd_direct says so (bf16, C = 64)
   if (s.bf16) {
-    if (s.DK == 128) MUIR_BCH(uint16_t, 128, 8);
-    else MUIR_BCH(uint16_t, 64, 4);
+    if (s.DK == 128) MUIR_BCH(uint16_t, 128, 8, true);
+    else MUIR_BCH(uint16_t, 64, 4, true);
   } else {
-    if (s.DK == 128) MUIR_BCH(float, 128, 8);
-    else MUIR_BCH(float, 64, 4);
+    if (s.DK == 128) MUIR_BCH(float, 128, 8, false);
+    else MUIR_BCH(float, 64, 4, false);
   }
 #undef MUIR_BCH
 #undef MUIR_BCH1

@@ -67,8 +67,16 @@ template <typename T> __device__ __forceinline__ float ldv(const T* base, uint32
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Four consecutive elements of a compute type as one raw word (8 or 16 bytes).
+template <typename TC> struct Raw4;
+template <> struct Raw4<uint16_t> { typedef uint2 type; };
+template <> struct Raw4<float> { typedef uint4 type; };
+
+// Converted in pairs: a whole-vector conversion compiles to one conversion per
+// value plus byte permutes to merge them, a pairwise one to one per two values.
 __device__ __forceinline__ i16x4 pack4(f32x4 v) {
-  return __builtin_bit_cast(i16x4, __builtin_convertvector(v, bf16x4));
+  u32x2 r = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  return __builtin_bit_cast(i16x4, r);
 }
 
 // Load 4 consecutive elements (16-byte aligned for fp32, 8-byte for bf16).

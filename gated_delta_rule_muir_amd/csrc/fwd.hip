@@ -114,10 +114,12 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
   const Tin* gb = gamma + ebase;
   auto gi = [&](int t, int j) -> uint32_t { return static_cast<uint32_t>(t) * HD + static_cast<uint32_t>(j); };
 
-  __shared__ float sB[NB + 1][DK];     // B_I = Lam at the end of block I-1 (B_0 = 0)
-  __shared__ float sBsum[NB][DK];      // sum of log_a over block I  (= B_{I+1} - B_I)
-  __shared__ float sBsuf[NB][DK];      // sum of log_a over blocks >= I  (= B_NB - B_I)
-  __shared__ float sTmp[TPC][DK];
+  // per block I and channel: B_I = Lam at the end of block I-1 (B_0 = 0)
+  __shared__ float sPart[NB][TPC][DK]; // sum of log_a over each part's 4 tokens of block I
+  __shared__ float sEB[NB][DK];        // exp(B_I)
+  __shared__ float sEBS[NB][DK];       // exp(Lam_C - B_{I+1})
+  __shared__ float sGB[NB][DK];        // exp(B_{I+1} - B_I)
+  __shared__ int sUnsafe;              // bit I: block I beyond LEAF_SAFE_RANGE
   __shared__ float sL[16][DK + 1];     // log_a of the block's tokens (per-pair fallback)
   __shared__ __attribute__((aligned(16))) TC sX[16][PT];   // ek * exp(Lam - B_I)
   __shared__ __attribute__((aligned(16))) TC sY[16][PT];   // qt * exp(Lam - B_I)
@@ -134,30 +136,43 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
   __shared__ float sG[DK];
   __shared__ __attribute__((aligned(16))) TC sStage[16][2 * DK + 8];
 
-  // ---- block sums of the log-decay and their prefix/suffix sums ----
+  // ---- sums of the log-decay over each part of each block, the block
+  // boundaries' factors, and the blocks beyond LEAF_SAFE_RANGE ----
+  if (tid == 0) sUnsafe = 0;
 #pragma unroll
-  for (int I = part; I < NB; I += TPC) {
+  for (int I = 0; I < NB; ++I) {
     float sacc = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) sacc += ldv(lb, gi(16 * I + rr, ej));
-    sBsum[I][ej] = sacc;
+    for (int rr = 0; rr < 4; ++rr) sacc += ldv(lb, gi(16 * I + 4 * part + rr, ej));
+    sPart[I][part][ej] = sacc;
   }
   __syncthreads();
   if (tid < DK) {
-    float acc = 0.f;
-    sB[0][tid] = 0.f;
+    float bsum[NB];
+    unsigned mask = 0;
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
-      acc += sBsum[I][tid];
-      sB[I + 1][tid] = acc;
+      float bs = 0.f;
+#pragma unroll
+      for (int p = 0; p < TPC; ++p) bs += sPart[I][p][tid];
+      bsum[I] = bs;
+      sGB[I][tid] = __expf(bs);
+      if (!(-bs <= LEAF_SAFE_RANGE)) mask |= 1u << I;
     }
+    float acc = 0.f;
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      sEB[I][tid] = __expf(acc);
+      acc += bsum[I];
+    }
+    out.gC[tid] = __expf(acc);
     float suf = 0.f;
 #pragma unroll
     for (int I = NB - 1; I >= 0; --I) {
-      suf += sBsum[I][tid];
-      sBsuf[I][tid] = suf;
+      sEBS[I][tid] = __expf(suf);
+      suf += bsum[I];
     }
-    out.gC[tid] = __expf(acc);
+    if (mask) atomicOr(&sUnsafe, static_cast<int>(mask));
   }
   __syncthreads();
 
@@ -211,22 +226,21 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
         run += lv[rr];
         cs[rr] = run;
       }
-      sTmp[part][ej] = run;
       sf[3] = 0.f;
       sf[2] = lv[3];
       sf[1] = lv[3] + lv[2];
       sf[0] = lv[3] + lv[2] + lv[1];
     }
-    const float BI = sB[I][ej];
-    const float bsum = sBsum[I][ej];
-    const float bsuf1 = I + 1 < NB ? sBsuf[I + 1][ej] : 0.f;
-    const int safe = __syncthreads_and(-bsum <= LEAF_SAFE_RANGE);
+    const int safe = !((sUnsafe >> I) & 1);
     float excl = 0.f, exsuf = 0.f;
+#pragma unroll
     for (int p = 0; p < TPC; ++p) {
-      if (p < part) excl += sTmp[p][ej];
-      if (p > part) exsuf += sTmp[p][ej];
+      if (p < part) excl += sPart[I][p][ej];
+      if (p > part) exsuf += sPart[I][p][ej];
     }
-    if (part == 0) sG[ej] = __expf(bsum);
+    const float eBI = sEB[I][ej];    // exp(B_I)
+    const float eBS = sEBS[I][ej];   // exp(Lam_C - B_{I+1})
+    if (part == 0) sG[ej] = sGB[I][ej];
     f32x4 keT, uT, ktT, qhT, kbT;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -234,9 +248,9 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
       const float loc = excl + cs[rr];         // Lam_r - B_I        (<= 0)
       const float suf = sf[rr] + exsuf;        // B_{I+1} - Lam_r    (<= 0)
       const float fs = __expf(loc);            // exp(Lam_r - B_I)
-      const float GL = __expf(BI + loc);       // exp(Lam_r)
+      const float GL = eBI * fs;               // exp(Lam_r)
       const float fe = __expf(suf);            // exp(B_{I+1} - Lam_r)
-      const float kb = __expf(suf + bsuf1);    // exp(Lam_C - Lam_r)
+      const float kb = fe * eBS;               // exp(Lam_C - Lam_r)
       const float ek = ev[rr] * kv[rr];
       const float qt = gv[rr] * qv[rr];
       if (!safe) sL[r][ej] = lv[rr];
@@ -376,14 +390,11 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
       for (int idx = tid; idx < 16 * DK / 4; idx += NTH) {
         const int r = idx / (DK / 4);
         const int j4 = (idx - r * (DK / 4)) * 4;
-        f32x4 wq, qq;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          wq[i] = M::to_f32(sStage[r][j4 + i]);
-          qq[i] = M::to_f32(sStage[r][DK + j4 + i]);
-        }
-        store4(out.W + static_cast<size_t>(r0 + r) * DK + j4, wq);
-        store4(out.Qp + static_cast<size_t>(r0 + r) * DK + j4, qq);
+        typedef typename Raw4<TC>::type R4;
+        *reinterpret_cast<R4*>(out.W + static_cast<size_t>(r0 + r) * DK + j4) =
+            *reinterpret_cast<const R4*>(&sStage[r][j4]);
+        *reinterpret_cast<R4*>(out.Qp + static_cast<size_t>(r0 + r) * DK + j4) =
+            *reinterpret_cast<const R4*>(&sStage[r][DK + j4]);
       }
       __syncthreads();
     }

@@ -11,8 +11,10 @@ namespace muir {
 //   W [C][DK], Q' [C][DK], Kbar^T [DK][C], U~^T [DV][C], O~^T [DV][C],
 //   W^T [DK][C], Q'^T [DK][C], Kbar [C][DK]
 // (W, Q' and Kbar in both orientations: the forward scan contracts them over
-// key channels, the reverse scan over tokens), then Gamma_C [DK] fp32 and the
-// leaf blocks T_II, P_II [C/16][2][16][16] (compute type).
+// key channels, the reverse scan over tokens), then Gamma_C [DK] fp32, the
+// leaf blocks T_II, P_II [C/16][2][16][16] (compute type) and the chunk's
+// deltas U~ - W S [C][DV] (compute type; written by the forward scan when it
+// saves the chunk states and the direct backward is used, see bwd_direct).
 enum SummaryPart { SP_W, SP_QP, SP_KBT, SP_UTT, SP_OTT, SP_WT, SP_QT, SP_KB, SP_END };
 __host__ __device__ constexpr size_t summary_part(int part, int C, int DK, int DV) {
   return part <= SP_UTT ? static_cast<size_t>(part) * C * DK
@@ -32,11 +34,17 @@ struct ChunkShape {
   size_t summary_elems() const { return summary_part(SP_END, C, DK, DV); }
   size_t gc_offset() const { return summary_elems() * tc_bytes(); }
   size_t tp_offset() const { return gc_offset() + static_cast<size_t>(DK) * 4; }
+  size_t dl_offset() const { return tp_offset() + static_cast<size_t>(C / 16) * 512 * tc_bytes(); }
   size_t summary_bytes() const {
-    size_t b = tp_offset() + static_cast<size_t>(C / 16) * 512 * tc_bytes();
+    size_t b = dl_offset() + static_cast<size_t>(C) * DV * tc_bytes();
     return (b + 255) & ~static_cast<size_t>(255);
   }
   size_t state_bytes() const { return static_cast<size_t>(DK) * DV * 4; }
+  // The backward takes the chunk's deltas from the forward scan and forms the
+  // states inside a chunk from S0 and those deltas (one reverse sweep over
+  // its blocks), instead of a forward sweep that recomputes both: for
+  // 64-token chunks in bf16, whose tiles then fit the LDS.
+  bool bwd_direct() const { return bf16 && C == 64; }
 };
 
 hipError_t launch_step(int N, int H, int dk, int dv, bool bf16, const void* q, const void* k,
@@ -49,9 +57,11 @@ hipError_t launch_fwd_prep(const ChunkShape& s, const void* q, const void* k, co
                            const void* log_a, const void* erase, const void* write,
                            const void* gamma, void* summ, hipStream_t stream);
 
-// Sequential over chunks: o (may be NULL), S_chunks (may be NULL), S_T (may be NULL).
+// Sequential over chunks: o (may be NULL), S_chunks (may be NULL), S_T (may be
+// NULL).  With `deltas` (the same summaries, writable) each chunk's deltas are
+// written into its summary.
 hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S0, void* o,
-                           float* S_chunks, float* S_T, hipStream_t stream);
+                           float* S_chunks, float* S_T, void* deltas, hipStream_t stream);
 
 // Reverse sequential over chunks: dS_chunks[c] = gradient w.r.t. the state at the
 // END of chunk c; dS0 (may be NULL).
@@ -59,8 +69,10 @@ hipError_t launch_bwd_scan(const ChunkShape& s, const void* summ, const void* dO
                            const float* dS_T, float* dS_chunks, float* dS0, hipStream_t stream);
 
 // Chunk-parallel: all input gradients of every chunk.  `summ` holds the
-// chunk summaries (their leaf blocks are read); `scratch` holds
-// bwd_chunk_scratch_bytes(s) per chunk (the chunk's deltas and their gradients).
+// chunk summaries (their leaf blocks are read; with bwd_direct also Kbar^T,
+// Gamma_C and the deltas); `scratch` holds bwd_chunk_scratch_bytes(s) per
+// chunk (the deltas and block-start states of the forward sweep; none with
+// bwd_direct).
 size_t bwd_chunk_scratch_bytes(const ChunkShape& s);
 hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, const void* v,
                             const void* log_a, const void* erase, const void* write,

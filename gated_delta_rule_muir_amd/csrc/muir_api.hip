@@ -148,7 +148,9 @@ muir_status_t muir_chunk_fwd(const muir_dims_t* dims, const void* q, const void*
   if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, workspace, hs) != hipSuccess)
     return MUIR_ERR_HIP;
   mark(hs);
-  if (muir::launch_fwd_scan(s, workspace, S0, o, S_chunks, S_T, hs) != hipSuccess)
+  // a forward that saves its chunk states keeps the deltas for the direct backward
+  void* deltas = S_chunks && s.bwd_direct() ? workspace : nullptr;
+  if (muir::launch_fwd_scan(s, workspace, S0, o, S_chunks, S_T, deltas, hs) != hipSuccess)
     return MUIR_ERR_HIP;
   mark(hs);
   return MUIR_OK;
@@ -193,6 +195,13 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void*
   const float* Sc = S_chunks;
   const void* summ = summaries;
   mark(hs);
+  // The direct backward reads the deltas that the forward scan keeps in the
+  // summaries when it saves the chunk states: both are taken from one forward
+  // call, or both recomputed here.
+  if (s.bwd_direct() && !(summ && Sc)) {
+    summ = nullptr;
+    Sc = nullptr;
+  }
   if (!summ) {
     // the forward's chunk summaries are not given: recompute them
     if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, ws, hs) != hipSuccess)
@@ -202,7 +211,8 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void*
   }
   if (!Sc) {
     // chunk-start states are not given: rerun the forward scan
-    if (muir::launch_fwd_scan(s, summ, S0, nullptr, S_rec, nullptr, hs) != hipSuccess)
+    void* deltas = s.bwd_direct() ? ws : nullptr;  // summ is ws here
+    if (muir::launch_fwd_scan(s, summ, S0, nullptr, S_rec, nullptr, deltas, hs) != hipSuccess)
       return MUIR_ERR_HIP;
     mark(hs);
     Sc = S_rec;

@@ -57,7 +57,7 @@ template <typename Tin, int DK, int NW>
 __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
     int T, int H, int C, const char* __restrict__ summ, size_t summ_bytes,
     const float* __restrict__ S0, Tin* __restrict__ o, float* __restrict__ S_chunks,
-    float* __restrict__ S_T) {
+    float* __restrict__ S_T, char* __restrict__ dsumm, size_t dl_offset) {
   typedef Tin TC;
   typedef MM<TC> M;
   typedef typename M::frag frag;
@@ -205,6 +205,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
     }
     // token t of the unit is sequence position c*C + sb*SB + t
     const size_t obase = ((static_cast<size_t>(b) * T + static_cast<size_t>(c) * C + sb * SB) * H + h) * DV;
+    // this chunk's deltas [C][DV] in its summary (when they are kept)
+    TC* dlc = dsumm ? reinterpret_cast<TC*>(dsumm + (static_cast<size_t>(bh) * NC + c) * summ_bytes + dl_offset)
+                    : nullptr;
 #pragma unroll 2
     for (int m = 0; m < SB / 16; ++m) {
       f32x4 Oa = zero4(), Da = zero4();
@@ -223,6 +226,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
       }
       const f32x4 ut = load4(reinterpret_cast<const TC*>(sU + au));
       const frag df = M::from_f32(ut - Da);
+      if (dlc) {
+        // the deltas in the compute type, as token rows (exact: a product with the identity)
+        const f32x4 tt = M::mma(df, ident, zero4());
+        store4(at(dlc, static_cast<uint32_t>((sb * SB + 16 * m + c16) * DV + col0 + 4 * g)), tt);
+      }
 #pragma unroll
       for (int s = 0; s < RT; ++s)
         dS[s] = M::mma(M::load(reinterpret_cast<const TC*>(sK + swz<LK>(16 * s + c16, (16 * m + 4 * g) * SZ))),
@@ -437,14 +445,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
 // Four waves (64 columns) per workgroup when that still fills the chip, else
 // one wave (16 columns) per workgroup for more independent chains.
 hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S0, void* o,
-                           float* S_chunks, float* S_T, hipStream_t stream) {
+                           float* S_chunks, float* S_T, void* deltas, hipStream_t stream) {
   const int heads = s.B * s.H;
   if (heads == 0) return hipSuccess;
   const bool wide = static_cast<long long>(heads) * (s.DV / 64) >= 256;
 #define MUIR_SCAN(TT, DD, NW)                                                                      \
   hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, NW>), dim3(heads * (s.DV / (16 * NW))),              \
                      dim3(64 * NW), 0, stream, s.T, s.H, s.C, (const char*)summ, s.summary_bytes(), \
-                     S0, (TT*)o, S_chunks, S_T)
+                     S0, (TT*)o, S_chunks, S_T, (char*)deltas, s.dl_offset())
   if (s.bf16) {
     if (s.DK == 128) {
       if (wide) MUIR_SCAN(uint16_t, 128, 4); else MUIR_SCAN(uint16_t, 128, 1);

@@ -111,8 +111,10 @@ size_t muir_chunk_fwd_workspace(const muir_dims_t* dims);
  *              chunk (kept for muir_chunk_bwd), or NULL to skip
  *   workspace: device scratch of at least muir_chunk_fwd_workspace(dims)
  *              bytes.  On return it holds the chunk summaries (the
- *              per-chunk solve results); a caller that keeps it unchanged
- *              may pass it to muir_chunk_bwd as `summaries`.
+ *              per-chunk solve results; with S_chunks also each chunk's
+ *              deltas when dtype is MUIR_BF16 and chunk is 64); a caller
+ *              that keeps it unchanged may pass it to muir_chunk_bwd as
+ *              `summaries`, together with S_chunks.
  */
 muir_status_t muir_chunk_fwd(const muir_dims_t* dims,
                              const void* q, const void* k, const void* v,
@@ -135,7 +137,11 @@ size_t muir_chunk_bwd_workspace(const muir_dims_t* dims);
  *   summaries: the workspace of a muir_chunk_fwd call on the same inputs,
  *              dims and S0, unchanged since (the chunk summaries it left
  *              there), or NULL (then recomputed inside, in the workspace);
- *              read only
+ *              read only.  With dtype MUIR_BF16 and chunk 64 the backward
+ *              also reads the chunk deltas that the forward keeps when it
+ *              saves S_chunks: there summaries and S_chunks are used only
+ *              together, from the same muir_chunk_fwd call, and both are
+ *              recomputed when either is NULL.
  *   dO       : [B, T, H, dv] dtype upstream gradient of o
  *   dS_T     : [B, H, dk, dv] fp32 upstream gradient of S_T, or NULL for 0
  *   dq, dk, dlog_a, derase, dgamma : [B, T, H, dk] fp32 outputs

@@ -158,3 +158,35 @@ def test_fwd_summary_intermediates():
             e = rel_err(got, want)
             _say(f"  chunk {c} {nm}: {e:.3e}")
             assert e <= 1e-4, (c, nm, e)
+
+
+def test_fwd_saved_deltas():
+    """A bf16 forward that saves its chunk states also keeps, in each chunk
+    summary, the chunk's deltas U~ - W S_c (S_c: the state at the chunk's
+    start), which the 64-token-chunk backward reads instead of recomputing
+    them.  Checked against the chunk model's U~, W and the oracle's S_c."""
+    from chunkwise_model import chunk_summary
+    m = _lib()
+    B, T, H, d, C = 1, 256, 1, 128, 64
+    inp = muir_inputs.seq_inputs(B, T, H, d, d, dtype="bf16", decay="channel", seed=8)
+    dv = to_dev(inp)
+    nbytes = m.muir_chunk_fwd_workspace(B, T, H, d, d, C)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    m.muir_chunk_fwd(*(dv[n] for n in NAMES), chunk=C, save_states=True, workspace=ws)
+    torch.cuda.synchronize()
+    per = nbytes // (T // C)
+    n = C * d
+    dl_off = 8 * n * 2 + d * 4 + (C // 16) * 512 * 2  # after the parts, Gamma_C and the leaf blocks
+    ref = chunk_summary(*(inp[nm][0, :, 0].double().numpy() for nm in NAMES), C)
+    for c in range(T // C):
+        blk = ws[c * per + dl_off: c * per + dl_off + n * 2].view(torch.bfloat16).cpu().double().numpy()
+        delta = blk.reshape(C, d)
+        if c == 0:
+            S_c = np.zeros((d, d))
+        else:
+            _, S_c = oracle.fwd(*(inp[nm][:, :c * C] for nm in NAMES))
+            S_c = S_c[0, 0]
+        want = ref[c]["Ut"] - ref[c]["W"] @ S_c
+        e = rel_err(delta, want)
+        _say(f"  chunk {c} deltas: {e:.3e}")
+        assert e <= TOL["bf16"], (c, e)
