@@ -32,6 +32,8 @@
 // deltas, the leaf inverse, the block-start state) is issued one step ahead
 // into registers (clamped at the ends of each sweep, so no load sits under a
 // branch) and committed to LDS when the step starts.
+#include <type_traits>
+
 #include "chunk_common.h"
 #include "kernels.h"
 #include "mma.h"
@@ -178,29 +180,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     ident = M::from_f32(idv);
   }
 
-  // ---- sums of the log-decay over each block and each part of it, and the
-  // blocks whose decay leaves LEAF_SAFE_RANGE (steep leaves) ----
-  if (tid == 0) sUnsafe = 0;
-#pragma unroll
-  for (int I = 0; I < NB; ++I) {
-    float sacc = 0.f;
-#pragma unroll
-    for (int rr = 0; rr < RPT; ++rr) sacc += ldv(lb, gi(16 * I + RPT * part + rr, ej));
-    sPart[I][part][ej] = sacc;
-  }
-  __syncthreads();
-  if (part == 0) {
-    unsigned mask = 0;
-#pragma unroll
-    for (int I = 0; I < NB; ++I) {
-      float bs = 0.f;
-#pragma unroll
-      for (int p = 0; p < TPC; ++p) bs += sPart[I][p][ej];
-      if (!(-bs <= LEAF_SAFE_RANGE)) mask |= 1u << I;
-    }
-    if (mask) atomicOr(&sUnsafe, static_cast<int>(mask));
-  }
-
   // within-block prefix (through each token) and suffix (after it) of log_a,
   // channel ej, tokens RPT*part + rr: loc = Lam_r - B_I, suf = B_{I+1} - Lam_r
   auto block_sums = [&](int I, const float* xl, float* loc, float* suf) {
@@ -296,189 +275,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     for (int i = 0; i < 4; ++i) gs[i] = sG[16 * s + 4 * g + i];
     return gs;
   };
-
-  // =========================== F: forward sweep ===========================
-  // slots: log_a, k, erase, write, v (channel ej, tokens RPT*part + rr), T/P word
-  float fl[RPT], fk[RPT], fe[RPT], fw[RPT], fv[RPT];
-  u32x2 ftp;
-  auto prefetch_f = [&](int I) {
-#pragma unroll
-    for (int rr = 0; rr < RPT; ++rr) {
-      const uint32_t o = gi(16 * I + RPT * part + rr, ej);
-      fl[rr] = ldv(lb, o);
-      fk[rr] = ldv(kb, o);
-      fe[rr] = ldv(eb, o);
-      fw[rr] = ldv(wb, o);
-      fv[rr] = ldv(vb, o);
-    }
-    ftp = tp_word(I);
-  };
-  // X = ek exp(Lam - B_I) rows, Ke = k exp(B_{I+1} - Lam) and U = write*v transposed
-  auto commit_f = [&](int I) {
-    float loc[RPT], suf[RPT];
-    block_sums(I, fl, loc, suf);
-#pragma unroll
-    for (int h4 = 0; h4 < RPT / 4; ++h4) {
-      f32x4 tA, tB;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int rr = 4 * h4 + q4;
-        const int r = RPT * part + rr;
-        sRowA[r][ej] = M::cvt(fe[rr] * fk[rr] * __expf(loc[rr]));
-        tA[q4] = fk[rr] * __expf(suf[rr]);
-        tB[q4] = fw[rr] * fv[rr];
-      }
-      const int t0 = RPT * part + 4 * h4;
-      store4(&sTA[ej][t0], tA);
-      store4(&sTB[ej][t0], tB);
-    }
-    tp_commit(ftp);
-    __syncthreads();
-  };
-
-  f32x4 S[RT][NT];
-  load_state(S, S0c);
-  // Direct form: the operands of the Horner steps below, Ke_I = k exp(B_{I+1} - Lam)
-  // at (token 4g+i of block I, channel colv(n)), and the block decays
-  // exp(B_{I+1} - B_I) in sGH, for every block but the last.
-  frag keH[DIRECT ? NB - 1 : 1][NT];
-  if constexpr (DIRECT) {
-    // the chunk's deltas (kept by the forward scan) into sDL, S0 into sSS
-    {
-      const TC* gD = reinterpret_cast<const TC*>(summ + static_cast<size_t>(chunk) * summ_bytes + dl_offset);
-      constexpr int DWR = DV / SEW;       // 16-byte words per delta row
-      constexpr int DWT = C * DWR / NTH;  // per thread
-      static_assert(DWT * NTH == C * DWR, "delta words");
-      u32x4 dw[DWT];
-#pragma unroll
-      for (int k2 = 0; k2 < DWT; ++k2)
-        dw[k2] = *reinterpret_cast<const u32x4*>(at(gD, static_cast<uint32_t>((tid + k2 * NTH) * SEW)));
-#pragma unroll
-      for (int k2 = 0; k2 < DWT; ++k2) {
-        const int w = tid + k2 * NTH;
-        const int row = w / DWR;
-        *reinterpret_cast<u32x4*>(&sDL[row][(w - row * DWR) * SEW]) = dw[k2];
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < RT; ++s)
-#pragma unroll
-      for (int n = 0; n < NT; ++n) store4(&sSS[16 * s + c16][col0(n) + 4 * g], turn(S[s][n]));
-#pragma unroll
-    for (int I = 0; I < NB - 1; ++I)
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        float l[4], kk[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t o = gi(16 * I + 4 * g + i, colv(n));
-          l[i] = ldv(lb, o);
-          kk[i] = ldv(kb, o);
-        }
-        // log-decay after each token to the block's end: within the lane's
-        // four tokens, plus the token groups of the lanes c16 + 16g' (g' > g)
-        const float s4 = (l[0] + l[1]) + (l[2] + l[3]);
-        const float t1 = __shfl(s4, c16 + 16, 64);
-        const float t2 = __shfl(s4, c16 + 32, 64);
-        const float t3 = __shfl(s4, c16 + 48, 64);
-        const float t0 = __shfl(s4, c16, 64);
-        float later = (g < 3 ? t3 : 0.f) + (g < 2 ? t2 : 0.f) + (g < 1 ? t1 : 0.f);
-        f32x4 kv;
-#pragma unroll
-        for (int i = 3; i >= 0; --i) {
-          kv[i] = kk[i] * __expf(later);
-          later += l[i];
-        }
-        keH[I][n] = M::from_f32(kv);
-        if (g == 0) sGH[I][colv(n)] = __expf(((t0 + t1) + t2) + t3);
-      }
-    __syncthreads();  // sDL, sSS, sGH, sPart, sUnsafe
-    // S becomes the chunk-end state S_C = diag(Gamma_C) S0 + Kbar^T Delta
-    // (for the rowsum term below), with Kbar^T and Gamma_C of the summary
-    {
-      const char* cs = summ + static_cast<size_t>(chunk) * summ_bytes;
-      const TC* gKT = reinterpret_cast<const TC*>(cs) + summary_part(SP_KBT, C, DK, DV);
-      const float* gGC = reinterpret_cast<const float*>(cs + summary_part(SP_END, C, DK, DV) * sizeof(TC));
-      frag dcol[NB][NT];  // Delta at (token 4g+i of block m, column colv(n))
-#pragma unroll
-      for (int m = 0; m < NB; ++m)
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          f32x4 t;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) t[i] = M::to_f32(sDL[16 * m + 4 * g + i][colv(n)]);
-          dcol[m][n] = M::from_f32(t);
-        }
-#pragma unroll
-      for (int s = 0; s < RT; ++s) {
-        const f32x4 gc = *reinterpret_cast<const f32x4*>(at(gGC, static_cast<uint32_t>(16 * s + 4 * g)));
-#pragma unroll
-        for (int n = 0; n < NT; ++n) S[s][n] *= gc;
-#pragma unroll
-        for (int m = 0; m < NB; ++m) {
-          const frag ka = M::load(at(gKT, static_cast<uint32_t>((16 * s + c16) * C + 16 * m + 4 * g)));
-#pragma unroll
-          for (int n = 0; n < NT; ++n) S[s][n] = M::mma(ka, dcol[m][n], S[s][n]);
-        }
-      }
-    }
-  } else {
-    prefetch_f(0);
-    __syncthreads();  // sPart, sUnsafe
-
-#pragma unroll 1
-    for (int I = 0; I < NB; ++I) {
-      const int r0 = 16 * I;
-      commit_f(I);
-      prefetch_f(I + 1 < NB ? I + 1 : I);
-      frag Sf[RT][NT];
-#pragma unroll
-      for (int s = 0; s < RT; ++s)
-#pragma unroll
-        for (int n = 0; n < NT; ++n) Sf[s][n] = M::from_f32(S[s][n]);
-      // the block-start state, as [dk][dv] rows, for the reverse sweep
-      {
-        TC* dst = gS + static_cast<size_t>(I) * DK * DV;
-#pragma unroll
-        for (int s = 0; s < RT; ++s)
-#pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            const f32x4 tt = M::mma(Sf[s][n], ident, zero4());  // row 16s+c16, columns col0(n)+4g+i
-            store4(at(dst, static_cast<uint32_t>((16 * s + c16) * DV + col0(n) + 4 * g)), tt);
-          }
-      }
-      // Delta_I = T_II (U_I - X_I S_I)
-      f32x4 Dl[NT];
-      {
-        f32x4 xs[NT];
-#pragma unroll
-        for (int n = 0; n < NT; ++n) xs[n] = zero4();
-#pragma unroll
-        for (int s = 0; s < RT; ++s) {
-          const frag xa = M::load(&sRowA[c16][16 * s + 4 * g]);
-#pragma unroll
-          for (int n = 0; n < NT; ++n) xs[n] = M::mma(xa, Sf[s][n], xs[n]);
-        }
-        const frag ta = M::load(&sT[c16][4 * g]);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          f32x4 rhs = load4(&sTB[colv(n)][4 * g]);
-          rhs -= xs[n];
-          Dl[n] = M::mma(ta, M::from_f32(rhs), zero4());
-          store4(at(gDel, static_cast<uint32_t>((r0 + c16) * DV + col0(n) + 4 * g)), turn(Dl[n]));
-        }
-      }
-      // S_{I+1} = diag(exp(B_{I+1} - B_I)) S_I + Ke_I^T Delta_I
-#pragma unroll
-      for (int s = 0; s < RT; ++s) {
-        const frag ka = M::load(&sTA[16 * s + c16][4 * g]);
-        const f32x4 gs = decay_scale(s);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) S[s][n] = M::mma(ka, M::from_f32(Dl[n]), S[s][n] * gs);
-      }
-      __syncthreads();
-    }
-  }  // F sweep
 
   // =========================== R: reverse sweep ===========================
   // slots: log_a, k, erase, q, gamma (channel ej, tokens RPT*part + rr);
@@ -590,10 +386,244 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     return safe;
   };
 
-  prefetch_r(NB - 1);
-  prefetch_r_out(NB - 1);
+  // =========================== F: forward sweep ===========================
+  // slots: log_a, k, erase, write, v (channel ej, tokens RPT*part + rr), T/P word
+  float fl[RPT], fk[RPT], fe[RPT], fw[RPT], fv[RPT];
+  u32x2 ftp;
+  auto prefetch_f = [&](int I) {
+#pragma unroll
+    for (int rr = 0; rr < RPT; ++rr) {
+      const uint32_t o = gi(16 * I + RPT * part + rr, ej);
+      fl[rr] = ldv(lb, o);
+      fk[rr] = ldv(kb, o);
+      fe[rr] = ldv(eb, o);
+      fw[rr] = ldv(wb, o);
+      fv[rr] = ldv(vb, o);
+    }
+    ftp = tp_word(I);
+  };
+  // X = ek exp(Lam - B_I) rows, Ke = k exp(B_{I+1} - Lam) and U = write*v transposed
+  auto commit_f = [&](int I) {
+    float loc[RPT], suf[RPT];
+    block_sums(I, fl, loc, suf);
+#pragma unroll
+    for (int h4 = 0; h4 < RPT / 4; ++h4) {
+      f32x4 tA, tB;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int rr = 4 * h4 + q4;
+        const int r = RPT * part + rr;
+        sRowA[r][ej] = M::cvt(fe[rr] * fk[rr] * __expf(loc[rr]));
+        tA[q4] = fk[rr] * __expf(suf[rr]);
+        tB[q4] = fw[rr] * fv[rr];
+      }
+      const int t0 = RPT * part + 4 * h4;
+      store4(&sTA[ej][t0], tA);
+      store4(&sTB[ej][t0], tB);
+    }
+    tp_commit(ftp);
+    __syncthreads();
+  };
+
+  f32x4 S[RT][NT];
   f32x4 D[RT][NT];
-  load_state(D, dSC);
+  // Direct form: the operands of the Horner steps in the reverse sweep,
+  // Ke_I = k exp(B_{I+1} - Lam) at (token 4g+i of block I, channel colv(n)),
+  // and the block decays exp(B_{I+1} - B_I) in sGH, for every block but the last.
+  frag keH[DIRECT ? NB - 1 : 1][NT];
+  // Direct form: every global read of the prologue is issued before the
+  // first wait -- the chunk's deltas and Kbar^T (16-byte words), Gamma_C, the
+  // Horner inputs, S0, dS_C and the first step's prefetch.
+  constexpr int DWR = DV / SEW;        // 16-byte words per delta row
+  constexpr int DWT = C * DWR / NTH;   // delta words per thread
+  constexpr int KWR = C / SEW;         // 16-byte words per Kbar^T row
+  constexpr int KWT = DK * KWR / NTH;  // Kbar^T words per thread
+  u32x4 dw[DIRECT ? DWT : 1], kw[DIRECT ? KWT : 1], gcw;
+  float hl[DIRECT ? NB - 1 : 1][NT][4], hk[DIRECT ? NB - 1 : 1][NT][4];
+  if constexpr (DIRECT) {
+    static_assert(DWT * NTH == C * DWR && KWT * NTH == DK * KWR && DK / 4 <= NTH && NB == 4,
+                  "direct-form prologue layout");
+    const char* cs = summ + static_cast<size_t>(chunk) * summ_bytes;
+    const TC* gD = reinterpret_cast<const TC*>(cs + dl_offset);
+    const TC* gKT = reinterpret_cast<const TC*>(cs) + summary_part(SP_KBT, C, DK, DV);
+    const float* gGC = reinterpret_cast<const float*>(cs + summary_part(SP_END, C, DK, DV) * sizeof(TC));
+#pragma unroll
+    for (int k2 = 0; k2 < DWT; ++k2)
+      dw[k2] = *reinterpret_cast<const u32x4*>(at(gD, static_cast<uint32_t>((tid + k2 * NTH) * SEW)));
+#pragma unroll
+    for (int k2 = 0; k2 < KWT; ++k2)
+      kw[k2] = *reinterpret_cast<const u32x4*>(at(gKT, static_cast<uint32_t>((tid + k2 * NTH) * SEW)));
+    gcw = *reinterpret_cast<const u32x4*>(at(gGC, static_cast<uint32_t>(4 * min(tid, DK / 4 - 1))));
+#pragma unroll
+    for (int I = 0; I < NB - 1; ++I)
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t o = gi(16 * I + 4 * g + i, colv(n));
+          hl[I][n][i] = ldv(lb, o);
+          hk[I][n][i] = ldv(kb, o);
+        }
+    load_state(S, S0c);
+    load_state(D, dSC);
+    prefetch_r(NB - 1);
+    prefetch_r_out(NB - 1);
+  }
+
+  // ---- sums of the log-decay over each block and each part of it, and the
+  // blocks whose decay leaves LEAF_SAFE_RANGE (steep leaves) ----
+  if (tid == 0) sUnsafe = 0;
+#pragma unroll
+  for (int I = 0; I < NB; ++I) {
+    float sacc = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < RPT; ++rr) sacc += ldv(lb, gi(16 * I + RPT * part + rr, ej));
+    sPart[I][part][ej] = sacc;
+  }
+  __syncthreads();
+  if (part == 0) {
+    unsigned mask = 0;
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      float bs = 0.f;
+#pragma unroll
+      for (int p = 0; p < TPC; ++p) bs += sPart[I][p][ej];
+      if (!(-bs <= LEAF_SAFE_RANGE)) mask |= 1u << I;
+    }
+    if (mask) atomicOr(&sUnsafe, static_cast<int>(mask));
+  }
+
+  if constexpr (DIRECT) {
+    // deltas into sDL; Kbar^T into sSD (until the sweep stages D there);
+    // Gamma_C into sG (until the sweep's block sums); S0 into sSS
+#pragma unroll
+    for (int k2 = 0; k2 < DWT; ++k2) {
+      const int w = tid + k2 * NTH;
+      const int row = w / DWR;
+      *reinterpret_cast<u32x4*>(&sDL[row][(w - row * DWR) * SEW]) = dw[k2];
+    }
+#pragma unroll
+    for (int k2 = 0; k2 < KWT; ++k2) {
+      const int w = tid + k2 * NTH;
+      const int row = w / KWR;
+      *reinterpret_cast<u32x4*>(&sSD[row][(w - row * KWR) * SEW]) = kw[k2];
+    }
+    if (tid < DK / 4) *reinterpret_cast<u32x4*>(&sG[4 * tid]) = gcw;
+#pragma unroll
+    for (int s = 0; s < RT; ++s)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) store4(&sSS[16 * s + c16][col0(n) + 4 * g], turn(S[s][n]));
+#pragma unroll
+    for (int I = 0; I < NB - 1; ++I)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const float* l = hl[I][n];
+        // log-decay after each token to the block's end: within the lane's
+        // four tokens, plus the token groups of the lanes c16 + 16g' (g' > g)
+        const float s4 = (l[0] + l[1]) + (l[2] + l[3]);
+        const float t1 = __shfl(s4, c16 + 16, 64);
+        const float t2 = __shfl(s4, c16 + 32, 64);
+        const float t3 = __shfl(s4, c16 + 48, 64);
+        const float t0 = __shfl(s4, c16, 64);
+        float later = (g < 3 ? t3 : 0.f) + (g < 2 ? t2 : 0.f) + (g < 1 ? t1 : 0.f);
+        f32x4 kv;
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+          kv[i] = hk[I][n][i] * __expf(later);
+          later += l[i];
+        }
+        keH[I][n] = M::from_f32(kv);
+        if (g == 0) sGH[I][colv(n)] = __expf(((t0 + t1) + t2) + t3);
+      }
+    __syncthreads();  // sDL, sSD, sG, sSS, sGH
+    // S becomes the chunk-end state S_C = diag(Gamma_C) S0 + Kbar^T Delta
+    // (for the rowsum term below)
+    {
+      frag dcol[NB][NT];  // Delta at (token 4g+i of block m, column colv(n))
+#pragma unroll
+      for (int m = 0; m < NB; ++m)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          f32x4 t;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) t[i] = M::to_f32(sDL[16 * m + 4 * g + i][colv(n)]);
+          dcol[m][n] = M::from_f32(t);
+        }
+#pragma unroll
+      for (int s = 0; s < RT; ++s) {
+        const f32x4 gc = decay_scale(s);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) S[s][n] *= gc;
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+          const frag ka = M::load(&sSD[16 * s + c16][16 * m + 4 * g]);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) S[s][n] = M::mma(ka, dcol[m][n], S[s][n]);
+        }
+      }
+    }
+  } else {
+    load_state(S, S0c);
+    prefetch_f(0);
+    __syncthreads();  // sPart, sUnsafe
+
+#pragma unroll 1
+    for (int I = 0; I < NB; ++I) {
+      const int r0 = 16 * I;
+      commit_f(I);
+      prefetch_f(I + 1 < NB ? I + 1 : I);
+      frag Sf[RT][NT];
+#pragma unroll
+      for (int s = 0; s < RT; ++s)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) Sf[s][n] = M::from_f32(S[s][n]);
+      // the block-start state, as [dk][dv] rows, for the reverse sweep
+      {
+        TC* dst = gS + static_cast<size_t>(I) * DK * DV;
+#pragma unroll
+        for (int s = 0; s < RT; ++s)
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            const f32x4 tt = M::mma(Sf[s][n], ident, zero4());  // row 16s+c16, columns col0(n)+4g+i
+            store4(at(dst, static_cast<uint32_t>((16 * s + c16) * DV + col0(n) + 4 * g)), tt);
+          }
+      }
+      // Delta_I = T_II (U_I - X_I S_I)
+      f32x4 Dl[NT];
+      {
+        f32x4 xs[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n) xs[n] = zero4();
+#pragma unroll
+        for (int s = 0; s < RT; ++s) {
+          const frag xa = M::load(&sRowA[c16][16 * s + 4 * g]);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) xs[n] = M::mma(xa, Sf[s][n], xs[n]);
+        }
+        const frag ta = M::load(&sT[c16][4 * g]);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          f32x4 rhs = load4(&sTB[colv(n)][4 * g]);
+          rhs -= xs[n];
+          Dl[n] = M::mma(ta, M::from_f32(rhs), zero4());
+          store4(at(gDel, static_cast<uint32_t>((r0 + c16) * DV + col0(n) + 4 * g)), turn(Dl[n]));
+        }
+      }
+      // S_{I+1} = diag(exp(B_{I+1} - B_I)) S_I + Ke_I^T Delta_I
+#pragma unroll
+      for (int s = 0; s < RT; ++s) {
+        const frag ka = M::load(&sTA[16 * s + c16][4 * g]);
+        const f32x4 gs = decay_scale(s);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) S[s][n] = M::mma(ka, M::from_f32(Dl[n]), S[s][n] * gs);
+      }
+      __syncthreads();
+    }
+    prefetch_r(NB - 1);
+    prefetch_r_out(NB - 1);
+    load_state(D, dSC);
+  }  // F sweep
+
   // chunk-end term rowsum(S_C * dS_C): S holds S_C here and D holds dS_C;
   // it enters dlog_a on every token of the chunk
 #pragma unroll
@@ -717,12 +747,27 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       //   S_J = exp(B_J) S0 + sum_{I<J} diag(exp(B_J - B_{I+1})) Ke_I^T Delta_I,
       // so each row x of dO_J, dR_J takes, in Horner form over the earlier
       // blocks I, acc <- exp(B_{I+1} - B_I) acc + (x . Delta_t) Ke_I[t] (every factor <= 1)
+      // (the products with the NI earlier blocks' deltas run as 2 NI
+      // interleaved chains over dv, then the Horner steps)
+      auto horner = [&](auto ni) {
+        constexpr int NI = decltype(ni)::value;
+        f32x4 mq[NI], me[NI];  // rows r of the block on lanes, contraction over the tokens of block I
 #pragma unroll
-      for (int I = 0; I < NB - 1; ++I) {
-        if (I < J) {
-          // rows r of the block on lanes, contraction over the tokens t of block I
-          const frag mqf = M::from_f32(leaf_pair(sDL + 16 * I, sDO));
-          const frag mef = M::from_f32(leaf_pair(sDL + 16 * I, sDR));
+        for (int I = 0; I < NI; ++I) mq[I] = me[I] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < DV / 16; ++kk) {
+          const frag bo = M::load(&sDO[c16][16 * kk + 4 * g]);
+          const frag br = M::load(&sDR[c16][16 * kk + 4 * g]);
+#pragma unroll
+          for (int I = 0; I < NI; ++I) {
+            const frag a = M::load(&sDL[16 * I + c16][16 * kk + 4 * g]);
+            mq[I] = M::mma(a, bo, mq[I]);
+            me[I] = M::mma(a, br, me[I]);
+          }
+        }
+#pragma unroll
+        for (int I = 0; I < NI; ++I) {
+          const frag mqf = M::from_f32(mq[I]), mef = M::from_f32(me[I]);
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
             const float gb = sGH[I][colv(n)];
@@ -730,7 +775,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
             acce[n] = M::mma(mef, keH[I][n], acce[n] * gb);
           }
         }
-      }
+      };
+      if (J == 3) horner(std::integral_constant<int, 3>());
+      else if (J == 2) horner(std::integral_constant<int, 2>());
+      else if (J == 1) horner(std::integral_constant<int, 1>());
     }
     // Leaf parts
     if (safe) {
