@@ -32,8 +32,6 @@
 // deltas, the leaf inverse, the block-start state) is issued one step ahead
 // into registers (clamped at the ends of each sweep, so no load sits under a
 // branch) and committed to LDS when the step starts.
-#include <type_traits>
-
 #include "chunk_common.h"
 #include "kernels.h"
 #include "mma.h"
@@ -148,14 +146,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
 
   __shared__ float sPart[NB][TPC][DK];                       // sum of log_a over each part's RPT tokens
   __shared__ int sUnsafe;                                    // bit I: block I beyond LEAF_SAFE_RANGE
-  __shared__ float sFs[16][DK + 4];                          // R: exp(Lam - B_J)
-  __shared__ float sFe[16][DK + 4];                          // R: exp(B_{J+1} - Lam)
   __shared__ __attribute__((aligned(16))) TC sRowA[16][PT];  // F: X rows   R: Ke rows
   __shared__ __attribute__((aligned(16))) TC sTA[DK][TP];    // F: Ke^T     R: X^T
   __shared__ __attribute__((aligned(16))) TC sTB[DK][TP];    // F: U^T      R: Y^T
-  __shared__ __attribute__((aligned(16))) TC sTY[DK][TP];    // R: Yhat^T
-  __shared__ __attribute__((aligned(16))) TC sTX[DK][TP];    // R: Xhat^T
-  __shared__ __attribute__((aligned(16))) TC sTZ[DK][TP];    // R: Z^T
   __shared__ __attribute__((aligned(16))) TC sDO[16][PV];    // dO rows of the block
   __shared__ __attribute__((aligned(16))) TC sDL[DIRECT ? C : 16][PV];  // delta rows (direct: of the chunk)
   __shared__ __attribute__((aligned(16))) TC sDR[16][PV];    // dR rows of the block
@@ -166,10 +159,19 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   __shared__ float sLf[2][16][17];                           // leaf matrices of steep blocks
   __shared__ float sG[DK];
   __shared__ float sGH[DIRECT ? NB - 1 : 1][DK];              // direct: block decays exp(B_{I+1} - B_I)
+  // The block's token-token products x_r . Delta_t over dv (x = dO, dR; r, t
+  // tokens), each formed once by one wave and read by all: for the deltas of
+  // the block itself masked to the leaf's triangle, in both orientations
+  // (sGd: rows r, sGT: rows t, the dR part negated), and in the direct form
+  // for each earlier block's deltas (sGh: rows r).
+  constexpr int GP = 16 + row_pad<TC>();
+  __shared__ __attribute__((aligned(16))) TC sGd[2][16][GP];
+  __shared__ __attribute__((aligned(16))) TC sGT[2][16][GP];
+  __shared__ __attribute__((aligned(16))) TC sGh[2][DIRECT ? NB - 1 : 1][16][GP];
   // per-wave partial rowsums of S_C * dS_C, used once before the reverse
-  // sweep (which then writes Yhat^T over it)
+  // sweep (which then writes X^T over it)
   static_assert(NW * DK * sizeof(float) <= sizeof(TC) * DK * TP, "rowsum scratch");
-  float (*sRow)[DK] = reinterpret_cast<float (*)[DK]>(&sTY[0][0]);
+  float (*sRow)[DK] = reinterpret_cast<float (*)[DK]>(&sTA[0][0]);
 
   // identity operand: a 16x16 product with it moves a tile's rows onto lanes
   frag ident;
@@ -279,11 +281,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   // =========================== R: reverse sweep ===========================
   // slots: log_a, k, erase, q, gamma (channel ej, tokens RPT*part + rr);
   // dO and delta rows (raw words); T/P word; the block-start state (16-byte
-  // words); q, gamma, v, write, k, erase at (token 4g+i, column colv(n))
+  // words); q, gamma, v, write, k, erase, log_a at (token 4g+i, column colv(n))
   float xl[RPT], xk[RPT], xe[RPT], xq[RPT], xg[RPT];
   u32x2 rdo[RW], rdl[RW], rtp;
   u32x4 rss[SPT];
-  float oq[NT][4], og[NT][4], ov[NT][4], ow[NT][4], ok[NT][4], oe[NT][4];
+  float oq[NT][4], og[NT][4], ov[NT][4], ow[NT][4], ok[NT][4], oe[NT][4], ol[NT][4];
   auto prefetch_r = [&](int J) {
     const int r0 = 16 * J;
 #pragma unroll
@@ -325,7 +327,31 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         ow[n][ii] = ldv(wb, o);
         ok[n][ii] = ldv(kb, o);
         oe[n][ii] = ldv(eb, o);
+        ol[n][ii] = ldv(lb, o);
       }
+  };
+  // log-decay of channel colv(n) over the block at the output mapping (tokens
+  // 4g+ii): loc = Lam - B_J (through the token), suf = B_{J+1} - Lam (after
+  // it); the lane's four tokens, plus the token groups of lanes c16 + 16g'
+  auto out_sums = [&](int n, float* loc, float* suf) {
+    const float* l = ol[n];
+    const float s4 = (l[0] + l[1]) + (l[2] + l[3]);
+    const float t0 = __shfl(s4, c16, 64);
+    const float t1 = __shfl(s4, c16 + 16, 64);
+    const float t2 = __shfl(s4, c16 + 32, 64);
+    const float t3 = __shfl(s4, c16 + 48, 64);
+    float run = (g > 0 ? t0 : 0.f) + (g > 1 ? t1 : 0.f) + (g > 2 ? t2 : 0.f);
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      run += l[ii];
+      loc[ii] = run;
+    }
+    float after = (g < 3 ? t3 : 0.f) + (g < 2 ? t2 : 0.f) + (g < 1 ? t1 : 0.f);
+#pragma unroll
+    for (int ii = 3; ii >= 0; --ii) {
+      suf[ii] = after;
+      after += l[ii];
+    }
   };
   // block-start state words of column pass p into sSS
   auto commit_state = [&](const u32x4* words, int p) {
@@ -337,42 +363,27 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       if (colw / SW == p) *reinterpret_cast<u32x4*>(&sSS[row][colw - p * SW]) = words[k2];
     }
   };
-  // Ke = k exp(B_{J+1} - Lam) rows; X = ek exp(Lam - B_J), Y = qt exp(Lam - B_J),
-  // Xhat = ek exp(Lam - B_{J+1}), Yhat = qt exp(Lam - B_{J+1}), Z = k exp(B_J - Lam)
-  // transposed; the factors exp(Lam - B_J), exp(B_{J+1} - Lam).  Xhat, Yhat, Z
-  // (>= 1) only on leaves within LEAF_SAFE_RANGE.  Returns that flag.
+  // Ke = k exp(B_{J+1} - Lam) rows; X = ek exp(Lam - B_J), Y = qt exp(Lam - B_J)
+  // transposed.  Returns whether the block's leaf is within LEAF_SAFE_RANGE.
   auto commit_r = [&](int J) -> int {
     const int safe = !((sUnsafe >> J) & 1);
     float loc[RPT], suf[RPT];
     block_sums(J, xl, loc, suf);
 #pragma unroll
     for (int h4 = 0; h4 < RPT / 4; ++h4) {
-      f32x4 tA, tB, tY, tX, tZ;
+      f32x4 tA, tB;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int rr = 4 * h4 + q4;
         const int r = RPT * part + rr;
         const float fs = __expf(loc[rr]);
-        const float fe2 = __expf(suf[rr]);
-        const float ie = safe ? __expf(-suf[rr]) : 0.f;
-        const float zi = safe ? __expf(-loc[rr]) : 0.f;
-        const float ek = xe[rr] * xk[rr];
-        const float qt = xg[rr] * xq[rr];
-        sFs[r][ej] = fs;
-        sFe[r][ej] = fe2;
-        sRowA[r][ej] = M::cvt(xk[rr] * fe2);
-        tA[q4] = ek * fs;
-        tB[q4] = qt * fs;
-        tY[q4] = qt * ie;
-        tX[q4] = ek * ie;
-        tZ[q4] = xk[rr] * zi;
+        sRowA[r][ej] = M::cvt(xk[rr] * __expf(suf[rr]));
+        tA[q4] = xe[rr] * xk[rr] * fs;
+        tB[q4] = xg[rr] * xq[rr] * fs;
       }
       const int t0 = RPT * part + 4 * h4;
       store4(&sTA[ej][t0], tA);
       store4(&sTB[ej][t0], tB);
-      store4(&sTY[ej][t0], tY);
-      store4(&sTX[ej][t0], tX);
-      store4(&sTZ[ej][t0], tZ);
     }
 #pragma unroll
     for (int e = 0; e < RW; ++e) {
@@ -726,6 +737,35 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         }
       }
       __syncthreads();  // also publishes the dR rows
+      if (p == 0) {
+        // the shared token-token products G = x . Delta_t, one per wave
+        const int np = DIRECT ? 2 * (J + 1) : 2;
+        for (int pr = wave; pr < np; pr += NW) {
+          const int x = pr & 1;                 // 0: dO rows, 1: dR rows
+          const int I = DIRECT ? pr >> 1 : J;   // the deltas' block
+          const TC (*xr)[PV] = x ? sDR : sDO;
+          const TC (*dr)[PV] = DIRECT ? sDL + 16 * I : sDL;
+          f32x4 gacc = zero4();  // lane (g, c16): x_{4g+i} . Delta_{c16}
+#pragma unroll
+          for (int kk = 0; kk < DV / 16; ++kk)
+            gacc = M::mma(M::load(&xr[c16][16 * kk + 4 * g]), M::load(&dr[c16][16 * kk + 4 * g]), gacc);
+          if (I == J) {
+            // leaf triangle: t <= r for dO, t < r for dR (negated in the t-row copy)
+            f32x4 gm, gt;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 4 * g + i;
+              const bool keep = x ? c16 < r : c16 <= r;
+              gm[i] = keep ? gacc[i] : 0.f;
+              gt[i] = keep ? (x ? -gacc[i] : gacc[i]) : 0.f;
+            }
+            store4(&sGT[x][c16][4 * g], gt);
+            store4(&sGd[x][c16][4 * g], turn(gm));
+          } else {
+            store4(&sGh[x][DIRECT ? I : 0][c16][4 * g], turn(gacc));
+          }
+        }
+      }
 #pragma unroll
       for (int kk = 0; kk < SW / 16; ++kk) {
         const int cc = p * SW + 16 * kk + 4 * g;
@@ -742,32 +782,17 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         }
       }
     }
+    __syncthreads();  // the shared products
     if constexpr (DIRECT) {
       // d(qt), d(ek) boundary parts with S_J in place of S0:
       //   S_J = exp(B_J) S0 + sum_{I<J} diag(exp(B_J - B_{I+1})) Ke_I^T Delta_I,
       // so each row x of dO_J, dR_J takes, in Horner form over the earlier
       // blocks I, acc <- exp(B_{I+1} - B_I) acc + (x . Delta_t) Ke_I[t] (every factor <= 1)
-      // (the products with the NI earlier blocks' deltas run as 2 NI
-      // interleaved chains over dv, then the Horner steps)
-      auto horner = [&](auto ni) {
-        constexpr int NI = decltype(ni)::value;
-        f32x4 mq[NI], me[NI];  // rows r of the block on lanes, contraction over the tokens of block I
 #pragma unroll
-        for (int I = 0; I < NI; ++I) mq[I] = me[I] = zero4();
-#pragma unroll
-        for (int kk = 0; kk < DV / 16; ++kk) {
-          const frag bo = M::load(&sDO[c16][16 * kk + 4 * g]);
-          const frag br = M::load(&sDR[c16][16 * kk + 4 * g]);
-#pragma unroll
-          for (int I = 0; I < NI; ++I) {
-            const frag a = M::load(&sDL[16 * I + c16][16 * kk + 4 * g]);
-            mq[I] = M::mma(a, bo, mq[I]);
-            me[I] = M::mma(a, br, me[I]);
-          }
-        }
-#pragma unroll
-        for (int I = 0; I < NI; ++I) {
-          const frag mqf = M::from_f32(mq[I]), mef = M::from_f32(me[I]);
+      for (int I = 0; I < NB - 1; ++I) {
+        if (I < J) {
+          const frag mqf = M::load(&sGh[0][I][c16][4 * g]);  // rows r, contraction over block I's tokens
+          const frag mef = M::load(&sGh[1][I][c16][4 * g]);
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
             const float gb = sGH[I][colv(n)];
@@ -775,31 +800,33 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
             acce[n] = M::mma(mef, keH[I][n], acce[n] * gb);
           }
         }
-      };
-      if (J == 3) horner(std::integral_constant<int, 3>());
-      else if (J == 2) horner(std::integral_constant<int, 2>());
-      else if (J == 1) horner(std::integral_constant<int, 1>());
+      }
     }
+    // log-decay sums at the output mapping (per-token factors and leaf operands)
+    float oloc[NT][4], osuf[NT][4];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) out_sums(n, oloc[n], osuf[n]);
     // Leaf parts
     if (safe) {
       // rows i on lanes, contraction over r:  (dO_r . Delta_i) Yhat_r, r >= i;  -(dR_r . Delta_i) Xhat_r, r > i
-      f32x4 l0 = leaf_pair(sDO, dlJ), l1 = leaf_pair(sDR, dlJ);
       // rows r on lanes, contraction over i:  (Delta_i . dO_r) Z_i, i <= r;  (Delta_i . dR_r) Z_i, i < r
-      f32x4 m0 = leaf_pair(dlJ, sDO), m1 = leaf_pair(dlJ, sDR);
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int a = 4 * g + ii;
-        l0[ii] = (c16 <= a) ? l0[ii] : 0.f;
-        l1[ii] = (c16 < a) ? -l1[ii] : 0.f;
-        m0[ii] = (a <= c16) ? m0[ii] : 0.f;
-        m1[ii] = (a < c16) ? m1[ii] : 0.f;
-      }
-      const frag l0f = M::from_f32(l0), l1f = M::from_f32(l1), m0f = M::from_f32(m0), m1f = M::from_f32(m1);
+      // with Yhat = qt exp(Lam - B_{J+1}), Xhat = ek exp(Lam - B_{J+1}), Z = k exp(B_J - Lam)
+      // (>= 1, within LEAF_SAFE_RANGE) built at the lane's (tokens 4g+i, channel colv(n))
+      const frag l0f = M::load(&sGT[0][c16][4 * g]), l1f = M::load(&sGT[1][c16][4 * g]);
+      const frag m0f = M::load(&sGd[0][c16][4 * g]), m1f = M::load(&sGd[1][c16][4 * g]);
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        acck[n] = M::mma(l0f, M::load(&sTY[colv(n)][4 * g]), acck[n]);
-        acck[n] = M::mma(l1f, M::load(&sTX[colv(n)][4 * g]), acck[n]);
-        const frag zb = M::load(&sTZ[colv(n)][4 * g]);
+        f32x4 yh, xh, zz;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float ie = __expf(-osuf[n][i]);
+          yh[i] = og[n][i] * oq[n][i] * ie;
+          xh[i] = oe[n][i] * ok[n][i] * ie;
+          zz[i] = ok[n][i] * __expf(-oloc[n][i]);
+        }
+        const frag zb = M::from_f32(zz);
+        acck[n] = M::mma(l0f, M::from_f32(yh), acck[n]);
+        acck[n] = M::mma(l1f, M::from_f32(xh), acck[n]);
         accq[n] = M::mma(m0f, zb, accq[n]);
         acce[n] = M::mma(m1f, zb, acce[n]);
       }
@@ -816,9 +843,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int t = 4 * g + ii;  // token of the block
-        float vk = sFe[t][j] * acck[n][ii];  // d(k)_t
-        float vq = sFs[t][j] * accq[n][ii];  // d(qt)_t
-        float ve = sFs[t][j] * acce[n][ii];  // -d(ek)_t
+        const float fs = __expf(oloc[n][ii]);          // exp(Lam_t - B_J)
+        float vk = __expf(osuf[n][ii]) * acck[n][ii];  // d(k)_t
+        float vq = fs * accq[n][ii];                   // d(qt)_t
+        float ve = fs * acce[n][ii];                   // -d(ek)_t
         if (!safe) {
           for (int r = t; r < 16; ++r) {
             const float f = pair_factor(r0, r, t, j);
