@@ -3,8 +3,8 @@
 
 One timed step = one chunkwise forward (saving chunk states) plus one
 chunkwise backward over the headline workload: B=8, T=4096, H=16,
-dk=dv=128, chunk 64, bf16 inputs, fp32 state/gradients, synthetic seeded
-inputs already resident in HBM.  `value` is tokens/s (B*T per step time).
+dk=dv=128, chunk 64, bf16 inputs and gradients, fp32 states, synthetic
+seeded inputs already resident in HBM.  `value` is tokens/s (B*T per step time).
 
 Beside it the line carries:
   roofline      the dominant kernel's algorithmic bytes per launch over its
@@ -45,16 +45,20 @@ def log(*a):
 
 
 # Algorithmic bytes per token-head of each kernel (d = head size, C = chunk,
-# bf16 inputs of 2 bytes, fp32 states and gradients): the bytes the kernel must
+# bf16 inputs and gradients of 2 bytes, fp32 states): the bytes the kernel must
 # read and write by construction -- its inputs and outputs, not its re-reads.
 def kernel_bytes(d: int, C: int, e: int = 2):
+    """Algorithmic HBM bytes per token-head of each kernel of the training
+    step (bf16, 64-token chunks: the forward scan keeps the chunk deltas and
+    the backward reads them with Kbar^T instead of recomputing them)."""
     st = 4 * d * d / C  # one fp32 state per chunk, per token
     lf = 2 * 256 * e / 16  # the leaf blocks T_II, P_II (16 x 16 each per 16 tokens)
     return {
         "fwd_prep": 7 * d * e + 8 * d * e + lf,         # 7 inputs -> W, Q', Kbar (both ways), U~, O~, leaves
-        "fwd_scan": 5 * d * e + d * e + st,             # summary -> o, chunk states
+        "fwd_scan": 5 * d * e + 2 * d * e + st,         # summary -> o, deltas, chunk states
         "bwd_scan": 3 * d * e + d * e + st,             # W, Q', Kbar, dO -> chunk-end state grads
-        "bwd_chunk": 7 * d * e + d * e + lf + 2 * st + 7 * d * 4,  # inputs, dO, leaves, S, dS -> 7 fp32 grads
+        # inputs, dO, deltas, Kbar^T, leaves, S, dS -> 7 grads in the input dtype
+        "bwd_chunk": 7 * d * e + 3 * d * e + lf + 2 * st + 7 * d * e,
     }
 
 

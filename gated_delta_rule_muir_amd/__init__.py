@@ -173,8 +173,9 @@ def muir_chunk_fwd(q, k, v, log_a, erase, write, gamma, S0=None, *, chunk: int =
 def muir_chunk_bwd(q, k, v, log_a, erase, write, gamma, dO, S0=None, S_chunks=None, dS_T=None, *,
                    chunk: int = 64, summaries: Optional[torch.Tensor] = None,
                    workspace: Optional[torch.Tensor] = None, want_dS0: bool = True):
-    """Chunkwise backward.  Returns a dict of fp32 gradients
-    (dq, dk, dv, dlog_a, derase, dwrite, dgamma, dS0).
+    """Chunkwise backward.  Returns a dict of gradients (dq, dk, dv, dlog_a,
+    derase, dwrite, dgamma in the input dtype, accumulated in fp32 and rounded
+    once; dS0 in fp32).
 
     `S_chunks` (from muir_chunk_fwd(save_states=True)) and `summaries` (the
     `workspace` tensor of that forward call, left unchanged) are saved forward
@@ -201,10 +202,10 @@ def muir_chunk_bwd(q, k, v, log_a, erase, write, gamma, dO, S0=None, S_chunks=No
         if (not summaries.is_cuda or summaries.device != dev or not summaries.is_contiguous()
                 or summaries.numel() * summaries.element_size() < need):
             raise ValueError(f"summaries: expected the forward workspace ({need} bytes on {dev})")
-    f32 = dict(dtype=torch.float32, device=dev)
-    g = {n: torch.empty((B, T, H, dk), **f32) for n in ("dq", "dk", "dlog_a", "derase", "dgamma")}
-    g.update({n: torch.empty((B, T, H, dv), **f32) for n in ("dv", "dwrite")})
-    g["dS0"] = torch.empty((B, H, dk, dv), **f32) if want_dS0 else None
+    gd = dict(dtype=dt, device=dev)
+    g = {n: torch.empty((B, T, H, dk), **gd) for n in ("dq", "dk", "dlog_a", "derase", "dgamma")}
+    g.update({n: torch.empty((B, T, H, dv), **gd) for n in ("dv", "dwrite")})
+    g["dS0"] = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None
     d = _dims(B, T, H, dk, dv, chunk, code)
     nbytes = int(lib().muir_chunk_bwd_workspace(ctypes.byref(d)))
     ws = _workspace(nbytes, dev, workspace)

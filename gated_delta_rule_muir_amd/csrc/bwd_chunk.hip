@@ -65,9 +65,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     const Tin* __restrict__ v, const Tin* __restrict__ log_a, const Tin* __restrict__ erase,
     const Tin* __restrict__ write, const Tin* __restrict__ gamma, const char* __restrict__ summ,
     size_t summ_bytes, size_t tp_offset, size_t dl_offset, const float* __restrict__ S_chunks,
-    const float* __restrict__ dS_chunks, const Tin* __restrict__ dO, float* __restrict__ dq,
-    float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dlog_a,
-    float* __restrict__ derase, float* __restrict__ dwrite, float* __restrict__ dgamma,
+    const float* __restrict__ dS_chunks, const Tin* __restrict__ dO, Tin* __restrict__ dq,
+    Tin* __restrict__ dk, Tin* __restrict__ dv, Tin* __restrict__ dlog_a,
+    Tin* __restrict__ derase, Tin* __restrict__ dwrite, Tin* __restrict__ dgamma,
     char* __restrict__ scratch) {
   typedef Tin TC;
   typedef MM<TC> M;
@@ -129,13 +129,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   const Tin* wb = write + ebase;
   const Tin* gb = gamma + ebase;
   const Tin* dOb = dO + ebase;
-  float* dqb = dq + ebase;
-  float* dkb = dk + ebase;
-  float* dvb = dv + ebase;
-  float* dlb = dlog_a + ebase;
-  float* deb = derase + ebase;
-  float* dwb = dwrite + ebase;
-  float* dgb = dgamma + ebase;
+  Tin* dqb = dq + ebase;
+  Tin* dkb = dk + ebase;
+  Tin* dvb = dv + ebase;
+  Tin* dlb = dlog_a + ebase;
+  Tin* deb = derase + ebase;
+  Tin* dwb = dwrite + ebase;
+  Tin* dgb = dgamma + ebase;
   auto gi = [&](int t, int j) -> uint32_t { return static_cast<uint32_t>(t) * HD + static_cast<uint32_t>(j); };
   TC* gDel = reinterpret_cast<TC*>(scratch + static_cast<size_t>(chunk) * bwd_scratch_bytes_tc<TC>(C, DK, DV));
   TC* gS = gDel + static_cast<size_t>(C) * DV;  // [NB][DK][DV]
@@ -256,6 +256,18 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   // by one identity product so that lane (g, c16) holds row c16, columns
   // 4g..4g+3
   auto turn = [&](f32x4 tile) -> f32x4 { return M::mma(M::from_f32(tile), ident, zero4()); };
+  // a gradient tile in MFMA-output layout (tokens r0 + 4g+i, channel colv(n))
+  // to its [B, T, H, D] tensor: in bf16 turned into token rows of four
+  // channels (one 8-byte store; the turn rounds to bf16 as the store would),
+  // in fp32 element by element
+  auto store_grad = [&](Tin* base, int r0, int n, f32x4 tile) {
+    if constexpr (sizeof(TC) == 2) {
+      store4(at(base, gi(r0 + c16, col0(n) + 4 * g)), turn(tile));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *at(base, gi(r0 + 4 * g + i, colv(n))) = tile[i];
+    }
+  };
 
   // (the lane offset is made opaque per call so that the addresses are formed
   // where they are used instead of being kept live across the sweeps)
@@ -706,12 +718,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       store4(&sDR[c16][col0(n) + 4 * g], turn(dRn[n]));
+      f32x4 gw, gv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t o = gi(r0 + 4 * g + i, colv(n));
-        *at(dwb, o) = ov[n][i] * dRn[n][i];
-        *at(dvb, o) = ow[n][i] * dRn[n][i];
+        gw[i] = ov[n][i] * dRn[n][i];
+        gv[i] = ow[n][i] * dRn[n][i];
       }
+      store_grad(dwb, r0, n, gw);
+      store_grad(dvb, r0, n, gv);
     }
     // Boundary parts, in column passes over dv:
     //   d(k)_i <- Delta_i . D rows,  d(qt)_r <- dO_r . S_J rows,  d(ek)_r <- dR_r . S_J rows
@@ -722,6 +736,16 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       accq[n] = zero4();
       acce[n] = zero4();
     }
+    // The shared token-token products G = x . Delta_t (x = dO, dR rows of the
+    // block), np of them, product pr by wave pr % NW: with the deltas of the
+    // block itself (pr < 2), and in the direct form of block pr/2 <= J.  A
+    // wave whose pr >= np forms a product it does not store (no branch in the
+    // contraction).
+    constexpr int PPW = DIRECT ? (2 * NB + NW - 1) / NW : (2 + NW - 1) / NW;
+    const int np = DIRECT ? 2 * (J + 1) : 2;
+    f32x4 gacc[PPW];
+#pragma unroll
+    for (int q2 = 0; q2 < PPW; ++q2) gacc[q2] = zero4();
 #pragma unroll
     for (int p = 0; p < SPLIT; ++p) {
       if (p > 0) {
@@ -737,35 +761,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         }
       }
       __syncthreads();  // also publishes the dR rows
-      if (p == 0) {
-        // the shared token-token products G = x . Delta_t, one per wave
-        const int np = DIRECT ? 2 * (J + 1) : 2;
-        for (int pr = wave; pr < np; pr += NW) {
-          const int x = pr & 1;                 // 0: dO rows, 1: dR rows
-          const int I = DIRECT ? pr >> 1 : J;   // the deltas' block
-          const TC (*xr)[PV] = x ? sDR : sDO;
-          const TC (*dr)[PV] = DIRECT ? sDL + 16 * I : sDL;
-          f32x4 gacc = zero4();  // lane (g, c16): x_{4g+i} . Delta_{c16}
-#pragma unroll
-          for (int kk = 0; kk < DV / 16; ++kk)
-            gacc = M::mma(M::load(&xr[c16][16 * kk + 4 * g]), M::load(&dr[c16][16 * kk + 4 * g]), gacc);
-          if (I == J) {
-            // leaf triangle: t <= r for dO, t < r for dR (negated in the t-row copy)
-            f32x4 gm, gt;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 4 * g + i;
-              const bool keep = x ? c16 < r : c16 <= r;
-              gm[i] = keep ? gacc[i] : 0.f;
-              gt[i] = keep ? (x ? -gacc[i] : gacc[i]) : 0.f;
-            }
-            store4(&sGT[x][c16][4 * g], gt);
-            store4(&sGd[x][c16][4 * g], turn(gm));
-          } else {
-            store4(&sGh[x][DIRECT ? I : 0][c16][4 * g], turn(gacc));
-          }
-        }
-      }
 #pragma unroll
       for (int kk = 0; kk < SW / 16; ++kk) {
         const int cc = p * SW + 16 * kk + 4 * g;
@@ -779,6 +774,52 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
           acck[n] = M::mma(al, bd, acck[n]);
           accq[n] = M::mma(ao, bs, accq[n]);
           acce[n] = M::mma(ar, bs, acce[n]);
+        }
+        if constexpr (SPLIT == 1) {
+          // this wave's shared products (dO or dR rows, the same operands)
+#pragma unroll
+          for (int q2 = 0; q2 < PPW; ++q2) {
+            const int pr = wave + q2 * NW;
+            const frag ax = (pr & 1) ? ar : ao;
+            gacc[q2] = M::mma(ax, M::load(&sDL[(DIRECT ? 16 * (pr >> 1) : 0) + c16][cc]), gacc[q2]);
+          }
+        }
+      }
+    }
+    if constexpr (SPLIT > 1) {
+      // (column passes: the products over the whole of dv, from the rows in LDS)
+#pragma unroll
+      for (int q2 = 0; q2 < PPW; ++q2) {
+        const int pr = wave + q2 * NW;
+        const TC (*xr)[PV] = (pr & 1) ? sDR : sDO;
+#pragma unroll
+        for (int kk = 0; kk < DV / 16; ++kk)
+          gacc[q2] = M::mma(M::load(&xr[c16][16 * kk + 4 * g]),
+                            M::load(&sDL[(DIRECT ? 16 * (pr >> 1) : 0) + c16][16 * kk + 4 * g]), gacc[q2]);
+      }
+    }
+#pragma unroll
+    for (int q2 = 0; q2 < PPW; ++q2) {
+      // lane (g, c16) of product pr: x_{4g+i} . Delta_{c16}, x = dO (pr even) or
+      // dR rows, the deltas of block pr/2 (direct form) or of this block
+      const int pr = wave + q2 * NW;
+      const int x = pr & 1;
+      const int I = DIRECT ? pr >> 1 : J;
+      if (pr < np) {
+        if (I == J) {
+          // leaf triangle: t <= r for dO, t < r for dR (negated in the t-row copy)
+          f32x4 gm, gt;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i;
+            const bool keep = x ? c16 < r : c16 <= r;
+            gm[i] = keep ? gacc[q2][i] : 0.f;
+            gt[i] = keep ? (x ? -gacc[q2][i] : gacc[q2][i]) : 0.f;
+          }
+          store4(&sGT[x][c16][4 * g], gt);
+          store4(&sGd[x][c16][4 * g], turn(gm));
+        } else {
+          store4(&sGh[x][DIRECT ? I : 0][c16][4 * g], turn(gacc[q2]));
         }
       }
     }
@@ -840,6 +881,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     for (int n = 0; n < NT; ++n) {
       const int j = colv(n);
       float dl[4];
+      f32x4 gq, gg, ge, gk, gl;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int t = 4 * g + ii;  // token of the block
@@ -862,11 +904,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
           }
         }
         const float dek = -ve;
-        const uint32_t o = gi(r0 + t, j);
-        *at(dqb, o) = og[n][ii] * vq;
-        *at(dgb, o) = oq[n][ii] * vq;
-        *at(deb, o) = ok[n][ii] * dek;
-        *at(dkb, o) = vk + oe[n][ii] * dek;
+        gq[ii] = og[n][ii] * vq;
+        gg[ii] = oq[n][ii] * vq;
+        ge[ii] = ok[n][ii] * dek;
+        gk[ii] = vk + oe[n][ii] * dek;
         dl[ii] = oe[n][ii] * ok[n][ii] * dek + og[n][ii] * oq[n][ii] * vq - ok[n][ii] * vk;
       }
       // suffix sums over the block's tokens (4g..4g+3 in this lane, the other
@@ -880,9 +921,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
 #pragma unroll
       for (int ii = 3; ii >= 0; --ii) {
         run += dl[ii];
-        *at(dlb, gi(r0 + 4 * g + ii, j)) = run;
+        gl[ii] = run;
       }
       carry[n] += t0 + t1 + t2 + t3;
+      store_grad(dqb, r0, n, gq);
+      store_grad(dgb, r0, n, gg);
+      store_grad(deb, r0, n, ge);
+      store_grad(dkb, r0, n, gk);
+      store_grad(dlb, r0, n, gl);
     }
     prefetch_r_out(J > 0 ? J - 1 : 0);
     // D <- diag(exp(B_{J+1} - B_J)) D + Y_J^T dO_J - X_J^T dR_J
@@ -916,8 +962,8 @@ size_t bwd_chunk_scratch_bytes(const ChunkShape& s) {
 hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, const void* v,
                             const void* log_a, const void* erase, const void* write,
                             const void* gamma, const void* summ, const float* S_chunks,
-                            const float* dS_chunks, const void* dO, float* dq, float* dk, float* dv,
-                            float* dlog_a, float* derase, float* dwrite, float* dgamma, void* scratch,
+                            const float* dS_chunks, const void* dO, void* dq, void* dk, void* dv,
+                            void* dlog_a, void* derase, void* dwrite, void* dgamma, void* scratch,
                             hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(s.nchunks());
   if (grid == 0) return hipSuccess;
@@ -925,8 +971,8 @@ hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, c
   hipLaunchKernelGGL((bwd_chunk_kernel<TT, DD, CC, NW, DIR>), dim3(grid), dim3(64 * NW), 0, stream, s.T, s.H, \
                      (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, (const TT*)erase,      \
                      (const TT*)write, (const TT*)gamma, (const char*)summ, s.summary_bytes(),          \
-                     s.tp_offset(), s.dl_offset(), S_chunks, dS_chunks, (const TT*)dO, dq, dk, dv, dlog_a, derase,     \
-                     dwrite, dgamma, (char*)scratch)
+                     s.tp_offset(), s.dl_offset(), S_chunks, dS_chunks, (const TT*)dO, (TT*)dq, (TT*)dk,      \
+                     (TT*)dv, (TT*)dlog_a, (TT*)derase, (TT*)dwrite, (TT*)dgamma, (char*)scratch)
 #define MUIR_BCH(TT, DD, NW, DIR64)                         \
   do {                                                      \
     if (s.C == 64) MUIR_BCH1(TT, DD, 64, NW, DIR64);        \

@@ -78,8 +78,8 @@ hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, c
                             const void* log_a, const void* erase, const void* write,
                             const void* gamma, const void* summ, const float* S_chunks,
                             const float* dS_chunks,
-                            const void* dO, float* dq, float* dk, float* dv, float* dlog_a,
-                            float* derase, float* dwrite, float* dgamma, void* scratch,
+                            const void* dO, void* dq, void* dk, void* dv, void* dlog_a,
+                            void* derase, void* dwrite, void* dgamma, void* scratch,
                             hipStream_t stream);
 
 }  // namespace muir

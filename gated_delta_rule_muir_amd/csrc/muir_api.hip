@@ -77,7 +77,7 @@ hipError_t copy_or_zero(float* dst, const float* src, size_t n, hipStream_t s) {
 
 extern "C" {
 
-int32_t muir_abi_version(void) { return 2; }
+int32_t muir_abi_version(void) { return 3; }
 
 int32_t muir_set_profile_events(void** events, int32_t count) {
   if (count < 0 || (count > 0 && !events)) return MUIR_ERR_NULL;
@@ -160,8 +160,8 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void*
                              const void* v, const void* log_a, const void* erase,
                              const void* write, const void* gamma, const float* S0,
                              const float* S_chunks, const void* summaries, const void* dO,
-                             const float* dS_T, float* dq, float* dk, float* dv, float* dlog_a,
-                             float* derase, float* dwrite, float* dgamma, float* dS0,
+                             const float* dS_T, void* dq, void* dk, void* dv, void* dlog_a,
+                             void* derase, void* dwrite, void* dgamma, float* dS0,
                              void* workspace, size_t workspace_bytes, void* stream) {
   ChunkShape s;
   muir_status_t st = check_dims(dims, &s);

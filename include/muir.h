@@ -24,9 +24,9 @@
  * Conventions shared by every call
  * --------------------------------
  *  - Every tensor pointer is a DEVICE pointer to dense, contiguous memory,
- *    aligned to 16 bytes.  Inputs and o/dO use the element type `dtype`
- *    (MUIR_F32 or MUIR_BF16); states, workspaces and gradients are fp32
- *    (except the workspace, whose content is opaque).
+ *    aligned to 16 bytes.  Inputs, o/dO and the gradients of the inputs use
+ *    the element type `dtype` (MUIR_F32 or MUIR_BF16); states and state
+ *    gradients are fp32; the workspace's content is opaque.
  *  - Sequence tensors are [B, T, H, D] with D contiguous; states are
  *    [B, H, dk, dv] row-major (dv contiguous).
  *  - The caller owns every buffer, including the workspace; the library
@@ -144,8 +144,9 @@ size_t muir_chunk_bwd_workspace(const muir_dims_t* dims);
  *              recomputed when either is NULL.
  *   dO       : [B, T, H, dv] dtype upstream gradient of o
  *   dS_T     : [B, H, dk, dv] fp32 upstream gradient of S_T, or NULL for 0
- *   dq, dk, dlog_a, derase, dgamma : [B, T, H, dk] fp32 outputs
- *   dv, dwrite                     : [B, T, H, dv] fp32 outputs
+ *   dq, dk, dlog_a, derase, dgamma : [B, T, H, dk] dtype outputs
+ *   dv, dwrite                     : [B, T, H, dv] dtype outputs
+ *              (accumulated in fp32 and rounded once on the store)
  *   dS0      : [B, H, dk, dv] fp32 output, or NULL to skip
  *   workspace: device scratch of at least muir_chunk_bwd_workspace(dims)
  *              bytes; contents are clobbered.
@@ -156,8 +157,8 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims,
                              const void* write, const void* gamma,
                              const float* S0, const float* S_chunks, const void* summaries,
                              const void* dO, const float* dS_T,
-                             float* dq, float* dk, float* dv, float* dlog_a,
-                             float* derase, float* dwrite, float* dgamma, float* dS0,
+                             void* dq, void* dk, void* dv, void* dlog_a,
+                             void* derase, void* dwrite, void* dgamma, float* dS0,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
