@@ -52,13 +52,14 @@ def kernel_bytes(d: int, C: int, e: int = 2):
     step (bf16, 64-token chunks: the forward scan keeps the chunk deltas and
     the backward reads them with Kbar^T instead of recomputing them)."""
     st = 4 * d * d / C  # one fp32 state per chunk, per token
+    sg = e * d * d / C  # one chunk-end state gradient (compute type) per chunk, per token
     lf = 2 * 256 * e / 16  # the leaf blocks T_II, P_II (16 x 16 each per 16 tokens)
     return {
         "fwd_prep": 7 * d * e + 8 * d * e + lf,         # 7 inputs -> W, Q', Kbar (both ways), U~, O~, leaves
         "fwd_scan": 5 * d * e + 2 * d * e + st,         # summary -> o, deltas, chunk states
-        "bwd_scan": 3 * d * e + d * e + st,             # W, Q', Kbar, dO -> chunk-end state grads
+        "bwd_scan": 3 * d * e + d * e + sg,             # W, Q', Kbar, dO -> chunk-end state grads
         # inputs, dO, deltas, Kbar^T, leaves, S, dS -> 7 grads in the input dtype
-        "bwd_chunk": 7 * d * e + 3 * d * e + lf + 2 * st + 7 * d * e,
+        "bwd_chunk": 7 * d * e + 3 * d * e + lf + st + sg + 7 * d * e,
     }
 
 

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     const Tin* __restrict__ v, const Tin* __restrict__ log_a, const Tin* __restrict__ erase,
     const Tin* __restrict__ write, const Tin* __restrict__ gamma, const char* __restrict__ summ,
     size_t summ_bytes, size_t tp_offset, size_t dl_offset, const float* __restrict__ S_chunks,
-    const float* __restrict__ dS_chunks, const Tin* __restrict__ dO, Tin* __restrict__ dq,
+    const Tin* __restrict__ dS_chunks, const Tin* __restrict__ dO, Tin* __restrict__ dq,
     Tin* __restrict__ dk, Tin* __restrict__ dv, Tin* __restrict__ dlog_a,
     Tin* __restrict__ derase, Tin* __restrict__ dwrite, Tin* __restrict__ dgamma,
     char* __restrict__ scratch) {
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   // T_II, P_II of the chunk's blocks, from the chunk summary, [NB][2][16][16]
   const TC* gTP = reinterpret_cast<const TC*>(summ + static_cast<size_t>(chunk) * summ_bytes + tp_offset);
   const float* S0c = S_chunks + static_cast<size_t>(chunk) * DK * DV;
-  const float* dSC = dS_chunks + static_cast<size_t>(chunk) * DK * DV;
+  const TC* dSC = dS_chunks + static_cast<size_t>(chunk) * DK * DV;  // transposed 16-row tiles
 
   __shared__ float sPart[NB][TPC][DK];                       // sum of log_a over each part's RPT tokens
   __shared__ int sUnsafe;                                    // bit I: block I beyond LEAF_SAFE_RANGE
@@ -280,6 +280,17 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       for (int s = 0; s < RT; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[s][n][i] = *at(src, lo + static_cast<uint32_t>((16 * s + i) * DV));
+    }
+  };
+  // the chunk-end state gradient from its transposed 16-row tiles (the
+  // lane's four rows of column colv(n) are one 8- or 16-byte word)
+  auto load_dstate = [&](f32x4 (*st)[NT]) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      uint32_t lo = static_cast<uint32_t>(colv(n) * 16 + 4 * g);
+      asm volatile("" : "+v"(lo));
+#pragma unroll
+      for (int s = 0; s < RT; ++s) st[s][n] = load4(at(dSC, lo + static_cast<uint32_t>(s * DV * 16)));
     }
   };
 
@@ -488,7 +499,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
           hk[I][n][i] = ldv(kb, o);
         }
     load_state(S, S0c);
-    load_state(D, dSC);
+    load_dstate(D);
     prefetch_r(NB - 1);
     prefetch_r_out(NB - 1);
   }
@@ -644,7 +655,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     }
     prefetch_r(NB - 1);
     prefetch_r_out(NB - 1);
-    load_state(D, dSC);
+    load_dstate(D);
   }  // F sweep
 
   // chunk-end term rowsum(S_C * dS_C): S holds S_C here and D holds dS_C;
@@ -962,7 +973,7 @@ size_t bwd_chunk_scratch_bytes(const ChunkShape& s) {
 hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, const void* v,
                             const void* log_a, const void* erase, const void* write,
                             const void* gamma, const void* summ, const float* S_chunks,
-                            const float* dS_chunks, const void* dO, void* dq, void* dk, void* dv,
+                            const void* dS_chunks, const void* dO, void* dq, void* dk, void* dv,
                             void* dlog_a, void* derase, void* dwrite, void* dgamma, void* scratch,
                             hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(s.nchunks());
@@ -971,7 +982,7 @@ hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, c
   hipLaunchKernelGGL((bwd_chunk_kernel<TT, DD, CC, NW, DIR>), dim3(grid), dim3(64 * NW), 0, stream, s.T, s.H, \
                      (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, (const TT*)erase,      \
                      (const TT*)write, (const TT*)gamma, (const char*)summ, s.summary_bytes(),          \
-                     s.tp_offset(), s.dl_offset(), S_chunks, dS_chunks, (const TT*)dO, (TT*)dq, (TT*)dk,      \
+                     s.tp_offset(), s.dl_offset(), S_chunks, (const TT*)dS_chunks, (const TT*)dO, (TT*)dq, (TT*)dk,      \
                      (TT*)dv, (TT*)dlog_a, (TT*)derase, (TT*)dwrite, (TT*)dgamma, (char*)scratch)
 #define MUIR_BCH(TT, DD, NW, DIR64)                         \
   do {                                                      \

@@ -64,9 +64,11 @@ hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S
                            float* S_chunks, float* S_T, void* deltas, hipStream_t stream);
 
 // Reverse sequential over chunks: dS_chunks[c] = gradient w.r.t. the state at the
-// END of chunk c; dS0 (may be NULL).
+// END of chunk c, in the compute type, as transposed 16-row tiles: element
+// (r, j) at ((r / 16) * DV + j) * 16 + r % 16 of the chunk's DK * DV block;
+// dS0 (fp32 [dk][dv], may be NULL).
 hipError_t launch_bwd_scan(const ChunkShape& s, const void* summ, const void* dO,
-                           const float* dS_T, float* dS_chunks, float* dS0, hipStream_t stream);
+                           const float* dS_T, void* dS_chunks, float* dS0, hipStream_t stream);
 
 // Chunk-parallel: all input gradients of every chunk.  `summ` holds the
 // chunk summaries (their leaf blocks are read; with bwd_direct also Kbar^T,
@@ -77,7 +79,7 @@ size_t bwd_chunk_scratch_bytes(const ChunkShape& s);
 hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, const void* v,
                             const void* log_a, const void* erase, const void* write,
                             const void* gamma, const void* summ, const float* S_chunks,
-                            const float* dS_chunks,
+                            const void* dS_chunks,
                             const void* dO, void* dq, void* dk, void* dv, void* dlog_a,
                             void* derase, void* dwrite, void* dgamma, void* scratch,
                             hipStream_t stream);

@@ -258,7 +258,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
 template <typename Tin, int DK, int NW>
 __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
     int T, int H, int C, const char* __restrict__ summ, size_t summ_bytes,
-    const Tin* __restrict__ dO, const float* __restrict__ dS_T, float* __restrict__ dS_chunks,
+    const Tin* __restrict__ dO, const float* __restrict__ dS_T, Tin* __restrict__ dS_chunks,
     float* __restrict__ dS0) {
   typedef Tin TC;
   typedef MM<TC> M;
@@ -394,12 +394,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
     prefetch(u + 1 < U ? u + 1 : u);
     __syncthreads();
     if (sb == NSB - 1) {
-      // gradient at the end of chunk c
-      float* dst = dS_chunks + (static_cast<size_t>(bh) * NC + c) * DK * DV;
+      // gradient at the end of chunk c, in the compute type, as transposed
+      // 16-row tiles (the lane's four rows of column colg are contiguous)
+      TC* dst = dS_chunks + (static_cast<size_t>(bh) * NC + c) * DK * DV;
 #pragma unroll
       for (int s = 0; s < RT; ++s) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] = dS[s][i];
+        store4(at(dst, static_cast<uint32_t>((s * DV + colg) * 16 + 4 * g)), dS[s]);
         dSf[s] = M::from_f32(dS[s]);
         Z[s] = zero4();
       }
@@ -471,14 +471,14 @@ hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S
 }
 
 hipError_t launch_bwd_scan(const ChunkShape& s, const void* summ, const void* dO, const float* dS_T,
-                           float* dS_chunks, float* dS0, hipStream_t stream) {
+                           void* dS_chunks, float* dS0, hipStream_t stream) {
   const int heads = s.B * s.H;
   if (heads == 0) return hipSuccess;
   const bool wide = static_cast<long long>(heads) * (s.DV / 64) >= 256;
 #define MUIR_BSCAN(TT, DD, NW)                                                                     \
   hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, NW>), dim3(heads * (s.DV / (16 * NW))),              \
                      dim3(64 * NW), 0, stream, s.T, s.H, s.C, (const char*)summ, s.summary_bytes(), \
-                     (const TT*)dO, dS_T, dS_chunks, dS0)
+                     (const TT*)dO, dS_T, (TT*)dS_chunks, dS0)
   if (s.bf16) {
     if (s.DK == 128) {
       if (wide) MUIR_BSCAN(uint16_t, 128, 4); else MUIR_BSCAN(uint16_t, 128, 1);
