@@ -120,20 +120,24 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
   __shared__ float sEBS[NB][DK];       // exp(Lam_C - B_{I+1})
   __shared__ float sGB[NB][DK];        // exp(B_{I+1} - B_I)
   __shared__ int sUnsafe;              // bit I: block I beyond LEAF_SAFE_RANGE
-  __shared__ float sL[16][DK + 1];     // log_a of the block's tokens (per-pair fallback)
-  __shared__ __attribute__((aligned(16))) TC sX[16][PT];   // ek * exp(Lam - B_I)
-  __shared__ __attribute__((aligned(16))) TC sY[16][PT];   // qt * exp(Lam - B_I)
-  __shared__ __attribute__((aligned(16))) TC sZ[16][PT];   // k * exp(B_I - Lam)   (leaf only)
-  __shared__ __attribute__((aligned(16))) TC sKe[DK][20];  // (k * exp(B_{I+1} - Lam))^T
-  __shared__ __attribute__((aligned(16))) TC sR[NH][20];   // [U | K~]^T
-  __shared__ __attribute__((aligned(16))) TC sQh[DK][20];  // (qt * exp(Lam))^T
+  // per-block operand tiles; in bf16 double-buffered (block I in buffer I & 1)
+  // so that the elementwise work of block I+1 runs beside block I's products
+  // (fp32 tiles take one buffer within the LDS and the two phases alternate)
+  constexpr bool PIPE = sizeof(TC) == 2;
+  constexpr int NBUF = PIPE ? 2 : 1;
+  __shared__ float sL[NBUF][16][DK + 1];     // log_a of the block's tokens (per-pair fallback)
+  __shared__ __attribute__((aligned(16))) TC sX[NBUF][16][PT];   // ek * exp(Lam - B_I)
+  __shared__ __attribute__((aligned(16))) TC sY[NBUF][16][PT];   // qt * exp(Lam - B_I)
+  __shared__ __attribute__((aligned(16))) TC sZ[NBUF][16][PT];   // k * exp(B_I - Lam)   (leaf only)
+  __shared__ __attribute__((aligned(16))) TC sKe[NBUF][DK][20];  // (k * exp(B_{I+1} - Lam))^T
+  __shared__ __attribute__((aligned(16))) TC sR[NBUF][NH][20];   // [U | K~]^T
+  __shared__ __attribute__((aligned(16))) TC sQh[NBUF][DK][20];  // (qt * exp(Lam))^T
   __shared__ float sAw[16][17];
   __shared__ float sPw[16][17];
   __shared__ float sTw[16][17];
   __shared__ float sPf[16][17];
   __shared__ __attribute__((aligned(16))) TC sT[16][20];
   __shared__ __attribute__((aligned(16))) TC sP[16][20];
-  __shared__ float sG[DK];
   __shared__ __attribute__((aligned(16))) TC sStage[16][2 * DK + 8];
 
   // ---- sums of the log-decay over each part of each block, the block
@@ -183,37 +187,39 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
     for (int n = 0; n < NT; ++n) Hs[s][n] = zero4();
 
   // ---- the next block's inputs are loaded one block ahead (4 tokens of
-  // channel ej); no load is under a branch, so they stay in flight ----
-  float pk[4], pe[4], pq[4], pg[4], pv[4], pw[4], pl[4];
+  // channel ej), kept raw until used (a conversion at the load would wait
+  // for it); no load is under a branch, so they stay in flight ----
+  Tin pk[4], pe[4], pq[4], pg[4], pv[4], pw[4], pl[4];
   auto prefetch = [&](int I) {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const uint32_t o = gi(16 * I + 4 * part + rr, ej);
-      pk[rr] = ldv(kb, o);
-      pe[rr] = ldv(eb, o);
-      pq[rr] = ldv(qb, o);
-      pg[rr] = ldv(gb, o);
-      pv[rr] = ldv(vb, o);
-      pw[rr] = ldv(wb, o);
-      pl[rr] = ldv(lb, o);
+      pk[rr] = *at(kb, o);
+      pe[rr] = *at(eb, o);
+      pq[rr] = *at(qb, o);
+      pg[rr] = *at(gb, o);
+      pv[rr] = *at(vb, o);
+      pw[rr] = *at(wb, o);
+      pl[rr] = *at(lb, o);
     }
   };
-  prefetch(0);
 
-#pragma unroll 1
-  for (int I = 0; I < NB; ++I) {
+  // ---- elementwise work of block I (4 tokens of channel ej) into its
+  // buffer: the scaled operand rows and transposed tiles, Kbar of the summary;
+  // consumes the prefetched inputs and issues the next block's loads ----
+  auto elementwise = [&](int I) {
+    const int bb = PIPE ? I & 1 : 0;
     const int r0 = 16 * I;
-    // ---- elementwise: 4 tokens of channel ej ----
     float kv[4], ev[4], qv[4], gv[4], vv[4], wv[4], lv[4];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      kv[rr] = pk[rr];
-      ev[rr] = pe[rr];
-      qv[rr] = pq[rr];
-      gv[rr] = pg[rr];
-      vv[rr] = pv[rr];
-      wv[rr] = pw[rr];
-      lv[rr] = pl[rr];
+      kv[rr] = M::to_f32(pk[rr]);
+      ev[rr] = M::to_f32(pe[rr]);
+      qv[rr] = M::to_f32(pq[rr]);
+      gv[rr] = M::to_f32(pg[rr]);
+      vv[rr] = M::to_f32(pv[rr]);
+      wv[rr] = M::to_f32(pw[rr]);
+      lv[rr] = M::to_f32(pl[rr]);
     }
     prefetch(I + 1 < NB ? I + 1 : I);
     // direct partial sums (never differences of cumulative sums): prefix of
@@ -232,15 +238,15 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
       sf[0] = lv[3] + lv[2] + lv[1];
     }
     const int safe = !((sUnsafe >> I) & 1);
-    float excl = 0.f, exsuf = 0.f;
+    float excl = 0.f, exsuf = 0.f;  // (selects, not branches: see sL below)
 #pragma unroll
     for (int p = 0; p < TPC; ++p) {
-      if (p < part) excl += sPart[I][p][ej];
-      if (p > part) exsuf += sPart[I][p][ej];
+      const float ps = sPart[I][p][ej];
+      excl += p < part ? ps : 0.f;
+      exsuf += p > part ? ps : 0.f;
     }
     const float eBI = sEB[I][ej];    // exp(B_I)
     const float eBS = sEBS[I][ej];   // exp(Lam_C - B_{I+1})
-    if (part == 0) sG[ej] = sGB[I][ej];
     f32x4 keT, uT, ktT, qhT, kbT;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -250,27 +256,61 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
       const float fs = __expf(loc);            // exp(Lam_r - B_I)
       const float GL = eBI * fs;               // exp(Lam_r)
       const float fe = __expf(suf);            // exp(B_{I+1} - Lam_r)
-      const float kb = fe * eBS;               // exp(Lam_C - Lam_r)
+      const float kbf = fe * eBS;              // exp(Lam_C - Lam_r)
       const float ek = ev[rr] * kv[rr];
       const float qt = gv[rr] * qv[rr];
-      if (!safe) sL[r][ej] = lv[rr];
-      sX[r][ej] = M::cvt(ek * fs);
-      sY[r][ej] = M::cvt(qt * fs);
-      sZ[r][ej] = M::cvt(safe ? kv[rr] * __expf(-loc) : 0.f);
+      sL[bb][r][ej] = lv[rr];  // (unconditional: a branch here would make the
+                               // compiler drain every load and store in flight)
+      sX[bb][r][ej] = M::cvt(ek * fs);
+      sY[bb][r][ej] = M::cvt(qt * fs);
+      sZ[bb][r][ej] = M::cvt(safe ? kv[rr] * __expf(-loc) : 0.f);
       keT[rr] = kv[rr] * fe;
       uT[rr] = wv[rr] * vv[rr];
       ktT[rr] = ek * GL;
       qhT[rr] = qt * GL;
-      kbT[rr] = kv[rr] * kb;
+      kbT[rr] = kv[rr] * kbf;
     }
-    store4(&sKe[ej][4 * part], keT);
-    store4(&sR[ej][4 * part], uT);
-    store4(&sR[DV + ej][4 * part], ktT);
-    store4(&sQh[ej][4 * part], qhT);
+    store4(&sKe[bb][ej][4 * part], keT);
+    store4(&sR[bb][ej][4 * part], uT);
+    store4(&sR[bb][DV + ej][4 * part], ktT);
+    store4(&sQh[bb][ej][4 * part], qhT);
     store4(out.KbT + static_cast<size_t>(ej) * C + r0 + 4 * part, kbT);
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) out.Kb[static_cast<size_t>(r0 + 4 * part + rr) * DK + ej] = M::cvt(kbT[rr]);
+  };
+
+  // T_II = (I + A_II)^-1 from A_II in sAw, with P_II from sPf, into sT, sP
+  // and the summary, by wave 0
+  auto leaf_inverse = [&](int I) {
+    const f32x4 t = neumann16(sAw, sPw, sTw);
+    TC* tp = out.TP + static_cast<size_t>(I) * 512;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g + i;
+      const TC tv = M::cvt(t[i]);
+      const TC pv = M::cvt(sPf[r][c16]);
+      sT[r][c16] = tv;
+      sP[r][c16] = pv;
+      tp[r * 16 + c16] = tv;  // kept for the backward
+      tp[256 + r * 16 + c16] = pv;
+    }
+  };
+
+  prefetch(0);
+  if (PIPE) {
+    elementwise(0);
     __syncthreads();
+  }
+
+#pragma unroll 1
+  for (int I = 0; I < NB; ++I) {
+    const int r0 = 16 * I;
+    const int bb = PIPE ? I & 1 : 0;
+    const int safe = !((sUnsafe >> I) & 1);
+    if (!PIPE) {
+      elementwise(I);
+      __syncthreads();
+    }
 
     // ---- X H and Y H for this wave's columns ----
     f32x4 XH[NT], YH[NT];
@@ -282,8 +322,8 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
     if (I > 0) {
 #pragma unroll
       for (int s = 0; s < RT; ++s) {
-        const frag xa = M::load(&sX[c16][16 * s + 4 * g]);
-        const frag ya = M::load(&sY[c16][16 * s + 4 * g]);
+        const frag xa = M::load(&sX[bb][c16][16 * s + 4 * g]);
+        const frag ya = M::load(&sY[bb][c16][16 * s + 4 * g]);
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           const frag hb = M::from_f32(Hs[s][n]);
@@ -292,24 +332,26 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
         }
       }
     }
-    // ---- leaf: A_II, P_II, T_II ----
-    if (safe) {
-      if (wave == 0) {
-        f32x4 a = zero4(), p = zero4();
+    // ---- leaf: A_II, P_II, T_II (wave 0, when the leaf is within range) ----
+    if (safe && wave == 0) {
+      f32x4 a = zero4(), p = zero4();
 #pragma unroll
-        for (int s = 0; s < RT; ++s) {
-          const frag zb = M::load(&sZ[c16][16 * s + 4 * g]);
-          a = M::mma(M::load(&sX[c16][16 * s + 4 * g]), zb, a);
-          p = M::mma(M::load(&sY[c16][16 * s + 4 * g]), zb, p);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g + i;
-          sAw[r][c16] = c16 < r ? a[i] : 0.f;
-          sPf[r][c16] = c16 <= r ? p[i] : 0.f;
-        }
+      for (int s = 0; s < RT; ++s) {
+        const frag zb = M::load(&sZ[bb][c16][16 * s + 4 * g]);
+        a = M::mma(M::load(&sX[bb][c16][16 * s + 4 * g]), zb, a);
+        p = M::mma(M::load(&sY[bb][c16][16 * s + 4 * g]), zb, p);
       }
-    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        sAw[r][c16] = c16 < r ? a[i] : 0.f;
+        sPf[r][c16] = c16 <= r ? p[i] : 0.f;
+      }
+      leaf_inverse(I);
+    }
+    // ---- the next block's elementwise work, beside this block's products ----
+    if (PIPE && I + 1 < NB) elementwise(I + 1);
+    if (!safe) {
       // per-pair factors exp(Lam_r - Lam_i) = exp(sum of log_a over (i, r]) in (0, 1]
       for (int pr = tid; pr < 256; pr += NTH) {
         const int r = pr >> 4;
@@ -319,7 +361,7 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
           for (int j = 0; j < DK; ++j) {
             const uint32_t gr = gi(r0 + r, j), gq = gi(r0 + i, j);
             float ls = 0.f;
-            for (int x = i + 1; x <= r; ++x) ls += sL[x][j];
+            for (int x = i + 1; x <= r; ++x) ls += sL[bb][x][j];
             const float kk = ldv(kb, gq) * __expf(ls);
             a += ldv(eb, gr) * ldv(kb, gr) * kk;
             p += ldv(gb, gr) * ldv(qb, gr) * kk;
@@ -329,20 +371,7 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
         sPf[r][i] = p;
       }
       __syncthreads();
-    }
-    if (wave == 0) {
-      const f32x4 t = neumann16(sAw, sPw, sTw);
-      TC* tp = out.TP + static_cast<size_t>(I) * 512;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g + i;
-        const TC tv = M::cvt(t[i]);
-        const TC pv = M::cvt(sPf[r][c16]);
-        sT[r][c16] = tv;
-        sP[r][c16] = pv;
-        tp[r * 16 + c16] = tv;  // kept for the backward
-        tp[256 + r * 16 + c16] = pv;
-      }
+      if (wave == 0) leaf_inverse(I);
     }
     __syncthreads();
 
@@ -353,7 +382,7 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const int colg = wave * 32 + 16 * n + c16;
-      const f32x4 rhs = load4(&sR[colg][4 * g]) - XH[n];
+      const f32x4 rhs = load4(&sR[bb][colg][4 * g]) - XH[n];
       const f32x4 uw = M::mma(ta, M::from_f32(rhs), zero4());
       const f32x4 op = M::mma(pa, M::from_f32(uw), YH[n]);
       UW[n] = uw;
@@ -362,7 +391,7 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
         store4(out.OtT + static_cast<size_t>(colg) * C + r0 + 4 * g, op);
       } else {
         const int j = colg - DV;
-        const f32x4 qv = load4(&sQh[j][4 * g]) - op;
+        const f32x4 qv = load4(&sQh[bb][j][4 * g]) - op;
         store4(out.Wt + static_cast<size_t>(j) * C + r0 + 4 * g, uw);
         store4(out.Qt + static_cast<size_t>(j) * C + r0 + 4 * g, qv);
 #pragma unroll
@@ -376,10 +405,10 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
     if (I + 1 < NB) {
 #pragma unroll
       for (int s = 0; s < RT; ++s) {
-        const frag ka = M::load(&sKe[16 * s + c16][4 * g]);
+        const frag ka = M::load(&sKe[bb][16 * s + c16][4 * g]);
         f32x4 gs;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) gs[i] = sG[16 * s + 4 * g + i];
+        for (int i = 0; i < 4; ++i) gs[i] = sGB[I][16 * s + 4 * g + i];
 #pragma unroll
         for (int n = 0; n < NT; ++n) Hs[s][n] = M::mma(ka, M::from_f32(UW[n]), Hs[s][n] * gs);
       }
