@@ -45,6 +45,21 @@ struct ChunkShape {
   // its blocks), instead of a forward sweep that recomputes both: for
   // 64-token chunks in bf16, whose tiles then fit the LDS.
   bool bwd_direct() const { return bf16 && C == 64; }
+  // Segments of the split scans: 1 when the heads' 64-column scans alone fill
+  // the chip; else the sequence is cut into the fewest power-of-two segments
+  // that do, with at least 4 chunks each.
+  int scan_segments() const {
+    const long long cols = static_cast<long long>(B) * H * (DV / 64);
+    int n = 1;
+    while (cols * n < 256 && NC() / (2 * n) >= 4) n *= 2;
+    return n;
+  }
+  // Workspace of the split scans: per head and segment, the transition and
+  // offset [dk][DV + DK] and the segment start [dk][dv], fp32.
+  size_t scan_split_bytes() const {
+    const int n = scan_segments();
+    return n > 1 ? static_cast<size_t>(B) * H * n * DK * (2 * DV + DK) * 4 : 0;
+  }
 };
 
 hipError_t launch_step(int N, int H, int dk, int dv, bool bf16, const void* q, const void* k,
@@ -59,16 +74,17 @@ hipError_t launch_fwd_prep(const ChunkShape& s, const void* q, const void* k, co
 
 // Sequential over chunks: o (may be NULL), S_chunks (may be NULL), S_T (may be
 // NULL).  With `deltas` (the same summaries, writable) each chunk's deltas are
-// written into its summary.
+// written into its summary.  `split`: scan_split_bytes(s) of workspace.
 hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S0, void* o,
-                           float* S_chunks, float* S_T, void* deltas, hipStream_t stream);
+                           float* S_chunks, float* S_T, void* deltas, float* split, hipStream_t stream);
 
 // Reverse sequential over chunks: dS_chunks[c] = gradient w.r.t. the state at the
 // END of chunk c, in the compute type, as transposed 16-row tiles: element
 // (r, j) at ((r / 16) * DV + j) * 16 + r % 16 of the chunk's DK * DV block;
 // dS0 (fp32 [dk][dv], may be NULL).
 hipError_t launch_bwd_scan(const ChunkShape& s, const void* summ, const void* dO,
-                           const float* dS_T, void* dS_chunks, float* dS0, hipStream_t stream);
+                           const float* dS_T, void* dS_chunks, float* dS0, float* split,
+                           hipStream_t stream);
 
 // Chunk-parallel: all input gradients of every chunk.  `summ` holds the
 // chunk summaries (their leaf blocks are read; with bwd_direct also Kbar^T,

@@ -32,18 +32,22 @@ muir_status_t check_dims(const muir_dims_t* d, ChunkShape* s) {
   return MUIR_OK;
 }
 
-size_t fwd_ws(const ChunkShape& s) { return s.nchunks() * s.summary_bytes(); }
+// Forward workspace: the chunk summaries, then the split scan's segment
+// transitions and starts (when the shape splits its scan).
+size_t fwd_ws(const ChunkShape& s) { return s.nchunks() * s.summary_bytes() + s.scan_split_bytes(); }
 
 // Backward workspace: chunk summaries (used when the caller passes none),
 // recomputed chunk states (used when the caller passes no S_chunks), the
-// chunk-end state gradients, and per-chunk scratch for the deltas and their
-// gradients.  Every part is always reserved, so the size does not depend on
-// which pointers are passed.
+// chunk-end state gradients, per-chunk scratch for the deltas and their
+// gradients, then the split scans' segment area (shared by the recomputed
+// forward scan and the reverse scan, which run one after the other).  Every
+// part is always reserved, so the size does not depend on which pointers are
+// passed.
 size_t bwd_scratch_bytes(const ChunkShape& s) {
   return (muir::bwd_chunk_scratch_bytes(s) + 255) & ~static_cast<size_t>(255);
 }
 size_t bwd_ws(const ChunkShape& s) {
-  return s.nchunks() * (s.summary_bytes() + 2 * s.state_bytes() + bwd_scratch_bytes(s));
+  return s.nchunks() * (s.summary_bytes() + 2 * s.state_bytes() + bwd_scratch_bytes(s)) + s.scan_split_bytes();
 }
 
 // Optional per-kernel timing: when the caller registers an array of HIP
@@ -150,7 +154,8 @@ muir_status_t muir_chunk_fwd(const muir_dims_t* dims, const void* q, const void*
   mark(hs);
   // a forward that saves its chunk states keeps the deltas for the direct backward
   void* deltas = S_chunks && s.bwd_direct() ? workspace : nullptr;
-  if (muir::launch_fwd_scan(s, workspace, S0, o, S_chunks, S_T, deltas, hs) != hipSuccess)
+  float* split = reinterpret_cast<float*>(static_cast<char*>(workspace) + s.nchunks() * s.summary_bytes());
+  if (muir::launch_fwd_scan(s, workspace, S0, o, S_chunks, S_T, deltas, split, hs) != hipSuccess)
     return MUIR_ERR_HIP;
   mark(hs);
   return MUIR_OK;
@@ -192,6 +197,7 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void*
   float* S_rec = reinterpret_cast<float*>(ws + s.nchunks() * s.summary_bytes());
   float* dS_chunks = S_rec + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
   float* scratch = dS_chunks + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
+  float* split = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) + s.nchunks() * bwd_scratch_bytes(s));
   const float* Sc = S_chunks;
   const void* summ = summaries;
   mark(hs);
@@ -212,12 +218,12 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void*
   if (!Sc) {
     // chunk-start states are not given: rerun the forward scan
     void* deltas = s.bwd_direct() ? ws : nullptr;  // summ is ws here
-    if (muir::launch_fwd_scan(s, summ, S0, nullptr, S_rec, nullptr, deltas, hs) != hipSuccess)
+    if (muir::launch_fwd_scan(s, summ, S0, nullptr, S_rec, nullptr, deltas, split, hs) != hipSuccess)
       return MUIR_ERR_HIP;
     mark(hs);
     Sc = S_rec;
   }
-  if (muir::launch_bwd_scan(s, summ, dO, dS_T, dS_chunks, dS0, hs) != hipSuccess)
+  if (muir::launch_bwd_scan(s, summ, dO, dS_T, dS_chunks, dS0, split, hs) != hipSuccess)
     return MUIR_ERR_HIP;
   mark(hs);
   if (muir::launch_bwd_chunk(s, q, k, v, log_a, erase, write, gamma, summ, Sc, dS_chunks, dO, dq,

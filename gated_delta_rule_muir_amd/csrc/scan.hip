@@ -53,11 +53,20 @@ template <typename TC> __device__ __forceinline__ typename MM<TC>::frag identity
 // ---------------------------------------------------------------------------
 // Forward.  Reads W [C][DK], Q' [C][DK], Kbar^T [DK][C], U~^T [DV][C],
 // O~^T [DV][C] and Gamma_C of each chunk summary (SummaryPart).
-template <typename Tin, int DK, int NW>
+//
+// Segments: the chunks of a sequence are split into nseg consecutive
+// segments, one workgroup row each.  With TRANS the kernel runs the
+// recurrence S <- (diag(Gamma_C) - Kbar^T W) S + Kbar^T U~ over its segment
+// from [S | P] = [0 | I] (dk more state columns, whose U~ is zero) and writes
+// the segment's offset E and transition P into trans[head][seg] ([dk][DV + DK]
+// fp32); without it, segment seg > 0 starts from S_seg[head][seg] ([dk][dv]
+// fp32, formed from those by seg_combine_kernel) and segment 0 from S0.
+template <typename Tin, int DK, int NW, bool TRANS>
 __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
     int T, int H, int C, const char* __restrict__ summ, size_t summ_bytes,
     const float* __restrict__ S0, Tin* __restrict__ o, float* __restrict__ S_chunks,
-    float* __restrict__ S_T, char* __restrict__ dsumm, size_t dl_offset) {
+    float* __restrict__ S_T, char* __restrict__ dsumm, size_t dl_offset, int nseg,
+    const float* __restrict__ S_seg, float* __restrict__ trans) {
   typedef Tin TC;
   typedef MM<TC> M;
   typedef typename M::frag frag;
@@ -79,12 +88,20 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
   constexpr int PK = words_per_thread<K_WORDS, NTH>();
   constexpr int PU = words_per_thread<U_WORDS, NTH>();
   constexpr int PG = words_per_thread<G_WORDS, NTH>();
+  constexpr int NCOL = TRANS ? DV + DK : DV;  // state columns ([S | P] with TRANS)
 
   const int NC = T / C;
   const int NSB = C / SB;
-  const int nvb = DV / NV;
-  const int bh = blockIdx.x / nvb;
-  const int vb = blockIdx.x - bh * nvb;
+  const int nvb = NCOL / NV;
+  const int bh = blockIdx.x / (nseg * nvb);
+  const int rem = blockIdx.x - bh * (nseg * nvb);
+  const int seg = rem / nvb;
+  const int vb = rem - seg * nvb;
+  const int L = (NC + nseg - 1) / nseg;  // chunks per segment
+  const int cbeg = min(NC, seg * L);
+  const int cend = min(NC, cbeg + L);
+  const bool pcols = TRANS && vb * NV >= DV;  // transition columns: no U~ (their loads read tile 0)
+  const int vbu = pcols ? 0 : vb;
   const int b = bh / H;
   const int h = bh - b * H;
   const int tid = threadIdx.x;
@@ -113,14 +130,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
     const uint32_t wofs = part(SP_W) + static_cast<uint32_t>(sb * SB * LW);
     const uint32_t qofs = part(SP_QP) + static_cast<uint32_t>(sb * SB * LW);
     const uint32_t kofs = part(SP_KBT) + static_cast<uint32_t>(sb * LK);
-    const uint32_t uofs = part(SP_UTT) + static_cast<uint32_t>(vb * NV * C * SZ + sb * LK);
-    const uint32_t oofs = part(SP_OTT) + static_cast<uint32_t>(vb * NV * C * SZ + sb * LK);
+    const uint32_t uofs = part(SP_UTT) + static_cast<uint32_t>(vbu * NV * C * SZ + sb * LK);
+    const uint32_t oofs = part(SP_OTT) + static_cast<uint32_t>(vbu * NV * C * SZ + sb * LK);
     const uint32_t gofs = part(SP_END);
 #pragma unroll
     for (int k = 0; k < PW; ++k) {
       const int w = min(tid + k * NTH, W_WORDS - 1);
       rw[k] = *reinterpret_cast<const u32x4*>(at(base, wofs + 16 * w));
-      rq[k] = *reinterpret_cast<const u32x4*>(at(base, qofs + 16 * w));
+      if constexpr (!TRANS) rq[k] = *reinterpret_cast<const u32x4*>(at(base, qofs + 16 * w));
     }
 #pragma unroll
     for (int k = 0; k < PK; ++k) {
@@ -132,7 +149,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
       const int w = min(tid + k * NTH, U_WORDS - 1);
       const uint32_t ro_ = (w / CK) * C * SZ + 16 * (w % CK);
       ru[k] = *reinterpret_cast<const u32x4*>(at(base, uofs + ro_));
-      ro[k] = *reinterpret_cast<const u32x4*>(at(base, oofs + ro_));
+      if constexpr (!TRANS) ro[k] = *reinterpret_cast<const u32x4*>(at(base, oofs + ro_));
     }
 #pragma unroll
     for (int k = 0; k < PG; ++k) {
@@ -147,7 +164,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
       const int w = min(tid + k * NTH, W_WORDS - 1);
       const int a = swz<LW>(w / CW, 16 * (w % CW));
       *reinterpret_cast<u32x4*>(sW + a) = rw[k];
-      *reinterpret_cast<u32x4*>(sQ + a) = rq[k];
+      if constexpr (!TRANS) *reinterpret_cast<u32x4*>(sQ + a) = rq[k];
     }
 #pragma unroll
     for (int k = 0; k < PK; ++k) {
@@ -158,8 +175,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
     for (int k = 0; k < PU; ++k) {
       const int w = min(tid + k * NTH, U_WORDS - 1);
       const int a = swz<LK>(w / CK, 16 * (w % CK));
-      *reinterpret_cast<u32x4*>(sU + a) = ru[k];
-      *reinterpret_cast<u32x4*>(sO + a) = ro[k];
+      const u32x4 zw = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sU + a) = pcols ? zw : ru[k];
+      if constexpr (!TRANS) *reinterpret_cast<u32x4*>(sO + a) = ro[k];
     }
 #pragma unroll
     for (int k = 0; k < PG; ++k) {
@@ -171,26 +189,34 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
   const frag ident = identity_frag<TC>(g, c16);
   const size_t sbase = static_cast<size_t>(bh) * DK * DV;
   f32x4 S[RT];
+  {
+    // the segment's start: [0 | I] with TRANS, else S0 or the segment state
+    const float* src = seg == 0 ? (S0 ? S0 + sbase : nullptr)
+                                : S_seg + (static_cast<size_t>(bh) * nseg + seg) * DK * DV;
 #pragma unroll
-  for (int s = 0; s < RT; ++s)
+    for (int s = 0; s < RT; ++s)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      S[s][i] = S0 ? S0[sbase + static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * s + 4 * g + i;
+        if constexpr (TRANS) S[s][i] = (pcols && row == colg - DV) ? 1.f : 0.f;
+        else S[s][i] = src ? src[static_cast<size_t>(row) * DV + colg] : 0.f;
+      }
+  }
   frag Sf[RT];
   f32x4 dS[RT];
 
-  const int U = NC * NSB;
-  if (U > 0) prefetch(0);
+  const int U0 = cbeg * NSB, U1 = cend * NSB;
+  if (U0 < U1) prefetch(U0);
 #pragma unroll 1
-  for (int u = 0; u < U; ++u) {
+  for (int u = U0; u < U1; ++u) {
     const int c = u / NSB;
     const int sb = u - c * NSB;
     __syncthreads();  // the previous unit's LDS reads are done
     commit();
-    prefetch(u + 1 < U ? u + 1 : u);
+    prefetch(u + 1 < U1 ? u + 1 : u);
     __syncthreads();
     if (sb == 0) {
-      if (S_chunks) {
+      if (!TRANS && S_chunks) {
         float* dst = S_chunks + (static_cast<size_t>(bh) * NC + c) * DK * DV;
 #pragma unroll
         for (int s = 0; s < RT; ++s)
@@ -206,19 +232,20 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
     // token t of the unit is sequence position c*C + sb*SB + t
     const size_t obase = ((static_cast<size_t>(b) * T + static_cast<size_t>(c) * C + sb * SB) * H + h) * DV;
     // this chunk's deltas [C][DV] in its summary (when they are kept)
-    TC* dlc = dsumm ? reinterpret_cast<TC*>(dsumm + (static_cast<size_t>(bh) * NC + c) * summ_bytes + dl_offset)
-                    : nullptr;
+    TC* dlc = (!TRANS && dsumm)
+                  ? reinterpret_cast<TC*>(dsumm + (static_cast<size_t>(bh) * NC + c) * summ_bytes + dl_offset)
+                  : nullptr;
 #pragma unroll 2
     for (int m = 0; m < SB / 16; ++m) {
       f32x4 Oa = zero4(), Da = zero4();
 #pragma unroll
       for (int s = 0; s < RT; ++s) {
         const int a = swz<LW>(16 * m + c16, (16 * s + 4 * g) * SZ);
-        if (o) Oa = M::mma(M::load(reinterpret_cast<const TC*>(sQ + a)), Sf[s], Oa);
+        if (!TRANS && o) Oa = M::mma(M::load(reinterpret_cast<const TC*>(sQ + a)), Sf[s], Oa);
         Da = M::mma(M::load(reinterpret_cast<const TC*>(sW + a)), Sf[s], Da);
       }
       const int au = swz<LK>(16 * wave + c16, (16 * m + 4 * g) * SZ);
-      if (o) {
+      if (!TRANS && o) {
         const f32x4 ot = load4(reinterpret_cast<const TC*>(sO + au));
         // tokens 4g+i, column c16 -> token c16, columns 4g..4g+3
         const f32x4 tt = M::mma(M::from_f32(Oa + ot), ident, zero4());
@@ -243,7 +270,13 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
         for (int i = 0; i < 4; ++i) S[s][i] = sgC[16 * s + 4 * g + i] * S[s][i] + dS[s][i];
     }
   }
-  if (S_T) {
+  if constexpr (TRANS) {
+    float* dst = trans + (static_cast<size_t>(bh) * nseg + seg) * DK * NCOL;
+#pragma unroll
+    for (int s = 0; s < RT; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * s + 4 * g + i) * NCOL + colg] = S[s][i];
+  } else if (S_T && seg == nseg - 1) {
 #pragma unroll
     for (int s = 0; s < RT; ++s)
 #pragma unroll
@@ -255,11 +288,17 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
 // Backward, on the same summaries: reads W^T [DK][C], Q'^T [DK][C] and
 // Kbar [C][DK] (the orientations whose contraction index is contiguous for
 // these products) and Gamma_C.
-template <typename Tin, int DK, int NW>
+//
+// Segments as in the forward, walked in reverse: with TRANS the kernel runs
+// dS <- (diag(Gamma_C) - W^T Kbar) dS + Q'^T dO over its segment from
+// [0 | I] (dk more columns, whose dO is zero) into trans[head][seg]; without
+// it, the last segment starts from dS_T and segment seg from dS_seg[head][seg]
+// (the gradient at the segment's end), and segment 0 writes dS0.
+template <typename Tin, int DK, int NW, bool TRANS>
 __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
     int T, int H, int C, const char* __restrict__ summ, size_t summ_bytes,
     const Tin* __restrict__ dO, const float* __restrict__ dS_T, Tin* __restrict__ dS_chunks,
-    float* __restrict__ dS0) {
+    float* __restrict__ dS0, int nseg, const float* __restrict__ dS_seg, float* __restrict__ trans) {
   typedef Tin TC;
   typedef MM<TC> M;
   typedef typename M::frag frag;
@@ -284,12 +323,20 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
   constexpr int PO = words_per_thread<O_WORDS, NTH>();
   constexpr int PG = words_per_thread<G_WORDS, NTH>();
   static_assert(LO >= 32, "dO row segment");
+  constexpr int NCOL = TRANS ? DV + DK : DV;  // state-gradient columns ([dS | P] with TRANS)
 
   const int NC = T / C;
   const int NSB = C / SB;
-  const int nvb = DV / NV;
-  const int bh = blockIdx.x / nvb;
-  const int vb = blockIdx.x - bh * nvb;
+  const int nvb = NCOL / NV;
+  const int bh = blockIdx.x / (nseg * nvb);
+  const int rem = blockIdx.x - bh * (nseg * nvb);
+  const int seg = rem / nvb;
+  const int vb = rem - seg * nvb;
+  const int L = (NC + nseg - 1) / nseg;  // chunks per segment
+  const int cbeg = min(NC, seg * L);
+  const int cend = min(NC, cbeg + L);
+  const bool pcols = TRANS && vb * NV >= DV;  // transition columns: no dO (their loads read tile 0)
+  const int vbu = pcols ? 0 : vb;
   const int b = bh / H;
   const int h = bh - b * H;
   const int tid = threadIdx.x;
@@ -308,8 +355,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
   const char* hsum = summ + static_cast<size_t>(bh) * NC * summ_bytes;
   u32x4 rt[PT], rq[PT], rk[PK], rd[PO], rg[PG];
 
-  // unit u walks the chunks in reverse, and each chunk's units in reverse
-  auto unit_c = [&](int u) { return NC - 1 - u / NSB; };
+  // unit u walks the segment's chunks in reverse, and each chunk's units in reverse
+  auto unit_c = [&](int u) { return cend - 1 - u / NSB; };
   auto unit_sb = [&](int u) { return NSB - 1 - (u - (u / NSB) * NSB); };
 
   auto prefetch = [&](int u) {
@@ -322,7 +369,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
     const uint32_t kofs = part(SP_KB) + static_cast<uint32_t>(sb * SB * LW);
     const uint32_t gofs = part(SP_END);
     const char* dob = reinterpret_cast<const char*>(
-        dO + ((static_cast<size_t>(b) * T + static_cast<size_t>(c) * C + sb * SB) * H + h) * DV + vb * NV);
+        dO + ((static_cast<size_t>(b) * T + static_cast<size_t>(c) * C + sb * SB) * H + h) * DV + vbu * NV);
 #pragma unroll
     for (int k = 0; k < PT; ++k) {
       const int w = min(tid + k * NTH, T_WORDS - 1);
@@ -363,7 +410,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
 #pragma unroll
     for (int k = 0; k < PO; ++k) {
       const int w = min(tid + k * NTH, O_WORDS - 1);
-      *reinterpret_cast<u32x4*>(sDO + swz<LO>(w / CO, 16 * (w % CO))) = rd[k];
+      const u32x4 zw = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(sDO + swz<LO>(w / CO, 16 * (w % CO))) = pcols ? zw : rd[k];
     }
 #pragma unroll
     for (int k = 0; k < PG; ++k) {
@@ -375,15 +423,23 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
   const frag ident = identity_frag<TC>(g, c16);
   const size_t sbase = static_cast<size_t>(bh) * DK * DV;
   f32x4 dS[RT];
+  {
+    // the segment's end: [0 | I] with TRANS, else dS_T or the segment state
+    const float* src = seg == nseg - 1 ? (dS_T ? dS_T + sbase : nullptr)
+                                       : dS_seg + (static_cast<size_t>(bh) * nseg + seg) * DK * DV;
 #pragma unroll
-  for (int s = 0; s < RT; ++s)
+    for (int s = 0; s < RT; ++s)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      dS[s][i] = dS_T ? dS_T[sbase + static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * s + 4 * g + i;
+        if constexpr (TRANS) dS[s][i] = (pcols && row == colg - DV) ? 1.f : 0.f;
+        else dS[s][i] = src ? src[static_cast<size_t>(row) * DV + colg] : 0.f;
+      }
+  }
   frag dSf[RT];
   f32x4 Z[RT];
 
-  const int U = NC * NSB;
+  const int U = (cend - cbeg) * NSB;
   if (U > 0) prefetch(0);
 #pragma unroll 1
   for (int u = 0; u < U; ++u) {
@@ -399,7 +455,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
       TC* dst = dS_chunks + (static_cast<size_t>(bh) * NC + c) * DK * DV;
 #pragma unroll
       for (int s = 0; s < RT; ++s) {
-        store4(at(dst, static_cast<uint32_t>((s * DV + colg) * 16 + 4 * g)), dS[s]);
+        if constexpr (!TRANS) store4(at(dst, static_cast<uint32_t>((s * DV + colg) * 16 + 4 * g)), dS[s]);
         dSf[s] = M::from_f32(dS[s]);
         Z[s] = zero4();
       }
@@ -432,7 +488,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
         for (int i = 0; i < 4; ++i) dS[s][i] = sgC[16 * s + 4 * g + i] * dS[s][i] + Z[s][i];
     }
   }
-  if (dS0) {
+  if constexpr (TRANS) {
+    float* dst = trans + (static_cast<size_t>(bh) * nseg + seg) * DK * NCOL;
+#pragma unroll
+    for (int s = 0; s < RT; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * s + 4 * g + i) * NCOL + colg] = dS[s][i];
+  } else if (dS0 && seg == 0) {
 #pragma unroll
     for (int s = 0; s < RT; ++s)
 #pragma unroll
@@ -440,60 +502,147 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
   }
 }
 
-}  // namespace
-
-// Four waves (64 columns) per workgroup when that still fills the chip, else
-// one wave (16 columns) per workgroup for more independent chains.
-hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S0, void* o,
-                           float* S_chunks, float* S_T, void* deltas, hipStream_t stream) {
-  const int heads = s.B * s.H;
-  if (heads == 0) return hipSuccess;
-  const bool wide = static_cast<long long>(heads) * (s.DV / 64) >= 256;
-#define MUIR_SCAN(TT, DD, NW)                                                                      \
-  hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, NW>), dim3(heads * (s.DV / (16 * NW))),              \
-                     dim3(64 * NW), 0, stream, s.T, s.H, s.C, (const char*)summ, s.summary_bytes(), \
-                     S0, (TT*)o, S_chunks, S_T, (char*)deltas, s.dl_offset())
-  if (s.bf16) {
-    if (s.DK == 128) {
-      if (wide) MUIR_SCAN(uint16_t, 128, 4); else MUIR_SCAN(uint16_t, 128, 1);
-    } else {
-      if (wide) MUIR_SCAN(uint16_t, 64, 4); else MUIR_SCAN(uint16_t, 64, 1);
+// ---------------------------------------------------------------------------
+// The segment recurrence of a split scan: x_next = P_g x + E_g with
+// [E_g | P_g] = trans[head][g] ([dk][DV + DK] fp32, from a TRANS scan),
+// applied from x0 (NULL: zero) over the segments in order (reverse: from the
+// last segment down); the value that starts each later segment (reverse: each
+// earlier one) goes to xseg[head][segment] ([dk][dv] fp32).  fp32 MFMA; four
+// waves of 16 columns per workgroup.
+template <int DK>
+__global__ __launch_bounds__(256) void seg_combine_kernel(int nseg, int reverse, const float* __restrict__ x0,
+                                                          const float* __restrict__ trans,
+                                                          float* __restrict__ xseg) {
+  typedef MM<float> MF;
+  constexpr int DV = DK;
+  constexpr int RT = DK / 16;
+  constexpr int NCOL = DV + DK;
+  const int nvb = DV / 64;
+  const int bh = blockIdx.x / nvb;
+  const int vb = blockIdx.x - bh * nvb;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int c16 = lane & 15;
+  const int colg = vb * 64 + 16 * wave + c16;
+  f32x4 X[RT];
+#pragma unroll
+  for (int s = 0; s < RT; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      X[s][i] = x0 ? x0[static_cast<size_t>(bh) * DK * DV + static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] : 0.f;
+#pragma unroll 1
+  for (int st = 0; st + 1 < nseg; ++st) {
+    const int gs = reverse ? nseg - 1 - st : st;  // the segment whose map applies
+    const int gd = reverse ? gs - 1 : gs + 1;     // the segment its result starts
+    const float* tr = trans + (static_cast<size_t>(bh) * nseg + gs) * DK * NCOL;
+    f32x4 Y[RT];
+#pragma unroll
+    for (int s = 0; s < RT; ++s) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Y[s][i] = tr[static_cast<size_t>(16 * s + 4 * g + i) * NCOL + colg];
+#pragma unroll
+      for (int kk = 0; kk < RT; ++kk) {
+        // P rows 16s + c16, columns 16kk + 4g..4g+3 as the left operand
+        const f32x4 a = *reinterpret_cast<const f32x4*>(tr + static_cast<size_t>(16 * s + c16) * NCOL + DV + 16 * kk + 4 * g);
+        Y[s] = MF::mma(a, X[kk], Y[s]);
+      }
     }
-  } else {
-    if (s.DK == 128) {
-      if (wide) MUIR_SCAN(float, 128, 4); else MUIR_SCAN(float, 128, 1);
-    } else {
-      if (wide) MUIR_SCAN(float, 64, 4); else MUIR_SCAN(float, 64, 1);
+    float* dst = xseg + (static_cast<size_t>(bh) * nseg + gd) * DK * DV;
+#pragma unroll
+    for (int s = 0; s < RT; ++s) {
+      X[s] = Y[s];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] = X[s][i];
     }
   }
-#undef MUIR_SCAN
+}
+
+}  // namespace
+
+// One scan over every head: four waves (64 columns) per workgroup when that
+// fills the chip; with fewer heads the sequence is split into segments
+// (ChunkShape::scan_segments): each segment's transition, the segment
+// recurrence, then every segment's scan from its start -- else one wave (16
+// columns) per workgroup.
+template <typename TT, int DD>
+hipError_t fwd_scan_typed(const ChunkShape& s, const void* summ, const float* S0, void* o,
+                          float* S_chunks, float* S_T, void* deltas, float* split, hipStream_t stream) {
+  const int heads = s.B * s.H;
+  const int nseg = s.scan_segments();
+  const size_t sb = s.summary_bytes();
+  if (nseg > 1) {
+    float* trans = split;
+    float* sseg = split + static_cast<size_t>(heads) * nseg * DD * (2 * DD);
+    hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, true>), dim3(heads * nseg * (2 * DD / 64)), dim3(256), 0,
+                       stream, s.T, s.H, s.C, (const char*)summ, sb, S0, (TT*)nullptr, (float*)nullptr,
+                       (float*)nullptr, (char*)nullptr, size_t(0), nseg, (const float*)nullptr, trans);
+    hipLaunchKernelGGL((seg_combine_kernel<DD>), dim3(heads * (DD / 64)), dim3(256), 0, stream, nseg, 0, S0,
+                       (const float*)trans, sseg);
+    hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, false>), dim3(heads * nseg * (DD / 64)), dim3(256), 0, stream,
+                       s.T, s.H, s.C, (const char*)summ, sb, S0, (TT*)o, S_chunks, S_T, (char*)deltas,
+                       s.dl_offset(), nseg, (const float*)sseg, (float*)nullptr);
+  } else if (static_cast<long long>(heads) * (DD / 64) >= 256) {
+    hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, false>), dim3(heads * (DD / 64)), dim3(256), 0, stream, s.T,
+                       s.H, s.C, (const char*)summ, sb, S0, (TT*)o, S_chunks, S_T, (char*)deltas, s.dl_offset(), 1,
+                       (const float*)nullptr, (float*)nullptr);
+  } else {
+    hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 1, false>), dim3(heads * (DD / 16)), dim3(64), 0, stream, s.T,
+                       s.H, s.C, (const char*)summ, sb, S0, (TT*)o, S_chunks, S_T, (char*)deltas, s.dl_offset(), 1,
+                       (const float*)nullptr, (float*)nullptr);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_scan(const ChunkShape& s, const void* summ, const void* dO, const float* dS_T,
-                           void* dS_chunks, float* dS0, hipStream_t stream) {
+template <typename TT, int DD>
+hipError_t bwd_scan_typed(const ChunkShape& s, const void* summ, const void* dO, const float* dS_T,
+                          void* dS_chunks, float* dS0, float* split, hipStream_t stream) {
   const int heads = s.B * s.H;
-  if (heads == 0) return hipSuccess;
-  const bool wide = static_cast<long long>(heads) * (s.DV / 64) >= 256;
-#define MUIR_BSCAN(TT, DD, NW)                                                                     \
-  hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, NW>), dim3(heads * (s.DV / (16 * NW))),              \
-                     dim3(64 * NW), 0, stream, s.T, s.H, s.C, (const char*)summ, s.summary_bytes(), \
-                     (const TT*)dO, dS_T, (TT*)dS_chunks, dS0)
-  if (s.bf16) {
-    if (s.DK == 128) {
-      if (wide) MUIR_BSCAN(uint16_t, 128, 4); else MUIR_BSCAN(uint16_t, 128, 1);
-    } else {
-      if (wide) MUIR_BSCAN(uint16_t, 64, 4); else MUIR_BSCAN(uint16_t, 64, 1);
-    }
+  const int nseg = s.scan_segments();
+  const size_t sb = s.summary_bytes();
+  if (nseg > 1) {
+    float* trans = split;
+    float* sseg = split + static_cast<size_t>(heads) * nseg * DD * (2 * DD);
+    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, true>), dim3(heads * nseg * (2 * DD / 64)), dim3(256), 0,
+                       stream, s.T, s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks,
+                       (float*)nullptr, nseg, (const float*)nullptr, trans);
+    hipLaunchKernelGGL((seg_combine_kernel<DD>), dim3(heads * (DD / 64)), dim3(256), 0, stream, nseg, 1, dS_T,
+                       (const float*)trans, sseg);
+    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, false>), dim3(heads * nseg * (DD / 64)), dim3(256), 0, stream,
+                       s.T, s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks, dS0, nseg,
+                       (const float*)sseg, (float*)nullptr);
+  } else if (static_cast<long long>(heads) * (DD / 64) >= 256) {
+    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, false>), dim3(heads * (DD / 64)), dim3(256), 0, stream, s.T,
+                       s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks, dS0, 1,
+                       (const float*)nullptr, (float*)nullptr);
   } else {
-    if (s.DK == 128) {
-      if (wide) MUIR_BSCAN(float, 128, 4); else MUIR_BSCAN(float, 128, 1);
-    } else {
-      if (wide) MUIR_BSCAN(float, 64, 4); else MUIR_BSCAN(float, 64, 1);
-    }
+    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 1, false>), dim3(heads * (DD / 16)), dim3(64), 0, stream, s.T,
+                       s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks, dS0, 1,
+                       (const float*)nullptr, (float*)nullptr);
   }
-#undef MUIR_BSCAN
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S0, void* o,
+                           float* S_chunks, float* S_T, void* deltas, float* split, hipStream_t stream) {
+  if (s.B * s.H == 0) return hipSuccess;
+  if (s.bf16) {
+    return s.DK == 128 ? fwd_scan_typed<uint16_t, 128>(s, summ, S0, o, S_chunks, S_T, deltas, split, stream)
+                       : fwd_scan_typed<uint16_t, 64>(s, summ, S0, o, S_chunks, S_T, deltas, split, stream);
+  }
+  return s.DK == 128 ? fwd_scan_typed<float, 128>(s, summ, S0, o, S_chunks, S_T, deltas, split, stream)
+                     : fwd_scan_typed<float, 64>(s, summ, S0, o, S_chunks, S_T, deltas, split, stream);
+}
+
+hipError_t launch_bwd_scan(const ChunkShape& s, const void* summ, const void* dO, const float* dS_T,
+                           void* dS_chunks, float* dS0, float* split, hipStream_t stream) {
+  if (s.B * s.H == 0) return hipSuccess;
+  if (s.bf16) {
+    return s.DK == 128 ? bwd_scan_typed<uint16_t, 128>(s, summ, dO, dS_T, dS_chunks, dS0, split, stream)
+                       : bwd_scan_typed<uint16_t, 64>(s, summ, dO, dS_T, dS_chunks, dS0, split, stream);
+  }
+  return s.DK == 128 ? bwd_scan_typed<float, 128>(s, summ, dO, dS_T, dS_chunks, dS0, split, stream)
+                     : bwd_scan_typed<float, 64>(s, summ, dO, dS_T, dS_chunks, dS0, split, stream);
 }
 
 }  // namespace muir

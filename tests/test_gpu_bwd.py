@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import muir_inputs
+import oracle
 from gpu_util import NAMES, TOL, oracle_bwd, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -97,3 +98,25 @@ def test_bwd_with_saved_summaries_equals_recompute():
     for n in GRADS:
         assert torch.equal(g1[n], ref[n]), n
         assert torch.equal(g2[n], ref[n]), n
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_split_scan_matches_oracle(dtype):
+    """One head over 64 chunks: the state scans split into 8 segments (each
+    segment's transition, the segment recurrence, then each segment's scan
+    from its start), forward and backward, against the oracle."""
+    m = _lib()
+    B, T, H, d, C = 1, 4096, 1, 128, 64
+    inp = muir_inputs.seq_inputs(B, T, H, d, d, dtype=dtype, decay="channel", seed=12, S0_scale=0.1,
+                                 with_dO=True, with_dST=True)
+    dv = to_dev(inp)
+    o, S_T, Sc = m.muir_chunk_fwd(*(dv[n] for n in NAMES), dv["S0"], chunk=C, save_states=True)
+    g = m.muir_chunk_bwd(*(dv[n] for n in NAMES), dv["dO"], S0=dv["S0"], S_chunks=Sc, dS_T=dv["dS_T"], chunk=C)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"])
+    ref = oracle.bwd(*(inp[n] for n in NAMES), inp["dO"], S0=inp["S0"], dS_T=inp["dS_T"])
+    errs = {"o": rel_err(o, o_ref), "S_T": rel_err(S_T, S_ref)}
+    errs.update({n: rel_err(g[n], ref[n]) for n in GRADS})
+    _say(f"split scan {dtype}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for n, e in errs.items():
+        assert e <= TOL[dtype], (n, e)

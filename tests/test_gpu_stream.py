@@ -7,9 +7,10 @@ previous segment's final state (S_T -> S0).  The stream then continues with
 inference; the fp32 state is the whole context).
 
 Checks:
-  * every chained segment equals the same tokens of one call over the whole
-    sequence, bitwise (o and the final state): chunk boundaries line up, so the
-    arithmetic is the same;
+  * every chained segment matches the same tokens of one call over the whole
+    sequence (o and the final state) within the bf16 tolerance: with two heads
+    both calls split their state scan into segments, at different places, so
+    the rounding differs;
   * head 0 against the fp64 oracle, sequentially over all 256K + 64 tokens:
     o of every prefill token, the state after the prefill, every decode
     output and the final state, each within 2e-2 (max |gpu - oracle| / max |oracle|).
@@ -48,9 +49,11 @@ def test_chunked_prefill_then_decode_256k():
     for s0 in range(0, T, SEG):
         seg = {n: dv[n][:, s0:s0 + SEG].contiguous() for n in NAMES}
         o_seg, S, _ = m.muir_chunk_fwd(*(seg[n] for n in NAMES), S, chunk=C, workspace=ws)
-        assert torch.equal(o_seg, o_full[:, s0:s0 + SEG]), s0
-    assert torch.equal(S, S_full)
-    _say("[stream] chained segments equal the single call")
+        e = rel_err(o_seg, o_full[:, s0:s0 + SEG])
+        assert e <= TOL, (s0, e)
+    e = rel_err(S, S_full)
+    assert e <= TOL, e
+    _say("[stream] chained segments match the single call")
 
     rates = muir_inputs.step_rates(H, d, seed=21)
     steps = [muir_inputs.step_inputs(B, H, d, d, t, rates=rates, dtype="bf16", seed=21) for t in range(STEPS)]
