@@ -27,8 +27,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libmuir.so")
 
 MUIR_F32, MUIR_BF16 = 0, 1
+MUIR_GAMMA_TOKEN, MUIR_GAMMA_STATIC, MUIR_GAMMA_NONE = 0, 1, 2
 STATUS = {0: "MUIR_OK", 1: "MUIR_ERR_NULL", 2: "MUIR_ERR_SHAPE", 3: "MUIR_ERR_DTYPE",
-          4: "MUIR_ERR_WORKSPACE", 5: "MUIR_ERR_ALIGN", 6: "MUIR_ERR_HIP"}
+          4: "MUIR_ERR_WORKSPACE", 5: "MUIR_ERR_ALIGN", 6: "MUIR_ERR_HIP", 7: "MUIR_ERR_MODE"}
 
 
 class MuirError(RuntimeError):
@@ -40,7 +41,7 @@ class MuirError(RuntimeError):
 class _Dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("gamma_mode", ctypes.c_int32)]
 
 
 _lib = None
@@ -71,7 +72,7 @@ def lib():
         L.muir_chunk_fwd.restype = ctypes.c_int
         L.muir_chunk_bwd.argtypes = [D] + [P] * 7 + [P, P, P, P, P] + [P] * 8 + [P, SZ, P]
         L.muir_chunk_bwd.restype = ctypes.c_int
-        L.muir_step.argtypes = [I32] * 5 + [P] * 7 + [P, P, P]
+        L.muir_step.argtypes = [I32] * 6 + [P] * 7 + [P, P, P]
         L.muir_step.restype = ctypes.c_int
         L.muir_set_profile_events.argtypes = [P, I32]
         L.muir_set_profile_events.restype = I32
@@ -116,17 +117,29 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _dims(B, T, H, dk, dv, chunk, dtype) -> _Dims:
-    return _Dims(B, T, H, dk, dv, chunk, dtype)
+def _dims(B, T, H, dk, dv, chunk, dtype, gamma_mode=MUIR_GAMMA_TOKEN) -> _Dims:
+    return _Dims(B, T, H, dk, dv, chunk, dtype, gamma_mode)
 
 
-def muir_chunk_fwd_workspace(B, T, H, dk, dv, chunk, dtype=MUIR_BF16) -> int:
-    d = _dims(B, T, H, dk, dv, chunk, dtype)
+def _gamma_mode(gamma, lead, H, dk, dt, dev) -> int:
+    """The readout gate's form from its shape: None (no gate), [H, dk] (static
+    per head and key channel) or lead + [H, dk] (per token)."""
+    if gamma is None:
+        return MUIR_GAMMA_NONE
+    if gamma.dim() == 2:
+        _check_io("gamma", gamma, (H, dk), dt, dev)
+        return MUIR_GAMMA_STATIC
+    _check_io("gamma", gamma, tuple(lead) + (H, dk), dt, dev)
+    return MUIR_GAMMA_TOKEN
+
+
+def muir_chunk_fwd_workspace(B, T, H, dk, dv, chunk, dtype=MUIR_BF16, gamma_mode=MUIR_GAMMA_TOKEN) -> int:
+    d = _dims(B, T, H, dk, dv, chunk, dtype, gamma_mode)
     return int(lib().muir_chunk_fwd_workspace(ctypes.byref(d)))
 
 
-def muir_chunk_bwd_workspace(B, T, H, dk, dv, chunk, dtype=MUIR_BF16) -> int:
-    d = _dims(B, T, H, dk, dv, chunk, dtype)
+def muir_chunk_bwd_workspace(B, T, H, dk, dv, chunk, dtype=MUIR_BF16, gamma_mode=MUIR_GAMMA_TOKEN) -> int:
+    d = _dims(B, T, H, dk, dv, chunk, dtype, gamma_mode)
     return int(lib().muir_chunk_bwd_workspace(ctypes.byref(d)))
 
 
@@ -140,7 +153,8 @@ def muir_chunk_fwd(q, k, v, log_a, erase, write, gamma, S0=None, *, chunk: int =
                    save_states: bool = False, final_state: bool = True,
                    workspace: Optional[torch.Tensor] = None, out=None
                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
-    """Chunkwise forward.  Inputs [B, T, H, D] (bf16 or fp32, on one GPU).
+    """Chunkwise forward.  Inputs [B, T, H, D] (bf16 or fp32, on one GPU);
+    gamma [B, T, H, dk], or [H, dk] (a static gate), or None (no gate).
 
     Returns (o [B,T,H,dv] in the input dtype, S_T [B,H,dk,dv] fp32 or None,
     S_chunks [B,H,T/chunk,dk,dv] fp32 or None).
@@ -149,8 +163,9 @@ def muir_chunk_fwd(q, k, v, log_a, erase, write, gamma, S0=None, *, chunk: int =
     dv = v.shape[3]
     dev, dt = q.device, q.dtype
     code = _dtype_code(q)
-    for n, t in (("q", q), ("k", k), ("log_a", log_a), ("erase", erase), ("gamma", gamma)):
+    for n, t in (("q", q), ("k", k), ("log_a", log_a), ("erase", erase)):
         _check_io(n, t, (B, T, H, dk), dt, dev)
+    gm = _gamma_mode(gamma, (B, T), H, dk, dt, dev)
     for n, t in (("v", v), ("write", write)):
         _check_io(n, t, (B, T, H, dv), dt, dev)
     if S0 is not None:
@@ -159,7 +174,7 @@ def muir_chunk_fwd(q, k, v, log_a, erase, write, gamma, S0=None, *, chunk: int =
     S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if final_state else None
     S_chunks = (torch.empty((B, H, T // chunk if chunk else 0, dk, dv), dtype=torch.float32, device=dev)
                 if save_states else None)
-    d = _dims(B, T, H, dk, dv, chunk, code)
+    d = _dims(B, T, H, dk, dv, chunk, code, gm)
     nbytes = int(lib().muir_chunk_fwd_workspace(ctypes.byref(d)))
     ws = _workspace(nbytes, dev, workspace)
     rc = lib().muir_chunk_fwd(ctypes.byref(d), *(_ptr(t) for t in (q, k, v, log_a, erase, write, gamma)),
@@ -174,8 +189,9 @@ def muir_chunk_bwd(q, k, v, log_a, erase, write, gamma, dO, S0=None, S_chunks=No
                    chunk: int = 64, summaries: Optional[torch.Tensor] = None,
                    workspace: Optional[torch.Tensor] = None, want_dS0: bool = True):
     """Chunkwise backward.  Returns a dict of gradients (dq, dk, dv, dlog_a,
-    derase, dwrite, dgamma in the input dtype, accumulated in fp32 and rounded
-    once; dS0 in fp32).
+    derase, dwrite in the input dtype, accumulated in fp32 and rounded once;
+    dgamma in the input dtype for a per-token gate, [H, dk] fp32 (summed over
+    batch and tokens) for a static one, None without a gate; dS0 in fp32).
 
     `S_chunks` (from muir_chunk_fwd(save_states=True)) and `summaries` (the
     `workspace` tensor of that forward call, left unchanged) are saved forward
@@ -187,8 +203,9 @@ def muir_chunk_bwd(q, k, v, log_a, erase, write, gamma, dO, S0=None, S_chunks=No
     dv = v.shape[3]
     dev, dt = q.device, q.dtype
     code = _dtype_code(q)
-    for n, t in (("q", q), ("k", k), ("log_a", log_a), ("erase", erase), ("gamma", gamma)):
+    for n, t in (("q", q), ("k", k), ("log_a", log_a), ("erase", erase)):
         _check_io(n, t, (B, T, H, dk), dt, dev)
+    gm = _gamma_mode(gamma, (B, T), H, dk, dt, dev)
     for n, t in (("v", v), ("write", write), ("dO", dO)):
         _check_io(n, t, (B, T, H, dv), dt, dev)
     if S0 is not None:
@@ -198,15 +215,17 @@ def muir_chunk_bwd(q, k, v, log_a, erase, write, gamma, dO, S0=None, S_chunks=No
     if S_chunks is not None:
         _check_io("S_chunks", S_chunks, (B, H, T // chunk, dk, dv), torch.float32, dev)
     if summaries is not None:
-        need = muir_chunk_fwd_workspace(B, T, H, dk, dv, chunk, code)
+        need = muir_chunk_fwd_workspace(B, T, H, dk, dv, chunk, code, gm)
         if (not summaries.is_cuda or summaries.device != dev or not summaries.is_contiguous()
                 or summaries.numel() * summaries.element_size() < need):
             raise ValueError(f"summaries: expected the forward workspace ({need} bytes on {dev})")
     gd = dict(dtype=dt, device=dev)
-    g = {n: torch.empty((B, T, H, dk), **gd) for n in ("dq", "dk", "dlog_a", "derase", "dgamma")}
+    g = {n: torch.empty((B, T, H, dk), **gd) for n in ("dq", "dk", "dlog_a", "derase")}
     g.update({n: torch.empty((B, T, H, dv), **gd) for n in ("dv", "dwrite")})
+    g["dgamma"] = (torch.empty((B, T, H, dk), **gd) if gm == MUIR_GAMMA_TOKEN else
+                   torch.empty((H, dk), dtype=torch.float32, device=dev) if gm == MUIR_GAMMA_STATIC else None)
     g["dS0"] = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None
-    d = _dims(B, T, H, dk, dv, chunk, code)
+    d = _dims(B, T, H, dk, dv, chunk, code, gm)
     nbytes = int(lib().muir_chunk_bwd_workspace(ctypes.byref(d)))
     ws = _workspace(nbytes, dev, workspace)
     rc = lib().muir_chunk_bwd(ctypes.byref(d), *(_ptr(t) for t in (q, k, v, log_a, erase, write, gamma)),
@@ -220,19 +239,21 @@ def muir_chunk_bwd(q, k, v, log_a, erase, write, gamma, dO, S0=None, S_chunks=No
 
 
 def muir_step(q, k, v, log_a, erase, write, gamma, S, *, out=None) -> torch.Tensor:
-    """One decode step for [N, H, D] inputs; S [N, H, dk, dv] fp32 is updated in place.
+    """One decode step for [N, H, D] inputs (gamma [N, H, dk], or [H, dk] for a
+    static gate, or None); S [N, H, dk, dv] fp32 is updated in place.
     Returns o [N, H, dv] in the input dtype."""
     N, H, dk = q.shape
     dv = v.shape[2]
     dev, dt = q.device, q.dtype
     code = _dtype_code(q)
-    for n, t in (("q", q), ("k", k), ("log_a", log_a), ("erase", erase), ("gamma", gamma)):
+    for n, t in (("q", q), ("k", k), ("log_a", log_a), ("erase", erase)):
         _check_io(n, t, (N, H, dk), dt, dev)
+    gm = _gamma_mode(gamma, (N,), H, dk, dt, dev)
     for n, t in (("v", v), ("write", write)):
         _check_io(n, t, (N, H, dv), dt, dev)
     _check_io("S", S, (N, H, dk, dv), torch.float32, dev)
     o = out if out is not None else torch.empty((N, H, dv), dtype=dt, device=dev)
-    rc = lib().muir_step(N, H, dk, dv, code, *(_ptr(t) for t in (q, k, v, log_a, erase, write, gamma)),
+    rc = lib().muir_step(N, H, dk, dv, code, gm, *(_ptr(t) for t in (q, k, v, log_a, erase, write, gamma)),
                          _ptr(S), _ptr(o), _stream(dev))
     if rc != 0:
         raise MuirError(rc, "muir_step")

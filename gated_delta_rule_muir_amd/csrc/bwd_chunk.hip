@@ -59,7 +59,7 @@ template <typename TC, int DK, int C> constexpr int stage_split() {
   return DK == 64 ? 1 : (sizeof(TC) == 2 ? (C == 64 ? 1 : 2) : (C == 64 ? 4 : 8));
 }
 
-template <typename Tin, int DK, int C, int NW, bool DIRECT>
+template <typename Tin, int DK, int C, int NW, bool DIRECT, bool GTOK>
 __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     int T, int H, const Tin* __restrict__ q, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ log_a, const Tin* __restrict__ erase,
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     const Tin* __restrict__ dS_chunks, const Tin* __restrict__ dO, Tin* __restrict__ dq,
     Tin* __restrict__ dk, Tin* __restrict__ dv, Tin* __restrict__ dlog_a,
     Tin* __restrict__ derase, Tin* __restrict__ dwrite, Tin* __restrict__ dgamma,
-    char* __restrict__ scratch) {
+    char* __restrict__ scratch, int gmode, float* __restrict__ dgam_part) {
   typedef Tin TC;
   typedef MM<TC> M;
   typedef typename M::frag frag;
@@ -127,7 +127,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   const Tin* lb = log_a + ebase;
   const Tin* eb = erase + ebase;
   const Tin* wb = write + ebase;
-  const Tin* gb = gamma + ebase;
+  // readout gate: per token at gb (as the other inputs), static at the
+  // head's row gst, or none (both then point into q; the value is not used)
+  const Tin* gbase = gmode == GAMMA_NONE ? q : gamma;
+  const Tin* gb = gbase + ebase;
+  const Tin* gst = gbase + static_cast<size_t>(h) * DK;
   const Tin* dOb = dO + ebase;
   Tin* dqb = dq + ebase;
   Tin* dkb = dk + ebase;
@@ -137,6 +141,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   Tin* dwb = dwrite + ebase;
   Tin* dgb = dgamma + ebase;
   auto gi = [&](int t, int j) -> uint32_t { return static_cast<uint32_t>(t) * HD + static_cast<uint32_t>(j); };
+  // the readout gate of element (t, j) of the chunk (GTOK: per token, as the
+  // other inputs; else static or none, chosen at run time)
+  auto gam = [&](int t, int j) -> float {
+    const uint32_t o = static_cast<uint32_t>(t) * HD + static_cast<uint32_t>(j);
+    if constexpr (GTOK) return ldv(gb, o);
+    const float x = ldv(gst, static_cast<uint32_t>(j));
+    return gmode == GAMMA_NONE ? 1.f : x;
+  };
   TC* gDel = reinterpret_cast<TC*>(scratch + static_cast<size_t>(chunk) * bwd_scratch_bytes_tc<TC>(C, DK, DV));
   TC* gS = gDel + static_cast<size_t>(C) * DV;  // [NB][DK][DV]
   // T_II, P_II of the chunk's blocks, from the chunk summary, [NB][2][16][16]
@@ -318,7 +330,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       xk[rr] = ldv(kb, o);
       xe[rr] = ldv(eb, o);
       xq[rr] = ldv(qb, o);
-      xg[rr] = ldv(gb, o);
+      xg[rr] = gam(r0 + RPT * part + rr, ej);
     }
 #pragma unroll
     for (int e = 0; e < RW; ++e) {
@@ -345,7 +357,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       for (int ii = 0; ii < 4; ++ii) {
         const uint32_t o = gi(r0 + 4 * g + ii, colv(n));
         oq[n][ii] = ldv(qb, o);
-        og[n][ii] = ldv(gb, o);
+        og[n][ii] = gam(r0 + 4 * g + ii, colv(n));
         ov[n][ii] = ldv(vb, o);
         ow[n][ii] = ldv(wb, o);
         ok[n][ii] = ldv(kb, o);
@@ -672,6 +684,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     }
   __syncthreads();
   float carry[NT];  // sum of dLam over the finished (later) tokens, channel colv(n)
+  float gsum[NT];   // static readout gate: this lane's share of the chunk's sum of dgamma
+#pragma unroll
+  for (int n = 0; n < NT; ++n) gsum[n] = 0.f;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     float t = 0.f;
@@ -904,7 +919,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
           for (int r = t; r < 16; ++r) {
             const float f = pair_factor(r0, r, t, j);
             const uint32_t orj = gi(r0 + r, j);
-            const float qt = ldv(gb, orj) * ldv(qb, orj);
+            const float qt = gam(r0 + r, j) * ldv(qb, orj);
             const float ek = ldv(eb, orj) * ldv(kb, orj);
             vk += f * (sLf[0][r][t] * qt - sLf[1][r][t] * ek);
           }
@@ -936,7 +951,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       }
       carry[n] += t0 + t1 + t2 + t3;
       store_grad(dqb, r0, n, gq);
-      store_grad(dgb, r0, n, gg);
+      if constexpr (GTOK) store_grad(dgb, r0, n, gg);
+      gsum[n] += (gg[0] + gg[1]) + (gg[2] + gg[3]);
       store_grad(deb, r0, n, ge);
       store_grad(dkb, r0, n, gk);
       store_grad(dlb, r0, n, gl);
@@ -961,6 +977,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     }
     __syncthreads();
   }
+  if (gmode == GAMMA_STATIC) {
+    // the chunk's sum of dgamma per key channel (lanes c16 + 16g' hold the token groups)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const float t0 = __shfl(gsum[n], c16, 64), t1 = __shfl(gsum[n], c16 + 16, 64);
+      const float t2 = __shfl(gsum[n], c16 + 32, 64), t3 = __shfl(gsum[n], c16 + 48, 64);
+      if (g == 0) dgam_part[static_cast<size_t>(chunk) * DK + colv(n)] = ((t0 + t1) + t2) + t3;
+    }
+  }
 }
 
 }  // namespace
@@ -975,15 +1000,22 @@ hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, c
                             const void* gamma, const void* summ, const float* S_chunks,
                             const void* dS_chunks, const void* dO, void* dq, void* dk, void* dv,
                             void* dlog_a, void* derase, void* dwrite, void* dgamma, void* scratch,
+                            float* dgam_part,
                             hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(s.nchunks());
   if (grid == 0) return hipSuccess;
-#define MUIR_BCH1(TT, DD, CC, NW, DIR)                                                                      \
-  hipLaunchKernelGGL((bwd_chunk_kernel<TT, DD, CC, NW, DIR>), dim3(grid), dim3(64 * NW), 0, stream, s.T, s.H, \
+#define MUIR_BCH2(TT, DD, CC, NW, DIR, GT)                                                                      \
+  hipLaunchKernelGGL((bwd_chunk_kernel<TT, DD, CC, NW, DIR, GT>), dim3(grid), dim3(64 * NW), 0, stream, s.T, s.H, \
                      (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, (const TT*)erase,      \
                      (const TT*)write, (const TT*)gamma, (const char*)summ, s.summary_bytes(),          \
                      s.tp_offset(), s.dl_offset(), S_chunks, (const TT*)dS_chunks, (const TT*)dO, (TT*)dq, (TT*)dk,      \
-                     (TT*)dv, (TT*)dlog_a, (TT*)derase, (TT*)dwrite, (TT*)dgamma, (char*)scratch)
+                     (TT*)dv, (TT*)dlog_a, (TT*)derase, (TT*)dwrite, (TT*)dgamma, (char*)scratch, s.gmode, \
+                     dgam_part)
+#define MUIR_BCH1(TT, DD, CC, NW, DIR)                              \
+  do {                                                              \
+    if (s.gmode == GAMMA_TOKEN) MUIR_BCH2(TT, DD, CC, NW, DIR, true); \
+    else MUIR_BCH2(TT, DD, CC, NW, DIR, false);                     \
+  } while (0)
 #define MUIR_BCH(TT, DD, NW, DIR64)                         \
   do {                                                      \
     if (s.C == 64) MUIR_BCH1(TT, DD, 64, NW, DIR64);        \
@@ -1001,6 +1033,34 @@ hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, c
   }
 #undef MUIR_BCH
 #undef MUIR_BCH1
+#undef MUIR_BCH2
+  return hipGetLastError();
+}
+
+namespace {
+// dgamma of a static readout gate: per (head, key channel), the sum of the
+// per-chunk partial sums over the batch and the chunks (fixed order).
+__global__ __launch_bounds__(256) void gamma_sum_kernel(int B, int H, int NC, int DK,
+                                                        const float* __restrict__ part,
+                                                        float* __restrict__ dgamma) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= H * DK) return;
+  const int h = idx / DK;
+  const int j = idx - h * DK;
+  float acc = 0.f;
+  for (int b = 0; b < B; ++b) {
+    const float* p = part + (static_cast<size_t>(b) * H + h) * NC * DK + j;
+    for (int c = 0; c < NC; ++c) acc += p[static_cast<size_t>(c) * DK];
+  }
+  dgamma[idx] = acc;
+}
+}  // namespace
+
+hipError_t launch_gamma_sum(const ChunkShape& s, const float* part, float* dgamma, hipStream_t stream) {
+  const int n = s.H * s.DK;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(gamma_sum_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, s.B, s.H, s.NC(), s.DK, part,
+                     dgamma);
   return hipGetLastError();
 }
 

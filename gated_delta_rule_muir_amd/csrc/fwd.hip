@@ -72,7 +72,7 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
     int T, int H, const Tin* __restrict__ q, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ log_a, const Tin* __restrict__ erase,
     const Tin* __restrict__ write, const Tin* __restrict__ gamma, char* __restrict__ summ,
-    size_t summ_bytes) {
+    size_t summ_bytes, int gmode) {
   typedef Tin TC;
   typedef MM<TC> M;
   typedef typename M::frag frag;
@@ -111,7 +111,12 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
   const Tin* lb = log_a + ebase;
   const Tin* eb = erase + ebase;
   const Tin* wb = write + ebase;
-  const Tin* gb = gamma + ebase;
+  // readout gate: element (t, j) at gsel + t * gts + j, with gsel and gts
+  // uniform -- per token (the gate's chunk base, stride H*dk), static (the
+  // head's row, stride 0), or none (q's chunk base; the value is not used)
+  const Tin* gsel = gmode == GAMMA_TOKEN ? gamma + ebase
+                    : gmode == GAMMA_STATIC ? gamma + static_cast<size_t>(h) * DK : q + ebase;
+  const uint32_t gts = gmode == GAMMA_STATIC ? 0u : HD;
   auto gi = [&](int t, int j) -> uint32_t { return static_cast<uint32_t>(t) * HD + static_cast<uint32_t>(j); };
 
   // per block I and channel: B_I = Lam at the end of block I-1 (B_0 = 0)
@@ -197,7 +202,7 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
       pk[rr] = *at(kb, o);
       pe[rr] = *at(eb, o);
       pq[rr] = *at(qb, o);
-      pg[rr] = *at(gb, o);
+      pg[rr] = *at(gsel, static_cast<uint32_t>(16 * I + 4 * part + rr) * gts + static_cast<uint32_t>(ej));
       pv[rr] = *at(vb, o);
       pw[rr] = *at(wb, o);
       pl[rr] = *at(lb, o);
@@ -216,7 +221,7 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
       kv[rr] = M::to_f32(pk[rr]);
       ev[rr] = M::to_f32(pe[rr]);
       qv[rr] = M::to_f32(pq[rr]);
-      gv[rr] = M::to_f32(pg[rr]);
+      gv[rr] = gmode == GAMMA_NONE ? 1.f : M::to_f32(pg[rr]);
       vv[rr] = M::to_f32(pv[rr]);
       wv[rr] = M::to_f32(pw[rr]);
       lv[rr] = M::to_f32(pl[rr]);
@@ -364,7 +369,8 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
             for (int x = i + 1; x <= r; ++x) ls += sL[bb][x][j];
             const float kk = ldv(kb, gq) * __expf(ls);
             a += ldv(eb, gr) * ldv(kb, gr) * kk;
-            p += ldv(gb, gr) * ldv(qb, gr) * kk;
+            const float gr_ = gmode == GAMMA_NONE ? 1.f : ldv(gsel, static_cast<uint32_t>(r0 + r) * gts + j);
+            p += gr_ * ldv(qb, gr) * kk;
           }
         }
         sAw[r][i] = i < r ? a : 0.f;
@@ -441,7 +447,7 @@ hipError_t launch_fwd_prep(const ChunkShape& s, const void* q, const void* k, co
   hipLaunchKernelGGL((fwd_prep_kernel<TT, DD, CC>), dim3(grid), dim3((2 * DD / 32) * 64), 0,         \
                      stream, s.T, s.H, (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, \
                      (const TT*)erase, (const TT*)write, (const TT*)gamma, (char*)summ,            \
-                     s.summary_bytes())
+                     s.summary_bytes(), s.gmode)
 #define MUIR_PREP(TT, DD)                         \
   do {                                            \
     if (s.C == 64) MUIR_PREP1(TT, DD, 64);        \

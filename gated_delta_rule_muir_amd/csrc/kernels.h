@@ -23,10 +23,15 @@ __host__ __device__ constexpr size_t summary_part(int part, int C, int DK, int D
                                static_cast<size_t>(part - SP_WT) * C * DK;
 }
 
+// Readout-gate forms: per token [B, T, H, dk]; static per (head, key channel)
+// [H, dk]; none (gamma = 1, no pointer).
+enum GammaMode { GAMMA_TOKEN = 0, GAMMA_STATIC = 1, GAMMA_NONE = 2 };
+
 // Sizes and derived quantities of one chunkwise call, validated by the API.
 struct ChunkShape {
   int B, T, H, DK, DV, C;
   bool bf16;
+  int gmode;  // GammaMode
   int NC() const { return T / C; }
   size_t nchunks() const { return static_cast<size_t>(B) * H * NC(); }
   size_t tc_bytes() const { return bf16 ? 2 : 4; }
@@ -62,12 +67,13 @@ struct ChunkShape {
   }
 };
 
-hipError_t launch_step(int N, int H, int dk, int dv, bool bf16, const void* q, const void* k,
-                       const void* v, const void* log_a, const void* erase, const void* write,
-                       const void* gamma, float* S, void* o, hipStream_t stream);
+hipError_t launch_step(int N, int H, int dk, int dv, bool bf16, int gmode, const void* q,
+                       const void* k, const void* v, const void* log_a, const void* erase,
+                       const void* write, const void* gamma, float* S, void* o, hipStream_t stream);
 
 // Chunk-parallel: per chunk summary (W, Q', Kbar, U~, O~, Gamma_C and the
-// 16-token leaf blocks T_II, P_II) into `summ`.
+// 16-token leaf blocks T_II, P_II) into `summ`.  `gamma` in the form s.gmode
+// (unused, and may be NULL, for GAMMA_NONE).
 hipError_t launch_fwd_prep(const ChunkShape& s, const void* q, const void* k, const void* v,
                            const void* log_a, const void* erase, const void* write,
                            const void* gamma, void* summ, hipStream_t stream);
@@ -98,6 +104,10 @@ hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, c
                             const void* dS_chunks,
                             const void* dO, void* dq, void* dk, void* dv, void* dlog_a,
                             void* derase, void* dwrite, void* dgamma, void* scratch,
-                            hipStream_t stream);
+                            float* dgam_part, hipStream_t stream);
+
+// dgamma [H][dk] fp32 of a static readout gate from bwd_chunk's per-chunk
+// partial sums ([nchunks][dk] fp32).
+hipError_t launch_gamma_sum(const ChunkShape& s, const float* part, float* dgamma, hipStream_t stream);
 
 }  // namespace muir

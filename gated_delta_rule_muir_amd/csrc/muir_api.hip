@@ -14,6 +14,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 muir_status_t check_dims(const muir_dims_t* d, ChunkShape* s) {
   if (!d) return MUIR_ERR_NULL;
   if (d->dtype != MUIR_F32 && d->dtype != MUIR_BF16) return MUIR_ERR_DTYPE;
+  if (d->gamma_mode < MUIR_GAMMA_TOKEN || d->gamma_mode > MUIR_GAMMA_NONE) return MUIR_ERR_MODE;
   if (d->B < 0 || d->T < 0 || d->H < 0) return MUIR_ERR_SHAPE;
   if (d->dk != d->dv || (d->dk != 64 && d->dk != 128)) return MUIR_ERR_SHAPE;
   if (d->chunk != 64 && d->chunk != 128 && d->chunk != 256) return MUIR_ERR_SHAPE;
@@ -29,6 +30,7 @@ muir_status_t check_dims(const muir_dims_t* d, ChunkShape* s) {
   s->DV = d->dv;
   s->C = d->chunk;
   s->bf16 = d->dtype == MUIR_BF16;
+  s->gmode = d->gamma_mode;
   return MUIR_OK;
 }
 
@@ -46,8 +48,20 @@ size_t fwd_ws(const ChunkShape& s) { return s.nchunks() * s.summary_bytes() + s.
 size_t bwd_scratch_bytes(const ChunkShape& s) {
   return (muir::bwd_chunk_scratch_bytes(s) + 255) & ~static_cast<size_t>(255);
 }
+// per-chunk partial sums of a static readout gate's gradient, [nchunks][dk] fp32
+size_t gamma_part_bytes(const ChunkShape& s) {
+  return (s.nchunks() * s.DK * 4 + 255) & ~static_cast<size_t>(255);
+}
 size_t bwd_ws(const ChunkShape& s) {
-  return s.nchunks() * (s.summary_bytes() + 2 * s.state_bytes() + bwd_scratch_bytes(s)) + s.scan_split_bytes();
+  return s.nchunks() * (s.summary_bytes() + 2 * s.state_bytes() + bwd_scratch_bytes(s)) + s.scan_split_bytes() +
+         gamma_part_bytes(s);
+}
+
+// The readout gate's pointer is required (and checked) unless the gate is absent.
+muir_status_t check_gate(const ChunkShape& s, const void* p) {
+  if (s.gmode == MUIR_GAMMA_NONE) return MUIR_OK;
+  if (!p) return MUIR_ERR_NULL;
+  return aligned16(p) ? MUIR_OK : MUIR_ERR_ALIGN;
 }
 
 // Optional per-kernel timing: when the caller registers an array of HIP
@@ -81,7 +95,7 @@ hipError_t copy_or_zero(float* dst, const float* src, size_t n, hipStream_t s) {
 
 extern "C" {
 
-int32_t muir_abi_version(void) { return 3; }
+int32_t muir_abi_version(void) { return 4; }
 
 int32_t muir_set_profile_events(void** events, int32_t count) {
   if (count < 0 || (count > 0 && !events)) return MUIR_ERR_NULL;
@@ -102,6 +116,7 @@ const char* muir_status_string(muir_status_t st) {
     case MUIR_ERR_WORKSPACE: return "workspace missing or too small";
     case MUIR_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case MUIR_ERR_HIP: return "a HIP kernel launch failed";
+    case MUIR_ERR_MODE: return "unknown readout-gate mode";
   }
   return "unknown status";
 }
@@ -128,11 +143,12 @@ muir_status_t muir_chunk_fwd(const muir_dims_t* dims, const void* q, const void*
   if (st != MUIR_OK) return st;
   const bool empty = s.nchunks() == 0;
   if (!empty) {
-    const void* req[] = {q, k, v, log_a, erase, write, gamma, o};
+    const void* req[] = {q, k, v, log_a, erase, write, o};
     for (const void* p : req)
       if (!p) return MUIR_ERR_NULL;
     for (const void* p : req)
       if (!aligned16(p)) return MUIR_ERR_ALIGN;
+    if ((st = check_gate(s, gamma)) != MUIR_OK) return st;
     if (!workspace || workspace_bytes < fwd_ws(s)) return MUIR_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MUIR_ERR_ALIGN;
   }
@@ -173,12 +189,13 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void*
   if (st != MUIR_OK) return st;
   const bool empty = s.nchunks() == 0;
   if (!empty) {
-    const void* req[] = {q, k, v, log_a, erase, write, gamma, dO,
-                         dq, dk, dv, dlog_a, derase, dwrite, dgamma};
+    const void* req[] = {q, k, v, log_a, erase, write, dO, dq, dk, dv, dlog_a, derase, dwrite};
     for (const void* p : req)
       if (!p) return MUIR_ERR_NULL;
     for (const void* p : req)
       if (!aligned16(p)) return MUIR_ERR_ALIGN;
+    if ((st = check_gate(s, gamma)) != MUIR_OK) return st;
+    if ((st = check_gate(s, dgamma)) != MUIR_OK) return st;
     if (!workspace || workspace_bytes < bwd_ws(s)) return MUIR_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MUIR_ERR_ALIGN;
   }
@@ -191,6 +208,12 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void*
       const size_t n = static_cast<size_t>(s.B) * s.H * s.DK * s.DV;
       if (copy_or_zero(dS0, dS_T, n, hs) != hipSuccess) return MUIR_ERR_HIP;
     }
+    // a static gate's gradient is a sum over no tokens
+    if (s.gmode == MUIR_GAMMA_STATIC && dgamma && s.H > 0) {
+      if ((st = check_gate(s, dgamma)) != MUIR_OK) return st;
+      if (copy_or_zero(static_cast<float*>(dgamma), nullptr, static_cast<size_t>(s.H) * s.DK, hs) != hipSuccess)
+        return MUIR_ERR_HIP;
+    }
     return MUIR_OK;
   }
   char* ws = static_cast<char*>(workspace);
@@ -198,6 +221,7 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void*
   float* dS_chunks = S_rec + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
   float* scratch = dS_chunks + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
   float* split = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) + s.nchunks() * bwd_scratch_bytes(s));
+  float* gpart = reinterpret_cast<float*>(reinterpret_cast<char*>(split) + s.scan_split_bytes());
   const float* Sc = S_chunks;
   const void* summ = summaries;
   mark(hs);
@@ -227,30 +251,38 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void*
     return MUIR_ERR_HIP;
   mark(hs);
   if (muir::launch_bwd_chunk(s, q, k, v, log_a, erase, write, gamma, summ, Sc, dS_chunks, dO, dq,
-                             dk, dv, dlog_a, derase, dwrite, dgamma, scratch, hs) != hipSuccess)
+                             dk, dv, dlog_a, derase, dwrite, dgamma, scratch, gpart, hs) != hipSuccess)
+    return MUIR_ERR_HIP;
+  if (s.gmode == MUIR_GAMMA_STATIC &&
+      muir::launch_gamma_sum(s, gpart, static_cast<float*>(dgamma), hs) != hipSuccess)
     return MUIR_ERR_HIP;
   mark(hs);
   return MUIR_OK;
 }
 
 muir_status_t muir_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtype,
-                        const void* q, const void* k, const void* v, const void* log_a,
-                        const void* erase, const void* write, const void* gamma, float* S,
-                        void* o, void* stream) {
+                        int32_t gamma_mode, const void* q, const void* k, const void* v,
+                        const void* log_a, const void* erase, const void* write, const void* gamma,
+                        float* S, void* o, void* stream) {
   if (dtype != MUIR_F32 && dtype != MUIR_BF16) return MUIR_ERR_DTYPE;
+  if (gamma_mode < MUIR_GAMMA_TOKEN || gamma_mode > MUIR_GAMMA_NONE) return MUIR_ERR_MODE;
   if (N < 0 || H < 0 || (dk != 64 && dk != 128) || dv <= 0 || dv % 64 != 0 || dv > 4096)
     return MUIR_ERR_SHAPE;
   if (static_cast<long long>(N) * H * (dv / 64) > (1LL << 30)) return MUIR_ERR_SHAPE;
   if (static_cast<long long>(N) * H == 0) return MUIR_OK;
-  const void* req[] = {q, k, v, log_a, erase, write, gamma, S, o};
+  const void* req[] = {q, k, v, log_a, erase, write, S, o};
   for (const void* p : req)
     if (!p) return MUIR_ERR_NULL;
   for (const void* p : req)
     if (!aligned16(p)) return MUIR_ERR_ALIGN;
+  if (gamma_mode != MUIR_GAMMA_NONE) {
+    if (!gamma) return MUIR_ERR_NULL;
+    if (!aligned16(gamma)) return MUIR_ERR_ALIGN;
+  }
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   mark(hs);
-  if (muir::launch_step(N, H, dk, dv, dtype == MUIR_BF16, q, k, v, log_a, erase, write, gamma, S,
-                        o, hs) != hipSuccess)
+  if (muir::launch_step(N, H, dk, dv, dtype == MUIR_BF16, gamma_mode, q, k, v, log_a, erase, write, gamma,
+                        S, o, hs) != hipSuccess)
     return MUIR_ERR_HIP;
   mark(hs);
   return MUIR_OK;

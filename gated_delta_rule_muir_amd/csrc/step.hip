@@ -14,6 +14,7 @@
 // slice (DK/16 rows x 4 columns) in registers between the reductions and the
 // write-back, so S is streamed exactly once each way with 16-byte accesses.
 #include "device_common.h"
+#include "kernels.h"
 
 namespace muir {
 
@@ -24,7 +25,7 @@ template <typename Tin, int DK>
 __global__ __launch_bounds__(STEP_THREADS) void step_kernel(
     int H, int DV, const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ log_a, const Tin* __restrict__ erase, const Tin* __restrict__ write,
-    const Tin* __restrict__ gamma, float* __restrict__ S, Tin* __restrict__ o) {
+    const Tin* __restrict__ gamma, float* __restrict__ S, Tin* __restrict__ o, int gmode) {
   constexpr int RP = DK / 16;  // rows per thread
   const int nslices = DV / STEP_COLS;
   const int head = blockIdx.x / nslices;  // flattened (n, h)
@@ -42,7 +43,12 @@ __global__ __launch_bounds__(STEP_THREADS) void step_kernel(
     float kj = Elem<Tin>::load(k, vk + j);
     s_alpha[j] = __expf(Elem<Tin>::load(log_a, vk + j));
     s_ek[j] = Elem<Tin>::load(erase, vk + j) * kj;
-    s_qt[j] = Elem<Tin>::load(gamma, vk + j) * Elem<Tin>::load(q, vk + j);
+    // readout gate per token, static per (head, channel), or none (its
+    // address then points into q and the value is not used)
+    const Tin* gsrc = gmode == GAMMA_NONE ? q : gamma;
+    const float graw = Elem<Tin>::load(gsrc, gmode == GAMMA_STATIC ? static_cast<size_t>(head % H) * DK + j : vk + j);
+    const float gj = gmode == GAMMA_NONE ? 1.f : graw;
+    s_qt[j] = gj * Elem<Tin>::load(q, vk + j);
     s_k[j] = kj;
   }
   __syncthreads();
@@ -111,15 +117,15 @@ __global__ __launch_bounds__(STEP_THREADS) void step_kernel(
   }
 }
 
-hipError_t launch_step(int N, int H, int dk, int dv, bool bf16, const void* q, const void* k,
-                       const void* v, const void* log_a, const void* erase, const void* write,
-                       const void* gamma, float* S, void* o, hipStream_t stream) {
+hipError_t launch_step(int N, int H, int dk, int dv, bool bf16, int gmode, const void* q,
+                       const void* k, const void* v, const void* log_a, const void* erase,
+                       const void* write, const void* gamma, float* S, void* o, hipStream_t stream) {
   const int grid = N * H * (dv / STEP_COLS);
   if (grid == 0) return hipSuccess;
 #define MUIR_STEP_LAUNCH(TT, DD)                                                                     \
   hipLaunchKernelGGL((step_kernel<TT, DD>), dim3(grid), dim3(STEP_THREADS), 0, stream, H, dv,        \
                      (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, (const TT*)erase,      \
-                     (const TT*)write, (const TT*)gamma, S, (TT*)o)
+                     (const TT*)write, (const TT*)gamma, S, (TT*)o, gmode)
   if (bf16) {
     if (dk == 128) MUIR_STEP_LAUNCH(uint16_t, 128);
     else MUIR_STEP_LAUNCH(uint16_t, 64);

@@ -62,17 +62,31 @@ typedef enum {
   MUIR_ERR_DTYPE = 3,     /* unknown dtype code */
   MUIR_ERR_WORKSPACE = 4, /* workspace pointer NULL or smaller than required */
   MUIR_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned */
-  MUIR_ERR_HIP = 6        /* a kernel launch failed */
+  MUIR_ERR_HIP = 6,       /* a kernel launch failed */
+  MUIR_ERR_MODE = 7       /* unknown readout-gate mode */
 } muir_status_t;
 
 typedef enum { MUIR_F32 = 0, MUIR_BF16 = 1 } muir_dtype_t;
 
+/*
+ * Form of the readout gate gamma (wolonglab summary, §Methodology and
+ * tab:abl: dynamic, static or no readout gate).
+ *   MUIR_GAMMA_TOKEN : per token, [B, T, H, dk] (decode: [N, H, dk]) dtype;
+ *                      its gradient has the same shape and dtype
+ *   MUIR_GAMMA_STATIC: one per (head, key channel), [H, dk] dtype; its
+ *                      gradient is [H, dk] fp32, summed over batch and tokens
+ *   MUIR_GAMMA_NONE  : gamma = 1; the gamma and dgamma pointers are not used
+ *                      and may be NULL
+ */
+typedef enum { MUIR_GAMMA_TOKEN = 0, MUIR_GAMMA_STATIC = 1, MUIR_GAMMA_NONE = 2 } muir_gamma_mode_t;
+
 /* Sizes of a chunkwise call. */
 typedef struct {
-  int32_t B, T, H;   /* batch, tokens, heads */
-  int32_t dk, dv;    /* key / value head size */
-  int32_t chunk;     /* tokens per triangular system */
-  int32_t dtype;     /* muir_dtype_t of q, k, v, gates, o, dO */
+  int32_t B, T, H;     /* batch, tokens, heads */
+  int32_t dk, dv;      /* key / value head size */
+  int32_t chunk;       /* tokens per triangular system */
+  int32_t dtype;       /* muir_dtype_t of q, k, v, gates, o, dO */
+  int32_t gamma_mode;  /* muir_gamma_mode_t */
 } muir_dims_t;
 
 /* Version of this interface (bumped on any signature change). */
@@ -102,8 +116,10 @@ size_t muir_chunk_fwd_workspace(const muir_dims_t* dims);
  * Chunkwise forward over T tokens (Methodology: each chunk is a triangular
  * system with boundary-split cumulative log-decay).
  *
- *   q, k, log_a, erase, gamma : [B, T, H, dk]  dtype
- *   v, write                  : [B, T, H, dv]  dtype
+ *   q, k, log_a, erase : [B, T, H, dk]  dtype
+ *   gamma              : by dims->gamma_mode: [B, T, H, dk] or [H, dk] dtype,
+ *                        or unused (NULL allowed) for MUIR_GAMMA_NONE
+ *   v, write           : [B, T, H, dv]  dtype
  *   S0       : [B, H, dk, dv] fp32 initial state, or NULL for zeros
  *   o        : [B, T, H, dv]  dtype, output
  *   S_T      : [B, H, dk, dv] fp32 final state, or NULL to skip
@@ -144,9 +160,12 @@ size_t muir_chunk_bwd_workspace(const muir_dims_t* dims);
  *              recomputed when either is NULL.
  *   dO       : [B, T, H, dv] dtype upstream gradient of o
  *   dS_T     : [B, H, dk, dv] fp32 upstream gradient of S_T, or NULL for 0
- *   dq, dk, dlog_a, derase, dgamma : [B, T, H, dk] dtype outputs
- *   dv, dwrite                     : [B, T, H, dv] dtype outputs
+ *   dq, dk, dlog_a, derase : [B, T, H, dk] dtype outputs
+ *   dv, dwrite             : [B, T, H, dv] dtype outputs
  *              (accumulated in fp32 and rounded once on the store)
+ *   dgamma   : by dims->gamma_mode: [B, T, H, dk] dtype; [H, dk] fp32 (the
+ *              sum over batch and tokens, in a fixed order); unused (NULL
+ *              allowed) for MUIR_GAMMA_NONE
  *   dS0      : [B, H, dk, dv] fp32 output, or NULL to skip
  *   workspace: device scratch of at least muir_chunk_bwd_workspace(dims)
  *              bytes; contents are clobbered.
@@ -165,14 +184,16 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims,
  * One decode step of the recurrence for N independent streams (abstract:
  * constant-memory inference; the state stays fp32).
  *
- *   q, k, log_a, erase, gamma : [N, H, dk] dtype
- *   v, write                  : [N, H, dv] dtype
+ *   q, k, log_a, erase : [N, H, dk] dtype
+ *   gamma              : by gamma_mode (muir_gamma_mode_t): [N, H, dk] or
+ *                        [H, dk] dtype, or unused (NULL allowed)
+ *   v, write           : [N, H, dv] dtype
  *   S : [N, H, dk, dv] fp32, read and updated in place (S_{t-1} -> S_t)
  *   o : [N, H, dv] dtype, output o_t
  * Supported sizes: dk in {64, 128}, dv a multiple of 64.
  */
 muir_status_t muir_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtype,
-                        const void* q, const void* k, const void* v,
+                        int32_t gamma_mode, const void* q, const void* k, const void* v,
                         const void* log_a, const void* erase,
                         const void* write, const void* gamma,
                         float* S, void* o, void* stream);

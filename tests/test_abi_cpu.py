@@ -10,7 +10,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "muir.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP = range(7)
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP, ERR_MODE = range(8)
 
 
 def _lib():
@@ -42,17 +42,17 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_cover_every_code():
     _, L = _lib()
     seen = set()
-    for code in range(7):
+    for code in range(8):
         s = L.muir_status_string(code).decode()
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 7
+    assert len(seen) == 8
     assert L.muir_status_string(99).decode() == "unknown status"
-    assert L.muir_abi_version() == 3
+    assert L.muir_abi_version() == 4
 
 
-def _dims(m, B=1, T=128, H=2, dk=64, dv=64, chunk=64, dtype=1):
-    return m._Dims(B, T, H, dk, dv, chunk, dtype)
+def _dims(m, B=1, T=128, H=2, dk=64, dv=64, chunk=64, dtype=1, gamma_mode=0):
+    return m._Dims(B, T, H, dk, dv, chunk, dtype, gamma_mode)
 
 
 FAKE = [ctypes.c_void_p(0x10000 + 0x1000 * i) for i in range(16)]  # aligned, never dereferenced
@@ -71,6 +71,8 @@ def _fwd(m, L, d, ptrs=None, ws=FAKE[12], ws_bytes=1 << 40):
     (dict(dk=96, dv=96), ERR_SHAPE),
     (dict(chunk=32), ERR_SHAPE),
     (dict(B=-1), ERR_SHAPE),
+    (dict(gamma_mode=3), ERR_MODE),
+    (dict(gamma_mode=-1), ERR_MODE),
 ])
 def test_fwd_rejects_bad_sizes(kw, code):
     m, L = _lib()
@@ -92,6 +94,13 @@ def test_fwd_rejects_null_misaligned_and_small_workspace():
     assert need > 0
     assert _fwd(m, L, d, ws_bytes=need - 1) == ERR_WORKSPACE
     assert _fwd(m, L, d, ws=None) == ERR_WORKSPACE
+    # the readout gate is required unless the gate is absent
+    p = list(FAKE[:7])
+    p[6] = None
+    assert _fwd(m, L, d, ptrs=p) == ERR_NULL
+    assert _fwd(m, L, _dims(m, gamma_mode=1), ptrs=p) == ERR_NULL
+    dn = _dims(m, gamma_mode=2)
+    assert _fwd(m, L, dn, ptrs=p, ws_bytes=L.muir_chunk_fwd_workspace(ctypes.byref(dn)) - 1) == ERR_WORKSPACE
 
 
 def test_bwd_rejects_bad_arguments():
@@ -110,22 +119,34 @@ def test_bwd_rejects_bad_arguments():
     assert call(d, grads=g) == ERR_NULL
     assert call(d, ws_bytes=need - 1) == ERR_WORKSPACE
     assert call(d, summaries=ctypes.c_void_p(FAKE[8].value + 8)) == ERR_ALIGN
+    # dgamma (the seventh gradient) is required unless the gate is absent
+    g = list(FAKE[:7])
+    g[6] = None
+    assert call(d, grads=g) == ERR_NULL
+    assert call(_dims(m, gamma_mode=1), grads=g) == ERR_NULL
+    dn = _dims(m, gamma_mode=2)
+    assert call(dn, grads=g, ws_bytes=L.muir_chunk_bwd_workspace(ctypes.byref(dn)) - 1) == ERR_WORKSPACE
 
 
 def test_step_rejects_bad_arguments():
     m, L = _lib()
     step = L.muir_step
     args = list(FAKE[:7]) + [FAKE[7], FAKE[8], None]
-    assert step(2, 2, 96, 128, 1, *args) == ERR_SHAPE
-    assert step(2, 2, 128, 100, 1, *args) == ERR_SHAPE
-    assert step(2, 2, 128, 128, 3, *args) == ERR_DTYPE
-    assert step(0, 2, 128, 128, 1, *args) == OK  # nothing to do, nothing launched
+    assert step(2, 2, 96, 128, 1, 0, *args) == ERR_SHAPE
+    assert step(2, 2, 128, 100, 1, 0, *args) == ERR_SHAPE
+    assert step(2, 2, 128, 128, 3, 0, *args) == ERR_DTYPE
+    assert step(2, 2, 128, 128, 1, 5, *args) == ERR_MODE
+    assert step(0, 2, 128, 128, 1, 0, *args) == OK  # nothing to do, nothing launched
     bad = list(args)
     bad[7] = None
-    assert step(2, 2, 128, 128, 1, *bad) == ERR_NULL
+    assert step(2, 2, 128, 128, 1, 0, *bad) == ERR_NULL
     bad = list(args)
     bad[0] = ctypes.c_void_p(0x10004)
-    assert step(2, 2, 128, 128, 1, *bad) == ERR_ALIGN
+    assert step(2, 2, 128, 128, 1, 0, *bad) == ERR_ALIGN
+    bad = list(args)
+    bad[6] = None  # gamma
+    assert step(2, 2, 128, 128, 1, 0, *bad) == ERR_NULL
+    assert step(2, 2, 128, 128, 1, 1, *bad) == ERR_NULL
 
 
 def test_profile_event_registration():

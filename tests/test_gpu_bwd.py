@@ -120,3 +120,74 @@ def test_split_scan_matches_oracle(dtype):
     _say(f"split scan {dtype}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     for n, e in errs.items():
         assert e <= TOL[dtype], (n, e)
+
+
+GATE_CASES = [
+    # name, B, T, H, d, C, dtype, decay, gate form
+    ("bf16_d128_c64_static", 2, 256, 2, 128, 64, "bf16", "channel", "static"),
+    ("bf16_d128_c64_none", 2, 256, 2, 128, 64, "bf16", "channel", "none"),
+    ("bf16_d128_c128_static", 1, 256, 2, 128, 128, "bf16", "channel_slow", "static"),
+    ("f32_d64_c64_static", 1, 128, 2, 64, 64, "f32", "uniform", "static"),
+    ("f32_d64_c64_none", 1, 128, 2, 64, 64, "f32", "steep", "none"),
+]
+
+
+@pytest.mark.parametrize("case", GATE_CASES, ids=[c[0] for c in GATE_CASES])
+def test_readout_gate_forms(case):
+    """Static readout gate ([H, dk], one per head and key channel) and no gate
+    (gamma = 1): forward and backward against the oracle run with the gate
+    expanded to every token; a static gate's gradient is the oracle's
+    per-token gradient summed over batch and tokens (wolonglab summary,
+    tab:abl: dynamic vs static vs no readout)."""
+    name, B, T, H, d, C, dtype, decay, form = case
+    m = _lib()
+    _say(f"gate case={name}")
+    inp = muir_inputs.seq_inputs(B, T, H, d, d, dtype=dtype, decay=decay, seed=13, S0_scale=0.1,
+                                 with_dO=True, with_dST=True)
+    tok = dict(inp)
+    if form == "static":
+        g_dev_src = inp["gamma"][0, 0].clone()  # one token's gate as the static [H, dk] gate
+        tok["gamma"] = g_dev_src[None, None].expand(B, T, H, d).contiguous()
+    else:
+        g_dev_src = None
+        tok["gamma"] = torch.ones_like(inp["gamma"])
+    dv = to_dev(inp)
+    gam = None if g_dev_src is None else g_dev_src.to("cuda")
+    args = [dv["q"], dv["k"], dv["v"], dv["log_a"], dv["erase"], dv["write"], gam]
+    o, S_T, Sc = m.muir_chunk_fwd(*args, dv["S0"], chunk=C, save_states=True)
+    g = m.muir_chunk_bwd(*args, dv["dO"], S0=dv["S0"], S_chunks=Sc, dS_T=dv["dS_T"], chunk=C)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.fwd(*(tok[n] for n in NAMES), S0=tok["S0"])
+    ref = oracle.bwd(*(tok[n] for n in NAMES), tok["dO"], S0=tok["S0"], dS_T=tok["dS_T"])
+    errs = {"o": rel_err(o, o_ref), "S_T": rel_err(S_T, S_ref)}
+    errs.update({n: rel_err(g[n], ref[n]) for n in GRADS if n != "dgamma"})
+    if form == "static":
+        assert tuple(g["dgamma"].shape) == (H, d) and g["dgamma"].dtype == torch.float32
+        errs["dgamma"] = rel_err(g["dgamma"], ref["dgamma"].sum(axis=(0, 1)))
+    else:
+        assert g["dgamma"] is None
+    _say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for n, e in errs.items():
+        assert e <= TOL[dtype], (n, e)
+
+
+@pytest.mark.parametrize("form", ["static", "none"])
+def test_step_readout_gate_forms(form):
+    """Decode steps with a static gate and without a gate, against the oracle's step."""
+    m = _lib()
+    N, H, dk, steps = 3, 2, 128, 5
+    rates = muir_inputs.step_rates(H, dk, seed=3)
+    S_gpu = torch.zeros((N, H, dk, dk), dtype=torch.float32, device="cuda")
+    S_ref = np.zeros((N, H, dk, dk))
+    for s in range(steps):
+        inp = muir_inputs.step_inputs(N, H, dk, dk, s, rates=rates, dtype="bf16", seed=3)
+        d = to_dev(inp)
+        gs = inp["gamma"][0] if form == "static" else None  # [H, dk]
+        o = m.muir_step(d["q"], d["k"], d["v"], d["log_a"], d["erase"], d["write"],
+                        None if gs is None else gs.to("cuda"), S_gpu)
+        tok = dict(inp)
+        tok["gamma"] = gs[None].expand(N, H, dk).contiguous() if gs is not None else torch.ones_like(inp["gamma"])
+        o_ref, S_ref = oracle.step(*(tok[n] for n in NAMES), S_ref)
+        torch.cuda.synchronize()
+        assert rel_err(o, o_ref) <= TOL["bf16"], (s, rel_err(o, o_ref))
+    assert rel_err(S_gpu, S_ref) <= TOL["bf16"]
