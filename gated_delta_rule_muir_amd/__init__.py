@@ -20,7 +20,9 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["muir_chunk_fwd", "muir_chunk_bwd", "muir_step", "muir_chunk_fwd_workspace",
-           "muir_chunk_bwd_workspace", "muir_set_profile_events", "muir_profile_events_recorded",
+           "muir_chunk_bwd_workspace", "muir_chunk_varlen_fwd", "muir_chunk_varlen_bwd",
+           "muir_chunk_varlen_fwd_workspace", "muir_chunk_varlen_bwd_workspace",
+           "muir_set_profile_events", "muir_profile_events_recorded",
            "lib", "library_path", "MuirError", "STATUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -72,6 +74,14 @@ def lib():
         L.muir_chunk_fwd.restype = ctypes.c_int
         L.muir_chunk_bwd.argtypes = [D] + [P] * 7 + [P, P, P, P, P] + [P] * 8 + [P, SZ, P]
         L.muir_chunk_bwd.restype = ctypes.c_int
+        L.muir_chunk_varlen_fwd_workspace.argtypes = [D]
+        L.muir_chunk_varlen_fwd_workspace.restype = SZ
+        L.muir_chunk_varlen_bwd_workspace.argtypes = [D]
+        L.muir_chunk_varlen_bwd_workspace.restype = SZ
+        L.muir_chunk_varlen_fwd.argtypes = [D, P] + [P] * 7 + [P, P, P] + [P, SZ, P]
+        L.muir_chunk_varlen_fwd.restype = ctypes.c_int
+        L.muir_chunk_varlen_bwd.argtypes = [D, P] + [P] * 7 + [P, P, P] + [P] * 8 + [P, SZ, P]
+        L.muir_chunk_varlen_bwd.restype = ctypes.c_int
         L.muir_step.argtypes = [I32] * 6 + [P] * 7 + [P, P, P]
         L.muir_step.restype = ctypes.c_int
         L.muir_set_profile_events.argtypes = [P, I32]
@@ -143,6 +153,10 @@ def muir_chunk_bwd_workspace(B, T, H, dk, dv, chunk, dtype=MUIR_BF16, gamma_mode
     return int(lib().muir_chunk_bwd_workspace(ctypes.byref(d)))
 
 
+def _nchunks(T: int, chunk: int) -> int:
+    return (T + chunk - 1) // chunk if chunk > 0 else 0
+
+
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
     if ws is not None and ws.numel() * ws.element_size() >= nbytes:
         return ws
@@ -156,8 +170,9 @@ def muir_chunk_fwd(q, k, v, log_a, erase, write, gamma, S0=None, *, chunk: int =
     """Chunkwise forward.  Inputs [B, T, H, D] (bf16 or fp32, on one GPU);
     gamma [B, T, H, dk], or [H, dk] (a static gate), or None (no gate).
 
+    Any T: a partial last chunk runs on zero-padded copies in the workspace.
     Returns (o [B,T,H,dv] in the input dtype, S_T [B,H,dk,dv] fp32 or None,
-    S_chunks [B,H,T/chunk,dk,dv] fp32 or None).
+    S_chunks [B,H,ceil(T/chunk),dk,dv] fp32 or None).
     """
     B, T, H, dk = q.shape
     dv = v.shape[3]
@@ -172,7 +187,7 @@ def muir_chunk_fwd(q, k, v, log_a, erase, write, gamma, S0=None, *, chunk: int =
         _check_io("S0", S0, (B, H, dk, dv), torch.float32, dev)
     o = out if out is not None else torch.empty((B, T, H, dv), dtype=dt, device=dev)
     S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if final_state else None
-    S_chunks = (torch.empty((B, H, T // chunk if chunk else 0, dk, dv), dtype=torch.float32, device=dev)
+    S_chunks = (torch.empty((B, H, _nchunks(T, chunk), dk, dv), dtype=torch.float32, device=dev)
                 if save_states else None)
     d = _dims(B, T, H, dk, dv, chunk, code, gm)
     nbytes = int(lib().muir_chunk_fwd_workspace(ctypes.byref(d)))
@@ -213,7 +228,7 @@ def muir_chunk_bwd(q, k, v, log_a, erase, write, gamma, dO, S0=None, S_chunks=No
     if dS_T is not None:
         _check_io("dS_T", dS_T, (B, H, dk, dv), torch.float32, dev)
     if S_chunks is not None:
-        _check_io("S_chunks", S_chunks, (B, H, T // chunk, dk, dv), torch.float32, dev)
+        _check_io("S_chunks", S_chunks, (B, H, _nchunks(T, chunk), dk, dv), torch.float32, dev)
     if summaries is not None:
         need = muir_chunk_fwd_workspace(B, T, H, dk, dv, chunk, code, gm)
         if (not summaries.is_cuda or summaries.device != dev or not summaries.is_contiguous()
@@ -235,6 +250,111 @@ def muir_chunk_bwd(q, k, v, log_a, erase, write, gamma, dO, S0=None, S_chunks=No
                               _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
     if rc != 0:
         raise MuirError(rc, "muir_chunk_bwd")
+    return g
+
+
+def muir_chunk_varlen_fwd_workspace(N, max_len, H, dk, dv, chunk, dtype=MUIR_BF16,
+                                    gamma_mode=MUIR_GAMMA_TOKEN) -> int:
+    d = _dims(N, max_len, H, dk, dv, chunk, dtype, gamma_mode)
+    return int(lib().muir_chunk_varlen_fwd_workspace(ctypes.byref(d)))
+
+
+def muir_chunk_varlen_bwd_workspace(N, max_len, H, dk, dv, chunk, dtype=MUIR_BF16,
+                                    gamma_mode=MUIR_GAMMA_TOKEN) -> int:
+    d = _dims(N, max_len, H, dk, dv, chunk, dtype, gamma_mode)
+    return int(lib().muir_chunk_varlen_bwd_workspace(ctypes.byref(d)))
+
+
+def _check_cu(cu_seqlens, dev, total: int, max_len: Optional[int]) -> Tuple[int, int]:
+    """Validates the [N + 1] int32 offsets of packed sequences; returns
+    (N, max_len).  Reading them back costs one device-to-host copy: callers
+    that know the longest length pass max_len (then only the shape is
+    checked, and max_len must bound every length)."""
+    if not cu_seqlens.is_cuda or cu_seqlens.device != dev:
+        raise ValueError(f"cu_seqlens: must be an int32 tensor on {dev}")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens: expected a 1-D int32 tensor [N + 1]")
+    if not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens: must be contiguous")
+    N = cu_seqlens.numel() - 1
+    if max_len is None:
+        c = cu_seqlens.cpu()
+        lens = c[1:] - c[:-1]
+        if int(c[0]) != 0 or int(c[-1]) != total or (N > 0 and int(lens.min()) < 0):
+            raise ValueError(f"cu_seqlens: must start at 0, not decrease and end at {total}")
+        max_len = int(lens.max()) if N > 0 else 0
+    return N, int(max_len)
+
+
+def muir_chunk_varlen_fwd(q, k, v, log_a, erase, write, gamma, cu_seqlens, S0=None, *, chunk: int = 64,
+                          max_len: Optional[int] = None, final_state: bool = True,
+                          workspace: Optional[torch.Tensor] = None, out=None
+                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Forward of packed variable-length sequences: inputs [T_total, H, D]
+    with sequence n in rows cu_seqlens[n] .. cu_seqlens[n+1]-1 (cu_seqlens an
+    int32 GPU tensor [N + 1]); gamma [T_total, H, dk], [H, dk] or None; S0
+    [N, H, dk, dv] fp32 or None.  Returns (o [T_total, H, dv], S_T [N, H, dk,
+    dv] fp32 or None)."""
+    Tt, H, dk = q.shape
+    dv = v.shape[2]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for n, t in (("q", q), ("k", k), ("log_a", log_a), ("erase", erase)):
+        _check_io(n, t, (Tt, H, dk), dt, dev)
+    gm = _gamma_mode(gamma, (Tt,), H, dk, dt, dev)
+    for n, t in (("v", v), ("write", write)):
+        _check_io(n, t, (Tt, H, dv), dt, dev)
+    N, L = _check_cu(cu_seqlens, dev, Tt, max_len)
+    if S0 is not None:
+        _check_io("S0", S0, (N, H, dk, dv), torch.float32, dev)
+    o = out if out is not None else torch.empty((Tt, H, dv), dtype=dt, device=dev)
+    S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if final_state else None
+    d = _dims(N, L, H, dk, dv, chunk, code, gm)
+    ws = _workspace(int(lib().muir_chunk_varlen_fwd_workspace(ctypes.byref(d))), dev, workspace)
+    rc = lib().muir_chunk_varlen_fwd(ctypes.byref(d), _ptr(cu_seqlens),
+                                     *(_ptr(t) for t in (q, k, v, log_a, erase, write, gamma)),
+                                     _ptr(S0), _ptr(o), _ptr(S_T), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                     _stream(dev))
+    if rc != 0:
+        raise MuirError(rc, "muir_chunk_varlen_fwd")
+    return o, S_T
+
+
+def muir_chunk_varlen_bwd(q, k, v, log_a, erase, write, gamma, dO, cu_seqlens, S0=None, dS_T=None, *,
+                          chunk: int = 64, max_len: Optional[int] = None,
+                          workspace: Optional[torch.Tensor] = None, want_dS0: bool = True):
+    """Backward of muir_chunk_varlen_fwd.  Returns the gradients as
+    muir_chunk_bwd does, per-token ones [T_total, H, D] and dS0 [N, H, dk, dv]."""
+    Tt, H, dk = q.shape
+    dv = v.shape[2]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for n, t in (("q", q), ("k", k), ("log_a", log_a), ("erase", erase)):
+        _check_io(n, t, (Tt, H, dk), dt, dev)
+    gm = _gamma_mode(gamma, (Tt,), H, dk, dt, dev)
+    for n, t in (("v", v), ("write", write), ("dO", dO)):
+        _check_io(n, t, (Tt, H, dv), dt, dev)
+    N, L = _check_cu(cu_seqlens, dev, Tt, max_len)
+    if S0 is not None:
+        _check_io("S0", S0, (N, H, dk, dv), torch.float32, dev)
+    if dS_T is not None:
+        _check_io("dS_T", dS_T, (N, H, dk, dv), torch.float32, dev)
+    gd = dict(dtype=dt, device=dev)
+    g = {n: torch.empty((Tt, H, dk), **gd) for n in ("dq", "dk", "dlog_a", "derase")}
+    g.update({n: torch.empty((Tt, H, dv), **gd) for n in ("dv", "dwrite")})
+    g["dgamma"] = (torch.empty((Tt, H, dk), **gd) if gm == MUIR_GAMMA_TOKEN else
+                   torch.empty((H, dk), dtype=torch.float32, device=dev) if gm == MUIR_GAMMA_STATIC else None)
+    g["dS0"] = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None
+    d = _dims(N, L, H, dk, dv, chunk, code, gm)
+    ws = _workspace(int(lib().muir_chunk_varlen_bwd_workspace(ctypes.byref(d))), dev, workspace)
+    rc = lib().muir_chunk_varlen_bwd(ctypes.byref(d), _ptr(cu_seqlens),
+                                     *(_ptr(t) for t in (q, k, v, log_a, erase, write, gamma)),
+                                     _ptr(S0), _ptr(dO), _ptr(dS_T),
+                                     *(_ptr(g[n]) for n in ("dq", "dk", "dv", "dlog_a", "derase", "dwrite",
+                                                            "dgamma", "dS0")),
+                                     _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
+    if rc != 0:
+        raise MuirError(rc, "muir_chunk_varlen_bwd")
     return g
 
 

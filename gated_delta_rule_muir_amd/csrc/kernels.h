@@ -32,7 +32,9 @@ struct ChunkShape {
   int B, T, H, DK, DV, C;
   bool bf16;
   int gmode;  // GammaMode
-  int NC() const { return T / C; }
+  // chunks per sequence, a partial last one included (the kernels only ever
+  // run on shapes whose T is a multiple of C)
+  int NC() const { return (T + C - 1) / C; }
   size_t nchunks() const { return static_cast<size_t>(B) * H * NC(); }
   size_t tc_bytes() const { return bf16 ? 2 : 4; }
   // Per-chunk block of the forward intermediates ("chunk summary"), see SummaryPart.

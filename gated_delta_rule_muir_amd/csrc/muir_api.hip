@@ -11,6 +11,8 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
 muir_status_t check_dims(const muir_dims_t* d, ChunkShape* s) {
   if (!d) return MUIR_ERR_NULL;
   if (d->dtype != MUIR_F32 && d->dtype != MUIR_BF16) return MUIR_ERR_DTYPE;
@@ -18,9 +20,9 @@ muir_status_t check_dims(const muir_dims_t* d, ChunkShape* s) {
   if (d->B < 0 || d->T < 0 || d->H < 0) return MUIR_ERR_SHAPE;
   if (d->dk != d->dv || (d->dk != 64 && d->dk != 128)) return MUIR_ERR_SHAPE;
   if (d->chunk != 64 && d->chunk != 128 && d->chunk != 256) return MUIR_ERR_SHAPE;
-  if (d->T % d->chunk != 0) return MUIR_ERR_SHAPE;
+  const long long nc = (static_cast<long long>(d->T) + d->chunk - 1) / d->chunk;
   // keep every flat index inside 32-bit chunk counts and 64-bit element counts
-  if (static_cast<long long>(d->B) * d->H * (d->T / d->chunk) > (1LL << 30)) return MUIR_ERR_SHAPE;
+  if (static_cast<long long>(d->B) * d->H * nc > (1LL << 30)) return MUIR_ERR_SHAPE;
   // the kernels address one chunk of a [B, T, H, D] tensor with 32-bit offsets
   if (static_cast<long long>(d->H) * d->dk * d->chunk * 4 >= (1LL << 31)) return MUIR_ERR_SHAPE;
   s->B = d->B;
@@ -34,6 +36,18 @@ muir_status_t check_dims(const muir_dims_t* d, ChunkShape* s) {
   return MUIR_OK;
 }
 
+// The shape the kernels run on: T rounded up to whole chunks.  A call whose
+// T is not a multiple of the chunk (a tail chunk), and every packed
+// variable-length call, runs on zero-padded [N, T_padded, H, D] copies of its
+// sequences: a zero token (k = q = v = 0, log_a = 0) leaves the state as it
+// is, so the padded run's states and every real token's results are those of
+// the unpadded sequence.
+ChunkShape padded(const ChunkShape& s) {
+  ChunkShape p = s;
+  p.T = (s.T + s.C - 1) / s.C * s.C;
+  return p;
+}
+
 // Forward workspace: the chunk summaries, then the split scan's segment
 // transitions and starts (when the shape splits its scan).
 size_t fwd_ws(const ChunkShape& s) { return s.nchunks() * s.summary_bytes() + s.scan_split_bytes(); }
@@ -42,19 +56,29 @@ size_t fwd_ws(const ChunkShape& s) { return s.nchunks() * s.summary_bytes() + s.
 // recomputed chunk states (used when the caller passes no S_chunks), the
 // chunk-end state gradients, per-chunk scratch for the deltas and their
 // gradients, then the split scans' segment area (shared by the recomputed
-// forward scan and the reverse scan, which run one after the other).  Every
-// part is always reserved, so the size does not depend on which pointers are
-// passed.
-size_t bwd_scratch_bytes(const ChunkShape& s) {
-  return (muir::bwd_chunk_scratch_bytes(s) + 255) & ~static_cast<size_t>(255);
-}
-// per-chunk partial sums of a static readout gate's gradient, [nchunks][dk] fp32
-size_t gamma_part_bytes(const ChunkShape& s) {
-  return (s.nchunks() * s.DK * 4 + 255) & ~static_cast<size_t>(255);
-}
+// forward scan and the reverse scan, which run one after the other) and a
+// static readout gate's per-chunk partial gradients.  Every part is always
+// reserved, so the size does not depend on which pointers are passed.
+size_t bwd_scratch_bytes(const ChunkShape& s) { return round256(muir::bwd_chunk_scratch_bytes(s)); }
+size_t gamma_part_bytes(const ChunkShape& s) { return round256(s.nchunks() * s.DK * 4); }
 size_t bwd_ws(const ChunkShape& s) {
   return s.nchunks() * (s.summary_bytes() + 2 * s.state_bytes() + bwd_scratch_bytes(s)) + s.scan_split_bytes() +
          gamma_part_bytes(s);
+}
+
+// Staging area of a padded call, after the kernels' workspace: one
+// [N, T_padded, H, D] copy per staged tensor, in the compute type -- the
+// inputs (the gate only when it is per token) and o, or the inputs, dO and
+// the gradients.
+size_t staged_bytes(const ChunkShape& p, int D) {
+  return round256(static_cast<size_t>(p.B) * p.T * p.H * D * p.tc_bytes());
+}
+int staged_dk_inputs(const ChunkShape& p) { return p.gmode == MUIR_GAMMA_TOKEN ? 5 : 4; }  // q, k, log_a, erase, [gamma]
+size_t fwd_stage_bytes(const ChunkShape& p) {
+  return staged_dk_inputs(p) * staged_bytes(p, p.DK) + 3 * staged_bytes(p, p.DV);  // + v, write, o
+}
+size_t bwd_stage_bytes(const ChunkShape& p) {
+  return 2 * staged_dk_inputs(p) * staged_bytes(p, p.DK) + 5 * staged_bytes(p, p.DV);  // + v, write, dO, dv, dwrite
 }
 
 // The readout gate's pointer is required (and checked) unless the gate is absent.
@@ -91,11 +115,267 @@ hipError_t copy_or_zero(float* dst, const float* src, size_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Sequence tensors between their caller layout and the padded layout, in
+// 16-byte words (WW per token).  Sequence n's tokens are rows
+// cu[n] .. cu[n+1]-1 of a packed [T_total, H, D] tensor when cu is given,
+// else rows n*Tsrc .. n*Tsrc + Tsrc-1 of a [N, Tsrc, H, D] tensor; in the
+// padded [N, Tp, H, D] copy, rows past a sequence's end are zero.  to_padded:
+// caller -> padded (every padded row written); else padded -> caller (the
+// real rows only).
+__global__ void stage_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int N, int Tsrc, int Tp,
+                             int WW, const int32_t* __restrict__ cu, int to_padded) {
+  const size_t total = static_cast<size_t>(N) * Tp * WW;
+  for (size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
+       idx += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const size_t row = idx / WW;
+    const int w = static_cast<int>(idx - row * WW);
+    const int n = static_cast<int>(row / Tp);
+    const int t = static_cast<int>(row - static_cast<size_t>(n) * Tp);
+    const long long start = cu ? cu[n] : static_cast<long long>(n) * Tsrc;
+    const int len = cu ? cu[n + 1] - cu[n] : Tsrc;
+    const size_t crow = static_cast<size_t>(start + t);
+    if (to_padded) {
+      const uint4 z = {0u, 0u, 0u, 0u};
+      dst[idx] = t < len ? src[crow * WW + w] : z;
+    } else if (t < len) {
+      dst[crow * WW + w] = src[idx];
+    }
+  }
+}
+
+hipError_t stage(const void* src, void* dst, const ChunkShape& p, int Tsrc, int D, const int32_t* cu,
+                 bool to_padded, hipStream_t s) {
+  const int WW = static_cast<int>(static_cast<size_t>(p.H) * D * p.tc_bytes() / 16);
+  const size_t total = static_cast<size_t>(p.B) * p.T * WW;
+  if (total == 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>(total / 256 + 1 < 8192 ? total / 256 + 1 : 8192);
+  hipLaunchKernelGGL(stage_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const uint4*>(src),
+                     static_cast<uint4*>(dst), p.B, Tsrc, p.T, WW, cu, to_padded ? 1 : 0);
+  return hipGetLastError();
+}
+
+// Pointers of one call: the seven inputs in the caller's order (q, k, v,
+// log_a, erase, write, gamma) and the seven gradients (dq, dk, dv, dlog_a,
+// derase, dwrite, dgamma); which ones have dk (else dv) channels.
+struct Inputs {
+  const void* x[7];
+};
+struct Grads {
+  void* x[7];
+};
+constexpr bool kIsDk[7] = {true, true, false, true, true, false, true};
+
+// The kernels of the forward on a shape whose T is a multiple of the chunk.
+muir_status_t fwd_core(const ChunkShape& s, const Inputs& in, const float* S0, void* o, float* S_T,
+                       float* S_chunks, void* workspace, hipStream_t hs) {
+  mark(hs);
+  if (muir::launch_fwd_prep(s, in.x[0], in.x[1], in.x[2], in.x[3], in.x[4], in.x[5], in.x[6], workspace, hs) !=
+      hipSuccess)
+    return MUIR_ERR_HIP;
+  mark(hs);
+  // a forward that saves its chunk states keeps the deltas for the direct backward
+  void* deltas = S_chunks && s.bwd_direct() ? workspace : nullptr;
+  float* split = reinterpret_cast<float*>(static_cast<char*>(workspace) + s.nchunks() * s.summary_bytes());
+  if (muir::launch_fwd_scan(s, workspace, S0, o, S_chunks, S_T, deltas, split, hs) != hipSuccess)
+    return MUIR_ERR_HIP;
+  mark(hs);
+  return MUIR_OK;
+}
+
+// The kernels of the backward on a shape whose T is a multiple of the chunk.
+muir_status_t bwd_core(const ChunkShape& s, const Inputs& in, const float* S0, const float* S_chunks,
+                       const void* summaries, const void* dO, const float* dS_T, const Grads& gr, float* dS0,
+                       void* workspace, hipStream_t hs) {
+  char* ws = static_cast<char*>(workspace);
+  float* S_rec = reinterpret_cast<float*>(ws + s.nchunks() * s.summary_bytes());
+  float* dS_chunks = S_rec + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
+  float* scratch = dS_chunks + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
+  float* split = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) + s.nchunks() * bwd_scratch_bytes(s));
+  float* gpart = reinterpret_cast<float*>(reinterpret_cast<char*>(split) + s.scan_split_bytes());
+  const float* Sc = S_chunks;
+  const void* summ = summaries;
+  mark(hs);
+  // The direct backward reads the deltas that the forward scan keeps in the
+  // summaries when it saves the chunk states: both are taken from one forward
+  // call, or both recomputed here.
+  if (s.bwd_direct() && !(summ && Sc)) {
+    summ = nullptr;
+    Sc = nullptr;
+  }
+  if (!summ) {
+    // the forward's chunk summaries are not given: recompute them
+    if (muir::launch_fwd_prep(s, in.x[0], in.x[1], in.x[2], in.x[3], in.x[4], in.x[5], in.x[6], ws, hs) !=
+        hipSuccess)
+      return MUIR_ERR_HIP;
+    mark(hs);
+    summ = ws;
+  }
+  if (!Sc) {
+    // chunk-start states are not given: rerun the forward scan
+    void* deltas = s.bwd_direct() ? ws : nullptr;  // summ is ws here
+    if (muir::launch_fwd_scan(s, summ, S0, nullptr, S_rec, nullptr, deltas, split, hs) != hipSuccess)
+      return MUIR_ERR_HIP;
+    mark(hs);
+    Sc = S_rec;
+  }
+  if (muir::launch_bwd_scan(s, summ, dO, dS_T, dS_chunks, dS0, split, hs) != hipSuccess) return MUIR_ERR_HIP;
+  mark(hs);
+  if (muir::launch_bwd_chunk(s, in.x[0], in.x[1], in.x[2], in.x[3], in.x[4], in.x[5], in.x[6], summ, Sc,
+                             dS_chunks, dO, gr.x[0], gr.x[1], gr.x[2], gr.x[3], gr.x[4], gr.x[5], gr.x[6],
+                             scratch, gpart, hs) != hipSuccess)
+    return MUIR_ERR_HIP;
+  if (s.gmode == MUIR_GAMMA_STATIC &&
+      muir::launch_gamma_sum(s, gpart, static_cast<float*>(gr.x[6]), hs) != hipSuccess)
+    return MUIR_ERR_HIP;
+  mark(hs);
+  return MUIR_OK;
+}
+
+// Carves the staged tensors out of the staging area, in call order.
+struct StageCursor {
+  char* p;
+  void* take(const ChunkShape& ps, int D) {
+    void* r = p;
+    p += staged_bytes(ps, D);
+    return r;
+  }
+};
+
+// Copies the caller's inputs into padded tensors carved from `cur`.
+muir_status_t stage_inputs(const ChunkShape& p, int Tsrc, const int32_t* cu, const Inputs& in, Inputs* out,
+                           StageCursor* cur, hipStream_t hs) {
+  for (int i = 0; i < 7; ++i) {
+    if (i == 6 && p.gmode != MUIR_GAMMA_TOKEN) {
+      out->x[6] = in.x[6];  // a static gate is [H, dk] and needs no staging; an absent one is not read
+      continue;
+    }
+    const int D = kIsDk[i] ? p.DK : p.DV;
+    void* dst = cur->take(p, D);
+    if (stage(in.x[i], dst, p, Tsrc, D, cu, true, hs) != hipSuccess) return MUIR_ERR_HIP;
+    out->x[i] = dst;
+  }
+  return MUIR_OK;
+}
+
+muir_status_t check_fwd_args(const ChunkShape& s, const Inputs& in, const float* S0, const void* o, const float* S_T,
+                             const float* S_chunks, const void* workspace, size_t workspace_bytes, size_t need) {
+  muir_status_t st;
+  if (s.nchunks() != 0) {
+    for (int i = 0; i < 6; ++i)
+      if (!in.x[i]) return MUIR_ERR_NULL;
+    if (!o) return MUIR_ERR_NULL;
+    for (int i = 0; i < 6; ++i)
+      if (!aligned16(in.x[i])) return MUIR_ERR_ALIGN;
+    if (!aligned16(o)) return MUIR_ERR_ALIGN;
+    if ((st = check_gate(s, in.x[6])) != MUIR_OK) return st;
+    if (!workspace || workspace_bytes < need) return MUIR_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MUIR_ERR_ALIGN;
+  }
+  const void* opt[] = {S0, S_T, S_chunks};
+  for (const void* p : opt)
+    if (p && !aligned16(p)) return MUIR_ERR_ALIGN;
+  return MUIR_OK;
+}
+
+muir_status_t check_bwd_args(const ChunkShape& s, const Inputs& in, const float* S0, const float* S_chunks,
+                             const void* summaries, const void* dO, const float* dS_T, const Grads& gr,
+                             const float* dS0, const void* workspace, size_t workspace_bytes, size_t need) {
+  muir_status_t st;
+  if (s.nchunks() != 0) {
+    for (int i = 0; i < 6; ++i)
+      if (!in.x[i] || !gr.x[i]) return MUIR_ERR_NULL;
+    if (!dO) return MUIR_ERR_NULL;
+    for (int i = 0; i < 6; ++i)
+      if (!aligned16(in.x[i]) || !aligned16(gr.x[i])) return MUIR_ERR_ALIGN;
+    if (!aligned16(dO)) return MUIR_ERR_ALIGN;
+    if ((st = check_gate(s, in.x[6])) != MUIR_OK) return st;
+    if ((st = check_gate(s, gr.x[6])) != MUIR_OK) return st;
+    if (!workspace || workspace_bytes < need) return MUIR_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MUIR_ERR_ALIGN;
+  }
+  const void* opt[] = {S0, S_chunks, summaries, dS_T, dS0};
+  for (const void* p : opt)
+    if (p && !aligned16(p)) return MUIR_ERR_ALIGN;
+  return MUIR_OK;
+}
+
+// No tokens (T == 0, or no sequences): the final state is the initial state,
+// the initial state's gradient is the final state's, and a static gate's
+// gradient is a sum over no tokens.
+muir_status_t fwd_empty(const ChunkShape& s, const float* S0, float* S_T, hipStream_t hs) {
+  if (S_T && s.B * s.H > 0) {
+    const size_t n = static_cast<size_t>(s.B) * s.H * s.DK * s.DV;
+    if (copy_or_zero(S_T, S0, n, hs) != hipSuccess) return MUIR_ERR_HIP;
+  }
+  return MUIR_OK;
+}
+muir_status_t bwd_empty(const ChunkShape& s, const float* dS_T, void* dgamma, float* dS0, hipStream_t hs) {
+  if (dS0 && s.B * s.H > 0) {
+    const size_t n = static_cast<size_t>(s.B) * s.H * s.DK * s.DV;
+    if (copy_or_zero(dS0, dS_T, n, hs) != hipSuccess) return MUIR_ERR_HIP;
+  }
+  if (s.gmode == MUIR_GAMMA_STATIC && dgamma && s.H > 0) {
+    if (!aligned16(dgamma)) return MUIR_ERR_ALIGN;
+    if (copy_or_zero(static_cast<float*>(dgamma), nullptr, static_cast<size_t>(s.H) * s.DK, hs) != hipSuccess)
+      return MUIR_ERR_HIP;
+  }
+  return MUIR_OK;
+}
+
+// Forward of batched ([N, T, H, D], cu == NULL) or packed (cu given)
+// sequences through the padded layout.
+muir_status_t fwd_staged(const ChunkShape& s, const int32_t* cu, const Inputs& in, const float* S0, void* o,
+                         float* S_T, float* S_chunks, void* workspace, hipStream_t hs) {
+  const ChunkShape p = padded(s);
+  StageCursor cur{static_cast<char*>(workspace) + fwd_ws(p)};
+  Inputs sin;
+  muir_status_t st = stage_inputs(p, s.T, cu, in, &sin, &cur, hs);
+  if (st != MUIR_OK) return st;
+  void* po = cur.take(p, p.DV);
+  if ((st = fwd_core(p, sin, S0, po, S_T, S_chunks, workspace, hs)) != MUIR_OK) return st;
+  return stage(po, o, p, s.T, p.DV, cu, false, hs) == hipSuccess ? MUIR_OK : MUIR_ERR_HIP;
+}
+
+muir_status_t bwd_staged(const ChunkShape& s, const int32_t* cu, const Inputs& in, const float* S0,
+                         const float* S_chunks, const void* summaries, const void* dO, const float* dS_T,
+                         const Grads& gr, float* dS0, void* workspace, hipStream_t hs) {
+  const ChunkShape p = padded(s);
+  StageCursor cur{static_cast<char*>(workspace) + bwd_ws(p)};
+  Inputs sin;
+  muir_status_t st = stage_inputs(p, s.T, cu, in, &sin, &cur, hs);
+  if (st != MUIR_OK) return st;
+  void* pdO = cur.take(p, p.DV);
+  if (stage(dO, pdO, p, s.T, p.DV, cu, true, hs) != hipSuccess) return MUIR_ERR_HIP;
+  Grads sg;
+  for (int i = 0; i < 7; ++i) {
+    if (i == 6 && p.gmode != MUIR_GAMMA_TOKEN) {
+      sg.x[6] = gr.x[6];  // a static gate's gradient is [H, dk] fp32; an absent gate has none
+      continue;
+    }
+    sg.x[i] = cur.take(p, kIsDk[i] ? p.DK : p.DV);
+  }
+  if ((st = bwd_core(p, sin, S0, S_chunks, summaries, pdO, dS_T, sg, dS0, workspace, hs)) != MUIR_OK) return st;
+  for (int i = 0; i < 7; ++i) {
+    if (i == 6 && p.gmode != MUIR_GAMMA_TOKEN) continue;
+    if (stage(sg.x[i], gr.x[i], p, s.T, kIsDk[i] ? p.DK : p.DV, cu, false, hs) != hipSuccess) return MUIR_ERR_HIP;
+  }
+  return MUIR_OK;
+}
+
+size_t fwd_need(const ChunkShape& s) {
+  return s.T % s.C == 0 ? fwd_ws(s) : fwd_ws(padded(s)) + fwd_stage_bytes(padded(s));
+}
+size_t bwd_need(const ChunkShape& s) {
+  return s.T % s.C == 0 ? bwd_ws(s) : bwd_ws(padded(s)) + bwd_stage_bytes(padded(s));
+}
+size_t varlen_fwd_need(const ChunkShape& s) { return fwd_ws(padded(s)) + fwd_stage_bytes(padded(s)); }
+size_t varlen_bwd_need(const ChunkShape& s) { return bwd_ws(padded(s)) + bwd_stage_bytes(padded(s)); }
+
 }  // namespace
 
 extern "C" {
 
-int32_t muir_abi_version(void) { return 4; }
+int32_t muir_abi_version(void) { return 5; }
 
 int32_t muir_set_profile_events(void** events, int32_t count) {
   if (count < 0 || (count > 0 && !events)) return MUIR_ERR_NULL;
@@ -124,13 +404,13 @@ const char* muir_status_string(muir_status_t st) {
 size_t muir_chunk_fwd_workspace(const muir_dims_t* dims) {
   ChunkShape s;
   if (check_dims(dims, &s) != MUIR_OK) return 0;
-  return fwd_ws(s);
+  return fwd_need(s);
 }
 
 size_t muir_chunk_bwd_workspace(const muir_dims_t* dims) {
   ChunkShape s;
   if (check_dims(dims, &s) != MUIR_OK) return 0;
-  return bwd_ws(s);
+  return bwd_need(s);
 }
 
 muir_status_t muir_chunk_fwd(const muir_dims_t* dims, const void* q, const void* k,
@@ -141,40 +421,13 @@ muir_status_t muir_chunk_fwd(const muir_dims_t* dims, const void* q, const void*
   ChunkShape s;
   muir_status_t st = check_dims(dims, &s);
   if (st != MUIR_OK) return st;
-  const bool empty = s.nchunks() == 0;
-  if (!empty) {
-    const void* req[] = {q, k, v, log_a, erase, write, o};
-    for (const void* p : req)
-      if (!p) return MUIR_ERR_NULL;
-    for (const void* p : req)
-      if (!aligned16(p)) return MUIR_ERR_ALIGN;
-    if ((st = check_gate(s, gamma)) != MUIR_OK) return st;
-    if (!workspace || workspace_bytes < fwd_ws(s)) return MUIR_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return MUIR_ERR_ALIGN;
-  }
-  const void* opt[] = {S0, S_T, S_chunks};
-  for (const void* p : opt)
-    if (p && !aligned16(p)) return MUIR_ERR_ALIGN;
+  const Inputs in{{q, k, v, log_a, erase, write, gamma}};
+  if ((st = check_fwd_args(s, in, S0, o, S_T, S_chunks, workspace, workspace_bytes, fwd_need(s))) != MUIR_OK)
+    return st;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  if (empty) {
-    // T == 0: the final state is the initial state
-    if (S_T && s.B * s.H > 0) {
-      const size_t n = static_cast<size_t>(s.B) * s.H * s.DK * s.DV;
-      if (copy_or_zero(S_T, S0, n, hs) != hipSuccess) return MUIR_ERR_HIP;
-    }
-    return MUIR_OK;
-  }
-  mark(hs);
-  if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, workspace, hs) != hipSuccess)
-    return MUIR_ERR_HIP;
-  mark(hs);
-  // a forward that saves its chunk states keeps the deltas for the direct backward
-  void* deltas = S_chunks && s.bwd_direct() ? workspace : nullptr;
-  float* split = reinterpret_cast<float*>(static_cast<char*>(workspace) + s.nchunks() * s.summary_bytes());
-  if (muir::launch_fwd_scan(s, workspace, S0, o, S_chunks, S_T, deltas, split, hs) != hipSuccess)
-    return MUIR_ERR_HIP;
-  mark(hs);
-  return MUIR_OK;
+  if (s.nchunks() == 0) return fwd_empty(s, S0, S_T, hs);
+  if (s.T % s.C == 0) return fwd_core(s, in, S0, o, S_T, S_chunks, workspace, hs);
+  return fwd_staged(s, nullptr, in, S0, o, S_T, S_chunks, workspace, hs);
 }
 
 muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void* k,
@@ -187,77 +440,64 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void*
   ChunkShape s;
   muir_status_t st = check_dims(dims, &s);
   if (st != MUIR_OK) return st;
-  const bool empty = s.nchunks() == 0;
-  if (!empty) {
-    const void* req[] = {q, k, v, log_a, erase, write, dO, dq, dk, dv, dlog_a, derase, dwrite};
-    for (const void* p : req)
-      if (!p) return MUIR_ERR_NULL;
-    for (const void* p : req)
-      if (!aligned16(p)) return MUIR_ERR_ALIGN;
-    if ((st = check_gate(s, gamma)) != MUIR_OK) return st;
-    if ((st = check_gate(s, dgamma)) != MUIR_OK) return st;
-    if (!workspace || workspace_bytes < bwd_ws(s)) return MUIR_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return MUIR_ERR_ALIGN;
-  }
-  const void* opt[] = {S0, S_chunks, summaries, dS_T, dS0};
-  for (const void* p : opt)
-    if (p && !aligned16(p)) return MUIR_ERR_ALIGN;
+  const Inputs in{{q, k, v, log_a, erase, write, gamma}};
+  const Grads gr{{dq, dk, dv, dlog_a, derase, dwrite, dgamma}};
+  if ((st = check_bwd_args(s, in, S0, S_chunks, summaries, dO, dS_T, gr, dS0, workspace, workspace_bytes,
+                           bwd_need(s))) != MUIR_OK)
+    return st;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  if (empty) {
-    if (dS0 && s.B * s.H > 0) {
-      const size_t n = static_cast<size_t>(s.B) * s.H * s.DK * s.DV;
-      if (copy_or_zero(dS0, dS_T, n, hs) != hipSuccess) return MUIR_ERR_HIP;
-    }
-    // a static gate's gradient is a sum over no tokens
-    if (s.gmode == MUIR_GAMMA_STATIC && dgamma && s.H > 0) {
-      if ((st = check_gate(s, dgamma)) != MUIR_OK) return st;
-      if (copy_or_zero(static_cast<float*>(dgamma), nullptr, static_cast<size_t>(s.H) * s.DK, hs) != hipSuccess)
-        return MUIR_ERR_HIP;
-    }
-    return MUIR_OK;
-  }
-  char* ws = static_cast<char*>(workspace);
-  float* S_rec = reinterpret_cast<float*>(ws + s.nchunks() * s.summary_bytes());
-  float* dS_chunks = S_rec + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
-  float* scratch = dS_chunks + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
-  float* split = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) + s.nchunks() * bwd_scratch_bytes(s));
-  float* gpart = reinterpret_cast<float*>(reinterpret_cast<char*>(split) + s.scan_split_bytes());
-  const float* Sc = S_chunks;
-  const void* summ = summaries;
-  mark(hs);
-  // The direct backward reads the deltas that the forward scan keeps in the
-  // summaries when it saves the chunk states: both are taken from one forward
-  // call, or both recomputed here.
-  if (s.bwd_direct() && !(summ && Sc)) {
-    summ = nullptr;
-    Sc = nullptr;
-  }
-  if (!summ) {
-    // the forward's chunk summaries are not given: recompute them
-    if (muir::launch_fwd_prep(s, q, k, v, log_a, erase, write, gamma, ws, hs) != hipSuccess)
-      return MUIR_ERR_HIP;
-    mark(hs);
-    summ = ws;
-  }
-  if (!Sc) {
-    // chunk-start states are not given: rerun the forward scan
-    void* deltas = s.bwd_direct() ? ws : nullptr;  // summ is ws here
-    if (muir::launch_fwd_scan(s, summ, S0, nullptr, S_rec, nullptr, deltas, split, hs) != hipSuccess)
-      return MUIR_ERR_HIP;
-    mark(hs);
-    Sc = S_rec;
-  }
-  if (muir::launch_bwd_scan(s, summ, dO, dS_T, dS_chunks, dS0, split, hs) != hipSuccess)
-    return MUIR_ERR_HIP;
-  mark(hs);
-  if (muir::launch_bwd_chunk(s, q, k, v, log_a, erase, write, gamma, summ, Sc, dS_chunks, dO, dq,
-                             dk, dv, dlog_a, derase, dwrite, dgamma, scratch, gpart, hs) != hipSuccess)
-    return MUIR_ERR_HIP;
-  if (s.gmode == MUIR_GAMMA_STATIC &&
-      muir::launch_gamma_sum(s, gpart, static_cast<float*>(dgamma), hs) != hipSuccess)
-    return MUIR_ERR_HIP;
-  mark(hs);
-  return MUIR_OK;
+  if (s.nchunks() == 0) return bwd_empty(s, dS_T, dgamma, dS0, hs);
+  if (s.T % s.C == 0) return bwd_core(s, in, S0, S_chunks, summaries, dO, dS_T, gr, dS0, workspace, hs);
+  return bwd_staged(s, nullptr, in, S0, S_chunks, summaries, dO, dS_T, gr, dS0, workspace, hs);
+}
+
+size_t muir_chunk_varlen_fwd_workspace(const muir_dims_t* dims) {
+  ChunkShape s;
+  if (check_dims(dims, &s) != MUIR_OK) return 0;
+  return varlen_fwd_need(s);
+}
+
+size_t muir_chunk_varlen_bwd_workspace(const muir_dims_t* dims) {
+  ChunkShape s;
+  if (check_dims(dims, &s) != MUIR_OK) return 0;
+  return varlen_bwd_need(s);
+}
+
+muir_status_t muir_chunk_varlen_fwd(const muir_dims_t* dims, const int32_t* cu_seqlens, const void* q,
+                                    const void* k, const void* v, const void* log_a, const void* erase,
+                                    const void* write, const void* gamma, const float* S0, void* o,
+                                    float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
+  ChunkShape s;
+  muir_status_t st = check_dims(dims, &s);
+  if (st != MUIR_OK) return st;
+  const Inputs in{{q, k, v, log_a, erase, write, gamma}};
+  if ((st = check_fwd_args(s, in, S0, o, S_T, nullptr, workspace, workspace_bytes, varlen_fwd_need(s))) !=
+      MUIR_OK)
+    return st;
+  if (s.nchunks() != 0 && !cu_seqlens) return MUIR_ERR_NULL;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (s.nchunks() == 0) return fwd_empty(s, S0, S_T, hs);
+  return fwd_staged(s, cu_seqlens, in, S0, o, S_T, nullptr, workspace, hs);
+}
+
+muir_status_t muir_chunk_varlen_bwd(const muir_dims_t* dims, const int32_t* cu_seqlens, const void* q,
+                                    const void* k, const void* v, const void* log_a, const void* erase,
+                                    const void* write, const void* gamma, const float* S0, const void* dO,
+                                    const float* dS_T, void* dq, void* dk, void* dv, void* dlog_a, void* derase,
+                                    void* dwrite, void* dgamma, float* dS0, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  ChunkShape s;
+  muir_status_t st = check_dims(dims, &s);
+  if (st != MUIR_OK) return st;
+  const Inputs in{{q, k, v, log_a, erase, write, gamma}};
+  const Grads gr{{dq, dk, dv, dlog_a, derase, dwrite, dgamma}};
+  if ((st = check_bwd_args(s, in, S0, nullptr, nullptr, dO, dS_T, gr, dS0, workspace, workspace_bytes,
+                           varlen_bwd_need(s))) != MUIR_OK)
+    return st;
+  if (s.nchunks() != 0 && !cu_seqlens) return MUIR_ERR_NULL;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (s.nchunks() == 0) return bwd_empty(s, dS_T, dgamma, dS0, hs);
+  return bwd_staged(s, cu_seqlens, in, S0, nullptr, nullptr, dO, dS_T, gr, dS0, workspace, hs);
 }
 
 muir_status_t muir_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtype,

@@ -43,7 +43,11 @@
  *  - log_a must be finite and <= 0.  "No decay" is log_a = 0; "full decay"
  *    is a large negative value (e.g. -1e4), for which exp() is 0.
  *  - Supported sizes: dk == dv, dk in {64, 128}; chunk in {64, 128, 256};
- *    T % chunk == 0.  Sizes B, T, H may be 0 (nothing is launched).
+ *    any T >= 0.  A T that is not a multiple of chunk ends in a partial
+ *    chunk: the call then runs on zero-padded copies of the sequences in its
+ *    workspace (a zero token leaves the state unchanged) and needs a larger
+ *    workspace.  Sizes B, T, H may be 0 (no sequence work is launched).
+ *  - nc = ceil(T / chunk) is the number of chunks of a sequence.
  */
 #ifndef MUIR_H_
 #define MUIR_H_
@@ -123,7 +127,7 @@ size_t muir_chunk_fwd_workspace(const muir_dims_t* dims);
  *   S0       : [B, H, dk, dv] fp32 initial state, or NULL for zeros
  *   o        : [B, T, H, dv]  dtype, output
  *   S_T      : [B, H, dk, dv] fp32 final state, or NULL to skip
- *   S_chunks : [B, H, T/chunk, dk, dv] fp32 state at the START of every
+ *   S_chunks : [B, H, nc, dk, dv] fp32 state at the START of every
  *              chunk (kept for muir_chunk_bwd), or NULL to skip
  *   workspace: device scratch of at least muir_chunk_fwd_workspace(dims)
  *              bytes.  On return it holds the chunk summaries (the
@@ -148,7 +152,7 @@ size_t muir_chunk_bwd_workspace(const muir_dims_t* dims);
  * custom backward pass is used; this is the adjoint of the recurrence above).
  *
  *   inputs as in muir_chunk_fwd, plus
- *   S_chunks : [B, H, T/chunk, dk, dv] fp32 from muir_chunk_fwd, or NULL
+ *   S_chunks : [B, H, nc, dk, dv] fp32 from muir_chunk_fwd, or NULL
  *              (then recomputed inside, in the workspace)
  *   summaries: the workspace of a muir_chunk_fwd call on the same inputs,
  *              dims and S0, unchanged since (the chunk summaries it left
@@ -179,6 +183,55 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims,
                              void* dq, void* dk, void* dv, void* dlog_a,
                              void* derase, void* dwrite, void* dgamma, float* dS0,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Packed variable-length sequences (the pages train on documents of mixed
+ * length; packing them end to end without padding is the usual layout).
+ * Sequence n is rows cu_seqlens[n] .. cu_seqlens[n+1]-1 of every sequence
+ * tensor, which is [T_total, H, D] with T_total = cu_seqlens[B]; each
+ * sequence starts from its own state and none sees another's tokens.
+ *
+ *   dims       : B = number of sequences, T = an upper bound on every
+ *                sequence's length (the longest one); the other fields as
+ *                for muir_chunk_fwd.  The workspace size depends on B * T.
+ *   cu_seqlens : [B + 1] int32 DEVICE array, cu_seqlens[0] = 0 and
+ *                non-decreasing.  Precondition (not checked, as the array is
+ *                on the device): every length is <= dims->T; tokens of a
+ *                longer sequence past dims->T are neither read nor written.
+ *   q, k, log_a, erase, (per-token) gamma : [T_total, H, dk] dtype
+ *   v, write, o                           : [T_total, H, dv] dtype
+ *   S0, S_T    : [B, H, dk, dv] fp32 per sequence, as in muir_chunk_fwd
+ * The call copies the sequences into zero-padded [B, T_pad, H, D] tensors in
+ * its workspace (T_pad = T rounded up to the chunk), runs the chunkwise
+ * kernels there, and copies the real tokens' results back.  Chunk states and
+ * summaries are not exported: the backward recomputes them.
+ */
+size_t muir_chunk_varlen_fwd_workspace(const muir_dims_t* dims);
+
+muir_status_t muir_chunk_varlen_fwd(const muir_dims_t* dims, const int32_t* cu_seqlens,
+                                    const void* q, const void* k, const void* v,
+                                    const void* log_a, const void* erase,
+                                    const void* write, const void* gamma,
+                                    const float* S0, void* o, float* S_T,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of muir_chunk_varlen_fwd: as muir_chunk_bwd, with the packed
+ * layout and cu_seqlens of muir_chunk_varlen_fwd for every sequence tensor
+ * (dO and the per-token gradients are [T_total, H, D]).  dS_T and dS0 are
+ * [B, H, dk, dv] per sequence; a static gate's gradient is [H, dk] fp32,
+ * summed over every sequence's tokens.
+ */
+size_t muir_chunk_varlen_bwd_workspace(const muir_dims_t* dims);
+
+muir_status_t muir_chunk_varlen_bwd(const muir_dims_t* dims, const int32_t* cu_seqlens,
+                                    const void* q, const void* k, const void* v,
+                                    const void* log_a, const void* erase,
+                                    const void* write, const void* gamma,
+                                    const float* S0, const void* dO, const float* dS_T,
+                                    void* dq, void* dk, void* dv, void* dlog_a,
+                                    void* derase, void* dwrite, void* dgamma, float* dS0,
+                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One decode step of the recurrence for N independent streams (abstract:

@@ -109,6 +109,39 @@ def seq_inputs(B: int, T: int, H: int, dk: int, dv: int, *, dtype: str = "bf16",
     return out
 
 
+def varlen_lengths(N: int, max_len: int, chunk: int, seed: int = 0) -> np.ndarray:
+    """Lengths of N packed documents, int64: a mix of an empty one, a single
+    token, exact chunk multiples, one chunk plus one token and uniform draws
+    in [1, max_len] (documents of mixed length, packed end to end)."""
+    rng = np.random.Generator(np.random.PCG64([seed, 1 << 21]))
+    fixed = [0, 1, chunk, chunk + 1, max_len]
+    lens = list(rng.integers(1, max_len + 1, size=N))
+    for i, n in enumerate(fixed[:N]):
+        lens[i] = min(n, max_len)
+    rng.shuffle(lens)
+    return np.asarray(lens, dtype=np.int64)
+
+
+def varlen_inputs(lens, H: int, dk: int, dv: int, *, dtype: str = "bf16", decay: str = "uniform",
+                  seed: int = 0, S0_scale: float = 0.0, with_dST: bool = False) -> Dict[str, torch.Tensor]:
+    """Inputs of one packed variable-length call: the seq_inputs recipe over
+    T_total = sum(lens) tokens in [T_total, H, D] layout (dO included), plus
+    cu_seqlens (int32 [N + 1]) and per-sequence S0 / dS_T ([N, H, dk, dv]
+    fp32 or None)."""
+    lens = np.asarray(lens, dtype=np.int64)
+    N, total = len(lens), int(lens.sum())
+    flat = seq_inputs(1, total, H, dk, dv, dtype=dtype, decay=decay, seed=seed, with_dO=True)
+    out = {n: t[0] for n, t in flat.items() if t is not None}
+    cu = np.zeros(N + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    out["cu_seqlens"] = torch.from_numpy(cu)
+    rng = np.random.Generator(np.random.PCG64([seed, 1 << 22]))
+    f32 = np.float32
+    out["S0"] = torch.from_numpy(S0_scale * rng.standard_normal((N, H, dk, dv), dtype=f32)) if S0_scale else None
+    out["dS_T"] = torch.from_numpy(rng.standard_normal((N, H, dk, dv), dtype=f32)) if with_dST else None
+    return out
+
+
 def step_rates(H: int, dk: int, seed: int = 0, mode: str = "channel") -> np.ndarray:
     """Per-(head, channel) decay rates for a decode stream, fixed over steps, [H, dk] fp32."""
     rng = np.random.Generator(np.random.PCG64([seed, 1 << 20]))

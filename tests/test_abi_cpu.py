@@ -29,7 +29,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("muir_chunk_fwd", "muir_chunk_bwd", "muir_step", "muir_chunk_fwd_workspace",
-              "muir_chunk_bwd_workspace", "muir_status_string", "muir_abi_version"):
+              "muir_chunk_bwd_workspace", "muir_chunk_varlen_fwd", "muir_chunk_varlen_bwd",
+              "muir_chunk_varlen_fwd_workspace", "muir_chunk_varlen_bwd_workspace",
+              "muir_status_string", "muir_abi_version"):
         assert n in names
 
 
@@ -48,7 +50,7 @@ def test_status_strings_cover_every_code():
         seen.add(s)
     assert len(seen) == 8
     assert L.muir_status_string(99).decode() == "unknown status"
-    assert L.muir_abi_version() == 4
+    assert L.muir_abi_version() == 5
 
 
 def _dims(m, B=1, T=128, H=2, dk=64, dv=64, chunk=64, dtype=1, gamma_mode=0):
@@ -66,7 +68,6 @@ def _fwd(m, L, d, ptrs=None, ws=FAKE[12], ws_bytes=1 << 40):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=5), ERR_DTYPE),
-    (dict(T=100), ERR_SHAPE),          # T % chunk != 0
     (dict(dk=64, dv=128), ERR_SHAPE),  # dk != dv
     (dict(dk=96, dv=96), ERR_SHAPE),
     (dict(chunk=32), ERR_SHAPE),
@@ -162,6 +163,56 @@ def test_workspace_sizes_scale_with_work():
     b = L.muir_chunk_fwd_workspace(ctypes.byref(_dims(m, B=2, T=256)))
     assert b == 2 * a and a % 256 == 0
     assert L.muir_chunk_fwd_workspace(ctypes.byref(_dims(m, T=0))) == 0 or True
+
+
+def test_partial_chunk_needs_a_staging_area():
+    """A T that ends inside a chunk is accepted; its workspace holds the
+    padded shape's workspace plus zero-padded copies of the sequences."""
+    m, L = _lib()
+    for fn in (L.muir_chunk_fwd_workspace, L.muir_chunk_bwd_workspace):
+        whole = fn(ctypes.byref(_dims(m, T=128)))
+        tail = fn(ctypes.byref(_dims(m, T=100)))
+        assert whole > 0 and tail > whole
+    d = _dims(m, T=100)
+    need = L.muir_chunk_fwd_workspace(ctypes.byref(d))
+    assert _fwd(m, L, d, ws_bytes=need - 1) == ERR_WORKSPACE
+    # the packed entry points size for dims.T as the longest sequence, padded
+    for fv, fd in ((L.muir_chunk_varlen_fwd_workspace, L.muir_chunk_fwd_workspace),
+                   (L.muir_chunk_varlen_bwd_workspace, L.muir_chunk_bwd_workspace)):
+        assert fv(ctypes.byref(_dims(m, B=3, T=100))) == fd(ctypes.byref(_dims(m, B=3, T=100)))
+        assert fv(ctypes.byref(_dims(m, B=3, T=128))) > fd(ctypes.byref(_dims(m, B=3, T=128)))
+        assert fv(ctypes.byref(_dims(m, chunk=48))) == 0
+
+
+def test_varlen_rejects_bad_arguments():
+    m, L = _lib()
+    d = _dims(m, B=3, T=100)
+    fneed = L.muir_chunk_varlen_fwd_workspace(ctypes.byref(d))
+    bneed = L.muir_chunk_varlen_bwd_workspace(ctypes.byref(d))
+
+    def fwd(dd, cu=FAKE[13], ptrs=None, ws_bytes=1 << 40):
+        p = list(FAKE[:7]) if ptrs is None else ptrs
+        return L.muir_chunk_varlen_fwd(ctypes.byref(dd) if dd is not None else None, cu, *p, None, FAKE[7],
+                                       None, FAKE[12], ctypes.c_size_t(ws_bytes), None)
+
+    def bwd(dd, cu=FAKE[13], grads=None, ws_bytes=1 << 40):
+        g = list(FAKE[:7]) if grads is None else grads
+        return L.muir_chunk_varlen_bwd(ctypes.byref(dd), cu, *FAKE[:7], None, FAKE[8], None, *g, None,
+                                       FAKE[12], ctypes.c_size_t(ws_bytes), None)
+    assert fwd(None) == ERR_NULL
+    assert fwd(d, cu=None) == ERR_NULL
+    assert bwd(d, cu=None) == ERR_NULL
+    assert fwd(_dims(m, B=3, T=100, dtype=7)) == ERR_DTYPE
+    assert fwd(_dims(m, B=3, T=100, gamma_mode=4)) == ERR_MODE
+    assert bwd(_dims(m, B=3, T=100, chunk=32)) == ERR_SHAPE
+    assert fwd(d, ws_bytes=fneed - 1) == ERR_WORKSPACE
+    assert bwd(d, ws_bytes=bneed - 1) == ERR_WORKSPACE
+    p = list(FAKE[:7])
+    p[4] = ctypes.c_void_p(0x10004)
+    assert fwd(d, ptrs=p) == ERR_ALIGN
+    g = list(FAKE[:7])
+    g[0] = None
+    assert bwd(d, grads=g) == ERR_NULL
 
 
 def test_binding_refuses_cpu_tensors():

@@ -30,14 +30,6 @@ def test_empty_sequence_passes_state_through():
     assert torch.count_nonzero(S_T2) == 0
 
 
-def test_ragged_length_is_rejected():
-    m = _lib()
-    q = torch.zeros((1, 100, 1, 64), dtype=torch.float32, device="cuda")
-    with pytest.raises(m.MuirError) as e:
-        m.muir_chunk_fwd(q, q, q, q, q, q, q, chunk=64)
-    assert e.value.code == 2
-
-
 @pytest.mark.parametrize("case", ["no_decay", "full_erase_recall", "zero_gamma", "zero_inputs"])
 def test_degenerate_cases(case):
     m = _lib()
