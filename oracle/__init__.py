@@ -16,6 +16,10 @@ Methodology section of the wolonglab summary page (row-wise decay, erase of
 the key's prediction, gated write, readout gate on the normalised query).
 The exact placement of each gate is a reading of that prose; it is written
 out in ``muir_oracle.c`` and pinned by ``tests/test_oracle_pins.py``.
+
+``oracle.gate_proj`` is the fp64 numpy oracle of the gate prologue (the fused
+low-rank gate projection and the q / k SiLU + L2 normalisation), pinned by
+``tests/test_oracle_gate_pins.py``.
 """
 from __future__ import annotations
 
