@@ -15,8 +15,9 @@ Beside it the line carries:
                 sample of the same workload (4 batch rows: 64 heads x 4096)
   secondary     long-context fwd+bwd (T=32768, chunk 128 and 256), one
                 1M-token stream (chunked prefill chained through the state,
-                then decode), and the streaming decode step (64 streams x 16
-                heads, 4096 steps)
+                then decode), the gate prologue at the layer's shape (fused
+                low-rank gate projection and q / k SiLU + L2, fwd + bwd), and
+                the streaming decode step (64 streams x 16 heads, 4096 steps)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -281,6 +282,77 @@ def stream_bench(m, torch, hiprt, T=1 << 20, H=16, d=128, seg=32768, chunk=64, s
             "prefill_tokens_per_s": T / (t1 - t0), "decode_us_per_token": (t2 - t1) * 1e6 / steps}
 
 
+def gate_bench(m, torch, hiprt, M=32768, d=2048, H=16, dk=128, dv=128, steps=10, warmup=2, seed=0):
+    """The gate prologue at the layer's shape (M = B*T tokens of width d):
+    fused gate projection forward + backward and the q / k SiLU + L2
+    normalisation forward + backward.  bf16, random weights, inputs drawn on
+    the GPU with the muir_inputs.gate_inputs recipe."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    bf = torch.bfloat16
+    sw, su, sb = m.gate_param_shapes(d, H, dk, dv)
+    x = torch.randn((M, d), generator=g, device="cuda").to(bf)
+    W_down = (torch.randn(sw, generator=g, device="cuda") / d ** 0.5).to(bf)
+    W_up = (torch.randn(su, generator=g, device="cuda") * (0.5 / 128 ** 0.5)).to(bf)
+    bias = torch.randn(sb, generator=g, device="cuda").to(bf)
+    dG = {n: torch.randn((M, H, D), generator=g, device="cuda").to(bf)
+          for n, D in zip(m.GATE_NAMES, (dk, dk, dv, dv, dk))}
+    qk = torch.randn((2, M, H, dk), generator=g, device="cuda").to(bf)
+    dqk = torch.randn((2, M, H, dk), generator=g, device="cuda").to(bf)
+    ws = torch.empty(m.muir_gate_proj_bwd_workspace(M, d, H, dk, dv), dtype=torch.uint8, device="cuda")
+
+    def step():
+        out = m.muir_gate_proj_fwd(x, W_down, W_up, bias, H=H, dk=dk, dv=dv)
+        gr = m.muir_gate_proj_bwd(x, W_down, W_up, bias, dG, H=H, dk=dk, dv=dv, z=out["z"], workspace=ws)
+        y = m.muir_qk_norm_fwd(qk)
+        du = m.muir_qk_norm_bwd(qk, dqk)
+        return out, gr, y, du
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    per = 8  # events: before/after each of the four calls
+    pool = hiprt.EventPool(per * steps)
+    m.muir_set_profile_events(pool.arr, pool.n)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rec = m.muir_profile_events_recorded()
+    m.muir_set_profile_events(None)
+    if rec != per * steps:
+        raise RuntimeError(f"expected {per * steps} profile events, got {rec}")
+    us = {k: 0.0 for k in ("proj_fwd", "proj_bwd", "qk_norm_fwd", "qk_norm_bwd")}
+    for s_ in range(steps):
+        for i, k in enumerate(us):
+            us[k] += pool.elapsed_ms(s_ * per + 2 * i, s_ * per + 2 * i + 1) * 1e3 / steps
+    pool.close()
+    e = 2
+    rw = 64 * H * dk * 2 + 128 * (H * dv * 2 + H * dk)  # sum over the gates of rank x width
+    fwd_flops = 2 * M * d * 512 + 2 * M * rw
+    bwd_flops = 3 * 2 * M * rw + 2 * 2 * M * d * 512  # pre, dz, dW_up; dx, dW_down
+    gw = M * H * (3 * dk + 2 * dv) * e
+    fwd_bytes = M * d * e + M * 512 * e + gw
+    bwd_bytes = M * d * e + M * 512 * e + gw + M * d * e  # x, z, dG in; dx out (weight grads are small)
+    qk_bytes = 5 * (2 * M * H * dk * e)  # q and k; fwd: u in, y out; bwd: u, dy in, du out
+    peak_f, peak_b = BF16_PEAK_TFLOPS * 1e12, HBM_PEAK_GBS * 1e9
+
+    def roof(fl, by, t_us):
+        t = t_us * 1e-6
+        floor = max(fl / peak_f, by / peak_b)
+        return {"tflops": fl / t / 1e12, "alg_GBs": by / t / 1e9, "alg_flops": fl, "alg_bytes": by,
+                "bound": "mfma" if fl / peak_f >= by / peak_b else "hbm", "frac": floor / t}
+    res = {"workload": f"gate prologue, M={M} tokens (8 x 4096) d={d} H={H} dk={dk} dv={dv} bf16",
+           "avg_us": us, "ms_per_step": (t1 - t0) * 1e3 / steps,
+           "proj_fwd": roof(fwd_flops, fwd_bytes, us["proj_fwd"]),
+           "proj_bwd": roof(bwd_flops, bwd_bytes, us["proj_bwd"]),
+           "qk_norm": {"alg_GBs": qk_bytes / ((us["qk_norm_fwd"] + us["qk_norm_bwd"]) * 1e-6) / 1e9}}
+    del x, W_down, W_up, bias, dG, qk, dqk, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -373,6 +445,11 @@ def main():
         sec["stream_1m"] = stream_bench(m, torch, hiprt)
         log(f"[bench]   prefill {sec['stream_1m']['prefill_tokens_per_s']:.4g} tokens/s, "
             f"decode {sec['stream_1m']['decode_us_per_token']:.1f} us/token")
+        log("[bench] secondary gate prologue (fused gate projection + q/k SiLU-L2, fwd+bwd)")
+        sec["gate_prologue_4k"] = gate_bench(m, torch, hiprt)
+        gpb = sec["gate_prologue_4k"]
+        log(f"[bench]   proj fwd {gpb['avg_us']['proj_fwd']:.1f} us ({gpb['proj_fwd']['tflops']:.0f} TFLOP/s), "
+            f"bwd {gpb['avg_us']['proj_bwd']:.1f} us ({gpb['proj_bwd']['tflops']:.0f} TFLOP/s)")
         log(f"[bench] secondary decode ({args.decode_steps} steps)")
         sec["decode_64x16"] = decode_bench(m, torch, hiprt, steps=args.decode_steps)
         log(f"[bench]   {sec['decode_64x16']['kernel_us_per_step']:.2f} us/step kernel")

@@ -22,6 +22,9 @@ import torch
 __all__ = ["muir_chunk_fwd", "muir_chunk_bwd", "muir_step", "muir_chunk_fwd_workspace",
            "muir_chunk_bwd_workspace", "muir_chunk_varlen_fwd", "muir_chunk_varlen_bwd",
            "muir_chunk_varlen_fwd_workspace", "muir_chunk_varlen_bwd_workspace",
+           "muir_gate_proj_fwd", "muir_gate_proj_bwd", "muir_gate_proj_bwd_workspace",
+           "muir_qk_norm_fwd", "muir_qk_norm_bwd",
+           "gate_param_shapes", "GATE_NAMES", "GATE_RANKS",
            "muir_set_profile_events", "muir_profile_events_recorded",
            "lib", "library_path", "MuirError", "STATUS"]
 
@@ -38,6 +41,11 @@ class MuirError(RuntimeError):
     def __init__(self, code: int, what: str):
         self.code = code
         super().__init__(f"{what}: {STATUS.get(code, code)} ({_status_text(code)})")
+
+
+class _GateDims(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int32), ("d", ctypes.c_int32), ("H", ctypes.c_int32), ("dk", ctypes.c_int32),
+                ("dv", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 class _Dims(ctypes.Structure):
@@ -82,6 +90,17 @@ def lib():
         L.muir_chunk_varlen_fwd.restype = ctypes.c_int
         L.muir_chunk_varlen_bwd.argtypes = [D, P] + [P] * 7 + [P, P, P] + [P] * 8 + [P, SZ, P]
         L.muir_chunk_varlen_bwd.restype = ctypes.c_int
+        GD = ctypes.POINTER(_GateDims)
+        L.muir_gate_proj_bwd_workspace.argtypes = [GD]
+        L.muir_gate_proj_bwd_workspace.restype = SZ
+        L.muir_gate_proj_fwd.argtypes = [GD] + [P] * 10 + [P]
+        L.muir_gate_proj_fwd.restype = ctypes.c_int
+        L.muir_gate_proj_bwd.argtypes = [GD] + [P] * 5 + [P] * 5 + [P] * 4 + [P, SZ, P]
+        L.muir_gate_proj_bwd.restype = ctypes.c_int
+        L.muir_qk_norm_fwd.argtypes = [ctypes.c_int64, I32, I32, P, P, P]
+        L.muir_qk_norm_fwd.restype = ctypes.c_int
+        L.muir_qk_norm_bwd.argtypes = [ctypes.c_int64, I32, I32, P, P, P, P]
+        L.muir_qk_norm_bwd.restype = ctypes.c_int
         L.muir_step.argtypes = [I32] * 6 + [P] * 7 + [P, P, P]
         L.muir_step.restype = ctypes.c_int
         L.muir_set_profile_events.argtypes = [P, I32]
@@ -378,6 +397,104 @@ def muir_step(q, k, v, log_a, erase, write, gamma, S, *, out=None) -> torch.Tens
     if rc != 0:
         raise MuirError(rc, "muir_step")
     return o
+
+
+# The fused gate projection: gate order and ranks of the shared down-projection.
+GATE_NAMES = ("log_a", "erase", "g", "write", "gamma")
+GATE_RANKS = (64, 64, 128, 128, 128)
+
+
+def gate_param_shapes(d: int, H: int, dk: int, dv: int):
+    """Shapes of (W_down, W_up, bias) of the gate projection: W_down [d, 512];
+    W_up the five up matrices back to back (flat); bias the five bias vectors
+    back to back (flat)."""
+    widths = (H * dk, H * dk, H * dv, H * dv, H * dk)
+    return (d, sum(GATE_RANKS)), (sum(r * w for r, w in zip(GATE_RANKS, widths)),), (sum(widths),)
+
+
+def muir_gate_proj_bwd_workspace(M, d, H, dk, dv, dtype=MUIR_BF16) -> int:
+    gd = _GateDims(M, d, H, dk, dv, dtype)
+    return int(lib().muir_gate_proj_bwd_workspace(ctypes.byref(gd)))
+
+
+def _gate_args(x, W_down, W_up, bias, H, dk, dv):
+    lead = tuple(x.shape[:-1])
+    d = x.shape[-1]
+    M = 1
+    for n in lead:
+        M *= n
+    dev, dt = x.device, x.dtype
+    code = _dtype_code(x)
+    _check_io("x", x, tuple(x.shape), dt, dev)
+    sw, su, sb = gate_param_shapes(d, H, dk, dv)
+    _check_io("W_down", W_down, sw, dt, dev)
+    _check_io("W_up", W_up, su, dt, dev)
+    _check_io("bias", bias, sb, dt, dev)
+    return lead, M, d, dev, dt, _GateDims(M, d, H, dk, dv, code)
+
+
+def muir_gate_proj_fwd(x, W_down, W_up, bias, *, H: int, dk: int, dv: int):
+    """The five gates of every token of x [..., d] from the fused low-rank
+    projection.  Returns {"z": [..., 512], "log_a", "erase", "gamma": [..., H, dk],
+    "g", "write": [..., H, dv]} in x's dtype."""
+    lead, M, d, dev, dt, gd = _gate_args(x, W_down, W_up, bias, H, dk, dv)
+    out = {"z": torch.empty(lead + (512,), dtype=dt, device=dev)}
+    for n, D in zip(GATE_NAMES, (dk, dk, dv, dv, dk)):
+        out[n] = torch.empty(lead + (H, D), dtype=dt, device=dev)
+    rc = lib().muir_gate_proj_fwd(ctypes.byref(gd), _ptr(x), _ptr(W_down), _ptr(W_up), _ptr(bias),
+                                  _ptr(out["z"]), *(_ptr(out[n]) for n in GATE_NAMES), _stream(dev))
+    if rc != 0:
+        raise MuirError(rc, "muir_gate_proj_fwd")
+    return out
+
+
+def muir_gate_proj_bwd(x, W_down, W_up, bias, d_gates, *, H: int, dk: int, dv: int, z=None,
+                       workspace: Optional[torch.Tensor] = None):
+    """Reverse mode of muir_gate_proj_fwd from the gates' gradients
+    (d_gates[name], shaped like the gates).  Returns {"dx" (x's dtype),
+    "dW_down", "dW_up", "dbias" (fp32)}.  z: the forward's z, or None."""
+    lead, M, d, dev, dt, gd = _gate_args(x, W_down, W_up, bias, H, dk, dv)
+    for n, D in zip(GATE_NAMES, (dk, dk, dv, dv, dk)):
+        _check_io("d" + n, d_gates[n], lead + (H, D), dt, dev)
+    if z is not None:
+        _check_io("z", z, lead + (512,), dt, dev)
+    sw, su, sb = gate_param_shapes(d, H, dk, dv)
+    g = {"dx": torch.empty(tuple(x.shape), dtype=dt, device=dev),
+         "dW_down": torch.empty(sw, dtype=torch.float32, device=dev),
+         "dW_up": torch.empty(su, dtype=torch.float32, device=dev),
+         "dbias": torch.empty(sb, dtype=torch.float32, device=dev)}
+    ws = _workspace(int(lib().muir_gate_proj_bwd_workspace(ctypes.byref(gd))), dev, workspace)
+    rc = lib().muir_gate_proj_bwd(ctypes.byref(gd), _ptr(x), _ptr(W_down), _ptr(W_up), _ptr(bias), _ptr(z),
+                                  *(_ptr(d_gates[n]) for n in GATE_NAMES),
+                                  *(_ptr(g[n]) for n in ("dx", "dW_down", "dW_up", "dbias")),
+                                  _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
+    if rc != 0:
+        raise MuirError(rc, "muir_gate_proj_bwd")
+    return g
+
+
+def muir_qk_norm_fwd(u, *, out=None):
+    """SiLU then L2 normalisation over the last axis (64 or 128 channels: one head)."""
+    D = u.shape[-1]
+    _check_io("u", u, tuple(u.shape), u.dtype, u.device)
+    y = out if out is not None else torch.empty_like(u)
+    rc = lib().muir_qk_norm_fwd(u.numel() // max(D, 1), D, _dtype_code(u), _ptr(u), _ptr(y), _stream(u.device))
+    if rc != 0:
+        raise MuirError(rc, "muir_qk_norm_fwd")
+    return y
+
+
+def muir_qk_norm_bwd(u, dy):
+    """Gradient of sum(dy * muir_qk_norm_fwd(u)) with respect to u."""
+    D = u.shape[-1]
+    _check_io("u", u, tuple(u.shape), u.dtype, u.device)
+    _check_io("dy", dy, tuple(u.shape), u.dtype, u.device)
+    du = torch.empty_like(u)
+    rc = lib().muir_qk_norm_bwd(u.numel() // max(D, 1), D, _dtype_code(u), _ptr(u), _ptr(dy), _ptr(du),
+                                _stream(u.device))
+    if rc != 0:
+        raise MuirError(rc, "muir_qk_norm_bwd")
+    return du
 
 
 def muir_set_profile_events(events=None, count: int = 0) -> None:

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmuir.so")
-SOURCES = ["muir_api.hip", "step.hip", "fwd.hip", "scan.hip", "bwd_chunk.hip"]
+SOURCES = ["muir_api.hip", "step.hip", "fwd.hip", "scan.hip", "bwd_chunk.hip", "gate_proj.hip"]
 ARCH = "gfx950"
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
@@ -34,7 +34,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every HIP source and link libmuir.so in the package directory."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]

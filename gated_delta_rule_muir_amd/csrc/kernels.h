@@ -112,4 +112,62 @@ hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, c
 // partial sums ([nchunks][dk] fp32).
 hipError_t launch_gamma_sum(const ChunkShape& s, const float* part, float* dgamma, hipStream_t stream);
 
+// ---- gate prologue ---------------------------------------------------------------
+
+// Channels of the shared down-projection (the five gate ranks 64 + 64 + 128 +
+// 128 + 128) and the guard of the q / k L2 normalisation.
+constexpr int GATE_RTOT = 512;
+constexpr float QK_L2_EPS = 1e-6f;
+enum GateAct { GATE_ACT_NONE = 0, GATE_ACT_LOGSIG = 1, GATE_ACT_SIG = 2, GATE_ACT_SIG2 = 3 };
+
+// One product C = A B of a grouped GEMM launch (elements; A is M x K, B is
+// K x N; the kernel instance fixes whether each operand is read along k or
+// across it).  bias / dG / act / colsum_off serve the gate epilogues.
+struct GemmProblem {
+  const void* A;
+  const void* B;
+  void* C;
+  int M, N, K;
+  int lda, ldb, ldc;
+  const void* bias;
+  const void* dG;
+  int act;
+  int colsum_off;
+};
+struct GemmBatch {
+  GemmProblem p[5];
+  int n;                // problems in the launch
+  int ksplit;           // splits of the contraction (fp32 partials)
+  int kchunk;           // contraction length per split (a multiple of 32)
+  size_t split_stride;  // floats between the partials of consecutive splits
+  float* colsum;        // per-tile column sums of the gate backward
+  int colsum_ld;
+};
+
+// Sizes of a gate-prologue call: M tokens of width d; H heads of dk key and
+// dv value channels.
+struct GateShape {
+  int M, d, H, dk, dv;
+  bool bf16;
+};
+// Backward workspace: recomputed z, dpre of the five gates, dz, split
+// partials of the weight gradients and the per-tile column sums.
+struct GateWorkspace {
+  size_t z_off, dpre_off, dz_off, part_off, colsum_off, bytes;
+  size_t part_stride;
+  int ksplit, kchunk, mtiles, colsum_ld;
+};
+GateWorkspace gate_workspace(const GateShape& s);
+// Elements of the packed up-projection weights (sum of rank x width).
+size_t gate_up_numel(const GateShape& s);
+hipError_t launch_gate_fwd(const GateShape& s, const void* x, const void* W_down, const void* W_up,
+                           const void* bias, void* z, void* const gates[5], hipStream_t stream);
+hipError_t launch_gate_bwd(const GateShape& s, const void* x, const void* W_down, const void* W_up,
+                           const void* bias, const void* z, const void* const dgates[5], void* dx,
+                           float* dW_down, float* dW_up, float* dbias, void* workspace, hipStream_t stream);
+// SiLU + L2 over rows of D in {64, 128} values: forward (dy == NULL, out = y)
+// or reverse (out = du).
+hipError_t launch_qk_norm(long long rows, int D, bool bf16, const void* u, const void* dy, void* out,
+                          hipStream_t stream);
+
 }  // namespace muir

@@ -368,6 +368,36 @@ size_t fwd_need(const ChunkShape& s) {
 size_t bwd_need(const ChunkShape& s) {
   return s.T % s.C == 0 ? bwd_ws(s) : bwd_ws(padded(s)) + bwd_stage_bytes(padded(s));
 }
+// Sizes of a gate-prologue call.
+muir_status_t check_gate_dims(const muir_gate_dims_t* d, muir::GateShape* s) {
+  if (!d) return MUIR_ERR_NULL;
+  if (d->dtype != MUIR_F32 && d->dtype != MUIR_BF16) return MUIR_ERR_DTYPE;
+  if (d->M < 0 || d->d <= 0 || d->d % 64 != 0 || d->d > (1 << 16) || d->H <= 0) return MUIR_ERR_SHAPE;
+  if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128)) return MUIR_ERR_SHAPE;
+  if (static_cast<long long>(d->H) * (d->dk > d->dv ? d->dk : d->dv) > (1 << 16)) return MUIR_ERR_SHAPE;
+  s->M = d->M;
+  s->d = d->d;
+  s->H = d->H;
+  s->dk = d->dk;
+  s->dv = d->dv;
+  s->bf16 = d->dtype == MUIR_BF16;
+  return MUIR_OK;
+}
+
+muir_status_t qk_norm_call(int64_t rows, int32_t D, int32_t dtype, const void* u, const void* dy, void* out,
+                           void* stream) {
+  if (dtype != MUIR_F32 && dtype != MUIR_BF16) return MUIR_ERR_DTYPE;
+  if (rows < 0 || (D != 64 && D != 128) || rows > (1LL << 40)) return MUIR_ERR_SHAPE;
+  if (rows == 0) return MUIR_OK;
+  if (!u || !out) return MUIR_ERR_NULL;
+  if (!aligned16(u) || !aligned16(out) || (dy && !aligned16(dy))) return MUIR_ERR_ALIGN;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  mark(hs);
+  if (muir::launch_qk_norm(rows, D, dtype == MUIR_BF16, u, dy, out, hs) != hipSuccess) return MUIR_ERR_HIP;
+  mark(hs);
+  return MUIR_OK;
+}
+
 size_t varlen_fwd_need(const ChunkShape& s) { return fwd_ws(padded(s)) + fwd_stage_bytes(padded(s)); }
 size_t varlen_bwd_need(const ChunkShape& s) { return bwd_ws(padded(s)) + bwd_stage_bytes(padded(s)); }
 
@@ -375,7 +405,7 @@ size_t varlen_bwd_need(const ChunkShape& s) { return bwd_ws(padded(s)) + bwd_sta
 
 extern "C" {
 
-int32_t muir_abi_version(void) { return 5; }
+int32_t muir_abi_version(void) { return 6; }
 
 int32_t muir_set_profile_events(void** events, int32_t count) {
   if (count < 0 || (count > 0 && !events)) return MUIR_ERR_NULL;
@@ -498,6 +528,84 @@ muir_status_t muir_chunk_varlen_bwd(const muir_dims_t* dims, const int32_t* cu_s
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (s.nchunks() == 0) return bwd_empty(s, dS_T, dgamma, dS0, hs);
   return bwd_staged(s, cu_seqlens, in, S0, nullptr, nullptr, dO, dS_T, gr, dS0, workspace, hs);
+}
+
+size_t muir_gate_proj_bwd_workspace(const muir_gate_dims_t* dims) {
+  muir::GateShape s;
+  if (check_gate_dims(dims, &s) != MUIR_OK) return 0;
+  return muir::gate_workspace(s).bytes;
+}
+
+muir_status_t muir_gate_proj_fwd(const muir_gate_dims_t* dims, const void* x, const void* W_down,
+                                 const void* W_up, const void* bias, void* z, void* log_a, void* erase,
+                                 void* g, void* write, void* gamma, void* stream) {
+  muir::GateShape s;
+  muir_status_t st = check_gate_dims(dims, &s);
+  if (st != MUIR_OK) return st;
+  if (s.M == 0) return MUIR_OK;
+  const void* req[] = {x, W_down, W_up, bias, z, log_a, erase, g, write, gamma};
+  for (const void* p : req)
+    if (!p) return MUIR_ERR_NULL;
+  for (const void* p : req)
+    if (!aligned16(p)) return MUIR_ERR_ALIGN;
+  void* const gates[5] = {log_a, erase, g, write, gamma};
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  mark(hs);
+  if (muir::launch_gate_fwd(s, x, W_down, W_up, bias, z, gates, hs) != hipSuccess) return MUIR_ERR_HIP;
+  mark(hs);
+  return MUIR_OK;
+}
+
+muir_status_t muir_gate_proj_bwd(const muir_gate_dims_t* dims, const void* x, const void* W_down,
+                                 const void* W_up, const void* bias, const void* z, const void* dlog_a,
+                                 const void* derase, const void* dg, const void* dwrite, const void* dgamma,
+                                 void* dx, float* dW_down, float* dW_up, float* dbias, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  muir::GateShape s;
+  muir_status_t st = check_gate_dims(dims, &s);
+  if (st != MUIR_OK) return st;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (s.M == 0) {
+    // no tokens: the weight gradients are sums over nothing
+    float* outs[] = {dW_down, dW_up, dbias};
+    for (float* p : outs)
+      if (!p) return MUIR_ERR_NULL;
+    for (float* p : outs)
+      if (!aligned16(p)) return MUIR_ERR_ALIGN;
+    const muir::GateWorkspace w = muir::gate_workspace(s);
+    const size_t n[] = {static_cast<size_t>(s.d) * muir::GATE_RTOT,
+                        muir::gate_up_numel(s),
+                        static_cast<size_t>(w.colsum_ld)};
+    for (int i = 0; i < 3; ++i)
+      if (copy_or_zero(outs[i], nullptr, n[i], hs) != hipSuccess) return MUIR_ERR_HIP;
+    return MUIR_OK;
+  }
+  const void* req[] = {x, W_down, W_up, bias, dlog_a, derase, dg, dwrite, dgamma, dx, dW_down, dW_up, dbias};
+  for (const void* p : req)
+    if (!p) return MUIR_ERR_NULL;
+  for (const void* p : req)
+    if (!aligned16(p)) return MUIR_ERR_ALIGN;
+  if (z && !aligned16(z)) return MUIR_ERR_ALIGN;
+  const muir::GateWorkspace w = muir::gate_workspace(s);
+  if (!workspace || workspace_bytes < w.bytes) return MUIR_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MUIR_ERR_ALIGN;
+  mark(hs);
+  const void* const dgates[5] = {dlog_a, derase, dg, dwrite, dgamma};
+  if (muir::launch_gate_bwd(s, x, W_down, W_up, bias, z, dgates, dx, dW_down, dW_up, dbias, workspace, hs) !=
+      hipSuccess)
+    return MUIR_ERR_HIP;
+  mark(hs);
+  return MUIR_OK;
+}
+
+muir_status_t muir_qk_norm_fwd(int64_t rows, int32_t D, int32_t dtype, const void* u, void* y, void* stream) {
+  return qk_norm_call(rows, D, dtype, u, nullptr, y, stream);
+}
+
+muir_status_t muir_qk_norm_bwd(int64_t rows, int32_t D, int32_t dtype, const void* u, const void* dy, void* du,
+                               void* stream) {
+  if (rows > 0 && !dy) return MUIR_ERR_NULL;
+  return qk_norm_call(rows, D, dtype, u, dy, du, stream);
 }
 
 muir_status_t muir_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dtype,

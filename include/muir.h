@@ -251,6 +251,75 @@ muir_status_t muir_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dt
                         const void* write, const void* gamma,
                         float* S, void* o, void* stream);
 
+/*
+ * Gate prologue (wolonglab summary page, §Methodology and fig:arch (b), (c)):
+ * the five per-token gates come from ONE low-rank projection of the
+ * token's input x -- a shared down-projection to 512 channels, split into
+ * rank slices (64, 64, 128, 128, 128) for the gates (f, b, g, w, q) in that
+ * order, each slice up-projected to its gate's width plus a per-channel bias:
+ *
+ *   z      = x W_down                                   [M, 512]
+ *   pre_i  = z[:, slice_i] U_i + c_i
+ *   log_a  = log sigmoid(pre_f)   [M, H, dk]   (decay; <= 0)
+ *   erase  = sigmoid(pre_b)       [M, H, dk]
+ *   g      = sigmoid(pre_g)       [M, H, dv]   (output gate, used after the operator)
+ *   write  = sigmoid(pre_w)       [M, H, dv]
+ *   gamma  = 2 sigmoid(pre_q)     [M, H, dk]   (readout gain)
+ *
+ * The activations are readings (the pages name the gates, not their
+ * nonlinearities).  Layouts (row-major, dtype unless stated):
+ *   x      : [M, d] tokens (M = B * T)
+ *   W_down : [d, 512]
+ *   W_up   : the five U_i back to back: U_f [64, H*dk], U_b [64, H*dk],
+ *            U_g [128, H*dv], U_w [128, H*dv], U_q [128, H*dk]
+ *   bias   : the five c_i back to back: [H*dk], [H*dk], [H*dv], [H*dv], [H*dk]
+ * Supported sizes: d a multiple of 64 up to 65536; dk, dv in {64, 128}.
+ */
+typedef struct {
+  int32_t M;      /* tokens */
+  int32_t d;      /* width of x */
+  int32_t H;      /* heads */
+  int32_t dk, dv; /* key / value channels per head */
+  int32_t dtype;  /* muir_dtype_t of x, the weights, z, the gates and their gradients */
+} muir_gate_dims_t;
+
+/*
+ * Forward: writes z (kept for the backward) and the five gates.  All
+ * pointers are required.  M == 0 launches nothing.
+ */
+muir_status_t muir_gate_proj_fwd(const muir_gate_dims_t* dims, const void* x, const void* W_down,
+                                 const void* W_up, const void* bias, void* z, void* log_a,
+                                 void* erase, void* g, void* write, void* gamma, void* stream);
+
+/* Bytes of workspace muir_gate_proj_bwd needs (0 if dims are invalid). */
+size_t muir_gate_proj_bwd_workspace(const muir_gate_dims_t* dims);
+
+/*
+ * Backward: from the gradients of the five gates (shaped like the gates,
+ * dtype) to dx [M, d] (dtype, overwritten), and dW_down [d, 512], dW_up
+ * and dbias (fp32, packed like W_up and bias, overwritten; sums over tokens
+ * in a fixed order).  z is the forward's z, or NULL to recompute it.  Every
+ * other pointer is required; the workspace is clobbered.
+ */
+muir_status_t muir_gate_proj_bwd(const muir_gate_dims_t* dims, const void* x, const void* W_down,
+                                 const void* W_up, const void* bias, const void* z,
+                                 const void* dlog_a, const void* derase, const void* dg,
+                                 const void* dwrite, const void* dgamma, void* dx, float* dW_down,
+                                 float* dW_up, float* dbias, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
+ * End of the q / k pathways (fig:arch (b); the operator takes unit keys and
+ * queries): for each of `rows` vectors u of D values (one head),
+ *   y = s / sqrt(sum s^2 + 1e-6),  s = u * sigmoid(u)  (SiLU).
+ * u, y, dy, du: [rows, D] dtype; D in {64, 128}.  muir_qk_norm_bwd writes
+ * du, the gradient of sum(dy * y) with respect to u.
+ */
+muir_status_t muir_qk_norm_fwd(int64_t rows, int32_t D, int32_t dtype, const void* u, void* y,
+                               void* stream);
+muir_status_t muir_qk_norm_bwd(int64_t rows, int32_t D, int32_t dtype, const void* u, const void* dy,
+                               void* du, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

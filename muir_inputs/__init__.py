@@ -142,6 +142,35 @@ def varlen_inputs(lens, H: int, dk: int, dv: int, *, dtype: str = "bf16", decay:
     return out
 
 
+GATE_RANKS = (64, 64, 128, 128, 128)
+
+
+def gate_inputs(M: int, d: int, H: int, dk: int, dv: int, *, dtype: str = "bf16", seed: int = 0,
+                with_grads: bool = True) -> Dict[str, torch.Tensor]:
+    """Inputs of one gate-prologue call (random weights stand in for trained
+    ones): x [M, d] ~ N(0, 1); W_down ~ N(0, 1/d) so z ~ N(0, 1); each up
+    matrix ~ N(0, 0.25 / rank); biases ~ N(0, 1) except the decay gate's,
+    which put exp(log_a) at exp(-r) for log-uniform rates r in [1e-4, 3]
+    per channel (slow and fast rows).  With grads: upstream gradients of the
+    five gates ~ N(0, 1).  Returns CPU tensors in dtype; W_up and bias flat,
+    packed in the gate order (log_a, erase, g, write, gamma)."""
+    rng = np.random.Generator(np.random.PCG64([seed, 1 << 23]))
+    f32 = np.float32
+    widths = (H * dk, H * dk, H * dv, H * dv, H * dk)
+    x = rng.standard_normal((M, d), dtype=f32)
+    Wd = rng.standard_normal((d, sum(GATE_RANKS)), dtype=f32) / np.sqrt(d)
+    ups = [rng.standard_normal((r, w), dtype=f32) * (0.5 / np.sqrt(r)) for r, w in zip(GATE_RANKS, widths)]
+    rates = np.exp(rng.uniform(np.log(1e-4), np.log(3.0), size=widths[0]))
+    biases = [(-np.log(np.expm1(rates))).astype(f32)] + [rng.standard_normal(w, dtype=f32) for w in widths[1:]]
+    out = {"x": _cast(x, dtype), "W_down": _cast(Wd.astype(f32), dtype),
+           "W_up": _cast(np.concatenate([u.reshape(-1) for u in ups]), dtype),
+           "bias": _cast(np.concatenate(biases), dtype)}
+    if with_grads:
+        for n, D in zip(("log_a", "erase", "g", "write", "gamma"), (dk, dk, dv, dv, dk)):
+            out["d" + n] = _cast(rng.standard_normal((M, H, D), dtype=f32), dtype)
+    return out
+
+
 def step_rates(H: int, dk: int, seed: int = 0, mode: str = "channel") -> np.ndarray:
     """Per-(head, channel) decay rates for a decode stream, fixed over steps, [H, dk] fp32."""
     rng = np.random.Generator(np.random.PCG64([seed, 1 << 20]))

@@ -50,7 +50,7 @@ def test_status_strings_cover_every_code():
         seen.add(s)
     assert len(seen) == 8
     assert L.muir_status_string(99).decode() == "unknown status"
-    assert L.muir_abi_version() == 5
+    assert L.muir_abi_version() == 6
 
 
 def _dims(m, B=1, T=128, H=2, dk=64, dv=64, chunk=64, dtype=1, gamma_mode=0):
@@ -213,6 +213,55 @@ def test_varlen_rejects_bad_arguments():
     g = list(FAKE[:7])
     g[0] = None
     assert bwd(d, grads=g) == ERR_NULL
+
+
+def _gdims(m, M=256, d=128, H=2, dk=64, dv=64, dtype=1):
+    return m._GateDims(M, d, H, dk, dv, dtype)
+
+
+def test_gate_proj_rejects_bad_arguments():
+    m, L = _lib()
+    fwd = lambda dd, p: L.muir_gate_proj_fwd(ctypes.byref(dd) if dd is not None else None, *p, None)
+    p = list(FAKE[:10])
+    assert fwd(None, p) == ERR_NULL
+    assert fwd(_gdims(m, dtype=4), p) == ERR_DTYPE
+    for kw in (dict(d=100), dict(d=0), dict(M=-1), dict(dk=96), dict(dv=32), dict(H=0)):
+        assert fwd(_gdims(m, **kw), p) == ERR_SHAPE, kw
+        assert L.muir_gate_proj_bwd_workspace(ctypes.byref(_gdims(m, **kw))) == 0
+    assert fwd(_gdims(m, M=0), [None] * 10) == OK  # no tokens: nothing launched
+    assert L.muir_gate_proj_bwd(ctypes.byref(_gdims(m, M=0)), *([None] * 11), None, None, None, None, 0, None) == ERR_NULL
+    for i in range(10):
+        q = list(p)
+        q[i] = None
+        assert fwd(_gdims(m), q) == ERR_NULL, i
+        q[i] = ctypes.c_void_p(FAKE[i].value + 4)
+        assert fwd(_gdims(m), q) == ERR_ALIGN, i
+    d = _gdims(m)
+    need = L.muir_gate_proj_bwd_workspace(ctypes.byref(d))
+    assert need > 0
+
+    def bwd(dd, ptrs=None, z=None, ws=FAKE[15], ws_bytes=1 << 40):
+        q = list(FAKE[:13]) if ptrs is None else ptrs
+        return L.muir_gate_proj_bwd(ctypes.byref(dd), *q[:4], z, *q[4:], ws, ctypes.c_size_t(ws_bytes), None)
+    assert bwd(d, ws_bytes=need - 1) == ERR_WORKSPACE
+    assert bwd(d, ws=None) == ERR_WORKSPACE
+    assert bwd(d, z=ctypes.c_void_p(0x10002)) == ERR_ALIGN
+    q = list(FAKE[:13])
+    q[8] = None  # dgamma
+    assert bwd(d, ptrs=q) == ERR_NULL
+    # the workspace grows with the tokens
+    assert L.muir_gate_proj_bwd_workspace(ctypes.byref(_gdims(m, M=4096))) > need
+
+
+def test_qk_norm_rejects_bad_arguments():
+    m, L = _lib()
+    assert L.muir_qk_norm_fwd(10, 96, 1, FAKE[0], FAKE[1], None) == ERR_SHAPE
+    assert L.muir_qk_norm_fwd(-1, 64, 1, FAKE[0], FAKE[1], None) == ERR_SHAPE
+    assert L.muir_qk_norm_fwd(10, 64, 2, FAKE[0], FAKE[1], None) == ERR_DTYPE
+    assert L.muir_qk_norm_fwd(10, 64, 1, None, FAKE[1], None) == ERR_NULL
+    assert L.muir_qk_norm_fwd(10, 64, 1, FAKE[0], ctypes.c_void_p(0x10002), None) == ERR_ALIGN
+    assert L.muir_qk_norm_bwd(10, 64, 1, FAKE[0], None, FAKE[1], None) == ERR_NULL
+    assert L.muir_qk_norm_fwd(0, 64, 1, None, None, None) == OK
 
 
 def test_binding_refuses_cpu_tensors():

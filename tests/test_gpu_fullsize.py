@@ -106,3 +106,52 @@ def test_decode_4096_steps_sampled_streams():
     e_s = rel_err(S[picks].cpu(), S_ref)
     _say(f"  decode o={e_o:.2e} S={e_s:.2e}")
     assert e_o <= TOL and e_s <= TOL
+
+
+def test_gate_prologue_full_layer():
+    """Gate prologue at the layer's shape (M = 8 x 4096 tokens, d = 2048,
+    H = 16, dk = dv = 128, bf16), as bench.py runs it.  Every token's gates
+    and dx depend on that token alone: sampled tokens against the oracle run
+    on those tokens.  The weight gradients are sums over tokens: the full
+    call equals the sum of the calls on four quarters of the tokens (to fp32
+    summation order), and the first quarter's match the oracle's."""
+    m = _lib()
+    M, d, H, dk, dv = 8 * 4096, 2048, 16, 128, 128
+    _say(f"gate prologue full layer M={M} d={d}")
+    inp = muir_inputs.gate_inputs(M, d, H, dk, dv, dtype="bf16", seed=41)
+    dev = {k: t.to("cuda") for k, t in inp.items()}
+    names = m.GATE_NAMES
+    args = (dev["W_down"], dev["W_up"], dev["bias"])
+    out = m.muir_gate_proj_fwd(dev["x"], *args, H=H, dk=dk, dv=dv)
+    g = m.muir_gate_proj_bwd(dev["x"], *args, {n: dev["d" + n] for n in names}, H=H, dk=dk, dv=dv, z=out["z"])
+    q4 = M // 4
+    parts = [m.muir_gate_proj_bwd(dev["x"][i * q4:(i + 1) * q4], *args,
+                                  {n: dev["d" + n][i * q4:(i + 1) * q4] for n in names}, H=H, dk=dk, dv=dv)
+             for i in range(4)]
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(5).choice(M, 48, replace=False))
+    rows[0], rows[-1] = 0, M - 1
+    sub = {k: inp[k][rows] for k in ["x"] + ["d" + n for n in names]}
+    ref = gp_fwd(sub["x"], inp, H, dk, dv)
+    rg = gp_bwd(sub["x"], inp, {n: sub["d" + n] for n in names}, H, dk, dv)
+    errs = {n: rel_err(out[n][rows], ref[n]) for n in names}
+    errs["dx"] = rel_err(g["dx"][rows], rg["dx"])
+    for n in ("dW_down", "dW_up", "dbias"):
+        errs[n + "_additive"] = rel_err(g[n], sum(p[n] for p in parts))
+    q = {k: inp[k][:q4] for k in ["x"] + ["d" + n for n in names]}
+    r0 = gp_bwd(q["x"], inp, {n: q["d" + n] for n in names}, H, dk, dv)
+    for n in ("dW_down", "dW_up", "dbias"):
+        errs[n + "_q0"] = rel_err(parts[0][n], r0[n])
+    _say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for n, e in errs.items():
+        assert e <= (1e-5 if n.endswith("_additive") else TOL), (n, e)
+
+
+def gp_fwd(x, inp, H, dk, dv):
+    from oracle import gate_proj
+    return gate_proj.gate_fwd(x, inp["W_down"], inp["W_up"], inp["bias"], H, dk, dv)
+
+
+def gp_bwd(x, inp, dG, H, dk, dv):
+    from oracle import gate_proj
+    return gate_proj.gate_bwd(x, inp["W_down"], inp["W_up"], inp["bias"], dG, H, dk, dv)
