@@ -405,11 +405,12 @@ GATE_RANKS = (64, 64, 128, 128, 128)
 
 
 def gate_param_shapes(d: int, H: int, dk: int, dv: int):
-    """Shapes of (W_down, W_up, bias) of the gate projection: W_down [d, 512];
-    W_up the five up matrices back to back (flat); bias the five bias vectors
-    back to back (flat)."""
+    """Shapes of (W_down, W_up, bias) of the gate projection, in a linear
+    layer's [out, in] layout: W_down [512, d]; W_up the five up matrices
+    [width_i, rank_i] back to back (flat); bias the five bias vectors back to
+    back (flat)."""
     widths = (H * dk, H * dk, H * dv, H * dv, H * dk)
-    return (d, sum(GATE_RANKS)), (sum(r * w for r, w in zip(GATE_RANKS, widths)),), (sum(widths),)
+    return (sum(GATE_RANKS), d), (sum(r * w for r, w in zip(GATE_RANKS, widths)),), (sum(widths),)
 
 
 def muir_gate_proj_bwd_workspace(M, d, H, dk, dv, dtype=MUIR_BF16) -> int:

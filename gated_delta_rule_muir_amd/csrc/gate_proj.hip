@@ -4,21 +4,20 @@
 // down-projection shared by the five gates, five up-projections at ranks
 // (64, 64, 128, 128, 128) with channel biases; fig:arch (b), (c)).
 //
-// All projections run through one grouped GEMM kernel: up to five
-// independent problems per launch (one per gate), 128 x BN tiles on four
+// The gates' up-projections run in gate_up_kernel (the rank-64/128
+// contraction with the activation, or its gradient and the bias sums, fused
+// into the epilogue).  Every other product runs through one grouped GEMM
+// kernel: up to five independent problems per launch, 128 x BN tiles on four
 // waves, bf16 (v_mfma_f32_16x16x32_bf16) or fp32 (v_mfma_f32_16x16x4_f32)
-// with fp32 accumulation, LDS double buffering, and an epilogue chosen at
-// compile time:
+// with fp32 accumulation, and an epilogue chosen at compile time:
 //   EPI_STORE     C = acc, in the compute type
-//   EPI_GATE      C = act(acc + bias), in the compute type
-//   EPI_GATE_BWD  dpre = dG * act'(acc + bias) stored in the compute type,
-//                 with per-tile column sums of dpre (the bias gradient)
 //   EPI_PARTIAL   fp32 partial of one split of the contraction
 // Operands are read either along their contiguous axis (k contiguous: rows of
 // A, columns of B^T) or across it (k strided), the latter transposed on the
-// way into LDS, so every product here -- x W, z U, dpre U^T, dz W^T, x^T dz,
-// z^T dpre -- runs without an explicit transpose.
+// way into LDS, so every product here -- x W_down^T, dpre U, dz W_down,
+// dz^T x, dpre^T z -- runs without an explicit transpose.
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.h"
 #include "mma.h"
@@ -29,9 +28,15 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int GEMM_THREADS = 256;
-constexpr int BK = 32;
+constexpr int UP_THREADS = 256;
+constexpr int UP_BN = 64;  // columns per tile of the up-projection kernel
 
-enum Epi { EPI_STORE = 0, EPI_GATE = 1, EPI_GATE_BWD = 2, EPI_PARTIAL = 3 };
+enum Epi {
+  EPI_STORE = 0,     // general GEMM: C = acc in the compute type
+  EPI_GATE = 1,      // up-projection: gate = act(acc + bias)
+  EPI_GATE_BWD = 2,  // up-projection: dpre = dG * act'(acc + bias), with per-tile column sums
+  EPI_PARTIAL = 3    // general GEMM: fp32 partial of one split of the contraction
+};
 
 // Per-compute-type GEMM fragment: bf16 contracts 32 per MFMA (8 values per
 // lane at k = 8*(lane/16) + i), fp32 contracts 16 per group of four MFMAs
@@ -56,13 +61,23 @@ template <> struct GF<float> {
   static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) { return MM<float>::mma(a, b, c); }
 };
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
+// Hardware exp2 / log2 / reciprocal (v_exp_f32, v_log_f32, v_rcp_f32, about
+// 1 ulp; denormal results flush to zero), far inside the tolerance of the
+// compute types.
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+__device__ __forceinline__ float sigmoidf_(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-LOG2E * x));
+}
 
 // Gate activations (readings of the pages: log-decay = log sigmoid; erase,
 // write and the output gate sigmoid; the readout gain 2 sigmoid).
+// log sigmoid(x) = min(x, 0) - log(1 + e^-|x|); the logarithm of 1 + e with
+// e <= 1 loses at most e ~ 6e-8 (absolute) when e is below fp32 resolution.
 __device__ __forceinline__ float act_fwd(int act, float x) {
   switch (act) {
-    case GATE_ACT_LOGSIG: return fminf(x, 0.f) - log1pf(__expf(-fabsf(x)));
+    case GATE_ACT_LOGSIG:
+      return fminf(x, 0.f) - LN2 * __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-LOG2E * fabsf(x)));
     case GATE_ACT_SIG: return sigmoidf_(x);
     case GATE_ACT_SIG2: return 2.f * sigmoidf_(x);
     default: return x;
@@ -73,40 +88,89 @@ __device__ __forceinline__ float act_grad(int act, float x) {
     case GATE_ACT_LOGSIG: return sigmoidf_(-x);
     case GATE_ACT_SIG: {
       const float s = sigmoidf_(x);
-      return s * (1.f - s);
+      return s - s * s;
     }
     case GATE_ACT_SIG2: {
       const float s = sigmoidf_(x);
-      return 2.f * s * (1.f - s);
+      return 2.f * (s - s * s);
     }
     default: return 1.f;
   }
 }
 
+// Arguments of the gates' up-projection kernel (all five gates in one launch).
+template <typename TC> struct GateUpArgs {
+  const TC* z;     // [M, 512]
+  const TC* U;     // packed up matrices
+  const TC* bias;  // packed biases
+  TC* out[5];      // gates (forward) or their pre-activation gradients (backward), [M, W_i]
+  const TC* dG[5];  // backward: the gates' gradients, [M, W_i]
+  float* colsum;   // backward: per-tile column sums [m tiles][colsum_ld]
+  int colsum_ld;
+  int M;
+  int r[5], W[5], zoff[5], act[5], csoff[5];
+  size_t woff[5], boff[5];
+};
+
+template <typename TC> struct GemmStep;
+template <> struct GemmStep<uint16_t> { static constexpr int BK = 64; };
+template <> struct GemmStep<float> { static constexpr int BK = 32; };
+
+// Transposes a block of 16-byte words: in[r] holds KR consecutive-k rows of E
+// columns; out[c] receives column c's KR values (k ascending).  bf16: 8 x 8
+// (byte permutes pair up the 16-bit halves), fp32: 4 x 4 (register moves).
+__device__ __forceinline__ void transpose_block(const uint4 (&in)[8], uint4 (&out)[8]) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(in);  // w[4*r + c/2]
+  uint32_t* o = reinterpret_cast<uint32_t*>(out);             // o[4*c + p]
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t lo = w[4 * (2 * p) + c / 2], hi = w[4 * (2 * p + 1) + c / 2];
+      o[4 * c + p] = __builtin_amdgcn_perm(hi, lo, (c & 1) ? 0x07060302u : 0x05040100u);
+    }
+}
+__device__ __forceinline__ void transpose_block(const uint4 (&in)[4], uint4 (&out)[4]) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(in);  // w[4*r + c]
+  uint32_t* o = reinterpret_cast<uint32_t*>(out);             // o[4*c + r]
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[4 * c + r] = w[4 * r + c];
+}
+
+// Grouped GEMM, C_g = A_g B_g for the problems of `batch` (blockIdx.y picks
+// problem and contraction split).  128 x BN tile on four waves (2 x 2), each
+// wave 64 x BN/2 as 16 x 16 MFMA tiles.  The MFMA is issued with the B tile
+// as its row operand, so each lane ends with four consecutive output columns
+// of one row (lane (g, c16): row c16, columns 4g .. 4g+3 of each 16 x 16
+// tile) and the epilogue stores straight from registers.
 template <typename TC, int BM, int BN, bool A_KC, bool B_KC, int EPI>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmBatch batch) {
   typedef GF<TC> F;
+  constexpr int BK = GemmStep<TC>::BK;
   constexpr int E = 16 / sizeof(TC);  // elements per 16-byte word
   constexpr int LDK = BK + F::PAD;    // LDS row pitch of an operand tile (elements)
-  constexpr int TM = BM / 32, TN = BN / 32;  // 16 x 16 tiles per wave (2 x 2 waves)
-  constexpr size_t OPS_BYTES = 2 * static_cast<size_t>(BM + BN) * LDK * sizeof(TC);
-  constexpr int LDC = BN + 4;  // fp32 pitch of the staged output tile
-  constexpr size_t EPI_BYTES = static_cast<size_t>(BM) * LDC * 4;
-  constexpr size_t SMEM = OPS_BYTES > EPI_BYTES ? OPS_BYTES : EPI_BYTES;
-  __shared__ __align__(16) char smem[SMEM];
-  TC* sA = reinterpret_cast<TC*>(smem);                          // [2][BM][LDK]
-  TC* sB = reinterpret_cast<TC*>(smem) + 2 * BM * LDK;           // [2][BN][LDK]
-  float* sC = reinterpret_cast<float*>(smem);                    // [BM][LDC] after the main loop
+  constexpr int TM = BM / 32, TN = BN / 32;  // 16 x 16 tiles per wave
+  __shared__ __align__(16) TC sA[BM * LDK];
+  __shared__ __align__(16) TC sB[BN * LDK];
 
-  const int grp = blockIdx.z / batch.ksplit;
-  const int split = blockIdx.z - grp * batch.ksplit;
+  const int grp = blockIdx.y / batch.ksplit;
+  const int split = blockIdx.y - grp * batch.ksplit;
   const GemmProblem& P = batch.p[grp];
-  const int m0 = blockIdx.x * BM;
-  const int n0 = blockIdx.y * BN;
-  if (m0 >= P.M || n0 >= P.N) return;
-  const int kchunk = batch.kchunk;
-  const int kbeg = split * kchunk;
-  const int kend = min(P.K, kbeg + kchunk);
+  // XCD-aware tile order: consecutive workgroup ids go to different XCDs, so
+  // each XCD is given a contiguous run of tiles, n fastest: the A rows of a
+  // tile row are then reused from that XCD's L2.
+  // (The grid's x extent is a multiple of 8, so blockIdx.x % 8 is the XCD.)
+  const int mt = (P.M + BM - 1) / BM, nt = (P.N + BN - 1) / BN;
+  const int ntile = mt * nt;
+  const int per_xcd = (ntile + 7) / 8;
+  const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (static_cast<int>(blockIdx.x / 8) >= per_xcd || t >= ntile) return;
+  const int m0 = (t / nt) * BM;
+  const int n0 = (t % nt) * BN;
+  const int kbeg = split * batch.kchunk;
+  const int kend = min(P.K, kbeg + batch.kchunk);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -116,91 +180,85 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmBatch batch) {
   const TC* __restrict__ gB = static_cast<const TC*>(P.B);
 
   // ---- global -> register staging --------------------------------------------
-  // k-contiguous operand: R rows of BK values, 16-byte words.
-  constexpr int KC_WORDS_A = BM * BK / E / GEMM_THREADS;
-  constexpr int KC_WORDS_B = BN * BK / E / GEMM_THREADS;
-  // k-strided operand: pairs of k rows x E columns.
-  constexpr int KS_ITEMS_A = (BK / 2) * (BM / E) / GEMM_THREADS;
-  constexpr int KS_ITEMS_B = (BK / 2) * (BN / E) / GEMM_THREADS;
-  constexpr int NA = A_KC ? KC_WORDS_A : 2 * KS_ITEMS_A;
-  constexpr int NB = B_KC ? KC_WORDS_B : 2 * KS_ITEMS_B;
-  static_assert(NA >= 1 && NB >= 1, "tile too small for the thread count");
-  uint4 ra[NA], rb[NB];
+  // k-contiguous operand: R rows of BK values as 16-byte words, 8 per row
+  // (row r, word w at tile index r * 8 + w).
+  constexpr int KCW_A = BM * BK / E / GEMM_THREADS, KCW_B = BN * BK / E / GEMM_THREADS;
+  // k-strided operand: blocks of KR k rows x E columns, staged by up to 128
+  // threads each (A: threads 0.., B: 128.. when A is k-strided too, else 0..).
+  constexpr int KR = 16 / sizeof(TC);
+  constexpr int KSB_A = (BK / KR) * (BM / E), KSB_B = (BK / KR) * (BN / E);
+  constexpr int KST_A = KSB_A < 128 ? KSB_A : 128, KST_B = KSB_B < 128 ? KSB_B : 128;
+  static_assert(A_KC || KSB_A % KST_A == 0, "k-strided A tile must split over its threads");
+  static_assert(B_KC || KSB_B % KST_B == 0, "k-strided B tile must split over its threads");
+  constexpr int KS_PER_A = A_KC ? 0 : KSB_A / KST_A;
+  constexpr int KS_PER_B = B_KC ? 0 : KSB_B / KST_B;
+  constexpr int NRA = A_KC ? KCW_A : KS_PER_A * KR;
+  constexpr int NRB = B_KC ? KCW_B : KS_PER_B * KR;
+  static_assert(NRA >= 1 && NRB >= 1, "tile too small for the thread count");
+  uint4 ra[NRA], rb[NRB];
+  constexpr int B_BASE = A_KC ? 0 : 128;
+  const bool a_ks_thread = !A_KC && tid < KST_A;
+  const bool b_ks_thread = !B_KC && tid >= B_BASE && tid < B_BASE + KST_B;
 
-  auto load_kc = [&](const TC* g, int ld, int rows_valid, int r0, int k0, uint4* r, int nwords) {
-    constexpr int WPR = BK / E;  // words per row
-    for (int w = 0; w < nwords; ++w) {
+  auto load_kc = [&](const TC* g, int ld, int rows_valid, int r0, int k0, uint4* r, int nw) {
+    constexpr int WPR = BK / E;
+    for (int w = 0; w < nw; ++w) {
       const int idx = tid + w * GEMM_THREADS;
       const int row = idx / WPR;
-      const int kk = (idx - row * WPR) * E;
-      const int gr = r0 + row;
-      const int gk = k0 + kk;
+      const int gk = k0 + (idx % WPR) * E;
       uint4 v = {0u, 0u, 0u, 0u};
-      if (gr < rows_valid && gk < kend) v = *reinterpret_cast<const uint4*>(g + static_cast<size_t>(gr) * ld + gk);
+      if (r0 + row < rows_valid && gk < kend)
+        v = *reinterpret_cast<const uint4*>(g + static_cast<size_t>(r0 + row) * ld + gk);
       r[w] = v;
     }
   };
-  auto load_ks = [&](const TC* g, int ld, int cols_valid, int c0, int k0, uint4* r, int nitems, int R) {
-    const int CPR = R / E;  // column words per k row
-    for (int it = 0; it < nitems; ++it) {
-      const int idx = tid + it * GEMM_THREADS;
-      const int kp = idx / CPR;
-      const int cw = idx - kp * CPR;
-      const int gk = k0 + 2 * kp;
-      const int gc = c0 + cw * E;
-      uint4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
-      if (gc < cols_valid) {
-        if (gk < kend) v0 = *reinterpret_cast<const uint4*>(g + static_cast<size_t>(gk) * ld + gc);
-        if (gk + 1 < kend) v1 = *reinterpret_cast<const uint4*>(g + static_cast<size_t>(gk + 1) * ld + gc);
-      }
-      r[2 * it] = v0;
-      r[2 * it + 1] = v1;
-    }
-  };
-  auto store_kc = [&](TC* s, const uint4* r, int nwords) {
+  auto store_kc = [&](TC* s, const uint4* r, int nw) {
     constexpr int WPR = BK / E;
-    for (int w = 0; w < nwords; ++w) {
+    for (int w = 0; w < nw; ++w) {
       const int idx = tid + w * GEMM_THREADS;
-      const int row = idx / WPR;
-      const int kk = (idx - row * WPR) * E;
-      *reinterpret_cast<uint4*>(s + row * LDK + kk) = r[w];
+      *reinterpret_cast<uint4*>(s + (idx / WPR) * LDK + (idx % WPR) * E) = r[w];
     }
   };
-  // k-strided words land transposed: column c's values for k and k+1 side by side.
-  auto store_ks = [&](TC* s, const uint4* r, int nitems, int R) {
-    const int CPR = R / E;
-    for (int it = 0; it < nitems; ++it) {
-      const int idx = tid + it * GEMM_THREADS;
-      const int kp = idx / CPR;
-      const int cw = idx - kp * CPR;
-      const TC* v0 = reinterpret_cast<const TC*>(&r[2 * it]);
-      const TC* v1 = reinterpret_cast<const TC*>(&r[2 * it + 1]);
+  // block b: k block kb = b % (BK / KR) (so the 8 lanes of a store phase write
+  // different k blocks of one column group: no LDS bank conflicts), column
+  // block cb = b / (BK / KR).
+  auto load_ks = [&](const TC* g, int ld, int cols_valid, int c0, int k0, uint4* r, int nb, int ks_tid, int nthr) {
+    for (int i = 0; i < nb; ++i) {
+      const int b = ks_tid + i * nthr;
+      const int kb = b % (BK / KR), cb = b / (BK / KR);
+      const int gc = c0 + cb * E;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        TC* dst = s + (cw * E + e) * LDK + 2 * kp;
-        if constexpr (sizeof(TC) == 2) {
-          const uint32_t pr = static_cast<uint32_t>(v0[e]) | (static_cast<uint32_t>(v1[e]) << 16);
-          *reinterpret_cast<uint32_t*>(dst) = pr;
-        } else {
-          f32x2 pr = {v0[e], v1[e]};
-          *reinterpret_cast<f32x2*>(dst) = pr;
-        }
+      for (int rr = 0; rr < KR; ++rr) {
+        const int gk = k0 + kb * KR + rr;
+        uint4 v = {0u, 0u, 0u, 0u};
+        if (gc < cols_valid && gk < kend) v = *reinterpret_cast<const uint4*>(g + static_cast<size_t>(gk) * ld + gc);
+        r[i * KR + rr] = v;
       }
+    }
+  };
+  auto store_ks = [&](TC* s, const uint4* r, int nb, int ks_tid, int nthr) {
+    for (int i = 0; i < nb; ++i) {
+      const int b = ks_tid + i * nthr;
+      const int kb = b % (BK / KR), cb = b / (BK / KR);
+      uint4 in[KR], out[KR];
+#pragma unroll
+      for (int rr = 0; rr < KR; ++rr) in[rr] = r[i * KR + rr];
+      transpose_block(in, out);
+#pragma unroll
+      for (int c = 0; c < E; ++c) *reinterpret_cast<uint4*>(s + (cb * E + c) * LDK + kb * KR) = out[c];
     }
   };
   auto load_tiles = [&](int k0) {
-    if constexpr (A_KC) load_kc(gA, P.lda, P.M, m0, k0, ra, NA);
-    else load_ks(gA, P.lda, P.M, m0, k0, ra, KS_ITEMS_A, BM);
-    if constexpr (B_KC) load_kc(gB, P.ldb, P.N, n0, k0, rb, NB);
-    else load_ks(gB, P.ldb, P.N, n0, k0, rb, KS_ITEMS_B, BN);
+    if constexpr (A_KC) load_kc(gA, P.lda, P.M, m0, k0, ra, NRA);
+    else if (a_ks_thread) load_ks(gA, P.lda, P.M, m0, k0, ra, KS_PER_A, tid, KST_A);
+    if constexpr (B_KC) load_kc(gB, P.ldb, P.N, n0, k0, rb, NRB);
+    else if (b_ks_thread) load_ks(gB, P.ldb, P.N, n0, k0, rb, KS_PER_B, tid - B_BASE, KST_B);
   };
-  auto store_tiles = [&](int buf) {
-    TC* a = sA + buf * BM * LDK;
-    TC* b = sB + buf * BN * LDK;
-    if constexpr (A_KC) store_kc(a, ra, NA);
-    else store_ks(a, ra, KS_ITEMS_A, BM);
-    if constexpr (B_KC) store_kc(b, rb, NB);
-    else store_ks(b, rb, KS_ITEMS_B, BN);
+  auto store_tiles = [&]() {
+    if constexpr (A_KC) store_kc(sA, ra, NRA);
+    else if (a_ks_thread) store_ks(sA, ra, KS_PER_A, tid, KST_A);
+    if constexpr (B_KC) store_kc(sB, rb, NRB);
+    else if (b_ks_thread) store_ks(sB, rb, KS_PER_B, tid - B_BASE, KST_B);
   };
 
   f32x4 acc[TM][TN];
@@ -210,112 +268,250 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmBatch batch) {
     for (int j = 0; j < TN; ++j) acc[i][j] = zero4();
 
   const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
-  if (nk > 0) {
-    load_tiles(kbeg);
-    store_tiles(0);
-  }
-  __syncthreads();
   const int fr = lane & 15;
   const int fk = (F::KF / 4) * (lane >> 4);
+  if (nk > 0) load_tiles(kbeg);
   for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) load_tiles(kbeg + (kt + 1) * BK);
-    const TC* a = sA + (kt & 1) * BM * LDK;
-    const TC* b = sB + (kt & 1) * BN * LDK;
+    store_tiles();
+    __syncthreads();
+    if (kt + 1 < nk) load_tiles(kbeg + (kt + 1) * BK);  // lands while this step computes
 #pragma unroll
     for (int ks = 0; ks < BK; ks += F::KF) {
       typename F::frag fa[TM], fb[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = F::load(a + (wm + 16 * i + fr) * LDK + ks + fk);
+      for (int i = 0; i < TM; ++i) fa[i] = F::load(sA + (wm + 16 * i + fr) * LDK + ks + fk);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = F::load(b + (wn + 16 * j + fr) * LDK + ks + fk);
+      for (int j = 0; j < TN; ++j) fb[j] = F::load(sB + (wn + 16 * j + fr) * LDK + ks + fk);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = F::mma(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = F::mma(fb[j], fa[i], acc[i][j]);
     }
-    if (more) store_tiles((kt + 1) & 1);
     __syncthreads();
   }
 
-  // ---- epilogue: stage the fp32 tile in LDS, then write coalesced -------------
-  // accumulator (i, j) of the wave: rows wm+16i + 4*(lane/16) + r, column wn+16j + lane%16
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sC[(wm + 16 * i + 4 * (lane >> 4) + r) * LDC + wn + 16 * j + fr] = acc[i][j][r];
-  __syncthreads();
-
+  // ---- epilogue, from registers ------------------------------------------------
+  // acc[i][j][r] = C[m0 + wm + 16i + fr][n0 + wn + 16j + 4g + r], g = lane / 16
+  const int g4 = 4 * (lane >> 4);
   if constexpr (EPI == EPI_PARTIAL) {
     float* out = static_cast<float*>(P.C) + static_cast<size_t>(split) * batch.split_stride;
-    constexpr int WPR = BN / 4;
-    for (int idx = tid; idx < BM * WPR; idx += GEMM_THREADS) {
-      const int row = idx / WPR;
-      const int c = (idx - row * WPR) * 4;
-      if (m0 + row < P.M && n0 + c < P.N) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(sC + row * LDC + c);
-        *reinterpret_cast<f32x4*>(out + static_cast<size_t>(m0 + row) * P.ldc + n0 + c) = v;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int gm = m0 + wm + 16 * i + fr;
+      if (gm >= P.M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int gn = n0 + wn + 16 * j + g4;
+        if (gn < P.N) *reinterpret_cast<f32x4*>(out + static_cast<size_t>(gm) * P.ldc + gn) = acc[i][j];
       }
     }
   } else {
-    // 8 (bf16) or 4 (fp32) consecutive columns per thread and row
-    constexpr int WPR = BN / E;
-    constexpr int ROWS_PER_PASS = GEMM_THREADS / WPR;
-    const int cw = tid % WPR;
-    const int rr = tid / WPR;
-    const int c = cw * E;
-    const bool col_ok = n0 + c < P.N;
-    float bias[E];
-    int act = P.act;
-    if constexpr (EPI == EPI_GATE || EPI == EPI_GATE_BWD) {
-      const TC* bp = static_cast<const TC*>(P.bias);
-#pragma unroll
-      for (int e = 0; e < E; ++e) bias[e] = col_ok ? Elem<TC>::load(bp, n0 + c + e) : 0.f;
-    }
-    float csum[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) csum[e] = 0.f;
     TC* out = static_cast<TC*>(P.C);
-    for (int row = rr; row < BM; row += ROWS_PER_PASS) {
-      const int gm = m0 + row;
-      if (gm >= P.M || !col_ok) continue;
-      float v[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) v[e] = sC[row * LDC + c + e];
-      const size_t o = static_cast<size_t>(gm) * P.ldc + n0 + c;
-      if constexpr (EPI == EPI_GATE) {
+    for (int i = 0; i < TM; ++i) {
+      const int gm = m0 + wm + 16 * i + fr;
+      if (gm >= P.M) continue;
 #pragma unroll
-        for (int e = 0; e < E; ++e) v[e] = act_fwd(act, v[e] + bias[e]);
-      } else if constexpr (EPI == EPI_GATE_BWD) {
-        uint4 graw = *reinterpret_cast<const uint4*>(static_cast<const TC*>(P.dG) + o);
-        const TC* gv = reinterpret_cast<const TC*>(&graw);
+      for (int j = 0; j < TN; ++j) {
+        const int gn = n0 + wn + 16 * j + g4;
+        if (gn < P.N) store4(out + static_cast<size_t>(gm) * P.ldc + gn, acc[i][j]);
+      }
+    }
+  }
+}
+
+// Activation as a template argument (one instance per gate form).
+template <int ACT> __device__ __forceinline__ float act_fwd_t(float x) { return act_fwd(ACT, x); }
+template <int ACT> __device__ __forceinline__ float act_grad_t(float x) { return act_grad(ACT, x); }
+
+// The gates' up-projections (contraction over one gate's rank, 64 or 128):
+// C = z_i U_i^T + c_i with an activation epilogue (EPI_GATE) or its gradient
+// (EPI_GATE_BWD).  One 128 x 64 output tile per workgroup of 4 waves; wave w
+// owns rows 32 w .. +31 and all 64 columns.  Every load is issued up front --
+// the wave's rows of z straight into MFMA fragments, the tile of U_i (64 rows
+// of [width, rank], rank contiguous) into LDS, and the backward's upstream
+// gradients -- and the stores come last, so no wait on a load ever sits
+// behind this workgroup's own stores (loads and stores share one counter).
+// The gradient tile is read, and the output tile written, through an LDS
+// staging tile in whole 128-byte rows (8 lanes per row), not in the MFMA
+// layout's 32-byte pieces.  blockIdx.y: the gate; blockIdx.x: the tile (row
+// tiles fastest within a column tile, so the tile of U_i is reused from L2).
+template <typename TC, int EPI>
+__global__ __launch_bounds__(UP_THREADS) void gate_up_kernel(GateUpArgs<TC> a) {
+  typedef GF<TC> F;
+  constexpr int E = 16 / sizeof(TC);
+  constexpr int RMAX = 128;
+  constexpr int LDK = RMAX + F::PAD;
+  constexpr int BM = 128, BN = UP_BN, TM = 2, TN = BN / 16;
+  constexpr int KSTEPS = RMAX / F::KF;
+  constexpr int MAXW = BN * (RMAX / E) / UP_THREADS;  // 16-byte words of the U tile per thread
+  constexpr int LDS_ = BN + E;                         // staging pitch (elements): one 16-byte pad per row
+  constexpr int WPR = BN / E;                          // 16-byte words per staged row
+  constexpr int SW = BM * WPR / UP_THREADS;            // staged words per thread
+  __shared__ __align__(16) TC sB[BN * LDK];
+  __shared__ __align__(16) TC sS[BM * LDS_];
+  __shared__ float red[4 * BN];
+
+  const int gi = blockIdx.y;
+  const int r = a.r[gi];
+  const int W = a.W[gi];
+  const int mt = (a.M + BM - 1) / BM;
+  const int ntile = mt * (W / BN);
+  if (static_cast<int>(blockIdx.x) >= ntile) return;
+  const int mtile = blockIdx.x % mt;
+  const int m0 = mtile * BM, n0 = (blockIdx.x / mt) * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = 32 * wave;
+  const int fr = lane & 15, fk = (F::KF / 4) * (lane >> 4), g4 = 4 * (lane >> 4);
+  const TC* __restrict__ z = a.z + a.zoff[gi];
+  const TC* __restrict__ U = a.U + a.woff[gi];
+  const TC* __restrict__ bias = a.bias + a.boff[gi];
+  TC* __restrict__ out = a.out[gi];
+  const int ksteps = r / F::KF;
+  // staged words of this wave's 32 rows: word s of the thread is row
+  // wm + s * (64 / WPR) + lane / WPR, columns (lane % WPR) * E ..
+  auto srow = [&](int sw) { return wm + sw * (64 / WPR) + lane / WPR; };
+  const int scol = (lane % WPR) * E;
+
+  // loads: U tile (to registers, then LDS), this wave's rows of z, dG
+  const int wpr = r / E;
+  const int nwords = BN * wpr;
+  uint4 rb[MAXW];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          v[e] = Elem<TC>::load(gv, e) * act_grad(act, v[e] + bias[e]);
-          csum[e] += v[e];
+  for (int w = 0; w < MAXW; ++w) {
+    const int idx = tid + w * UP_THREADS;
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (idx < nwords) v = *reinterpret_cast<const uint4*>(U + static_cast<size_t>(n0 + idx / wpr) * r + (idx % wpr) * E);
+    rb[w] = v;
+  }
+  typename F::frag fa[TM][KSTEPS];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int gm = m0 + wm + 16 * i + fr;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (gm < a.M && ks < ksteps)
+        v = *reinterpret_cast<const uint4*>(z + static_cast<size_t>(gm) * GATE_RTOT + ks * F::KF + fk);
+      fa[i][ks] = __builtin_bit_cast(typename F::frag, v);
+    }
+  }
+  uint4 dgw[SW];
+  if constexpr (EPI == EPI_GATE_BWD) {
+    const TC* dG = a.dG[gi] + n0 + scol;
+#pragma unroll
+    for (int sw = 0; sw < SW; ++sw) {
+      const int gm = min(m0 + srow(sw), a.M - 1);  // rows past M are read but not used
+      dgw[sw] = *reinterpret_cast<const uint4*>(dG + static_cast<size_t>(gm) * W);
+    }
+  }
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w) {
+    const int idx = tid + w * UP_THREADS;
+    if (idx < nwords) *reinterpret_cast<uint4*>(&sB[(idx / wpr) * LDK + (idx % wpr) * E]) = rb[w];
+  }
+  if constexpr (EPI == EPI_GATE_BWD) {
+#pragma unroll
+    for (int sw = 0; sw < SW; ++sw) *reinterpret_cast<uint4*>(&sS[srow(sw) * LDS_ + scol]) = dgw[sw];
+  }
+  __syncthreads();
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = zero4();
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    if (ks < ksteps) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const typename F::frag fb = F::load(&sB[(16 * j + fr) * LDK + ks * F::KF + fk]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) acc[i][j] = F::mma(fb, fa[i][ks], acc[i][j]);
+      }
+    }
+  }
+
+  // epilogue in the MFMA layout (lane: row wm + 16i + fr, columns 16j + 4g ..
+  // + 3 of the tile), through this wave's rows of the staging tile
+  auto epilogue = [&](auto act_tag) {
+    constexpr int ACT = decltype(act_tag)::value;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int c = 16 * j + g4;
+      const f32x4 bv = load4(bias + n0 + c);
+      float cs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm + 16 * i + fr;
+        f32x4 v = acc[i][j];
+        if constexpr (EPI == EPI_GATE) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = act_fwd_t<ACT>(v[q] + bv[q]);
+        } else {
+          const f32x4 gv = load4(&sS[row * LDS_ + c]);
+          const bool row_ok = m0 + row < a.M;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[q] = gv[q] * act_grad_t<ACT>(v[q] + bv[q]);
+            cs[q] += row_ok ? v[q] : 0.f;
+          }
+        }
+        store4(&sS[row * LDS_ + c], v);
+      }
+      if constexpr (EPI == EPI_GATE_BWD) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float sm = sum16(cs[q]);
+          if (fr == 0) red[wave * BN + c + q] = sm;
         }
       }
-      uint4 w;
-      TC* wv = reinterpret_cast<TC*>(&w);
-#pragma unroll
-      for (int e = 0; e < E; ++e) Elem<TC>::store(wv, e, v[e]);
-      *reinterpret_cast<uint4*>(out + o) = w;
     }
-    if constexpr (EPI == EPI_GATE_BWD) {
-      // column sums of this tile's dpre: reduce the ROWS_PER_PASS row groups in LDS
-      __syncthreads();
-      float* red = sC;  // [ROWS_PER_PASS][BN]
+  };
+  switch (a.act[gi]) {
+    case GATE_ACT_LOGSIG: epilogue(std::integral_constant<int, GATE_ACT_LOGSIG>{}); break;
+    case GATE_ACT_SIG: epilogue(std::integral_constant<int, GATE_ACT_SIG>{}); break;
+    case GATE_ACT_SIG2: epilogue(std::integral_constant<int, GATE_ACT_SIG2>{}); break;
+    default: epilogue(std::integral_constant<int, GATE_ACT_NONE>{}); break;
+  }
+  // this wave's rows back out in whole rows (the wave wrote them itself: LDS
+  // operations of one wave complete in order)
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  TC* o = out + n0 + scol;
 #pragma unroll
-      for (int e = 0; e < E; ++e) red[rr * BN + c + e] = csum[e];
-      __syncthreads();
-      if (tid < BN && n0 + tid < P.N) {
-        float s = 0.f;
-        for (int g = 0; g < ROWS_PER_PASS; ++g) s += red[g * BN + tid];
-        batch.colsum[static_cast<size_t>(blockIdx.x) * batch.colsum_ld + P.colsum_off + n0 + tid] = s;
-      }
-    }
+  for (int sw = 0; sw < SW; ++sw) {
+    const int row = srow(sw);
+    if (m0 + row < a.M)
+      *reinterpret_cast<uint4*>(o + static_cast<size_t>(m0 + row) * W) =
+          *reinterpret_cast<const uint4*>(&sS[row * LDS_ + scol]);
+  }
+  if constexpr (EPI == EPI_GATE_BWD) {
+    // column sums of the tile's dpre: the four waves' partial sums
+    __syncthreads();
+    if (tid < BN)
+      a.colsum[static_cast<size_t>(mtile) * a.colsum_ld + a.csoff[gi] + n0 + tid] =
+          red[tid] + red[BN + tid] + red[2 * BN + tid] + red[3 * BN + tid];
+  }
+}
+
+// Column sums of a [rows][ncols] fp32 array (the bias gradient from the
+// per-row-tile partial sums): 32 columns per block, the rows split over 8
+// thread groups, then combined in LDS in a fixed order.
+__global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ part, int rows, int ncols,
+                                                     float* __restrict__ out) {
+  __shared__ float red[8][32];
+  const int c = blockIdx.x * 32 + (threadIdx.x & 31);
+  const int g = threadIdx.x >> 5;
+  float s = 0.f;
+  if (c < ncols)
+    for (int r = g; r < rows; r += 8) s += part[static_cast<size_t>(r) * ncols + c];
+  red[g][threadIdx.x & 31] = s;
+  __syncthreads();
+  if (threadIdx.x < 32 && c < ncols) {
+    float t = 0.f;
+    for (int k = 0; k < 8; ++k) t += red[k][threadIdx.x];
+    out[c] = t;
   }
 }
 
@@ -392,14 +588,12 @@ __global__ __launch_bounds__(256) void qk_norm_bwd_kernel(const TC* __restrict__
 
 template <typename TC, int BM, int BN, bool A_KC, bool B_KC, int EPI>
 hipError_t run_gemm(const GemmBatch& b, hipStream_t stream) {
-  int mt = 0, nt = 0;
-  for (int i = 0; i < b.n; ++i) {
-    mt = std::max(mt, (b.p[i].M + BM - 1) / BM);
-    nt = std::max(nt, (b.p[i].N + BN - 1) / BN);
-  }
-  if (mt == 0 || nt == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<TC, BM, BN, A_KC, B_KC, EPI>), dim3(mt, nt, b.n * b.ksplit), dim3(GEMM_THREADS),
-                     0, stream, b);
+  int tiles = 0;
+  for (int i = 0; i < b.n; ++i) tiles = std::max(tiles, ((b.p[i].M + BM - 1) / BM) * ((b.p[i].N + BN - 1) / BN));
+  if (tiles == 0) return hipSuccess;
+  const int grid = (tiles + 7) / 8 * 8;  // whole rounds of the 8 XCDs
+  hipLaunchKernelGGL((gemm_kernel<TC, BM, BN, A_KC, B_KC, EPI>), dim3(grid, b.n * b.ksplit), dim3(GEMM_THREADS), 0,
+                     stream, b);
   return hipGetLastError();
 }
 
@@ -439,6 +633,33 @@ GateLayout gate_layout(const GateShape& s) {
 const int kActs[5] = {GATE_ACT_LOGSIG, GATE_ACT_SIG, GATE_ACT_SIG, GATE_ACT_SIG, GATE_ACT_SIG2};
 
 template <typename TC>
+GateUpArgs<TC> gate_up_args(const GateLayout& L, const TC* z, const TC* U, const TC* bias) {
+  GateUpArgs<TC> u = {};
+  u.z = z;
+  u.U = U;
+  u.bias = bias;
+  u.M = L.M;
+  for (int i = 0; i < 5; ++i) {
+    u.r[i] = L.r[i];
+    u.W[i] = L.W[i];
+    u.zoff[i] = L.zoff[i];
+    u.woff[i] = L.woff[i];
+    u.boff[i] = L.boff[i];
+    u.act[i] = kActs[i];
+  }
+  return u;
+}
+
+template <typename TC, int EPI>
+hipError_t run_gate_up(const GateUpArgs<TC>& u, hipStream_t stream) {
+  int gx = 0;
+  for (int i = 0; i < 5; ++i) gx = std::max(gx, ((u.M + 127) / 128) * (u.W[i] / UP_BN));
+  if (gx == 0) return hipSuccess;
+  hipLaunchKernelGGL((gate_up_kernel<TC, EPI>), dim3(gx, 5), dim3(UP_THREADS), 0, stream, u);
+  return hipGetLastError();
+}
+
+template <typename TC>
 hipError_t gate_fwd_typed(const GateShape& s, const void* x, const void* W_down, const void* W_up, const void* bias,
                           void* z, void* const gates[5], hipStream_t stream) {
   const GateLayout L = gate_layout(s);
@@ -448,21 +669,12 @@ hipError_t gate_fwd_typed(const GateShape& s, const void* x, const void* W_down,
   b.n = 1;
   b.ksplit = 1;
   b.kchunk = s.d;
-  b.p[0] = GemmProblem{x, W_down, z, s.M, GATE_RTOT, s.d, s.d, GATE_RTOT, GATE_RTOT};
-  hipError_t e = run_gemm<TC, 128, 128, true, false, EPI_STORE>(b, stream);
+  b.p[0] = GemmProblem{x, W_down, z, s.M, GATE_RTOT, s.d, s.d, s.d, GATE_RTOT};  // z = x W_down^T
+  hipError_t e = run_gemm<TC, 128, 128, true, true, EPI_STORE>(b, stream);
   if (e != hipSuccess) return e;
-  GemmBatch u = {};
-  u.n = 5;
-  u.ksplit = 1;
-  u.kchunk = 128;
-  for (int i = 0; i < 5; ++i) {
-    GemmProblem& p = u.p[i];
-    p = GemmProblem{static_cast<const TC*>(z) + L.zoff[i], Wu + L.woff[i], gates[i], s.M, L.W[i], L.r[i],
-                    GATE_RTOT, L.W[i], L.W[i]};
-    p.bias = bs + L.boff[i];
-    p.act = kActs[i];
-  }
-  return run_gemm<TC, 128, 128, true, false, EPI_GATE>(u, stream);
+  GateUpArgs<TC> u = gate_up_args<TC>(L, static_cast<const TC*>(z), Wu, bs);
+  for (int i = 0; i < 5; ++i) u.out[i] = static_cast<TC*>(gates[i]);
+  return run_gate_up<TC, EPI_GATE>(u, stream);
 }
 
 template <typename TC>
@@ -486,8 +698,8 @@ hipError_t gate_bwd_typed(const GateShape& s, const void* x, const void* W_down,
     b.n = 1;
     b.ksplit = 1;
     b.kchunk = s.d;
-    b.p[0] = GemmProblem{x, W_down, z, s.M, GATE_RTOT, s.d, s.d, GATE_RTOT, GATE_RTOT};
-    if ((e = run_gemm<TC, 128, 128, true, false, EPI_STORE>(b, stream)) != hipSuccess) return e;
+    b.p[0] = GemmProblem{x, W_down, z, s.M, GATE_RTOT, s.d, s.d, s.d, GATE_RTOT};
+    if ((e = run_gemm<TC, 128, 128, true, true, EPI_STORE>(b, stream)) != hipSuccess) return e;
     zr = z;
   }
   size_t dpo[5];
@@ -498,53 +710,46 @@ hipError_t gate_bwd_typed(const GateShape& s, const void* x, const void* W_down,
   }
   // 1. dpre_i = dG_i * act'(z_i U_i + c_i), with per-tile column sums
   {
-    GemmBatch u = {};
-    u.n = 5;
-    u.ksplit = 1;
-    u.kchunk = 128;
+  GateUpArgs<TC> u = gate_up_args<TC>(L, zr, Wu, bs);
     u.colsum = csum;
     u.colsum_ld = W.colsum_ld;
     int coff = 0;
     for (int i = 0; i < 5; ++i) {
-      GemmProblem& p = u.p[i];
-      p = GemmProblem{zr + L.zoff[i], Wu + L.woff[i], dpre + dpo[i], s.M, L.W[i], L.r[i], GATE_RTOT, L.W[i],
-                      L.W[i]};
-      p.bias = bs + L.boff[i];
-      p.act = kActs[i];
-      p.dG = dgates[i];
-      p.colsum_off = coff;
+      u.out[i] = dpre + dpo[i];
+      u.dG[i] = static_cast<const TC*>(dgates[i]);
+      u.csoff[i] = coff;
       coff += L.W[i];
     }
-    if ((e = run_gemm<TC, 128, 128, true, false, EPI_GATE_BWD>(u, stream)) != hipSuccess) return e;
+    if ((e = run_gate_up<TC, EPI_GATE_BWD>(u, stream)) != hipSuccess) return e;
   }
-  // 2. dz[:, slice_i] = dpre_i U_i^T
+  // 2. dz[:, slice_i] = dpre_i U_i
   {
     GemmBatch u = {};
     u.n = 5;
     u.ksplit = 1;
     u.kchunk = std::max(L.W[0], L.W[2]);
     for (int i = 0; i < 5; ++i)
-      u.p[i] = GemmProblem{dpre + dpo[i], Wu + L.woff[i], dz + L.zoff[i], s.M, L.r[i], L.W[i], L.W[i], L.W[i],
+      u.p[i] = GemmProblem{dpre + dpo[i], Wu + L.woff[i], dz + L.zoff[i], s.M, L.r[i], L.W[i], L.W[i], L.r[i],
                            GATE_RTOT};
-    if ((e = run_gemm<TC, 128, 64, true, true, EPI_STORE>(u, stream)) != hipSuccess) return e;
+    if ((e = run_gemm<TC, 128, 64, true, false, EPI_STORE>(u, stream)) != hipSuccess) return e;
   }
-  // 3. dx = dz W_down^T
+  // 3. dx = dz W_down
   {
     GemmBatch b = {};
     b.n = 1;
     b.ksplit = 1;
     b.kchunk = GATE_RTOT;
-    b.p[0] = GemmProblem{dz, W_down, dx, s.M, s.d, GATE_RTOT, GATE_RTOT, GATE_RTOT, s.d};
-    if ((e = run_gemm<TC, 128, 128, true, true, EPI_STORE>(b, stream)) != hipSuccess) return e;
+    b.p[0] = GemmProblem{dz, W_down, dx, s.M, s.d, GATE_RTOT, GATE_RTOT, s.d, s.d};
+    if ((e = run_gemm<TC, 128, 128, true, false, EPI_STORE>(b, stream)) != hipSuccess) return e;
   }
-  // 4. dW_down = x^T dz (split over tokens), 5. dW_up_i = z_i^T dpre_i (split over tokens)
+  // 4. dW_down = dz^T x (split over tokens), 5. dW_up_i = dpre_i^T z_i (split over tokens)
   {
     GemmBatch b = {};
     b.n = 1;
     b.ksplit = W.ksplit;
     b.kchunk = W.kchunk;
     b.split_stride = W.part_stride;
-    b.p[0] = GemmProblem{x, dz, part, s.d, GATE_RTOT, s.M, s.d, GATE_RTOT, GATE_RTOT};
+    b.p[0] = GemmProblem{dz, x, part, GATE_RTOT, s.d, s.M, GATE_RTOT, s.d, s.d};
     if ((e = run_gemm<TC, 128, 128, false, false, EPI_PARTIAL>(b, stream)) != hipSuccess) return e;
     const size_t n = static_cast<size_t>(s.d) * GATE_RTOT;
     hipLaunchKernelGGL(split_sum_kernel, dim3(static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 4096))), dim3(256),
@@ -558,9 +763,9 @@ hipError_t gate_bwd_typed(const GateShape& s, const void* x, const void* W_down,
     u.kchunk = W.kchunk;
     u.split_stride = W.part_stride;
     for (int i = 0; i < 5; ++i)
-      u.p[i] = GemmProblem{zr + L.zoff[i], dpre + dpo[i], part + L.woff[i], L.r[i], L.W[i], s.M, GATE_RTOT, L.W[i],
-                           L.W[i]};
-    if ((e = run_gemm<TC, 128, 128, false, false, EPI_PARTIAL>(u, stream)) != hipSuccess) return e;
+      u.p[i] = GemmProblem{dpre + dpo[i], zr + L.zoff[i], part + L.woff[i], L.W[i], L.r[i], s.M, L.W[i], GATE_RTOT,
+                           L.r[i]};
+    if ((e = run_gemm<TC, 128, 64, false, false, EPI_PARTIAL>(u, stream)) != hipSuccess) return e;
     const size_t n = L.woff[4] + static_cast<size_t>(L.r[4]) * L.W[4];
     hipLaunchKernelGGL(split_sum_kernel, dim3(static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 4096))), dim3(256),
                        0, stream, part, W.ksplit, W.part_stride, n, dW_up);
@@ -568,9 +773,8 @@ hipError_t gate_bwd_typed(const GateShape& s, const void* x, const void* W_down,
   }
   // 6. dbias = column sums over the token tiles
   {
-    const size_t n = W.colsum_ld;
-    hipLaunchKernelGGL(split_sum_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, csum,
-                       W.mtiles, static_cast<size_t>(W.colsum_ld), n, dbias);
+    hipLaunchKernelGGL(colsum_kernel, dim3(static_cast<unsigned>((W.colsum_ld + 31) / 32)), dim3(256), 0, stream,
+                       csum, W.mtiles, W.colsum_ld, dbias);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -600,7 +804,7 @@ GateWorkspace gate_workspace(const GateShape& s) {
   // the token contraction of the weight gradients is split so that the
   // launches fill the chip: about 4096 tokens per split, at most 16 splits
   w.ksplit = std::max(1, std::min(16, (s.M + 4095) / 4096));
-  w.kchunk = ((s.M + w.ksplit - 1) / w.ksplit + BK - 1) / BK * BK;
+  w.kchunk = ((s.M + w.ksplit - 1) / w.ksplit + 63) / 64 * 64;  // whole main-loop steps
   const size_t up = L.woff[4] + static_cast<size_t>(L.r[4]) * L.W[4];
   w.part_stride = r256(std::max(static_cast<size_t>(s.d) * GATE_RTOT, up) * 4) / 4;
   w.part_off = off;

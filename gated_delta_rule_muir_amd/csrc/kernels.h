@@ -122,26 +122,20 @@ enum GateAct { GATE_ACT_NONE = 0, GATE_ACT_LOGSIG = 1, GATE_ACT_SIG = 2, GATE_AC
 
 // One product C = A B of a grouped GEMM launch (elements; A is M x K, B is
 // K x N; the kernel instance fixes whether each operand is read along k or
-// across it).  bias / dG / act / colsum_off serve the gate epilogues.
+// across it).
 struct GemmProblem {
   const void* A;
   const void* B;
   void* C;
   int M, N, K;
   int lda, ldb, ldc;
-  const void* bias;
-  const void* dG;
-  int act;
-  int colsum_off;
 };
 struct GemmBatch {
   GemmProblem p[5];
   int n;                // problems in the launch
   int ksplit;           // splits of the contraction (fp32 partials)
-  int kchunk;           // contraction length per split (a multiple of 32)
+  int kchunk;           // contraction length per split
   size_t split_stride;  // floats between the partials of consecutive splits
-  float* colsum;        // per-tile column sums of the gate backward
-  int colsum_ld;
 };
 
 // Sizes of a gate-prologue call: M tokens of width d; H heads of dk key and

@@ -258,8 +258,8 @@ muir_status_t muir_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dt
  * rank slices (64, 64, 128, 128, 128) for the gates (f, b, g, w, q) in that
  * order, each slice up-projected to its gate's width plus a per-channel bias:
  *
- *   z      = x W_down                                   [M, 512]
- *   pre_i  = z[:, slice_i] U_i + c_i
+ *   z      = x W_down^T                                 [M, 512]
+ *   pre_i  = z[:, slice_i] U_i^T + c_i
  *   log_a  = log sigmoid(pre_f)   [M, H, dk]   (decay; <= 0)
  *   erase  = sigmoid(pre_b)       [M, H, dk]
  *   g      = sigmoid(pre_g)       [M, H, dv]   (output gate, used after the operator)
@@ -267,11 +267,12 @@ muir_status_t muir_step(int32_t N, int32_t H, int32_t dk, int32_t dv, int32_t dt
  *   gamma  = 2 sigmoid(pre_q)     [M, H, dk]   (readout gain)
  *
  * The activations are readings (the pages name the gates, not their
- * nonlinearities).  Layouts (row-major, dtype unless stated):
+ * nonlinearities).  Layouts (row-major, dtype unless stated; weights in a
+ * linear layer's [out, in] layout):
  *   x      : [M, d] tokens (M = B * T)
- *   W_down : [d, 512]
- *   W_up   : the five U_i back to back: U_f [64, H*dk], U_b [64, H*dk],
- *            U_g [128, H*dv], U_w [128, H*dv], U_q [128, H*dk]
+ *   W_down : [512, d]
+ *   W_up   : the five U_i back to back: U_f [H*dk, 64], U_b [H*dk, 64],
+ *            U_g [H*dv, 128], U_w [H*dv, 128], U_q [H*dk, 128]
  *   bias   : the five c_i back to back: [H*dk], [H*dk], [H*dv], [H*dv], [H*dk]
  * Supported sizes: d a multiple of 64 up to 65536; dk, dv in {64, 128}.
  */
@@ -296,7 +297,7 @@ size_t muir_gate_proj_bwd_workspace(const muir_gate_dims_t* dims);
 
 /*
  * Backward: from the gradients of the five gates (shaped like the gates,
- * dtype) to dx [M, d] (dtype, overwritten), and dW_down [d, 512], dW_up
+ * dtype) to dx [M, d] (dtype, overwritten), and dW_down [512, d], dW_up
  * and dbias (fp32, packed like W_up and bias, overwritten; sums over tokens
  * in a fixed order).  z is the forward's z, or NULL to recompute it.  Every
  * other pointer is required; the workspace is clobbered.

@@ -152,14 +152,16 @@ def gate_inputs(M: int, d: int, H: int, dk: int, dv: int, *, dtype: str = "bf16"
     matrix ~ N(0, 0.25 / rank); biases ~ N(0, 1) except the decay gate's,
     which put exp(log_a) at exp(-r) for log-uniform rates r in [1e-4, 3]
     per channel (slow and fast rows).  With grads: upstream gradients of the
-    five gates ~ N(0, 1).  Returns CPU tensors in dtype; W_up and bias flat,
-    packed in the gate order (log_a, erase, g, write, gamma)."""
+    five gates ~ N(0, 1).  Returns CPU tensors in dtype; weights in a linear
+    layer's [out, in] layout (W_down [512, d], up matrices [width, rank]);
+    W_up and bias flat, packed in the gate order (log_a, erase, g, write,
+    gamma)."""
     rng = np.random.Generator(np.random.PCG64([seed, 1 << 23]))
     f32 = np.float32
     widths = (H * dk, H * dk, H * dv, H * dv, H * dk)
     x = rng.standard_normal((M, d), dtype=f32)
-    Wd = rng.standard_normal((d, sum(GATE_RANKS)), dtype=f32) / np.sqrt(d)
-    ups = [rng.standard_normal((r, w), dtype=f32) * (0.5 / np.sqrt(r)) for r, w in zip(GATE_RANKS, widths)]
+    Wd = rng.standard_normal((sum(GATE_RANKS), d), dtype=f32) / np.sqrt(d)
+    ups = [rng.standard_normal((w, r), dtype=f32) * (0.5 / np.sqrt(r)) for r, w in zip(GATE_RANKS, widths)]
     rates = np.exp(rng.uniform(np.log(1e-4), np.log(3.0), size=widths[0]))
     biases = [(-np.log(np.expm1(rates))).astype(f32)] + [rng.standard_normal(w, dtype=f32) for w in widths[1:]]
     out = {"x": _cast(x, dtype), "W_down": _cast(Wd.astype(f32), dtype),

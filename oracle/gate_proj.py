@@ -26,10 +26,11 @@ Readings where the pages are silent (each one stated where it is used):
     around 1);
   * L2 normalisation of a head's vector u: u / sqrt(sum u^2 + 1e-6).
 
-Parameter layout: W_down [d, 512]; W_up holds the five up matrices back to
-back, each row-major [r_i, width_i]; bias holds the five bias vectors back
-to back.  Every function here is plain numpy in float64; reverse mode is the
-adjoint of each step, written out by hand.
+Parameter layout, that of a linear layer's weight ([out, in]): W_down
+[512, d] (z = x W_down^T); W_up holds the five up matrices back to back,
+each row-major [width_i, r_i] (pre_i = z_i U_i^T + c_i); bias holds the five
+bias vectors back to back.  Every function here is plain numpy in float64;
+reverse mode is the adjoint of each step, written out by hand.
 """
 from __future__ import annotations
 
@@ -59,7 +60,7 @@ def slices(H: int, dk: int, dv: int) -> List[Dict[str, Tuple[int, int]]]:
     range of the packed W_up (flattened offset and shape) and of the packed bias."""
     out, z0, w0, b0 = [], 0, 0, 0
     for r, wd in zip(RANKS, widths(H, dk, dv)):
-        out.append({"z": (z0, z0 + r), "w": (w0, w0 + r * wd), "b": (b0, b0 + wd), "shape": (r, wd)})
+        out.append({"z": (z0, z0 + r), "w": (w0, w0 + r * wd), "b": (b0, b0 + wd), "shape": (wd, r)})
         z0, w0, b0 = z0 + r, w0 + r * wd, b0 + wd
     return out
 
@@ -102,12 +103,12 @@ def gate_fwd(x, W_down, W_up, bias, H: int, dk: int, dv: int) -> Dict[str, np.nd
     "log_a", "erase", "write", "gamma": [M, H, dk or dv], "g": [M, H, dv]}."""
     x, W_down, W_up, bias = (_f64(a) for a in (x, W_down, W_up, bias))
     M = x.shape[0]
-    z = x @ W_down  # the shared down-projection
+    z = x @ W_down.T  # the shared down-projection
     out = {"z": z}
     for name, sl, D in zip(GATES, slices(H, dk, dv), (dk, dk, dv, dv, dk)):
         U = W_up[sl["w"][0]:sl["w"][1]].reshape(sl["shape"])
         c = bias[sl["b"][0]:sl["b"][1]]
-        pre = z[:, sl["z"][0]:sl["z"][1]] @ U + c  # this gate's rank slice, up-projected, plus channel bias
+        pre = z[:, sl["z"][0]:sl["z"][1]] @ U.T + c  # this gate's rank slice, up-projected, plus channel bias
         out[name] = _act(name, pre).reshape(M, H, D)
     return out
 
@@ -115,11 +116,11 @@ def gate_fwd(x, W_down, W_up, bias, H: int, dk: int, dv: int) -> Dict[str, np.nd
 def gate_bwd(x, W_down, W_up, bias, d_gates: Dict[str, object], H: int, dk: int, dv: int
              ) -> Dict[str, np.ndarray]:
     """Reverse mode of gate_fwd: from the gradients of the five gates
-    (d_gates[name], shaped like the gate) to dx [M, d], dW_down [d, 512],
+    (d_gates[name], shaped like the gate) to dx [M, d], dW_down [512, d],
     dW_up and dbias (packed like W_up and bias)."""
     x, W_down, W_up, bias = (_f64(a) for a in (x, W_down, W_up, bias))
     M = x.shape[0]
-    z = x @ W_down
+    z = x @ W_down.T
     dz = np.zeros_like(z)
     dW_up = np.zeros_like(W_up)
     dbias = np.zeros_like(bias)
@@ -127,12 +128,12 @@ def gate_bwd(x, W_down, W_up, bias, d_gates: Dict[str, object], H: int, dk: int,
         U = W_up[sl["w"][0]:sl["w"][1]].reshape(sl["shape"])
         c = bias[sl["b"][0]:sl["b"][1]]
         zi = z[:, sl["z"][0]:sl["z"][1]]
-        pre = zi @ U + c
+        pre = zi @ U.T + c
         dpre = _f64(d_gates[name]).reshape(M, -1) * _act_grad(name, pre)
         dbias[sl["b"][0]:sl["b"][1]] = dpre.sum(axis=0)
-        dW_up[sl["w"][0]:sl["w"][1]] = (zi.T @ dpre).reshape(-1)
-        dz[:, sl["z"][0]:sl["z"][1]] = dpre @ U.T
-    return {"dx": dz @ W_down.T, "dW_down": x.T @ dz, "dW_up": dW_up, "dbias": dbias}
+        dW_up[sl["w"][0]:sl["w"][1]] = (dpre.T @ zi).reshape(-1)
+        dz[:, sl["z"][0]:sl["z"][1]] = dpre @ U
+    return {"dx": dz @ W_down, "dW_down": dz.T @ x, "dW_up": dW_up, "dbias": dbias}
 
 
 def qk_norm_fwd(u) -> np.ndarray:

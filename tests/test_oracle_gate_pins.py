@@ -19,12 +19,12 @@ H, DK, DV = 1, 2, 3  # small widths: key gates 2 channels, value gates 3
 
 def _params(rng, d, scale=0.2):
     nw, nb = gp.up_numel(H, DK, DV)
-    return (rng.standard_normal((d, 512)) * scale, rng.standard_normal(nw) * scale,
+    return (rng.standard_normal((512, d)) * scale, rng.standard_normal(nw) * scale,
             rng.standard_normal(nb) * scale)
 
 
 def test_packed_sizes_follow_the_ranks():
-    """W_up holds 64*2 + 64*2 + 128*3 + 128*3 + 128*2 values for widths
+    """W_up holds 2*64 + 2*64 + 3*128 + 3*128 + 2*128 values for widths
     (H*dk, H*dk, H*dv, H*dv, H*dk) = (2, 2, 3, 3, 2); the biases 2+2+3+3+2."""
     assert gp.up_numel(H, DK, DV) == (128 + 128 + 384 + 384 + 256, 12)
     assert sum(gp.RANKS) == 512
@@ -61,7 +61,7 @@ def _pre(out):
             "write": _logit(out["write"]), "gamma": _logit(out["gamma"] / 2)}
 
 
-# (z column, gate it belongs to, row within that gate's up matrix)
+# (z column, gate it belongs to, column of that gate's up matrix [width, rank])
 ROUTES = [(0, "log_a", 0), (63, "log_a", 63), (64, "erase", 0), (127, "erase", 63), (128, "g", 0),
           (255, "g", 127), (256, "write", 0), (383, "write", 127), (384, "gamma", 0), (511, "gamma", 127)]
 # flat offset of each gate's up matrix in W_up, and its width
@@ -71,10 +71,11 @@ UP_AT = {"log_a": (0, 2), "erase": (128, 2), "g": (256, 3), "write": (640, 3), "
 @pytest.mark.parametrize("col,gate,row", ROUTES)
 def test_each_gate_reads_only_its_rank_slice(col, gate, row):
     """A down-projection that maps the token to one channel of z moves only
-    the gate whose rank slice holds that channel, by that row of its up matrix."""
+    the gate whose rank slice holds that channel, by that column of its up
+    matrix (stored [width, rank], a linear layer's [out, in])."""
     rng = np.random.default_rng(col)
-    Wd = np.zeros((1, 512))
-    Wd[0, col] = 1.0
+    Wd = np.zeros((512, 1))
+    Wd[col, 0] = 1.0
     nw, nb = gp.up_numel(H, DK, DV)
     Wu = rng.uniform(-1, 1, nw)
     out = gp.gate_fwd(np.ones((1, 1)), Wd, Wu, np.zeros(nb), H, DK, DV)
@@ -83,7 +84,8 @@ def test_each_gate_reads_only_its_rank_slice(col, gate, row):
         got = pre[name].reshape(-1)
         if name == gate:
             off, w = UP_AT[name]
-            assert np.allclose(got, Wu[off + row * w: off + (row + 1) * w], rtol=1e-9, atol=1e-12)
+            rank = 64 if name in ("log_a", "erase") else 128
+            assert np.allclose(got, Wu[off + row: off + w * rank: rank], rtol=1e-9, atol=1e-12)
         else:
             assert np.allclose(got, 0.0, atol=1e-12), name
 
@@ -111,7 +113,7 @@ def test_log_decay_is_a_nonpositive_log_sigmoid():
     """log alpha = log sigmoid(pre): <= 0 everywhere, ~ pre far below 0 and
     ~ -e^-pre far above it (closed forms, no overflow)."""
     nw, nb = gp.up_numel(H, DK, DV)
-    Wd = np.zeros((1, 512))
+    Wd = np.zeros((512, 1))
     for pre, expect in ((-40.0, -40.0 - math.log1p(math.exp(-40.0))), (40.0, -math.log1p(math.exp(-40.0))),
                         (-800.0, -800.0), (0.0, -math.log(2.0))):
         b = np.full(nb, pre)
