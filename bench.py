@@ -51,8 +51,9 @@ def log(*a):
 def kernel_bytes(d: int, C: int, e: int = 2):
     """Algorithmic HBM bytes per token-head of each kernel of the training
     step (bf16, 64-token chunks: the forward scan keeps the chunk deltas and
-    the backward reads them with Kbar^T instead of recomputing them)."""
-    st = 4 * d * d / C  # one fp32 state per chunk, per token
+    the chunk-start states in the compute type, and the backward reads them
+    with Kbar^T instead of recomputing them)."""
+    st = e * d * d / C  # one chunk-start state (compute type) per chunk, per token
     sg = e * d * d / C  # one chunk-end state gradient (compute type) per chunk, per token
     lf = 2 * 256 * e / 16  # the leaf blocks T_II, P_II (16 x 16 each per 16 tokens)
     return {

@@ -191,7 +191,8 @@ def muir_chunk_fwd(q, k, v, log_a, erase, write, gamma, S0=None, *, chunk: int =
 
     Any T: a partial last chunk runs on zero-padded copies in the workspace.
     Returns (o [B,T,H,dv] in the input dtype, S_T [B,H,dk,dv] fp32 or None,
-    S_chunks [B,H,ceil(T/chunk),dk,dv] fp32 or None).
+    S_chunks [B,H,ceil(T/chunk),dk,dv] in the input dtype (the chunk-start
+    states kept for muir_chunk_bwd) or None).
     """
     B, T, H, dk = q.shape
     dv = v.shape[3]
@@ -206,7 +207,7 @@ def muir_chunk_fwd(q, k, v, log_a, erase, write, gamma, S0=None, *, chunk: int =
         _check_io("S0", S0, (B, H, dk, dv), torch.float32, dev)
     o = out if out is not None else torch.empty((B, T, H, dv), dtype=dt, device=dev)
     S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if final_state else None
-    S_chunks = (torch.empty((B, H, _nchunks(T, chunk), dk, dv), dtype=torch.float32, device=dev)
+    S_chunks = (torch.empty((B, H, _nchunks(T, chunk), dk, dv), dtype=dt, device=dev)
                 if save_states else None)
     d = _dims(B, T, H, dk, dv, chunk, code, gm)
     nbytes = int(lib().muir_chunk_fwd_workspace(ctypes.byref(d)))
@@ -247,7 +248,7 @@ def muir_chunk_bwd(q, k, v, log_a, erase, write, gamma, dO, S0=None, S_chunks=No
     if dS_T is not None:
         _check_io("dS_T", dS_T, (B, H, dk, dv), torch.float32, dev)
     if S_chunks is not None:
-        _check_io("S_chunks", S_chunks, (B, H, _nchunks(T, chunk), dk, dv), torch.float32, dev)
+        _check_io("S_chunks", S_chunks, (B, H, _nchunks(T, chunk), dk, dv), dt, dev)
     if summaries is not None:
         need = muir_chunk_fwd_workspace(B, T, H, dk, dv, chunk, code, gm)
         if (not summaries.is_cuda or summaries.device != dev or not summaries.is_contiguous()

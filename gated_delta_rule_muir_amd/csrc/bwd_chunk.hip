@@ -64,7 +64,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     int T, int H, const Tin* __restrict__ q, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ log_a, const Tin* __restrict__ erase,
     const Tin* __restrict__ write, const Tin* __restrict__ gamma, const char* __restrict__ summ,
-    size_t summ_bytes, size_t tp_offset, size_t dl_offset, const float* __restrict__ S_chunks,
+    size_t summ_bytes, size_t tp_offset, size_t dl_offset, const Tin* __restrict__ S_chunks,
     const Tin* __restrict__ dS_chunks, const Tin* __restrict__ dO, Tin* __restrict__ dq,
     Tin* __restrict__ dk, Tin* __restrict__ dv, Tin* __restrict__ dlog_a,
     Tin* __restrict__ derase, Tin* __restrict__ dwrite, Tin* __restrict__ dgamma,
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   TC* gS = gDel + static_cast<size_t>(C) * DV;  // [NB][DK][DV]
   // T_II, P_II of the chunk's blocks, from the chunk summary, [NB][2][16][16]
   const TC* gTP = reinterpret_cast<const TC*>(summ + static_cast<size_t>(chunk) * summ_bytes + tp_offset);
-  const float* S0c = S_chunks + static_cast<size_t>(chunk) * DK * DV;
+  const Tin* S0c = S_chunks + static_cast<size_t>(chunk) * DK * DV;  // [dk][dv] rows, compute type
   const TC* dSC = dS_chunks + static_cast<size_t>(chunk) * DK * DV;  // transposed 16-row tiles
 
   __shared__ float sPart[NB][TPC][DK];                       // sum of log_a over each part's RPT tokens
@@ -283,15 +283,27 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
 
   // (the lane offset is made opaque per call so that the addresses are formed
   // where they are used instead of being kept live across the sweeps)
-  auto load_state = [&](f32x4 (*st)[NT], const float* src) {
+  auto load_state = [&](f32x4 (*st)[NT], const Tin* src) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      uint32_t lo = static_cast<uint32_t>(4 * g * DV + colv(n));
-      asm volatile("" : "+v"(lo));
+      if constexpr (sizeof(Tin) == 4) {
+        uint32_t lo = static_cast<uint32_t>(4 * g * DV + colv(n));
+        asm volatile("" : "+v"(lo));
 #pragma unroll
-      for (int s = 0; s < RT; ++s)
+        for (int s = 0; s < RT; ++s)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st[s][n][i] = *at(src, lo + static_cast<uint32_t>((16 * s + i) * DV));
+          for (int i = 0; i < 4; ++i) st[s][n][i] = *at(src, lo + static_cast<uint32_t>((16 * s + i) * DV));
+      } else {
+        // row 16s + c16, columns col0(n) + 4g .. + 3 as one 8-byte word, turned
+        // onto the accumulator layout by an identity product (exact)
+        uint32_t lo = static_cast<uint32_t>(c16 * DV + col0(n) + 4 * g);
+        asm volatile("" : "+v"(lo));
+#pragma unroll
+        for (int s = 0; s < RT; ++s) {
+          const uint2 w = *reinterpret_cast<const uint2*>(at(src, lo + static_cast<uint32_t>(16 * s * DV)));
+          st[s][n] = M::mma(__builtin_bit_cast(frag, w), ident, zero4());
+        }
+      }
     }
   };
   // the chunk-end state gradient from its transposed 16-row tiles (the
@@ -997,7 +1009,7 @@ size_t bwd_chunk_scratch_bytes(const ChunkShape& s) {
 
 hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, const void* v,
                             const void* log_a, const void* erase, const void* write,
-                            const void* gamma, const void* summ, const float* S_chunks,
+                            const void* gamma, const void* summ, const void* S_chunks,
                             const void* dS_chunks, const void* dO, void* dq, void* dk, void* dv,
                             void* dlog_a, void* derase, void* dwrite, void* dgamma, void* scratch,
                             float* dgam_part,
@@ -1008,7 +1020,7 @@ hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, c
   hipLaunchKernelGGL((bwd_chunk_kernel<TT, DD, CC, NW, DIR, GT>), dim3(grid), dim3(64 * NW), 0, stream, s.T, s.H, \
                      (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, (const TT*)erase,      \
                      (const TT*)write, (const TT*)gamma, (const char*)summ, s.summary_bytes(),          \
-                     s.tp_offset(), s.dl_offset(), S_chunks, (const TT*)dS_chunks, (const TT*)dO, (TT*)dq, (TT*)dk,      \
+                     s.tp_offset(), s.dl_offset(), (const TT*)S_chunks, (const TT*)dS_chunks, (const TT*)dO, (TT*)dq, (TT*)dk,      \
                      (TT*)dv, (TT*)dlog_a, (TT*)derase, (TT*)dwrite, (TT*)dgamma, (char*)scratch, s.gmode, \
                      dgam_part)
 #define MUIR_BCH1(TT, DD, CC, NW, DIR)                              \

@@ -80,11 +80,11 @@ hipError_t launch_fwd_prep(const ChunkShape& s, const void* q, const void* k, co
                            const void* log_a, const void* erase, const void* write,
                            const void* gamma, void* summ, hipStream_t stream);
 
-// Sequential over chunks: o (may be NULL), S_chunks (may be NULL), S_T (may be
-// NULL).  With `deltas` (the same summaries, writable) each chunk's deltas are
+// Sequential over chunks: o (may be NULL), S_chunks (may be NULL: the
+// chunk-start states in the compute type, [dk][dv] rows), S_T (may be NULL).  With `deltas` (the same summaries, writable) each chunk's deltas are
 // written into its summary.  `split`: scan_split_bytes(s) of workspace.
 hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S0, void* o,
-                           float* S_chunks, float* S_T, void* deltas, float* split, hipStream_t stream);
+                           void* S_chunks, float* S_T, void* deltas, float* split, hipStream_t stream);
 
 // Reverse sequential over chunks: dS_chunks[c] = gradient w.r.t. the state at the
 // END of chunk c, in the compute type, as transposed 16-row tiles: element
@@ -102,7 +102,7 @@ hipError_t launch_bwd_scan(const ChunkShape& s, const void* summ, const void* dO
 size_t bwd_chunk_scratch_bytes(const ChunkShape& s);
 hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, const void* v,
                             const void* log_a, const void* erase, const void* write,
-                            const void* gamma, const void* summ, const float* S_chunks,
+                            const void* gamma, const void* summ, const void* S_chunks,
                             const void* dS_chunks,
                             const void* dO, void* dq, void* dk, void* dv, void* dlog_a,
                             void* derase, void* dwrite, void* dgamma, void* scratch,

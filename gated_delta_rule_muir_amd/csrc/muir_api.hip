@@ -167,7 +167,7 @@ constexpr bool kIsDk[7] = {true, true, false, true, true, false, true};
 
 // The kernels of the forward on a shape whose T is a multiple of the chunk.
 muir_status_t fwd_core(const ChunkShape& s, const Inputs& in, const float* S0, void* o, float* S_T,
-                       float* S_chunks, void* workspace, hipStream_t hs) {
+                       void* S_chunks, void* workspace, hipStream_t hs) {
   mark(hs);
   if (muir::launch_fwd_prep(s, in.x[0], in.x[1], in.x[2], in.x[3], in.x[4], in.x[5], in.x[6], workspace, hs) !=
       hipSuccess)
@@ -183,7 +183,7 @@ muir_status_t fwd_core(const ChunkShape& s, const Inputs& in, const float* S0, v
 }
 
 // The kernels of the backward on a shape whose T is a multiple of the chunk.
-muir_status_t bwd_core(const ChunkShape& s, const Inputs& in, const float* S0, const float* S_chunks,
+muir_status_t bwd_core(const ChunkShape& s, const Inputs& in, const float* S0, const void* S_chunks,
                        const void* summaries, const void* dO, const float* dS_T, const Grads& gr, float* dS0,
                        void* workspace, hipStream_t hs) {
   char* ws = static_cast<char*>(workspace);
@@ -192,7 +192,7 @@ muir_status_t bwd_core(const ChunkShape& s, const Inputs& in, const float* S0, c
   float* scratch = dS_chunks + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
   float* split = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) + s.nchunks() * bwd_scratch_bytes(s));
   float* gpart = reinterpret_cast<float*>(reinterpret_cast<char*>(split) + s.scan_split_bytes());
-  const float* Sc = S_chunks;
+  const void* Sc = S_chunks;
   const void* summ = summaries;
   mark(hs);
   // The direct backward reads the deltas that the forward scan keeps in the
@@ -258,7 +258,7 @@ muir_status_t stage_inputs(const ChunkShape& p, int Tsrc, const int32_t* cu, con
 }
 
 muir_status_t check_fwd_args(const ChunkShape& s, const Inputs& in, const float* S0, const void* o, const float* S_T,
-                             const float* S_chunks, const void* workspace, size_t workspace_bytes, size_t need) {
+                             const void* S_chunks, const void* workspace, size_t workspace_bytes, size_t need) {
   muir_status_t st;
   if (s.nchunks() != 0) {
     for (int i = 0; i < 6; ++i)
@@ -277,7 +277,7 @@ muir_status_t check_fwd_args(const ChunkShape& s, const Inputs& in, const float*
   return MUIR_OK;
 }
 
-muir_status_t check_bwd_args(const ChunkShape& s, const Inputs& in, const float* S0, const float* S_chunks,
+muir_status_t check_bwd_args(const ChunkShape& s, const Inputs& in, const float* S0, const void* S_chunks,
                              const void* summaries, const void* dO, const float* dS_T, const Grads& gr,
                              const float* dS0, const void* workspace, size_t workspace_bytes, size_t need) {
   muir_status_t st;
@@ -325,7 +325,7 @@ muir_status_t bwd_empty(const ChunkShape& s, const float* dS_T, void* dgamma, fl
 // Forward of batched ([N, T, H, D], cu == NULL) or packed (cu given)
 // sequences through the padded layout.
 muir_status_t fwd_staged(const ChunkShape& s, const int32_t* cu, const Inputs& in, const float* S0, void* o,
-                         float* S_T, float* S_chunks, void* workspace, hipStream_t hs) {
+                         float* S_T, void* S_chunks, void* workspace, hipStream_t hs) {
   const ChunkShape p = padded(s);
   StageCursor cur{static_cast<char*>(workspace) + fwd_ws(p)};
   Inputs sin;
@@ -337,7 +337,7 @@ muir_status_t fwd_staged(const ChunkShape& s, const int32_t* cu, const Inputs& i
 }
 
 muir_status_t bwd_staged(const ChunkShape& s, const int32_t* cu, const Inputs& in, const float* S0,
-                         const float* S_chunks, const void* summaries, const void* dO, const float* dS_T,
+                         const void* S_chunks, const void* summaries, const void* dO, const float* dS_T,
                          const Grads& gr, float* dS0, void* workspace, hipStream_t hs) {
   const ChunkShape p = padded(s);
   StageCursor cur{static_cast<char*>(workspace) + bwd_ws(p)};
@@ -405,7 +405,7 @@ size_t varlen_bwd_need(const ChunkShape& s) { return bwd_ws(padded(s)) + bwd_sta
 
 extern "C" {
 
-int32_t muir_abi_version(void) { return 6; }
+int32_t muir_abi_version(void) { return 7; }
 
 int32_t muir_set_profile_events(void** events, int32_t count) {
   if (count < 0 || (count > 0 && !events)) return MUIR_ERR_NULL;
@@ -446,7 +446,7 @@ size_t muir_chunk_bwd_workspace(const muir_dims_t* dims) {
 muir_status_t muir_chunk_fwd(const muir_dims_t* dims, const void* q, const void* k,
                              const void* v, const void* log_a, const void* erase,
                              const void* write, const void* gamma, const float* S0, void* o,
-                             float* S_T, float* S_chunks, void* workspace,
+                             float* S_T, void* S_chunks, void* workspace,
                              size_t workspace_bytes, void* stream) {
   ChunkShape s;
   muir_status_t st = check_dims(dims, &s);
@@ -463,7 +463,7 @@ muir_status_t muir_chunk_fwd(const muir_dims_t* dims, const void* q, const void*
 muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void* k,
                              const void* v, const void* log_a, const void* erase,
                              const void* write, const void* gamma, const float* S0,
-                             const float* S_chunks, const void* summaries, const void* dO,
+                             const void* S_chunks, const void* summaries, const void* dO,
                              const float* dS_T, void* dq, void* dk, void* dv, void* dlog_a,
                              void* derase, void* dwrite, void* dgamma, float* dS0,
                              void* workspace, size_t workspace_bytes, void* stream) {

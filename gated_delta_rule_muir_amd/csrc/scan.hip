@@ -64,7 +64,7 @@ template <typename TC> __device__ __forceinline__ typename MM<TC>::frag identity
 template <typename Tin, int DK, int NW, bool TRANS>
 __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
     int T, int H, int C, const char* __restrict__ summ, size_t summ_bytes,
-    const float* __restrict__ S0, Tin* __restrict__ o, float* __restrict__ S_chunks,
+    const float* __restrict__ S0, Tin* __restrict__ o, Tin* __restrict__ S_chunks,
     float* __restrict__ S_T, char* __restrict__ dsumm, size_t dl_offset, int nseg,
     const float* __restrict__ S_seg, float* __restrict__ trans) {
   typedef Tin TC;
@@ -217,11 +217,21 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
     __syncthreads();
     if (sb == 0) {
       if (!TRANS && S_chunks) {
-        float* dst = S_chunks + (static_cast<size_t>(bh) * NC + c) * DK * DV;
+        // the chunk-start state, kept for the backward in the compute type
+        Tin* dst = S_chunks + (static_cast<size_t>(bh) * NC + c) * DK * DV;
+        if constexpr (sizeof(Tin) == 4) {
 #pragma unroll
-        for (int s = 0; s < RT; ++s)
+          for (int s = 0; s < RT; ++s)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] = S[s][i];
+            for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] = S[s][i];
+        } else {
+          // rounded once, then turned onto rows by an identity product (exact):
+          // row 16s + c16, four columns per lane
+#pragma unroll
+          for (int s = 0; s < RT; ++s)
+            store4(at(dst, static_cast<uint32_t>((16 * s + c16) * DV + col0 + 4 * g)),
+                   M::mma(M::from_f32(S[s]), ident, zero4()));
+        }
       }
 #pragma unroll
       for (int s = 0; s < RT; ++s) {
@@ -567,7 +577,8 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(int nseg, int reverse,
 // columns) per workgroup.
 template <typename TT, int DD>
 hipError_t fwd_scan_typed(const ChunkShape& s, const void* summ, const float* S0, void* o,
-                          float* S_chunks, float* S_T, void* deltas, float* split, hipStream_t stream) {
+                          void* S_chunks_v, float* S_T, void* deltas, float* split, hipStream_t stream) {
+  TT* S_chunks = static_cast<TT*>(S_chunks_v);
   const int heads = s.B * s.H;
   const int nseg = s.scan_segments();
   const size_t sb = s.summary_bytes();
@@ -575,7 +586,7 @@ hipError_t fwd_scan_typed(const ChunkShape& s, const void* summ, const float* S0
     float* trans = split;
     float* sseg = split + static_cast<size_t>(heads) * nseg * DD * (2 * DD);
     hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, true>), dim3(heads * nseg * (2 * DD / 64)), dim3(256), 0,
-                       stream, s.T, s.H, s.C, (const char*)summ, sb, S0, (TT*)nullptr, (float*)nullptr,
+                       stream, s.T, s.H, s.C, (const char*)summ, sb, S0, (TT*)nullptr, (TT*)nullptr,
                        (float*)nullptr, (char*)nullptr, size_t(0), nseg, (const float*)nullptr, trans);
     hipLaunchKernelGGL((seg_combine_kernel<DD>), dim3(heads * (DD / 64)), dim3(256), 0, stream, nseg, 0, S0,
                        (const float*)trans, sseg);
@@ -624,7 +635,7 @@ hipError_t bwd_scan_typed(const ChunkShape& s, const void* summ, const void* dO,
 }
 
 hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S0, void* o,
-                           float* S_chunks, float* S_T, void* deltas, float* split, hipStream_t stream) {
+                           void* S_chunks, float* S_T, void* deltas, float* split, hipStream_t stream) {
   if (s.B * s.H == 0) return hipSuccess;
   if (s.bf16) {
     return s.DK == 128 ? fwd_scan_typed<uint16_t, 128>(s, summ, S0, o, S_chunks, S_T, deltas, split, stream)

@@ -127,8 +127,10 @@ size_t muir_chunk_fwd_workspace(const muir_dims_t* dims);
  *   S0       : [B, H, dk, dv] fp32 initial state, or NULL for zeros
  *   o        : [B, T, H, dv]  dtype, output
  *   S_T      : [B, H, dk, dv] fp32 final state, or NULL to skip
- *   S_chunks : [B, H, nc, dk, dv] fp32 state at the START of every
- *              chunk (kept for muir_chunk_bwd), or NULL to skip
+ *   S_chunks : [B, H, nc, dk, dv] dtype: the state at the START of every
+ *              chunk, rounded once to the input type (kept for
+ *              muir_chunk_bwd, which takes the state in that type), or NULL
+ *              to skip
  *   workspace: device scratch of at least muir_chunk_fwd_workspace(dims)
  *              bytes.  On return it holds the chunk summaries (the
  *              per-chunk solve results; with S_chunks also each chunk's
@@ -140,7 +142,7 @@ muir_status_t muir_chunk_fwd(const muir_dims_t* dims,
                              const void* q, const void* k, const void* v,
                              const void* log_a, const void* erase,
                              const void* write, const void* gamma,
-                             const float* S0, void* o, float* S_T, float* S_chunks,
+                             const float* S0, void* o, float* S_T, void* S_chunks,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace muir_chunk_bwd needs for `dims` (0 if dims are invalid). */
@@ -152,7 +154,7 @@ size_t muir_chunk_bwd_workspace(const muir_dims_t* dims);
  * custom backward pass is used; this is the adjoint of the recurrence above).
  *
  *   inputs as in muir_chunk_fwd, plus
- *   S_chunks : [B, H, nc, dk, dv] fp32 from muir_chunk_fwd, or NULL
+ *   S_chunks : [B, H, nc, dk, dv] dtype from muir_chunk_fwd, or NULL
  *              (then recomputed inside, in the workspace)
  *   summaries: the workspace of a muir_chunk_fwd call on the same inputs,
  *              dims and S0, unchanged since (the chunk summaries it left
@@ -178,7 +180,7 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims,
                              const void* q, const void* k, const void* v,
                              const void* log_a, const void* erase,
                              const void* write, const void* gamma,
-                             const float* S0, const float* S_chunks, const void* summaries,
+                             const float* S0, const void* S_chunks, const void* summaries,
                              const void* dO, const float* dS_T,
                              void* dq, void* dk, void* dv, void* dlog_a,
                              void* derase, void* dwrite, void* dgamma, float* dS0,

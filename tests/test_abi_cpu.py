@@ -50,7 +50,7 @@ def test_status_strings_cover_every_code():
         seen.add(s)
     assert len(seen) == 8
     assert L.muir_status_string(99).decode() == "unknown status"
-    assert L.muir_abi_version() == 6
+    assert L.muir_abi_version() == 7
 
 
 def _dims(m, B=1, T=128, H=2, dk=64, dv=64, chunk=64, dtype=1, gamma_mode=0):
