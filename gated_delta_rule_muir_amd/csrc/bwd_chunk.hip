@@ -167,7 +167,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   __shared__ __attribute__((aligned(16))) TC sT[16][TP];     // T_II of the block
   __shared__ __attribute__((aligned(16))) TC sP[16][TP];     // P_II of the block
   __shared__ __attribute__((aligned(16))) TC sSD[DK][PS];    // staged D columns, [dk][dv]
-  __shared__ __attribute__((aligned(16))) TC sSS[DK][PS];    // staged S_J (direct: S0) columns, [dk][dv]
+  __shared__ __attribute__((aligned(16))) TC sSS[DIRECT ? 1 : DK][PS];  // staged S_J columns, [dk][dv] (two sweeps)
+  // direct form: the block's inputs q, k, v, write, erase, log_a, gamma as
+  // token rows, read by both the elementwise and the output mapping
+  __shared__ __attribute__((aligned(16))) TC sIn[DIRECT ? 7 : 1][16][PV];
   __shared__ float sLf[2][16][17];                           // leaf matrices of steep blocks
   __shared__ float sG[DK];
   __shared__ float sGH[DIRECT ? NB - 1 : 1][DK];              // direct: block decays exp(B_{I+1} - B_I)
@@ -337,12 +340,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     const int r0 = 16 * J;
 #pragma unroll
     for (int rr = 0; rr < RPT; ++rr) {
-      const uint32_t o = gi(r0 + RPT * part + rr, ej);
-      xl[rr] = ldv(lb, o);
-      xk[rr] = ldv(kb, o);
-      xe[rr] = ldv(eb, o);
-      xq[rr] = ldv(qb, o);
-      xg[rr] = gam(r0 + RPT * part + rr, ej);
+      if constexpr (!DIRECT) {
+        const uint32_t o = gi(r0 + RPT * part + rr, ej);
+        xl[rr] = ldv(lb, o);
+        xk[rr] = ldv(kb, o);
+        xe[rr] = ldv(eb, o);
+        xq[rr] = ldv(qb, o);
+        xg[rr] = gam(r0 + RPT * part + rr, ej);
+      }
     }
 #pragma unroll
     for (int e = 0; e < RW; ++e) {
@@ -376,6 +381,73 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         oe[n][ii] = ldv(eb, o);
         ol[n][ii] = ldv(lb, o);
       }
+  };
+  // Direct form: the block's inputs into sIn.  Tensor t (q, k, v, write,
+  // erase, log_a, gamma; gamma only when per token) is moved by wave t % NW,
+  // 16 rows of DV values as 16-byte words, loaded a step ahead into registers.
+  constexpr int NTEN = 7;
+  constexpr int SPWV = (NTEN + NW - 1) / NW;  // tensors per wave
+  constexpr int IWR = DV / SEW;               // 16-byte words per input row
+  constexpr int IWT = 16 * IWR / 64;          // words per lane and tensor
+  static_assert(!DIRECT || (16 * IWR) % 64 == 0, "input staging layout");
+  u32x4 iw[DIRECT ? SPWV * IWT : 1];
+  auto in_ptr = [&](int t) -> const Tin* {
+    return t == 0 ? qb : t == 1 ? kb : t == 2 ? vb : t == 3 ? wb : t == 4 ? eb : t == 5 ? lb : gb;
+  };
+  auto load_in = [&](int J) {
+    if constexpr (DIRECT) {
+#pragma unroll
+      for (int sl = 0; sl < SPWV; ++sl) {
+        const int t = wave + sl * NW;  // wave-uniform
+        if (t < (GTOK ? NTEN : NTEN - 1)) {
+          const Tin* base = in_ptr(t);
+#pragma unroll
+          for (int k2 = 0; k2 < IWT; ++k2) {
+            const int w = lane + 64 * k2;
+            const int row = w / IWR;
+            iw[sl * IWT + k2] = *reinterpret_cast<const u32x4*>(at(base, gi(16 * J + row, (w - row * IWR) * SEW)));
+          }
+        }
+      }
+    }
+  };
+  auto store_in = [&]() {
+    if constexpr (DIRECT) {
+#pragma unroll
+      for (int sl = 0; sl < SPWV; ++sl) {
+        const int t = wave + sl * NW;
+        if (t < (GTOK ? NTEN : NTEN - 1)) {
+#pragma unroll
+          for (int k2 = 0; k2 < IWT; ++k2) {
+            const int w = lane + 64 * k2;
+            const int row = w / IWR;
+            *reinterpret_cast<u32x4*>(&sIn[t][row][(w - row * IWR) * SEW]) = iw[sl * IWT + k2];
+          }
+        }
+      }
+    }
+  };
+  // a static gate's value per channel (none: 1)
+  auto gam_static = [&](int j) -> float { return gmode == GAMMA_NONE ? 1.f : ldv(gst, static_cast<uint32_t>(j)); };
+  // Direct form: the block's inputs at the output mapping, from sIn
+  auto in_out = [&]() {
+    if constexpr (DIRECT) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const float gs = GTOK ? 0.f : gam_static(colv(n));
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int t = 4 * g + ii, j = colv(n);
+          oq[n][ii] = M::to_f32(sIn[0][t][j]);
+          ok[n][ii] = M::to_f32(sIn[1][t][j]);
+          ov[n][ii] = M::to_f32(sIn[2][t][j]);
+          ow[n][ii] = M::to_f32(sIn[3][t][j]);
+          oe[n][ii] = M::to_f32(sIn[4][t][j]);
+          ol[n][ii] = M::to_f32(sIn[5][t][j]);
+          og[n][ii] = GTOK ? M::to_f32(sIn[6][t][j]) : gs;
+        }
+      }
+    }
   };
   // log-decay of channel colv(n) over the block at the output mapping (tokens
   // 4g+ii): loc = Lam - B_J (through the token), suf = B_{J+1} - Lam (after
@@ -414,6 +486,18 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   // transposed.  Returns whether the block's leaf is within LEAF_SAFE_RANGE.
   auto commit_r = [&](int J) -> int {
     const int safe = !((sUnsafe >> J) & 1);
+    if constexpr (DIRECT) {
+      const float gs = GTOK ? 0.f : gam_static(ej);
+#pragma unroll
+      for (int rr = 0; rr < RPT; ++rr) {
+        const int r = RPT * part + rr;
+        xq[rr] = M::to_f32(sIn[0][r][ej]);
+        xk[rr] = M::to_f32(sIn[1][r][ej]);
+        xe[rr] = M::to_f32(sIn[4][r][ej]);
+        xl[rr] = M::to_f32(sIn[5][r][ej]);
+        xg[rr] = GTOK ? M::to_f32(sIn[6][r][ej]) : gs;
+      }
+    }
     float loc[RPT], suf[RPT];
     block_sums(J, xl, loc, suf);
 #pragma unroll
@@ -489,6 +573,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   // Ke_I = k exp(B_{I+1} - Lam) at (token 4g+i of block I, channel colv(n)),
   // and the block decays exp(B_{I+1} - B_I) in sGH, for every block but the last.
   frag keH[DIRECT ? NB - 1 : 1][NT];
+  frag s0f[NT][DIRECT ? DV / 16 : 1];  // direct form: S0 rows of the wave's key channels
   // Direct form: every global read of the prologue is issued before the
   // first wait -- the chunk's deltas and Kbar^T (16-byte words), Gamma_C, the
   // Horner inputs, S0, dS_C and the first step's prefetch.
@@ -523,9 +608,16 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
           hk[I][n][i] = ldv(kb, o);
         }
     load_state(S, S0c);
+    // S0 rows of this wave's key channels as the right operands of the
+    // boundary products (rows colv(n), dv columns 16kk + 4g ..)
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int kk = 0; kk < DV / 16; ++kk)
+        s0f[n][kk] = *reinterpret_cast<const frag*>(at(S0c, static_cast<uint32_t>((col0(n) + c16) * DV + 16 * kk + 4 * g)));
     load_dstate(D);
     prefetch_r(NB - 1);
-    prefetch_r_out(NB - 1);
+    load_in(NB - 1);
   }
 
   // ---- sums of the log-decay over each block and each part of it, and the
@@ -553,7 +645,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
 
   if constexpr (DIRECT) {
     // deltas into sDL; Kbar^T into sSD (until the sweep stages D there);
-    // Gamma_C into sG (until the sweep's block sums); S0 into sSS
+    // Gamma_C into sG (until the sweep's block sums); the last block's inputs
+    // into sIn
 #pragma unroll
     for (int k2 = 0; k2 < DWT; ++k2) {
       const int w = tid + k2 * NTH;
@@ -567,10 +660,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       *reinterpret_cast<u32x4*>(&sSD[row][(w - row * KWR) * SEW]) = kw[k2];
     }
     if (tid < DK / 4) *reinterpret_cast<u32x4*>(&sG[4 * tid]) = gcw;
-#pragma unroll
-    for (int s = 0; s < RT; ++s)
-#pragma unroll
-      for (int n = 0; n < NT; ++n) store4(&sSS[16 * s + c16][col0(n) + 4 * g], turn(S[s][n]));
+    store_in();
 #pragma unroll
     for (int I = 0; I < NB - 1; ++I)
 #pragma unroll
@@ -593,7 +683,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         keH[I][n] = M::from_f32(kv);
         if (g == 0) sGH[I][colv(n)] = __expf(((t0 + t1) + t2) + t3);
       }
-    __syncthreads();  // sDL, sSD, sG, sSS, sGH
+    __syncthreads();  // sDL, sSD, sG, sIn, sGH
     // S becomes the chunk-end state S_C = diag(Gamma_C) S0 + Kbar^T Delta
     // (for the rowsum term below)
     {
@@ -719,6 +809,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       for (int k2 = 0; k2 < SPT; ++k2) css[k2] = rss[k2];
     }
     prefetch_r(J > 0 ? J - 1 : 0);
+    load_in(J > 0 ? J - 1 : 0);  // (direct form) the next block's inputs, written to sIn at the step's end
+    in_out();                    // (direct form) this block's inputs at the output mapping
     // dR_J = T_JJ^T (Ke_J D + P_JJ^T dO_J)
     f32x4 dRn[NT];
     frag dOf[NT];
@@ -808,7 +900,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           const frag bd = M::load(&sSD[colv(n)][16 * kk + 4 * g]);
-          const frag bs = M::load(&sSS[colv(n)][16 * kk + 4 * g]);
+          const frag bs = DIRECT ? s0f[n][kk] : M::load(&sSS[colv(n)][16 * kk + 4 * g]);
           acck[n] = M::mma(al, bd, acck[n]);
           accq[n] = M::mma(ao, bs, accq[n]);
           acce[n] = M::mma(ar, bs, acce[n]);
@@ -969,7 +1061,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       store_grad(dkb, r0, n, gk);
       store_grad(dlb, r0, n, gl);
     }
-    prefetch_r_out(J > 0 ? J - 1 : 0);
+    if constexpr (!DIRECT) prefetch_r_out(J > 0 ? J - 1 : 0);
     // D <- diag(exp(B_{J+1} - B_J)) D + Y_J^T dO_J - X_J^T dR_J
     {
       frag dRf[NT];
@@ -988,6 +1080,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       }
     }
     __syncthreads();
+    if (DIRECT && J > 0) {
+      store_in();  // the next block's inputs (every read of this block's is done)
+      __syncthreads();
+    }
   }
   if (gmode == GAMMA_STATIC) {
     // the chunk's sum of dgamma per key channel (lanes c16 + 16g' hold the token groups)
