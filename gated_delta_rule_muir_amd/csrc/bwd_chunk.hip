@@ -595,7 +595,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       dw[k2] = *reinterpret_cast<const u32x4*>(at(gD, static_cast<uint32_t>((tid + k2 * NTH) * SEW)));
 #pragma unroll
     for (int k2 = 0; k2 < KWT; ++k2)
-      kw[k2] = *reinterpret_cast<const u32x4*>(at(gKT, static_cast<uint32_t>((tid + k2 * NTH) * SEW)));
+      kw[k2] = *reinterpret_cast<const u32x4*>(
+          at(gKT, tpart_index((tid + k2 * NTH) / KWR, ((tid + k2 * NTH) % KWR) * SEW, DK)));  // 16-token tiles
     gcw = *reinterpret_cast<const u32x4*>(at(gGC, static_cast<uint32_t>(4 * min(tid, DK / 4 - 1))));
 #pragma unroll
     for (int I = 0; I < NB - 1; ++I)

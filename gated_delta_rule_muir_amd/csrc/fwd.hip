@@ -279,7 +279,7 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
     store4(&sR[bb][ej][4 * part], uT);
     store4(&sR[bb][DV + ej][4 * part], ktT);
     store4(&sQh[bb][ej][4 * part], qhT);
-    store4(out.KbT + static_cast<size_t>(ej) * C + r0 + 4 * part, kbT);
+    store4(out.KbT + tpart_index(ej, r0 + 4 * part, DK), kbT);
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) out.Kb[static_cast<size_t>(r0 + 4 * part + rr) * DK + ej] = M::cvt(kbT[rr]);
   };
@@ -393,13 +393,13 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
       const f32x4 op = M::mma(pa, M::from_f32(uw), YH[n]);
       UW[n] = uw;
       if (colg < DV) {
-        store4(out.UtT + static_cast<size_t>(colg) * C + r0 + 4 * g, uw);
-        store4(out.OtT + static_cast<size_t>(colg) * C + r0 + 4 * g, op);
+        store4(out.UtT + tpart_index(colg, r0 + 4 * g, DV), uw);
+        store4(out.OtT + tpart_index(colg, r0 + 4 * g, DV), op);
       } else {
         const int j = colg - DV;
         const f32x4 qv = load4(&sQh[bb][j][4 * g]) - op;
-        store4(out.Wt + static_cast<size_t>(j) * C + r0 + 4 * g, uw);
-        store4(out.Qt + static_cast<size_t>(j) * C + r0 + 4 * g, qv);
+        store4(out.Wt + tpart_index(j, r0 + 4 * g, DK), uw);
+        store4(out.Qt + tpart_index(j, r0 + 4 * g, DK), qv);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           sStage[4 * g + i][j] = M::cvt(uw[i]);

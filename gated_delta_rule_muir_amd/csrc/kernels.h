@@ -23,6 +23,14 @@ __host__ __device__ constexpr size_t summary_part(int part, int C, int DK, int D
                                static_cast<size_t>(part - SP_WT) * C * DK;
 }
 
+// The transposed parts (Kbar^T, U~^T, O~^T, W^T, Q'^T: logically [D][C]) are
+// stored as 16-token tiles [C/16][D][16], so that each 16-token block's tile
+// is one contiguous run: element (row d, token t) is at this index.
+__host__ __device__ constexpr uint32_t tpart_index(int d, int t, int D) {
+  return (static_cast<uint32_t>(t >> 4) * static_cast<uint32_t>(D) + static_cast<uint32_t>(d)) * 16u +
+         static_cast<uint32_t>(t & 15);
+}
+
 // Readout-gate forms: per token [B, T, H, dk]; static per (head, key channel)
 // [H, dk]; none (gamma = 1, no pointer).
 enum GammaMode { GAMMA_TOKEN = 0, GAMMA_STATIC = 1, GAMMA_NONE = 2 };

@@ -129,9 +129,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
     auto part = [&](int p) { return static_cast<uint32_t>(summary_part(p, C, DK, DV) * SZ); };
     const uint32_t wofs = part(SP_W) + static_cast<uint32_t>(sb * SB * LW);
     const uint32_t qofs = part(SP_QP) + static_cast<uint32_t>(sb * SB * LW);
-    const uint32_t kofs = part(SP_KBT) + static_cast<uint32_t>(sb * LK);
-    const uint32_t uofs = part(SP_UTT) + static_cast<uint32_t>(vbu * NV * C * SZ + sb * LK);
-    const uint32_t oofs = part(SP_OTT) + static_cast<uint32_t>(vbu * NV * C * SZ + sb * LK);
+    // (the transposed parts in 16-token tiles: row r, word ww of the unit
+    // is token sb * SB + ww * (16 / SZ))
+    const uint32_t kofs = part(SP_KBT);
+    const uint32_t uofs = part(SP_UTT);
+    const uint32_t oofs = part(SP_OTT);
+    auto tofs = [&](int r, int ww, int D) {
+      return static_cast<uint32_t>(tpart_index(r, sb * SB + ww * (16 / SZ), D) * SZ);
+    };
     const uint32_t gofs = part(SP_END);
 #pragma unroll
     for (int k = 0; k < PW; ++k) {
@@ -142,12 +147,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
 #pragma unroll
     for (int k = 0; k < PK; ++k) {
       const int w = min(tid + k * NTH, K_WORDS - 1);
-      rk[k] = *reinterpret_cast<const u32x4*>(at(base, kofs + (w / CK) * C * SZ + 16 * (w % CK)));
+      rk[k] = *reinterpret_cast<const u32x4*>(at(base, kofs + tofs(w / CK, w % CK, DK)));
     }
 #pragma unroll
     for (int k = 0; k < PU; ++k) {
       const int w = min(tid + k * NTH, U_WORDS - 1);
-      const uint32_t ro_ = (w / CK) * C * SZ + 16 * (w % CK);
+      const uint32_t ro_ = tofs(vbu * NV + w / CK, w % CK, DV);
       ru[k] = *reinterpret_cast<const u32x4*>(at(base, uofs + ro_));
       if constexpr (!TRANS) ro[k] = *reinterpret_cast<const u32x4*>(at(base, oofs + ro_));
     }
@@ -374,8 +379,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
     const int sb = unit_sb(u);
     const char* base = hsum + static_cast<size_t>(c) * summ_bytes;
     auto part = [&](int p) { return static_cast<uint32_t>(summary_part(p, C, DK, DV) * SZ); };
-    const uint32_t tofs = part(SP_WT) + static_cast<uint32_t>(sb * LK);
-    const uint32_t qofs = part(SP_QT) + static_cast<uint32_t>(sb * LK);
+    const uint32_t tofs = part(SP_WT);  // (16-token tiles, as in the forward scan)
+    const uint32_t qofs = part(SP_QT);
     const uint32_t kofs = part(SP_KB) + static_cast<uint32_t>(sb * SB * LW);
     const uint32_t gofs = part(SP_END);
     const char* dob = reinterpret_cast<const char*>(
@@ -383,7 +388,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
 #pragma unroll
     for (int k = 0; k < PT; ++k) {
       const int w = min(tid + k * NTH, T_WORDS - 1);
-      const uint32_t r = (w / CK) * C * SZ + 16 * (w % CK);
+      const uint32_t r = static_cast<uint32_t>(tpart_index(w / CK, sb * SB + (w % CK) * (16 / SZ), DK) * SZ);
       rt[k] = *reinterpret_cast<const u32x4*>(at(base, tofs + r));
       rq[k] = *reinterpret_cast<const u32x4*>(at(base, qofs + r));
     }

@@ -113,10 +113,16 @@ def test_steps_equal_chunk_fwd():
     assert rel_err(S, S_T) <= 1e-4
 
 
+def untile(flat, D, C):
+    """A transposed summary part, [D][C], from its 16-token tiles [C/16][D][16]."""
+    return flat.reshape(C // 16, D, 16).transpose(1, 0, 2).reshape(D, C)
+
+
 def test_fwd_summary_intermediates():
     """The chunk summary in the workspace equals the plain chunkwise quantities
     (fp32 path, one head): W, U~, Q', O~, Kbar (and the transposed copies of
-    W, Q', Kbar), exp(L_C), and each 16-token leaf block's (I + A_II)^-1 and P_II."""
+    W, Q', Kbar), exp(L_C), and each 16-token leaf block's (I + A_II)^-1 and P_II.
+    The transposed parts are laid out in 16-token tiles."""
     from chunkwise_model import chunk_summary
     m = _lib()
     B, T, H, d, C = 1, 128, 1, 64, 64
@@ -133,11 +139,8 @@ def test_fwd_summary_intermediates():
         blk = ws[c * per:(c + 1) * per].view(torch.float32).cpu().double().numpy()
         W = blk[:n].reshape(C, d)
         Qp = blk[n: 2 * n].reshape(C, d)
-        KbT = blk[2 * n: 3 * n].reshape(d, C)
-        UtT = blk[3 * n: 4 * n].reshape(d, C)
-        OtT = blk[4 * n: 5 * n].reshape(d, C)
-        Wt = blk[5 * n: 6 * n].reshape(d, C)
-        Qt = blk[6 * n: 7 * n].reshape(d, C)
+        # the transposed parts are stored as 16-token tiles [C/16][d][16]
+        KbT, UtT, OtT, Wt, Qt = (untile(blk[k * n:(k + 1) * n], d, C) for k in (2, 3, 4, 5, 6))
         Kb = blk[7 * n: 8 * n].reshape(C, d)
         gC = blk[8 * n: 8 * n + d]
         TP = blk[8 * n + d: 8 * n + d + (C // 16) * 512].reshape(C // 16, 2, 16, 16)
