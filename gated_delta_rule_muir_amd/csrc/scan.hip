@@ -35,6 +35,18 @@ template <int L> __device__ __forceinline__ int swz(int row, int byte) {
   return row * L + (((byte >> 4) ^ key) << 4) + (byte & 15);
 }
 
+// Workgroup id -> (group, member): the nvb workgroups of one (head, segment)
+// read the same chunk summaries, so they are placed on one XCD (consecutive
+// workgroup ids go round-robin over the 8 XCDs, each with its own L2) and
+// dispatched together: member k of group P is workgroup
+// ((P / 8) * m + k) * 8 + P % 8.  A grid that is not a whole number of
+// 8-group rounds keeps the plain order.
+__device__ __forceinline__ int2 xcd_group(int id, int m, int ngroups) {
+  if (ngroups % 8 != 0) return make_int2(id / m, id % m);
+  const int xcd = id % 8, slot = id / 8;
+  return make_int2((slot / m) * 8 + xcd, slot % m);
+}
+
 template <int WORDS, int NTH> constexpr int words_per_thread() { return (WORDS + NTH - 1) / NTH; }
 
 // Tokens per unit: 16 NW (bf16) or 8 NW (fp32), at least 16; a unit's tiles
@@ -93,10 +105,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
   const int NC = T / C;
   const int NSB = C / SB;
   const int nvb = NCOL / NV;
-  const int bh = blockIdx.x / (nseg * nvb);
-  const int rem = blockIdx.x - bh * (nseg * nvb);
-  const int seg = rem / nvb;
-  const int vb = rem - seg * nvb;
+  const int2 gm = xcd_group(blockIdx.x, nvb, static_cast<int>(gridDim.x) / nvb);
+  const int bh = gm.x / nseg;
+  const int seg = gm.x - bh * nseg;
+  const int vb = gm.y;
   const int L = (NC + nseg - 1) / nseg;  // chunks per segment
   const int cbeg = min(NC, seg * L);
   const int cend = min(NC, cbeg + L);
@@ -343,10 +355,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
   const int NC = T / C;
   const int NSB = C / SB;
   const int nvb = NCOL / NV;
-  const int bh = blockIdx.x / (nseg * nvb);
-  const int rem = blockIdx.x - bh * (nseg * nvb);
-  const int seg = rem / nvb;
-  const int vb = rem - seg * nvb;
+  const int2 gm = xcd_group(blockIdx.x, nvb, static_cast<int>(gridDim.x) / nvb);
+  const int bh = gm.x / nseg;
+  const int seg = gm.x - bh * nseg;
+  const int vb = gm.y;
   const int L = (NC + nseg - 1) / nseg;  // chunks per segment
   const int cbeg = min(NC, seg * L);
   const int cend = min(NC, cbeg + L);
