@@ -264,13 +264,21 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
                   : nullptr;
 #pragma unroll 2
     for (int m = 0; m < SB / 16; ++m) {
-      f32x4 Oa = zero4(), Da = zero4();
+      // two accumulators per product (even and odd key tiles): independent
+      // MFMA chains of half the length
+      f32x4 Oa0 = zero4(), Oa1 = zero4(), Da0 = zero4(), Da1 = zero4();
 #pragma unroll
-      for (int s = 0; s < RT; ++s) {
-        const int a = swz<LW>(16 * m + c16, (16 * s + 4 * g) * SZ);
-        if (!TRANS && o) Oa = M::mma(M::load(reinterpret_cast<const TC*>(sQ + a)), Sf[s], Oa);
-        Da = M::mma(M::load(reinterpret_cast<const TC*>(sW + a)), Sf[s], Da);
+      for (int s = 0; s < RT; s += 2) {
+        const int a0 = swz<LW>(16 * m + c16, (16 * s + 4 * g) * SZ);
+        const int a1 = swz<LW>(16 * m + c16, (16 * (s + 1) + 4 * g) * SZ);
+        if constexpr (!TRANS) {
+          Oa0 = M::mma(M::load(reinterpret_cast<const TC*>(sQ + a0)), Sf[s], Oa0);
+          Oa1 = M::mma(M::load(reinterpret_cast<const TC*>(sQ + a1)), Sf[s + 1], Oa1);
+        }
+        Da0 = M::mma(M::load(reinterpret_cast<const TC*>(sW + a0)), Sf[s], Da0);
+        Da1 = M::mma(M::load(reinterpret_cast<const TC*>(sW + a1)), Sf[s + 1], Da1);
       }
+      const f32x4 Oa = Oa0 + Oa1, Da = Da0 + Da1;
       const int au = swz<LK>(16 * wave + c16, (16 * m + 4 * g) * SZ);
       if (!TRANS && o) {
         const f32x4 ot = load4(reinterpret_cast<const TC*>(sO + au));
@@ -490,10 +498,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
 #pragma unroll 2
     for (int m = 0; m < SB / 16; ++m) {
       // X = Kbar_m dS_next (16 tokens x this wave's 16 columns)
-      f32x4 X = zero4();
+      f32x4 X0 = zero4(), X1 = zero4();  // even and odd key tiles: two independent chains
 #pragma unroll
-      for (int s = 0; s < RT; ++s)
-        X = M::mma(M::load(reinterpret_cast<const TC*>(sKb + swz<LW>(16 * m + c16, (16 * s + 4 * g) * SZ))), dSf[s], X);
+      for (int s = 0; s < RT; s += 2) {
+        X0 = M::mma(M::load(reinterpret_cast<const TC*>(sKb + swz<LW>(16 * m + c16, (16 * s + 4 * g) * SZ))), dSf[s],
+                    X0);
+        X1 = M::mma(M::load(reinterpret_cast<const TC*>(sKb + swz<LW>(16 * m + c16, (16 * (s + 1) + 4 * g) * SZ))),
+                    dSf[s + 1], X1);
+      }
+      const f32x4 X = X0 + X1;
       // dO rows as the right operand (tokens along the contraction): one
       // identity product turns the row fragment around
       const f32x4 dot = M::mma(
