@@ -827,15 +827,22 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         ptf = M::from_f32(pv);
         ttf = M::from_f32(tv);
       }
-      f32x4 acc[NT];
+      // even and odd key tiles in two independent MFMA chains
+      f32x4 acc[NT], acc1[NT];
 #pragma unroll
-      for (int n = 0; n < NT; ++n) acc[n] = zero4();
+      for (int n = 0; n < NT; ++n) acc[n] = acc1[n] = zero4();
 #pragma unroll
-      for (int s = 0; s < RT; ++s) {
+      for (int s = 0; s < RT; s += 2) {
         const frag ka = M::load(&sRowA[c16][16 * s + 4 * g]);
+        const frag kb2 = M::load(&sRowA[c16][16 * (s + 1) + 4 * g]);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) acc[n] = M::mma(ka, M::from_f32(D[s][n]), acc[n]);
+        for (int n = 0; n < NT; ++n) {
+          acc[n] = M::mma(ka, M::from_f32(D[s][n]), acc[n]);
+          acc1[n] = M::mma(kb2, M::from_f32(D[s + 1][n]), acc1[n]);
+        }
       }
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n] += acc1[n];
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         f32x4 dov;
