@@ -38,34 +38,53 @@ __global__ __launch_bounds__(STEP_THREADS) void step_kernel(
   __shared__ float s_red[2][STEP_THREADS / 64][4][STEP_COLS];  // [r|p][wave][row-group in wave][col]
   __shared__ float s_qk;
 
+  // Every global read is issued before the first wait, in the order it is
+  // needed: the per-head vectors, this thread's part of the state slice, and
+  // its write and v words (kept raw until used).  Loads complete in order, so
+  // the wait for the vectors does not wait for the state.
   const size_t vk = static_cast<size_t>(head) * DK;
-  for (int j = tid; j < DK; j += STEP_THREADS) {
-    float kj = Elem<Tin>::load(k, vk + j);
-    s_alpha[j] = __expf(Elem<Tin>::load(log_a, vk + j));
-    s_ek[j] = Elem<Tin>::load(erase, vk + j) * kj;
-    // readout gate per token, static per (head, channel), or none (its
-    // address then points into q and the value is not used)
-    const Tin* gsrc = gmode == GAMMA_NONE ? q : gamma;
-    const float graw = Elem<Tin>::load(gsrc, gmode == GAMMA_STATIC ? static_cast<size_t>(head % H) * DK + j : vk + j);
-    const float gj = gmode == GAMMA_NONE ? 1.f : graw;
-    s_qt[j] = gj * Elem<Tin>::load(q, vk + j);
-    s_k[j] = kj;
+  constexpr int VPT = (DK + STEP_THREADS - 1) / STEP_THREADS;  // vector elements per thread
+  float xk[VPT], xl[VPT], xe[VPT], xg[VPT], xq[VPT];
+  // readout gate per token, static per (head, channel), or none (its address
+  // then points into q and the value is not used)
+  const Tin* gsrc = gmode == GAMMA_NONE ? q : gamma;
+#pragma unroll
+  for (int e = 0; e < VPT; ++e) {
+    const int j = min(tid + e * STEP_THREADS, DK - 1);
+    xk[e] = Elem<Tin>::load(k, vk + j);
+    xl[e] = Elem<Tin>::load(log_a, vk + j);
+    xe[e] = Elem<Tin>::load(erase, vk + j);
+    xg[e] = Elem<Tin>::load(gsrc, gmode == GAMMA_STATIC ? static_cast<size_t>(head % H) * DK + j : vk + j);
+    xq[e] = Elem<Tin>::load(q, vk + j);
+  }
+  const int col0 = slice * STEP_COLS + 4 * cg;
+  float* Sh = S + static_cast<size_t>(head) * DK * DV;
+  f32x4 st[RP];
+#pragma unroll
+  for (int p = 0; p < RP; ++p) st[p] = load4(Sh + static_cast<size_t>(rg + 16 * p) * DV + col0);
+  const size_t vv = static_cast<size_t>(head) * DV + col0;
+  const typename Raw4<Tin>::type wraw = *reinterpret_cast<const typename Raw4<Tin>::type*>(write + vv);
+  const typename Raw4<Tin>::type vraw = *reinterpret_cast<const typename Raw4<Tin>::type*>(v + vv);
+
+  // (threads past DK repeat element DK-1 with the same values: no branch, so
+  // the compiler does not drain the state loads at a join)
+#pragma unroll
+  for (int e = 0; e < VPT; ++e) {
+    const int j = min(tid + e * STEP_THREADS, DK - 1);
+    s_alpha[j] = __expf(xl[e]);
+    s_ek[j] = xe[e] * xk[e];
+    s_qt[j] = (gmode == GAMMA_NONE ? 1.f : xg[e]) * xq[e];
+    s_k[j] = xk[e];
   }
   __syncthreads();
 
-  // q~ . k : one wave reduces it while the others start streaming S.
+  // q~ . k : one wave reduces it while the others go on with the state.
   if (tid < 64) {
     float acc = 0.f;
     for (int j = tid; j < DK; j += 64) acc += s_qt[j] * s_k[j];
     acc = wave_sum(acc);
     if (tid == 0) s_qk = acc;
   }
-
-  const int col0 = slice * STEP_COLS + 4 * cg;
-  float* Sh = S + static_cast<size_t>(head) * DK * DV;
-  f32x4 st[RP];
-#pragma unroll
-  for (int p = 0; p < RP; ++p) st[p] = load4(Sh + static_cast<size_t>(rg + 16 * p) * DV + col0);
 
   f32x4 racc = zero4(), pacc = zero4();
 #pragma unroll
@@ -103,8 +122,7 @@ __global__ __launch_bounds__(STEP_THREADS) void step_kernel(
       rr[i] += s_red[0][w][0][4 * cg + i];
       pp[i] += s_red[1][w][0][4 * cg + i];
     }
-  const size_t vv = static_cast<size_t>(head) * DV + col0;
-  f32x4 u = load4(write + vv) * load4(v + vv);
+  const f32x4 u = load4(reinterpret_cast<const Tin*>(&wraw)) * load4(reinterpret_cast<const Tin*>(&vraw));
   f32x4 d = u - pp;
   if (tid < 16) {
     f32x4 ov = rr + s_qk * d;
