@@ -243,8 +243,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   auto leaf_pair = [&](const TC (*A)[PV], const TC (*Bm)[PV]) -> f32x4 {
     f32x4 acc = zero4();
 #pragma unroll
-    for (int kk = 0; kk < DV / 16; ++kk)
-      acc = M::mma(M::load(&A[c16][16 * kk + 4 * g]), M::load(&Bm[c16][16 * kk + 4 * g]), acc);
+    for (int kk = 0; kk < DV / 16; kk += 2)
+      acc = M::mma2(M::load(&A[c16][16 * kk + 4 * g]), M::load(&Bm[c16][16 * kk + 4 * g]),
+                    M::load(&A[c16][16 * kk + 16 + 4 * g]), M::load(&Bm[c16][16 * kk + 16 + 4 * g]), acc);
     return acc;
   };
   // dst[r][i] = A_r . B_i, masked to i <= r (or i < r when strict): the leaf
@@ -704,10 +705,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
 #pragma unroll
         for (int n = 0; n < NT; ++n) S[s][n] *= gc;
 #pragma unroll
-        for (int m = 0; m < NB; ++m) {
+        for (int m = 0; m < NB; m += 2) {
           const frag ka = M::load(&sSD[16 * s + c16][16 * m + 4 * g]);
+          const frag ka1 = M::load(&sSD[16 * s + c16][16 * m + 16 + 4 * g]);
 #pragma unroll
-          for (int n = 0; n < NT; ++n) S[s][n] = M::mma(ka, dcol[m][n], S[s][n]);
+          for (int n = 0; n < NT; ++n) S[s][n] = M::mma2(ka, dcol[m][n], ka1, dcol[m + 1][n], S[s][n]);
         }
       }
     }
@@ -744,10 +746,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
 #pragma unroll
         for (int n = 0; n < NT; ++n) xs[n] = zero4();
 #pragma unroll
-        for (int s = 0; s < RT; ++s) {
+        for (int s = 0; s < RT; s += 2) {
           const frag xa = M::load(&sRowA[c16][16 * s + 4 * g]);
+          const frag xa1 = M::load(&sRowA[c16][16 * s + 16 + 4 * g]);
 #pragma unroll
-          for (int n = 0; n < NT; ++n) xs[n] = M::mma(xa, Sf[s][n], xs[n]);
+          for (int n = 0; n < NT; ++n) xs[n] = M::mma2(xa, Sf[s][n], xa1, Sf[s + 1][n], xs[n]);
         }
         const frag ta = M::load(&sT[c16][4 * g]);
 #pragma unroll
@@ -827,22 +830,18 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         ptf = M::from_f32(pv);
         ttf = M::from_f32(tv);
       }
-      // even and odd key tiles in two independent MFMA chains
-      f32x4 acc[NT], acc1[NT];
+      // key tiles in pairs, one 32-deep product each
+      f32x4 acc[NT];
 #pragma unroll
-      for (int n = 0; n < NT; ++n) acc[n] = acc1[n] = zero4();
+      for (int n = 0; n < NT; ++n) acc[n] = zero4();
 #pragma unroll
       for (int s = 0; s < RT; s += 2) {
         const frag ka = M::load(&sRowA[c16][16 * s + 4 * g]);
         const frag kb2 = M::load(&sRowA[c16][16 * (s + 1) + 4 * g]);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          acc[n] = M::mma(ka, M::from_f32(D[s][n]), acc[n]);
-          acc1[n] = M::mma(kb2, M::from_f32(D[s + 1][n]), acc1[n]);
-        }
+        for (int n = 0; n < NT; ++n)
+          acc[n] = M::mma2(ka, M::from_f32(D[s][n]), kb2, M::from_f32(D[s + 1][n]), acc[n]);
       }
-#pragma unroll
-      for (int n = 0; n < NT; ++n) acc[n] += acc1[n];
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         f32x4 dov;
@@ -899,27 +898,44 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         }
       }
       __syncthreads();  // also publishes the dR rows
+      // contraction tiles in pairs (one 32-deep product each) when the pass
+      // holds an even number of them
+      constexpr int KP = (SW / 16) % 2 == 0 ? 2 : 1;
+      auto mmk = [&](const frag* a, const frag* b, f32x4 c) -> f32x4 {
+        if constexpr (KP == 2) return M::mma2(a[0], b[0], a[1], b[1], c);
+        else return M::mma(a[0], b[0], c);
+      };
 #pragma unroll
-      for (int kk = 0; kk < SW / 16; ++kk) {
+      for (int kk = 0; kk < SW / 16; kk += KP) {
         const int cc = p * SW + 16 * kk + 4 * g;
-        const frag al = M::load(&dlJ[c16][cc]);
-        const frag ao = M::load(&sDO[c16][cc]);
-        const frag ar = M::load(&sDR[c16][cc]);
+        frag al[KP], ao[KP], ar[KP];
+#pragma unroll
+        for (int u = 0; u < KP; ++u) {
+          al[u] = M::load(&dlJ[c16][cc + 16 * u]);
+          ao[u] = M::load(&sDO[c16][cc + 16 * u]);
+          ar[u] = M::load(&sDR[c16][cc + 16 * u]);
+        }
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          const frag bd = M::load(&sSD[colv(n)][16 * kk + 4 * g]);
-          const frag bs = DIRECT ? s0f[n][kk] : M::load(&sSS[colv(n)][16 * kk + 4 * g]);
-          acck[n] = M::mma(al, bd, acck[n]);
-          accq[n] = M::mma(ao, bs, accq[n]);
-          acce[n] = M::mma(ar, bs, acce[n]);
+          frag bd[KP], bs[KP];
+#pragma unroll
+          for (int u = 0; u < KP; ++u) {
+            bd[u] = M::load(&sSD[colv(n)][16 * (kk + u) + 4 * g]);
+            bs[u] = DIRECT ? s0f[n][kk + u] : M::load(&sSS[colv(n)][16 * (kk + u) + 4 * g]);
+          }
+          acck[n] = mmk(al, bd, acck[n]);
+          accq[n] = mmk(ao, bs, accq[n]);
+          acce[n] = mmk(ar, bs, acce[n]);
         }
         if constexpr (SPLIT == 1) {
           // this wave's shared products (dO or dR rows, the same operands)
 #pragma unroll
           for (int q2 = 0; q2 < PPW; ++q2) {
             const int pr = wave + q2 * NW;
-            const frag ax = (pr & 1) ? ar : ao;
-            gacc[q2] = M::mma(ax, M::load(&sDL[(DIRECT ? 16 * (pr >> 1) : 0) + c16][cc]), gacc[q2]);
+            frag bl[KP];
+#pragma unroll
+            for (int u = 0; u < KP; ++u) bl[u] = M::load(&sDL[(DIRECT ? 16 * (pr >> 1) : 0) + c16][cc + 16 * u]);
+            gacc[q2] = mmk((pr & 1) ? ar : ao, bl, gacc[q2]);
           }
         }
       }
@@ -931,9 +947,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         const int pr = wave + q2 * NW;
         const TC (*xr)[PV] = (pr & 1) ? sDR : sDO;
 #pragma unroll
-        for (int kk = 0; kk < DV / 16; ++kk)
-          gacc[q2] = M::mma(M::load(&xr[c16][16 * kk + 4 * g]),
-                            M::load(&sDL[(DIRECT ? 16 * (pr >> 1) : 0) + c16][16 * kk + 4 * g]), gacc[q2]);
+        for (int kk = 0; kk < DV / 16; kk += 2) {
+          const TC* dl = &sDL[(DIRECT ? 16 * (pr >> 1) : 0) + c16][16 * kk + 4 * g];
+          gacc[q2] = M::mma2(M::load(&xr[c16][16 * kk + 4 * g]), M::load(dl), M::load(&xr[c16][16 * kk + 16 + 4 * g]),
+                             M::load(dl + 16), gacc[q2]);
+        }
       }
     }
 #pragma unroll
@@ -1004,8 +1022,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
           zz[i] = ok[n][i] * __expf(-oloc[n][i]);
         }
         const frag zb = M::from_f32(zz);
-        acck[n] = M::mma(l0f, M::from_f32(yh), acck[n]);
-        acck[n] = M::mma(l1f, M::from_f32(xh), acck[n]);
+        acck[n] = M::mma2(l0f, M::from_f32(yh), l1f, M::from_f32(xh), acck[n]);
         accq[n] = M::mma(m0f, zb, accq[n]);
         acce[n] = M::mma(m1f, zb, acce[n]);
       }
@@ -1081,10 +1098,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         const frag xa = M::load(&sTA[16 * s + c16][4 * g]);
         const f32x4 gs = decay_scale(s);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const f32x4 t = M::mma(ya, dOf[n], D[s][n] * gs);
-          D[s][n] = M::mma(xa, dRf[n], t);
-        }
+        for (int n = 0; n < NT; ++n) D[s][n] = M::mma2(ya, dOf[n], xa, dRf[n], D[s][n] * gs);
       }
     }
     __syncthreads();

@@ -22,6 +22,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // ---- bf16 storage helpers (raw 16-bit patterns) ------------------------------
 
@@ -100,6 +102,19 @@ __device__ __forceinline__ void store4(uint16_t* p, f32x4 v) {
 // acc += A(16x16 bf16) * B(16x16 bf16); operands packed as 4 bf16 per lane.
 __device__ __forceinline__ f32x4 mma16_bf16(i16x4 a, i16x4 b, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+}
+
+// acc += A1 B1 + A2 B2 for two 16-deep bf16 products as ONE 32-deep product
+// (v_mfma_f32_16x16x32_bf16, whose lane l holds contraction slots
+// 8*(l/16) + i, i < 8): both operands take the first pair's four values in
+// slots 0-3 and the second pair's in slots 4-7, so the slots match up and the
+// sum is the same.  On gfx950 the 32-deep product issues in the same time as
+// one 16-deep product.
+__device__ __forceinline__ f32x4 mma32_bf16(i16x4 a1, i16x4 b1, i16x4 a2, i16x4 b2, f32x4 acc) {
+  const i16x8 a = __builtin_shufflevector(a1, a2, 0, 1, 2, 3, 4, 5, 6, 7);
+  const i16x8 b = __builtin_shufflevector(b1, b2, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                 acc, 0, 0, 0);
 }
 
 // acc += A(16x4 f32) * B(4x16 f32); one value per lane.

@@ -137,13 +137,33 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
   __shared__ __attribute__((aligned(16))) TC sKe[NBUF][DK][20];  // (k * exp(B_{I+1} - Lam))^T
   __shared__ __attribute__((aligned(16))) TC sR[NBUF][NH][20];   // [U | K~]^T
   __shared__ __attribute__((aligned(16))) TC sQh[NBUF][DK][20];  // (qt * exp(Lam))^T
-  __shared__ float sAw[16][17];
-  __shared__ float sPw[16][17];
-  __shared__ float sTw[16][17];
+  __shared__ float sAw[16][17];  // A_II and P_II of a leaf beyond the safe range
   __shared__ float sPf[16][17];
   __shared__ __attribute__((aligned(16))) TC sT[16][20];
   __shared__ __attribute__((aligned(16))) TC sP[16][20];
   __shared__ __attribute__((aligned(16))) TC sStage[16][2 * DK + 8];
+
+  // ---- the next block's inputs are loaded one block ahead (4 tokens of
+  // channel ej), kept raw until used (a conversion at the load would wait
+  // for it); no load is under a branch, so they stay in flight.  The first
+  // block's are issued before the prologue's own loads, so that both wait
+  // on one round trip ----
+  Tin pk[4], pe[4], pq[4], pg[4], pv[4], pw[4], pl[4];
+  auto prefetch = [&](int I) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const uint32_t o = gi(16 * I + 4 * part + rr, ej);
+      pk[rr] = *at(kb, o);
+      pe[rr] = *at(eb, o);
+      pq[rr] = *at(qb, o);
+      pg[rr] = *at(gsel, static_cast<uint32_t>(16 * I + 4 * part + rr) * gts + static_cast<uint32_t>(ej));
+      pv[rr] = *at(vb, o);
+      pw[rr] = *at(wb, o);
+      pl[rr] = *at(lb, o);
+    }
+  };
+
+  prefetch(0);
 
   // ---- sums of the log-decay over each part of each block, the block
   // boundaries' factors, and the blocks beyond LEAF_SAFE_RANGE ----
@@ -190,24 +210,6 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
   for (int s = 0; s < RT; ++s)
 #pragma unroll
     for (int n = 0; n < NT; ++n) Hs[s][n] = zero4();
-
-  // ---- the next block's inputs are loaded one block ahead (4 tokens of
-  // channel ej), kept raw until used (a conversion at the load would wait
-  // for it); no load is under a branch, so they stay in flight ----
-  Tin pk[4], pe[4], pq[4], pg[4], pv[4], pw[4], pl[4];
-  auto prefetch = [&](int I) {
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const uint32_t o = gi(16 * I + 4 * part + rr, ej);
-      pk[rr] = *at(kb, o);
-      pe[rr] = *at(eb, o);
-      pq[rr] = *at(qb, o);
-      pg[rr] = *at(gsel, static_cast<uint32_t>(16 * I + 4 * part + rr) * gts + static_cast<uint32_t>(ej));
-      pv[rr] = *at(vb, o);
-      pw[rr] = *at(wb, o);
-      pl[rr] = *at(lb, o);
-    }
-  };
 
   // ---- elementwise work of block I (4 tokens of channel ej) into its
   // buffer: the scaled operand rows and transposed tiles, Kbar of the summary;
@@ -284,16 +286,16 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
     for (int rr = 0; rr < 4; ++rr) out.Kb[static_cast<size_t>(r0 + 4 * part + rr) * DK + ej] = M::cvt(kbT[rr]);
   };
 
-  // T_II = (I + A_II)^-1 from A_II in sAw, with P_II from sPf, into sT, sP
-  // and the summary, by wave 0
-  auto leaf_inverse = [&](int I) {
-    const f32x4 t = neumann16(sAw, sPw, sTw);
+  // T_II = (I + A_II)^-1 from A_II (both lane layouts, see neumann16), with
+  // P_II (accumulator layout), into sT, sP and the summary, by wave 0
+  auto leaf_inverse = [&](int I, f32x4 a_acc, f32x4 a_tr, f32x4 p_acc) {
+    const f32x4 t = neumann16(a_acc, a_tr);
     TC* tp = out.TP + static_cast<size_t>(I) * 512;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * g + i;
       const TC tv = M::cvt(t[i]);
-      const TC pv = M::cvt(sPf[r][c16]);
+      const TC pv = M::cvt(p_acc[i]);
       sT[r][c16] = tv;
       sP[r][c16] = pv;
       tp[r * 16 + c16] = tv;  // kept for the backward
@@ -301,7 +303,6 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
     }
   };
 
-  prefetch(0);
   if (PIPE) {
     elementwise(0);
     __syncthreads();
@@ -326,33 +327,45 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
     }
     if (I > 0) {
 #pragma unroll
-      for (int s = 0; s < RT; ++s) {
+      for (int s = 0; s < RT; s += 2) {
         const frag xa = M::load(&sX[bb][c16][16 * s + 4 * g]);
         const frag ya = M::load(&sY[bb][c16][16 * s + 4 * g]);
+        const frag xa1 = M::load(&sX[bb][c16][16 * s + 16 + 4 * g]);
+        const frag ya1 = M::load(&sY[bb][c16][16 * s + 16 + 4 * g]);
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           const frag hb = M::from_f32(Hs[s][n]);
-          XH[n] = M::mma(xa, hb, XH[n]);
-          YH[n] = M::mma(ya, hb, YH[n]);
+          const frag hb1 = M::from_f32(Hs[s + 1][n]);
+          XH[n] = M::mma2(xa, hb, xa1, hb1, XH[n]);
+          YH[n] = M::mma2(ya, hb, ya1, hb1, YH[n]);
         }
       }
     }
     // ---- leaf: A_II, P_II, T_II (wave 0, when the leaf is within range) ----
     if (safe && wave == 0) {
-      f32x4 a = zero4(), p = zero4();
+      // A = X Z^T and P = Y Z^T in the accumulator layout, and A^T = Z X^T,
+      // i.e. A in the other layout, from the same operands swapped
+      f32x4 a = zero4(), at = zero4(), p = zero4();
 #pragma unroll
-      for (int s = 0; s < RT; ++s) {
+      for (int s = 0; s < RT; s += 2) {
         const frag zb = M::load(&sZ[bb][c16][16 * s + 4 * g]);
-        a = M::mma(M::load(&sX[bb][c16][16 * s + 4 * g]), zb, a);
-        p = M::mma(M::load(&sY[bb][c16][16 * s + 4 * g]), zb, p);
+        const frag xa = M::load(&sX[bb][c16][16 * s + 4 * g]);
+        const frag ya = M::load(&sY[bb][c16][16 * s + 4 * g]);
+        const frag zb1 = M::load(&sZ[bb][c16][16 * s + 16 + 4 * g]);
+        const frag xa1 = M::load(&sX[bb][c16][16 * s + 16 + 4 * g]);
+        const frag ya1 = M::load(&sY[bb][c16][16 * s + 16 + 4 * g]);
+        a = M::mma2(xa, zb, xa1, zb1, a);
+        at = M::mma2(zb, xa, zb1, xa1, at);
+        p = M::mma2(ya, zb, ya1, zb1, p);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * g + i;
-        sAw[r][c16] = c16 < r ? a[i] : 0.f;
-        sPf[r][c16] = c16 <= r ? p[i] : 0.f;
+        a[i] = c16 < r ? a[i] : 0.f;    // A[r][c16], strictly lower
+        at[i] = r < c16 ? at[i] : 0.f;  // A[c16][r]
+        p[i] = c16 <= r ? p[i] : 0.f;
       }
-      leaf_inverse(I);
+      leaf_inverse(I, a, at, p);
     }
     // ---- the next block's elementwise work, beside this block's products ----
     if (PIPE && I + 1 < NB) elementwise(I + 1);
@@ -377,7 +390,16 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
         sPf[r][i] = p;
       }
       __syncthreads();
-      if (wave == 0) leaf_inverse(I);
+      if (wave == 0) {
+        f32x4 a, at, p;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a[i] = sAw[4 * g + i][c16];
+          at[i] = sAw[c16][4 * g + i];
+          p[i] = sPf[4 * g + i][c16];
+        }
+        leaf_inverse(I, a, at, p);
+      }
     }
     __syncthreads();
 
