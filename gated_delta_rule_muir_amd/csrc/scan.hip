@@ -27,12 +27,35 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Byte offset of (row, byte) in an LDS tile with rows of L bytes (a power of
-// two >= 32), 16-byte chunks permuted per row.
-template <int L> __device__ __forceinline__ int swz(int row, int byte) {
-  constexpr int CPR = L / 16;
-  const int key = CPR >= 16 ? (row & 15) : ((row / (16 / CPR)) & (CPR - 1));
-  return row * L + (((byte >> 4) ^ key) << 4) + (byte & 15);
+// LDS tile addressing.  A tile has rows of L bytes; its G-byte granules (G =
+// 8 for bf16 fragments, read 8 bytes per lane, or 16 for fp32 ones) are
+// XOR-permuted per row.  LDS serves a fragment read 128 bytes at a time (32
+// banks of 4 bytes): 16 lanes of an 8-byte read, 8 of a 16-byte one, each lane
+// on its own row at the same column.  The key spreads those rows over distinct
+// granules of the 128-byte bank window (rows shorter than the window share
+// it, and the key then runs over the rows of one window).  XOR on 16-byte
+// chunks would leave 8-byte reads two-way conflicted.
+template <int L, int G> __device__ __forceinline__ int swz_key(int row) {
+  constexpr int S = L / G;                       // granules per row
+  constexpr int WIN = 128 / G;                   // granules per bank window
+  constexpr int RPW = S >= WIN ? 1 : WIN / S;    // rows per bank window
+  constexpr int KS = S >= WIN ? WIN : S;
+  return (row / RPW) & (KS - 1);
+}
+template <int L, int G> __device__ __forceinline__ int swz(int row, int byte) {
+  return row * L + (((byte / G) ^ swz_key<L, G>(row)) * G) + (byte % G);
+}
+// Writes the 16-byte word holding bytes [16 c, 16 c + 16) of a row.  With
+// 8-byte granules its halves land in one aligned 16-byte chunk, swapped when
+// the key is odd.
+template <int L, int G> __device__ __forceinline__ void put16(char* tile, int row, int c, u32x4 w) {
+  if constexpr (G == 16) {
+    *reinterpret_cast<u32x4*>(tile + swz<L, 16>(row, 16 * c)) = w;
+  } else {
+    const int key = swz_key<L, 8>(row);
+    const u32x4 sw = {w[2], w[3], w[0], w[1]};
+    *reinterpret_cast<u32x4*>(tile + row * L + ((c ^ (key >> 1)) << 4)) = (key & 1) ? sw : w;
+  }
 }
 
 // Workgroup id -> (group, member): the nvb workgroups of one (head, segment)
@@ -87,6 +110,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
   constexpr int NV = 16 * NW;
   constexpr int NTH = 64 * NW;
   constexpr int SZ = sizeof(TC);
+  constexpr int GR = SZ == 2 ? 8 : 16;  // LDS swizzle granule: the fragment read size
   constexpr int SB = scan_unit<TC, NW>();
   constexpr int LW = DK * SZ;       // bytes per W / Q' row
   constexpr int LK = SB * SZ;       // bytes per unit segment of a Kbar^T / U~^T / O~^T row
@@ -179,22 +203,20 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
 #pragma unroll
     for (int k = 0; k < PW; ++k) {
       const int w = min(tid + k * NTH, W_WORDS - 1);
-      const int a = swz<LW>(w / CW, 16 * (w % CW));
-      *reinterpret_cast<u32x4*>(sW + a) = rw[k];
-      if constexpr (!TRANS) *reinterpret_cast<u32x4*>(sQ + a) = rq[k];
+      put16<LW, GR>(sW, w / CW, w % CW, rw[k]);
+      if constexpr (!TRANS) put16<LW, GR>(sQ, w / CW, w % CW, rq[k]);
     }
 #pragma unroll
     for (int k = 0; k < PK; ++k) {
       const int w = min(tid + k * NTH, K_WORDS - 1);
-      *reinterpret_cast<u32x4*>(sK + swz<LK>(w / CK, 16 * (w % CK))) = rk[k];
+      put16<LK, GR>(sK, w / CK, w % CK, rk[k]);
     }
 #pragma unroll
     for (int k = 0; k < PU; ++k) {
       const int w = min(tid + k * NTH, U_WORDS - 1);
-      const int a = swz<LK>(w / CK, 16 * (w % CK));
       const u32x4 zw = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(sU + a) = pcols ? zw : ru[k];
-      if constexpr (!TRANS) *reinterpret_cast<u32x4*>(sO + a) = ro[k];
+      put16<LK, GR>(sU, w / CK, w % CK, pcols ? zw : ru[k]);
+      if constexpr (!TRANS) put16<LK, GR>(sO, w / CK, w % CK, ro[k]);
     }
 #pragma unroll
     for (int k = 0; k < PG; ++k) {
@@ -269,8 +291,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
       f32x4 Oa0 = zero4(), Oa1 = zero4(), Da0 = zero4(), Da1 = zero4();
 #pragma unroll
       for (int s = 0; s < RT; s += 2) {
-        const int a0 = swz<LW>(16 * m + c16, (16 * s + 4 * g) * SZ);
-        const int a1 = swz<LW>(16 * m + c16, (16 * (s + 1) + 4 * g) * SZ);
+        const int a0 = swz<LW, GR>(16 * m + c16, (16 * s + 4 * g) * SZ);
+        const int a1 = swz<LW, GR>(16 * m + c16, (16 * (s + 1) + 4 * g) * SZ);
         if constexpr (!TRANS) {
           Oa0 = M::mma(M::load(reinterpret_cast<const TC*>(sQ + a0)), Sf[s], Oa0);
           Oa1 = M::mma(M::load(reinterpret_cast<const TC*>(sQ + a1)), Sf[s + 1], Oa1);
@@ -279,7 +301,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
         Da1 = M::mma(M::load(reinterpret_cast<const TC*>(sW + a1)), Sf[s + 1], Da1);
       }
       const f32x4 Oa = Oa0 + Oa1, Da = Da0 + Da1;
-      const int au = swz<LK>(16 * wave + c16, (16 * m + 4 * g) * SZ);
+      const int au = swz<LK, GR>(16 * wave + c16, (16 * m + 4 * g) * SZ);
       if (!TRANS && o) {
         const f32x4 ot = load4(reinterpret_cast<const TC*>(sO + au));
         // tokens 4g+i, column c16 -> token c16, columns 4g..4g+3
@@ -295,7 +317,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
       }
 #pragma unroll
       for (int s = 0; s < RT; ++s)
-        dS[s] = M::mma(M::load(reinterpret_cast<const TC*>(sK + swz<LK>(16 * s + c16, (16 * m + 4 * g) * SZ))),
+        dS[s] = M::mma(M::load(reinterpret_cast<const TC*>(sK + swz<LK, GR>(16 * s + c16, (16 * m + 4 * g) * SZ))),
                        df, dS[s]);
     }
     if (sb == NSB - 1) {
@@ -342,6 +364,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
   constexpr int NV = 16 * NW;
   constexpr int NTH = 64 * NW;
   constexpr int SZ = sizeof(TC);
+  constexpr int GR = SZ == 2 ? 8 : 16;  // LDS swizzle granule: the fragment read size
   constexpr int SB = scan_unit<TC, NW>();
   constexpr int LW = DK * SZ;       // bytes per Kbar row
   constexpr int LK = SB * SZ;       // bytes per unit segment of a W^T / Q'^T row
@@ -433,20 +456,19 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
 #pragma unroll
     for (int k = 0; k < PT; ++k) {
       const int w = min(tid + k * NTH, T_WORDS - 1);
-      const int a = swz<LK>(w / CK, 16 * (w % CK));
-      *reinterpret_cast<u32x4*>(sWt + a) = rt[k];
-      *reinterpret_cast<u32x4*>(sQt + a) = rq[k];
+      put16<LK, GR>(sWt, w / CK, w % CK, rt[k]);
+      put16<LK, GR>(sQt, w / CK, w % CK, rq[k]);
     }
 #pragma unroll
     for (int k = 0; k < PK; ++k) {
       const int w = min(tid + k * NTH, K_WORDS - 1);
-      *reinterpret_cast<u32x4*>(sKb + swz<LW>(w / CW, 16 * (w % CW))) = rk[k];
+      put16<LW, GR>(sKb, w / CW, w % CW, rk[k]);
     }
 #pragma unroll
     for (int k = 0; k < PO; ++k) {
       const int w = min(tid + k * NTH, O_WORDS - 1);
       const u32x4 zw = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(sDO + swz<LO>(w / CO, 16 * (w % CO))) = pcols ? zw : rd[k];
+      put16<LO, GR>(sDO, w / CO, w % CO, pcols ? zw : rd[k]);
     }
 #pragma unroll
     for (int k = 0; k < PG; ++k) {
@@ -501,22 +523,22 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
       f32x4 X0 = zero4(), X1 = zero4();  // even and odd key tiles: two independent chains
 #pragma unroll
       for (int s = 0; s < RT; s += 2) {
-        X0 = M::mma(M::load(reinterpret_cast<const TC*>(sKb + swz<LW>(16 * m + c16, (16 * s + 4 * g) * SZ))), dSf[s],
+        X0 = M::mma(M::load(reinterpret_cast<const TC*>(sKb + swz<LW, GR>(16 * m + c16, (16 * s + 4 * g) * SZ))), dSf[s],
                     X0);
-        X1 = M::mma(M::load(reinterpret_cast<const TC*>(sKb + swz<LW>(16 * m + c16, (16 * (s + 1) + 4 * g) * SZ))),
+        X1 = M::mma(M::load(reinterpret_cast<const TC*>(sKb + swz<LW, GR>(16 * m + c16, (16 * (s + 1) + 4 * g) * SZ))),
                     dSf[s + 1], X1);
       }
       const f32x4 X = X0 + X1;
       // dO rows as the right operand (tokens along the contraction): one
       // identity product turns the row fragment around
       const f32x4 dot = M::mma(
-          M::load(reinterpret_cast<const TC*>(sDO + swz<LO>(16 * m + c16, (16 * wave + 4 * g) * SZ))), ident,
+          M::load(reinterpret_cast<const TC*>(sDO + swz<LO, GR>(16 * m + c16, (16 * wave + 4 * g) * SZ))), ident,
           zero4());
       const frag dof = M::from_f32(dot);
       const frag xf = M::from_f32(-X);
 #pragma unroll
       for (int s = 0; s < RT; ++s) {
-        const int a = swz<LK>(16 * s + c16, (16 * m + 4 * g) * SZ);
+        const int a = swz<LK, GR>(16 * s + c16, (16 * m + 4 * g) * SZ);
         Z[s] = M::mma(M::load(reinterpret_cast<const TC*>(sQt + a)), dof, Z[s]);
         Z[s] = M::mma(M::load(reinterpret_cast<const TC*>(sWt + a)), xf, Z[s]);
       }
