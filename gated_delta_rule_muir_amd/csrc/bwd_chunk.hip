@@ -49,9 +49,21 @@ __host__ __device__ constexpr size_t bwd_scratch_bytes_tc(int C, int DK, int DV)
   return (static_cast<size_t>(C) * DV + static_cast<size_t>(C / 16) * DK * DV) * sizeof(TC);
 }
 
-// LDS row padding (elements) that keeps 16 lanes reading 4 consecutive
-// elements of 16 different rows on distinct banks.
-template <typename TC> constexpr int row_pad() { return sizeof(TC) == 2 ? 8 : 4; }
+// LDS row padding (elements).  LDS serves a fragment read 128 bytes at a
+// time (32 banks of 4 bytes): 16 lanes of an 8-byte bf16 read, 8 lanes of a
+// 16-byte fp32 one, each on its own row at the same column.  Rows padded by 8
+// bytes (bf16) or 16 bytes (fp32) put those rows on distinct banks; a 16-byte
+// pad would leave the bf16 reads two-way conflicted.  bf16 rows are then only
+// 8-byte aligned, so 16-byte words go into them as two 8-byte stores (put16).
+template <typename TC> constexpr int row_pad() { return 4; }  // 8 bytes (bf16), 16 bytes (fp32)
+
+// A 16-byte word into an LDS row that may be only 8-byte aligned.
+__device__ __forceinline__ void put16(void* p, u32x4 w) {
+  u32x2* q = reinterpret_cast<u32x2*>(p);
+  const u32x2 lo = {w[0], w[1]}, hi = {w[2], w[3]};
+  q[0] = lo;
+  q[1] = hi;
+}
 
 // Column passes for the two staged states ([DK][DV / SPLIT] each), chosen so
 // the kernel's LDS stays within 160 KB.
@@ -84,7 +96,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   constexpr int PT = DK + row_pad<TC>();
   constexpr int PV = DV + row_pad<TC>();
   constexpr int PS = SW + row_pad<TC>();
-  constexpr int TP = sizeof(TC) == 2 ? 24 : 20;  // row length of the [.][16] transposed tiles
+  constexpr int TP = 20;  // row length of the [.][16] transposed tiles (40 or 80 bytes: distinct banks over 16 or 8 rows)
   constexpr int EPT = 16 * DV / NTH;  // row-tile elements per thread
   constexpr int RC = DV / EPT;        // threads per row of a [16][DV] tile
   constexpr int EPW = 8 / static_cast<int>(sizeof(TC));  // elements per 8-byte word
@@ -422,7 +434,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
           for (int k2 = 0; k2 < IWT; ++k2) {
             const int w = lane + 64 * k2;
             const int row = w / IWR;
-            *reinterpret_cast<u32x4*>(&sIn[t][row][(w - row * IWR) * SEW]) = iw[sl * IWT + k2];
+            put16(&sIn[t][row][(w - row * IWR) * SEW], iw[sl * IWT + k2]);
           }
         }
       }
@@ -480,7 +492,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       const int w = tid + k2 * NTH;
       const int row = w / SWR;
       const int colw = (w - row * SWR) * SEW;
-      if (colw / SW == p) *reinterpret_cast<u32x4*>(&sSS[row][colw - p * SW]) = words[k2];
+      if (colw / SW == p) put16(&sSS[row][colw - p * SW], words[k2]);
     }
   };
   // Ke = k exp(B_{J+1} - Lam) rows; X = ek exp(Lam - B_J), Y = qt exp(Lam - B_J)
@@ -653,13 +665,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     for (int k2 = 0; k2 < DWT; ++k2) {
       const int w = tid + k2 * NTH;
       const int row = w / DWR;
-      *reinterpret_cast<u32x4*>(&sDL[row][(w - row * DWR) * SEW]) = dw[k2];
+      put16(&sDL[row][(w - row * DWR) * SEW], dw[k2]);
     }
 #pragma unroll
     for (int k2 = 0; k2 < KWT; ++k2) {
       const int w = tid + k2 * NTH;
       const int row = w / KWR;
-      *reinterpret_cast<u32x4*>(&sSD[row][(w - row * KWR) * SEW]) = kw[k2];
+      put16(&sSD[row][(w - row * KWR) * SEW], kw[k2]);
     }
     if (tid < DK / 4) *reinterpret_cast<u32x4*>(&sG[4 * tid]) = gcw;
     store_in();
