@@ -224,6 +224,25 @@ def decode_bench(m, torch, hiprt, N=64, H=16, d=128, steps=4096, seed=0):
     kt = sum(pool.elapsed_ms(2 * i, 2 * i + 1) for i in range(steps)) / steps
     pool.close()
     wall = (t1 - t0) * 1e3 / steps
+    # the same steps replayed from one captured HIP graph (as a serving loop
+    # would issue them), from the same initial state: its final state must
+    # equal the eager run's bit for bit
+    S_eager = S.clone()
+    graph = torch.cuda.CUDAGraph()
+    S.zero_()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for t in range(steps):
+            m.muir_step(q[t], k[t], v[t], log_a, erase[t], write[t], gamma[t], S, out=o)
+    S.zero_()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    graph_ok = bool(torch.equal(S, S_eager))
+    del graph, S_eager
+    gwall = (t3 - t2) * 1e3 / steps
     state_bytes = 2 * N * H * d * d * 4
     in_bytes = N * H * d * 2 * 7 + N * H * d * 2
     del q, k, v, erase, write, gamma
@@ -231,6 +250,8 @@ def decode_bench(m, torch, hiprt, N=64, H=16, d=128, steps=4096, seed=0):
     return {"workload": f"decode N={N} H={H} d={d} fp32 state, {steps} steps",
             "tokens_per_s": N / (wall * 1e-3), "wall_us_per_step": wall * 1e3,
             "kernel_us_per_step": kt * 1e3,
+            "graph_tokens_per_s": N / (gwall * 1e-3), "graph_wall_us_per_step": gwall * 1e3,
+            "graph_matches_eager": graph_ok,
             "hbm_GBs_at_kernel_time": (state_bytes + in_bytes) / (kt * 1e-3) / 1e9,
             "bytes_per_step": state_bytes + in_bytes,
             "note": "state (%d MiB) may be served partly from the 256 MB Infinity Cache" % (N * H * d * d * 4 >> 20)}
