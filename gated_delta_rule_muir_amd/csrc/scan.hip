@@ -517,7 +517,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
         Z[s] = zero4();
       }
     }
-#pragma unroll 2
+    // (the unit's token tiles fully unrolled: their X products are independent,
+    // so their MFMA chains interleave)
+#pragma unroll
     for (int m = 0; m < SB / 16; ++m) {
       // X = Kbar_m dS_next (16 tokens x this wave's 16 columns)
       f32x4 X0 = zero4(), X1 = zero4();  // even and odd key tiles: two independent chains
