@@ -250,10 +250,11 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
   for (int u = U0; u < U1; ++u) {
     const int c = u / NSB;
     const int sb = u - c * NSB;
-    __syncthreads();  // the previous unit's LDS reads are done
-    commit();
-    prefetch(u + 1 < U1 ? u + 1 : u);
-    __syncthreads();
+    // The chunk-start state is stored first, ahead of this unit's commit and
+    // the next unit's loads: vector memory instructions issue in order, so
+    // stores queued behind a unit of loads wait for them.  (Measured at B = 8,
+    // T = 4096, H = 16, d = 128, bf16: 304 us here, 321 us between the commit
+    // and the prefetch, 328 us after the prefetch.)
     if (sb == 0) {
       if (!TRANS && S_chunks) {
         // the chunk-start state, kept for the backward in the compute type
@@ -278,6 +279,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
         dS[s] = zero4();
       }
     }
+    __syncthreads();  // the previous unit's LDS reads are done
+    commit();
+    prefetch(u + 1 < U1 ? u + 1 : u);
+    __syncthreads();
     // token t of the unit is sequence position c*C + sb*SB + t
     const size_t obase = ((static_cast<size_t>(b) * T + static_cast<size_t>(c) * C + sb * SB) * H + h) * DV;
     // this chunk's deltas [C][DV] in its summary (when they are kept)
@@ -504,8 +509,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
     const int sb = unit_sb(u);
     __syncthreads();
     commit();
-    prefetch(u + 1 < U ? u + 1 : u);
-    __syncthreads();
+    // The chunk-end gradient is stored after the commit, before the next
+    // unit's loads are issued.  (Measured at B = 8, T = 4096, H = 16, d = 128,
+    // bf16: 206 us here, 238 us ahead of the commit, where the commit's waits
+    // then also wait for these stores, 210 us after the prefetch.)
     if (sb == NSB - 1) {
       // gradient at the end of chunk c, in the compute type, as transposed
       // 16-row tiles (the lane's four rows of column colg are contiguous)
@@ -517,6 +524,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
         Z[s] = zero4();
       }
     }
+    prefetch(u + 1 < U ? u + 1 : u);
+    __syncthreads();
     // (the unit's token tiles fully unrolled: their X products are independent,
     // so their MFMA chains interleave)
 #pragma unroll
