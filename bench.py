@@ -254,7 +254,9 @@ def decode_bench(m, torch, hiprt, N=64, H=16, d=128, steps=4096, seed=0):
             "graph_matches_eager": graph_ok,
             "hbm_GBs_at_kernel_time": (state_bytes + in_bytes) / (kt * 1e-3) / 1e9,
             "bytes_per_step": state_bytes + in_bytes,
-            "note": "state (%d MiB) may be served partly from the 256 MB Infinity Cache" % (N * H * d * d * 4 >> 20)}
+            "graph_hbm_GBs": (state_bytes + in_bytes) / (gwall * 1e-3) / 1e9,
+            "note": ("state (%d MiB) may be served partly from the 256 MB Infinity Cache" if N * H * d * d * 4 < (256 << 20)
+                     else "state (%d MiB) larger than the 256 MB Infinity Cache") % (N * H * d * d * 4 >> 20)}
 
 
 def stream_bench(m, torch, hiprt, T=1 << 20, H=16, d=128, seg=32768, chunk=64, steps=1024, seed=0):
@@ -475,6 +477,11 @@ def main():
         log(f"[bench] secondary decode ({args.decode_steps} steps)")
         sec["decode_64x16"] = decode_bench(m, torch, hiprt, steps=args.decode_steps)
         log(f"[bench]   {sec['decode_64x16']['kernel_us_per_step']:.2f} us/step kernel")
+        # the same step on a 512 MiB state, which the 256 MB Infinity Cache cannot hold
+        log("[bench] secondary decode, 512 streams (512 MiB state), 256 steps")
+        sec["decode_512x16"] = decode_bench(m, torch, hiprt, N=512, steps=256)
+        log(f"[bench]   {sec['decode_512x16']['kernel_us_per_step']:.2f} us/step kernel, "
+            f"{sec['decode_512x16']['graph_wall_us_per_step']:.2f} us/step graph")
         result["secondary"] = sec
     print(json.dumps(result), flush=True)
 
