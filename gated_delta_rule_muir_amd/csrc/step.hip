@@ -21,7 +21,10 @@ namespace muir {
 constexpr int STEP_THREADS = 256;
 constexpr int STEP_COLS = 64;  // state columns per workgroup
 
-template <typename Tin, int DK>
+// NT: the state is streamed with non-temporal loads and stores (chosen for
+// states larger than the 256 MB Infinity Cache; smaller ones stay cacheable
+// across steps).
+template <typename Tin, int DK, bool NT>
 __global__ __launch_bounds__(STEP_THREADS) void step_kernel(
     int H, int DV, const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ log_a, const Tin* __restrict__ erase, const Tin* __restrict__ write,
@@ -61,7 +64,11 @@ __global__ __launch_bounds__(STEP_THREADS) void step_kernel(
   float* Sh = S + static_cast<size_t>(head) * DK * DV;
   f32x4 st[RP];
 #pragma unroll
-  for (int p = 0; p < RP; ++p) st[p] = load4(Sh + static_cast<size_t>(rg + 16 * p) * DV + col0);
+  for (int p = 0; p < RP; ++p) {
+    const float* src = Sh + static_cast<size_t>(rg + 16 * p) * DV + col0;
+    if constexpr (NT) st[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src));
+    else st[p] = load4(src);
+  }
   const size_t vv = static_cast<size_t>(head) * DV + col0;
   const typename Raw4<Tin>::type wraw = *reinterpret_cast<const typename Raw4<Tin>::type*>(write + vv);
   const typename Raw4<Tin>::type vraw = *reinterpret_cast<const typename Raw4<Tin>::type*>(v + vv);
@@ -131,7 +138,9 @@ __global__ __launch_bounds__(STEP_THREADS) void step_kernel(
 #pragma unroll
   for (int p = 0; p < RP; ++p) {
     const int row = rg + 16 * p;
-    store4(Sh + static_cast<size_t>(row) * DV + col0, st[p] + s_k[row] * d);
+    float* dst = Sh + static_cast<size_t>(row) * DV + col0;
+    if constexpr (NT) __builtin_nontemporal_store(st[p] + s_k[row] * d, reinterpret_cast<f32x4*>(dst));
+    else store4(dst, st[p] + s_k[row] * d);
   }
 }
 
@@ -140,10 +149,17 @@ hipError_t launch_step(int N, int H, int dk, int dv, bool bf16, int gmode, const
                        const void* write, const void* gamma, float* S, void* o, hipStream_t stream) {
   const int grid = N * H * (dv / STEP_COLS);
   if (grid == 0) return hipSuccess;
-#define MUIR_STEP_LAUNCH(TT, DD)                                                                     \
-  hipLaunchKernelGGL((step_kernel<TT, DD>), dim3(grid), dim3(STEP_THREADS), 0, stream, H, dv,        \
+  // states beyond the Infinity Cache (256 MB) are streamed non-temporally
+  const bool nt = static_cast<size_t>(N) * H * dk * dv * sizeof(float) >= (static_cast<size_t>(256) << 20);
+#define MUIR_STEP_LAUNCH1(TT, DD, NTV)                                                                  \
+  hipLaunchKernelGGL((step_kernel<TT, DD, NTV>), dim3(grid), dim3(STEP_THREADS), 0, stream, H, dv,     \
                      (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, (const TT*)erase,      \
                      (const TT*)write, (const TT*)gamma, S, (TT*)o, gmode)
+#define MUIR_STEP_LAUNCH(TT, DD)                    \
+  do {                                              \
+    if (nt) MUIR_STEP_LAUNCH1(TT, DD, true);        \
+    else MUIR_STEP_LAUNCH1(TT, DD, false);          \
+  } while (0)
   if (bf16) {
     if (dk == 128) MUIR_STEP_LAUNCH(uint16_t, 128);
     else MUIR_STEP_LAUNCH(uint16_t, 64);
@@ -152,6 +168,7 @@ hipError_t launch_step(int N, int H, int dk, int dv, bool bf16, int gmode, const
     else MUIR_STEP_LAUNCH(float, 64);
   }
 #undef MUIR_STEP_LAUNCH
+#undef MUIR_STEP_LAUNCH1
   return hipGetLastError();
 }
 

@@ -3,7 +3,8 @@ times, on outputs the oracle can compute one (batch, head) at a time.
 
   layer 4K  : B=8, T=4096, H=16, d=128, chunk 64, bf16   (forward and backward)
   long 32K  : B=1, T=32768, H=16, d=128, chunk 128 / 256  (forward and backward)
-  decode    : 64 streams x 16 heads x d=128, 4096 steps  (every step's output)
+  decode    : 64 streams x 16 heads x d=128, 4096 steps  (every step's output);
+              512 streams x 16 heads, 16 steps (a state beyond the Infinity Cache)
 
 Tolerance: max |gpu - oracle| / max |oracle| per tensor on the sampled slice <= 2e-2.
 """
@@ -106,6 +107,32 @@ def test_decode_4096_steps_sampled_streams():
     e_s = rel_err(S[picks].cpu(), S_ref)
     _say(f"  decode o={e_o:.2e} S={e_s:.2e}")
     assert e_o <= TOL and e_s <= TOL
+
+
+def test_decode_state_beyond_infinity_cache():
+    """512 streams x 16 heads (a 512 MiB state, which the step streams with
+    non-temporal loads and stores), 16 steps; streams 0 and 511 replayed by
+    the oracle at every step and on the final state."""
+    m = _lib()
+    N, H, d, steps = 512, 16, 128, 16
+    _say("decode 512 MiB state: generating inputs on the device")
+    inp = muir_inputs.step_inputs_torch(N, H, d, d, steps, device="cuda", seed=6)
+    S = torch.zeros((N, H, d, d), dtype=torch.float32, device="cuda")
+    picks = [0, N - 1]
+    outs = torch.empty((steps, len(picks), H, d), dtype=torch.bfloat16, device="cuda")
+    for t in range(steps):
+        o = m.muir_step(inp["q"][t], inp["k"][t], inp["v"][t], inp["log_a"], inp["erase"][t],
+                        inp["write"][t], inp["gamma"][t], S)
+        outs[t] = o[picks]
+    torch.cuda.synchronize()
+    seq = {n: inp[n][:, picks].transpose(0, 1).cpu() for n in ("q", "k", "v", "erase", "write", "gamma")}
+    seq["log_a"] = inp["log_a"][picks].unsqueeze(1).expand(len(picks), steps, H, d).cpu()
+    o_ref, S_ref = oracle.fwd(*(seq[n] for n in NAMES))
+    e_o = rel_err(outs.transpose(0, 1).cpu(), o_ref)
+    e_s = rel_err(S[picks].cpu(), S_ref)
+    _say(f"  decode 512 MiB o={e_o:.2e} S={e_s:.2e}")
+    assert e_o <= TOL and e_s <= TOL
+    del S
 
 
 def test_gate_prologue_full_layer():
