@@ -40,8 +40,6 @@ namespace muir {
 
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 // Per-chunk scratch, in the compute type: deltas [C][DV], then the state at
 // the start of every 16-token block [C/16][DK][DV] (row-major, as staged).
 template <typename TC>

@@ -68,6 +68,7 @@ template <typename T> __device__ __forceinline__ float ldv(const T* base, uint32
 }
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Four consecutive elements of a compute type as one raw word (8 or 16 bytes).
 template <typename TC> struct Raw4;

@@ -30,6 +30,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 constexpr int GEMM_THREADS = 256;
 constexpr int UP_THREADS = 256;
 constexpr int UP_BN = 64;  // columns per tile of the up-projection kernel
+constexpr int UP_CT = 8;   // consecutive column tiles per workgroup of the up-projection kernel
 
 enum Epi {
   EPI_STORE = 0,     // general GEMM: C = acc in the compute type
@@ -324,18 +325,47 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmBatch batch) {
 template <int ACT> __device__ __forceinline__ float act_fwd_t(float x) { return act_fwd(ACT, x); }
 template <int ACT> __device__ __forceinline__ float act_grad_t(float x) { return act_grad(ACT, x); }
 
+// One column tile's operands of the up-projection kernel, to registers: the
+// U block (BN rows of the gate's rank, as 16-byte words; words past the
+// block repeat its last) and, for the backward (DG), this thread's staged
+// words of the upstream gradient (rows dgrow0 + s * RSTEP, clamped to the
+// last row; rows past it are not used).
+template <typename TC, bool DG, int MAXW, int SW, int RSTEP>
+__device__ __forceinline__ void up_load_tile(u32x4 (&rb)[MAXW], u32x4 (&dgw)[SW], const TC* __restrict__ U,
+                                             const TC* __restrict__ dG, int n0, int r, int W, int nwords, int tid,
+                                             int dgrow0, int M, int scol) {
+  constexpr int E = 16 / sizeof(TC);
+  const int wpr = r / E;
+#pragma unroll
+  for (int w = 0; w < MAXW; ++w) {
+    const int idx = min(tid + w * UP_THREADS, nwords - 1);
+    rb[w] = *reinterpret_cast<const u32x4*>(U + static_cast<size_t>(n0 + idx / wpr) * r + (idx % wpr) * E);
+  }
+  if constexpr (DG) {
+#pragma unroll
+    for (int sw = 0; sw < SW; ++sw) {
+      const int gm = min(dgrow0 + sw * RSTEP, M - 1);
+      dgw[sw] = *reinterpret_cast<const u32x4*>(dG + static_cast<size_t>(gm) * W + n0 + scol);
+    }
+  }
+}
+
 // The gates' up-projections (contraction over one gate's rank, 64 or 128):
 // C = z_i U_i^T + c_i with an activation epilogue (EPI_GATE) or its gradient
-// (EPI_GATE_BWD).  One 128 x 64 output tile per workgroup of 4 waves; wave w
-// owns rows 32 w .. +31 and all 64 columns.  Every load is issued up front --
-// the wave's rows of z straight into MFMA fragments, the tile of U_i (64 rows
-// of [width, rank], rank contiguous) into LDS, and the backward's upstream
-// gradients -- and the stores come last, so no wait on a load ever sits
-// behind this workgroup's own stores (loads and stores share one counter).
-// The gradient tile is read, and the output tile written, through an LDS
-// staging tile in whole 128-byte rows (8 lanes per row), not in the MFMA
-// layout's 32-byte pieces.  blockIdx.y: the gate; blockIdx.x: the tile (row
-// tiles fastest within a column tile, so the tile of U_i is reused from L2).
+// (EPI_GATE_BWD).  A workgroup of 4 waves owns a 128-row block of one gate
+// and UP_CT consecutive 64-column tiles; wave w owns rows 32 w .. +31.  The
+// wave's rows of z are loaded once, straight into MFMA fragments, and stay in
+// registers across the tiles (one tile per workgroup read each row block of z
+// once per tile).  Each tile's U_i block (64 rows of [width, rank], rank
+// contiguous) and, in the backward, its upstream gradients are loaded during
+// the previous tile's products and written to LDS at the tile's start.  The
+// next tile's loads are issued before this tile's stores and without a branch
+// (addresses clamped), so no wait on them sits behind this workgroup's own
+// stores (loads and stores share one counter).  The gradient tile is read,
+// and the output tile written, through an LDS staging tile in whole 128-byte
+// rows (8 lanes per row), not in the MFMA layout's 32-byte pieces.
+// blockIdx.x: the row block (fastest), then the group of column tiles;
+// blockIdx.y: the gate.
 template <typename TC, int EPI>
 __global__ __launch_bounds__(UP_THREADS) void gate_up_kernel(GateUpArgs<TC> a) {
   typedef GF<TC> F;
@@ -356,10 +386,13 @@ __global__ __launch_bounds__(UP_THREADS) void gate_up_kernel(GateUpArgs<TC> a) {
   const int r = a.r[gi];
   const int W = a.W[gi];
   const int mt = (a.M + BM - 1) / BM;
-  const int ntile = mt * (W / BN);
-  if (static_cast<int>(blockIdx.x) >= ntile) return;
+  const int ntiles = W / BN;
+  const int ngrp = (ntiles + UP_CT - 1) / UP_CT;
+  if (static_cast<int>(blockIdx.x) >= mt * ngrp) return;
   const int mtile = blockIdx.x % mt;
-  const int m0 = mtile * BM, n0 = (blockIdx.x / mt) * BN;
+  const int t0 = (blockIdx.x / mt) * UP_CT;
+  const int t1 = min(ntiles, t0 + UP_CT);
+  const int m0 = mtile * BM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = 32 * wave;
   const int fr = lane & 15, fk = (F::KF / 4) * (lane >> 4), g4 = 4 * (lane >> 4);
@@ -372,18 +405,10 @@ __global__ __launch_bounds__(UP_THREADS) void gate_up_kernel(GateUpArgs<TC> a) {
   // wm + s * (64 / WPR) + lane / WPR, columns (lane % WPR) * E ..
   auto srow = [&](int sw) { return wm + sw * (64 / WPR) + lane / WPR; };
   const int scol = (lane % WPR) * E;
-
-  // loads: U tile (to registers, then LDS), this wave's rows of z, dG
   const int wpr = r / E;
   const int nwords = BN * wpr;
-  uint4 rb[MAXW];
-#pragma unroll
-  for (int w = 0; w < MAXW; ++w) {
-    const int idx = tid + w * UP_THREADS;
-    uint4 v = {0u, 0u, 0u, 0u};
-    if (idx < nwords) v = *reinterpret_cast<const uint4*>(U + static_cast<size_t>(n0 + idx / wpr) * r + (idx % wpr) * E);
-    rb[w] = v;
-  }
+
+  // the wave's rows of z, once
   typename F::frag fa[TM][KSTEPS];
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -396,102 +421,108 @@ __global__ __launch_bounds__(UP_THREADS) void gate_up_kernel(GateUpArgs<TC> a) {
       fa[i][ks] = __builtin_bit_cast(typename F::frag, v);
     }
   }
-  uint4 dgw[SW];
-  if constexpr (EPI == EPI_GATE_BWD) {
-    const TC* dG = a.dG[gi] + n0 + scol;
-#pragma unroll
-    for (int sw = 0; sw < SW; ++sw) {
-      const int gm = min(m0 + srow(sw), a.M - 1);  // rows past M are read but not used
-      dgw[sw] = *reinterpret_cast<const uint4*>(dG + static_cast<size_t>(gm) * W);
-    }
-  }
-#pragma unroll
-  for (int w = 0; w < MAXW; ++w) {
-    const int idx = tid + w * UP_THREADS;
-    if (idx < nwords) *reinterpret_cast<uint4*>(&sB[(idx / wpr) * LDK + (idx % wpr) * E]) = rb[w];
-  }
-  if constexpr (EPI == EPI_GATE_BWD) {
-#pragma unroll
-    for (int sw = 0; sw < SW; ++sw) *reinterpret_cast<uint4*>(&sS[srow(sw) * LDS_ + scol]) = dgw[sw];
-  }
-  __syncthreads();
+  // a tile's U block and upstream gradients, to registers
+  u32x4 rb[MAXW];
+  u32x4 dgw[SW];
+  const int dgrow0 = m0 + wm + lane / WPR;
+  up_load_tile<TC, EPI == EPI_GATE_BWD, MAXW, SW, 64 / WPR>(rb, dgw, U, a.dG[gi], t0 * BN, r, W, nwords, tid,
+                                                            dgrow0, a.M, scol);
 
-  f32x4 acc[TM][TN];
+#pragma unroll 1
+  for (int t = t0; t < t1; ++t) {
+    const int n0 = t * BN;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int w = 0; w < MAXW; ++w) {
+      const int idx = min(tid + w * UP_THREADS, nwords - 1);
+      *reinterpret_cast<u32x4*>(&sB[(idx / wpr) * LDK + (idx % wpr) * E]) = rb[w];
+    }
+    if constexpr (EPI == EPI_GATE_BWD) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = zero4();
+      for (int sw = 0; sw < SW; ++sw) *reinterpret_cast<u32x4*>(&sS[srow(sw) * LDS_ + scol]) = dgw[sw];
+    }
+    __syncthreads();
+    // the next tile's, in flight during this one
+    up_load_tile<TC, EPI == EPI_GATE_BWD, MAXW, SW, 64 / WPR>(rb, dgw, U, a.dG[gi], (t + 1 < t1 ? t + 1 : t) * BN, r,
+                                                              W, nwords, tid, dgrow0, a.M, scol);
+
+    f32x4 acc[TM][TN];
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-    if (ks < ksteps) {
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      if (ks < ksteps) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const typename F::frag fb = F::load(&sB[(16 * j + fr) * LDK + ks * F::KF + fk]);
+#pragma unroll
+          for (int i = 0; i < TM; ++i) acc[i][j] = F::mma(fb, fa[i][ks], acc[i][j]);
+        }
+      }
+    }
+
+    // epilogue in the MFMA layout (lane: row wm + 16i + fr, columns 16j + 4g ..
+    // + 3 of the tile), through this wave's rows of the staging tile
+    auto epilogue = [&](auto act_tag) {
+      constexpr int ACT = decltype(act_tag)::value;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const typename F::frag fb = F::load(&sB[(16 * j + fr) * LDK + ks * F::KF + fk]);
+        const int c = 16 * j + g4;
+        const f32x4 bv = load4(bias + n0 + c);
+        float cs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < TM; ++i) acc[i][j] = F::mma(fb, fa[i][ks], acc[i][j]);
-      }
-    }
-  }
-
-  // epilogue in the MFMA layout (lane: row wm + 16i + fr, columns 16j + 4g ..
-  // + 3 of the tile), through this wave's rows of the staging tile
-  auto epilogue = [&](auto act_tag) {
-    constexpr int ACT = decltype(act_tag)::value;
+        for (int i = 0; i < TM; ++i) {
+          const int row = wm + 16 * i + fr;
+          f32x4 v = acc[i][j];
+          if constexpr (EPI == EPI_GATE) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int c = 16 * j + g4;
-      const f32x4 bv = load4(bias + n0 + c);
-      float cs[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q < 4; ++q) v[q] = act_fwd_t<ACT>(v[q] + bv[q]);
+          } else {
+            const f32x4 gv = load4(&sS[row * LDS_ + c]);
+            const bool row_ok = m0 + row < a.M;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm + 16 * i + fr;
-        f32x4 v = acc[i][j];
-        if constexpr (EPI == EPI_GATE) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = act_fwd_t<ACT>(v[q] + bv[q]);
-        } else {
-          const f32x4 gv = load4(&sS[row * LDS_ + c]);
-          const bool row_ok = m0 + row < a.M;
+            for (int q = 0; q < 4; ++q) {
+              v[q] = gv[q] * act_grad_t<ACT>(v[q] + bv[q]);
+              cs[q] += row_ok ? v[q] : 0.f;
+            }
+          }
+          store4(&sS[row * LDS_ + c], v);
+        }
+        if constexpr (EPI == EPI_GATE_BWD) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            v[q] = gv[q] * act_grad_t<ACT>(v[q] + bv[q]);
-            cs[q] += row_ok ? v[q] : 0.f;
+            const float sm = sum16(cs[q]);
+            if (fr == 0) red[wave * BN + c + q] = sm;
           }
         }
-        store4(&sS[row * LDS_ + c], v);
       }
-      if constexpr (EPI == EPI_GATE_BWD) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float sm = sum16(cs[q]);
-          if (fr == 0) red[wave * BN + c + q] = sm;
-        }
-      }
+    };
+    switch (a.act[gi]) {
+      case GATE_ACT_LOGSIG: epilogue(std::integral_constant<int, GATE_ACT_LOGSIG>{}); break;
+      case GATE_ACT_SIG: epilogue(std::integral_constant<int, GATE_ACT_SIG>{}); break;
+      case GATE_ACT_SIG2: epilogue(std::integral_constant<int, GATE_ACT_SIG2>{}); break;
+      default: epilogue(std::integral_constant<int, GATE_ACT_NONE>{}); break;
     }
-  };
-  switch (a.act[gi]) {
-    case GATE_ACT_LOGSIG: epilogue(std::integral_constant<int, GATE_ACT_LOGSIG>{}); break;
-    case GATE_ACT_SIG: epilogue(std::integral_constant<int, GATE_ACT_SIG>{}); break;
-    case GATE_ACT_SIG2: epilogue(std::integral_constant<int, GATE_ACT_SIG2>{}); break;
-    default: epilogue(std::integral_constant<int, GATE_ACT_NONE>{}); break;
-  }
-  // this wave's rows back out in whole rows (the wave wrote them itself: LDS
-  // operations of one wave complete in order)
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  TC* o = out + n0 + scol;
+    // this wave's rows back out in whole rows (the wave wrote them itself: LDS
+    // operations of one wave complete in order)
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    TC* o = out + n0 + scol;
 #pragma unroll
-  for (int sw = 0; sw < SW; ++sw) {
-    const int row = srow(sw);
-    if (m0 + row < a.M)
-      *reinterpret_cast<uint4*>(o + static_cast<size_t>(m0 + row) * W) =
-          *reinterpret_cast<const uint4*>(&sS[row * LDS_ + scol]);
-  }
-  if constexpr (EPI == EPI_GATE_BWD) {
-    // column sums of the tile's dpre: the four waves' partial sums
-    __syncthreads();
-    if (tid < BN)
-      a.colsum[static_cast<size_t>(mtile) * a.colsum_ld + a.csoff[gi] + n0 + tid] =
-          red[tid] + red[BN + tid] + red[2 * BN + tid] + red[3 * BN + tid];
+    for (int sw = 0; sw < SW; ++sw) {
+      const int row = srow(sw);
+      if (m0 + row < a.M)
+        *reinterpret_cast<uint4*>(o + static_cast<size_t>(m0 + row) * W) =
+            *reinterpret_cast<const uint4*>(&sS[row * LDS_ + scol]);
+    }
+    if constexpr (EPI == EPI_GATE_BWD) {
+      // column sums of the tile's dpre: the four waves' partial sums
+      __syncthreads();
+      if (tid < BN)
+        a.colsum[static_cast<size_t>(mtile) * a.colsum_ld + a.csoff[gi] + n0 + tid] =
+            red[tid] + red[BN + tid] + red[2 * BN + tid] + red[3 * BN + tid];
+    }
+    __syncthreads();  // the tile's LDS (U block, staging, partial sums) is free again
   }
 }
 
@@ -653,7 +684,7 @@ GateUpArgs<TC> gate_up_args(const GateLayout& L, const TC* z, const TC* U, const
 template <typename TC, int EPI>
 hipError_t run_gate_up(const GateUpArgs<TC>& u, hipStream_t stream) {
   int gx = 0;
-  for (int i = 0; i < 5; ++i) gx = std::max(gx, ((u.M + 127) / 128) * (u.W[i] / UP_BN));
+  for (int i = 0; i < 5; ++i) gx = std::max(gx, ((u.M + 127) / 128) * ((u.W[i] / UP_BN + UP_CT - 1) / UP_CT));
   if (gx == 0) return hipSuccess;
   hipLaunchKernelGGL((gate_up_kernel<TC, EPI>), dim3(gx, 5), dim3(UP_THREADS), 0, stream, u);
   return hipGetLastError();

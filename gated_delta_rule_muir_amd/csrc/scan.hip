@@ -25,8 +25,6 @@ namespace muir {
 
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 // LDS tile addressing.  A tile has rows of L bytes; its G-byte granules (G =
 // 8 for bf16 fragments, read 8 bytes per lane, or 16 for fp32 ones) are
 // XOR-permuted per row.  LDS serves a fragment read 128 bytes at a time (32
