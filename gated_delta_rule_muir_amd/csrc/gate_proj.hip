@@ -378,9 +378,9 @@ __global__ __launch_bounds__(UP_THREADS) void gate_up_kernel(GateUpArgs<TC> a) {
   constexpr int LDS_ = BN + E;                         // staging pitch (elements): one 16-byte pad per row
   constexpr int WPR = BN / E;                          // 16-byte words per staged row
   constexpr int SW = BM * WPR / UP_THREADS;            // staged words per thread
-  __shared__ __align__(16) TC sB[BN * LDK];
+  __shared__ __align__(16) TC sB[2][BN * LDK];  // U blocks of the current and the next tile
   __shared__ __align__(16) TC sS[BM * LDS_];
-  __shared__ float red[4 * BN];
+  __shared__ float red[2][4 * BN];
 
   const int gi = blockIdx.y;
   const int r = a.r[gi];
@@ -425,37 +425,56 @@ __global__ __launch_bounds__(UP_THREADS) void gate_up_kernel(GateUpArgs<TC> a) {
   u32x4 rb[MAXW];
   u32x4 dgw[SW];
   const int dgrow0 = m0 + wm + lane / WPR;
-  up_load_tile<TC, EPI == EPI_GATE_BWD, MAXW, SW, 64 / WPR>(rb, dgw, U, a.dG[gi], t0 * BN, r, W, nwords, tid,
-                                                            dgrow0, a.M, scol);
-
-#pragma unroll 1
-  for (int t = t0; t < t1; ++t) {
-    const int n0 = t * BN;
+  constexpr bool BWD = EPI == EPI_GATE_BWD;
+  auto put_tile = [&](TC* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int w = 0; w < MAXW; ++w) {
       const int idx = min(tid + w * UP_THREADS, nwords - 1);
-      *reinterpret_cast<u32x4*>(&sB[(idx / wpr) * LDK + (idx % wpr) * E]) = rb[w];
+      *reinterpret_cast<u32x4*>(&dst[(idx / wpr) * LDK + (idx % wpr) * E]) = rb[w];
     }
-    if constexpr (EPI == EPI_GATE_BWD) {
+    if constexpr (BWD) {
 #pragma unroll
       for (int sw = 0; sw < SW; ++sw) *reinterpret_cast<u32x4*>(&sS[srow(sw) * LDS_ + scol]) = dgw[sw];
     }
-    __syncthreads();
-    // the next tile's, in flight during this one
-    up_load_tile<TC, EPI == EPI_GATE_BWD, MAXW, SW, 64 / WPR>(rb, dgw, U, a.dG[gi], (t + 1 < t1 ? t + 1 : t) * BN, r,
-                                                              W, nwords, tid, dgrow0, a.M, scol);
+  };
+  // the four waves' column sums of a tile's dpre, from its partial-sum buffer
+  auto put_colsum = [&](int t, const float* rd) __attribute__((always_inline)) {
+    if (tid < BN)
+      a.colsum[static_cast<size_t>(mtile) * a.colsum_ld + a.csoff[gi] + t * BN + tid] =
+          rd[tid] + rd[BN + tid] + rd[2 * BN + tid] + rd[3 * BN + tid];
+  };
+  up_load_tile<TC, BWD, MAXW, SW, 64 / WPR>(rb, dgw, U, a.dG[gi], t0 * BN, r, W, nwords, tid, dgrow0, a.M, scol);
+  put_tile(sB[0]);
 
+#pragma unroll 1
+  for (int t = t0; t < t1; ++t) {
+    const int buf = (t - t0) & 1;
+    const int n0 = t * BN;
+    // tile t's U block is in sB[buf] (and its dG words in sS); every wave is
+    // done with tile t - 1, so sB[buf ^ 1] and red[buf ^ 1] are free once read
+    __syncthreads();
+    if constexpr (BWD) {
+      if (t > t0) put_colsum(t - 1, red[buf ^ 1]);
+    }
+    // the next tile's operands, in flight during this one
+    up_load_tile<TC, BWD, MAXW, SW, 64 / WPR>(rb, dgw, U, a.dG[gi], (t + 1 < t1 ? t + 1 : t) * BN, r, W, nwords,
+                                              tid, dgrow0, a.M, scol);
+
+    // accumulators start from the bias (lane: columns 16j + 4g .. + 3)
     f32x4 acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < TN; ++j) {
+      const f32x4 bv = load4(bias + n0 + 16 * j + g4);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = zero4();
+      for (int i = 0; i < TM; ++i) acc[i][j] = bv;
+    }
+    const TC* sb = sB[buf];
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       if (ks < ksteps) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const typename F::frag fb = F::load(&sB[(16 * j + fr) * LDK + ks * F::KF + fk]);
+          const typename F::frag fb = F::load(&sb[(16 * j + fr) * LDK + ks * F::KF + fk]);
 #pragma unroll
           for (int i = 0; i < TM; ++i) acc[i][j] = F::mma(fb, fa[i][ks], acc[i][j]);
         }
@@ -464,36 +483,36 @@ __global__ __launch_bounds__(UP_THREADS) void gate_up_kernel(GateUpArgs<TC> a) {
 
     // epilogue in the MFMA layout (lane: row wm + 16i + fr, columns 16j + 4g ..
     // + 3 of the tile), through this wave's rows of the staging tile
+    float* rd = red[buf];
     auto epilogue = [&](auto act_tag) {
       constexpr int ACT = decltype(act_tag)::value;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int c = 16 * j + g4;
-        const f32x4 bv = load4(bias + n0 + c);
         float cs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           const int row = wm + 16 * i + fr;
           f32x4 v = acc[i][j];
-          if constexpr (EPI == EPI_GATE) {
+          if constexpr (!BWD) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = act_fwd_t<ACT>(v[q] + bv[q]);
+            for (int q = 0; q < 4; ++q) v[q] = act_fwd_t<ACT>(v[q]);
           } else {
             const f32x4 gv = load4(&sS[row * LDS_ + c]);
             const bool row_ok = m0 + row < a.M;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              v[q] = gv[q] * act_grad_t<ACT>(v[q] + bv[q]);
+              v[q] = gv[q] * act_grad_t<ACT>(v[q]);
               cs[q] += row_ok ? v[q] : 0.f;
             }
           }
           store4(&sS[row * LDS_ + c], v);
         }
-        if constexpr (EPI == EPI_GATE_BWD) {
+        if constexpr (BWD) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float sm = sum16(cs[q]);
-            if (fr == 0) red[wave * BN + c + q] = sm;
+            if (fr == 0) rd[wave * BN + c + q] = sm;
           }
         }
       }
@@ -515,14 +534,14 @@ __global__ __launch_bounds__(UP_THREADS) void gate_up_kernel(GateUpArgs<TC> a) {
         *reinterpret_cast<uint4*>(o + static_cast<size_t>(m0 + row) * W) =
             *reinterpret_cast<const uint4*>(&sS[row * LDS_ + scol]);
     }
-    if constexpr (EPI == EPI_GATE_BWD) {
-      // column sums of the tile's dpre: the four waves' partial sums
-      __syncthreads();
-      if (tid < BN)
-        a.colsum[static_cast<size_t>(mtile) * a.colsum_ld + a.csoff[gi] + n0 + tid] =
-            red[tid] + red[BN + tid] + red[2 * BN + tid] + red[3 * BN + tid];
-    }
-    __syncthreads();  // the tile's LDS (U block, staging, partial sums) is free again
+    // the next tile's operands to LDS: sB[buf ^ 1] was last read in tile t - 1,
+    // which every wave finished before this tile's barrier; the dG words go to
+    // this wave's own staging rows after its reads of them above
+    if (t + 1 < t1) put_tile(sB[buf ^ 1]);
+  }
+  if constexpr (BWD) {
+    __syncthreads();
+    put_colsum(t1 - 1, red[(t1 - 1 - t0) & 1]);
   }
 }
 
