@@ -31,6 +31,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -76,26 +77,41 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "gated_delta_rule_muir_amd", "csrc")
 
 
-def library_sources_sha256() -> str:
-    """SHA-256 over the HIP library's sources (file names and contents, sorted)."""
+# the source file that defines each measured kernel
+KERNEL_SOURCE = {"fwd_prep": "fwd.hip", "fwd_scan": "scan.hip", "bwd_scan": "scan.hip",
+                 "bwd_chunk": "bwd_chunk.hip", "step": "step.hip"}
+
+
+def kernel_sources_sha256(kernel: str) -> str:
+    """SHA-256 over the source of `kernel` and the library headers it includes,
+    transitively (file names and contents, sorted by name)."""
+    seen, todo = set(), [KERNEL_SOURCE[kernel]]
+    while todo:
+        fn = todo.pop()
+        if fn in seen:
+            continue
+        seen.add(fn)
+        with open(os.path.join(CSRC, fn)) as f:
+            for inc in re.findall(r'^\s*#include\s+"([^"]+)"', f.read(), flags=re.M):
+                if os.path.exists(os.path.join(CSRC, inc)):
+                    todo.append(inc)
     h = hashlib.sha256()
-    for fn in sorted(os.listdir(CSRC)):
-        if fn.endswith((".hip", ".h")):
-            h.update(fn.encode())
-            with open(os.path.join(CSRC, fn), "rb") as f:
-                h.update(f.read())
+    for fn in sorted(seen):
+        h.update(fn.encode())
+        with open(os.path.join(CSRC, fn), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
 def measured_traffic(kernel: str, workload: str):
     """Counter-measured HBM bytes per launch of `kernel`, or None if there is
-    no record or the library changed since it was taken."""
+    no record or the kernel's sources changed since it was taken."""
     path = os.path.join(HERE, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("sources_sha256") != library_sources_sha256():
+    if rec.get("sources_sha256") != kernel_sources_sha256(kernel):
         return None
     return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
 
