@@ -400,6 +400,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--secondary", default="",
+                    help="comma-separated secondary lines to run (default: all), e.g. gate_prologue_4k")
     ap.add_argument("--decode-steps", type=int, default=4096)
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a 1 GiB elementwise copy (counter calibration)")
@@ -468,7 +470,11 @@ def main():
         sec = {}
         del dv
         torch.cuda.empty_cache()
+        chosen = set(filter(None, args.secondary.split(",")))
+        want = lambda name: not chosen or name in chosen  # noqa: E731
         for name in ("long_32k_c128", "long_32k_c256"):
+            if not want(name):
+                continue
             w = muir_inputs.WORKLOADS[name]
             log(f"[bench] secondary {name}")
             dv2, _ = gen_seq(w.B, w.T, w.H, w.dk, w.dtype, w.decay, 0, torch, muir_inputs)
@@ -481,23 +487,27 @@ def main():
             log(f"[bench]   {sec[name]['tokens_per_s']:.4g} tokens/s")
             del dv2
             torch.cuda.empty_cache()
-        log("[bench] secondary stream (1M-token prefill, then decode)")
-        sec["stream_1m"] = stream_bench(m, torch, hiprt)
-        log(f"[bench]   prefill {sec['stream_1m']['prefill_tokens_per_s']:.4g} tokens/s, "
-            f"decode {sec['stream_1m']['decode_us_per_token']:.1f} us/token")
-        log("[bench] secondary gate prologue (fused gate projection + q/k SiLU-L2, fwd+bwd)")
-        sec["gate_prologue_4k"] = gate_bench(m, torch, hiprt)
-        gpb = sec["gate_prologue_4k"]
-        log(f"[bench]   proj fwd {gpb['avg_us']['proj_fwd']:.1f} us ({gpb['proj_fwd']['tflops']:.0f} TFLOP/s), "
-            f"bwd {gpb['avg_us']['proj_bwd']:.1f} us ({gpb['proj_bwd']['tflops']:.0f} TFLOP/s)")
-        log(f"[bench] secondary decode ({args.decode_steps} steps)")
-        sec["decode_64x16"] = decode_bench(m, torch, hiprt, steps=args.decode_steps)
-        log(f"[bench]   {sec['decode_64x16']['kernel_us_per_step']:.2f} us/step kernel")
-        # the same step on a 512 MiB state, which the 256 MB Infinity Cache cannot hold
-        log("[bench] secondary decode, 512 streams (512 MiB state), 256 steps")
-        sec["decode_512x16"] = decode_bench(m, torch, hiprt, N=512, steps=256)
-        log(f"[bench]   {sec['decode_512x16']['kernel_us_per_step']:.2f} us/step kernel, "
-            f"{sec['decode_512x16']['graph_wall_us_per_step']:.2f} us/step graph")
+        if want("stream_1m"):
+            log("[bench] secondary stream (1M-token prefill, then decode)")
+            sec["stream_1m"] = stream_bench(m, torch, hiprt)
+            log(f"[bench]   prefill {sec['stream_1m']['prefill_tokens_per_s']:.4g} tokens/s, "
+                f"decode {sec['stream_1m']['decode_us_per_token']:.1f} us/token")
+        if want("gate_prologue_4k"):
+            log("[bench] secondary gate prologue (fused gate projection + q/k SiLU-L2, fwd+bwd)")
+            sec["gate_prologue_4k"] = gate_bench(m, torch, hiprt)
+            gpb = sec["gate_prologue_4k"]
+            log(f"[bench]   proj fwd {gpb['avg_us']['proj_fwd']:.1f} us ({gpb['proj_fwd']['tflops']:.0f} TFLOP/s), "
+                f"bwd {gpb['avg_us']['proj_bwd']:.1f} us ({gpb['proj_bwd']['tflops']:.0f} TFLOP/s)")
+        if want("decode_64x16"):
+            log(f"[bench] secondary decode ({args.decode_steps} steps)")
+            sec["decode_64x16"] = decode_bench(m, torch, hiprt, steps=args.decode_steps)
+            log(f"[bench]   {sec['decode_64x16']['kernel_us_per_step']:.2f} us/step kernel")
+        if want("decode_512x16"):
+            # the same step on a 512 MiB state, which the 256 MB Infinity Cache cannot hold
+            log("[bench] secondary decode, 512 streams (512 MiB state), 256 steps")
+            sec["decode_512x16"] = decode_bench(m, torch, hiprt, N=512, steps=256)
+            log(f"[bench]   {sec['decode_512x16']['kernel_us_per_step']:.2f} us/step kernel, "
+                f"{sec['decode_512x16']['graph_wall_us_per_step']:.2f} us/step graph")
         result["secondary"] = sec
     print(json.dumps(result), flush=True)
 
