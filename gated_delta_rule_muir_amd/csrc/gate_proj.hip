@@ -576,64 +576,131 @@ __global__ void split_sum_kernel(const float* __restrict__ part, int nsplit, siz
   }
 }
 
-// SiLU then L2 normalisation over each row of D values (one head of q or k):
-// y = s / sqrt(sum s^2 + eps), s = u sigmoid(u).  D / 4 lanes per row, four
-// values per lane; the row sums are taken with lane shuffles inside the group.
-template <typename TC, int D>
-__global__ __launch_bounds__(256) void qk_norm_fwd_kernel(const TC* __restrict__ u, TC* __restrict__ y,
-                                                          long long rows) {
-  constexpr int G = D / 4;  // lanes per row
-  const long long row = (static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x) / G;
-  const int l = threadIdx.x % G;
-  const bool ok = row < rows;
-  f32x4 s = zero4();
-  if (ok) {
-    const f32x4 x = load4(u + row * D + 4 * l);
+// One 16-byte word of a row as fp32 values, and back (bf16: the hardware
+// round-to-nearest-even conversion, as every other bf16 store here).
+template <typename TC> struct QkWord;
+template <> struct QkWord<uint16_t> {
+  static constexpr int V = 8;
+  static __device__ __forceinline__ void unpack(u32x4 w, float (&x)[V]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = x[i] * sigmoidf_(x[i]);
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+      x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+    }
   }
-  float ss = s[0] * s[0] + s[1] * s[1] + s[2] * s[2] + s[3] * s[3];
+  static __device__ __forceinline__ u32x4 pack(const float (&x)[V]) {
+    u32x4 w;
 #pragma unroll
-  for (int off = G / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
-  const float inv = rsqrtf(ss + QK_L2_EPS);
-  if (ok) store4(y + row * D + 4 * l, s * inv);
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    return w;
+  }
+};
+template <> struct QkWord<float> {
+  static constexpr int V = 4;
+  // (whole-vector casts: a bit cast of one subscripted vector element was
+  // compiled as a cast of element 0)
+  static __device__ __forceinline__ void unpack(u32x4 w, float (&x)[V]) {
+    const f32x4 f = __builtin_bit_cast(f32x4, w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = f[i];
+  }
+  static __device__ __forceinline__ u32x4 pack(const float (&x)[V]) {
+    const f32x4 f = {x[0], x[1], x[2], x[3]};
+    return __builtin_bit_cast(u32x4, f);
+  }
+};
+
+constexpr int QK_THREADS = 256;
+constexpr int QK_RPT = 4;  // rows per thread group, all loaded before the first use
+template <typename TC, int D> struct QkShape {
+  static constexpr int V = QkWord<TC>::V;     // values per lane (one 16-byte word)
+  static constexpr int G = D / V;             // lanes per row
+  static constexpr int RB = QK_THREADS / G;   // rows per pass of the workgroup
+  static constexpr int ROWS = RB * QK_RPT;    // rows per workgroup
+};
+
+// SiLU then L2 normalisation over each row of D values (one head of q or k):
+// y = s / sqrt(sum s^2 + eps), s = u sigmoid(u).  A row is G lanes of one
+// 16-byte word each; the row sums are taken with lane shuffles inside the
+// group.  Each lane group handles QK_RPT rows, RB apart, and issues all their
+// loads first, so that several words per lane are in flight.
+template <typename TC, int D>
+__global__ __launch_bounds__(QK_THREADS) void qk_norm_fwd_kernel(const TC* __restrict__ u, TC* __restrict__ y,
+                                                                 long long rows) {
+  typedef QkShape<TC, D> S;
+  typedef QkWord<TC> W;
+  const int l = threadIdx.x % S::G;
+  const long long r0 = static_cast<long long>(blockIdx.x) * S::ROWS + threadIdx.x / S::G;
+  // rows past the end read the last row (rows >= 1) and are not stored
+  u32x4 w[QK_RPT];
+#pragma unroll
+  for (int k = 0; k < QK_RPT; ++k)
+    w[k] = *reinterpret_cast<const u32x4*>(u + min(r0 + k * S::RB, rows - 1) * D + S::V * l);
+#pragma unroll
+  for (int k = 0; k < QK_RPT; ++k) {
+    const long long row = r0 + k * S::RB;
+    float x[S::V];
+    W::unpack(w[k], x);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < S::V; ++i) {
+      x[i] = x[i] * sigmoidf_(x[i]);
+      ss += x[i] * x[i];
+    }
+#pragma unroll
+    for (int off = S::G / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    const float inv = rsqrtf(ss + QK_L2_EPS);
+#pragma unroll
+    for (int i = 0; i < S::V; ++i) x[i] *= inv;
+    if (row < rows) *reinterpret_cast<u32x4*>(y + row * D + S::V * l) = W::pack(x);
+  }
 }
 
-// Reverse mode: du = (dy - y (y . dy)) / n * silu'(u).
+// Reverse mode: du = (dy - y (y . dy)) / n * silu'(u), rows as in the forward.
 template <typename TC, int D>
-__global__ __launch_bounds__(256) void qk_norm_bwd_kernel(const TC* __restrict__ u, const TC* __restrict__ dy,
-                                                          TC* __restrict__ du, long long rows) {
-  constexpr int G = D / 4;
-  const long long row = (static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x) / G;
-  const int l = threadIdx.x % G;
-  const bool ok = row < rows;
-  f32x4 x = zero4(), g = zero4(), s, sg;
-  if (ok) {
-    x = load4(u + row * D + 4 * l);
-    g = load4(dy + row * D + 4 * l);
+__global__ __launch_bounds__(QK_THREADS) void qk_norm_bwd_kernel(const TC* __restrict__ u, const TC* __restrict__ dy,
+                                                                 TC* __restrict__ du, long long rows) {
+  typedef QkShape<TC, D> S;
+  typedef QkWord<TC> W;
+  const int l = threadIdx.x % S::G;
+  const long long r0 = static_cast<long long>(blockIdx.x) * S::ROWS + threadIdx.x / S::G;
+  // rows past the end read the last row (rows >= 1) and are not stored
+  u32x4 wu[QK_RPT], wg[QK_RPT];
+#pragma unroll
+  for (int k = 0; k < QK_RPT; ++k) {
+    const long long off = min(r0 + k * S::RB, rows - 1) * D + S::V * l;
+    wu[k] = *reinterpret_cast<const u32x4*>(u + off);
+    wg[k] = *reinterpret_cast<const u32x4*>(dy + off);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sg[i] = sigmoidf_(x[i]);
-    s[i] = x[i] * sg[i];
-  }
-  float ss = s[0] * s[0] + s[1] * s[1] + s[2] * s[2] + s[3] * s[3];
-  float sd = s[0] * g[0] + s[1] * g[1] + s[2] * g[2] + s[3] * g[3];
+  for (int k = 0; k < QK_RPT; ++k) {
+    const long long row = r0 + k * S::RB;
+    float x[S::V], g[S::V], s[S::V], sg[S::V];
+    W::unpack(wu[k], x);
+    W::unpack(wg[k], g);
+    float ss = 0.f, sd = 0.f;
 #pragma unroll
-  for (int off = G / 2; off >= 1; off >>= 1) {
-    ss += __shfl_xor(ss, off, 64);
-    sd += __shfl_xor(sd, off, 64);
-  }
-  const float n2 = ss + QK_L2_EPS;
-  const float inv = rsqrtf(n2);
-  const float ydy = sd * inv;  // y . dy
-  f32x4 r;
+    for (int i = 0; i < S::V; ++i) {
+      sg[i] = sigmoidf_(x[i]);
+      s[i] = x[i] * sg[i];
+      ss += s[i] * s[i];
+      sd += s[i] * g[i];
+    }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float ds = (g[i] - s[i] * inv * ydy) * inv;
-    r[i] = ds * (sg[i] * (1.f + x[i] * (1.f - sg[i])));
+    for (int off = S::G / 2; off >= 1; off >>= 1) {
+      ss += __shfl_xor(ss, off, 64);
+      sd += __shfl_xor(sd, off, 64);
+    }
+    const float inv = rsqrtf(ss + QK_L2_EPS);
+    const float ydy = sd * inv;  // y . dy
+    float r[S::V];
+#pragma unroll
+    for (int i = 0; i < S::V; ++i) {
+      const float ds = (g[i] - s[i] * inv * ydy) * inv;
+      r[i] = ds * (sg[i] * (1.f + x[i] * (1.f - sg[i])));
+    }
+    if (row < rows) *reinterpret_cast<u32x4*>(du + row * D + S::V * l) = W::pack(r);
   }
-  if (ok) store4(du + row * D + 4 * l, r);
 }
 
 template <typename TC, int BM, int BN, bool A_KC, bool B_KC, int EPI>
@@ -885,15 +952,16 @@ hipError_t launch_gate_bwd(const GateShape& s, const void* x, const void* W_down
 hipError_t launch_qk_norm(long long rows, int D, bool bf16, const void* u, const void* dy, void* out,
                           hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  const long long threads = rows * (D / 4);
-  const unsigned blocks = static_cast<unsigned>((threads + 255) / 256);
 #define MUIR_QKN(TC, DD)                                                                                        \
-  if (dy)                                                                                                        \
-    hipLaunchKernelGGL((qk_norm_bwd_kernel<TC, DD>), dim3(blocks), dim3(256), 0, stream,                         \
-                       static_cast<const TC*>(u), static_cast<const TC*>(dy), static_cast<TC*>(out), rows);      \
-  else                                                                                                           \
-    hipLaunchKernelGGL((qk_norm_fwd_kernel<TC, DD>), dim3(blocks), dim3(256), 0, stream,                         \
-                       static_cast<const TC*>(u), static_cast<TC*>(out), rows);
+  {                                                                                                              \
+    const unsigned blocks = static_cast<unsigned>((rows + QkShape<TC, DD>::ROWS - 1) / QkShape<TC, DD>::ROWS);   \
+    if (dy)                                                                                                      \
+      hipLaunchKernelGGL((qk_norm_bwd_kernel<TC, DD>), dim3(blocks), dim3(QK_THREADS), 0, stream,                \
+                         static_cast<const TC*>(u), static_cast<const TC*>(dy), static_cast<TC*>(out), rows);    \
+    else                                                                                                         \
+      hipLaunchKernelGGL((qk_norm_fwd_kernel<TC, DD>), dim3(blocks), dim3(QK_THREADS), 0, stream,                \
+                         static_cast<const TC*>(u), static_cast<TC*>(out), rows);                                \
+  }
   if (bf16) {
     if (D == 64) { MUIR_QKN(uint16_t, 64) } else { MUIR_QKN(uint16_t, 128) }
   } else {
