@@ -848,7 +848,7 @@ hipError_t gate_bwd_typed(const GateShape& s, const void* x, const void* W_down,
     for (int i = 0; i < 5; ++i)
       u.p[i] = GemmProblem{dpre + dpo[i], Wu + L.woff[i], dz + L.zoff[i], s.M, L.r[i], L.W[i], L.W[i], L.r[i],
                            GATE_RTOT};
-    if ((e = run_gemm<TC, 128, 64, true, false, EPI_STORE>(u, stream)) != hipSuccess) return e;
+    if ((e = run_gemm<TC, 128, 128, true, false, EPI_STORE>(u, stream)) != hipSuccess) return e;
   }
   // 3. dx = dz W_down
   {
