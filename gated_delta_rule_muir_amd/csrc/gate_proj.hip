@@ -882,7 +882,7 @@ hipError_t gate_bwd_typed(const GateShape& s, const void* x, const void* W_down,
     for (int i = 0; i < 5; ++i)
       u.p[i] = GemmProblem{dpre + dpo[i], zr + L.zoff[i], part + L.woff[i], L.W[i], L.r[i], s.M, L.W[i], GATE_RTOT,
                            L.r[i]};
-    if ((e = run_gemm<TC, 128, 64, false, false, EPI_PARTIAL>(u, stream)) != hipSuccess) return e;
+    if ((e = run_gemm<TC, 128, 128, false, false, EPI_PARTIAL>(u, stream)) != hipSuccess) return e;
     const size_t n = L.woff[4] + static_cast<size_t>(L.r[4]) * L.W[4];
     hipLaunchKernelGGL(split_sum_kernel, dim3(static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 4096))), dim3(256),
                        0, stream, part, W.ksplit, W.part_stride, n, dW_up);
