@@ -18,9 +18,9 @@ Readings where the pages are silent (each one stated where it is used):
     erase b, output gate g, write w, readout q (gamma), at column offsets
     0, 64, 128, 256, 384 of the down-projection;
   * widths: f, b, q have H*dk channels (key channels), g, w have H*dv;
-  * no bias on the down-projection; the channel biases sit on the
-    up-projections ("channel biases so low-rank gates retain independent
-    operating points");
+  * no bias on the down-projection; the per-channel biases sit on the
+    up-projections, so that each low-rank gate keeps an operating point of
+    its own;
   * activations: log alpha = log sigmoid (a log-decay, <= 0); erase, write
     and the output gate are sigmoids; gamma = 2 sigmoid (a gain in (0, 2)
     around 1);
