@@ -137,8 +137,9 @@ def _one_step_state(S, q, k, v, la, er, wr, ga):
 
 
 def test_erase_sensitivity_is_key_energy_times_row_energy():
-    """Methodology: erase-gate changes are weighted by k_{t,j}^2 and the existing
-    row energy; write-gate changes act directly on v_t.  Measured by central
+    """Methodology: how much a change in the erase gate of channel j moves the
+    state scales with k_{t,j}^2 times the energy already in row j, while a
+    change in the write gate moves the written value v_t itself.  Measured by central
     differences of one oracle step:  ||dS_t/d erase_j|| = |k_j| ||S'_j||  and
     ||dS_t/d write_m|| = |v_m|.  Reading the prediction through k and erasing
     along erase*k instead would give |k_j| ||k^T S'|| and fail here."""
