@@ -3,21 +3,28 @@
 
 One timed step = one chunkwise forward (saving chunk states) plus one
 chunkwise backward over the headline workload: B=8, T=4096, H=16,
-dk=dv=128, chunk 64, bf16 inputs and gradients, fp32 states, synthetic
-seeded inputs already resident in HBM.  `value` is tokens/s (B*T per step time).
+dk=dv=128, chunk 64, bf16 inputs, fp32 gradients, fp32 running state,
+synthetic seeded inputs already resident in HBM.  `value` is tokens/s (B*T
+per step time).
 
 Beside it the line carries:
   roofline      the dominant kernel's algorithmic bytes per launch over its
                 average duration (HIP events recorded by the library between
-                its own launches, on the launch stream, inside the timed loop)
+                its own launches, on the launch stream, inside the timed loop);
+                algorithmic bytes are the operator's own inputs and outputs
+                (inputs, o / dO, saved chunk states and gradients, at the
+                dtypes written), never the kernels' intermediates, which show
+                up only in the measured `traffic`
   kernels       the same for every kernel of the step
+  step_model    the whole step's algorithmic bytes and flops over its time
   cpu_baseline  the fp64 sequential oracle on the host cores, on a bounded
                 sample of the same workload (4 batch rows: 64 heads x 4096)
-  secondary     long-context fwd+bwd (T=32768, chunk 128 and 256), one
-                1M-token stream (chunked prefill chained through the state,
-                then decode), the gate prologue at the layer's shape (fused
-                low-rank gate projection and q / k SiLU + L2, fwd + bwd), and
-                the streaming decode step (64 streams x 16 heads, 4096 steps)
+  secondary     the same step with bf16 gradients, long-context fwd+bwd
+                (T=32768, chunk 128 and 256), one 1M-token stream (chunked
+                prefill chained through the state, then decode), the gate
+                prologue at the layer's shape (fused low-rank gate projection
+                and q / k SiLU + L2, fwd + bwd), and the streaming decode step
+                (64 streams x 16 heads, 4096 steps; and a 512 MiB state)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 
@@ -46,24 +53,32 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# Algorithmic bytes per token-head of each kernel (d = head size, C = chunk,
-# bf16 inputs and gradients of 2 bytes, fp32 states): the bytes the kernel must
-# read and write by construction -- its inputs and outputs, not its re-reads.
-def kernel_bytes(d: int, C: int, e: int = 2):
-    """Algorithmic HBM bytes per token-head of each kernel of the training
-    step (bf16, 64-token chunks: the forward scan keeps the chunk deltas and
-    the chunk-start states in the compute type, and the backward reads them
-    with Kbar^T instead of recomputing them)."""
-    st = e * d * d / C  # one chunk-start state (compute type) per chunk, per token
-    sg = e * d * d / C  # one chunk-end state gradient (compute type) per chunk, per token
-    lf = 2 * 256 * e / 16  # the leaf blocks T_II, P_II (16 x 16 each per 16 tokens)
-    return {
-        "fwd_prep": 7 * d * e + 8 * d * e + lf,         # 7 inputs -> W, Q', Kbar (both ways), U~, O~, leaves
-        "fwd_scan": 5 * d * e + 2 * d * e + st,         # summary -> o, deltas, chunk states
-        "bwd_scan": 3 * d * e + d * e + sg,             # W, Q', Kbar, dO -> chunk-end state grads
-        # inputs, dO, deltas, Kbar^T, leaves, S, dS -> 7 grads in the input dtype
-        "bwd_chunk": 7 * d * e + 3 * d * e + lf + st + sg + 7 * d * e,
-    }
+# Algorithmic bytes per token-head (d = head size, C = chunk; e, es, eg: bytes
+# of an input, of a saved chunk-state element and of a gradient element): the
+# operator's own inputs and outputs only -- the seven inputs, o, dO, the
+# chunk-start states the forward saves for the backward, and the seven
+# gradients, each at the dtype written.  The kernels' intermediates (chunk
+# summaries, deltas, state gradients) are not counted: they appear only in
+# the measured traffic, whose ratio to these bytes shows what the
+# decomposition into kernels costs.
+def step_bytes(d: int, C: int, e: int = 2, es: int = 2, eg: int = 4):
+    """(forward, backward) algorithmic bytes per token-head: inputs 7de, o de
+    and the saved states d^2 es / C; inputs, dO, saved states and the
+    gradients 7d eg."""
+    fwd = 7 * d * e + d * e + d * d * es / C
+    bwd = 7 * d * e + d * e + d * d * es / C + 7 * d * eg
+    return fwd, bwd
+
+
+def kernel_bytes(d: int, C: int, e: int = 2, es: int = 2, eg: int = 4):
+    """Algorithmic bytes per token-head that each kernel of the step itself
+    moves: the prep kernel reads the inputs, the forward scan writes o and
+    the chunk-start states, the reverse scan reads dO, and the chunk
+    gradient kernel reads the inputs, dO and the states and writes the seven
+    gradients (dO is counted by both backward kernels, which both read it)."""
+    st = d * d * es / C
+    return {"fwd_prep": 7 * d * e, "fwd_scan": d * e + st, "bwd_scan": d * e,
+            "bwd_chunk": 7 * d * e + d * e + st + 7 * d * eg}
 
 
 def step_flops(d: int, C: int):
@@ -134,17 +149,21 @@ def gen_seq(B, T, H, d, dtype, decay, seed, torch, muir_inputs):
     return {n: (t.to("cuda") if t is not None else None) for n, t in inp.items()}, inp
 
 
-def time_fwdbwd(m, dv, C, steps, warmup, torch, hiprt, names, profile=True):
-    """Run warmup + timed fwd+bwd steps; returns (ms_per_step, per-kernel avg ms)."""
+def time_fwdbwd(m, dv, C, steps, warmup, torch, hiprt, names, profile=True, grad_dtype=None):
+    """Run warmup + timed fwd+bwd steps; returns (ms_per_step, per-kernel avg ms).
+    grad_dtype: the gradients' dtype (None: fp32)."""
     B, T, H, d = dv["q"].shape
     dev = dv["q"].device
+    gcode = m.MUIR_BF16 if grad_dtype == torch.bfloat16 else m.MUIR_F32
     fws = torch.empty(m.muir_chunk_fwd_workspace(B, T, H, d, d, C), dtype=torch.uint8, device=dev)
-    bws = torch.empty(m.muir_chunk_bwd_workspace(B, T, H, d, d, C), dtype=torch.uint8, device=dev)
+    bws = torch.empty(m.muir_chunk_bwd_workspace(B, T, H, d, d, C, grad_dtype=gcode), dtype=torch.uint8,
+                      device=dev)
     args = [dv[n] for n in names]
 
     def step():
         o, S_T, Sc = m.muir_chunk_fwd(*args, chunk=C, save_states=True, workspace=fws)
-        g = m.muir_chunk_bwd(*args, dv["dO"], S_chunks=Sc, summaries=fws, chunk=C, workspace=bws)
+        g = m.muir_chunk_bwd(*args, dv["dO"], S_chunks=Sc, summaries=fws, chunk=C, workspace=bws,
+                             grad_dtype=grad_dtype)
         return o, g
 
     for _ in range(warmup):
@@ -177,6 +196,37 @@ def time_fwdbwd(m, dv, C, steps, warmup, torch, hiprt, names, profile=True):
         kern = {k: v / steps for k, v in acc.items()}
         pool.close()
     return (t1 - t0) * 1e3 / steps, kern
+
+
+def roofline_report(kern, ms, d, C, nth, workload, eg):
+    """Per-kernel and whole-step figures from the algorithmic bytes (step_bytes,
+    kernel_bytes; gradients of eg bytes) of nth token-heads.  `roofline` is
+    the dominant (longest) kernel's: its algorithmic bytes per launch over its
+    average launch time, against the HBM peak (every kernel and the step are
+    below the bf16 MFMA ridge, see step_model), plus its measured HBM traffic
+    per launch when the counter record matches its sources."""
+    kb = kernel_bytes(d, C, eg=eg)
+    kernels = {}
+    for kn, t in kern.items():
+        byt = kb[kn] * nth
+        kernels[kn] = {"avg_us": t * 1e3, "alg_bytes": byt, "GBs": byt / (t * 1e-3) / 1e9,
+                       "hbm_frac": byt / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    dom = max(kern, key=lambda k: kern[k])
+    traffic = measured_traffic(dom, workload) if eg == 4 else None
+    roof = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GBs"], "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": kernels[dom]["GBs"] / HBM_PEAK_GBS, "traffic": traffic,
+            "traffic_over_alg": None if traffic is None else traffic / (kb[dom] * nth),
+            "alg_bytes_per_launch": kb[dom] * nth, "avg_launch_us": kernels[dom]["avg_us"]}
+    fb, bb = step_bytes(d, C, eg=eg)
+    fwd_f, bwd_f = step_flops(d, C)
+    sb, sf = (fb + bb) * nth, (fwd_f + bwd_f) * nth
+    t = ms * 1e-3
+    step_model = {"alg_bytes": sb, "alg_GBs": sb / t / 1e9, "alg_flops": sf,
+                  "hbm_floor_us": sb / (HBM_PEAK_GBS * 1e9) * 1e6,
+                  "mfma_floor_us": sf / (BF16_PEAK_TFLOPS * 1e12) * 1e6,
+                  "frac": max(sb / (HBM_PEAK_GBS * 1e9), sf / (BF16_PEAK_TFLOPS * 1e12)) / t,
+                  "mfma_util_alg": sf / t / (BF16_PEAK_TFLOPS * 1e12)}
+    return kernels, roof, step_model
 
 
 def cpu_baseline(inp_cpu, names, torch):
@@ -275,51 +325,44 @@ def decode_bench(m, torch, hiprt, N=64, H=16, d=128, steps=4096, seed=0):
                      else "state (%d MiB) larger than the 256 MB Infinity Cache") % (N * H * d * d * 4 >> 20)}
 
 
-def stream_bench(m, torch, hiprt, T=1 << 20, H=16, d=128, seg=32768, chunk=64, steps=1024, seed=0):
-    """One long stream (B=1): chunked prefill of T tokens in `seg`-token
-    segments chained through the state (S_T -> S0), then `steps` decode tokens
-    from that state.  Inputs are drawn on the GPU (torch generator)."""
-    g = torch.Generator(device="cuda")
-    g.manual_seed(seed)
-    bf = torch.bfloat16
-
-    def unit(x):
-        s = torch.nn.functional.silu(x)
-        return s / s.norm(dim=-1, keepdim=True).clamp_min(1e-12)
-
-    def draw(n):
-        shp = (1, n, H, d)
-        rates = torch.exp(torch.empty((H, d), device="cuda").uniform_(-9.2103, 1.0986, generator=g))
-        return [unit(torch.randn(shp, generator=g, device="cuda")).to(bf),
-                unit(torch.randn(shp, generator=g, device="cuda")).to(bf),
-                torch.randn(shp, generator=g, device="cuda").to(bf),
-                (-rates).expand(shp).to(bf).contiguous(),
-                torch.sigmoid(torch.randn(shp, generator=g, device="cuda")).to(bf),
-                torch.sigmoid(torch.randn(shp, generator=g, device="cuda")).to(bf),
-                (2 * torch.sigmoid(torch.randn(shp, generator=g, device="cuda"))).to(bf)]
-
-    segs = [draw(seg) for _ in range(T // seg)]
-    dec = [t[0].contiguous() for t in draw(steps)]  # [steps, H, d]
+def stream_bench(m, torch, muir_inputs):
+    """The stream_1m workload: one stream (B=1) prefilled in segments chained
+    through the state (S_T -> S0), then decode tokens from that state.  The
+    segments are muir_inputs.stream_segment_torch draws, the same inputs on
+    which tests/test_gpu_stream.py checks heads 0 and H-1 against the oracle;
+    they are drawn on the GPU before the timed region."""
+    w = muir_inputs.WORKLOADS["stream_1m"]
+    H, d, chunk, seg = w.H, w.dk, w.chunk, w.extra["segment"]
+    seed, steps = w.extra["seed"], w.extra["decode_steps"]
+    names = ("q", "k", "v", "log_a", "erase", "write", "gamma")
+    segs = []
+    for i in range(w.T // seg):
+        x = muir_inputs.stream_segment_torch(i, seg, H, d, d, device="cuda", decay=w.decay, seed=seed)
+        segs.append([x[n] for n in names])
+    x = muir_inputs.stream_segment_torch(w.T // seg, steps, H, d, d, device="cuda", decay=w.decay, seed=seed)
+    dec = [[x[n][:, t].contiguous() for n in names] for t in range(steps)]
     ws = torch.empty(m.muir_chunk_fwd_workspace(1, seg, H, d, d, chunk), dtype=torch.uint8, device="cuda")
-    o = torch.empty((1, seg, H, d), dtype=bf, device="cuda")
+    o = torch.empty((1, seg, H, d), dtype=torch.bfloat16, device="cuda")
     m.muir_chunk_fwd(*segs[0], chunk=chunk, workspace=ws, out=o)  # warm-up
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     S = None
-    for x in segs:
-        _, S, _ = m.muir_chunk_fwd(*x, S, chunk=chunk, workspace=ws, out=o)
+    for xs in segs:
+        _, S, _ = m.muir_chunk_fwd(*xs, S, chunk=chunk, workspace=ws, out=o)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    od = torch.empty((1, H, d), dtype=bf, device="cuda")
-    for t in range(steps):
-        m.muir_step(*(x[t:t + 1] for x in dec), S, out=od)
+    od = torch.empty((1, H, d), dtype=torch.bfloat16, device="cuda")
+    for xt in dec:
+        m.muir_step(*xt, S, out=od)
     torch.cuda.synchronize()
     t2 = time.perf_counter()
     del segs, dec
     torch.cuda.empty_cache()
-    return {"workload": f"one stream, H={H} d={d}: prefill {T} tokens in {seg}-token segments "
+    return {"workload": f"stream_1m: one stream, H={H} d={d}: prefill {w.T} tokens in {seg}-token segments "
                         f"(chunk {chunk}, state chained), then {steps} decode tokens",
-            "prefill_tokens_per_s": T / (t1 - t0), "decode_us_per_token": (t2 - t1) * 1e6 / steps}
+            "prefill_tokens_per_s": w.T / (t1 - t0), "decode_us_per_token": (t2 - t1) * 1e6 / steps,
+            "parity": "same inputs as tests/test_gpu_stream.py::test_stream_1m_prefill_then_decode, which checks "
+                      f"heads 0 and {H - 1} against the fp64 oracle over every token"}
 
 
 def gate_bench(m, torch, hiprt, M=32768, d=2048, H=16, dk=128, dv=128, steps=10, warmup=2, seed=0):
@@ -434,32 +477,19 @@ def main():
     nth = B * T * H
     log(f"[bench] {ms:.3f} ms/step -> {ntok / (ms * 1e-3):.4g} tokens/s")
 
-    kb = kernel_bytes(d, C)
-    kernels = {}
-    for kn, t in kern.items():
-        byt = kb[kn] * nth
-        kernels[kn] = {"avg_us": t * 1e3, "alg_bytes": byt, "GBs": byt / (t * 1e-3) / 1e9,
-                       "hbm_frac": byt / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    dom = max(kern, key=lambda k: kern[k])
-    fwd_f, bwd_f = step_flops(d, C)
-    step_bytes = sum(kb.values()) * nth
-    traffic = measured_traffic(dom, wl.name)
-    roof = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GBs"], "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": kernels[dom]["GBs"] / HBM_PEAK_GBS, "traffic": traffic,
-            "alg_bytes_per_launch": kb[dom] * nth, "avg_launch_us": kernels[dom]["avg_us"]}
+    kernels, roof, step_model = roofline_report(kern, ms, d, C, nth, wl.name, eg=4)
     result = {
         "metric": METRIC, "value": ntok / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "dk": d, "dv": d, "chunk": C,
                    "inputs": "bf16, seeded (muir_inputs), per-channel decay rates 1e-4..3",
+                   "gradients": "fp32", "saved_chunk_states": "bf16", "running_state": "fp32",
                    "step": "muir_chunk_fwd (saving chunk states; its workspace keeps the chunk "
-                           "summaries) + muir_chunk_bwd (reusing both)"},
+                           "summaries) + muir_chunk_bwd (reusing both), fp32 gradients"},
         "roofline": roof,
         "kernels": kernels,
-        "step_model": {"alg_bytes": step_bytes, "alg_GBs": step_bytes / (ms * 1e-3) / 1e9,
-                       "alg_flops": (fwd_f + bwd_f) * nth,
-                       "mfma_util_alg": (fwd_f + bwd_f) * nth / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)},
+        "step_model": step_model,
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) on one batch row ...")
@@ -468,10 +498,19 @@ def main():
     del inp_cpu
     if not args.no_secondary:
         sec = {}
-        del dv
-        torch.cuda.empty_cache()
         chosen = set(filter(None, args.secondary.split(",")))
         want = lambda name: not chosen or name in chosen  # noqa: E731
+        if want("layer_fwdbwd_4k_bf16grads"):
+            log("[bench] secondary: the same step with bf16 gradients")
+            ms2, k2 = time_fwdbwd(m, dv, C, max(5, args.steps // 2), 2, torch, hiprt, names,
+                                  grad_dtype=torch.bfloat16)
+            kern2, roof2, sm2 = roofline_report(k2, ms2, d, C, nth, wl.name, eg=2)
+            sec["layer_fwdbwd_4k_bf16grads"] = {"tokens_per_s": ntok / (ms2 * 1e-3), "ms_per_step": ms2,
+                                                 "gradients": "bf16", "kernels": kern2, "roofline": roof2,
+                                                 "step_model": sm2}
+            log(f"[bench]   {ntok / (ms2 * 1e-3):.4g} tokens/s")
+        del dv
+        torch.cuda.empty_cache()
         for name in ("long_32k_c128", "long_32k_c256"):
             if not want(name):
                 continue
@@ -479,17 +518,15 @@ def main():
             log(f"[bench] secondary {name}")
             dv2, _ = gen_seq(w.B, w.T, w.H, w.dk, w.dtype, w.decay, 0, torch, muir_inputs)
             ms2, k2 = time_fwdbwd(m, dv2, w.chunk, 5, 2, torch, hiprt, names)
-            fwd_f2, bwd_f2 = step_flops(w.dk, w.chunk)
-            nth2 = w.B * w.T * w.H
-            sec[name] = {"tokens_per_s": w.B * w.T / (ms2 * 1e-3), "ms_per_step": ms2,
-                         "kernels_us": {k: v * 1e3 for k, v in k2.items()},
-                         "mfma_util_alg": (fwd_f2 + bwd_f2) * nth2 / (ms2 * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)}
+            kern2, roof2, sm2 = roofline_report(k2, ms2, w.dk, w.chunk, w.B * w.T * w.H, w.name, eg=4)
+            sec[name] = {"tokens_per_s": w.B * w.T / (ms2 * 1e-3), "ms_per_step": ms2, "gradients": "fp32",
+                         "kernels": kern2, "roofline": roof2, "step_model": sm2}
             log(f"[bench]   {sec[name]['tokens_per_s']:.4g} tokens/s")
             del dv2
             torch.cuda.empty_cache()
         if want("stream_1m"):
             log("[bench] secondary stream (1M-token prefill, then decode)")
-            sec["stream_1m"] = stream_bench(m, torch, hiprt)
+            sec["stream_1m"] = stream_bench(m, torch, muir_inputs)
             log(f"[bench]   prefill {sec['stream_1m']['prefill_tokens_per_s']:.4g} tokens/s, "
                 f"decode {sec['stream_1m']['decode_us_per_token']:.1f} us/token")
         if want("gate_prologue_4k"):

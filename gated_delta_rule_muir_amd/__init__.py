@@ -51,7 +51,7 @@ class _GateDims(ctypes.Structure):
 class _Dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("gamma_mode", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("gamma_mode", ctypes.c_int32), ("grad_dtype", ctypes.c_int32)]
 
 
 _lib = None
@@ -146,8 +146,18 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _dims(B, T, H, dk, dv, chunk, dtype, gamma_mode=MUIR_GAMMA_TOKEN) -> _Dims:
-    return _Dims(B, T, H, dk, dv, chunk, dtype, gamma_mode)
+def _dims(B, T, H, dk, dv, chunk, dtype, gamma_mode=MUIR_GAMMA_TOKEN, grad_dtype=MUIR_F32) -> _Dims:
+    return _Dims(B, T, H, dk, dv, chunk, dtype, gamma_mode, grad_dtype)
+
+
+def _grad_code(grad_dtype, dt) -> int:
+    """Code of the per-token gradients' element type: fp32 (the default) or,
+    for bf16 inputs, bf16."""
+    if grad_dtype is None or grad_dtype == torch.float32:
+        return MUIR_F32
+    if grad_dtype == torch.bfloat16 and dt == torch.bfloat16:
+        return MUIR_BF16
+    raise TypeError(f"grad_dtype {grad_dtype}: fp32, or bf16 for bf16 inputs")
 
 
 def _gamma_mode(gamma, lead, H, dk, dt, dev) -> int:
@@ -167,8 +177,9 @@ def muir_chunk_fwd_workspace(B, T, H, dk, dv, chunk, dtype=MUIR_BF16, gamma_mode
     return int(lib().muir_chunk_fwd_workspace(ctypes.byref(d)))
 
 
-def muir_chunk_bwd_workspace(B, T, H, dk, dv, chunk, dtype=MUIR_BF16, gamma_mode=MUIR_GAMMA_TOKEN) -> int:
-    d = _dims(B, T, H, dk, dv, chunk, dtype, gamma_mode)
+def muir_chunk_bwd_workspace(B, T, H, dk, dv, chunk, dtype=MUIR_BF16, gamma_mode=MUIR_GAMMA_TOKEN,
+                             grad_dtype=MUIR_F32) -> int:
+    d = _dims(B, T, H, dk, dv, chunk, dtype, gamma_mode, grad_dtype)
     return int(lib().muir_chunk_bwd_workspace(ctypes.byref(d)))
 
 
@@ -222,11 +233,13 @@ def muir_chunk_fwd(q, k, v, log_a, erase, write, gamma, S0=None, *, chunk: int =
 
 def muir_chunk_bwd(q, k, v, log_a, erase, write, gamma, dO, S0=None, S_chunks=None, dS_T=None, *,
                    chunk: int = 64, summaries: Optional[torch.Tensor] = None,
-                   workspace: Optional[torch.Tensor] = None, want_dS0: bool = True):
+                   workspace: Optional[torch.Tensor] = None, want_dS0: bool = True,
+                   grad_dtype: Optional[torch.dtype] = None):
     """Chunkwise backward.  Returns a dict of gradients (dq, dk, dv, dlog_a,
-    derase, dwrite in the input dtype, accumulated in fp32 and rounded once;
-    dgamma in the input dtype for a per-token gate, [H, dk] fp32 (summed over
-    batch and tokens) for a static one, None without a gate; dS0 in fp32).
+    derase, dwrite in `grad_dtype`: fp32 by default, or bf16 for bf16 inputs,
+    accumulated in fp32 and rounded once; dgamma in `grad_dtype` for a
+    per-token gate, [H, dk] fp32 (summed over batch and tokens) for a static
+    one, None without a gate; dS0 in fp32).
 
     `S_chunks` (from muir_chunk_fwd(save_states=True)) and `summaries` (the
     `workspace` tensor of that forward call, left unchanged) are saved forward
@@ -254,13 +267,14 @@ def muir_chunk_bwd(q, k, v, log_a, erase, write, gamma, dO, S0=None, S_chunks=No
         if (not summaries.is_cuda or summaries.device != dev or not summaries.is_contiguous()
                 or summaries.numel() * summaries.element_size() < need):
             raise ValueError(f"summaries: expected the forward workspace ({need} bytes on {dev})")
-    gd = dict(dtype=dt, device=dev)
+    gcode = _grad_code(grad_dtype, dt)
+    gd = dict(dtype=torch.bfloat16 if gcode == MUIR_BF16 else torch.float32, device=dev)
     g = {n: torch.empty((B, T, H, dk), **gd) for n in ("dq", "dk", "dlog_a", "derase")}
     g.update({n: torch.empty((B, T, H, dv), **gd) for n in ("dv", "dwrite")})
     g["dgamma"] = (torch.empty((B, T, H, dk), **gd) if gm == MUIR_GAMMA_TOKEN else
                    torch.empty((H, dk), dtype=torch.float32, device=dev) if gm == MUIR_GAMMA_STATIC else None)
     g["dS0"] = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None
-    d = _dims(B, T, H, dk, dv, chunk, code, gm)
+    d = _dims(B, T, H, dk, dv, chunk, code, gm, gcode)
     nbytes = int(lib().muir_chunk_bwd_workspace(ctypes.byref(d)))
     ws = _workspace(nbytes, dev, workspace)
     rc = lib().muir_chunk_bwd(ctypes.byref(d), *(_ptr(t) for t in (q, k, v, log_a, erase, write, gamma)),
@@ -280,8 +294,8 @@ def muir_chunk_varlen_fwd_workspace(N, max_len, H, dk, dv, chunk, dtype=MUIR_BF1
 
 
 def muir_chunk_varlen_bwd_workspace(N, max_len, H, dk, dv, chunk, dtype=MUIR_BF16,
-                                    gamma_mode=MUIR_GAMMA_TOKEN) -> int:
-    d = _dims(N, max_len, H, dk, dv, chunk, dtype, gamma_mode)
+                                    gamma_mode=MUIR_GAMMA_TOKEN, grad_dtype=MUIR_F32) -> int:
+    d = _dims(N, max_len, H, dk, dv, chunk, dtype, gamma_mode, grad_dtype)
     return int(lib().muir_chunk_varlen_bwd_workspace(ctypes.byref(d)))
 
 
@@ -342,9 +356,11 @@ def muir_chunk_varlen_fwd(q, k, v, log_a, erase, write, gamma, cu_seqlens, S0=No
 
 def muir_chunk_varlen_bwd(q, k, v, log_a, erase, write, gamma, dO, cu_seqlens, S0=None, dS_T=None, *,
                           chunk: int = 64, max_len: Optional[int] = None,
-                          workspace: Optional[torch.Tensor] = None, want_dS0: bool = True):
+                          workspace: Optional[torch.Tensor] = None, want_dS0: bool = True,
+                          grad_dtype: Optional[torch.dtype] = None):
     """Backward of muir_chunk_varlen_fwd.  Returns the gradients as
-    muir_chunk_bwd does, per-token ones [T_total, H, D] and dS0 [N, H, dk, dv]."""
+    muir_chunk_bwd does (per-token ones [T_total, H, D] in `grad_dtype`, fp32
+    by default) and dS0 [N, H, dk, dv]."""
     Tt, H, dk = q.shape
     dv = v.shape[2]
     dev, dt = q.device, q.dtype
@@ -359,13 +375,14 @@ def muir_chunk_varlen_bwd(q, k, v, log_a, erase, write, gamma, dO, cu_seqlens, S
         _check_io("S0", S0, (N, H, dk, dv), torch.float32, dev)
     if dS_T is not None:
         _check_io("dS_T", dS_T, (N, H, dk, dv), torch.float32, dev)
-    gd = dict(dtype=dt, device=dev)
+    gcode = _grad_code(grad_dtype, dt)
+    gd = dict(dtype=torch.bfloat16 if gcode == MUIR_BF16 else torch.float32, device=dev)
     g = {n: torch.empty((Tt, H, dk), **gd) for n in ("dq", "dk", "dlog_a", "derase")}
     g.update({n: torch.empty((Tt, H, dv), **gd) for n in ("dv", "dwrite")})
     g["dgamma"] = (torch.empty((Tt, H, dk), **gd) if gm == MUIR_GAMMA_TOKEN else
                    torch.empty((H, dk), dtype=torch.float32, device=dev) if gm == MUIR_GAMMA_STATIC else None)
     g["dS0"] = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if want_dS0 else None
-    d = _dims(N, L, H, dk, dv, chunk, code, gm)
+    d = _dims(N, L, H, dk, dv, chunk, code, gm, gcode)
     ws = _workspace(int(lib().muir_chunk_varlen_bwd_workspace(ctypes.byref(d))), dev, workspace)
     rc = lib().muir_chunk_varlen_bwd(ctypes.byref(d), _ptr(cu_seqlens),
                                      *(_ptr(t) for t in (q, k, v, log_a, erase, write, gamma)),

@@ -69,15 +69,18 @@ template <typename TC, int DK, int C> constexpr int stage_split() {
   return DK == 64 ? 1 : (sizeof(TC) == 2 ? (C == 64 ? 1 : 2) : (C == 64 ? 4 : 8));
 }
 
-template <typename Tin, int DK, int C, int NW, bool DIRECT, bool GTOK>
+// Tin: element type of the inputs, dO, the chunk states and the MFMA
+// operands; Tg: element type of the per-token gradients (Tin, or fp32 for
+// bf16 inputs).
+template <typename Tin, typename Tg, int DK, int C, int NW, bool DIRECT, bool GTOK>
 __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     int T, int H, const Tin* __restrict__ q, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ log_a, const Tin* __restrict__ erase,
     const Tin* __restrict__ write, const Tin* __restrict__ gamma, const char* __restrict__ summ,
     size_t summ_bytes, size_t tp_offset, size_t dl_offset, const Tin* __restrict__ S_chunks,
-    const Tin* __restrict__ dS_chunks, const Tin* __restrict__ dO, Tin* __restrict__ dq,
-    Tin* __restrict__ dk, Tin* __restrict__ dv, Tin* __restrict__ dlog_a,
-    Tin* __restrict__ derase, Tin* __restrict__ dwrite, Tin* __restrict__ dgamma,
+    const Tin* __restrict__ dS_chunks, const Tin* __restrict__ dO, Tg* __restrict__ dq,
+    Tg* __restrict__ dk, Tg* __restrict__ dv, Tg* __restrict__ dlog_a,
+    Tg* __restrict__ derase, Tg* __restrict__ dwrite, Tg* __restrict__ dgamma,
     char* __restrict__ scratch, int gmode, float* __restrict__ dgam_part) {
   typedef Tin TC;
   typedef MM<TC> M;
@@ -143,13 +146,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   const Tin* gb = gbase + ebase;
   const Tin* gst = gbase + static_cast<size_t>(h) * DK;
   const Tin* dOb = dO + ebase;
-  Tin* dqb = dq + ebase;
-  Tin* dkb = dk + ebase;
-  Tin* dvb = dv + ebase;
-  Tin* dlb = dlog_a + ebase;
-  Tin* deb = derase + ebase;
-  Tin* dwb = dwrite + ebase;
-  Tin* dgb = dgamma + ebase;
+  Tg* dqb = dq + ebase;
+  Tg* dkb = dk + ebase;
+  Tg* dvb = dv + ebase;
+  Tg* dlb = dlog_a + ebase;
+  Tg* deb = derase + ebase;
+  Tg* dwb = dwrite + ebase;
+  Tg* dgb = dgamma + ebase;
   auto gi = [&](int t, int j) -> uint32_t { return static_cast<uint32_t>(t) * HD + static_cast<uint32_t>(j); };
   // the readout gate of element (t, j) of the chunk (GTOK: per token, as the
   // other inputs; else static or none, chosen at run time)
@@ -199,12 +202,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   float (*sRow)[DK] = reinterpret_cast<float (*)[DK]>(&sTA[0][0]);
 
   // identity operand: a 16x16 product with it moves a tile's rows onto lanes
+  // (identf: the same in fp32, for fp32 gradients of bf16 inputs)
   frag ident;
+  f32x4 identf;
   {
-    f32x4 idv;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) idv[i] = (4 * g + i == c16) ? 1.f : 0.f;
-    ident = M::from_f32(idv);
+    for (int i = 0; i < 4; ++i) identf[i] = (4 * g + i == c16) ? 1.f : 0.f;
+    ident = M::from_f32(identf);
   }
 
   // within-block prefix (through each token) and suffix (after it) of log_a,
@@ -283,12 +287,16 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   // 4g..4g+3
   auto turn = [&](f32x4 tile) -> f32x4 { return M::mma(M::from_f32(tile), ident, zero4()); };
   // a gradient tile in MFMA-output layout (tokens r0 + 4g+i, channel colv(n))
-  // to its [B, T, H, D] tensor: in bf16 turned into token rows of four
-  // channels (one 8-byte store; the turn rounds to bf16 as the store would),
-  // in fp32 element by element
-  auto store_grad = [&](Tin* base, int r0, int n, f32x4 tile) {
-    if constexpr (sizeof(TC) == 2) {
+  // to its [B, T, H, D] tensor, turned into token rows of four channels (one
+  // 8- or 16-byte store per lane): bf16 gradients by the bf16 identity product
+  // (which rounds to bf16 as the store would), fp32 gradients of bf16 inputs
+  // by an fp32 identity product (exact), fp32 gradients of fp32 inputs
+  // element by element
+  auto store_grad = [&](Tg* base, int r0, int n, f32x4 tile) {
+    if constexpr (sizeof(Tg) == 2) {
       store4(at(base, gi(r0 + c16, col0(n) + 4 * g)), turn(tile));
+    } else if constexpr (sizeof(TC) == 2) {
+      store4(at(base, gi(r0 + c16, col0(n) + 4 * g)), MM<float>::mma(tile, identf, zero4()));
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) *at(base, gi(r0 + 4 * g + i, colv(n))) = tile[i];
@@ -1144,32 +1152,35 @@ hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, c
                             hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(s.nchunks());
   if (grid == 0) return hipSuccess;
-#define MUIR_BCH2(TT, DD, CC, NW, DIR, GT)                                                                      \
-  hipLaunchKernelGGL((bwd_chunk_kernel<TT, DD, CC, NW, DIR, GT>), dim3(grid), dim3(64 * NW), 0, stream, s.T, s.H, \
-                     (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, (const TT*)erase,      \
-                     (const TT*)write, (const TT*)gamma, (const char*)summ, s.summary_bytes(),          \
-                     s.tp_offset(), s.dl_offset(), (const TT*)S_chunks, (const TT*)dS_chunks, (const TT*)dO, (TT*)dq, (TT*)dk,      \
-                     (TT*)dv, (TT*)dlog_a, (TT*)derase, (TT*)dwrite, (TT*)dgamma, (char*)scratch, s.gmode, \
+#define MUIR_BCH2(TT, TG, DD, CC, NW, DIR, GT)                                                              \
+  hipLaunchKernelGGL((bwd_chunk_kernel<TT, TG, DD, CC, NW, DIR, GT>), dim3(grid), dim3(64 * NW), 0, stream, s.T, \
+                     s.H, (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, (const TT*)erase,        \
+                     (const TT*)write, (const TT*)gamma, (const char*)summ, s.summary_bytes(), s.tp_offset(),    \
+                     s.dl_offset(), (const TT*)S_chunks, (const TT*)dS_chunks, (const TT*)dO, (TG*)dq, (TG*)dk,  \
+                     (TG*)dv, (TG*)dlog_a, (TG*)derase, (TG*)dwrite, (TG*)dgamma, (char*)scratch, s.gmode,       \
                      dgam_part)
-#define MUIR_BCH1(TT, DD, CC, NW, DIR)                              \
-  do {                                                              \
-    if (s.gmode == GAMMA_TOKEN) MUIR_BCH2(TT, DD, CC, NW, DIR, true); \
-    else MUIR_BCH2(TT, DD, CC, NW, DIR, false);                     \
+#define MUIR_BCH1(TT, TG, DD, CC, NW, DIR)                              \
+  do {                                                                  \
+    if (s.gmode == GAMMA_TOKEN) MUIR_BCH2(TT, TG, DD, CC, NW, DIR, true); \
+    else MUIR_BCH2(TT, TG, DD, CC, NW, DIR, false);                     \
   } while (0)
-#define MUIR_BCH(TT, DD, NW, DIR64)                         \
-  do {                                                      \
-    if (s.C == 64) MUIR_BCH1(TT, DD, 64, NW, DIR64);        \
-    else if (s.C == 128) MUIR_BCH1(TT, DD, 128, NW, false); \
-    else MUIR_BCH1(TT, DD, 256, NW, false);                 \
+#define MUIR_BCH(TT, TG, DD, NW, DIR64)                         \
+  do {                                                          \
+    if (s.C == 64) MUIR_BCH1(TT, TG, DD, 64, NW, DIR64);        \
+    else if (s.C == 128) MUIR_BCH1(TT, TG, DD, 128, NW, false); \
+    else MUIR_BCH1(TT, TG, DD, 256, NW, false);                 \
   } while (0)
   // one 16-column tile per wave: 8 waves at d = 128, 4 at d = 64; the direct
   // form exactly where ChunkShape::bwd_direct says so (bf16, C = 64)
-  if (s.bf16) {
-    if (s.DK == 128) MUIR_BCH(uint16_t, 128, 8, true);
-    else MUIR_BCH(uint16_t, 64, 4, true);
+  if (s.bf16 && s.gbf16) {
+    if (s.DK == 128) MUIR_BCH(uint16_t, uint16_t, 128, 8, true);
+    else MUIR_BCH(uint16_t, uint16_t, 64, 4, true);
+  } else if (s.bf16) {
+    if (s.DK == 128) MUIR_BCH(uint16_t, float, 128, 8, true);
+    else MUIR_BCH(uint16_t, float, 64, 4, true);
   } else {
-    if (s.DK == 128) MUIR_BCH(float, 128, 8, false);
-    else MUIR_BCH(float, 64, 4, false);
+    if (s.DK == 128) MUIR_BCH(float, float, 128, 8, false);
+    else MUIR_BCH(float, float, 64, 4, false);
   }
 #undef MUIR_BCH
 #undef MUIR_BCH1

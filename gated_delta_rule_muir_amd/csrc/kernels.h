@@ -39,12 +39,14 @@ enum GammaMode { GAMMA_TOKEN = 0, GAMMA_STATIC = 1, GAMMA_NONE = 2 };
 struct ChunkShape {
   int B, T, H, DK, DV, C;
   bool bf16;
-  int gmode;  // GammaMode
+  bool gbf16;  // per-token gradients in bf16 (else fp32)
+  int gmode;   // GammaMode
   // chunks per sequence, a partial last one included (the kernels only ever
   // run on shapes whose T is a multiple of C)
   int NC() const { return (T + C - 1) / C; }
   size_t nchunks() const { return static_cast<size_t>(B) * H * NC(); }
   size_t tc_bytes() const { return bf16 ? 2 : 4; }
+  size_t tg_bytes() const { return gbf16 ? 2 : 4; }  // one per-token gradient element
   // Per-chunk block of the forward intermediates ("chunk summary"), see SummaryPart.
   size_t summary_elems() const { return summary_part(SP_END, C, DK, DV); }
   size_t gc_offset() const { return summary_elems() * tc_bytes(); }
@@ -102,7 +104,8 @@ hipError_t launch_bwd_scan(const ChunkShape& s, const void* summ, const void* dO
                            const float* dS_T, void* dS_chunks, float* dS0, float* split,
                            hipStream_t stream);
 
-// Chunk-parallel: all input gradients of every chunk.  `summ` holds the
+// Chunk-parallel: all input gradients of every chunk (per-token ones in the
+// element type s.gbf16 selects).  `summ` holds the
 // chunk summaries (their leaf blocks are read; with bwd_direct also Kbar^T,
 // Gamma_C and the deltas); `scratch` holds bwd_chunk_scratch_bytes(s) per
 // chunk (the deltas and block-start states of the forward sweep; none with

@@ -13,9 +13,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
-muir_status_t check_dims(const muir_dims_t* d, ChunkShape* s) {
+// `bwd`: the sizes of a backward call, whose per-token gradients are fp32 or,
+// for bf16 inputs, bf16 (the forward calls ignore grad_dtype).
+muir_status_t check_dims(const muir_dims_t* d, ChunkShape* s, bool bwd = false) {
   if (!d) return MUIR_ERR_NULL;
   if (d->dtype != MUIR_F32 && d->dtype != MUIR_BF16) return MUIR_ERR_DTYPE;
+  if (bwd && d->grad_dtype != MUIR_F32 && !(d->grad_dtype == MUIR_BF16 && d->dtype == MUIR_BF16))
+    return MUIR_ERR_DTYPE;
   if (d->gamma_mode < MUIR_GAMMA_TOKEN || d->gamma_mode > MUIR_GAMMA_NONE) return MUIR_ERR_MODE;
   if (d->B < 0 || d->T < 0 || d->H < 0) return MUIR_ERR_SHAPE;
   if (d->dk != d->dv || (d->dk != 64 && d->dk != 128)) return MUIR_ERR_SHAPE;
@@ -32,6 +36,7 @@ muir_status_t check_dims(const muir_dims_t* d, ChunkShape* s) {
   s->DV = d->dv;
   s->C = d->chunk;
   s->bf16 = d->dtype == MUIR_BF16;
+  s->gbf16 = bwd && d->grad_dtype == MUIR_BF16;
   s->gmode = d->gamma_mode;
   return MUIR_OK;
 }
@@ -67,18 +72,19 @@ size_t bwd_ws(const ChunkShape& s) {
 }
 
 // Staging area of a padded call, after the kernels' workspace: one
-// [N, T_padded, H, D] copy per staged tensor, in the compute type -- the
-// inputs (the gate only when it is per token) and o, or the inputs, dO and
-// the gradients.
-size_t staged_bytes(const ChunkShape& p, int D) {
-  return round256(static_cast<size_t>(p.B) * p.T * p.H * D * p.tc_bytes());
+// [N, T_padded, H, D] copy per staged tensor -- the inputs (the gate only
+// when it is per token) and o, or the inputs, dO and the gradients; inputs,
+// o and dO in the compute type, gradients in their own type (esize bytes).
+size_t staged_bytes(const ChunkShape& p, int D, size_t esize) {
+  return round256(static_cast<size_t>(p.B) * p.T * p.H * D * esize);
 }
 int staged_dk_inputs(const ChunkShape& p) { return p.gmode == MUIR_GAMMA_TOKEN ? 5 : 4; }  // q, k, log_a, erase, [gamma]
 size_t fwd_stage_bytes(const ChunkShape& p) {
-  return staged_dk_inputs(p) * staged_bytes(p, p.DK) + 3 * staged_bytes(p, p.DV);  // + v, write, o
+  return staged_dk_inputs(p) * staged_bytes(p, p.DK, p.tc_bytes()) + 3 * staged_bytes(p, p.DV, p.tc_bytes());  // + v, write, o
 }
 size_t bwd_stage_bytes(const ChunkShape& p) {
-  return 2 * staged_dk_inputs(p) * staged_bytes(p, p.DK) + 5 * staged_bytes(p, p.DV);  // + v, write, dO, dv, dwrite
+  return staged_dk_inputs(p) * (staged_bytes(p, p.DK, p.tc_bytes()) + staged_bytes(p, p.DK, p.tg_bytes())) +
+         3 * staged_bytes(p, p.DV, p.tc_bytes()) + 2 * staged_bytes(p, p.DV, p.tg_bytes());  // + v, write, dO; dv, dwrite
 }
 
 // The readout gate's pointer is required (and checked) unless the gate is absent.
@@ -143,9 +149,9 @@ __global__ void stage_kernel(const uint4* __restrict__ src, uint4* __restrict__ 
   }
 }
 
-hipError_t stage(const void* src, void* dst, const ChunkShape& p, int Tsrc, int D, const int32_t* cu,
+hipError_t stage(const void* src, void* dst, const ChunkShape& p, int Tsrc, int D, size_t esize, const int32_t* cu,
                  bool to_padded, hipStream_t s) {
-  const int WW = static_cast<int>(static_cast<size_t>(p.H) * D * p.tc_bytes() / 16);
+  const int WW = static_cast<int>(static_cast<size_t>(p.H) * D * esize / 16);
   const size_t total = static_cast<size_t>(p.B) * p.T * WW;
   if (total == 0) return hipSuccess;
   const unsigned blocks = static_cast<unsigned>(total / 256 + 1 < 8192 ? total / 256 + 1 : 8192);
@@ -234,9 +240,9 @@ muir_status_t bwd_core(const ChunkShape& s, const Inputs& in, const float* S0, c
 // Carves the staged tensors out of the staging area, in call order.
 struct StageCursor {
   char* p;
-  void* take(const ChunkShape& ps, int D) {
+  void* take(const ChunkShape& ps, int D, size_t esize) {
     void* r = p;
-    p += staged_bytes(ps, D);
+    p += staged_bytes(ps, D, esize);
     return r;
   }
 };
@@ -250,8 +256,8 @@ muir_status_t stage_inputs(const ChunkShape& p, int Tsrc, const int32_t* cu, con
       continue;
     }
     const int D = kIsDk[i] ? p.DK : p.DV;
-    void* dst = cur->take(p, D);
-    if (stage(in.x[i], dst, p, Tsrc, D, cu, true, hs) != hipSuccess) return MUIR_ERR_HIP;
+    void* dst = cur->take(p, D, p.tc_bytes());
+    if (stage(in.x[i], dst, p, Tsrc, D, p.tc_bytes(), cu, true, hs) != hipSuccess) return MUIR_ERR_HIP;
     out->x[i] = dst;
   }
   return MUIR_OK;
@@ -331,9 +337,9 @@ muir_status_t fwd_staged(const ChunkShape& s, const int32_t* cu, const Inputs& i
   Inputs sin;
   muir_status_t st = stage_inputs(p, s.T, cu, in, &sin, &cur, hs);
   if (st != MUIR_OK) return st;
-  void* po = cur.take(p, p.DV);
+  void* po = cur.take(p, p.DV, p.tc_bytes());
   if ((st = fwd_core(p, sin, S0, po, S_T, S_chunks, workspace, hs)) != MUIR_OK) return st;
-  return stage(po, o, p, s.T, p.DV, cu, false, hs) == hipSuccess ? MUIR_OK : MUIR_ERR_HIP;
+  return stage(po, o, p, s.T, p.DV, p.tc_bytes(), cu, false, hs) == hipSuccess ? MUIR_OK : MUIR_ERR_HIP;
 }
 
 muir_status_t bwd_staged(const ChunkShape& s, const int32_t* cu, const Inputs& in, const float* S0,
@@ -344,20 +350,21 @@ muir_status_t bwd_staged(const ChunkShape& s, const int32_t* cu, const Inputs& i
   Inputs sin;
   muir_status_t st = stage_inputs(p, s.T, cu, in, &sin, &cur, hs);
   if (st != MUIR_OK) return st;
-  void* pdO = cur.take(p, p.DV);
-  if (stage(dO, pdO, p, s.T, p.DV, cu, true, hs) != hipSuccess) return MUIR_ERR_HIP;
+  void* pdO = cur.take(p, p.DV, p.tc_bytes());
+  if (stage(dO, pdO, p, s.T, p.DV, p.tc_bytes(), cu, true, hs) != hipSuccess) return MUIR_ERR_HIP;
   Grads sg;
   for (int i = 0; i < 7; ++i) {
     if (i == 6 && p.gmode != MUIR_GAMMA_TOKEN) {
       sg.x[6] = gr.x[6];  // a static gate's gradient is [H, dk] fp32; an absent gate has none
       continue;
     }
-    sg.x[i] = cur.take(p, kIsDk[i] ? p.DK : p.DV);
+    sg.x[i] = cur.take(p, kIsDk[i] ? p.DK : p.DV, p.tg_bytes());
   }
   if ((st = bwd_core(p, sin, S0, S_chunks, summaries, pdO, dS_T, sg, dS0, workspace, hs)) != MUIR_OK) return st;
   for (int i = 0; i < 7; ++i) {
     if (i == 6 && p.gmode != MUIR_GAMMA_TOKEN) continue;
-    if (stage(sg.x[i], gr.x[i], p, s.T, kIsDk[i] ? p.DK : p.DV, cu, false, hs) != hipSuccess) return MUIR_ERR_HIP;
+    if (stage(sg.x[i], gr.x[i], p, s.T, kIsDk[i] ? p.DK : p.DV, p.tg_bytes(), cu, false, hs) != hipSuccess)
+      return MUIR_ERR_HIP;
   }
   return MUIR_OK;
 }
@@ -405,7 +412,7 @@ size_t varlen_bwd_need(const ChunkShape& s) { return bwd_ws(padded(s)) + bwd_sta
 
 extern "C" {
 
-int32_t muir_abi_version(void) { return 7; }
+int32_t muir_abi_version(void) { return 8; }
 
 int32_t muir_set_profile_events(void** events, int32_t count) {
   if (count < 0 || (count > 0 && !events)) return MUIR_ERR_NULL;
@@ -439,7 +446,7 @@ size_t muir_chunk_fwd_workspace(const muir_dims_t* dims) {
 
 size_t muir_chunk_bwd_workspace(const muir_dims_t* dims) {
   ChunkShape s;
-  if (check_dims(dims, &s) != MUIR_OK) return 0;
+  if (check_dims(dims, &s, true) != MUIR_OK) return 0;
   return bwd_need(s);
 }
 
@@ -468,7 +475,7 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims, const void* q, const void*
                              void* derase, void* dwrite, void* dgamma, float* dS0,
                              void* workspace, size_t workspace_bytes, void* stream) {
   ChunkShape s;
-  muir_status_t st = check_dims(dims, &s);
+  muir_status_t st = check_dims(dims, &s, true);
   if (st != MUIR_OK) return st;
   const Inputs in{{q, k, v, log_a, erase, write, gamma}};
   const Grads gr{{dq, dk, dv, dlog_a, derase, dwrite, dgamma}};
@@ -489,7 +496,7 @@ size_t muir_chunk_varlen_fwd_workspace(const muir_dims_t* dims) {
 
 size_t muir_chunk_varlen_bwd_workspace(const muir_dims_t* dims) {
   ChunkShape s;
-  if (check_dims(dims, &s) != MUIR_OK) return 0;
+  if (check_dims(dims, &s, true) != MUIR_OK) return 0;
   return varlen_bwd_need(s);
 }
 
@@ -517,7 +524,7 @@ muir_status_t muir_chunk_varlen_bwd(const muir_dims_t* dims, const int32_t* cu_s
                                     void* dwrite, void* dgamma, float* dS0, void* workspace,
                                     size_t workspace_bytes, void* stream) {
   ChunkShape s;
-  muir_status_t st = check_dims(dims, &s);
+  muir_status_t st = check_dims(dims, &s, true);
   if (st != MUIR_OK) return st;
   const Inputs in{{q, k, v, log_a, erase, write, gamma}};
   const Grads gr{{dq, dk, dv, dlog_a, derase, dwrite, dgamma}};

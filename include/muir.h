@@ -24,8 +24,9 @@
  * Conventions shared by every call
  * --------------------------------
  *  - Every tensor pointer is a DEVICE pointer to dense, contiguous memory,
- *    aligned to 16 bytes.  Inputs, o/dO and the gradients of the inputs use
- *    the element type `dtype` (MUIR_F32 or MUIR_BF16); states and state
+ *    aligned to 16 bytes.  Inputs and o/dO use the element type `dtype`
+ *    (MUIR_F32 or MUIR_BF16); the gradients of the inputs use `grad_dtype`
+ *    (fp32 by default, bf16 on request for bf16 inputs); states and state
  *    gradients are fp32; the workspace's content is opaque.
  *  - Sequence tensors are [B, T, H, D] with D contiguous; states are
  *    [B, H, dk, dv] row-major (dv contiguous).
@@ -76,7 +77,7 @@ typedef enum { MUIR_F32 = 0, MUIR_BF16 = 1 } muir_dtype_t;
  * Form of the readout gate gamma (wolonglab summary, §Methodology and
  * tab:abl: dynamic, static or no readout gate).
  *   MUIR_GAMMA_TOKEN : per token, [B, T, H, dk] (decode: [N, H, dk]) dtype;
- *                      its gradient has the same shape and dtype
+ *                      its gradient has the same shape, in grad_dtype
  *   MUIR_GAMMA_STATIC: one per (head, key channel), [H, dk] dtype; its
  *                      gradient is [H, dk] fp32, summed over batch and tokens
  *   MUIR_GAMMA_NONE  : gamma = 1; the gamma and dgamma pointers are not used
@@ -84,13 +85,21 @@ typedef enum { MUIR_F32 = 0, MUIR_BF16 = 1 } muir_dtype_t;
  */
 typedef enum { MUIR_GAMMA_TOKEN = 0, MUIR_GAMMA_STATIC = 1, MUIR_GAMMA_NONE = 2 } muir_gamma_mode_t;
 
-/* Sizes of a chunkwise call. */
+/*
+ * Sizes of a chunkwise call.  `grad_dtype` is the element type of the
+ * per-token gradients that the backward writes (dq, dk, dv, dlog_a, derase,
+ * dwrite and a per-token dgamma): MUIR_F32 (0, so a zero-initialised struct
+ * asks for fp32 gradients) or, with dtype MUIR_BF16 only, MUIR_BF16 (each
+ * gradient accumulated in fp32 and rounded once on the store).  The forward
+ * calls ignore it.
+ */
 typedef struct {
   int32_t B, T, H;     /* batch, tokens, heads */
   int32_t dk, dv;      /* key / value head size */
   int32_t chunk;       /* tokens per triangular system */
   int32_t dtype;       /* muir_dtype_t of q, k, v, gates, o, dO */
   int32_t gamma_mode;  /* muir_gamma_mode_t */
+  int32_t grad_dtype;  /* muir_dtype_t of the per-token gradients (backward) */
 } muir_dims_t;
 
 /* Version of this interface (bumped on any signature change). */
@@ -166,12 +175,14 @@ size_t muir_chunk_bwd_workspace(const muir_dims_t* dims);
  *              recomputed when either is NULL.
  *   dO       : [B, T, H, dv] dtype upstream gradient of o
  *   dS_T     : [B, H, dk, dv] fp32 upstream gradient of S_T, or NULL for 0
- *   dq, dk, dlog_a, derase : [B, T, H, dk] dtype outputs
- *   dv, dwrite             : [B, T, H, dv] dtype outputs
- *              (accumulated in fp32 and rounded once on the store)
- *   dgamma   : by dims->gamma_mode: [B, T, H, dk] dtype; [H, dk] fp32 (the
- *              sum over batch and tokens, in a fixed order); unused (NULL
- *              allowed) for MUIR_GAMMA_NONE
+ *   dq, dk, dlog_a, derase : [B, T, H, dk] grad_dtype outputs
+ *   dv, dwrite             : [B, T, H, dv] grad_dtype outputs
+ *              (accumulated in fp32; in bf16 rounded once on the store)
+ *   dgamma   : by dims->gamma_mode: [B, T, H, dk] grad_dtype; [H, dk] fp32
+ *              (the sum over batch and tokens, in a fixed order); unused
+ *              (NULL allowed) for MUIR_GAMMA_NONE
+ *   A grad_dtype other than MUIR_F32 or, for bf16 inputs, MUIR_BF16 returns
+ *   MUIR_ERR_DTYPE.
  *   dS0      : [B, H, dk, dv] fp32 output, or NULL to skip
  *   workspace: device scratch of at least muir_chunk_bwd_workspace(dims)
  *              bytes; contents are clobbered.
@@ -220,7 +231,8 @@ muir_status_t muir_chunk_varlen_fwd(const muir_dims_t* dims, const int32_t* cu_s
 /*
  * Backward of muir_chunk_varlen_fwd: as muir_chunk_bwd, with the packed
  * layout and cu_seqlens of muir_chunk_varlen_fwd for every sequence tensor
- * (dO and the per-token gradients are [T_total, H, D]).  dS_T and dS0 are
+ * (dO is [T_total, H, D] dtype, the per-token gradients [T_total, H, D]
+ * grad_dtype).  dS_T and dS0 are
  * [B, H, dk, dv] per sequence; a static gate's gradient is [H, dk] fp32,
  * summed over every sequence's tokens.
  */

@@ -225,6 +225,35 @@ def step_inputs_torch(N: int, H: int, dk: int, dv: int, steps: int, *, device, d
     return out
 
 
+def stream_segment_torch(index: int, seg_len: int, H: int, dk: int, dv: int, *, device, dtype: str = "bf16",
+                         decay: str = "channel_slow", seed: int = 0) -> Dict[str, torch.Tensor]:
+    """Segment `index` (tokens index*seg_len .. +seg_len-1) of one long stream
+    (B = 1), drawn on `device`: [1, seg_len, H, D] tensors with the seq_inputs
+    distributions.  The per-(head, channel) decay rates belong to the stream
+    (drawn once, on the host, from `seed` with the 'channel' or
+    'channel_slow' recipe); the other tensors are drawn per segment with a
+    torch generator seeded from (seed, index), so any segment can be
+    regenerated on its own.  Values differ from the numpy streams."""
+    rates = step_rates(H, dk, seed=seed, mode=decay)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 1_000_003 + 7 + index)
+    dt = _DT[dtype]
+
+    def unit(x):
+        s = torch.nn.functional.silu(x)
+        return s / s.norm(dim=-1, keepdim=True).clamp_min(1e-12)
+
+    shp_k, shp_v = (1, seg_len, H, dk), (1, seg_len, H, dv)
+    out = {"q": unit(torch.randn(shp_k, generator=g, device=device)).to(dt),
+           "k": unit(torch.randn(shp_k, generator=g, device=device)).to(dt),
+           "v": torch.randn(shp_v, generator=g, device=device).to(dt)}
+    out["log_a"] = torch.from_numpy(-rates).to(device)[None, None].expand(shp_k).to(dt).contiguous()
+    out["erase"] = torch.sigmoid(torch.randn(shp_k, generator=g, device=device)).to(dt)
+    out["write"] = torch.sigmoid(torch.randn(shp_v, generator=g, device=device)).to(dt)
+    out["gamma"] = (2 * torch.sigmoid(torch.randn(shp_k, generator=g, device=device))).to(dt)
+    return out
+
+
 @dataclass(frozen=True)
 class Workload:
     """One workload: a name, its sizes and its input recipe."""
@@ -247,6 +276,10 @@ WORKLOADS = {
     "layer_fwdbwd_4k": Workload("layer_fwdbwd_4k", 8, 4096, 16, 128, 128, 64, "bf16", "channel", backward=True),
     "long_32k_c128": Workload("long_32k_c128", 1, 32768, 16, 128, 128, 128, "bf16", "channel_slow", backward=True),
     "long_32k_c256": Workload("long_32k_c256", 1, 32768, 16, 128, 128, 256, "bf16", "channel_slow", backward=True),
+    # one 1M-token stream: chunked prefill in 32K-token segments chained through
+    # the state, then decode tokens (stream_segment_torch draws the segments)
+    "stream_1m": Workload("stream_1m", 1, 1 << 20, 16, 128, 128, 64, "bf16", "channel_slow",
+                          extra={"segment": 32768, "decode_steps": 64, "seed": 31}),
     "decode_64x16": Workload("decode_64x16", 64, 4096, 16, 128, 128, 1, "bf16", "channel",
                              extra={"steps": 4096}),
 }

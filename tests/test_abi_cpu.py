@@ -50,11 +50,11 @@ def test_status_strings_cover_every_code():
         seen.add(s)
     assert len(seen) == 8
     assert L.muir_status_string(99).decode() == "unknown status"
-    assert L.muir_abi_version() == 7
+    assert L.muir_abi_version() == 8
 
 
-def _dims(m, B=1, T=128, H=2, dk=64, dv=64, chunk=64, dtype=1, gamma_mode=0):
-    return m._Dims(B, T, H, dk, dv, chunk, dtype, gamma_mode)
+def _dims(m, B=1, T=128, H=2, dk=64, dv=64, chunk=64, dtype=1, gamma_mode=0, grad_dtype=0):
+    return m._Dims(B, T, H, dk, dv, chunk, dtype, gamma_mode, grad_dtype)
 
 
 FAKE = [ctypes.c_void_p(0x10000 + 0x1000 * i) for i in range(16)]  # aligned, never dereferenced
@@ -127,6 +127,30 @@ def test_bwd_rejects_bad_arguments():
     assert call(_dims(m, gamma_mode=1), grads=g) == ERR_NULL
     dn = _dims(m, gamma_mode=2)
     assert call(dn, grads=g, ws_bytes=L.muir_chunk_bwd_workspace(ctypes.byref(dn)) - 1) == ERR_WORKSPACE
+
+
+def test_gradient_dtype_is_checked_and_sized():
+    """Per-token gradients are fp32 (grad_dtype 0, the zero-initialised
+    default) or, for bf16 inputs only, bf16; anything else is a dtype error.
+    A staged (partial-chunk) backward sizes its gradient copies by that type."""
+    m, L = _lib()
+    for kw in (dict(dtype=0, grad_dtype=1), dict(grad_dtype=2), dict(grad_dtype=-1)):
+        assert L.muir_chunk_bwd_workspace(ctypes.byref(_dims(m, **kw))) == 0, kw
+        assert L.muir_chunk_varlen_bwd_workspace(ctypes.byref(_dims(m, **kw))) == 0, kw
+        dd = _dims(m, **kw)
+        assert L.muir_chunk_bwd(ctypes.byref(dd), *FAKE[:7], None, None, None, FAKE[8], None, *FAKE[:7],
+                                None, FAKE[12], ctypes.c_size_t(1 << 40), None) == ERR_DTYPE
+    assert m._Dims().grad_dtype == 0
+    for T in (128, 100):
+        f32 = L.muir_chunk_bwd_workspace(ctypes.byref(_dims(m, T=T, grad_dtype=0)))
+        b16 = L.muir_chunk_bwd_workspace(ctypes.byref(_dims(m, T=T, grad_dtype=1)))
+        assert f32 > 0 and b16 > 0
+        # whole chunks: no staging, same workspace; a tail stages the gradients
+        assert (f32 == b16) if T == 128 else (f32 > b16)
+    # the forward ignores it (fp32 inputs with a bf16 gradient code are fine there)
+    assert L.muir_chunk_fwd_workspace(ctypes.byref(_dims(m, dtype=0, grad_dtype=1))) > 0
+    assert (L.muir_chunk_fwd_workspace(ctypes.byref(_dims(m, T=100, grad_dtype=0))) ==
+            L.muir_chunk_fwd_workspace(ctypes.byref(_dims(m, T=100, grad_dtype=1))))
 
 
 def test_step_rejects_bad_arguments():

@@ -75,3 +75,53 @@ def test_more_than_one_gpu_is_refused():
                        timeout=300)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_algorithmic_bytes_per_token_head():
+    """The byte model counts only the operator's own inputs and outputs.  At
+    d = 128, C = 64: forward 7 inputs + o + a saved state per chunk; backward
+    7 inputs + dO + the saved state + 7 gradients.  With fp32 states and
+    gradients that is 3,072 + 6,656 = 9,728 B; as written here (bf16 saved
+    states, fp32 gradients) 2,560 + 6,144 = 8,704 B; with bf16 gradients
+    6,912 B.  The chunk-gradient kernel alone moves the whole backward's."""
+    f, b = bench.step_bytes(128, 64, e=2, es=4, eg=4)
+    assert (f, b) == (3072, 6656)
+    f, b = bench.step_bytes(128, 64)
+    assert (f, b) == (2560, 6144)
+    assert sum(bench.step_bytes(128, 64, eg=2)) == 6912
+    kb = bench.kernel_bytes(128, 64)
+    assert kb["bwd_chunk"] == b
+    assert kb["fwd_prep"] + kb["fwd_scan"] == f
+    # larger chunks save fewer states
+    assert sum(bench.step_bytes(128, 256)) < sum(bench.step_bytes(128, 128)) < sum(bench.step_bytes(128, 64))
+
+
+def test_roofline_report_arithmetic():
+    kern = {"fwd_prep": 0.5, "fwd_scan": 0.25, "bwd_scan": 0.2, "bwd_chunk": 1.0}  # ms
+    nth = 8 * 4096 * 16
+    kernels, roof, sm = bench.roofline_report(kern, 2.0, 128, 64, nth, "no_such_workload", eg=4)
+    assert roof["kernel"] == "bwd_chunk" and roof["traffic"] is None
+    assert abs(roof["achieved"] - 6144 * nth / 1e-3 / 1e9) < 1e-6
+    assert abs(roof["frac"] - roof["achieved"] / 8000.0) < 1e-12
+    assert abs(sm["alg_bytes"] - 8704 * nth) < 1e-3
+    assert abs(sm["frac"] - sm["hbm_floor_us"] / 2000.0) < 1e-12  # HBM-bound: bytes floor over step time
+
+
+def test_per_head_error_catches_a_small_head():
+    """The per-(batch, head) error sees an error that the whole-tensor ratio
+    hides behind another head's larger scale."""
+    import numpy as np
+    sys.path.insert(0, HERE)
+    from gpu_util import err2, rel_err, rel_err_heads
+    y = np.ones((1, 8, 2, 4))
+    y[:, :, 1] *= 1e-3            # head 1 is 1000x smaller
+    x = y.copy()
+    x[0, 3, 1, 2] += 1e-4         # a 10% error inside head 1
+    assert rel_err(x, y) < 2e-4
+    assert abs(rel_err_heads(x, y, (0, 2)) - 0.1) < 1e-9
+    assert err2(x, y, (0, 2)) == rel_err_heads(x, y, (0, 2))
+    # an all-zero head contributes its absolute error
+    y[:, :, 1] = 0
+    x = y.copy()
+    x[0, 0, 1, 0] = 3e-3
+    assert abs(rel_err_heads(x, y, (0, 2)) - 3e-3) < 1e-12

@@ -11,7 +11,7 @@ import torch
 
 import muir_inputs
 import oracle
-from gpu_util import NAMES, TOL, oracle_fwd, rel_err, to_dev
+from gpu_util import NAMES, SEQ_AXES, STATE_AXES, STEP_AXES, TOL, err2, oracle_fwd, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -41,8 +41,8 @@ def test_step_matches_oracle(dtype, dk):
         o = m.muir_step(*(d[n] for n in NAMES), S_gpu)
         o_ref, S_ref = oracle.step(*(inp[n] for n in NAMES), S_ref)
         torch.cuda.synchronize()
-        assert rel_err(o, o_ref) <= TOL[dtype], (s, rel_err(o, o_ref))
-    assert rel_err(S_gpu, S_ref) <= TOL[dtype]
+        assert err2(o, o_ref, STEP_AXES) <= TOL[dtype], (s, err2(o, o_ref, STEP_AXES))
+    assert err2(S_gpu, S_ref, STATE_AXES) <= TOL[dtype]
 
 
 CASES = [
@@ -58,6 +58,13 @@ CASES = [
     ("bf16_d128_c128_steep", 1, 256, 2, 128, 128, "bf16", "steep", 0.0),
     ("f32_d128_c64_spiky", 1, 128, 2, 128, 64, "f32", "spiky", 0.1),
     ("bf16_d128_c256_spiky", 1, 512, 2, 128, 256, "bf16", "spiky", 0.1),
+    # every (dtype, d, chunk) kernel instance over several chunks
+    ("f32_d128_c128", 1, 384, 2, 128, 128, "f32", "channel_slow", 0.1),
+    ("f32_d64_c128", 1, 384, 2, 64, 128, "f32", "uniform", 0.1),
+    ("f32_d128_c256", 1, 768, 1, 128, 256, "f32", "channel_slow", 0.1),
+    ("f32_d64_c256", 1, 768, 2, 64, 256, "f32", "channel", 0.1),
+    ("bf16_d64_c128", 2, 384, 2, 64, 128, "bf16", "channel", 0.1),
+    ("bf16_d64_c256", 1, 768, 3, 64, 256, "bf16", "channel_slow", 0.1),
 ]
 
 
@@ -71,7 +78,7 @@ def test_chunk_fwd_matches_oracle(case):
     o, S_T, S_chunks = m.muir_chunk_fwd(*(dv[n] for n in NAMES), dv["S0"], chunk=C, save_states=True)
     torch.cuda.synchronize()
     o_ref, S_ref = oracle_fwd(inp)
-    eo, es = rel_err(o, o_ref), rel_err(S_T, S_ref)
+    eo, es = err2(o, o_ref, SEQ_AXES), err2(S_T, S_ref, STATE_AXES)
     _say(f"  err o={eo:.3e} S_T={es:.3e}")
     assert eo <= TOL[dtype]
     assert es <= TOL[dtype]
