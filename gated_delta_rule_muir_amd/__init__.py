@@ -19,7 +19,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["muir_chunk_fwd", "muir_chunk_bwd", "muir_step", "muir_chunk_fwd_workspace",
+__all__ = ["muir_chunk_fwd", "muir_chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "muir_chunk_bwd", "muir_step",
+           "muir_chunk_fwd_workspace",
            "muir_chunk_bwd_workspace", "muir_chunk_varlen_fwd", "muir_chunk_varlen_bwd",
            "muir_chunk_varlen_fwd_workspace", "muir_chunk_varlen_bwd_workspace",
            "muir_gate_proj_fwd", "muir_gate_proj_bwd", "muir_gate_proj_bwd_workspace",
@@ -34,7 +35,10 @@ _LIB_PATH = os.path.join(_PKG, "libmuir.so")
 MUIR_F32, MUIR_BF16 = 0, 1
 MUIR_GAMMA_TOKEN, MUIR_GAMMA_STATIC, MUIR_GAMMA_NONE = 0, 1, 2
 STATUS = {0: "MUIR_OK", 1: "MUIR_ERR_NULL", 2: "MUIR_ERR_SHAPE", 3: "MUIR_ERR_DTYPE",
-          4: "MUIR_ERR_WORKSPACE", 5: "MUIR_ERR_ALIGN", 6: "MUIR_ERR_HIP", 7: "MUIR_ERR_MODE"}
+          4: "MUIR_ERR_WORKSPACE", 5: "MUIR_ERR_ALIGN", 6: "MUIR_ERR_HIP", 7: "MUIR_ERR_MODE",
+          8: "MUIR_ERR_SCRATCH"}
+# size of the fixed scratch array of muir_chunk_fwd_noalloc (MUIR_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class MuirError(RuntimeError):
@@ -80,6 +84,8 @@ def lib():
         L.muir_chunk_bwd_workspace.restype = SZ
         L.muir_chunk_fwd.argtypes = [D] + [P] * 7 + [P, P, P, P] + [P, SZ, P]
         L.muir_chunk_fwd.restype = ctypes.c_int
+        L.muir_chunk_fwd_noalloc.argtypes = [D] + [P] * 7 + [P, P, P, P] + [P]
+        L.muir_chunk_fwd_noalloc.restype = ctypes.c_int
         L.muir_chunk_bwd.argtypes = [D] + [P] * 7 + [P, P, P, P, P] + [P] * 8 + [P, SZ, P]
         L.muir_chunk_bwd.restype = ctypes.c_int
         L.muir_chunk_varlen_fwd_workspace.argtypes = [D]
@@ -228,6 +234,45 @@ def muir_chunk_fwd(q, k, v, log_a, erase, write, gamma, S0=None, *, chunk: int =
                               _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
     if rc != 0:
         raise MuirError(rc, "muir_chunk_fwd")
+    return o, S_T, S_chunks
+
+
+def muir_chunk_fwd_noalloc(q, k, v, log_a, erase, write, gamma, S0=None, *, chunk: int = 64,
+                           save_states: bool = False, final_state: bool = True, out=None, S_T_out=None,
+                           S_chunks_out=None):
+    """muir_chunk_fwd without a workspace: the library takes it from its fixed
+    per-GPU scratch array (NOALLOC_SCRATCH_BYTES), so the C call allocates
+    nothing; calls that need more raise MuirError (MUIR_ERR_SCRATCH).  Calls
+    that overlap in time on one GPU race on that array.  Outputs may be passed
+    in (out, S_T_out, S_chunks_out); those not passed are allocated here,
+    before the call.  Returns (o, S_T or None, S_chunks or None)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for n, t in (("q", q), ("k", k), ("log_a", log_a), ("erase", erase)):
+        _check_io(n, t, (B, T, H, dk), dt, dev)
+    gm = _gamma_mode(gamma, (B, T), H, dk, dt, dev)
+    for n, t in (("v", v), ("write", write)):
+        _check_io(n, t, (B, T, H, dv), dt, dev)
+    if S0 is not None:
+        _check_io("S0", S0, (B, H, dk, dv), torch.float32, dev)
+    o = out if out is not None else torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _check_io("out", o, (B, T, H, dv), dt, dev)
+    S_T = None
+    if final_state:
+        S_T = S_T_out if S_T_out is not None else torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        _check_io("S_T_out", S_T, (B, H, dk, dv), torch.float32, dev)
+    S_chunks = None
+    if save_states:
+        shp = (B, H, _nchunks(T, chunk), dk, dv)
+        S_chunks = S_chunks_out if S_chunks_out is not None else torch.empty(shp, dtype=dt, device=dev)
+        _check_io("S_chunks_out", S_chunks, shp, dt, dev)
+    d = _dims(B, T, H, dk, dv, chunk, code, gm)
+    rc = lib().muir_chunk_fwd_noalloc(ctypes.byref(d), *(_ptr(t) for t in (q, k, v, log_a, erase, write, gamma)),
+                                      _ptr(S0), _ptr(o), _ptr(S_T), _ptr(S_chunks), _stream(dev))
+    if rc != 0:
+        raise MuirError(rc, "muir_chunk_fwd_noalloc")
     return o, S_T, S_chunks
 
 

@@ -3,9 +3,17 @@
 // anything and never allocates, frees or synchronises.
 #include <muir.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 using muir::ChunkShape;
+
+// Workspace of the no-allocation forward (muir_chunk_fwd_noalloc): one array
+// per GPU, in the library's code object.  Host code never uses this name as
+// an address (on the host it is only a stand-in); it takes the device
+// address from hipGetSymbolAddress, once per device (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[MUIR_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -195,8 +203,8 @@ muir_status_t bwd_core(const ChunkShape& s, const Inputs& in, const float* S0, c
   char* ws = static_cast<char*>(workspace);
   float* S_rec = reinterpret_cast<float*>(ws + s.nchunks() * s.summary_bytes());
   float* dS_chunks = S_rec + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
-  float* scratch = dS_chunks + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
-  float* split = reinterpret_cast<float*>(reinterpret_cast<char*>(scratch) + s.nchunks() * bwd_scratch_bytes(s));
+  float* chunk_scratch = dS_chunks + s.nchunks() * static_cast<size_t>(s.DK) * s.DV;
+  float* split = reinterpret_cast<float*>(reinterpret_cast<char*>(chunk_scratch) + s.nchunks() * bwd_scratch_bytes(s));
   float* gpart = reinterpret_cast<float*>(reinterpret_cast<char*>(split) + s.scan_split_bytes());
   const void* Sc = S_chunks;
   const void* summ = summaries;
@@ -228,7 +236,7 @@ muir_status_t bwd_core(const ChunkShape& s, const Inputs& in, const float* S0, c
   mark(hs);
   if (muir::launch_bwd_chunk(s, in.x[0], in.x[1], in.x[2], in.x[3], in.x[4], in.x[5], in.x[6], summ, Sc,
                              dS_chunks, dO, gr.x[0], gr.x[1], gr.x[2], gr.x[3], gr.x[4], gr.x[5], gr.x[6],
-                             scratch, gpart, hs) != hipSuccess)
+                             chunk_scratch, gpart, hs) != hipSuccess)
     return MUIR_ERR_HIP;
   if (s.gmode == MUIR_GAMMA_STATIC &&
       muir::launch_gamma_sum(s, gpart, static_cast<float*>(gr.x[6]), hs) != hipSuccess)
@@ -263,8 +271,9 @@ muir_status_t stage_inputs(const ChunkShape& p, int Tsrc, const int32_t* cu, con
   return MUIR_OK;
 }
 
-muir_status_t check_fwd_args(const ChunkShape& s, const Inputs& in, const float* S0, const void* o, const float* S_T,
-                             const void* S_chunks, const void* workspace, size_t workspace_bytes, size_t need) {
+// The tensors of a forward call (the workspace is checked by check_workspace).
+muir_status_t check_fwd_tensors(const ChunkShape& s, const Inputs& in, const float* S0, const void* o,
+                                const float* S_T, const void* S_chunks) {
   muir_status_t st;
   if (s.nchunks() != 0) {
     for (int i = 0; i < 6; ++i)
@@ -274,13 +283,24 @@ muir_status_t check_fwd_args(const ChunkShape& s, const Inputs& in, const float*
       if (!aligned16(in.x[i])) return MUIR_ERR_ALIGN;
     if (!aligned16(o)) return MUIR_ERR_ALIGN;
     if ((st = check_gate(s, in.x[6])) != MUIR_OK) return st;
-    if (!workspace || workspace_bytes < need) return MUIR_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return MUIR_ERR_ALIGN;
   }
   const void* opt[] = {S0, S_T, S_chunks};
   for (const void* p : opt)
     if (p && !aligned16(p)) return MUIR_ERR_ALIGN;
   return MUIR_OK;
+}
+
+// A caller's workspace, needed whenever there are chunks to run.
+muir_status_t check_workspace(const ChunkShape& s, const void* workspace, size_t workspace_bytes, size_t need) {
+  if (s.nchunks() == 0) return MUIR_OK;
+  if (!workspace || workspace_bytes < need) return MUIR_ERR_WORKSPACE;
+  return aligned16(workspace) ? MUIR_OK : MUIR_ERR_ALIGN;
+}
+
+muir_status_t check_fwd_args(const ChunkShape& s, const Inputs& in, const float* S0, const void* o, const float* S_T,
+                             const void* S_chunks, const void* workspace, size_t workspace_bytes, size_t need) {
+  const muir_status_t st = check_fwd_tensors(s, in, S0, o, S_T, S_chunks);
+  return st != MUIR_OK ? st : check_workspace(s, workspace, workspace_bytes, need);
 }
 
 muir_status_t check_bwd_args(const ChunkShape& s, const Inputs& in, const float* S0, const void* S_chunks,
@@ -405,6 +425,25 @@ muir_status_t qk_norm_call(int64_t rows, int32_t D, int32_t dtype, const void* u
   return MUIR_OK;
 }
 
+// Device address of the no-allocation scratch array on the current device,
+// looked up once per device (each GPU holds its own copy of the array at its
+// own address) and kept; NULL if the lookup fails.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+void* noalloc_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 size_t varlen_fwd_need(const ChunkShape& s) { return fwd_ws(padded(s)) + fwd_stage_bytes(padded(s)); }
 size_t varlen_bwd_need(const ChunkShape& s) { return bwd_ws(padded(s)) + bwd_stage_bytes(padded(s)); }
 
@@ -434,6 +473,7 @@ const char* muir_status_string(muir_status_t st) {
     case MUIR_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case MUIR_ERR_HIP: return "a HIP kernel launch failed";
     case MUIR_ERR_MODE: return "unknown readout-gate mode";
+    case MUIR_ERR_SCRATCH: return "the call needs more than the no-allocation scratch (MUIR_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -442,6 +482,24 @@ size_t muir_chunk_fwd_workspace(const muir_dims_t* dims) {
   ChunkShape s;
   if (check_dims(dims, &s) != MUIR_OK) return 0;
   return fwd_need(s);
+}
+
+muir_status_t muir_chunk_fwd_noalloc(const muir_dims_t* dims, const void* q, const void* k, const void* v,
+                                     const void* log_a, const void* erase, const void* write, const void* gamma,
+                                     const float* S0, void* o, float* S_T, void* S_chunks, void* stream) {
+  ChunkShape s;
+  muir_status_t st = check_dims(dims, &s);
+  if (st != MUIR_OK) return st;
+  const size_t need = fwd_need(s);
+  if (need > MUIR_NOALLOC_SCRATCH_BYTES) return MUIR_ERR_SCRATCH;
+  const Inputs in{{q, k, v, log_a, erase, write, gamma}};
+  if ((st = check_fwd_tensors(s, in, S0, o, S_T, S_chunks)) != MUIR_OK) return st;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (s.nchunks() == 0) return fwd_empty(s, S0, S_T, hs);
+  void* ws = noalloc_scratch();
+  if (!ws) return MUIR_ERR_HIP;
+  if (s.T % s.C == 0) return fwd_core(s, in, S0, o, S_T, S_chunks, ws, hs);
+  return fwd_staged(s, nullptr, in, S0, o, S_T, S_chunks, ws, hs);
 }
 
 size_t muir_chunk_bwd_workspace(const muir_dims_t* dims) {

@@ -68,7 +68,8 @@ typedef enum {
   MUIR_ERR_WORKSPACE = 4, /* workspace pointer NULL or smaller than required */
   MUIR_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned */
   MUIR_ERR_HIP = 6,       /* a kernel launch failed */
-  MUIR_ERR_MODE = 7       /* unknown readout-gate mode */
+  MUIR_ERR_MODE = 7,      /* unknown readout-gate mode */
+  MUIR_ERR_SCRATCH = 8    /* more work than the fixed scratch of a no-allocation call holds */
 } muir_status_t;
 
 typedef enum { MUIR_F32 = 0, MUIR_BF16 = 1 } muir_dtype_t;
@@ -153,6 +154,34 @@ muir_status_t muir_chunk_fwd(const muir_dims_t* dims,
                              const void* write, const void* gamma,
                              const float* S0, void* o, float* S_T, void* S_chunks,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * No-allocation forward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  It is muir_chunk_fwd (same arguments, results and errors)
+ * with its workspace taken from a fixed scratch array of
+ * MUIR_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on,
+ * from the first such call on that GPU until the process ends; the call
+ * itself allocates and frees nothing.  The caller still passes every input
+ * and output.
+ *   - A call for which muir_chunk_fwd_workspace(dims) exceeds
+ *     MUIR_NOALLOC_SCRATCH_BYTES returns MUIR_ERR_SCRATCH and launches
+ *     nothing.  At dk = dv = 128, bf16, chunk 64 a call needs about 2.4 to
+ *     3.2 KB per token and head (more when few heads split the state scan
+ *     into segments): one 2,048-token sequence of 16 heads takes 98 MiB.
+ *   - Every call on one GPU uses that GPU's one array.  Calls that overlap in
+ *     time on the same GPU (other streams or host threads) race on it; the
+ *     caller serialises them.  Successive calls on one stream are ordered.
+ *   - What the array holds after a call is not part of the interface: it
+ *     cannot be passed to muir_chunk_bwd as `summaries`.
+ */
+#define MUIR_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+muir_status_t muir_chunk_fwd_noalloc(const muir_dims_t* dims,
+                                     const void* q, const void* k, const void* v,
+                                     const void* log_a, const void* erase,
+                                     const void* write, const void* gamma,
+                                     const float* S0, void* o, float* S_T, void* S_chunks,
+                                     void* stream);
 
 /* Bytes of workspace muir_chunk_bwd needs for `dims` (0 if dims are invalid). */
 size_t muir_chunk_bwd_workspace(const muir_dims_t* dims);

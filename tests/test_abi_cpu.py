@@ -10,7 +10,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "muir.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP, ERR_MODE = range(8)
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP, ERR_MODE, ERR_SCRATCH = range(9)
 
 
 def _lib():
@@ -44,11 +44,11 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_cover_every_code():
     _, L = _lib()
     seen = set()
-    for code in range(8):
+    for code in range(9):
         s = L.muir_status_string(code).decode()
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 8
+    assert len(seen) == 9
     assert L.muir_status_string(99).decode() == "unknown status"
     assert L.muir_abi_version() == 8
 
@@ -151,6 +151,33 @@ def test_gradient_dtype_is_checked_and_sized():
     assert L.muir_chunk_fwd_workspace(ctypes.byref(_dims(m, dtype=0, grad_dtype=1))) > 0
     assert (L.muir_chunk_fwd_workspace(ctypes.byref(_dims(m, T=100, grad_dtype=0))) ==
             L.muir_chunk_fwd_workspace(ctypes.byref(_dims(m, T=100, grad_dtype=1))))
+
+
+def test_noalloc_fwd_checks_before_touching_the_gpu():
+    """The no-allocation forward rejects work beyond its fixed scratch
+    (MUIR_NOALLOC_SCRATCH_BYTES) and bad arguments before any HIP call."""
+    m, L = _lib()
+    text = open(HEADER).read()
+    assert re.search(r"#define MUIR_NOALLOC_SCRATCH_BYTES \(\(size_t\)128 << 20\)", text)
+    assert m.NOALLOC_SCRATCH_BYTES == 128 << 20
+
+    def call(dd, ptrs=None):
+        p = list(FAKE[:7]) if ptrs is None else ptrs
+        return L.muir_chunk_fwd_noalloc(ctypes.byref(dd) if dd is not None else None, *p, None, FAKE[7], None,
+                                        None, None)
+    big = _dims(m, B=1, T=65536, H=16, dk=128, dv=128)
+    assert L.muir_chunk_fwd_workspace(ctypes.byref(big)) > m.NOALLOC_SCRATCH_BYTES
+    assert call(big) == ERR_SCRATCH
+    fits = _dims(m, B=1, T=2048, H=16, dk=128, dv=128)
+    assert 0 < L.muir_chunk_fwd_workspace(ctypes.byref(fits)) <= m.NOALLOC_SCRATCH_BYTES
+    assert call(None) == ERR_NULL
+    assert call(_dims(m, dtype=4)) == ERR_DTYPE
+    assert call(_dims(m, chunk=32)) == ERR_SHAPE
+    p = list(FAKE[:7])
+    p[1] = None
+    assert call(fits, ptrs=p) == ERR_NULL
+    p[1] = ctypes.c_void_p(0x10008)
+    assert call(fits, ptrs=p) == ERR_ALIGN
 
 
 def test_step_rejects_bad_arguments():
