@@ -19,7 +19,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["muir_chunk_fwd", "muir_chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "muir_chunk_bwd", "muir_step",
+__all__ = ["muir_check_inputs", "muir_chunk_fwd", "muir_chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "muir_chunk_bwd", "muir_step",
            "muir_chunk_fwd_workspace",
            "muir_chunk_bwd_workspace", "muir_chunk_varlen_fwd", "muir_chunk_varlen_bwd",
            "muir_chunk_varlen_fwd_workspace", "muir_chunk_varlen_bwd_workspace",
@@ -36,7 +36,7 @@ MUIR_F32, MUIR_BF16 = 0, 1
 MUIR_GAMMA_TOKEN, MUIR_GAMMA_STATIC, MUIR_GAMMA_NONE = 0, 1, 2
 STATUS = {0: "MUIR_OK", 1: "MUIR_ERR_NULL", 2: "MUIR_ERR_SHAPE", 3: "MUIR_ERR_DTYPE",
           4: "MUIR_ERR_WORKSPACE", 5: "MUIR_ERR_ALIGN", 6: "MUIR_ERR_HIP", 7: "MUIR_ERR_MODE",
-          8: "MUIR_ERR_SCRATCH"}
+          8: "MUIR_ERR_SCRATCH", 9: "MUIR_ERR_NONFINITE"}
 # size of the fixed scratch array of muir_chunk_fwd_noalloc (MUIR_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 128 << 20
 
@@ -107,6 +107,8 @@ def lib():
         L.muir_qk_norm_fwd.restype = ctypes.c_int
         L.muir_qk_norm_bwd.argtypes = [ctypes.c_int64, I32, I32, P, P, P, P]
         L.muir_qk_norm_bwd.restype = ctypes.c_int
+        L.muir_check_values.argtypes = [ctypes.c_int64, I32, P, I32, P, P]
+        L.muir_check_values.restype = ctypes.c_int
         L.muir_step.argtypes = [I32] * 6 + [P] * 7 + [P, P, P]
         L.muir_step.restype = ctypes.c_int
         L.muir_set_profile_events.argtypes = [P, I32]
@@ -178,6 +180,35 @@ def _gamma_mode(gamma, lead, H, dk, dt, dev) -> int:
     return MUIR_GAMMA_TOKEN
 
 
+def muir_check_inputs(tensors, *, log_decay=("log_a",), raise_on_error: bool = True):
+    """Debug check of input tensors against the operator's preconditions:
+    every value finite, and the log-decay tensors (names in `log_decay`) at
+    most 0.  `tensors` maps names to GPU tensors (None entries are skipped).
+    Counts on the device with muir_check_values, then reads the counts back
+    (this synchronises with the current stream).  Returns {name: (non-finite
+    count, positive log-decay count)}; with raise_on_error, raises MuirError
+    (MUIR_ERR_NONFINITE) naming the tensors at fault."""
+    items = [(n, t) for n, t in tensors.items() if t is not None]
+    if not items:
+        return {}
+    dev = items[0][1].device
+    counts = torch.zeros((len(items), 2), dtype=torch.int32, device=dev)
+    for i, (n, t) in enumerate(items):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n}: must be a contiguous GPU tensor")
+        rc = lib().muir_check_values(t.numel(), _dtype_code(t), _ptr(t), 1 if n in log_decay else 0,
+                                     ctypes.c_void_p(counts.data_ptr() + 8 * i), _stream(t.device))
+        if rc != 0:
+            raise MuirError(rc, f"muir_check_values({n})")
+    c = counts.cpu().tolist()
+    out = {n: (int(c[i][0]), int(c[i][1])) for i, (n, _) in enumerate(items)}
+    bad = {n: v for n, v in out.items() if v[0] or v[1]}
+    if bad and raise_on_error:
+        detail = ", ".join(f"{n}: {a} non-finite, {b} log-decays above 0" for n, (a, b) in bad.items())
+        raise MuirError(9, f"input check ({detail})")
+    return out
+
+
 def muir_chunk_fwd_workspace(B, T, H, dk, dv, chunk, dtype=MUIR_BF16, gamma_mode=MUIR_GAMMA_TOKEN) -> int:
     d = _dims(B, T, H, dk, dv, chunk, dtype, gamma_mode)
     return int(lib().muir_chunk_fwd_workspace(ctypes.byref(d)))
@@ -201,10 +232,11 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
 
 def muir_chunk_fwd(q, k, v, log_a, erase, write, gamma, S0=None, *, chunk: int = 64,
                    save_states: bool = False, final_state: bool = True,
-                   workspace: Optional[torch.Tensor] = None, out=None
+                   workspace: Optional[torch.Tensor] = None, out=None, check_inputs: bool = False
                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]:
     """Chunkwise forward.  Inputs [B, T, H, D] (bf16 or fp32, on one GPU);
     gamma [B, T, H, dk], or [H, dk] (a static gate), or None (no gate).
+    check_inputs: first run muir_check_inputs on them (debugging; synchronises).
 
     Any T: a partial last chunk runs on zero-padded copies in the workspace.
     Returns (o [B,T,H,dv] in the input dtype, S_T [B,H,dk,dv] fp32 or None,
@@ -222,6 +254,8 @@ def muir_chunk_fwd(q, k, v, log_a, erase, write, gamma, S0=None, *, chunk: int =
         _check_io(n, t, (B, T, H, dv), dt, dev)
     if S0 is not None:
         _check_io("S0", S0, (B, H, dk, dv), torch.float32, dev)
+    if check_inputs:
+        muir_check_inputs(dict(q=q, k=k, v=v, log_a=log_a, erase=erase, write=write, gamma=gamma, S0=S0))
     o = out if out is not None else torch.empty((B, T, H, dv), dtype=dt, device=dev)
     S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if final_state else None
     S_chunks = (torch.empty((B, H, _nchunks(T, chunk), dk, dv), dtype=dt, device=dev)
@@ -279,8 +313,8 @@ def muir_chunk_fwd_noalloc(q, k, v, log_a, erase, write, gamma, S0=None, *, chun
 def muir_chunk_bwd(q, k, v, log_a, erase, write, gamma, dO, S0=None, S_chunks=None, dS_T=None, *,
                    chunk: int = 64, summaries: Optional[torch.Tensor] = None,
                    workspace: Optional[torch.Tensor] = None, want_dS0: bool = True,
-                   grad_dtype: Optional[torch.dtype] = None):
-    """Chunkwise backward.  Returns a dict of gradients (dq, dk, dv, dlog_a,
+                   grad_dtype: Optional[torch.dtype] = None, check_inputs: bool = False):
+    """Chunkwise backward (check_inputs: as muir_chunk_fwd's, over the inputs, dO, S0 and dS_T).  Returns a dict of gradients (dq, dk, dv, dlog_a,
     derase, dwrite in `grad_dtype`: fp32 by default, or bf16 for bf16 inputs,
     accumulated in fp32 and rounded once; dgamma in `grad_dtype` for a
     per-token gate, [H, dk] fp32 (summed over batch and tokens) for a static
@@ -313,6 +347,9 @@ def muir_chunk_bwd(q, k, v, log_a, erase, write, gamma, dO, S0=None, S_chunks=No
                 or summaries.numel() * summaries.element_size() < need):
             raise ValueError(f"summaries: expected the forward workspace ({need} bytes on {dev})")
     gcode = _grad_code(grad_dtype, dt)
+    if check_inputs:
+        muir_check_inputs(dict(q=q, k=k, v=v, log_a=log_a, erase=erase, write=write, gamma=gamma, dO=dO,
+                               S0=S0, dS_T=dS_T))
     gd = dict(dtype=torch.bfloat16 if gcode == MUIR_BF16 else torch.float32, device=dev)
     g = {n: torch.empty((B, T, H, dk), **gd) for n in ("dq", "dk", "dlog_a", "derase")}
     g.update({n: torch.empty((B, T, H, dv), **gd) for n in ("dv", "dwrite")})
@@ -440,10 +477,11 @@ def muir_chunk_varlen_bwd(q, k, v, log_a, erase, write, gamma, dO, cu_seqlens, S
     return g
 
 
-def muir_step(q, k, v, log_a, erase, write, gamma, S, *, out=None) -> torch.Tensor:
+def muir_step(q, k, v, log_a, erase, write, gamma, S, *, out=None, check_inputs: bool = False) -> torch.Tensor:
     """One decode step for [N, H, D] inputs (gamma [N, H, dk], or [H, dk] for a
     static gate, or None); S [N, H, dk, dv] fp32 is updated in place.
-    Returns o [N, H, dv] in the input dtype."""
+    Returns o [N, H, dv] in the input dtype.  check_inputs: as muir_chunk_fwd's
+    (the state included)."""
     N, H, dk = q.shape
     dv = v.shape[2]
     dev, dt = q.device, q.dtype
@@ -454,6 +492,8 @@ def muir_step(q, k, v, log_a, erase, write, gamma, S, *, out=None) -> torch.Tens
     for n, t in (("v", v), ("write", write)):
         _check_io(n, t, (N, H, dv), dt, dev)
     _check_io("S", S, (N, H, dk, dv), torch.float32, dev)
+    if check_inputs:
+        muir_check_inputs(dict(q=q, k=k, v=v, log_a=log_a, erase=erase, write=write, gamma=gamma, S=S))
     o = out if out is not None else torch.empty((N, H, dv), dtype=dt, device=dev)
     rc = lib().muir_step(N, H, dk, dv, code, gm, *(_ptr(t) for t in (q, k, v, log_a, erase, write, gamma)),
                          _ptr(S), _ptr(o), _stream(dev))

@@ -202,13 +202,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   float (*sRow)[DK] = reinterpret_cast<float (*)[DK]>(&sTA[0][0]);
 
   // identity operand: a 16x16 product with it moves a tile's rows onto lanes
-  // (identf: the same in fp32, for fp32 gradients of bf16 inputs)
   frag ident;
-  f32x4 identf;
   {
+    f32x4 idv;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) identf[i] = (4 * g + i == c16) ? 1.f : 0.f;
-    ident = M::from_f32(identf);
+    for (int i = 0; i < 4; ++i) idv[i] = (4 * g + i == c16) ? 1.f : 0.f;
+    ident = M::from_f32(idv);
   }
 
   // within-block prefix (through each token) and suffix (after it) of log_a,
@@ -287,16 +286,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   // 4g..4g+3
   auto turn = [&](f32x4 tile) -> f32x4 { return M::mma(M::from_f32(tile), ident, zero4()); };
   // a gradient tile in MFMA-output layout (tokens r0 + 4g+i, channel colv(n))
-  // to its [B, T, H, D] tensor, turned into token rows of four channels (one
-  // 8- or 16-byte store per lane): bf16 gradients by the bf16 identity product
-  // (which rounds to bf16 as the store would), fp32 gradients of bf16 inputs
-  // by an fp32 identity product (exact), fp32 gradients of fp32 inputs
-  // element by element
+  // to its [B, T, H, D] tensor: bf16 gradients turned into token rows of four
+  // channels by the bf16 identity product (which rounds to bf16 as the store
+  // would; one 8-byte store per lane), fp32 gradients element by element (4
+  // stores of 64-byte row pieces: measured 7% faster for the whole kernel than
+  // turning the tile with an fp32 identity product for 16-byte stores)
   auto store_grad = [&](Tg* base, int r0, int n, f32x4 tile) {
     if constexpr (sizeof(Tg) == 2) {
       store4(at(base, gi(r0 + c16, col0(n) + 4 * g)), turn(tile));
-    } else if constexpr (sizeof(TC) == 2) {
-      store4(at(base, gi(r0 + c16, col0(n) + 4 * g)), MM<float>::mma(tile, identf, zero4()));
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) *at(base, gi(r0 + 4 * g + i, colv(n))) = tile[i];
@@ -601,10 +598,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   constexpr int KWR = C / SEW;         // 16-byte words per Kbar^T row
   constexpr int KWT = DK * KWR / NTH;  // Kbar^T words per thread
   u32x4 dw[DIRECT ? DWT : 1], kw[DIRECT ? KWT : 1], gcw;
-  float hl[DIRECT ? NB - 1 : 1][NT][4], hk[DIRECT ? NB - 1 : 1][NT][4];
+  // direct form: log_a of every block and k of the earlier ones at (token
+  // 4g+i of block I, channel colv(n)): the Horner inputs, and the per-part
+  // decay sums (part p of the elementwise mapping is token group g = p here)
+  float hl[DIRECT ? NB : 1][NT][4], hk[DIRECT ? NB - 1 : 1][NT][4];
   if constexpr (DIRECT) {
     static_assert(DWT * NTH == C * DWR && KWT * NTH == DK * KWR && DK / 4 <= NTH && NB == 4,
                   "direct-form prologue layout");
+    static_assert(TPC == 4 && RPT == 4, "direct form: one elementwise part per token group of the output mapping");
     const char* cs = summ + static_cast<size_t>(chunk) * summ_bytes;
     const TC* gD = reinterpret_cast<const TC*>(cs + dl_offset);
     const TC* gKT = reinterpret_cast<const TC*>(cs) + summary_part(SP_KBT, C, DK, DV);
@@ -618,14 +619,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
           at(gKT, tpart_index((tid + k2 * NTH) / KWR, ((tid + k2 * NTH) % KWR) * SEW, DK)));  // 16-token tiles
     gcw = *reinterpret_cast<const u32x4*>(at(gGC, static_cast<uint32_t>(4 * min(tid, DK / 4 - 1))));
 #pragma unroll
-    for (int I = 0; I < NB - 1; ++I)
+    for (int I = 0; I < NB; ++I)
 #pragma unroll
       for (int n = 0; n < NT; ++n)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t o = gi(16 * I + 4 * g + i, colv(n));
           hl[I][n][i] = ldv(lb, o);
-          hk[I][n][i] = ldv(kb, o);
+          if (I < NB - 1) hk[I < NB - 1 ? I : 0][n][i] = ldv(kb, o);
         }
     load_state(S, S0c);
     // S0 rows of this wave's key channels as the right operands of the
@@ -643,12 +644,20 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   // ---- sums of the log-decay over each block and each part of it, and the
   // blocks whose decay leaves LEAF_SAFE_RANGE (steep leaves) ----
   if (tid == 0) sUnsafe = 0;
+  if constexpr (DIRECT) {
+    // from the log-decay already in registers at the output mapping
 #pragma unroll
-  for (int I = 0; I < NB; ++I) {
-    float sacc = 0.f;
+    for (int I = 0; I < NB; ++I)
 #pragma unroll
-    for (int rr = 0; rr < RPT; ++rr) sacc += ldv(lb, gi(16 * I + RPT * part + rr, ej));
-    sPart[I][part][ej] = sacc;
+      for (int n = 0; n < NT; ++n) sPart[I][g][colv(n)] = (hl[I][n][0] + hl[I][n][1]) + (hl[I][n][2] + hl[I][n][3]);
+  } else {
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+      float sacc = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < RPT; ++rr) sacc += ldv(lb, gi(16 * I + RPT * part + rr, ej));
+      sPart[I][part][ej] = sacc;
+    }
   }
   __syncthreads();
   if (part == 0) {

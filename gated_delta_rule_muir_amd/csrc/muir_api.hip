@@ -444,6 +444,34 @@ void* noalloc_scratch() {
   return g_scratch_ptr[dev];
 }
 
+// Counts the values of x[0..n) that break the inputs' preconditions: NaN or
+// infinite (exponent bits all set), and, for a log-decay, finite and above 0
+// (sign bit clear, not zero).  Per-lane counts, a wave sum, one atomic add per wave.
+template <typename T>
+__global__ __launch_bounds__(256) void check_values_kernel(int64_t n, const T* __restrict__ x, int log_decay,
+                                                           int32_t* __restrict__ counts) {
+  constexpr uint32_t kExp = sizeof(T) == 2 ? 0x7F80u : 0x7F800000u;
+  constexpr uint32_t kSign = sizeof(T) == 2 ? 0x8000u : 0x80000000u;
+  int bad = 0, pos = 0;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    uint32_t b;
+    if constexpr (sizeof(T) == 2) b = x[i];
+    else b = __float_as_uint(x[i]);
+    bad += (b & kExp) == kExp;
+    pos += log_decay && !(b & kSign) && b != 0u && (b & kExp) != kExp;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    bad += __shfl_xor(bad, off, 64);
+    pos += __shfl_xor(pos, off, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    if (bad) atomicAdd(&counts[0], bad);
+    if (pos) atomicAdd(&counts[1], pos);
+  }
+}
+
 size_t varlen_fwd_need(const ChunkShape& s) { return fwd_ws(padded(s)) + fwd_stage_bytes(padded(s)); }
 size_t varlen_bwd_need(const ChunkShape& s) { return bwd_ws(padded(s)) + bwd_stage_bytes(padded(s)); }
 
@@ -474,8 +502,29 @@ const char* muir_status_string(muir_status_t st) {
     case MUIR_ERR_HIP: return "a HIP kernel launch failed";
     case MUIR_ERR_MODE: return "unknown readout-gate mode";
     case MUIR_ERR_SCRATCH: return "the call needs more than the no-allocation scratch (MUIR_NOALLOC_SCRATCH_BYTES)";
+    case MUIR_ERR_NONFINITE: return "an input is NaN or infinite, or a log-decay is above 0";
   }
   return "unknown status";
+}
+
+muir_status_t muir_check_values(int64_t n, int32_t dtype, const void* x, int32_t log_decay, int32_t* counts,
+                                void* stream) {
+  if (dtype != MUIR_F32 && dtype != MUIR_BF16) return MUIR_ERR_DTYPE;
+  if (n < 0) return MUIR_ERR_SHAPE;
+  if (n == 0) return MUIR_OK;
+  if (!x || !counts) return MUIR_ERR_NULL;
+  const size_t es = dtype == MUIR_BF16 ? 2 : 4;
+  if ((reinterpret_cast<uintptr_t>(x) & (es - 1)) || (reinterpret_cast<uintptr_t>(counts) & 3)) return MUIR_ERR_ALIGN;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const int64_t want = (n + 255) / 256;
+  const unsigned blocks = static_cast<unsigned>(want < 4096 ? want : 4096);
+  if (dtype == MUIR_BF16)
+    hipLaunchKernelGGL(check_values_kernel<uint16_t>, dim3(blocks), dim3(256), 0, hs, n,
+                       static_cast<const uint16_t*>(x), log_decay ? 1 : 0, counts);
+  else
+    hipLaunchKernelGGL(check_values_kernel<float>, dim3(blocks), dim3(256), 0, hs, n, static_cast<const float*>(x),
+                       log_decay ? 1 : 0, counts);
+  return hipGetLastError() == hipSuccess ? MUIR_OK : MUIR_ERR_HIP;
 }
 
 size_t muir_chunk_fwd_workspace(const muir_dims_t* dims) {

@@ -69,7 +69,10 @@ typedef enum {
   MUIR_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned */
   MUIR_ERR_HIP = 6,       /* a kernel launch failed */
   MUIR_ERR_MODE = 7,      /* unknown readout-gate mode */
-  MUIR_ERR_SCRATCH = 8    /* more work than the fixed scratch of a no-allocation call holds */
+  MUIR_ERR_SCRATCH = 8,   /* more work than the fixed scratch of a no-allocation call holds */
+  MUIR_ERR_NONFINITE = 9  /* an input breaks its precondition: NaN or infinite values, or log_a > 0
+                             (reported by the checks built on muir_check_values, never by the
+                             compute calls, which do not read their inputs on the host) */
 } muir_status_t;
 
 typedef enum { MUIR_F32 = 0, MUIR_BF16 = 1 } muir_dtype_t;
@@ -122,6 +125,21 @@ int32_t muir_profile_events_recorded(void);
 
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* muir_status_string(muir_status_t status);
+
+/*
+ * Debug check of one input tensor against the operator's preconditions
+ * (every value finite; a log-decay at most 0, since a decay exp(log_a) above
+ * 1 would make the recurrence grow without bound).  Adds to counts[0] the
+ * number of NaN or infinite values among the n elements of x (dtype), and,
+ * when log_decay is nonzero, to counts[1] the number of finite values above 0.
+ * counts is an int32 [2] DEVICE array that the call only adds to, so one
+ * zeroed array can gather several tensors; read it back after the stream has
+ * run the call.  Asynchronous; x needs no particular alignment beyond its
+ * element size.  n == 0 launches nothing.  Meant for debugging: a caller
+ * that reads the counts back synchronises with the stream.
+ */
+muir_status_t muir_check_values(int64_t n, int32_t dtype, const void* x, int32_t log_decay,
+                                int32_t* counts, void* stream);
 
 /* Bytes of workspace muir_chunk_fwd needs for `dims` (0 if dims are invalid). */
 size_t muir_chunk_fwd_workspace(const muir_dims_t* dims);

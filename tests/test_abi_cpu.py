@@ -10,7 +10,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "muir.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP, ERR_MODE, ERR_SCRATCH = range(9)
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP, ERR_MODE, ERR_SCRATCH, ERR_NONFINITE = range(10)
 
 
 def _lib():
@@ -44,11 +44,11 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_cover_every_code():
     _, L = _lib()
     seen = set()
-    for code in range(9):
+    for code in range(10):
         s = L.muir_status_string(code).decode()
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 9
+    assert len(seen) == 10
     assert L.muir_status_string(99).decode() == "unknown status"
     assert L.muir_abi_version() == 8
 
@@ -178,6 +178,18 @@ def test_noalloc_fwd_checks_before_touching_the_gpu():
     assert call(fits, ptrs=p) == ERR_NULL
     p[1] = ctypes.c_void_p(0x10008)
     assert call(fits, ptrs=p) == ERR_ALIGN
+
+
+def test_check_values_rejects_bad_arguments():
+    m, L = _lib()
+    chk = L.muir_check_values
+    assert chk(10, 3, FAKE[0], 0, FAKE[1], None) == ERR_DTYPE
+    assert chk(-1, 1, FAKE[0], 0, FAKE[1], None) == ERR_SHAPE
+    assert chk(0, 1, None, 0, None, None) == OK  # nothing to check, nothing launched
+    assert chk(10, 1, None, 0, FAKE[1], None) == ERR_NULL
+    assert chk(10, 1, FAKE[0], 1, None, None) == ERR_NULL
+    assert chk(10, 0, ctypes.c_void_p(0x10002), 0, FAKE[1], None) == ERR_ALIGN  # fp32 needs 4-byte alignment
+    assert chk(10, 1, FAKE[0], 0, ctypes.c_void_p(0x10002), None) == ERR_ALIGN
 
 
 def test_step_rejects_bad_arguments():

@@ -105,3 +105,51 @@ def test_split_sequence_chains_state():
     for n in ("dq", "dk", "dv", "dlog_a", "derase", "dwrite", "dgamma"):
         assert rel_err(torch.cat([ga[n], gb[n]], 1), g[n]) <= 1e-5, n
     assert rel_err(ga["dS0"], g["dS0"]) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_input_check_counts_what_breaks_the_preconditions(dtype):
+    """muir_check_values counts NaN and infinite values (any input) and
+    log-decays above 0, exactly, over odd lengths and offset views; +0 and -0
+    are fine log-decays.  The compute calls' check_inputs option raises
+    MUIR_ERR_NONFINITE naming the tensor."""
+    import gated_delta_rule_muir_amd as m
+    m.lib()
+    gen = torch.Generator().manual_seed(3)
+    x = torch.randn(10007, generator=gen).to(dtype)
+    la = -torch.rand(10007, generator=gen).to(dtype)
+    x[[5, 700, 10006]] = float("nan")
+    x[[1, 9000]] = float("inf")
+    x[4444] = -float("inf")
+    la[[0, 17, 5000, 10005]] = torch.tensor([0.5, 1e-3, 7.0, 1e-30]).to(dtype)
+    la[[20, 21]] = torch.tensor([0.0, -0.0]).to(dtype)
+    la[30] = float("nan")
+    xd, lad = x.cuda(), la.cuda()
+    got = m.muir_check_inputs({"v": xd, "log_a": lad}, raise_on_error=False)
+    # 1e-30 is tiny but above 0, and counts; the NaN log-decay counts once, as non-finite
+    assert got["v"] == (6, 0), got
+    assert got["log_a"] == (1, 4), got
+    # a view that starts one element in, and an odd length
+    got = m.muir_check_inputs({"v": xd[1:9001], "log_a": lad[18:10005]}, raise_on_error=False)
+    assert got["v"] == (5, 0) and got["log_a"] == (1, 1), got
+    with pytest.raises(m.MuirError) as e:
+        m.muir_check_inputs({"v": xd})
+    assert e.value.code == 9 and "v:" in str(e.value)
+    clean = {"q": torch.randn(64, device="cuda").to(dtype), "log_a": -torch.rand(64, device="cuda").to(dtype)}
+    assert m.muir_check_inputs(clean) == {"q": (0, 0), "log_a": (0, 0)}
+
+    inp = to_dev(muir_inputs.seq_inputs(1, 64, 2, 64, 64, dtype="bf16" if dtype == torch.bfloat16 else "f32",
+                                        seed=2, with_dO=True))
+    args = [inp[n] for n in NAMES]
+    m.muir_chunk_fwd(*args, chunk=64, check_inputs=True)  # clean: no error
+    bad = dict(inp)
+    bad["log_a"] = inp["log_a"].clone()
+    bad["log_a"][0, 3, 1, 7] = 0.25
+    with pytest.raises(m.MuirError) as e:
+        m.muir_chunk_fwd(*(bad[n] for n in NAMES), chunk=64, check_inputs=True)
+    assert e.value.code == 9 and "log_a" in str(e.value)
+    bad = dict(inp)
+    bad["dO"] = inp["dO"].clone()
+    bad["dO"][0, 0, 0, 0] = float("nan")
+    with pytest.raises(m.MuirError):
+        m.muir_chunk_bwd(*args, bad["dO"], chunk=64, check_inputs=True)
