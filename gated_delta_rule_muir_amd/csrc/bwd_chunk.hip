@@ -40,11 +40,29 @@ namespace muir {
 
 namespace {
 
-// Per-chunk scratch, in the compute type: deltas [C][DV], then the state at
-// the start of every 16-token block [C/16][DK][DV] (row-major, as staged).
-template <typename TC>
+// Forms of the per-chunk backward:
+//   0: two sweeps (fp32 inputs): a forward sweep over the 16-token blocks
+//      solves for the deltas and keeps every block-start state, then the
+//      reverse sweep;
+//   1: direct (bf16, 64-token chunks): the chunk's deltas come from the
+//      forward scan, and the reverse sweep forms every block-start state
+//      from the chunk-start state and the deltas (Horner over the earlier
+//      blocks);
+//   2: direct over sub-chunks (bf16, 128- and 256-token chunks): a forward
+//      pass over the chunk's 64-token sub-chunks carries the state with the
+//      forward scan's deltas and keeps each later sub-chunk's start state;
+//      the reverse sweep then runs form 1 within each sub-chunk.
+enum BwdForm { BWD_TWO_SWEEP = 0, BWD_DIRECT = 1, BWD_SUB = 2 };
+
+// Per-chunk scratch, in the compute type.  Form 0: deltas [C][DV], then the
+// state at the start of every 16-token block [C/16][DK][DV] (row-major, as
+// staged).  Form 2: the start state of sub-chunks 1 .. C/64 - 1 [.][DK][DV]
+// (sub-chunk 0 starts from the chunk's own start state).  Form 1: none.
+template <typename TC, int FORM>
 __host__ __device__ constexpr size_t bwd_scratch_bytes_tc(int C, int DK, int DV) {
-  return (static_cast<size_t>(C) * DV + static_cast<size_t>(C / 16) * DK * DV) * sizeof(TC);
+  return FORM == BWD_TWO_SWEEP ? (static_cast<size_t>(C) * DV + static_cast<size_t>(C / 16) * DK * DV) * sizeof(TC)
+         : FORM == BWD_SUB     ? static_cast<size_t>(C / 64 - 1) * DK * DV * sizeof(TC)
+                               : 0;
 }
 
 // LDS row padding (elements).  LDS serves a fragment read 128 bytes at a
@@ -71,8 +89,8 @@ template <typename TC, int DK, int C> constexpr int stage_split() {
 
 // Tin: element type of the inputs, dO, the chunk states and the MFMA
 // operands; Tg: element type of the per-token gradients (Tin, or fp32 for
-// bf16 inputs).
-template <typename Tin, typename Tg, int DK, int C, int NW, bool DIRECT, bool GTOK>
+// bf16 inputs); FORM: BwdForm.
+template <typename Tin, typename Tg, int DK, int C, int NW, int FORM, bool GTOK>
 __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     int T, int H, const Tin* __restrict__ q, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ log_a, const Tin* __restrict__ erase,
@@ -92,7 +110,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   constexpr int TPC = NTH / DK;       // elementwise: threads per key channel
   constexpr int RPT = 16 / TPC;       // elementwise: consecutive tokens per thread
   constexpr int NB = C / 16;
-  constexpr int SPLIT = stage_split<TC, DK, C>();
+  // the direct machinery (forms 1 and 2): the reverse sweep forms the state at
+  // each block start within a span of NBS blocks (a 64-token chunk or
+  // sub-chunk) from the span's start state
+  constexpr bool DIRECT = FORM != BWD_TWO_SWEEP;
+  constexpr bool SUB = FORM == BWD_SUB;
+  constexpr int NBS = DIRECT ? 4 : NB;
+  constexpr int NSUB = NB / NBS;
+  static_assert(NB % NBS == 0 && (FORM != BWD_DIRECT || NB == 4) && (!SUB || NB > 4), "backward form");
+  constexpr int SPLIT = DIRECT ? 1 : stage_split<TC, DK, C>();
   constexpr int SW = DV / SPLIT;
   constexpr int PT = DK + row_pad<TC>();
   constexpr int PV = DV + row_pad<TC>();
@@ -162,8 +188,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     const float x = ldv(gst, static_cast<uint32_t>(j));
     return gmode == GAMMA_NONE ? 1.f : x;
   };
-  TC* gDel = reinterpret_cast<TC*>(scratch + static_cast<size_t>(chunk) * bwd_scratch_bytes_tc<TC>(C, DK, DV));
-  TC* gS = gDel + static_cast<size_t>(C) * DV;  // [NB][DK][DV]
+  TC* gDel = reinterpret_cast<TC*>(scratch + static_cast<size_t>(chunk) * bwd_scratch_bytes_tc<TC, FORM>(C, DK, DV));
+  TC* gS = gDel + static_cast<size_t>(C) * DV;  // form 0: [NB][DK][DV]
+  TC* gSub = gDel;                              // form 2: [NSUB - 1][DK][DV]
   // T_II, P_II of the chunk's blocks, from the chunk summary, [NB][2][16][16]
   const TC* gTP = reinterpret_cast<const TC*>(summ + static_cast<size_t>(chunk) * summ_bytes + tp_offset);
   const Tin* S0c = S_chunks + static_cast<size_t>(chunk) * DK * DV;  // [dk][dv] rows, compute type
@@ -175,7 +202,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   __shared__ __attribute__((aligned(16))) TC sTA[DK][TP];    // F: Ke^T     R: X^T
   __shared__ __attribute__((aligned(16))) TC sTB[DK][TP];    // F: U^T      R: Y^T
   __shared__ __attribute__((aligned(16))) TC sDO[16][PV];    // dO rows of the block
-  __shared__ __attribute__((aligned(16))) TC sDL[DIRECT ? C : 16][PV];  // delta rows (direct: of the chunk)
+  __shared__ __attribute__((aligned(16))) TC sDL[DIRECT ? 16 * NBS : 16][PV];  // delta rows (direct: of the span)
   __shared__ __attribute__((aligned(16))) TC sDR[16][PV];    // dR rows of the block
   __shared__ __attribute__((aligned(16))) TC sT[16][TP];     // T_II of the block
   __shared__ __attribute__((aligned(16))) TC sP[16][TP];     // P_II of the block
@@ -186,7 +213,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   __shared__ __attribute__((aligned(16))) TC sIn[DIRECT ? 7 : 1][16][PV];
   __shared__ float sLf[2][16][17];                           // leaf matrices of steep blocks
   __shared__ float sG[DK];
-  __shared__ float sGH[DIRECT ? NB - 1 : 1][DK];              // direct: block decays exp(B_{I+1} - B_I)
+  __shared__ float sGH[DIRECT ? NBS - 1 : 1][DK];             // direct: block decays exp(B_{I+1} - B_I)
   // The block's token-token products x_r . Delta_t over dv (x = dO, dR; r, t
   // tokens), each formed once by one wave and read by all: for the deltas of
   // the block itself masked to the leaf's triangle, in both orientations
@@ -195,7 +222,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   constexpr int GP = 16 + row_pad<TC>();
   __shared__ __attribute__((aligned(16))) TC sGd[2][16][GP];
   __shared__ __attribute__((aligned(16))) TC sGT[2][16][GP];
-  __shared__ __attribute__((aligned(16))) TC sGh[2][DIRECT ? NB - 1 : 1][16][GP];
+  __shared__ __attribute__((aligned(16))) TC sGh[2][DIRECT ? NBS - 1 : 1][16][GP];
   // per-wave partial rowsums of S_C * dS_C, used once before the reverse
   // sweep (which then writes X^T over it)
   static_assert(NW * DK * sizeof(float) <= sizeof(TC) * DK * TP, "rowsum scratch");
@@ -588,7 +615,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   // Direct form: the operands of the Horner steps in the reverse sweep,
   // Ke_I = k exp(B_{I+1} - Lam) at (token 4g+i of block I, channel colv(n)),
   // and the block decays exp(B_{I+1} - B_I) in sGH, for every block but the last.
-  frag keH[DIRECT ? NB - 1 : 1][NT];
+  frag keH[DIRECT ? NBS - 1 : 1][NT];
   frag s0f[NT][DIRECT ? DV / 16 : 1];  // direct form: S0 rows of the wave's key channels
   // Direct form: every global read of the prologue is issued before the
   // first wait -- the chunk's deltas and Kbar^T (16-byte words), Gamma_C, the
@@ -601,8 +628,59 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   // direct form: log_a of every block and k of the earlier ones at (token
   // 4g+i of block I, channel colv(n)): the Horner inputs, and the per-part
   // decay sums (part p of the elementwise mapping is token group g = p here)
-  float hl[DIRECT ? NB : 1][NT][4], hk[DIRECT ? NB - 1 : 1][NT][4];
-  if constexpr (DIRECT) {
+  float hl[DIRECT ? NBS : 1][NT][4], hk[DIRECT ? NBS - 1 : 1][NT][4];
+  // The Horner operands of a span from hl, hk (keH, and the block decays in sGH).
+  auto horner_setup = [&]() {
+    if constexpr (DIRECT)
+#pragma unroll
+    for (int I = 0; I < NBS - 1; ++I)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const float* l = hl[I][n];
+        // log-decay after each token to the block's end: within the lane's
+        // four tokens, plus the token groups of the lanes c16 + 16g' (g' > g)
+        const float s4 = (l[0] + l[1]) + (l[2] + l[3]);
+        const float t1 = __shfl(s4, c16 + 16, 64);
+        const float t2 = __shfl(s4, c16 + 32, 64);
+        const float t3 = __shfl(s4, c16 + 48, 64);
+        const float t0 = __shfl(s4, c16, 64);
+        float later = (g < 3 ? t3 : 0.f) + (g < 2 ? t2 : 0.f) + (g < 1 ? t1 : 0.f);
+        f32x4 kv;
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+          kv[i] = hk[I][n][i] * __expf(later);
+          later += l[i];
+        }
+        keH[I][n] = M::from_f32(kv);
+        if (g == 0) sGH[I][colv(n)] = __expf(((t0 + t1) + t2) + t3);
+      }
+  };
+  // log_a of the span's blocks and k of all but its last, at (token 4g+i of
+  // block I of the span starting at block I0, channel colv(n))
+  auto horner_loads = [&](int I0) {
+    if constexpr (DIRECT)
+#pragma unroll
+    for (int I = 0; I < NBS; ++I)
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t o = gi(16 * (I0 + I) + 4 * g + i, colv(n));
+          hl[I][n][i] = ldv(lb, o);
+          if (I < NBS - 1) hk[I < NBS - 1 ? I : 0][n][i] = ldv(kb, o);
+        }
+  };
+  // the span's start state: its rows of this wave's key channels as the right
+  // operands of the boundary products (rows colv(n), dv columns 16kk + 4g ..)
+  auto load_s0f = [&](const Tin* src) {
+    if constexpr (DIRECT)
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int kk = 0; kk < DV / 16; ++kk)
+        s0f[n][kk] = *reinterpret_cast<const frag*>(at(src, static_cast<uint32_t>((col0(n) + c16) * DV + 16 * kk + 4 * g)));
+  };
+  if constexpr (FORM == BWD_DIRECT) {
     static_assert(DWT * NTH == C * DWR && KWT * NTH == DK * KWR && DK / 4 <= NTH && NB == 4,
                   "direct-form prologue layout");
     static_assert(TPC == 4 && RPT == 4, "direct form: one elementwise part per token group of the output mapping");
@@ -618,24 +696,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       kw[k2] = *reinterpret_cast<const u32x4*>(
           at(gKT, tpart_index((tid + k2 * NTH) / KWR, ((tid + k2 * NTH) % KWR) * SEW, DK)));  // 16-token tiles
     gcw = *reinterpret_cast<const u32x4*>(at(gGC, static_cast<uint32_t>(4 * min(tid, DK / 4 - 1))));
-#pragma unroll
-    for (int I = 0; I < NB; ++I)
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t o = gi(16 * I + 4 * g + i, colv(n));
-          hl[I][n][i] = ldv(lb, o);
-          if (I < NB - 1) hk[I < NB - 1 ? I : 0][n][i] = ldv(kb, o);
-        }
+    horner_loads(0);
     load_state(S, S0c);
-    // S0 rows of this wave's key channels as the right operands of the
-    // boundary products (rows colv(n), dv columns 16kk + 4g ..)
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-      for (int kk = 0; kk < DV / 16; ++kk)
-        s0f[n][kk] = *reinterpret_cast<const frag*>(at(S0c, static_cast<uint32_t>((col0(n) + c16) * DV + 16 * kk + 4 * g)));
+    load_s0f(S0c);
     load_dstate(D);
     prefetch_r(NB - 1);
     load_in(NB - 1);
@@ -644,7 +707,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   // ---- sums of the log-decay over each block and each part of it, and the
   // blocks whose decay leaves LEAF_SAFE_RANGE (steep leaves) ----
   if (tid == 0) sUnsafe = 0;
-  if constexpr (DIRECT) {
+  if constexpr (FORM == BWD_DIRECT) {
     // from the log-decay already in registers at the output mapping
 #pragma unroll
     for (int I = 0; I < NB; ++I)
@@ -672,7 +735,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     if (mask) atomicOr(&sUnsafe, static_cast<int>(mask));
   }
 
-  if constexpr (DIRECT) {
+  if constexpr (FORM == BWD_DIRECT) {
     // deltas into sDL; Kbar^T into sSD (until the sweep stages D there);
     // Gamma_C into sG (until the sweep's block sums); the last block's inputs
     // into sIn
@@ -690,28 +753,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     }
     if (tid < DK / 4) *reinterpret_cast<u32x4*>(&sG[4 * tid]) = gcw;
     store_in();
-#pragma unroll
-    for (int I = 0; I < NB - 1; ++I)
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const float* l = hl[I][n];
-        // log-decay after each token to the block's end: within the lane's
-        // four tokens, plus the token groups of the lanes c16 + 16g' (g' > g)
-        const float s4 = (l[0] + l[1]) + (l[2] + l[3]);
-        const float t1 = __shfl(s4, c16 + 16, 64);
-        const float t2 = __shfl(s4, c16 + 32, 64);
-        const float t3 = __shfl(s4, c16 + 48, 64);
-        const float t0 = __shfl(s4, c16, 64);
-        float later = (g < 3 ? t3 : 0.f) + (g < 2 ? t2 : 0.f) + (g < 1 ? t1 : 0.f);
-        f32x4 kv;
-#pragma unroll
-        for (int i = 3; i >= 0; --i) {
-          kv[i] = hk[I][n][i] * __expf(later);
-          later += l[i];
-        }
-        keH[I][n] = M::from_f32(kv);
-        if (g == 0) sGH[I][colv(n)] = __expf(((t0 + t1) + t2) + t3);
-      }
+    horner_setup();
     __syncthreads();  // sDL, sSD, sG, sIn, sGH
     // S becomes the chunk-end state S_C = diag(Gamma_C) S0 + Kbar^T Delta
     // (for the rowsum term below)
@@ -740,6 +782,105 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         }
       }
     }
+  } else if constexpr (SUB) {
+    // Forward pass over the 64-token sub-chunks:
+    //   S_{g+1} = diag(Gamma_g) S_g + Kbar_g^T Delta_g,
+    // with the deltas the forward scan kept in the chunk summary and
+    // Kbar_g = k exp(Lam_end - Lam), the keys decayed to the sub-chunk's end
+    // (every factor <= 1).  The start state of each later sub-chunk goes to the
+    // scratch (compute type, [dk][dv] rows) for the reverse sweep; S ends as
+    // the chunk-end state S_C.
+    constexpr int SWT = 16 * NBS * DV / SEW / NTH;  // 16-byte delta words per thread and sub-chunk
+    static_assert(SWT * NTH * SEW == 16 * NBS * DV && RPT == 4, "sub-chunk pass layout");
+    const TC* gD = reinterpret_cast<const TC*>(summ + static_cast<size_t>(chunk) * summ_bytes + dl_offset);
+    load_state(S, S0c);
+    load_dstate(D);
+    prefetch_r(NB - 1);
+    load_in(NB - 1);
+    __syncthreads();  // sPart
+#pragma unroll 1
+    for (int sg = 0; sg < NSUB; ++sg) {
+      u32x4 dwl[SWT];
+#pragma unroll
+      for (int k2 = 0; k2 < SWT; ++k2)
+        dwl[k2] = *reinterpret_cast<const u32x4*>(
+            at(gD, static_cast<uint32_t>(16 * NBS * sg * DV + (tid + k2 * NTH) * SEW)));
+      float fk[NBS][RPT], fl2[NBS][RPT];
+#pragma unroll
+      for (int bl = 0; bl < NBS; ++bl)
+#pragma unroll
+        for (int rr = 0; rr < RPT; ++rr) {
+          const uint32_t o = gi(16 * (NBS * sg + bl) + RPT * part + rr, ej);
+          fk[bl][rr] = ldv(kb, o);
+          fl2[bl][rr] = ldv(lb, o);
+        }
+      // Kbar_g^T into sSD ([dk][tokens of the sub-chunk]), Gamma_g into sG
+      float later = 0.f;  // log-decay of the sub-chunk's blocks after block bl (channel ej)
+#pragma unroll
+      for (int bl = NBS - 1; bl >= 0; --bl) {
+        const int I = NBS * sg + bl;
+        float exsuf = 0.f, bs = 0.f;
+#pragma unroll
+        for (int p = 0; p < TPC; ++p) {
+          const float ps = sPart[I][p][ej];
+          if (p > part) exsuf += ps;
+          bs += ps;
+        }
+        float s2 = 0.f;
+        f32x4 kv;
+#pragma unroll
+        for (int rr = RPT - 1; rr >= 0; --rr) {
+          kv[rr] = fk[bl][rr] * __expf(s2 + exsuf + later);
+          s2 += fl2[bl][rr];
+        }
+        store4(&sSD[ej][16 * bl + RPT * part], kv);
+        later += bs;
+      }
+      if (part == 0) sG[ej] = __expf(later);
+#pragma unroll
+      for (int k2 = 0; k2 < SWT; ++k2) {
+        const int w = tid + k2 * NTH;
+        const int row = w / DWR;
+        put16(&sDL[row][(w - row * DWR) * SEW], dwl[k2]);
+      }
+      __syncthreads();
+      if (sg > 0) {
+        // the sub-chunk's start state, rounded once, as [dk][dv] rows
+        TC* dst = gSub + static_cast<size_t>(sg - 1) * DK * DV;
+#pragma unroll
+        for (int s2 = 0; s2 < RT; ++s2)
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            const f32x4 tt = M::mma(M::from_f32(S[s2][n]), ident, zero4());  // row 16s+c16, columns col0(n)+4g+i
+            store4(at(dst, static_cast<uint32_t>((16 * s2 + c16) * DV + col0(n) + 4 * g)), tt);
+          }
+      }
+      frag dcol[NBS][NT];  // Delta at (token 4g+i of block m, column colv(n))
+#pragma unroll
+      for (int m = 0; m < NBS; ++m)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          f32x4 t;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) t[i] = M::to_f32(sDL[16 * m + 4 * g + i][colv(n)]);
+          dcol[m][n] = M::from_f32(t);
+        }
+#pragma unroll
+      for (int s2 = 0; s2 < RT; ++s2) {
+        const f32x4 gc = decay_scale(s2);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) S[s2][n] *= gc;
+#pragma unroll
+        for (int m = 0; m < NBS; m += 2) {
+          const frag ka = M::load(&sSD[16 * s2 + c16][16 * m + 4 * g]);
+          const frag ka1 = M::load(&sSD[16 * s2 + c16][16 * m + 16 + 4 * g]);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) S[s2][n] = M::mma2(ka, dcol[m][n], ka1, dcol[m + 1][n], S[s2][n]);
+        }
+      }
+      __syncthreads();  // sDL, sSD and sG are rewritten by the next sub-chunk
+    }
+    store_in();  // the last block's inputs, for the reverse sweep
   } else {
     load_state(S, S0c);
     prefetch_f(0);
@@ -832,7 +973,33 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
 #pragma unroll 1
   for (int J = NB - 1; J >= 0; --J) {
     const int r0 = 16 * J;
-    const TC (*dlJ)[PV] = DIRECT ? sDL + r0 : sDL;  // the block's delta rows
+    const int jl = J % NBS;  // the block within its span (direct forms)
+    if constexpr (SUB) {
+      if (jl == NBS - 1) {
+        // a sub-chunk's last block: its start state (the chunk's, or from the
+        // forward pass), its deltas and its Horner operands; the previous
+        // step's closing barrier ended every read of the later sub-chunk's
+        // and the commit below publishes these
+        const int sg = J / NBS;
+        constexpr int SWT = 16 * NBS * DV / SEW / NTH;
+        const TC* gD = reinterpret_cast<const TC*>(summ + static_cast<size_t>(chunk) * summ_bytes + dl_offset);
+        u32x4 dwl[SWT];
+#pragma unroll
+        for (int k2 = 0; k2 < SWT; ++k2)
+          dwl[k2] = *reinterpret_cast<const u32x4*>(
+              at(gD, static_cast<uint32_t>(16 * NBS * sg * DV + (tid + k2 * NTH) * SEW)));
+        horner_loads(NBS * sg);
+        load_s0f(sg == 0 ? S0c : gSub + static_cast<size_t>(sg - 1) * DK * DV);
+#pragma unroll
+        for (int k2 = 0; k2 < SWT; ++k2) {
+          const int w = tid + k2 * NTH;
+          const int row = w / DWR;
+          put16(&sDL[row][(w - row * DWR) * SEW], dwl[k2]);
+        }
+        horner_setup();
+      }
+    }
+    const TC (*dlJ)[PV] = DIRECT ? sDL + 16 * jl : sDL;  // the block's delta rows
     const int safe = commit_r(J);
     u32x4 css[SPLIT > 1 ? SPT : 1];  // this block's state words for the later column passes
     if (SPLIT > 1) {
@@ -902,11 +1069,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     }
     // The shared token-token products G = x . Delta_t (x = dO, dR rows of the
     // block), np of them, product pr by wave pr % NW: with the deltas of the
-    // block itself (pr < 2), and in the direct form of block pr/2 <= J.  A
-    // wave whose pr >= np forms a product it does not store (no branch in the
-    // contraction).
-    constexpr int PPW = DIRECT ? (2 * NB + NW - 1) / NW : (2 + NW - 1) / NW;
-    const int np = DIRECT ? 2 * (J + 1) : 2;
+    // block itself (pr < 2), and in the direct forms of block pr/2 <= jl of
+    // the span.  A wave whose pr >= np forms a product it does not store (no
+    // branch in the contraction).
+    constexpr int PPW = DIRECT ? (2 * NBS + NW - 1) / NW : (2 + NW - 1) / NW;
+    const int np = DIRECT ? 2 * (jl + 1) : 2;
     f32x4 gacc[PPW];
 #pragma unroll
     for (int q2 = 0; q2 < PPW; ++q2) gacc[q2] = zero4();
@@ -984,12 +1151,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
 #pragma unroll
     for (int q2 = 0; q2 < PPW; ++q2) {
       // lane (g, c16) of product pr: x_{4g+i} . Delta_{c16}, x = dO (pr even) or
-      // dR rows, the deltas of block pr/2 (direct form) or of this block
+      // dR rows, the deltas of block pr/2 of the span (direct forms) or of this block
       const int pr = wave + q2 * NW;
       const int x = pr & 1;
-      const int I = DIRECT ? pr >> 1 : J;
+      const int I = DIRECT ? pr >> 1 : jl;
       if (pr < np) {
-        if (I == J) {
+        if (I == jl) {
           // leaf triangle: t <= r for dO, t < r for dR (negated in the t-row copy)
           f32x4 gm, gt;
 #pragma unroll
@@ -1013,8 +1180,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       // so each row x of dO_J, dR_J takes, in Horner form over the earlier
       // blocks I, acc <- exp(B_{I+1} - B_I) acc + (x . Delta_t) Ke_I[t] (every factor <= 1)
 #pragma unroll
-      for (int I = 0; I < NB - 1; ++I) {
-        if (I < J) {
+      for (int I = 0; I < NBS - 1; ++I) {
+        if (I < jl) {
           const frag mqf = M::load(&sGh[0][I][c16][4 * g]);  // rows r, contraction over block I's tokens
           const frag mef = M::load(&sGh[1][I][c16][4 * g]);
 #pragma unroll
@@ -1148,8 +1315,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
 }  // namespace
 
 size_t bwd_chunk_scratch_bytes(const ChunkShape& s) {
-  if (s.bwd_direct()) return 0;
-  return s.bf16 ? bwd_scratch_bytes_tc<uint16_t>(s.C, s.DK, s.DV) : bwd_scratch_bytes_tc<float>(s.C, s.DK, s.DV);
+  if (!s.bf16) return bwd_scratch_bytes_tc<float, BWD_TWO_SWEEP>(s.C, s.DK, s.DV);
+  return s.C == 64 ? bwd_scratch_bytes_tc<uint16_t, BWD_DIRECT>(s.C, s.DK, s.DV)
+                   : bwd_scratch_bytes_tc<uint16_t, BWD_SUB>(s.C, s.DK, s.DV);
 }
 
 hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, const void* v,
@@ -1161,35 +1329,36 @@ hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, c
                             hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(s.nchunks());
   if (grid == 0) return hipSuccess;
-#define MUIR_BCH2(TT, TG, DD, CC, NW, DIR, GT)                                                              \
-  hipLaunchKernelGGL((bwd_chunk_kernel<TT, TG, DD, CC, NW, DIR, GT>), dim3(grid), dim3(64 * NW), 0, stream, s.T, \
+#define MUIR_BCH2(TT, TG, DD, CC, NW, FORM, GT)                                                              \
+  hipLaunchKernelGGL((bwd_chunk_kernel<TT, TG, DD, CC, NW, FORM, GT>), dim3(grid), dim3(64 * NW), 0, stream, s.T, \
                      s.H, (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, (const TT*)erase,        \
                      (const TT*)write, (const TT*)gamma, (const char*)summ, s.summary_bytes(), s.tp_offset(),    \
                      s.dl_offset(), (const TT*)S_chunks, (const TT*)dS_chunks, (const TT*)dO, (TG*)dq, (TG*)dk,  \
                      (TG*)dv, (TG*)dlog_a, (TG*)derase, (TG*)dwrite, (TG*)dgamma, (char*)scratch, s.gmode,       \
                      dgam_part)
-#define MUIR_BCH1(TT, TG, DD, CC, NW, DIR)                              \
-  do {                                                                  \
-    if (s.gmode == GAMMA_TOKEN) MUIR_BCH2(TT, TG, DD, CC, NW, DIR, true); \
-    else MUIR_BCH2(TT, TG, DD, CC, NW, DIR, false);                     \
+#define MUIR_BCH1(TT, TG, DD, CC, NW, FORM)                              \
+  do {                                                                   \
+    if (s.gmode == GAMMA_TOKEN) MUIR_BCH2(TT, TG, DD, CC, NW, FORM, true); \
+    else MUIR_BCH2(TT, TG, DD, CC, NW, FORM, false);                     \
   } while (0)
-#define MUIR_BCH(TT, TG, DD, NW, DIR64)                         \
-  do {                                                          \
-    if (s.C == 64) MUIR_BCH1(TT, TG, DD, 64, NW, DIR64);        \
-    else if (s.C == 128) MUIR_BCH1(TT, TG, DD, 128, NW, false); \
-    else MUIR_BCH1(TT, TG, DD, 256, NW, false);                 \
+#define MUIR_BCH(TT, TG, DD, NW, F64, FL)                    \
+  do {                                                       \
+    if (s.C == 64) MUIR_BCH1(TT, TG, DD, 64, NW, F64);       \
+    else if (s.C == 128) MUIR_BCH1(TT, TG, DD, 128, NW, FL); \
+    else MUIR_BCH1(TT, TG, DD, 256, NW, FL);                 \
   } while (0)
-  // one 16-column tile per wave: 8 waves at d = 128, 4 at d = 64; the direct
-  // form exactly where ChunkShape::bwd_direct says so (bf16, C = 64)
+  // one 16-column tile per wave: 8 waves at d = 128, 4 at d = 64; bf16 inputs
+  // take the direct forms (their chunk deltas are kept by the forward scan,
+  // ChunkShape::bwd_direct), fp32 inputs the two sweeps
   if (s.bf16 && s.gbf16) {
-    if (s.DK == 128) MUIR_BCH(uint16_t, uint16_t, 128, 8, true);
-    else MUIR_BCH(uint16_t, uint16_t, 64, 4, true);
+    if (s.DK == 128) MUIR_BCH(uint16_t, uint16_t, 128, 8, BWD_DIRECT, BWD_SUB);
+    else MUIR_BCH(uint16_t, uint16_t, 64, 4, BWD_DIRECT, BWD_SUB);
   } else if (s.bf16) {
-    if (s.DK == 128) MUIR_BCH(uint16_t, float, 128, 8, true);
-    else MUIR_BCH(uint16_t, float, 64, 4, true);
+    if (s.DK == 128) MUIR_BCH(uint16_t, float, 128, 8, BWD_DIRECT, BWD_SUB);
+    else MUIR_BCH(uint16_t, float, 64, 4, BWD_DIRECT, BWD_SUB);
   } else {
-    if (s.DK == 128) MUIR_BCH(float, float, 128, 8, false);
-    else MUIR_BCH(float, float, 64, 4, false);
+    if (s.DK == 128) MUIR_BCH(float, float, 128, 8, BWD_TWO_SWEEP, BWD_TWO_SWEEP);
+    else MUIR_BCH(float, float, 64, 4, BWD_TWO_SWEEP, BWD_TWO_SWEEP);
   }
 #undef MUIR_BCH
 #undef MUIR_BCH1

@@ -59,9 +59,10 @@ struct ChunkShape {
   size_t state_bytes() const { return static_cast<size_t>(DK) * DV * 4; }
   // The backward takes the chunk's deltas from the forward scan and forms the
   // states inside a chunk from S0 and those deltas (one reverse sweep over
-  // its blocks), instead of a forward sweep that recomputes both: for
-  // 64-token chunks in bf16, whose tiles then fit the LDS.
-  bool bwd_direct() const { return bf16 && C == 64; }
+  // its blocks; longer chunks first carry the state over their 64-token
+  // sub-chunks), instead of a forward sweep that recomputes both: for bf16,
+  // whose tiles then fit the LDS.
+  bool bwd_direct() const { return bf16; }
   // Segments of the split scans: 1 when the heads' 64-column scans alone fill
   // the chip; else the sequence is cut into the fewest power-of-two segments
   // that do, with at least 4 chunks each.
