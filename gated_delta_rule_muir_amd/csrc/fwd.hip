@@ -139,8 +139,10 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
   __shared__ __attribute__((aligned(16))) TC sQh[NBUF][DK][20];  // (qt * exp(Lam))^T
   __shared__ float sAw[16][17];  // A_II and P_II of a leaf beyond the safe range
   __shared__ float sPf[16][17];
-  __shared__ __attribute__((aligned(16))) TC sT[16][20];
-  __shared__ __attribute__((aligned(16))) TC sP[16][20];
+  // T_II, P_II of the block (bf16: in buffer I & 1, since block I+1's are
+  // formed while block I's are read)
+  __shared__ __attribute__((aligned(16))) TC sT[NBUF][16][20];
+  __shared__ __attribute__((aligned(16))) TC sP[NBUF][16][20];
   __shared__ __attribute__((aligned(16))) TC sStage[16][2 * DK + 8];
 
   // ---- the next block's inputs are loaded one block ahead (4 tokens of
@@ -290,22 +292,52 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
   // P_II (accumulator layout), into sT, sP and the summary, by wave 0
   auto leaf_inverse = [&](int I, f32x4 a_acc, f32x4 a_tr, f32x4 p_acc) {
     const f32x4 t = neumann16(a_acc, a_tr);
+    const int tb = PIPE ? I & 1 : 0;
     TC* tp = out.TP + static_cast<size_t>(I) * 512;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * g + i;
       const TC tv = M::cvt(t[i]);
       const TC pv = M::cvt(p_acc[i]);
-      sT[r][c16] = tv;
-      sP[r][c16] = pv;
+      sT[tb][r][c16] = tv;
+      sP[tb][r][c16] = pv;
       tp[r * 16 + c16] = tv;  // kept for the backward
       tp[256 + r * 16 + c16] = pv;
     }
+  };
+  // the leaf of block I within LEAF_SAFE_RANGE from its operand tiles: A = X Z^T
+  // and P = Y Z^T in the accumulator layout, and A^T = Z X^T (A in the other
+  // layout, from the same operands swapped); by wave 0
+  auto leaf_safe = [&](int I) {
+    const int lb2 = PIPE ? I & 1 : 0;
+    f32x4 a = zero4(), at = zero4(), p = zero4();
+#pragma unroll
+    for (int s = 0; s < RT; s += 2) {
+      const frag zb = M::load(&sZ[lb2][c16][16 * s + 4 * g]);
+      const frag xa = M::load(&sX[lb2][c16][16 * s + 4 * g]);
+      const frag ya = M::load(&sY[lb2][c16][16 * s + 4 * g]);
+      const frag zb1 = M::load(&sZ[lb2][c16][16 * s + 16 + 4 * g]);
+      const frag xa1 = M::load(&sX[lb2][c16][16 * s + 16 + 4 * g]);
+      const frag ya1 = M::load(&sY[lb2][c16][16 * s + 16 + 4 * g]);
+      a = M::mma2(xa, zb, xa1, zb1, a);
+      at = M::mma2(zb, xa, zb1, xa1, at);
+      p = M::mma2(ya, zb, ya1, zb1, p);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g + i;
+      a[i] = c16 < r ? a[i] : 0.f;    // A[r][c16], strictly lower
+      at[i] = r < c16 ? at[i] : 0.f;  // A[c16][r]
+      p[i] = c16 <= r ? p[i] : 0.f;
+    }
+    leaf_inverse(I, a, at, p);
   };
 
   if (PIPE) {
     elementwise(0);
     __syncthreads();
+    // block 0's leaf (each later block's is formed during the block before it)
+    if (!(sUnsafe & 1) && wave == 0) leaf_safe(0);
   }
 
 #pragma unroll 1
@@ -341,32 +373,9 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
         }
       }
     }
-    // ---- leaf: A_II, P_II, T_II (wave 0, when the leaf is within range) ----
-    if (safe && wave == 0) {
-      // A = X Z^T and P = Y Z^T in the accumulator layout, and A^T = Z X^T,
-      // i.e. A in the other layout, from the same operands swapped
-      f32x4 a = zero4(), at = zero4(), p = zero4();
-#pragma unroll
-      for (int s = 0; s < RT; s += 2) {
-        const frag zb = M::load(&sZ[bb][c16][16 * s + 4 * g]);
-        const frag xa = M::load(&sX[bb][c16][16 * s + 4 * g]);
-        const frag ya = M::load(&sY[bb][c16][16 * s + 4 * g]);
-        const frag zb1 = M::load(&sZ[bb][c16][16 * s + 16 + 4 * g]);
-        const frag xa1 = M::load(&sX[bb][c16][16 * s + 16 + 4 * g]);
-        const frag ya1 = M::load(&sY[bb][c16][16 * s + 16 + 4 * g]);
-        a = M::mma2(xa, zb, xa1, zb1, a);
-        at = M::mma2(zb, xa, zb1, xa1, at);
-        p = M::mma2(ya, zb, ya1, zb1, p);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g + i;
-        a[i] = c16 < r ? a[i] : 0.f;    // A[r][c16], strictly lower
-        at[i] = r < c16 ? at[i] : 0.f;  // A[c16][r]
-        p[i] = c16 <= r ? p[i] : 0.f;
-      }
-      leaf_inverse(I, a, at, p);
-    }
+    // ---- leaf: A_II, P_II, T_II (wave 0, when the leaf is within range;
+    // in bf16 it was formed during the previous block) ----
+    if (!PIPE && safe && wave == 0) leaf_safe(I);
     // ---- the next block's elementwise work, beside this block's products ----
     if (PIPE && I + 1 < NB) elementwise(I + 1);
     if (!safe) {
@@ -403,9 +412,12 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
     }
     __syncthreads();
 
+    // ---- the next block's leaf (bf16), beside this block's products ----
+    if (PIPE && I + 1 < NB && !((sUnsafe >> (I + 1)) & 1) && wave == 0) leaf_safe(I + 1);
     // ---- [U~|W]_I = T_II (R_I - X_I H_I);  [O~|PW]_I = Y_I H_I + P_II [U~|W]_I ----
-    const frag ta = M::load(&sT[c16][4 * g]);
-    const frag pa = M::load(&sP[c16][4 * g]);
+    const int tb = PIPE ? I & 1 : 0;
+    const frag ta = M::load(&sT[tb][c16][4 * g]);
+    const frag pa = M::load(&sP[tb][c16][4 * g]);
     f32x4 UW[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
