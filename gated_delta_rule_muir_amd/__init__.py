@@ -241,7 +241,8 @@ def muir_chunk_fwd(q, k, v, log_a, erase, write, gamma, S0=None, *, chunk: int =
     Any T: a partial last chunk runs on zero-padded copies in the workspace.
     Returns (o [B,T,H,dv] in the input dtype, S_T [B,H,dk,dv] fp32 or None,
     S_chunks [B,H,ceil(T/chunk),dk,dv] in the input dtype (the chunk-start
-    states kept for muir_chunk_bwd) or None).
+    states kept for muir_chunk_bwd, each stored as 16 x 16 tiles, see
+    include/muir.h) or None).
     """
     B, T, H, dk = q.shape
     dv = v.shape[3]

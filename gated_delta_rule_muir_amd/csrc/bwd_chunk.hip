@@ -190,10 +190,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   };
   TC* gDel = reinterpret_cast<TC*>(scratch + static_cast<size_t>(chunk) * bwd_scratch_bytes_tc<TC, FORM>(C, DK, DV));
   TC* gS = gDel + static_cast<size_t>(C) * DV;  // form 0: [NB][DK][DV]
-  TC* gSub = gDel;                              // form 2: [NSUB - 1][DK][DV]
+  TC* gSub = gDel;                              // form 2: [NSUB - 1] states as 16 x 16 tiles
   // T_II, P_II of the chunk's blocks, from the chunk summary, [NB][2][16][16]
   const TC* gTP = reinterpret_cast<const TC*>(summ + static_cast<size_t>(chunk) * summ_bytes + tp_offset);
-  const Tin* S0c = S_chunks + static_cast<size_t>(chunk) * DK * DV;  // [dk][dv] rows, compute type
+  const Tin* S0c = S_chunks + static_cast<size_t>(chunk) * DK * DV;  // 16 x 16 tiles (stile_index), compute type
   const TC* dSC = dS_chunks + static_cast<size_t>(chunk) * DK * DV;  // transposed 16-row tiles
 
   __shared__ float sPart[NB][TPC][DK];                       // sum of log_a over each part's RPT tokens
@@ -327,26 +327,28 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     }
   };
 
+  // A saved state (16 x 16 tiles, stile_index) in the accumulator layout.
   // (the lane offset is made opaque per call so that the addresses are formed
   // where they are used instead of being kept live across the sweeps)
   auto load_state = [&](f32x4 (*st)[NT], const Tin* src) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       if constexpr (sizeof(Tin) == 4) {
-        uint32_t lo = static_cast<uint32_t>(4 * g * DV + colv(n));
+        uint32_t lo = stile_index(4 * g, colv(n), DV);
         asm volatile("" : "+v"(lo));
 #pragma unroll
         for (int s = 0; s < RT; ++s)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) st[s][n][i] = *at(src, lo + static_cast<uint32_t>((16 * s + i) * DV));
+          for (int i = 0; i < 4; ++i) st[s][n][i] = *at(src, lo + static_cast<uint32_t>(s * (DV / 16) * 256 + 16 * i));
       } else {
-        // row 16s + c16, columns col0(n) + 4g .. + 3 as one 8-byte word, turned
-        // onto the accumulator layout by an identity product (exact)
-        uint32_t lo = static_cast<uint32_t>(c16 * DV + col0(n) + 4 * g);
+        // row 16s + c16, columns col0(n) + 4g .. + 3 as one 8-byte word (the
+        // wave reads one whole tile), turned onto the accumulator layout by an
+        // identity product (exact)
+        uint32_t lo = stile_index(c16, col0(n) + 4 * g, DV);
         asm volatile("" : "+v"(lo));
 #pragma unroll
         for (int s = 0; s < RT; ++s) {
-          const uint2 w = *reinterpret_cast<const uint2*>(at(src, lo + static_cast<uint32_t>(16 * s * DV)));
+          const uint2 w = *reinterpret_cast<const uint2*>(at(src, lo + static_cast<uint32_t>(s * (DV / 16) * 256)));
           st[s][n] = M::mma(__builtin_bit_cast(frag, w), ident, zero4());
         }
       }
@@ -678,7 +680,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     for (int n = 0; n < NT; ++n)
 #pragma unroll
       for (int kk = 0; kk < DV / 16; ++kk)
-        s0f[n][kk] = *reinterpret_cast<const frag*>(at(src, static_cast<uint32_t>((col0(n) + c16) * DV + 16 * kk + 4 * g)));
+        s0f[n][kk] = *reinterpret_cast<const frag*>(at(src, stile_index(col0(n) + c16, 16 * kk + 4 * g, DV)));
   };
   if constexpr (FORM == BWD_DIRECT) {
     static_assert(DWT * NTH == C * DWR && KWT * NTH == DK * KWR && DK / 4 <= NTH && NB == 4,
@@ -845,14 +847,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       }
       __syncthreads();
       if (sg > 0) {
-        // the sub-chunk's start state, rounded once, as [dk][dv] rows
+        // the sub-chunk's start state, rounded once, as 16 x 16 tiles
         TC* dst = gSub + static_cast<size_t>(sg - 1) * DK * DV;
 #pragma unroll
         for (int s2 = 0; s2 < RT; ++s2)
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
             const f32x4 tt = M::mma(M::from_f32(S[s2][n]), ident, zero4());  // row 16s+c16, columns col0(n)+4g+i
-            store4(at(dst, static_cast<uint32_t>((16 * s2 + c16) * DV + col0(n) + 4 * g)), tt);
+            store4(at(dst, stile_index(16 * s2 + c16, col0(n) + 4 * g, DV)), tt);
           }
       }
       frag dcol[NBS][NT];  // Delta at (token 4g+i of block m, column colv(n))

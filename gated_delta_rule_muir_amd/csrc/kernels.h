@@ -31,6 +31,18 @@ __host__ __device__ constexpr uint32_t tpart_index(int d, int t, int D) {
          static_cast<uint32_t>(t & 15);
 }
 
+// A state kept for the backward (the chunk-start states S_chunks, and the
+// backward's own sub-chunk start states) is stored as 16 x 16 tiles, row-major
+// within a tile and tile-row-major over the state: element (r, j) of a
+// [DK][DV] state is at this index.  Every access to these states (a lane's
+// four consecutive columns of one row, for 16 rows and 16 columns at a time)
+// then covers one contiguous 512-byte tile (bf16) instead of 32-byte pieces
+// of 16 rows.
+__host__ __device__ constexpr uint32_t stile_index(int r, int j, int DV) {
+  return (static_cast<uint32_t>(r >> 4) * static_cast<uint32_t>(DV >> 4) + static_cast<uint32_t>(j >> 4)) * 256u +
+         static_cast<uint32_t>(r & 15) * 16u + static_cast<uint32_t>(j & 15);
+}
+
 // Readout-gate forms: per token [B, T, H, dk]; static per (head, key channel)
 // [H, dk]; none (gamma = 1, no pointer).
 enum GammaMode { GAMMA_TOKEN = 0, GAMMA_STATIC = 1, GAMMA_NONE = 2 };

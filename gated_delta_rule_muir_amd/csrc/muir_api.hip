@@ -479,7 +479,7 @@ size_t varlen_bwd_need(const ChunkShape& s) { return bwd_ws(padded(s)) + bwd_sta
 
 extern "C" {
 
-int32_t muir_abi_version(void) { return 8; }
+int32_t muir_abi_version(void) { return 9; }
 
 int32_t muir_set_profile_events(void** events, int32_t count) {
   if (count < 0 || (count > 0 && !events)) return MUIR_ERR_NULL;

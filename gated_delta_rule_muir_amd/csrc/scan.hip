@@ -256,19 +256,19 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
     if (sb == 0) {
       if (!TRANS && S_chunks) {
         // the chunk-start state, kept for the backward in the compute type
+        // (as 16 x 16 tiles, stile_index)
         Tin* dst = S_chunks + (static_cast<size_t>(bh) * NC + c) * DK * DV;
         if constexpr (sizeof(Tin) == 4) {
 #pragma unroll
           for (int s = 0; s < RT; ++s)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] = S[s][i];
+            for (int i = 0; i < 4; ++i) dst[stile_index(16 * s + 4 * g + i, colg, DV)] = S[s][i];
         } else {
           // rounded once, then turned onto rows by an identity product (exact):
-          // row 16s + c16, four columns per lane
+          // row 16s + c16, four columns per lane -- one 512-byte tile per store
 #pragma unroll
           for (int s = 0; s < RT; ++s)
-            store4(at(dst, static_cast<uint32_t>((16 * s + c16) * DV + col0 + 4 * g)),
-                   M::mma(M::from_f32(S[s]), ident, zero4()));
+            store4(at(dst, stile_index(16 * s + c16, col0 + 4 * g, DV)), M::mma(M::from_f32(S[s]), ident, zero4()));
         }
       }
 #pragma unroll

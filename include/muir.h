@@ -158,7 +158,9 @@ size_t muir_chunk_fwd_workspace(const muir_dims_t* dims);
  *   S_chunks : [B, H, nc, dk, dv] dtype: the state at the START of every
  *              chunk, rounded once to the input type (kept for
  *              muir_chunk_bwd, which takes the state in that type), or NULL
- *              to skip
+ *              to skip.  Each [dk, dv] state is stored as 16 x 16 tiles:
+ *              element (r, j) is at ((r/16) * (dv/16) + j/16) * 256 +
+ *              (r%16) * 16 + j%16 of its state (each tile row-major).
  *   workspace: device scratch of at least muir_chunk_fwd_workspace(dims)
  *              bytes.  On return it holds the chunk summaries (the
  *              per-chunk solve results; with S_chunks also each chunk's

@@ -57,6 +57,15 @@ def grad_axes(name: str):
     return STATE_AXES if name == "dS0" else SEQ_AXES
 
 
+def untile_states(x):
+    """Saved chunk states (S_chunks) to plain [..., dk, dv]: the library keeps
+    each state as 16 x 16 tiles, element (r, j) at flat position
+    ((r // 16) * (dv // 16) + j // 16) * 256 + (r % 16) * 16 + j % 16."""
+    *lead, dk, dv = x.shape
+    t = x.reshape(*lead, dk // 16, dv // 16, 16, 16)
+    return t.transpose(-3, -2).reshape(*lead, dk, dv)
+
+
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 NAMES = ("q", "k", "v", "log_a", "erase", "write", "gamma")
 

@@ -125,3 +125,18 @@ def test_per_head_error_catches_a_small_head():
     x = y.copy()
     x[0, 0, 1, 0] = 3e-3
     assert abs(rel_err_heads(x, y, (0, 2)) - 3e-3) < 1e-12
+
+
+def test_untile_states_follows_the_documented_tile_layout():
+    """The tests' untile helper inverts the saved-state layout of the header:
+    element (r, j) at ((r/16)(dv/16) + j/16) 256 + (r%16) 16 + j%16."""
+    import torch
+    sys.path.insert(0, HERE)
+    from gpu_util import untile_states
+    dk, dv = 64, 128
+    flat = torch.arange(2 * dk * dv, dtype=torch.float64).reshape(2, dk, dv)
+    plain = untile_states(flat)
+    for r, j in ((0, 0), (5, 17), (16, 0), (63, 127), (31, 100)):
+        want = ((r // 16) * (dv // 16) + j // 16) * 256 + (r % 16) * 16 + j % 16
+        assert plain[0, r, j] == want and plain[1, r, j] == dk * dv + want
+    assert sorted(plain.flatten().tolist()) == flat.flatten().tolist()
