@@ -56,8 +56,9 @@ enum BwdForm { BWD_TWO_SWEEP = 0, BWD_DIRECT = 1, BWD_SUB = 2 };
 
 // Per-chunk scratch, in the compute type.  Form 0: deltas [C][DV], then the
 // state at the start of every 16-token block [C/16][DK][DV] (row-major, as
-// staged).  Form 2: the start state of sub-chunks 1 .. C/64 - 1 [.][DK][DV]
-// (sub-chunk 0 starts from the chunk's own start state).  Form 1: none.
+// staged).  Form 2: the start state of sub-chunks 1 .. C/64 - 1, each
+// [DK][DV] as 16 x 16 tiles like the saved chunk states (sub-chunk 0 starts
+// from the chunk's own start state).  Form 1: none.
 template <typename TC, int FORM>
 __host__ __device__ constexpr size_t bwd_scratch_bytes_tc(int C, int DK, int DV) {
   return FORM == BWD_TWO_SWEEP ? (static_cast<size_t>(C) * DV + static_cast<size_t>(C / 16) * DK * DV) * sizeof(TC)
