@@ -104,18 +104,29 @@ hipError_t launch_fwd_prep(const ChunkShape& s, const void* q, const void* k, co
                            const void* gamma, void* summ, hipStream_t stream);
 
 // Sequential over chunks: o (may be NULL), S_chunks (may be NULL: the
-// chunk-start states in the compute type, [dk][dv] rows), S_T (may be NULL).  With `deltas` (the same summaries, writable) each chunk's deltas are
-// written into its summary.  `split`: scan_split_bytes(s) of workspace.
+// chunk-start states in the compute type, as 16 x 16 tiles, stile_index),
+// S_T (may be NULL).  With `deltas` (the same summaries, writable) each
+// chunk's deltas are written into its summary.  `split`: scan_split_bytes(s)
+// of workspace; when the scan splits into segments it starts with each
+// segment's offset and transition, [dk][dv + dk] fp32 per head and segment,
+// which the reverse scan reads (ftrans).
 hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S0, void* o,
                            void* S_chunks, float* S_T, void* deltas, float* split, hipStream_t stream);
+
+// Only the segment transitions of launch_fwd_scan (into the start of
+// `split`); nothing when the scan does not split.
+hipError_t launch_fwd_trans(const ChunkShape& s, const void* summ, float* split, hipStream_t stream);
 
 // Reverse sequential over chunks: dS_chunks[c] = gradient w.r.t. the state at the
 // END of chunk c, in the compute type, as transposed 16-row tiles: element
 // (r, j) at ((r / 16) * DV + j) * 16 + r % 16 of the chunk's DK * DV block;
-// dS0 (fp32 [dk][dv], may be NULL).
+// dS0 (fp32 [dk][dv], may be NULL).  When the scan splits into segments,
+// `ftrans` holds the forward's segment transitions (the start of the split
+// area of a launch_fwd_scan or launch_fwd_trans on the same summaries; it may
+// be `split` itself, whose transition columns this call leaves unchanged).
 hipError_t launch_bwd_scan(const ChunkShape& s, const void* summ, const void* dO,
                            const float* dS_T, void* dS_chunks, float* dS0, float* split,
-                           hipStream_t stream);
+                           const float* ftrans, hipStream_t stream);
 
 // Chunk-parallel: all input gradients of every chunk (per-token ones in the
 // element type s.gbf16 selects).  `summ` holds the

@@ -216,6 +216,12 @@ muir_status_t bwd_core(const ChunkShape& s, const Inputs& in, const float* S0, c
     summ = nullptr;
     Sc = nullptr;
   }
+  // A split reverse scan takes the forward's segment transitions: from the
+  // forward's workspace (after its summaries) when that is given, else from
+  // the forward scan rerun here, else formed here on their own.
+  const float* ftrans =
+      summ ? reinterpret_cast<const float*>(static_cast<const char*>(summ) + s.nchunks() * s.summary_bytes())
+           : split;
   if (!summ) {
     // the forward's chunk summaries are not given: recompute them
     if (muir::launch_fwd_prep(s, in.x[0], in.x[1], in.x[2], in.x[3], in.x[4], in.x[5], in.x[6], ws, hs) !=
@@ -223,16 +229,20 @@ muir_status_t bwd_core(const ChunkShape& s, const Inputs& in, const float* S0, c
       return MUIR_ERR_HIP;
     mark(hs);
     summ = ws;
+    if (Sc && muir::launch_fwd_trans(s, summ, split, hs) != hipSuccess) return MUIR_ERR_HIP;
   }
   if (!Sc) {
-    // chunk-start states are not given: rerun the forward scan
+    // chunk-start states are not given: rerun the forward scan (it leaves
+    // the segment transitions in `split`)
     void* deltas = s.bwd_direct() ? ws : nullptr;  // summ is ws here
     if (muir::launch_fwd_scan(s, summ, S0, nullptr, S_rec, nullptr, deltas, split, hs) != hipSuccess)
       return MUIR_ERR_HIP;
     mark(hs);
     Sc = S_rec;
+    ftrans = split;
   }
-  if (muir::launch_bwd_scan(s, summ, dO, dS_T, dS_chunks, dS0, split, hs) != hipSuccess) return MUIR_ERR_HIP;
+  if (muir::launch_bwd_scan(s, summ, dO, dS_T, dS_chunks, dS0, split, ftrans, hs) != hipSuccess)
+    return MUIR_ERR_HIP;
   mark(hs);
   if (muir::launch_bwd_chunk(s, in.x[0], in.x[1], in.x[2], in.x[3], in.x[4], in.x[5], in.x[6], summ, Sc,
                              dS_chunks, dO, gr.x[0], gr.x[1], gr.x[2], gr.x[3], gr.x[4], gr.x[5], gr.x[6],

@@ -350,10 +350,15 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
 // these products) and Gamma_C.
 //
 // Segments as in the forward, walked in reverse: with TRANS the kernel runs
-// dS <- (diag(Gamma_C) - W^T Kbar) dS + Q'^T dO over its segment from
-// [0 | I] (dk more columns, whose dO is zero) into trans[head][seg]; without
-// it, the last segment starts from dS_T and segment seg from dS_seg[head][seg]
-// (the gradient at the segment's end), and segment 0 writes dS0.
+// dS <- (diag(Gamma_C) - W^T Kbar) dS + Q'^T dO over its segment from zero
+// and writes the segment's offset E into columns 0 .. DV-1 of
+// trans[head][seg] ([dk][DV + DK] fp32, the forward's layout).  The
+// segment's transition is not formed here: it is the transpose of the
+// forward's, Prod_c M_c^T = (Prod_c M_c)^T with M_c = diag(Gamma_C) - Kbar^T W
+// taken in the opposite order, and seg_combine_kernel reads it from the
+// forward's trans.  Without TRANS, the last segment starts from dS_T and
+// segment seg from dS_seg[head][seg] (the gradient at the segment's end), and
+// segment 0 writes dS0.
 template <typename Tin, int DK, int NW, bool TRANS>
 __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
     int T, int H, int C, const char* __restrict__ summ, size_t summ_bytes,
@@ -384,11 +389,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
   constexpr int PO = words_per_thread<O_WORDS, NTH>();
   constexpr int PG = words_per_thread<G_WORDS, NTH>();
   static_assert(LO >= 32, "dO row segment");
-  constexpr int NCOL = TRANS ? DV + DK : DV;  // state-gradient columns ([dS | P] with TRANS)
+  constexpr int TS = DV + DK;  // row stride of trans
 
   const int NC = T / C;
   const int NSB = C / SB;
-  const int nvb = NCOL / NV;
+  const int nvb = DV / NV;
   const int2 gm = xcd_group(blockIdx.x, nvb, static_cast<int>(gridDim.x) / nvb);
   const int bh = gm.x / nseg;
   const int seg = gm.x - bh * nseg;
@@ -396,8 +401,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
   const int L = (NC + nseg - 1) / nseg;  // chunks per segment
   const int cbeg = min(NC, seg * L);
   const int cend = min(NC, cbeg + L);
-  const bool pcols = TRANS && vb * NV >= DV;  // transition columns: no dO (their loads read tile 0)
-  const int vbu = pcols ? 0 : vb;
   const int b = bh / H;
   const int h = bh - b * H;
   const int tid = threadIdx.x;
@@ -430,7 +433,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
     const uint32_t kofs = part(SP_KB) + static_cast<uint32_t>(sb * SB * LW);
     const uint32_t gofs = part(SP_END);
     const char* dob = reinterpret_cast<const char*>(
-        dO + ((static_cast<size_t>(b) * T + static_cast<size_t>(c) * C + sb * SB) * H + h) * DV + vbu * NV);
+        dO + ((static_cast<size_t>(b) * T + static_cast<size_t>(c) * C + sb * SB) * H + h) * DV + vb * NV);
 #pragma unroll
     for (int k = 0; k < PT; ++k) {
       const int w = min(tid + k * NTH, T_WORDS - 1);
@@ -470,8 +473,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
 #pragma unroll
     for (int k = 0; k < PO; ++k) {
       const int w = min(tid + k * NTH, O_WORDS - 1);
-      const u32x4 zw = {0u, 0u, 0u, 0u};
-      put16<LO, GR>(sDO, w / CO, w % CO, pcols ? zw : rd[k]);
+      put16<LO, GR>(sDO, w / CO, w % CO, rd[k]);
     }
 #pragma unroll
     for (int k = 0; k < PG; ++k) {
@@ -484,17 +486,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
   const size_t sbase = static_cast<size_t>(bh) * DK * DV;
   f32x4 dS[RT];
   {
-    // the segment's end: [0 | I] with TRANS, else dS_T or the segment state
-    const float* src = seg == nseg - 1 ? (dS_T ? dS_T + sbase : nullptr)
-                                       : dS_seg + (static_cast<size_t>(bh) * nseg + seg) * DK * DV;
+    // the segment's end: zero with TRANS, else dS_T or the segment state
+    const float* src = TRANS ? nullptr
+                       : seg == nseg - 1 ? (dS_T ? dS_T + sbase : nullptr)
+                                         : dS_seg + (static_cast<size_t>(bh) * nseg + seg) * DK * DV;
 #pragma unroll
     for (int s = 0; s < RT; ++s)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * s + 4 * g + i;
-        if constexpr (TRANS) dS[s][i] = (pcols && row == colg - DV) ? 1.f : 0.f;
-        else dS[s][i] = src ? src[static_cast<size_t>(row) * DV + colg] : 0.f;
-      }
+      for (int i = 0; i < 4; ++i) dS[s][i] = src ? src[static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] : 0.f;
   }
   frag dSf[RT];
   f32x4 Z[RT];
@@ -560,11 +559,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
     }
   }
   if constexpr (TRANS) {
-    float* dst = trans + (static_cast<size_t>(bh) * nseg + seg) * DK * NCOL;
+    float* dst = trans + (static_cast<size_t>(bh) * nseg + seg) * DK * TS;
 #pragma unroll
     for (int s = 0; s < RT; ++s)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * s + 4 * g + i) * NCOL + colg] = dS[s][i];
+      for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * s + 4 * g + i) * TS + colg] = dS[s][i];
   } else if (dS0 && seg == 0) {
 #pragma unroll
     for (int s = 0; s < RT; ++s)
@@ -574,58 +573,91 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// The segment recurrence of a split scan: x_next = P_g x + E_g with
-// [E_g | P_g] = trans[head][g] ([dk][DV + DK] fp32, from a TRANS scan),
-// applied from x0 (NULL: zero) over the segments in order (reverse: from the
-// last segment down); the value that starts each later segment (reverse: each
-// earlier one) goes to xseg[head][segment] ([dk][dv] fp32).  fp32 MFMA; four
-// waves of 16 columns per workgroup.
-template <int DK>
-__global__ __launch_bounds__(256) void seg_combine_kernel(int nseg, int reverse, const float* __restrict__ x0,
-                                                          const float* __restrict__ trans,
-                                                          float* __restrict__ xseg) {
+// The segment recurrence of a split scan, applied from x0 (NULL: zero) over
+// the segments in order (reverse: from the last segment down); the value that
+// starts each later segment (reverse: each earlier one) goes to
+// xseg[head][segment] ([dk][dv] fp32).  E and P point to [head][g][dk][DV + DK]
+// fp32 arrays (the TRANS scans' layout) holding the offset E_g in columns
+// 0 .. DV-1 and, in P, the forward transition P_g in columns DV .. DV+DK-1:
+// forward x_next = P_g x + E_g, reverse x_next = P_g^T x + E_g.  fp32 MFMA.
+//
+// The recurrence is a chain of nseg - 1 dependent products, so its length is
+// what counts: one workgroup per (head, 16 columns) and one wave per 16 rows,
+// each forming its 16 x 16 tile of the next value (16 fp32 MFMA products per
+// 16-deep step of the contraction); the tiles meet in LDS, where every wave
+// reads the whole column block as its right operand for the next segment.
+// Each wave's P rows and E values of the next segment are loaded while the
+// current one is formed.  The products are summed in the same order as by a
+// single wave holding the whole column block.
+template <int DK, bool REV>
+__global__ __launch_bounds__(4 * DK) void seg_combine_kernel(int nseg, const float* __restrict__ x0,
+                                                             const float* __restrict__ E,
+                                                             const float* __restrict__ P,
+                                                             float* __restrict__ xseg) {
   typedef MM<float> MF;
   constexpr int DV = DK;
   constexpr int RT = DK / 16;
   constexpr int NCOL = DV + DK;
-  const int nvb = DV / 64;
-  const int bh = blockIdx.x / nvb;
-  const int vb = blockIdx.x - bh * nvb;
+  constexpr int NVB = DV / 16;
+  const int bh = blockIdx.x / NVB;
+  const int vb = blockIdx.x - bh * NVB;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int s = threadIdx.x >> 6;  // this wave's row tile
   const int g = lane >> 4;
   const int c16 = lane & 15;
-  const int colg = vb * 64 + 16 * wave + c16;
-  f32x4 X[RT];
+  const int colg = vb * 16 + c16;
+  // the current value, per row tile in the accumulator layout, double-buffered
+  __shared__ f32x4 sX[2][RT][64];
+
+  // the map applied at step st: rows 16s + c16, columns 16kk + 4g .. + 3 of
+  // P_g (reverse: of P_g^T, four loads of 16 consecutive columns of P_g) as
+  // the left operand, and E_g at rows 16s + 4g + i, column colg
+  auto load_step = [&](int st, f32x4 (&a)[RT], f32x4& e) {
+    const int gs = REV ? nseg - 1 - st : st;
+    const size_t base = (static_cast<size_t>(bh) * nseg + gs) * DK * NCOL;
+    const float* pg = P + base + DV;
+    if constexpr (REV) {
 #pragma unroll
-  for (int s = 0; s < RT; ++s)
+      for (int kk = 0; kk < RT; ++kk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[kk][j] = pg[static_cast<size_t>(16 * kk + 4 * g + j) * NCOL + 16 * s + c16];
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < RT; ++kk)
+        a[kk] = *reinterpret_cast<const f32x4*>(pg + static_cast<size_t>(16 * s + c16) * NCOL + 16 * kk + 4 * g);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[i] = E[base + static_cast<size_t>(16 * s + 4 * g + i) * NCOL + colg];
+  };
+
+  f32x4 a0[RT], e0;
+  load_step(0, a0, e0);  // (nseg >= 2 whenever the kernel is launched)
+  {
+    f32x4 x;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      X[s][i] = x0 ? x0[static_cast<size_t>(bh) * DK * DV + static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] : 0.f;
+      x[i] = x0 ? x0[static_cast<size_t>(bh) * DK * DV + static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] : 0.f;
+    sX[0][s][lane] = x;
+  }
+  __syncthreads();
+  int cur = 0;
 #pragma unroll 1
   for (int st = 0; st + 1 < nseg; ++st) {
-    const int gs = reverse ? nseg - 1 - st : st;  // the segment whose map applies
-    const int gd = reverse ? gs - 1 : gs + 1;     // the segment its result starts
-    const float* tr = trans + (static_cast<size_t>(bh) * nseg + gs) * DK * NCOL;
-    f32x4 Y[RT];
+    f32x4 a1[RT], e1;
+    load_step(st + 2 < nseg ? st + 1 : st, a1, e1);  // the next step's map (clamped at the end)
+    f32x4 y = e0;
 #pragma unroll
-    for (int s = 0; s < RT; ++s) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Y[s][i] = tr[static_cast<size_t>(16 * s + 4 * g + i) * NCOL + colg];
-#pragma unroll
-      for (int kk = 0; kk < RT; ++kk) {
-        // P rows 16s + c16, columns 16kk + 4g..4g+3 as the left operand
-        const f32x4 a = *reinterpret_cast<const f32x4*>(tr + static_cast<size_t>(16 * s + c16) * NCOL + DV + 16 * kk + 4 * g);
-        Y[s] = MF::mma(a, X[kk], Y[s]);
-      }
-    }
+    for (int kk = 0; kk < RT; ++kk) y = MF::mma(a0[kk], sX[cur][kk][lane], y);
+    const int gd = REV ? nseg - 2 - st : st + 1;  // the segment this value starts
     float* dst = xseg + (static_cast<size_t>(bh) * nseg + gd) * DK * DV;
 #pragma unroll
-    for (int s = 0; s < RT; ++s) {
-      X[s] = Y[s];
+    for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] = y[i];
+    sX[cur ^ 1][s][lane] = y;
+    __syncthreads();
+    cur ^= 1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] = X[s][i];
-    }
+    for (int kk = 0; kk < RT; ++kk) a0[kk] = a1[kk];
+    e0 = e1;
   }
 }
 
@@ -636,6 +668,16 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(int nseg, int reverse,
 // (ChunkShape::scan_segments): each segment's transition, the segment
 // recurrence, then every segment's scan from its start -- else one wave (16
 // columns) per workgroup.
+// Each segment's offset and transition, [E_g | P_g], into trans.
+template <typename TT, int DD>
+void fwd_trans_typed(const ChunkShape& s, const void* summ, float* trans, hipStream_t stream) {
+  const int heads = s.B * s.H;
+  const int nseg = s.scan_segments();
+  hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, true>), dim3(heads * nseg * (2 * DD / 64)), dim3(256), 0, stream,
+                     s.T, s.H, s.C, (const char*)summ, s.summary_bytes(), (const float*)nullptr, (TT*)nullptr,
+                     (TT*)nullptr, (float*)nullptr, (char*)nullptr, size_t(0), nseg, (const float*)nullptr, trans);
+}
+
 template <typename TT, int DD>
 hipError_t fwd_scan_typed(const ChunkShape& s, const void* summ, const float* S0, void* o,
                           void* S_chunks_v, float* S_T, void* deltas, float* split, hipStream_t stream) {
@@ -646,11 +688,9 @@ hipError_t fwd_scan_typed(const ChunkShape& s, const void* summ, const float* S0
   if (nseg > 1) {
     float* trans = split;
     float* sseg = split + static_cast<size_t>(heads) * nseg * DD * (2 * DD);
-    hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, true>), dim3(heads * nseg * (2 * DD / 64)), dim3(256), 0,
-                       stream, s.T, s.H, s.C, (const char*)summ, sb, S0, (TT*)nullptr, (TT*)nullptr,
-                       (float*)nullptr, (char*)nullptr, size_t(0), nseg, (const float*)nullptr, trans);
-    hipLaunchKernelGGL((seg_combine_kernel<DD>), dim3(heads * (DD / 64)), dim3(256), 0, stream, nseg, 0, S0,
-                       (const float*)trans, sseg);
+    fwd_trans_typed<TT, DD>(s, summ, trans, stream);
+    hipLaunchKernelGGL((seg_combine_kernel<DD, false>), dim3(heads * (DD / 16)), dim3(4 * DD), 0, stream, nseg, S0,
+                       (const float*)trans, (const float*)trans, sseg);
     hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, false>), dim3(heads * nseg * (DD / 64)), dim3(256), 0, stream,
                        s.T, s.H, s.C, (const char*)summ, sb, S0, (TT*)o, S_chunks, S_T, (char*)deltas,
                        s.dl_offset(), nseg, (const float*)sseg, (float*)nullptr);
@@ -668,18 +708,20 @@ hipError_t fwd_scan_typed(const ChunkShape& s, const void* summ, const float* S0
 
 template <typename TT, int DD>
 hipError_t bwd_scan_typed(const ChunkShape& s, const void* summ, const void* dO, const float* dS_T,
-                          void* dS_chunks, float* dS0, float* split, hipStream_t stream) {
+                          void* dS_chunks, float* dS0, float* split, const float* ftrans, hipStream_t stream) {
   const int heads = s.B * s.H;
   const int nseg = s.scan_segments();
   const size_t sb = s.summary_bytes();
   if (nseg > 1) {
+    // each segment's offset into the E columns of trans; the transitions are
+    // the transposes of the forward's, read from ftrans
     float* trans = split;
     float* sseg = split + static_cast<size_t>(heads) * nseg * DD * (2 * DD);
-    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, true>), dim3(heads * nseg * (2 * DD / 64)), dim3(256), 0,
-                       stream, s.T, s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks,
-                       (float*)nullptr, nseg, (const float*)nullptr, trans);
-    hipLaunchKernelGGL((seg_combine_kernel<DD>), dim3(heads * (DD / 64)), dim3(256), 0, stream, nseg, 1, dS_T,
-                       (const float*)trans, sseg);
+    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, true>), dim3(heads * nseg * (DD / 64)), dim3(256), 0, stream,
+                       s.T, s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks, (float*)nullptr,
+                       nseg, (const float*)nullptr, trans);
+    hipLaunchKernelGGL((seg_combine_kernel<DD, true>), dim3(heads * (DD / 16)), dim3(4 * DD), 0, stream, nseg, dS_T,
+                       (const float*)trans, ftrans, sseg);
     hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, false>), dim3(heads * nseg * (DD / 64)), dim3(256), 0, stream,
                        s.T, s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks, dS0, nseg,
                        (const float*)sseg, (float*)nullptr);
@@ -706,15 +748,27 @@ hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S
                      : fwd_scan_typed<float, 64>(s, summ, S0, o, S_chunks, S_T, deltas, split, stream);
 }
 
+hipError_t launch_fwd_trans(const ChunkShape& s, const void* summ, float* split, hipStream_t stream) {
+  if (s.B * s.H == 0 || s.scan_segments() < 2) return hipSuccess;
+  if (s.bf16) {
+    if (s.DK == 128) fwd_trans_typed<uint16_t, 128>(s, summ, split, stream);
+    else fwd_trans_typed<uint16_t, 64>(s, summ, split, stream);
+  } else {
+    if (s.DK == 128) fwd_trans_typed<float, 128>(s, summ, split, stream);
+    else fwd_trans_typed<float, 64>(s, summ, split, stream);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_scan(const ChunkShape& s, const void* summ, const void* dO, const float* dS_T,
-                           void* dS_chunks, float* dS0, float* split, hipStream_t stream) {
+                           void* dS_chunks, float* dS0, float* split, const float* ftrans, hipStream_t stream) {
   if (s.B * s.H == 0) return hipSuccess;
   if (s.bf16) {
-    return s.DK == 128 ? bwd_scan_typed<uint16_t, 128>(s, summ, dO, dS_T, dS_chunks, dS0, split, stream)
-                       : bwd_scan_typed<uint16_t, 64>(s, summ, dO, dS_T, dS_chunks, dS0, split, stream);
+    return s.DK == 128 ? bwd_scan_typed<uint16_t, 128>(s, summ, dO, dS_T, dS_chunks, dS0, split, ftrans, stream)
+                       : bwd_scan_typed<uint16_t, 64>(s, summ, dO, dS_T, dS_chunks, dS0, split, ftrans, stream);
   }
-  return s.DK == 128 ? bwd_scan_typed<float, 128>(s, summ, dO, dS_T, dS_chunks, dS0, split, stream)
-                     : bwd_scan_typed<float, 64>(s, summ, dO, dS_T, dS_chunks, dS0, split, stream);
+  return s.DK == 128 ? bwd_scan_typed<float, 128>(s, summ, dO, dS_T, dS_chunks, dS0, split, ftrans, stream)
+                     : bwd_scan_typed<float, 64>(s, summ, dO, dS_T, dS_chunks, dS0, split, ftrans, stream);
 }
 
 }  // namespace muir

@@ -164,9 +164,10 @@ size_t muir_chunk_fwd_workspace(const muir_dims_t* dims);
  *   workspace: device scratch of at least muir_chunk_fwd_workspace(dims)
  *              bytes.  On return it holds the chunk summaries (the
  *              per-chunk solve results; with S_chunks also each chunk's
- *              deltas when dtype is MUIR_BF16); a caller
- *              that keeps it unchanged may pass it to muir_chunk_bwd as
- *              `summaries`, together with S_chunks.
+ *              deltas when dtype is MUIR_BF16) and, when few heads make the
+ *              state scan split the sequence into segments, each segment's
+ *              state transition; a caller that keeps it unchanged may pass
+ *              it to muir_chunk_bwd as `summaries`, together with S_chunks.
  */
 muir_status_t muir_chunk_fwd(const muir_dims_t* dims,
                              const void* q, const void* k, const void* v,
@@ -215,9 +216,9 @@ size_t muir_chunk_bwd_workspace(const muir_dims_t* dims);
  *   S_chunks : [B, H, nc, dk, dv] dtype from muir_chunk_fwd, or NULL
  *              (then recomputed inside, in the workspace)
  *   summaries: the workspace of a muir_chunk_fwd call on the same inputs,
- *              dims and S0, unchanged since (the chunk summaries it left
- *              there), or NULL (then recomputed inside, in the workspace);
- *              read only.  With dtype MUIR_BF16 the backward also reads the
+ *              dims and S0, unchanged since (the chunk summaries and segment
+ *              transitions it left there), or NULL (then recomputed inside,
+ *              in the workspace); read only.  With dtype MUIR_BF16 the backward also reads the
  *              chunk deltas that the forward keeps when it saves S_chunks:
  *              there summaries and S_chunks are used only together, from the
  *              same muir_chunk_fwd call, and both are recomputed when either

@@ -161,24 +161,36 @@ def test_bwd_with_saved_summaries_equals_recompute(C):
         assert torch.equal(g2[n], ref[n]), n
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_split_scan_matches_oracle(dtype):
+@pytest.mark.parametrize("dtype,d", [("f32", 128), ("bf16", 128), ("f32", 64), ("bf16", 64)])
+def test_split_scan_matches_oracle(dtype, d):
     """One head over 64 chunks: the state scans split into 8 segments (each
     segment's transition, the segment recurrence, then each segment's scan
-    from its start), forward and backward, against the oracle."""
+    from its start), forward and backward, against the oracle.  The reverse
+    scan takes the forward's segment transitions, transposed: from the
+    forward's workspace, from the forward scan it reruns, or (fp32, chunk
+    states given without summaries) formed on their own; every way gives the
+    same gradients, bit for bit."""
     m = _lib()
-    B, T, H, d, C = 1, 4096, 1, 128, 64
+    B, T, H, C = 1, 4096, 1, 64
     inp = muir_inputs.seq_inputs(B, T, H, d, d, dtype=dtype, decay="channel", seed=12, S0_scale=0.1,
                                  with_dO=True, with_dST=True)
     dv = to_dev(inp)
-    o, S_T, Sc = m.muir_chunk_fwd(*(dv[n] for n in NAMES), dv["S0"], chunk=C, save_states=True)
-    g = m.muir_chunk_bwd(*(dv[n] for n in NAMES), dv["dO"], S0=dv["S0"], S_chunks=Sc, dS_T=dv["dS_T"], chunk=C)
+    code = m.MUIR_F32 if dtype == "f32" else m.MUIR_BF16
+    ws = torch.empty(m.muir_chunk_fwd_workspace(B, T, H, d, d, C, code), dtype=torch.uint8, device="cuda")
+    o, S_T, Sc = m.muir_chunk_fwd(*(dv[n] for n in NAMES), dv["S0"], chunk=C, save_states=True, workspace=ws)
+    bargs = (*(dv[n] for n in NAMES), dv["dO"])
+    g = m.muir_chunk_bwd(*bargs, S0=dv["S0"], S_chunks=Sc, summaries=ws, dS_T=dv["dS_T"], chunk=C)
+    others = [m.muir_chunk_bwd(*bargs, S0=dv["S0"], S_chunks=Sc, dS_T=dv["dS_T"], chunk=C),
+              m.muir_chunk_bwd(*bargs, S0=dv["S0"], dS_T=dv["dS_T"], chunk=C)]
     torch.cuda.synchronize()
+    for g2 in others:
+        for n in GRADS:
+            assert torch.equal(g[n], g2[n]), n
     o_ref, S_ref = oracle.fwd(*(inp[n] for n in NAMES), S0=inp["S0"])
     ref = oracle.bwd(*(inp[n] for n in NAMES), inp["dO"], S0=inp["S0"], dS_T=inp["dS_T"])
     errs = {"o": err2(o, o_ref, SEQ_AXES), "S_T": err2(S_T, S_ref, STATE_AXES)}
     errs.update({n: err2(g[n], ref[n], grad_axes(n)) for n in GRADS})
-    _say(f"split scan {dtype}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    _say(f"split scan {dtype} d={d}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     for n, e in errs.items():
         assert e <= TOL[dtype], (n, e)
 
