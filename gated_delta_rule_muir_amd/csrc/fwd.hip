@@ -44,9 +44,6 @@ struct SummaryView {
   TC* KbT;   // [DK][C]
   TC* UtT;   // [DV][C]
   TC* OtT;   // [DV][C]
-  TC* Wt;    // [DK][C]
-  TC* Qt;    // [DK][C]
-  TC* Kb;    // [C][DK]
   float* gC; // [DK]
   TC* TP;    // [C/16][2][16][16]: T_II, P_II of each 16-token block
   __device__ SummaryView(char* base, int C, int DK, int DV) {
@@ -56,9 +53,6 @@ struct SummaryView {
     KbT = b + summary_part(SP_KBT, C, DK, DV);
     UtT = b + summary_part(SP_UTT, C, DK, DV);
     OtT = b + summary_part(SP_OTT, C, DK, DV);
-    Wt = b + summary_part(SP_WT, C, DK, DV);
-    Qt = b + summary_part(SP_QT, C, DK, DV);
-    Kb = b + summary_part(SP_KB, C, DK, DV);
     gC = reinterpret_cast<float*>(b + summary_part(SP_END, C, DK, DV));
     TP = reinterpret_cast<TC*>(gC + DK);
   }
@@ -284,8 +278,6 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
     store4(&sR[bb][DV + ej][4 * part], ktT);
     store4(&sQh[bb][ej][4 * part], qhT);
     store4(out.KbT + tpart_index(ej, r0 + 4 * part, DK), kbT);
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) out.Kb[static_cast<size_t>(r0 + 4 * part + rr) * DK + ej] = M::cvt(kbT[rr]);
   };
 
   // T_II = (I + A_II)^-1 from A_II (both lane layouts, see neumann16), with
@@ -432,8 +424,6 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
       } else {
         const int j = colg - DV;
         const f32x4 qv = load4(&sQh[bb][j][4 * g]) - op;
-        store4(out.Wt + tpart_index(j, r0 + 4 * g, DK), uw);
-        store4(out.Qt + tpart_index(j, r0 + 4 * g, DK), qv);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           sStage[4 * g + i][j] = M::cvt(uw[i]);

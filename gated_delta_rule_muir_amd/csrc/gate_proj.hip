@@ -146,10 +146,9 @@ __device__ __forceinline__ void transpose_block(const uint4 (&in)[4], uint4 (&ou
 // as its row operand, so each lane ends with four consecutive output columns
 // of one row (lane (g, c16): row c16, columns 4g .. 4g+3 of each 16 x 16
 // tile) and the epilogue stores straight from registers.
-template <typename TC, int BM, int BN, bool A_KC, bool B_KC, int EPI>
+template <typename TC, int BM, int BN, bool A_KC, bool B_KC, int EPI, int BK>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmBatch batch) {
   typedef GF<TC> F;
-  constexpr int BK = GemmStep<TC>::BK;
   constexpr int E = 16 / sizeof(TC);  // elements per 16-byte word
   constexpr int LDK = BK + F::PAD;    // LDS row pitch of an operand tile (elements)
   constexpr int TM = BM / 32, TN = BN / 32;  // 16 x 16 tiles per wave
@@ -703,13 +702,13 @@ __global__ __launch_bounds__(QK_THREADS) void qk_norm_bwd_kernel(const TC* __res
   }
 }
 
-template <typename TC, int BM, int BN, bool A_KC, bool B_KC, int EPI>
+template <typename TC, int BM, int BN, bool A_KC, bool B_KC, int EPI, int BK = GemmStep<TC>::BK>
 hipError_t run_gemm(const GemmBatch& b, hipStream_t stream) {
   int tiles = 0;
   for (int i = 0; i < b.n; ++i) tiles = std::max(tiles, ((b.p[i].M + BM - 1) / BM) * ((b.p[i].N + BN - 1) / BN));
   if (tiles == 0) return hipSuccess;
   const int grid = (tiles + 7) / 8 * 8;  // whole rounds of the 8 XCDs
-  hipLaunchKernelGGL((gemm_kernel<TC, BM, BN, A_KC, B_KC, EPI>), dim3(grid, b.n * b.ksplit), dim3(GEMM_THREADS), 0,
+  hipLaunchKernelGGL((gemm_kernel<TC, BM, BN, A_KC, B_KC, EPI, BK>), dim3(grid, b.n * b.ksplit), dim3(GEMM_THREADS), 0,
                      stream, b);
   return hipGetLastError();
 }

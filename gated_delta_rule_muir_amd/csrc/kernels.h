@@ -8,22 +8,19 @@
 namespace muir {
 
 // Parts of a chunk summary, in order; offsets in compute-type elements.
-//   W [C][DK], Q' [C][DK], Kbar^T [DK][C], U~^T [DV][C], O~^T [DV][C],
-//   W^T [DK][C], Q'^T [DK][C], Kbar [C][DK]
-// (W, Q' and Kbar in both orientations: the forward scan contracts them over
-// key channels, the reverse scan over tokens), then Gamma_C [DK] fp32, the
+//   W [C][DK], Q' [C][DK], Kbar^T [DK][C], U~^T [DV][C], O~^T [DV][C]
+// (the forward scan's orientations; the reverse scan contracts W, Q' and
+// Kbar the other way and reads them transposed from LDS), then Gamma_C [DK] fp32, the
 // leaf blocks T_II, P_II [C/16][2][16][16] (compute type) and the chunk's
 // deltas U~ - W S [C][DV] (compute type; written by the forward scan when it
 // saves the chunk states and the direct backward is used, see bwd_direct).
-enum SummaryPart { SP_W, SP_QP, SP_KBT, SP_UTT, SP_OTT, SP_WT, SP_QT, SP_KB, SP_END };
+enum SummaryPart { SP_W, SP_QP, SP_KBT, SP_UTT, SP_OTT, SP_END };
 __host__ __device__ constexpr size_t summary_part(int part, int C, int DK, int DV) {
   return part <= SP_UTT ? static_cast<size_t>(part) * C * DK
-         : part <= SP_WT ? static_cast<size_t>(3) * C * DK + static_cast<size_t>(part - SP_UTT) * C * DV
-                         : static_cast<size_t>(3) * C * DK + static_cast<size_t>(2) * C * DV +
-                               static_cast<size_t>(part - SP_WT) * C * DK;
+                        : static_cast<size_t>(3) * C * DK + static_cast<size_t>(part - SP_UTT) * C * DV;
 }
 
-// The transposed parts (Kbar^T, U~^T, O~^T, W^T, Q'^T: logically [D][C]) are
+// The transposed parts (Kbar^T, U~^T, O~^T: logically [D][C]) are
 // stored as 16-token tiles [C/16][D][16], so that each 16-token block's tile
 // is one contiguous run: element (row d, token t) is at this index.
 __host__ __device__ constexpr uint32_t tpart_index(int d, int t, int D) {

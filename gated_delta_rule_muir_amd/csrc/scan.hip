@@ -56,6 +56,41 @@ template <int L, int G> __device__ __forceinline__ void put16(char* tile, int ro
   }
 }
 
+// Tiles read transposed (the reverse scan): rows r hold the forward's
+// orientation, and a fragment needs, in lane (c16, g), the four values at rows
+// k0 + 4g .. k0 + 4g + 3 of column n0 + c16 -- the MFMA operand whose
+// contraction runs along the rows.
+//   bf16: one ds_read_b64_tr_b16.  Lane l of each 16-lane group reads the
+//   8 bytes at row k0 + 4g + l/4, columns n0 + 4 (l%4) .. + 3; the
+//   instruction hands lane c16 of the group the four values of column
+//   n0 + c16, one from each of the four rows, in row order.  Two groups (32
+//   lanes, eight rows x 32 bytes) are served together from 256 bytes of banks
+//   (a timing loop at full LDS load: no slower than 64 lanes reading 512
+//   contiguous bytes), so rows of 128 bytes or more are padded by 32 bytes:
+//   a pitch of an odd number of 32-byte units puts eight consecutive rows'
+//   pieces on distinct banks.  (Rows of 256 bytes XOR-permuted by 4 (row % 4)
+//   granules measured 20% slower, rows padded by 16 bytes the same.)
+//   fp32: four 4-byte reads, unpadded rows.
+template <int SZ> constexpr int tpitch(int L) { return SZ == 2 && L >= 128 ? L + 32 : L; }
+// Writes the 16-byte word c of row `row` of a transposed-read tile of pitch P.
+template <int P> __device__ __forceinline__ void put_t(char* tile, int row, int c, u32x4 w) {
+  *reinterpret_cast<u32x4*>(tile + row * P + 16 * c) = w;
+}
+template <typename TC, int P> __device__ __forceinline__ typename MM<TC>::frag frag_t(const char* tile, int k0, int n0,
+                                                                                   int lane) {
+  const int g = lane >> 4, l = lane & 15;
+  if constexpr (sizeof(TC) == 2) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(tile + (k0 + 4 * g + (l >> 2)) * P + 2 * (n0 + 4 * (l & 3))));
+  } else {
+    f32x4 a;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const float*>(tile + (k0 + 4 * g + t) * P + 4 * (n0 + l));
+    return a;
+  }
+}
+
 // Workgroup id -> (group, member): the nvb workgroups of one (head, segment)
 // read the same chunk summaries, so they are placed on one XCD (consecutive
 // workgroup ids go round-robin over the 8 XCDs, each with its own L2) and
@@ -345,9 +380,9 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Backward, on the same summaries: reads W^T [DK][C], Q'^T [DK][C] and
-// Kbar [C][DK] (the orientations whose contraction index is contiguous for
-// these products) and Gamma_C.
+// Backward, on the same summaries: reads W [C][DK], Q' [C][DK], Kbar^T and
+// Gamma_C, the forward scan's operands, and takes W^T, Q'^T and Kbar as
+// transposed fragment reads of the staged tiles (frag_t).
 //
 // Segments as in the forward, walked in reverse: with TRANS the kernel runs
 // dS <- (diag(Gamma_C) - W^T Kbar) dS + Q'^T dO over its segment from zero
@@ -374,18 +409,19 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
   constexpr int SZ = sizeof(TC);
   constexpr int GR = SZ == 2 ? 8 : 16;  // LDS swizzle granule: the fragment read size
   constexpr int SB = scan_unit<TC, NW>();
-  constexpr int LW = DK * SZ;       // bytes per Kbar row
-  constexpr int LK = SB * SZ;       // bytes per unit segment of a W^T / Q'^T row
+  constexpr int LW = DK * SZ;       // bytes per W / Q' row
+  constexpr int LK = SB * SZ;       // bytes per unit segment of a Kbar^T row
+  constexpr int PWT = tpitch<SZ>(LW), PKT = tpitch<SZ>(LK);  // their LDS pitches
   constexpr int LO = NV * SZ;       // bytes per dO row segment of this workgroup
   constexpr int CW = LW / 16;
   constexpr int CK = LK / 16;
   constexpr int CO = LO / 16;
-  constexpr int K_WORDS = SB * CW;  // Kbar
-  constexpr int T_WORDS = DK * CK;  // W^T, also Q'^T
+  constexpr int W_WORDS = SB * CW;  // W, also Q'
+  constexpr int K_WORDS = DK * CK;  // Kbar^T
   constexpr int O_WORDS = SB * CO;
   constexpr int G_WORDS = DK / 4;
   constexpr int PK = words_per_thread<K_WORDS, NTH>();
-  constexpr int PT = words_per_thread<T_WORDS, NTH>();
+  constexpr int PW = words_per_thread<W_WORDS, NTH>();
   constexpr int PO = words_per_thread<O_WORDS, NTH>();
   constexpr int PG = words_per_thread<G_WORDS, NTH>();
   static_assert(LO >= 32, "dO row segment");
@@ -410,14 +446,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
   const int c16 = lane & 15;
   const int colg = vb * NV + 16 * wave + c16;
 
-  __shared__ __attribute__((aligned(16))) char sWt[DK * LK];
-  __shared__ __attribute__((aligned(16))) char sQt[DK * LK];
-  __shared__ __attribute__((aligned(16))) char sKb[SB * LW];
+  __shared__ __attribute__((aligned(16))) char sW[SB * PWT];   // read transposed (frag_t)
+  __shared__ __attribute__((aligned(16))) char sQ[SB * PWT];   // read transposed
+  __shared__ __attribute__((aligned(16))) char sKt[DK * PKT];  // read transposed
   __shared__ __attribute__((aligned(16))) char sDO[SB * LO];
   __shared__ __attribute__((aligned(16))) float sgC[DK];
 
   const char* hsum = summ + static_cast<size_t>(bh) * NC * summ_bytes;
-  u32x4 rt[PT], rq[PT], rk[PK], rd[PO], rg[PG];
+  u32x4 rw[PW], rq[PW], rk[PK], rd[PO], rg[PG];
 
   // unit u walks the segment's chunks in reverse, and each chunk's units in reverse
   auto unit_c = [&](int u) { return cend - 1 - u / NSB; };
@@ -428,23 +464,23 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
     const int sb = unit_sb(u);
     const char* base = hsum + static_cast<size_t>(c) * summ_bytes;
     auto part = [&](int p) { return static_cast<uint32_t>(summary_part(p, C, DK, DV) * SZ); };
-    const uint32_t tofs = part(SP_WT);  // (16-token tiles, as in the forward scan)
-    const uint32_t qofs = part(SP_QT);
-    const uint32_t kofs = part(SP_KB) + static_cast<uint32_t>(sb * SB * LW);
+    const uint32_t wofs = part(SP_W) + static_cast<uint32_t>(sb * SB * LW);
+    const uint32_t qofs = part(SP_QP) + static_cast<uint32_t>(sb * SB * LW);
+    const uint32_t kofs = part(SP_KBT);  // (16-token tiles, as in the forward scan)
     const uint32_t gofs = part(SP_END);
     const char* dob = reinterpret_cast<const char*>(
         dO + ((static_cast<size_t>(b) * T + static_cast<size_t>(c) * C + sb * SB) * H + h) * DV + vb * NV);
 #pragma unroll
-    for (int k = 0; k < PT; ++k) {
-      const int w = min(tid + k * NTH, T_WORDS - 1);
-      const uint32_t r = static_cast<uint32_t>(tpart_index(w / CK, sb * SB + (w % CK) * (16 / SZ), DK) * SZ);
-      rt[k] = *reinterpret_cast<const u32x4*>(at(base, tofs + r));
-      rq[k] = *reinterpret_cast<const u32x4*>(at(base, qofs + r));
+    for (int k = 0; k < PW; ++k) {
+      const int w = min(tid + k * NTH, W_WORDS - 1);
+      rw[k] = *reinterpret_cast<const u32x4*>(at(base, wofs + 16 * w));
+      rq[k] = *reinterpret_cast<const u32x4*>(at(base, qofs + 16 * w));
     }
 #pragma unroll
     for (int k = 0; k < PK; ++k) {
       const int w = min(tid + k * NTH, K_WORDS - 1);
-      rk[k] = *reinterpret_cast<const u32x4*>(at(base, kofs + 16 * w));
+      const uint32_t r = static_cast<uint32_t>(tpart_index(w / CK, sb * SB + (w % CK) * (16 / SZ), DK) * SZ);
+      rk[k] = *reinterpret_cast<const u32x4*>(at(base, kofs + r));
     }
 #pragma unroll
     for (int k = 0; k < PO; ++k) {
@@ -460,15 +496,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
 
   auto commit = [&]() {
 #pragma unroll
-    for (int k = 0; k < PT; ++k) {
-      const int w = min(tid + k * NTH, T_WORDS - 1);
-      put16<LK, GR>(sWt, w / CK, w % CK, rt[k]);
-      put16<LK, GR>(sQt, w / CK, w % CK, rq[k]);
+    for (int k = 0; k < PW; ++k) {
+      const int w = min(tid + k * NTH, W_WORDS - 1);
+      put_t<PWT>(sW, w / CW, w % CW, rw[k]);
+      put_t<PWT>(sQ, w / CW, w % CW, rq[k]);
     }
 #pragma unroll
     for (int k = 0; k < PK; ++k) {
       const int w = min(tid + k * NTH, K_WORDS - 1);
-      put16<LW, GR>(sKb, w / CW, w % CW, rk[k]);
+      put_t<PKT>(sKt, w / CK, w % CK, rk[k]);
     }
 #pragma unroll
     for (int k = 0; k < PO; ++k) {
@@ -525,30 +561,58 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
     __syncthreads();
     // (the unit's token tiles fully unrolled: their X products are independent,
     // so their MFMA chains interleave)
+    constexpr int NM = SB / 16;
+    if constexpr (SZ == 2 && NM % 2 == 0) {
+      // bf16: token tiles in pairs, each pair of 16-deep products (two key
+      // tiles for X, two token tiles for Z) issued as one 32-deep product
 #pragma unroll
-    for (int m = 0; m < SB / 16; ++m) {
-      // X = Kbar_m dS_next (16 tokens x this wave's 16 columns)
-      f32x4 X0 = zero4(), X1 = zero4();  // even and odd key tiles: two independent chains
+      for (int m = 0; m < NM; m += 2) {
+        frag dof[2], xf[2];
 #pragma unroll
-      for (int s = 0; s < RT; s += 2) {
-        X0 = M::mma(M::load(reinterpret_cast<const TC*>(sKb + swz<LW, GR>(16 * m + c16, (16 * s + 4 * g) * SZ))), dSf[s],
-                    X0);
-        X1 = M::mma(M::load(reinterpret_cast<const TC*>(sKb + swz<LW, GR>(16 * m + c16, (16 * (s + 1) + 4 * g) * SZ))),
-                    dSf[s + 1], X1);
+        for (int h = 0; h < 2; ++h) {
+          // X = Kbar_{m+h} dS_next (16 tokens x this wave's 16 columns)
+          f32x4 X = zero4();
+#pragma unroll
+          for (int s = 0; s < RT; s += 2)
+            X = M::mma2(frag_t<TC, PKT>(sKt, 16 * s, 16 * (m + h), lane), dSf[s],
+                        frag_t<TC, PKT>(sKt, 16 * (s + 1), 16 * (m + h), lane), dSf[s + 1], X);
+          // dO rows as the right operand (tokens along the contraction): one
+          // identity product turns the row fragment around
+          const f32x4 dot = M::mma(
+              M::load(reinterpret_cast<const TC*>(sDO + swz<LO, GR>(16 * (m + h) + c16, (16 * wave + 4 * g) * SZ))),
+              ident, zero4());
+          dof[h] = M::from_f32(dot);
+          xf[h] = M::from_f32(-X);
+        }
+#pragma unroll
+        for (int s = 0; s < RT; ++s) {
+          Z[s] = M::mma2(frag_t<TC, PWT>(sQ, 16 * m, 16 * s, lane), dof[0],
+                         frag_t<TC, PWT>(sQ, 16 * (m + 1), 16 * s, lane), dof[1], Z[s]);
+          Z[s] = M::mma2(frag_t<TC, PWT>(sW, 16 * m, 16 * s, lane), xf[0],
+                         frag_t<TC, PWT>(sW, 16 * (m + 1), 16 * s, lane), xf[1], Z[s]);
+        }
       }
-      const f32x4 X = X0 + X1;
-      // dO rows as the right operand (tokens along the contraction): one
-      // identity product turns the row fragment around
-      const f32x4 dot = M::mma(
-          M::load(reinterpret_cast<const TC*>(sDO + swz<LO, GR>(16 * m + c16, (16 * wave + 4 * g) * SZ))), ident,
-          zero4());
-      const frag dof = M::from_f32(dot);
-      const frag xf = M::from_f32(-X);
+    } else {
 #pragma unroll
-      for (int s = 0; s < RT; ++s) {
-        const int a = swz<LK, GR>(16 * s + c16, (16 * m + 4 * g) * SZ);
-        Z[s] = M::mma(M::load(reinterpret_cast<const TC*>(sQt + a)), dof, Z[s]);
-        Z[s] = M::mma(M::load(reinterpret_cast<const TC*>(sWt + a)), xf, Z[s]);
+      for (int m = 0; m < NM; ++m) {
+        // X = Kbar_m dS_next (16 tokens x this wave's 16 columns)
+        f32x4 X0 = zero4(), X1 = zero4();  // even and odd key tiles: two independent chains
+#pragma unroll
+        for (int s = 0; s < RT; s += 2) {
+          X0 = M::mma(frag_t<TC, PKT>(sKt, 16 * s, 16 * m, lane), dSf[s], X0);
+          X1 = M::mma(frag_t<TC, PKT>(sKt, 16 * (s + 1), 16 * m, lane), dSf[s + 1], X1);
+        }
+        const f32x4 X = X0 + X1;
+        const f32x4 dot = M::mma(
+            M::load(reinterpret_cast<const TC*>(sDO + swz<LO, GR>(16 * m + c16, (16 * wave + 4 * g) * SZ))), ident,
+            zero4());
+        const frag dof = M::from_f32(dot);
+        const frag xf = M::from_f32(-X);
+#pragma unroll
+        for (int s = 0; s < RT; ++s) {
+          Z[s] = M::mma(frag_t<TC, PWT>(sQ, 16 * m, 16 * s, lane), dof, Z[s]);
+          Z[s] = M::mma(frag_t<TC, PWT>(sW, 16 * m, 16 * s, lane), xf, Z[s]);
+        }
       }
     }
     if (sb == 0) {

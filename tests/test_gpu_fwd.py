@@ -127,9 +127,9 @@ def untile(flat, D, C):
 
 def test_fwd_summary_intermediates():
     """The chunk summary in the workspace equals the plain chunkwise quantities
-    (fp32 path, one head): W, U~, Q', O~, Kbar (and the transposed copies of
-    W, Q', Kbar), exp(L_C), and each 16-token leaf block's (I + A_II)^-1 and P_II.
-    The transposed parts are laid out in 16-token tiles."""
+    (fp32 path, one head): W, U~, Q', O~, Kbar, exp(L_C), and each 16-token
+    leaf block's (I + A_II)^-1 and P_II.  The transposed parts are laid out in
+    16-token tiles."""
     from chunkwise_model import chunk_summary
     m = _lib()
     B, T, H, d, C = 1, 128, 1, 64, 64
@@ -147,18 +147,13 @@ def test_fwd_summary_intermediates():
         W = blk[:n].reshape(C, d)
         Qp = blk[n: 2 * n].reshape(C, d)
         # the transposed parts are stored as 16-token tiles [C/16][d][16]
-        KbT, UtT, OtT, Wt, Qt = (untile(blk[k * n:(k + 1) * n], d, C) for k in (2, 3, 4, 5, 6))
-        Kb = blk[7 * n: 8 * n].reshape(C, d)
-        gC = blk[8 * n: 8 * n + d]
-        TP = blk[8 * n + d: 8 * n + d + (C // 16) * 512].reshape(C // 16, 2, 16, 16)
+        KbT, UtT, OtT = (untile(blk[k * n:(k + 1) * n], d, C) for k in (2, 3, 4))
+        gC = blk[5 * n: 5 * n + d]
+        TP = blk[5 * n + d: 5 * n + d + (C // 16) * 512].reshape(C // 16, 2, 16, 16)
         r = ref[c]
         # exp(L_C) of fast channels sits in the fp32 denormal range, where the
         # device exponential flushes to zero: compare it with an absolute floor.
         np.testing.assert_allclose(gC, r["gC"], rtol=1e-4, atol=1e-36)
-        # the second orientations are copies of the same values
-        np.testing.assert_array_equal(Wt, W.T)
-        np.testing.assert_array_equal(Qt, Qp.T)
-        np.testing.assert_array_equal(Kb, KbT.T)
         leaves_T = np.stack([np.linalg.inv(np.eye(16) + r["A"][16 * i:16 * i + 16, 16 * i:16 * i + 16])
                              for i in range(C // 16)])
         leaves_P = np.stack([r["P"][16 * i:16 * i + 16, 16 * i:16 * i + 16] for i in range(C // 16)])
@@ -186,7 +181,7 @@ def test_fwd_saved_deltas():
     torch.cuda.synchronize()
     per = nbytes // (T // C)
     n = C * d
-    dl_off = 8 * n * 2 + d * 4 + (C // 16) * 512 * 2  # after the parts, Gamma_C and the leaf blocks
+    dl_off = 5 * n * 2 + d * 4 + (C // 16) * 512 * 2  # after the parts, Gamma_C and the leaf blocks
     ref = chunk_summary(*(inp[nm][0, :, 0].double().numpy() for nm in NAMES), C)
     for c in range(T // C):
         blk = ws[c * per + dl_off: c * per + dl_off + n * 2].view(torch.bfloat16).cpu().double().numpy()
