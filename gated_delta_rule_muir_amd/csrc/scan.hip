@@ -129,8 +129,8 @@ template <typename TC> __device__ __forceinline__ typename MM<TC>::frag identity
 // the segment's offset E and transition P into trans[head][seg] ([dk][DV + DK]
 // fp32); without it, segment seg > 0 starts from S_seg[head][seg] ([dk][dv]
 // fp32, formed from those by seg_combine_kernel) and segment 0 from S0.
-template <typename Tin, int DK, int NW, bool TRANS>
-__global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
+template <typename Tin, int DK, int NW, bool TRANS, int RS>
+__global__ __launch_bounds__(64 * NW * RS) __attribute__((amdgpu_waves_per_eu(TRANS ? 2 : 1))) void fwd_scan_kernel(
     int T, int H, int C, const char* __restrict__ summ, size_t summ_bytes,
     const float* __restrict__ S0, Tin* __restrict__ o, Tin* __restrict__ S_chunks,
     float* __restrict__ S_T, char* __restrict__ dsumm, size_t dl_offset, int nseg,
@@ -141,7 +141,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
   constexpr int DV = DK;
   constexpr int RT = DK / 16;
   constexpr int NV = 16 * NW;
-  constexpr int NTH = 64 * NW;
+  constexpr int NTH = 64 * NW * RS;
+  constexpr int RTW = RT / RS;  // row tiles of the state per wave
   constexpr int SZ = sizeof(TC);
   constexpr int GR = SZ == 2 ? 8 : 16;  // LDS swizzle granule: the fragment read size
   constexpr int SB = scan_unit<TC, NW>();
@@ -158,6 +159,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
   constexpr int PU = words_per_thread<U_WORDS, NTH>();
   constexpr int PG = words_per_thread<G_WORDS, NTH>();
   constexpr int NCOL = TRANS ? DV + DK : DV;  // state columns ([S | P] with TRANS)
+  constexpr int NM = SB / 16;                 // 16-token tiles per unit
+  static_assert(RTW % 2 == 0 && (RS == 1 || RS == 2), "row split");
 
   const int NC = T / C;
   const int NSB = C / SB;
@@ -176,9 +179,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wc = RS == 1 ? wave : wave % NW;  // this wave's 16 state columns within the workgroup's NV
+  const int wr = RS == 1 ? 0 : wave / NW;     // and its share of the rows: tiles s0 .. s0 + RTW - 1
+  const int s0 = wr * RTW;
   const int g = lane >> 4;
   const int c16 = lane & 15;
-  const int col0 = vb * NV + 16 * wave;  // this wave's first state column
+  const int col0 = vb * NV + 16 * wc;  // this wave's first state column
   const int colg = col0 + c16;
 
   __shared__ __attribute__((aligned(16))) char sW[SB * LW];
@@ -187,6 +193,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
   __shared__ __attribute__((aligned(16))) char sU[NV * LK];
   __shared__ __attribute__((aligned(16))) char sO[NV * LK];
   __shared__ __attribute__((aligned(16))) float sgC[DK];
+  // row split: each wave's partial Q'S and W S over its rows, for its partner
+  __shared__ f32x4 sXo[RS > 1 ? NW * RS : 1][RS > 1 ? NM : 1][2][64];
 
   const char* hsum = summ + static_cast<size_t>(bh) * NC * summ_bytes;  // this head's summaries
   u32x4 rw[PW], rq[PW], rk[PK], ru[PU], ro[PU], rg[PG];
@@ -260,22 +268,22 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
 
   const frag ident = identity_frag<TC>(g, c16);
   const size_t sbase = static_cast<size_t>(bh) * DK * DV;
-  f32x4 S[RT];
+  f32x4 S[RTW];  // rows 16 (s0 + sl) + 4g + i, column colg
   {
     // the segment's start: [0 | I] with TRANS, else S0 or the segment state
     const float* src = seg == 0 ? (S0 ? S0 + sbase : nullptr)
                                 : S_seg + (static_cast<size_t>(bh) * nseg + seg) * DK * DV;
 #pragma unroll
-    for (int s = 0; s < RT; ++s)
+    for (int s = 0; s < RTW; ++s)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 16 * s + 4 * g + i;
+        const int row = 16 * (s0 + s) + 4 * g + i;
         if constexpr (TRANS) S[s][i] = (pcols && row == colg - DV) ? 1.f : 0.f;
         else S[s][i] = src ? src[static_cast<size_t>(row) * DV + colg] : 0.f;
       }
   }
-  frag Sf[RT];
-  f32x4 dS[RT];
+  frag Sf[RTW];
+  f32x4 dS[RTW];
 
   const int U0 = cbeg * NSB, U1 = cend * NSB;
   if (U0 < U1) prefetch(U0);
@@ -295,19 +303,20 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
         Tin* dst = S_chunks + (static_cast<size_t>(bh) * NC + c) * DK * DV;
         if constexpr (sizeof(Tin) == 4) {
 #pragma unroll
-          for (int s = 0; s < RT; ++s)
+          for (int s = 0; s < RTW; ++s)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[stile_index(16 * s + 4 * g + i, colg, DV)] = S[s][i];
+            for (int i = 0; i < 4; ++i) dst[stile_index(16 * (s0 + s) + 4 * g + i, colg, DV)] = S[s][i];
         } else {
           // rounded once, then turned onto rows by an identity product (exact):
           // row 16s + c16, four columns per lane -- one 512-byte tile per store
 #pragma unroll
-          for (int s = 0; s < RT; ++s)
-            store4(at(dst, stile_index(16 * s + c16, col0 + 4 * g, DV)), M::mma(M::from_f32(S[s]), ident, zero4()));
+          for (int s = 0; s < RTW; ++s)
+            store4(at(dst, stile_index(16 * (s0 + s) + c16, col0 + 4 * g, DV)),
+                   M::mma(M::from_f32(S[s]), ident, zero4()));
         }
       }
 #pragma unroll
-      for (int s = 0; s < RT; ++s) {
+      for (int s = 0; s < RTW; ++s) {
         Sf[s] = M::from_f32(S[s]);
         dS[s] = zero4();
       }
@@ -322,25 +331,12 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
     TC* dlc = (!TRANS && dsumm)
                   ? reinterpret_cast<TC*>(dsumm + (static_cast<size_t>(bh) * NC + c) * summ_bytes + dl_offset)
                   : nullptr;
-#pragma unroll 2
-    for (int m = 0; m < SB / 16; ++m) {
-      // two accumulators per product (even and odd key tiles): independent
-      // MFMA chains of half the length
-      f32x4 Oa0 = zero4(), Oa1 = zero4(), Da0 = zero4(), Da1 = zero4();
-#pragma unroll
-      for (int s = 0; s < RT; s += 2) {
-        const int a0 = swz<LW, GR>(16 * m + c16, (16 * s + 4 * g) * SZ);
-        const int a1 = swz<LW, GR>(16 * m + c16, (16 * (s + 1) + 4 * g) * SZ);
-        if constexpr (!TRANS) {
-          Oa0 = M::mma(M::load(reinterpret_cast<const TC*>(sQ + a0)), Sf[s], Oa0);
-          Oa1 = M::mma(M::load(reinterpret_cast<const TC*>(sQ + a1)), Sf[s + 1], Oa1);
-        }
-        Da0 = M::mma(M::load(reinterpret_cast<const TC*>(sW + a0)), Sf[s], Da0);
-        Da1 = M::mma(M::load(reinterpret_cast<const TC*>(sW + a1)), Sf[s + 1], Da1);
-      }
-      const f32x4 Oa = Oa0 + Oa1, Da = Da0 + Da1;
-      const int au = swz<LK, GR>(16 * wave + c16, (16 * m + 4 * g) * SZ);
-      if (!TRANS && o) {
+    // One 16-token tile of the unit from its full Q'S and W S: o (by the
+    // first row half) and the deltas (by the last) stored; returns the deltas
+    // as the operand of the state update.
+    auto tile_out = [&](int m, const f32x4& Oa, const f32x4& Da) -> frag {
+      const int au = swz<LK, GR>(16 * wc + c16, (16 * m + 4 * g) * SZ);
+      if (!TRANS && o && wr == 0) {
         const f32x4 ot = load4(reinterpret_cast<const TC*>(sO + au));
         // tokens 4g+i, column c16 -> token c16, columns 4g..4g+3
         const f32x4 tt = M::mma(M::from_f32(Oa + ot), ident, zero4());
@@ -348,34 +344,104 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
       }
       const f32x4 ut = load4(reinterpret_cast<const TC*>(sU + au));
       const frag df = M::from_f32(ut - Da);
-      if (dlc) {
+      if (dlc && wr == RS - 1) {
         // the deltas in the compute type, as token rows (exact: a product with the identity)
         const f32x4 tt = M::mma(df, ident, zero4());
         store4(at(dlc, static_cast<uint32_t>((sb * SB + 16 * m + c16) * DV + col0 + 4 * g)), tt);
       }
+      return df;
+    };
+    if constexpr (RS == 1) {
+      // each 16-token tile of the unit in turn, its products used at once
+#pragma unroll 2
+      for (int m = 0; m < NM; ++m) {
+        // two accumulators per product (even and odd key tiles): independent
+        // MFMA chains of half the length
+        f32x4 Oa0 = zero4(), Oa1 = zero4(), Da0 = zero4(), Da1 = zero4();
 #pragma unroll
-      for (int s = 0; s < RT; ++s)
-        dS[s] = M::mma(M::load(reinterpret_cast<const TC*>(sK + swz<LK, GR>(16 * s + c16, (16 * m + 4 * g) * SZ))),
-                       df, dS[s]);
+        for (int s = 0; s < RT; s += 2) {
+          const int a0 = swz<LW, GR>(16 * m + c16, (16 * s + 4 * g) * SZ);
+          const int a1 = swz<LW, GR>(16 * m + c16, (16 * (s + 1) + 4 * g) * SZ);
+          if constexpr (!TRANS) {
+            Oa0 = M::mma(M::load(reinterpret_cast<const TC*>(sQ + a0)), Sf[s], Oa0);
+            Oa1 = M::mma(M::load(reinterpret_cast<const TC*>(sQ + a1)), Sf[s + 1], Oa1);
+          }
+          Da0 = M::mma(M::load(reinterpret_cast<const TC*>(sW + a0)), Sf[s], Da0);
+          Da1 = M::mma(M::load(reinterpret_cast<const TC*>(sW + a1)), Sf[s + 1], Da1);
+        }
+        const frag df = tile_out(m, Oa0 + Oa1, Da0 + Da1);
+#pragma unroll
+        for (int s = 0; s < RT; ++s)
+          dS[s] = M::mma(M::load(reinterpret_cast<const TC*>(sK + swz<LK, GR>(16 * s + c16, (16 * m + 4 * g) * SZ))),
+                         df, dS[s]);
+      }
+    } else {
+      // Q'S and W S of the unit's token tiles over this wave's rows (two
+      // independent chains: even and odd key tiles)
+      f32x4 Oa[NM], Da[NM];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        f32x4 Oa0 = zero4(), Oa1 = zero4(), Da0 = zero4(), Da1 = zero4();
+#pragma unroll
+        for (int sl = 0; sl < RTW; sl += 2) {
+          const int s = s0 + sl;
+          const int a0 = swz<LW, GR>(16 * m + c16, (16 * s + 4 * g) * SZ);
+          const int a1 = swz<LW, GR>(16 * m + c16, (16 * (s + 1) + 4 * g) * SZ);
+          if constexpr (!TRANS) {
+            Oa0 = M::mma(M::load(reinterpret_cast<const TC*>(sQ + a0)), Sf[sl], Oa0);
+            Oa1 = M::mma(M::load(reinterpret_cast<const TC*>(sQ + a1)), Sf[sl + 1], Oa1);
+          }
+          Da0 = M::mma(M::load(reinterpret_cast<const TC*>(sW + a0)), Sf[sl], Da0);
+          Da1 = M::mma(M::load(reinterpret_cast<const TC*>(sW + a1)), Sf[sl + 1], Da1);
+        }
+        Oa[m] = Oa0 + Oa1;
+        Da[m] = Da0 + Da1;
+      }
+      if constexpr (RS == 2) {
+        // the two row halves exchange their partial sums through LDS (the
+        // same sum on both sides: addition commutes)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          if constexpr (!TRANS) sXo[wave][m][0][lane] = Oa[m];
+          sXo[wave][m][1][lane] = Da[m];
+        }
+        __syncthreads();
+        const int pw = wc + NW * (1 - wr);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          if constexpr (!TRANS) Oa[m] += sXo[pw][m][0][lane];
+          Da[m] += sXo[pw][m][1][lane];
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const frag df = tile_out(m, Oa[m], Da[m]);
+#pragma unroll
+        for (int sl = 0; sl < RTW; ++sl)
+          dS[sl] = M::mma(
+              M::load(reinterpret_cast<const TC*>(sK + swz<LK, GR>(16 * (s0 + sl) + c16, (16 * m + 4 * g) * SZ))), df,
+              dS[sl]);
+      }
     }
     if (sb == NSB - 1) {
 #pragma unroll
-      for (int s = 0; s < RT; ++s)
+      for (int s = 0; s < RTW; ++s)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[s][i] = sgC[16 * s + 4 * g + i] * S[s][i] + dS[s][i];
+        for (int i = 0; i < 4; ++i) S[s][i] = sgC[16 * (s0 + s) + 4 * g + i] * S[s][i] + dS[s][i];
     }
   }
   if constexpr (TRANS) {
     float* dst = trans + (static_cast<size_t>(bh) * nseg + seg) * DK * NCOL;
 #pragma unroll
-    for (int s = 0; s < RT; ++s)
+    for (int s = 0; s < RTW; ++s)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * s + 4 * g + i) * NCOL + colg] = S[s][i];
+      for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * (s0 + s) + 4 * g + i) * NCOL + colg] = S[s][i];
   } else if (S_T && seg == nseg - 1) {
 #pragma unroll
-    for (int s = 0; s < RT; ++s)
+    for (int s = 0; s < RTW; ++s)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S_T[sbase + static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] = S[s][i];
+      for (int i = 0; i < 4; ++i)
+        S_T[sbase + static_cast<size_t>(16 * (s0 + s) + 4 * g + i) * DV + colg] = S[s][i];
   }
 }
 
@@ -394,8 +460,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_scan_kernel(
 // forward's trans.  Without TRANS, the last segment starts from dS_T and
 // segment seg from dS_seg[head][seg] (the gradient at the segment's end), and
 // segment 0 writes dS0.
-template <typename Tin, int DK, int NW, bool TRANS>
-__global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
+template <typename Tin, int DK, int NW, bool TRANS, int RS>
+__global__ __launch_bounds__(64 * NW * RS) void bwd_scan_kernel(
     int T, int H, int C, const char* __restrict__ summ, size_t summ_bytes,
     const Tin* __restrict__ dO, const float* __restrict__ dS_T, Tin* __restrict__ dS_chunks,
     float* __restrict__ dS0, int nseg, const float* __restrict__ dS_seg, float* __restrict__ trans) {
@@ -405,7 +471,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
   constexpr int DV = DK;
   constexpr int RT = DK / 16;
   constexpr int NV = 16 * NW;
-  constexpr int NTH = 64 * NW;
+  constexpr int NTH = 64 * NW * RS;
+  constexpr int RTW = RT / RS;  // row tiles of the state gradient per wave
   constexpr int SZ = sizeof(TC);
   constexpr int GR = SZ == 2 ? 8 : 16;  // LDS swizzle granule: the fragment read size
   constexpr int SB = scan_unit<TC, NW>();
@@ -426,6 +493,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
   constexpr int PG = words_per_thread<G_WORDS, NTH>();
   static_assert(LO >= 32, "dO row segment");
   constexpr int TS = DV + DK;  // row stride of trans
+  constexpr int NM = SB / 16;  // 16-token tiles per unit
+  static_assert(RTW % 2 == 0 && (RS == 1 || RS == 2), "row split");
 
   const int NC = T / C;
   const int NSB = C / SB;
@@ -442,15 +511,20 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int wc = RS == 1 ? wave : wave % NW;  // this wave's 16 columns within the workgroup's NV
+  const int wr = RS == 1 ? 0 : wave / NW;     // and its share of the rows: tiles s0 .. s0 + RTW - 1
+  const int s0 = wr * RTW;
   const int g = lane >> 4;
   const int c16 = lane & 15;
-  const int colg = vb * NV + 16 * wave + c16;
+  const int colg = vb * NV + 16 * wc + c16;
 
   __shared__ __attribute__((aligned(16))) char sW[SB * PWT];   // read transposed (frag_t)
   __shared__ __attribute__((aligned(16))) char sQ[SB * PWT];   // read transposed
   __shared__ __attribute__((aligned(16))) char sKt[DK * PKT];  // read transposed
   __shared__ __attribute__((aligned(16))) char sDO[SB * LO];
   __shared__ __attribute__((aligned(16))) float sgC[DK];
+  // row split: each wave's partial Kbar dS over its rows, for its partner
+  __shared__ f32x4 sXb[RS > 1 ? NW * RS : 1][RS > 1 ? NM : 1][64];
 
   const char* hsum = summ + static_cast<size_t>(bh) * NC * summ_bytes;
   u32x4 rw[PW], rq[PW], rk[PK], rd[PO], rg[PG];
@@ -520,19 +594,20 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
 
   const frag ident = identity_frag<TC>(g, c16);
   const size_t sbase = static_cast<size_t>(bh) * DK * DV;
-  f32x4 dS[RT];
+  f32x4 dS[RTW];  // rows 16 (s0 + sl) + 4g + i, column colg
   {
     // the segment's end: zero with TRANS, else dS_T or the segment state
     const float* src = TRANS ? nullptr
                        : seg == nseg - 1 ? (dS_T ? dS_T + sbase : nullptr)
                                          : dS_seg + (static_cast<size_t>(bh) * nseg + seg) * DK * DV;
 #pragma unroll
-    for (int s = 0; s < RT; ++s)
+    for (int s = 0; s < RTW; ++s)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dS[s][i] = src ? src[static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] : 0.f;
+      for (int i = 0; i < 4; ++i)
+        dS[s][i] = src ? src[static_cast<size_t>(16 * (s0 + s) + 4 * g + i) * DV + colg] : 0.f;
   }
-  frag dSf[RT];
-  f32x4 Z[RT];
+  frag dSf[RTW];
+  f32x4 Z[RTW];
 
   const int U = (cend - cbeg) * NSB;
   if (U > 0) prefetch(0);
@@ -551,88 +626,100 @@ __global__ __launch_bounds__(64 * NW) void bwd_scan_kernel(
       // 16-row tiles (the lane's four rows of column colg are contiguous)
       TC* dst = dS_chunks + (static_cast<size_t>(bh) * NC + c) * DK * DV;
 #pragma unroll
-      for (int s = 0; s < RT; ++s) {
-        if constexpr (!TRANS) store4(at(dst, static_cast<uint32_t>((s * DV + colg) * 16 + 4 * g)), dS[s]);
+      for (int s = 0; s < RTW; ++s) {
+        if constexpr (!TRANS) store4(at(dst, static_cast<uint32_t>(((s0 + s) * DV + colg) * 16 + 4 * g)), dS[s]);
         dSf[s] = M::from_f32(dS[s]);
         Z[s] = zero4();
       }
     }
     prefetch(u + 1 < U ? u + 1 : u);
     __syncthreads();
-    // (the unit's token tiles fully unrolled: their X products are independent,
-    // so their MFMA chains interleave)
-    constexpr int NM = SB / 16;
+    // X = Kbar_m dS_next over this wave's rows, for each token tile m of the
+    // unit (independent products, so their MFMA chains interleave)
+    f32x4 X[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      if constexpr (SZ == 2) {
+        // bf16: pairs of key tiles in one 32-deep product
+        X[m] = zero4();
+#pragma unroll
+        for (int sl = 0; sl < RTW; sl += 2)
+          X[m] = M::mma2(frag_t<TC, PKT>(sKt, 16 * (s0 + sl), 16 * m, lane), dSf[sl],
+                         frag_t<TC, PKT>(sKt, 16 * (s0 + sl + 1), 16 * m, lane), dSf[sl + 1], X[m]);
+      } else {
+        f32x4 X0 = zero4(), X1 = zero4();  // even and odd key tiles: two independent chains
+#pragma unroll
+        for (int sl = 0; sl < RTW; sl += 2) {
+          X0 = M::mma(frag_t<TC, PKT>(sKt, 16 * (s0 + sl), 16 * m, lane), dSf[sl], X0);
+          X1 = M::mma(frag_t<TC, PKT>(sKt, 16 * (s0 + sl + 1), 16 * m, lane), dSf[sl + 1], X1);
+        }
+        X[m] = X0 + X1;
+      }
+    }
+    if constexpr (RS == 2) {
+      // the two row halves exchange their partial sums through LDS (the
+      // same sum on both sides: addition commutes)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) sXb[wave][m][lane] = X[m];
+      __syncthreads();
+      const int pw = wc + NW * (1 - wr);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) X[m] += sXb[pw][m][lane];
+    }
+    // dO rows as the right operand (tokens along the contraction): one
+    // identity product turns the row fragment around
+    auto dO_frag = [&](int m) {
+      return M::from_f32(M::mma(
+          M::load(reinterpret_cast<const TC*>(sDO + swz<LO, GR>(16 * m + c16, (16 * wc + 4 * g) * SZ))), ident,
+          zero4()));
+    };
     if constexpr (SZ == 2 && NM % 2 == 0) {
-      // bf16: token tiles in pairs, each pair of 16-deep products (two key
-      // tiles for X, two token tiles for Z) issued as one 32-deep product
+      // bf16: token tiles in pairs, each pair of 16-deep products issued as
+      // one 32-deep product
 #pragma unroll
       for (int m = 0; m < NM; m += 2) {
-        frag dof[2], xf[2];
+        const frag dof0 = dO_frag(m), dof1 = dO_frag(m + 1);
+        const frag xf0 = M::from_f32(-X[m]), xf1 = M::from_f32(-X[m + 1]);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          // X = Kbar_{m+h} dS_next (16 tokens x this wave's 16 columns)
-          f32x4 X = zero4();
-#pragma unroll
-          for (int s = 0; s < RT; s += 2)
-            X = M::mma2(frag_t<TC, PKT>(sKt, 16 * s, 16 * (m + h), lane), dSf[s],
-                        frag_t<TC, PKT>(sKt, 16 * (s + 1), 16 * (m + h), lane), dSf[s + 1], X);
-          // dO rows as the right operand (tokens along the contraction): one
-          // identity product turns the row fragment around
-          const f32x4 dot = M::mma(
-              M::load(reinterpret_cast<const TC*>(sDO + swz<LO, GR>(16 * (m + h) + c16, (16 * wave + 4 * g) * SZ))),
-              ident, zero4());
-          dof[h] = M::from_f32(dot);
-          xf[h] = M::from_f32(-X);
-        }
-#pragma unroll
-        for (int s = 0; s < RT; ++s) {
-          Z[s] = M::mma2(frag_t<TC, PWT>(sQ, 16 * m, 16 * s, lane), dof[0],
-                         frag_t<TC, PWT>(sQ, 16 * (m + 1), 16 * s, lane), dof[1], Z[s]);
-          Z[s] = M::mma2(frag_t<TC, PWT>(sW, 16 * m, 16 * s, lane), xf[0],
-                         frag_t<TC, PWT>(sW, 16 * (m + 1), 16 * s, lane), xf[1], Z[s]);
+        for (int sl = 0; sl < RTW; ++sl) {
+          const int s = s0 + sl;
+          Z[sl] = M::mma2(frag_t<TC, PWT>(sQ, 16 * m, 16 * s, lane), dof0,
+                          frag_t<TC, PWT>(sQ, 16 * (m + 1), 16 * s, lane), dof1, Z[sl]);
+          Z[sl] = M::mma2(frag_t<TC, PWT>(sW, 16 * m, 16 * s, lane), xf0,
+                          frag_t<TC, PWT>(sW, 16 * (m + 1), 16 * s, lane), xf1, Z[sl]);
         }
       }
     } else {
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
-        // X = Kbar_m dS_next (16 tokens x this wave's 16 columns)
-        f32x4 X0 = zero4(), X1 = zero4();  // even and odd key tiles: two independent chains
+        const frag dof = dO_frag(m);
+        const frag xf = M::from_f32(-X[m]);
 #pragma unroll
-        for (int s = 0; s < RT; s += 2) {
-          X0 = M::mma(frag_t<TC, PKT>(sKt, 16 * s, 16 * m, lane), dSf[s], X0);
-          X1 = M::mma(frag_t<TC, PKT>(sKt, 16 * (s + 1), 16 * m, lane), dSf[s + 1], X1);
-        }
-        const f32x4 X = X0 + X1;
-        const f32x4 dot = M::mma(
-            M::load(reinterpret_cast<const TC*>(sDO + swz<LO, GR>(16 * m + c16, (16 * wave + 4 * g) * SZ))), ident,
-            zero4());
-        const frag dof = M::from_f32(dot);
-        const frag xf = M::from_f32(-X);
-#pragma unroll
-        for (int s = 0; s < RT; ++s) {
-          Z[s] = M::mma(frag_t<TC, PWT>(sQ, 16 * m, 16 * s, lane), dof, Z[s]);
-          Z[s] = M::mma(frag_t<TC, PWT>(sW, 16 * m, 16 * s, lane), xf, Z[s]);
+        for (int sl = 0; sl < RTW; ++sl) {
+          Z[sl] = M::mma(frag_t<TC, PWT>(sQ, 16 * m, 16 * (s0 + sl), lane), dof, Z[sl]);
+          Z[sl] = M::mma(frag_t<TC, PWT>(sW, 16 * m, 16 * (s0 + sl), lane), xf, Z[sl]);
         }
       }
     }
     if (sb == 0) {
 #pragma unroll
-      for (int s = 0; s < RT; ++s)
+      for (int s = 0; s < RTW; ++s)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dS[s][i] = sgC[16 * s + 4 * g + i] * dS[s][i] + Z[s][i];
+        for (int i = 0; i < 4; ++i) dS[s][i] = sgC[16 * (s0 + s) + 4 * g + i] * dS[s][i] + Z[s][i];
     }
   }
   if constexpr (TRANS) {
     float* dst = trans + (static_cast<size_t>(bh) * nseg + seg) * DK * TS;
 #pragma unroll
-    for (int s = 0; s < RT; ++s)
+    for (int s = 0; s < RTW; ++s)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * s + 4 * g + i) * TS + colg] = dS[s][i];
+      for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * (s0 + s) + 4 * g + i) * TS + colg] = dS[s][i];
   } else if (dS0 && seg == 0) {
 #pragma unroll
-    for (int s = 0; s < RT; ++s)
+    for (int s = 0; s < RTW; ++s)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dS0[sbase + static_cast<size_t>(16 * s + 4 * g + i) * DV + colg] = dS[s][i];
+      for (int i = 0; i < 4; ++i)
+        dS0[sbase + static_cast<size_t>(16 * (s0 + s) + 4 * g + i) * DV + colg] = dS[s][i];
   }
 }
 
@@ -737,7 +824,7 @@ template <typename TT, int DD>
 void fwd_trans_typed(const ChunkShape& s, const void* summ, float* trans, hipStream_t stream) {
   const int heads = s.B * s.H;
   const int nseg = s.scan_segments();
-  hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, true>), dim3(heads * nseg * (2 * DD / 64)), dim3(256), 0, stream,
+  hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, true, 1>), dim3(heads * nseg * (2 * DD / 64)), dim3(256), 0, stream,
                      s.T, s.H, s.C, (const char*)summ, s.summary_bytes(), (const float*)nullptr, (TT*)nullptr,
                      (TT*)nullptr, (float*)nullptr, (char*)nullptr, size_t(0), nseg, (const float*)nullptr, trans);
 }
@@ -755,15 +842,15 @@ hipError_t fwd_scan_typed(const ChunkShape& s, const void* summ, const float* S0
     fwd_trans_typed<TT, DD>(s, summ, trans, stream);
     hipLaunchKernelGGL((seg_combine_kernel<DD, false>), dim3(heads * (DD / 16)), dim3(4 * DD), 0, stream, nseg, S0,
                        (const float*)trans, (const float*)trans, sseg);
-    hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, false>), dim3(heads * nseg * (DD / 64)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, false, 2>), dim3(heads * nseg * (DD / 64)), dim3(512), 0, stream,
                        s.T, s.H, s.C, (const char*)summ, sb, S0, (TT*)o, S_chunks, S_T, (char*)deltas,
                        s.dl_offset(), nseg, (const float*)sseg, (float*)nullptr);
   } else if (static_cast<long long>(heads) * (DD / 64) >= 256) {
-    hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, false>), dim3(heads * (DD / 64)), dim3(256), 0, stream, s.T,
+    hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, false, 2>), dim3(heads * (DD / 64)), dim3(512), 0, stream, s.T,
                        s.H, s.C, (const char*)summ, sb, S0, (TT*)o, S_chunks, S_T, (char*)deltas, s.dl_offset(), 1,
                        (const float*)nullptr, (float*)nullptr);
   } else {
-    hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 1, false>), dim3(heads * (DD / 16)), dim3(64), 0, stream, s.T,
+    hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 1, false, 1>), dim3(heads * (DD / 16)), dim3(64), 0, stream, s.T,
                        s.H, s.C, (const char*)summ, sb, S0, (TT*)o, S_chunks, S_T, (char*)deltas, s.dl_offset(), 1,
                        (const float*)nullptr, (float*)nullptr);
   }
@@ -781,20 +868,20 @@ hipError_t bwd_scan_typed(const ChunkShape& s, const void* summ, const void* dO,
     // the transposes of the forward's, read from ftrans
     float* trans = split;
     float* sseg = split + static_cast<size_t>(heads) * nseg * DD * (2 * DD);
-    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, true>), dim3(heads * nseg * (DD / 64)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, true, 2>), dim3(heads * nseg * (DD / 64)), dim3(512), 0, stream,
                        s.T, s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks, (float*)nullptr,
                        nseg, (const float*)nullptr, trans);
     hipLaunchKernelGGL((seg_combine_kernel<DD, true>), dim3(heads * (DD / 16)), dim3(4 * DD), 0, stream, nseg, dS_T,
                        (const float*)trans, ftrans, sseg);
-    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, false>), dim3(heads * nseg * (DD / 64)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, false, 2>), dim3(heads * nseg * (DD / 64)), dim3(512), 0, stream,
                        s.T, s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks, dS0, nseg,
                        (const float*)sseg, (float*)nullptr);
   } else if (static_cast<long long>(heads) * (DD / 64) >= 256) {
-    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, false>), dim3(heads * (DD / 64)), dim3(256), 0, stream, s.T,
+    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, false, 2>), dim3(heads * (DD / 64)), dim3(512), 0, stream, s.T,
                        s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks, dS0, 1,
                        (const float*)nullptr, (float*)nullptr);
   } else {
-    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 1, false>), dim3(heads * (DD / 16)), dim3(64), 0, stream, s.T,
+    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 1, false, 1>), dim3(heads * (DD / 16)), dim3(64), 0, stream, s.T,
                        s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks, dS0, 1,
                        (const float*)nullptr, (float*)nullptr);
   }
