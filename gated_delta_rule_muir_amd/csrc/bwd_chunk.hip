@@ -211,7 +211,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   __shared__ __attribute__((aligned(16))) TC sSS[DIRECT ? 1 : DK][PS];  // staged S_J columns, [dk][dv] (two sweeps)
   // direct form: the block's inputs q, k, v, write, erase, log_a, gamma as
   // token rows, read by both the elementwise and the output mapping
-  __shared__ __attribute__((aligned(16))) TC sIn[DIRECT ? 7 : 1][16][PV];
+  // (rows of 288 bytes for d = 128: read by transposing reads, tr_in, whose
+  // eight rows of a 32-lane pass then fall on distinct banks)
+  // Two buffers where they fit (64-token chunks): the next block's tiles are
+  // then written before the closing barrier of the current one.
+  constexpr int PVI = DIRECT ? DV + 16 : 1;
+  constexpr int NIB = FORM == BWD_DIRECT ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) TC sIn[NIB][DIRECT ? 7 : 1][16][PVI];
+  int ibuf = 0;  // the buffer of the block being processed
   __shared__ float sLf[2][16][17];                           // leaf matrices of steep blocks
   __shared__ float sG[DK];
   __shared__ float sGH[DIRECT ? NBS - 1 : 1][DK];             // direct: block decays exp(B_{I+1} - B_I)
@@ -457,7 +464,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       }
     }
   };
-  auto store_in = [&]() {
+  auto store_in = [&](int buf) {
     if constexpr (DIRECT) {
 #pragma unroll
       for (int sl = 0; sl < SPWV; ++sl) {
@@ -467,11 +474,21 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
           for (int k2 = 0; k2 < IWT; ++k2) {
             const int w = lane + 64 * k2;
             const int row = w / IWR;
-            put16(&sIn[t][row][(w - row * IWR) * SEW], iw[sl * IWT + k2]);
+            put16(&sIn[buf][t][row][(w - row * IWR) * SEW], iw[sl * IWT + k2]);
           }
         }
       }
     }
+  };
+  // Direct form: four consecutive tokens of one channel of input tile x, by a
+  // transposing read: lane l of each 16-lane group reads row row0 + l/4,
+  // channels cb + 4 (l%4) .. + 3, and receives the four rows' values of
+  // channel cb + l (cb: its group's first channel)
+  auto tr_in = [&](int x, int row0, int cb) -> i16x4 {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const int l = lane & 15;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(&sIn[ibuf][x][row0 + (l >> 2)][cb + 4 * (l & 3)]));
   };
   // a static gate's value per channel (none: 1)
   auto gam_static = [&](int j) -> float { return gmode == GAMMA_NONE ? 1.f : ldv(gst, static_cast<uint32_t>(j)); };
@@ -481,16 +498,20 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         const float gs = GTOK ? 0.f : gam_static(colv(n));
+        // tokens 4g .. 4g+3 of channel colv(n)
+        const i16x4 fq = tr_in(0, 4 * g, col0(n)), fk = tr_in(1, 4 * g, col0(n)), fv = tr_in(2, 4 * g, col0(n)),
+                    fw = tr_in(3, 4 * g, col0(n)), fe = tr_in(4, 4 * g, col0(n)), fl = tr_in(5, 4 * g, col0(n));
+        i16x4 fg = fq;
+        if constexpr (GTOK) fg = tr_in(6, 4 * g, col0(n));
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-          const int t = 4 * g + ii, j = colv(n);
-          oq[n][ii] = M::to_f32(sIn[0][t][j]);
-          ok[n][ii] = M::to_f32(sIn[1][t][j]);
-          ov[n][ii] = M::to_f32(sIn[2][t][j]);
-          ow[n][ii] = M::to_f32(sIn[3][t][j]);
-          oe[n][ii] = M::to_f32(sIn[4][t][j]);
-          ol[n][ii] = M::to_f32(sIn[5][t][j]);
-          og[n][ii] = GTOK ? M::to_f32(sIn[6][t][j]) : gs;
+          oq[n][ii] = M::to_f32(static_cast<uint16_t>(fq[ii]));
+          ok[n][ii] = M::to_f32(static_cast<uint16_t>(fk[ii]));
+          ov[n][ii] = M::to_f32(static_cast<uint16_t>(fv[ii]));
+          ow[n][ii] = M::to_f32(static_cast<uint16_t>(fw[ii]));
+          oe[n][ii] = M::to_f32(static_cast<uint16_t>(fe[ii]));
+          ol[n][ii] = M::to_f32(static_cast<uint16_t>(fl[ii]));
+          og[n][ii] = GTOK ? M::to_f32(static_cast<uint16_t>(fg[ii])) : gs;
         }
       }
     }
@@ -534,14 +555,21 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     const int safe = !((sUnsafe >> J) & 1);
     if constexpr (DIRECT) {
       const float gs = GTOK ? 0.f : gam_static(ej);
+      // tokens RPT part .. + 3 of channel ej (the lane's channel within its
+      // 16-lane group: ej % 16 == lane % 16)
+      static_assert(RPT == 4 && DK % 64 == 0, "elementwise mapping of the transposing reads");
+      const int cb = ej & ~15;
+      const i16x4 fq = tr_in(0, RPT * part, cb), fk = tr_in(1, RPT * part, cb), fe = tr_in(4, RPT * part, cb),
+                  fl = tr_in(5, RPT * part, cb);
+      i16x4 fg = fq;
+      if constexpr (GTOK) fg = tr_in(6, RPT * part, cb);
 #pragma unroll
       for (int rr = 0; rr < RPT; ++rr) {
-        const int r = RPT * part + rr;
-        xq[rr] = M::to_f32(sIn[0][r][ej]);
-        xk[rr] = M::to_f32(sIn[1][r][ej]);
-        xe[rr] = M::to_f32(sIn[4][r][ej]);
-        xl[rr] = M::to_f32(sIn[5][r][ej]);
-        xg[rr] = GTOK ? M::to_f32(sIn[6][r][ej]) : gs;
+        xq[rr] = M::to_f32(static_cast<uint16_t>(fq[rr]));
+        xk[rr] = M::to_f32(static_cast<uint16_t>(fk[rr]));
+        xe[rr] = M::to_f32(static_cast<uint16_t>(fe[rr]));
+        xl[rr] = M::to_f32(static_cast<uint16_t>(fl[rr]));
+        xg[rr] = GTOK ? M::to_f32(static_cast<uint16_t>(fg[rr])) : gs;
       }
     }
     float loc[RPT], suf[RPT];
@@ -755,7 +783,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       put16(&sSD[row][(w - row * KWR) * SEW], kw[k2]);
     }
     if (tid < DK / 4) *reinterpret_cast<u32x4*>(&sG[4 * tid]) = gcw;
-    store_in();
+    store_in((NB - 1) % NIB);
     horner_setup();
     __syncthreads();  // sDL, sSD, sG, sIn, sGH
     // S becomes the chunk-end state S_C = diag(Gamma_C) S0 + Kbar^T Delta
@@ -883,7 +911,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       }
       __syncthreads();  // sDL, sSD and sG are rewritten by the next sub-chunk
     }
-    store_in();  // the last block's inputs, for the reverse sweep
+    store_in((NB - 1) % NIB);  // the last block's inputs, for the reverse sweep
   } else {
     load_state(S, S0c);
     prefetch_f(0);
@@ -1003,6 +1031,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       }
     }
     const TC (*dlJ)[PV] = DIRECT ? sDL + 16 * jl : sDL;  // the block's delta rows
+    ibuf = J % NIB;
     const int safe = commit_r(J);
     u32x4 css[SPLIT > 1 ? SPT : 1];  // this block's state words for the later column passes
     if (SPLIT > 1) {
@@ -1298,9 +1327,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         for (int n = 0; n < NT; ++n) D[s][n] = M::mma2(ya, dOf[n], xa, dRf[n], D[s][n] * gs);
       }
     }
+    if (NIB == 2 && J > 0) store_in((J - 1) % NIB);  // the other buffer: its last reader was block J+1
     __syncthreads();
-    if (DIRECT && J > 0) {
-      store_in();  // the next block's inputs (every read of this block's is done)
+    if (NIB == 1 && DIRECT && J > 0) {
+      store_in(0);  // the next block's inputs (every read of this block's is done)
       __syncthreads();
     }
   }
