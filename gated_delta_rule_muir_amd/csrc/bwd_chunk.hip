@@ -490,6 +490,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_i16x4*)(&sIn[ibuf][x][row0 + (l >> 2)][cb + 4 * (l & 3)]));
   };
+  // bf16: rows 4g .. 4g+3 of column n0 + c16 of a [16][pitch] tile as a
+  // fragment (the transposed read of a tile held as token rows)
+  auto tr_tile = [&](const TC* tile, int pitch, int n0) -> i16x4 {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const int l = lane & 15;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(tile + (4 * g + (l >> 2)) * pitch + n0 + 4 * (l & 3)));
+  };
   // a static gate's value per channel (none: 1)
   auto gam_static = [&](int j) -> float { return gmode == GAMMA_NONE ? 1.f : ldv(gst, static_cast<uint32_t>(j)); };
   // Direct form: the block's inputs at the output mapping, from sIn
@@ -1046,7 +1054,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     frag dOf[NT];
     {
       frag ptf, ttf;
-      {
+      if constexpr (sizeof(TC) == 2) {
+        ttf = __builtin_bit_cast(frag, tr_tile(&sT[0][0], TP, 0));
+        ptf = __builtin_bit_cast(frag, tr_tile(&sP[0][0], TP, 0));
+      } else {
         f32x4 pv, tv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1070,10 +1081,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       }
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        f32x4 dov;
+        if constexpr (sizeof(TC) == 2) {
+          dOf[n] = __builtin_bit_cast(frag, tr_tile(&sDO[0][0], PV, col0(n)));
+        } else {
+          f32x4 dov;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dov[i] = M::to_f32(sDO[4 * g + i][colv(n)]);
-        dOf[n] = M::from_f32(dov);
+          for (int i = 0; i < 4; ++i) dov[i] = M::to_f32(sDO[4 * g + i][colv(n)]);
+          dOf[n] = M::from_f32(dov);
+        }
         acc[n] = M::mma(ptf, dOf[n], acc[n]);
         dRn[n] = M::mma(ttf, M::from_f32(acc[n]), zero4());
       }
