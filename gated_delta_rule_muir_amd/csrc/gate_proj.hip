@@ -36,7 +36,8 @@ enum Epi {
   EPI_STORE = 0,     // general GEMM: C = acc in the compute type
   EPI_GATE = 1,      // up-projection: gate = act(acc + bias)
   EPI_GATE_BWD = 2,  // up-projection: dpre = dG * act'(acc + bias), with per-tile column sums
-  EPI_PARTIAL = 3    // general GEMM: fp32 partial of one split of the contraction
+  EPI_PARTIAL = 3,   // general GEMM: fp32 partial of one split of the contraction
+  EPI_GATE_DZ = 4    // up-projection: as EPI_GATE_BWD, and dz = dpre U accumulated over the whole width
 };
 
 // Per-compute-type GEMM fragment: bf16 contracts 32 per MFMA (8 values per
@@ -104,7 +105,8 @@ template <typename TC> struct GateUpArgs {
   const TC* z;     // [M, 512]
   const TC* U;     // packed up matrices
   const TC* bias;  // packed biases
-  TC* out[5];      // gates (forward) or their pre-activation gradients (backward), [M, W_i]
+  TC* out[5];      // gates (forward) or their pre-activation gradients (EPI_GATE_BWD), [M, W_i]
+  TC* dz;          // EPI_GATE_DZ: [M, 512], gate i's slice at its z offset
   const TC* dG[5];  // backward: the gates' gradients, [M, W_i]
   float* colsum;   // backward: per-tile column sums [m tiles][colsum_ld]
   int colsum_ld;
@@ -324,31 +326,6 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmBatch batch) {
 template <int ACT> __device__ __forceinline__ float act_fwd_t(float x) { return act_fwd(ACT, x); }
 template <int ACT> __device__ __forceinline__ float act_grad_t(float x) { return act_grad(ACT, x); }
 
-// One column tile's operands of the up-projection kernel, to registers: the
-// U block (BN rows of the gate's rank, as 16-byte words; words past the
-// block repeat its last) and, for the backward (DG), this thread's staged
-// words of the upstream gradient (rows dgrow0 + s * RSTEP, clamped to the
-// last row; rows past it are not used).
-template <typename TC, bool DG, int MAXW, int SW, int RSTEP>
-__device__ __forceinline__ void up_load_tile(u32x4 (&rb)[MAXW], u32x4 (&dgw)[SW], const TC* __restrict__ U,
-                                             const TC* __restrict__ dG, int n0, int r, int W, int nwords, int tid,
-                                             int dgrow0, int M, int scol) {
-  constexpr int E = 16 / sizeof(TC);
-  const int wpr = r / E;
-#pragma unroll
-  for (int w = 0; w < MAXW; ++w) {
-    const int idx = min(tid + w * UP_THREADS, nwords - 1);
-    rb[w] = *reinterpret_cast<const u32x4*>(U + static_cast<size_t>(n0 + idx / wpr) * r + (idx % wpr) * E);
-  }
-  if constexpr (DG) {
-#pragma unroll
-    for (int sw = 0; sw < SW; ++sw) {
-      const int gm = min(dgrow0 + sw * RSTEP, M - 1);
-      dgw[sw] = *reinterpret_cast<const u32x4*>(dG + static_cast<size_t>(gm) * W + n0 + scol);
-    }
-  }
-}
-
 // The gates' up-projections (contraction over one gate's rank, 64 or 128):
 // C = z_i U_i^T + c_i with an activation epilogue (EPI_GATE) or its gradient
 // (EPI_GATE_BWD).  A workgroup of 4 waves owns a 128-row block of one gate
@@ -364,33 +341,55 @@ __device__ __forceinline__ void up_load_tile(u32x4 (&rb)[MAXW], u32x4 (&dgw)[SW]
 // and the output tile written, through an LDS staging tile in whole 128-byte
 // rows (8 lanes per row), not in the MFMA layout's 32-byte pieces.
 // blockIdx.x: the row block (fastest), then the group of column tiles;
-// blockIdx.y: the gate.
-template <typename TC, int EPI>
-__global__ __launch_bounds__(UP_THREADS) void gate_up_kernel(GateUpArgs<TC> a) {
+// blockIdx.y: the gate.  The gate's rank and activation are template
+// arguments of the body (one instance per form), so its loops carry no
+// run-time bounds.
+//
+// EPI_GATE_DZ (bf16) also forms the gate's slice of dz = dpre U: a workgroup
+// then takes every column tile of its row block, and each tile's dpre, still
+// in registers, is the right operand of a product with U's block read
+// transposed from LDS (ds_read_b64_tr_b16): the lane's four consecutive
+// columns of the tile are four consecutive contraction indices, so two
+// tiles' values make one 32-deep product.  dz stays in registers until the
+// row block is done, and dpre need not be re-read for it.
+template <typename TC, int EPI> struct UpShape {
+  static constexpr int RMAX = 128;
+  // U block rows: 272 bytes, or 288 for the transposing reads of EPI_GATE_DZ
+  // (an odd number of 32-byte units: the four rows of each lane group's read
+  // fall on distinct banks)
+  static constexpr int LDK = RMAX + (EPI == EPI_GATE_DZ ? 16 : GF<TC>::PAD);
+  static constexpr int BM = 128;
+  static constexpr int LDS_ = UP_BN + 16 / static_cast<int>(sizeof(TC));  // staging pitch: one 16-byte pad per row
+};
+
+template <typename TC, int EPI, int R, int ACT>
+__device__ __forceinline__ void gate_up_body(const GateUpArgs<TC>& a, TC* __restrict__ sBm, TC* __restrict__ sS,
+                                             float* __restrict__ redm) {
   typedef GF<TC> F;
+  typedef UpShape<TC, EPI> S;
+  constexpr bool DZ = EPI == EPI_GATE_DZ;
+  constexpr bool BWD = EPI == EPI_GATE_BWD || DZ;
+  static_assert(!DZ || sizeof(TC) == 2, "the fused dz product is bf16");
   constexpr int E = 16 / sizeof(TC);
-  constexpr int RMAX = 128;
-  constexpr int LDK = RMAX + F::PAD;
-  constexpr int BM = 128, BN = UP_BN, TM = 2, TN = BN / 16;
-  constexpr int KSTEPS = RMAX / F::KF;
-  constexpr int MAXW = BN * (RMAX / E) / UP_THREADS;  // 16-byte words of the U tile per thread
-  constexpr int LDS_ = BN + E;                         // staging pitch (elements): one 16-byte pad per row
-  constexpr int WPR = BN / E;                          // 16-byte words per staged row
-  constexpr int SW = BM * WPR / UP_THREADS;            // staged words per thread
-  __shared__ __align__(16) TC sB[2][BN * LDK];  // U blocks of the current and the next tile
-  __shared__ __align__(16) TC sS[BM * LDS_];
-  __shared__ float red[2][4 * BN];
+  constexpr int LDK = S::LDK, LDS_ = S::LDS_;
+  constexpr int BM = S::BM, BN = UP_BN, TM = 2, TN = BN / 16;
+  constexpr int KSTEPS = R / F::KF;
+  constexpr int WPU = R / E;                   // 16-byte words per U row
+  constexpr int MAXW = BN * WPU / UP_THREADS;  // 16-byte words of the U block per thread
+  constexpr int WPR = BN / E;                  // 16-byte words per staged row
+  constexpr int SW = BM * WPR / UP_THREADS;    // staged words per thread
+  static_assert(MAXW * UP_THREADS == BN * WPU && SW * UP_THREADS == BM * WPR && R <= S::RMAX, "tile layout");
 
   const int gi = blockIdx.y;
-  const int r = a.r[gi];
   const int W = a.W[gi];
   const int mt = (a.M + BM - 1) / BM;
   const int ntiles = W / BN;
-  const int ngrp = (ntiles + UP_CT - 1) / UP_CT;
+  const int ct = DZ ? ntiles : UP_CT;  // column tiles per workgroup
+  const int ngrp = (ntiles + ct - 1) / ct;
   if (static_cast<int>(blockIdx.x) >= mt * ngrp) return;
   const int mtile = blockIdx.x % mt;
-  const int t0 = (blockIdx.x / mt) * UP_CT;
-  const int t1 = min(ntiles, t0 + UP_CT);
+  const int t0 = (blockIdx.x / mt) * ct;
+  const int t1 = min(ntiles, t0 + ct);
   const int m0 = mtile * BM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = 32 * wave;
@@ -398,14 +397,12 @@ __global__ __launch_bounds__(UP_THREADS) void gate_up_kernel(GateUpArgs<TC> a) {
   const TC* __restrict__ z = a.z + a.zoff[gi];
   const TC* __restrict__ U = a.U + a.woff[gi];
   const TC* __restrict__ bias = a.bias + a.boff[gi];
+  const TC* __restrict__ dG = a.dG[gi];
   TC* __restrict__ out = a.out[gi];
-  const int ksteps = r / F::KF;
   // staged words of this wave's 32 rows: word s of the thread is row
   // wm + s * (64 / WPR) + lane / WPR, columns (lane % WPR) * E ..
   auto srow = [&](int sw) { return wm + sw * (64 / WPR) + lane / WPR; };
   const int scol = (lane % WPR) * E;
-  const int wpr = r / E;
-  const int nwords = BN * wpr;
 
   // the wave's rows of z, once
   typename F::frag fa[TM][KSTEPS];
@@ -415,21 +412,34 @@ __global__ __launch_bounds__(UP_THREADS) void gate_up_kernel(GateUpArgs<TC> a) {
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       uint4 v = {0u, 0u, 0u, 0u};
-      if (gm < a.M && ks < ksteps)
-        v = *reinterpret_cast<const uint4*>(z + static_cast<size_t>(gm) * GATE_RTOT + ks * F::KF + fk);
+      if (gm < a.M) v = *reinterpret_cast<const uint4*>(z + static_cast<size_t>(gm) * GATE_RTOT + ks * F::KF + fk);
       fa[i][ks] = __builtin_bit_cast(typename F::frag, v);
     }
   }
-  // a tile's U block and upstream gradients, to registers
+  // a tile's U block and, for the backward, this thread's staged words of the
+  // upstream gradient (rows clamped to the last; rows past it are not used)
   u32x4 rb[MAXW];
-  u32x4 dgw[SW];
+  u32x4 dgw[BWD ? SW : 1];
   const int dgrow0 = m0 + wm + lane / WPR;
-  constexpr bool BWD = EPI == EPI_GATE_BWD;
+  auto load_tile = [&](int n0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int w = 0; w < MAXW; ++w) {
+      const int idx = tid + w * UP_THREADS;
+      rb[w] = *reinterpret_cast<const u32x4*>(U + static_cast<size_t>(n0 + idx / WPU) * R + (idx % WPU) * E);
+    }
+    if constexpr (BWD) {
+#pragma unroll
+      for (int sw = 0; sw < SW; ++sw) {
+        const int gm = min(dgrow0 + sw * (64 / WPR), a.M - 1);
+        dgw[sw] = *reinterpret_cast<const u32x4*>(dG + static_cast<size_t>(gm) * W + n0 + scol);
+      }
+    }
+  };
   auto put_tile = [&](TC* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int w = 0; w < MAXW; ++w) {
-      const int idx = min(tid + w * UP_THREADS, nwords - 1);
-      *reinterpret_cast<u32x4*>(&dst[(idx / wpr) * LDK + (idx % wpr) * E]) = rb[w];
+      const int idx = tid + w * UP_THREADS;
+      *reinterpret_cast<u32x4*>(&dst[(idx / WPU) * LDK + (idx % WPU) * E]) = rb[w];
     }
     if constexpr (BWD) {
 #pragma unroll
@@ -442,22 +452,36 @@ __global__ __launch_bounds__(UP_THREADS) void gate_up_kernel(GateUpArgs<TC> a) {
       a.colsum[static_cast<size_t>(mtile) * a.colsum_ld + a.csoff[gi] + t * BN + tid] =
           rd[tid] + rd[BN + tid] + rd[2 * BN + tid] + rd[3 * BN + tid];
   };
-  up_load_tile<TC, BWD, MAXW, SW, 64 / WPR>(rb, dgw, U, a.dG[gi], t0 * BN, r, W, nwords, tid, dgrow0, a.M, scol);
-  put_tile(sB[0]);
+  // EPI_GATE_DZ: dz^T of the wave's rows, [rank tile s][row tile i] in the MFMA
+  // layout (lane: rank 16s + 4g .. + 3, row wm + 16i + fr), and the tile's
+  // dpre as bf16 operands (lane: columns 16j + 4g .. + 3, row wm + 16i + fr)
+  constexpr int RTZ = DZ ? R / 16 : 1;
+  f32x4 dzacc[RTZ][TM];
+  typename MM<TC>::frag dp[DZ ? TM : 1][DZ ? TN : 1];
+  if constexpr (DZ) {
+#pragma unroll
+    for (int s2 = 0; s2 < RTZ; ++s2)
+#pragma unroll
+      for (int i = 0; i < TM; ++i) dzacc[s2][i] = zero4();
+  }
+
+  load_tile(t0 * BN);
+  put_tile(sBm);
 
 #pragma unroll 1
   for (int t = t0; t < t1; ++t) {
     const int buf = (t - t0) & 1;
     const int n0 = t * BN;
-    // tile t's U block is in sB[buf] (and its dG words in sS); every wave is
-    // done with tile t - 1, so sB[buf ^ 1] and red[buf ^ 1] are free once read
+    const TC* sb = sBm + buf * BN * LDK;
+    float* rd = redm + buf * 4 * BN;
+    // tile t's U block is in buffer buf (and its dG words in sS); every wave is
+    // done with tile t - 1, so the other buffers are free once read
     __syncthreads();
     if constexpr (BWD) {
-      if (t > t0) put_colsum(t - 1, red[buf ^ 1]);
+      if (t > t0) put_colsum(t - 1, redm + (buf ^ 1) * 4 * BN);
     }
     // the next tile's operands, in flight during this one
-    up_load_tile<TC, BWD, MAXW, SW, 64 / WPR>(rb, dgw, U, a.dG[gi], (t + 1 < t1 ? t + 1 : t) * BN, r, W, nwords,
-                                              tid, dgrow0, a.M, scol);
+    load_tile((t + 1 < t1 ? t + 1 : t) * BN);
 
     // accumulators start from the bias (lane: columns 16j + 4g .. + 3)
     f32x4 acc[TM][TN];
@@ -467,81 +491,295 @@ __global__ __launch_bounds__(UP_THREADS) void gate_up_kernel(GateUpArgs<TC> a) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) acc[i][j] = bv;
     }
-    const TC* sb = sB[buf];
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      if (ks < ksteps) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const typename F::frag fb = F::load(&sb[(16 * j + fr) * LDK + ks * F::KF + fk]);
+      for (int j = 0; j < TN; ++j) {
+        const typename F::frag fb = F::load(&sb[(16 * j + fr) * LDK + ks * F::KF + fk]);
 #pragma unroll
-          for (int i = 0; i < TM; ++i) acc[i][j] = F::mma(fb, fa[i][ks], acc[i][j]);
-        }
+        for (int i = 0; i < TM; ++i) acc[i][j] = F::mma(fb, fa[i][ks], acc[i][j]);
       }
     }
 
     // epilogue in the MFMA layout (lane: row wm + 16i + fr, columns 16j + 4g ..
     // + 3 of the tile), through this wave's rows of the staging tile
-    float* rd = red[buf];
-    auto epilogue = [&](auto act_tag) {
-      constexpr int ACT = decltype(act_tag)::value;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int c = 16 * j + g4;
-        float cs[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TN; ++j) {
+      const int c = 16 * j + g4;
+      float cs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int row = wm + 16 * i + fr;
-          f32x4 v = acc[i][j];
-          if constexpr (!BWD) {
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm + 16 * i + fr;
+        f32x4 v = acc[i][j];
+        if constexpr (!BWD) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = act_fwd_t<ACT>(v[q]);
-          } else {
-            const f32x4 gv = load4(&sS[row * LDS_ + c]);
-            const bool row_ok = m0 + row < a.M;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              v[q] = gv[q] * act_grad_t<ACT>(v[q]);
-              cs[q] += row_ok ? v[q] : 0.f;
-            }
-          }
-          store4(&sS[row * LDS_ + c], v);
-        }
-        if constexpr (BWD) {
+          for (int q = 0; q < 4; ++q) v[q] = act_fwd_t<ACT>(v[q]);
+        } else {
+          const f32x4 gv = load4(&sS[row * LDS_ + c]);
+          const bool row_ok = m0 + row < a.M;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float sm = sum16(cs[q]);
-            if (fr == 0) rd[wave * BN + c + q] = sm;
+            v[q] = gv[q] * act_grad_t<ACT>(v[q]);
+            cs[q] += row_ok ? v[q] : 0.f;
           }
+          if constexpr (DZ) dp[i][j] = MM<TC>::from_f32(v);
+        }
+        if constexpr (!DZ) store4(&sS[row * LDS_ + c], v);
+      }
+      if constexpr (BWD) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float sm = sum16(cs[q]);
+          if (fr == 0) rd[wave * BN + c + q] = sm;
         }
       }
-    };
-    switch (a.act[gi]) {
-      case GATE_ACT_LOGSIG: epilogue(std::integral_constant<int, GATE_ACT_LOGSIG>{}); break;
-      case GATE_ACT_SIG: epilogue(std::integral_constant<int, GATE_ACT_SIG>{}); break;
-      case GATE_ACT_SIG2: epilogue(std::integral_constant<int, GATE_ACT_SIG2>{}); break;
-      default: epilogue(std::integral_constant<int, GATE_ACT_NONE>{}); break;
     }
     // this wave's rows back out in whole rows (the wave wrote them itself: LDS
-    // operations of one wave complete in order)
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    TC* o = out + n0 + scol;
+    // operations of one wave complete in order); EPI_GATE_DZ keeps no dpre
+    if constexpr (!DZ) {
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      TC* o = out + n0 + scol;
 #pragma unroll
-    for (int sw = 0; sw < SW; ++sw) {
-      const int row = srow(sw);
-      if (m0 + row < a.M)
-        *reinterpret_cast<uint4*>(o + static_cast<size_t>(m0 + row) * W) =
-            *reinterpret_cast<const uint4*>(&sS[row * LDS_ + scol]);
+      for (int sw = 0; sw < SW; ++sw) {
+        const int row = srow(sw);
+        if (m0 + row < a.M)
+          *reinterpret_cast<uint4*>(o + static_cast<size_t>(m0 + row) * W) =
+              *reinterpret_cast<const uint4*>(&sS[row * LDS_ + scol]);
+      }
     }
-    // the next tile's operands to LDS: sB[buf ^ 1] was last read in tile t - 1,
-    // which every wave finished before this tile's barrier; the dG words go to
-    // this wave's own staging rows after its reads of them above
-    if (t + 1 < t1) put_tile(sB[buf ^ 1]);
+    if constexpr (DZ) {
+      // dz^T[16s.., rows] += U_block^T dpre^T: the U block's rows 16jj + 4g ..
+      // + 3 (and the next tile's) of rank column 16s + fr, read transposed
+      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+      const TC* ub = sb + (4 * (lane >> 4) + ((lane & 15) >> 2)) * LDK + 4 * (lane & 3);
+#pragma unroll
+      for (int s2 = 0; s2 < RTZ; ++s2) {
+#pragma unroll
+        for (int jj = 0; jj < TN; jj += 2) {
+          const i16x4 u0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(ub + 16 * jj * LDK + 16 * s2));
+          const i16x4 u1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(ub + (16 * jj + 16) * LDK + 16 * s2));
+#pragma unroll
+          for (int i = 0; i < TM; ++i) dzacc[s2][i] = MM<TC>::mma2(u0, dp[i][jj], u1, dp[i][jj + 1], dzacc[s2][i]);
+        }
+      }
+    }
+    // the next tile's operands to LDS: the other U buffer was last read in
+    // tile t - 1, which every wave finished before this tile's barrier; the dG
+    // words go to this wave's own staging rows after its reads of them above
+    if (t + 1 < t1) put_tile(sBm + (buf ^ 1) * BN * LDK);
   }
   if constexpr (BWD) {
     __syncthreads();
-    put_colsum(t1 - 1, red[(t1 - 1 - t0) & 1]);
+    put_colsum(t1 - 1, redm + ((t1 - 1 - t0) & 1) * 4 * BN);
   }
+  if constexpr (DZ) {
+    // lane: dz[row wm + 16i + fr][z offset + 16s + 4g .. + 3]
+    TC* dzo = a.dz + a.zoff[gi] + g4;
+#pragma unroll
+    for (int s2 = 0; s2 < RTZ; ++s2) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int gm = m0 + wm + 16 * i + fr;
+        if (gm < a.M) store4(dzo + static_cast<size_t>(gm) * GATE_RTOT + 16 * s2, dzacc[s2][i]);
+      }
+    }
+  }
+}
+
+// One body instance per (rank, activation); the gates' ranks are 64 or 128.
+#define MUIR_GATE_FORMS(BODY)                                       \
+  switch (a.act[gi]) {                                              \
+    case GATE_ACT_LOGSIG:                                           \
+      if (r == 64) BODY(64, GATE_ACT_LOGSIG); else BODY(128, GATE_ACT_LOGSIG); \
+      break;                                                        \
+    case GATE_ACT_SIG:                                              \
+      if (r == 64) BODY(64, GATE_ACT_SIG); else BODY(128, GATE_ACT_SIG); \
+      break;                                                        \
+    case GATE_ACT_SIG2:                                             \
+      if (r == 64) BODY(64, GATE_ACT_SIG2); else BODY(128, GATE_ACT_SIG2); \
+      break;                                                        \
+    default:                                                        \
+      if (r == 64) BODY(64, GATE_ACT_NONE); else BODY(128, GATE_ACT_NONE); \
+      break;                                                        \
+  }
+
+template <typename TC, int EPI>
+__global__ __launch_bounds__(UP_THREADS) __attribute__((amdgpu_waves_per_eu(EPI == EPI_GATE_DZ ? 2 : 1))) void
+gate_up_kernel(GateUpArgs<TC> a) {
+  typedef UpShape<TC, EPI> S;
+  __shared__ __align__(16) TC sB[2 * UP_BN * S::LDK];  // U blocks of the current and the next tile
+  __shared__ __align__(16) TC sS[S::BM * S::LDS_];
+  __shared__ float red[2 * 4 * UP_BN];
+  const int gi = blockIdx.y;
+  const int r = a.r[gi];
+#define MUIR_UP_BODY(RR, AA) gate_up_body<TC, EPI, RR, AA>(a, sB, sS, red)
+  MUIR_GATE_FORMS(MUIR_UP_BODY)
+#undef MUIR_UP_BODY
+}
+
+// Arguments of the up-projections' weight-gradient kernel (bf16).
+struct GateDwArgs {
+  const uint16_t* z;      // [M, 512]
+  const uint16_t* U;      // packed up matrices ([W_i, r_i] each, rank contiguous)
+  const uint16_t* bias;   // packed biases
+  const uint16_t* dG[5];  // the gates' gradients, [M, W_i]
+  float* part;            // fp32 partials, split s at part + s * split_stride, gate i at woff[i]
+  size_t split_stride;
+  int M, ksplit, kchunk;
+  int r[5], W[5], zoff[5], act[5];
+  size_t woff[5], boff[5];
+};
+
+// dU_i = dpre_i^T z_i, summed over one split of the tokens, with
+// dpre_i = dG_i * act'(z_i U_i^T + c_i) recomputed from z instead of read
+// back (bf16).  A workgroup owns 64 columns of one gate's width (16 per
+// wave) and runs through its split in blocks of 64 tokens.  Per block:
+//   pre[t][w] (MFMA layout: lane holds tokens 4g .. + 3 of one column w),
+//     z rows from LDS times the lane's column of U, held in registers;
+//   dpre = dG * act'(pre), with dG read transposed from LDS into the same
+//     layout, so the values are already the right operand of
+//   dU^T[r][w] += z^T dpre, z read transposed from LDS (ds_read_b64_tr_b16):
+//     four consecutive tokens per lane, two token tiles per 32-deep product.
+// The next block's z and dG rows are loaded while this block computes and
+// stored into the other LDS buffer after it: one barrier per block.  Tokens
+// past M are zero (dG = 0 gives dpre = 0).  Workgroups of one split sit on
+// one XCD, so its z rows are fetched into that XCD's L2 once.  The rank and
+// activation are template arguments of the body.
+constexpr int DW_WB = 64, DW_TB = 64;
+constexpr int DW_PZ = 128 + 16;   // z rows: 288 bytes (an odd number of 32-byte units)
+constexpr int DW_PG = DW_WB + 16; // dG rows: 160 bytes
+
+template <int R, int ACT>
+__device__ __forceinline__ void gate_dw_body(const GateDwArgs& a, uint16_t* __restrict__ sZm, uint16_t* __restrict__ sGm) {
+  typedef uint16_t TC;
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  constexpr int WB = DW_WB, TB = DW_TB, PZ = DW_PZ, PG = DW_PG;
+  constexpr int RW = R / 8;                 // 16-byte words per z row of the gate
+  constexpr int ZW = TB * RW / 256;         // 16-byte z words per thread and block
+  constexpr int GW = TB * WB / 8 / 256;     // 16-byte dG words per thread and block
+  constexpr int KS = R / 32, RT = R / 16;
+  static_assert(ZW * 256 == TB * RW && GW * 256 == TB * WB / 8, "block layout");
+
+  const int gi = blockIdx.y;
+  const int W = a.W[gi];
+  const int nwt = W / WB;
+  const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+  const int wt = j % nwt;
+  const int split = (j / nwt) * 8 + xcd;
+  if (split >= a.ksplit) return;
+  const int w0 = wt * WB;
+  const int kbeg = split * a.kchunk;
+  const int kend = min(a.M, kbeg + a.kchunk);
+  const int nblk = kend > kbeg ? (kend - kbeg + TB - 1) / TB : 0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int wcol = w0 + 16 * wave + c16;
+  const TC* __restrict__ z = a.z + a.zoff[gi];
+  const TC* __restrict__ U = a.U + a.woff[gi];
+  const TC* __restrict__ dG = a.dG[gi];
+
+  // the lane's column of U as the right operand of the pre product (k = r)
+  bf16x8 ub[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    ub[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(U + static_cast<size_t>(wcol) * R + 32 * ks + 8 * g));
+  const float cb = bf16_to_f32(a.bias[a.boff[gi] + wcol]);
+
+  // Rows past the split's end are read at its last row (no branch around the
+  // loads); their dG words are then zeroed, which makes their dpre zero.
+  u32x4 zr[ZW], gr[GW];
+  auto load_block = [&](int b) __attribute__((always_inline)) {
+    const int t0 = kbeg + b * TB;
+#pragma unroll
+    for (int u = 0; u < ZW; ++u) {
+      const int idx = tid + 256 * u;
+      const int row = min(t0 + idx / RW, kend - 1), c = idx % RW;
+      zr[u] = *reinterpret_cast<const u32x4*>(z + static_cast<size_t>(row) * GATE_RTOT + 8 * c);
+    }
+#pragma unroll
+    for (int u = 0; u < GW; ++u) {
+      const int idx = tid + 256 * u;
+      const int row = t0 + (idx >> 3), c = idx & 7;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(dG + static_cast<size_t>(min(row, kend - 1)) * W + w0 + 8 * c);
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      gr[u] = row < kend ? v : zero;
+    }
+  };
+  auto store_block = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < ZW; ++u) {
+      const int idx = tid + 256 * u;
+      *reinterpret_cast<u32x4*>(&sZm[buf * TB * PZ + (idx / RW) * PZ + 8 * (idx % RW)]) = zr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < GW; ++u) {
+      const int idx = tid + 256 * u;
+      *reinterpret_cast<u32x4*>(&sGm[buf * TB * PG + (idx >> 3) * PG + 8 * (idx & 7)]) = gr[u];
+    }
+  };
+
+  f32x4 du[RT];
+#pragma unroll
+  for (int s2 = 0; s2 < RT; ++s2) du[s2] = zero4();
+
+  if (nblk > 0) {
+    load_block(0);
+    store_block(0);
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int b = 0; b < nblk; ++b) {
+    const int buf = b & 1;
+    if (b + 1 < nblk) load_block(b + 1);
+    const TC* zb = sZm + buf * TB * PZ;
+    const TC* gb = sGm + buf * TB * PG;
+    i16x4 dpf[TB / 16];
+#pragma unroll
+    for (int tt = 0; tt < TB / 16; ++tt) {
+      f32x4 acc = {cb, cb, cb, cb};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&zb[(16 * tt + c16) * PZ + 32 * ks + 8 * g])),
+            ub[ks], acc, 0, 0, 0);
+      // dG at (tokens 16tt + 4g .. + 3, column 16 wave + c16)
+      const i16x4 gq = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(gb + (16 * tt + 4 * g + (c16 >> 2)) * PG + 16 * wave + 4 * (c16 & 3)));
+      f32x4 dv;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dv[q] = bf16_to_f32(static_cast<uint16_t>(gq[q])) * act_grad_t<ACT>(acc[q]);
+      dpf[tt] = pack4(dv);
+    }
+    // dU^T[16s + 4g .., column] += z^T dpre over the block's tokens
+    const TC* zt = zb + (4 * g + (c16 >> 2)) * PZ + 4 * (c16 & 3);
+#pragma unroll
+    for (int s2 = 0; s2 < RT; ++s2) {
+#pragma unroll
+      for (int tt = 0; tt < TB / 16; tt += 2) {
+        const i16x4 z0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(zt + 16 * tt * PZ + 16 * s2));
+        const i16x4 z1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(zt + (16 * tt + 16) * PZ + 16 * s2));
+        du[s2] = mma32_bf16(z0, dpf[tt], z1, dpf[tt + 1], du[s2]);
+      }
+    }
+    // the next block into the other buffer: every wave finished reading it
+    // before this block's barrier
+    if (b + 1 < nblk) store_block(buf ^ 1);
+    __syncthreads();
+  }
+  // lane: dU[column wcol][16s + 4g .. + 3]
+  float* out = a.part + static_cast<size_t>(split) * a.split_stride + a.woff[gi] + static_cast<size_t>(wcol) * R + 4 * g;
+#pragma unroll
+  for (int s2 = 0; s2 < RT; ++s2) *reinterpret_cast<f32x4*>(out + 16 * s2) = du[s2];
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gate_dw_kernel(GateDwArgs a) {
+  __shared__ __align__(16) uint16_t sZ[2 * DW_TB * DW_PZ];
+  __shared__ __align__(16) uint16_t sG[2 * DW_TB * DW_PG];
+  const int gi = blockIdx.y;
+  const int r = a.r[gi];
+#define MUIR_DW_BODY(RR, AA) gate_dw_body<RR, AA>(a, sZ, sG)
+  MUIR_GATE_FORMS(MUIR_DW_BODY)
+#undef MUIR_DW_BODY
 }
 
 // Column sums of a [rows][ncols] fp32 array (the bias gradient from the
@@ -768,8 +1006,9 @@ GateUpArgs<TC> gate_up_args(const GateLayout& L, const TC* z, const TC* U, const
 
 template <typename TC, int EPI>
 hipError_t run_gate_up(const GateUpArgs<TC>& u, hipStream_t stream) {
+  constexpr int ct = EPI == EPI_GATE_DZ ? 1 << 30 : UP_CT;  // EPI_GATE_DZ: every column tile in one workgroup
   int gx = 0;
-  for (int i = 0; i < 5; ++i) gx = std::max(gx, ((u.M + 127) / 128) * ((u.W[i] / UP_BN + UP_CT - 1) / UP_CT));
+  for (int i = 0; i < 5; ++i) gx = std::max(gx, ((u.M + 127) / 128) * ((u.W[i] / UP_BN + ct - 1) / ct));
   if (gx == 0) return hipSuccess;
   hipLaunchKernelGGL((gate_up_kernel<TC, EPI>), dim3(gx, 5), dim3(UP_THREADS), 0, stream, u);
   return hipGetLastError();
@@ -836,10 +1075,17 @@ hipError_t gate_bwd_typed(const GateShape& s, const void* x, const void* W_down,
       u.csoff[i] = coff;
       coff += L.W[i];
     }
-    if ((e = run_gate_up<TC, EPI_GATE_BWD>(u, stream)) != hipSuccess) return e;
+    if constexpr (sizeof(TC) == 2) {
+      // with 2. fused: dz[:, slice_i] = dpre_i U_i; dpre itself is not kept
+      // (the weight gradient recomputes it)
+      u.dz = dz;
+      if ((e = run_gate_up<TC, EPI_GATE_DZ>(u, stream)) != hipSuccess) return e;
+    } else {
+      if ((e = run_gate_up<TC, EPI_GATE_BWD>(u, stream)) != hipSuccess) return e;
+    }
   }
   // 2. dz[:, slice_i] = dpre_i U_i
-  {
+  if constexpr (sizeof(TC) == 4) {
     GemmBatch u = {};
     u.n = 5;
     u.ksplit = 1;
@@ -873,15 +1119,42 @@ hipError_t gate_bwd_typed(const GateShape& s, const void* x, const void* W_down,
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   {
-    GemmBatch u = {};
-    u.n = 5;
-    u.ksplit = W.ksplit;
-    u.kchunk = W.kchunk;
-    u.split_stride = W.part_stride;
-    for (int i = 0; i < 5; ++i)
-      u.p[i] = GemmProblem{dpre + dpo[i], zr + L.zoff[i], part + L.woff[i], L.W[i], L.r[i], s.M, L.W[i], GATE_RTOT,
-                           L.r[i]};
-    if ((e = run_gemm<TC, 128, 128, false, false, EPI_PARTIAL>(u, stream)) != hipSuccess) return e;
+    if constexpr (sizeof(TC) == 2) {
+      // dpre recomputed from z (never stored)
+      GateDwArgs d = {};
+      d.z = zr;
+      d.U = Wu;
+      d.bias = bs;
+      d.part = part;
+      d.split_stride = W.part_stride;
+      d.M = s.M;
+      d.ksplit = W.ksplit;
+      d.kchunk = W.kchunk;
+      int nwt = 0;
+      for (int i = 0; i < 5; ++i) {
+        d.dG[i] = static_cast<const TC*>(dgates[i]);
+        d.r[i] = L.r[i];
+        d.W[i] = L.W[i];
+        d.zoff[i] = L.zoff[i];
+        d.act[i] = kActs[i];
+        d.woff[i] = L.woff[i];
+        d.boff[i] = L.boff[i];
+        nwt = std::max(nwt, L.W[i] / 64);
+      }
+      const int gx = 8 * nwt * ((W.ksplit + 7) / 8);
+      hipLaunchKernelGGL(gate_dw_kernel, dim3(gx, 5), dim3(256), 0, stream, d);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+      GemmBatch u = {};
+      u.n = 5;
+      u.ksplit = W.ksplit;
+      u.kchunk = W.kchunk;
+      u.split_stride = W.part_stride;
+      for (int i = 0; i < 5; ++i)
+        u.p[i] = GemmProblem{dpre + dpo[i], zr + L.zoff[i], part + L.woff[i], L.W[i], L.r[i], s.M, L.W[i], GATE_RTOT,
+                             L.r[i]};
+      if ((e = run_gemm<TC, 128, 128, false, false, EPI_PARTIAL>(u, stream)) != hipSuccess) return e;
+    }
     const size_t n = L.woff[4] + static_cast<size_t>(L.r[4]) * L.W[4];
     hipLaunchKernelGGL(split_sum_kernel, dim3(static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 4096))), dim3(256),
                        0, stream, part, W.ksplit, W.part_stride, n, dW_up);
@@ -911,10 +1184,11 @@ GateWorkspace gate_workspace(const GateShape& s) {
   size_t off = 0;
   w.z_off = off;
   off += r256(static_cast<size_t>(s.M) * GATE_RTOT * tc);
+  // dpre is kept only by the fp32 path (bf16 recomputes it where it is used)
   w.dpre_off = off;
   size_t dp = 0;
   for (int i = 0; i < 5; ++i) dp += static_cast<size_t>(s.M) * L.W[i];
-  off += r256(dp * tc);
+  if (!s.bf16) off += r256(dp * tc);
   w.dz_off = off;
   off += r256(static_cast<size_t>(s.M) * GATE_RTOT * tc);
   // the token contraction of the weight gradients is split so that the

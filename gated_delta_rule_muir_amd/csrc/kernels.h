@@ -176,7 +176,7 @@ struct GateShape {
   int M, d, H, dk, dv;
   bool bf16;
 };
-// Backward workspace: recomputed z, dpre of the five gates, dz, split
+// Backward workspace: recomputed z, dpre of the five gates (fp32 only), dz, split
 // partials of the weight gradients and the per-tile column sums.
 struct GateWorkspace {
   size_t z_off, dpre_off, dz_off, part_off, colsum_off, bytes;
