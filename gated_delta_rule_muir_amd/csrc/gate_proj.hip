@@ -632,8 +632,9 @@ struct GateDwArgs {
 
 // dU_i = dpre_i^T z_i, summed over one split of the tokens, with
 // dpre_i = dG_i * act'(z_i U_i^T + c_i) recomputed from z instead of read
-// back (bf16).  A workgroup owns 64 columns of one gate's width (16 per
-// wave) and runs through its split in blocks of 64 tokens.  Per block:
+// back (bf16).  A workgroup owns 128 columns of one gate's width (32 per
+// wave, two 16-column tiles that share every z operand read) and runs
+// through its split in blocks of 64 tokens.  Per block:
 //   pre[t][w] (MFMA layout: lane holds tokens 4g .. + 3 of one column w),
 //     z rows from LDS times the lane's column of U, held in registers;
 //   dpre = dG * act'(pre), with dG read transposed from LDS into the same
@@ -645,24 +646,26 @@ struct GateDwArgs {
 // past M are zero (dG = 0 gives dpre = 0).  Workgroups of one split sit on
 // one XCD, so its z rows are fetched into that XCD's L2 once.  The rank and
 // activation are template arguments of the body.
-constexpr int DW_WB = 64, DW_TB = 64;
-constexpr int DW_PZ = 128 + 16;   // z rows: 288 bytes (an odd number of 32-byte units)
-constexpr int DW_PG = DW_WB + 16; // dG rows: 160 bytes
+constexpr int DW_WPW = 2;               // 16-column tiles per wave
+constexpr int DW_WB = 64 * DW_WPW, DW_TB = 64;
+constexpr int DW_PZ = 128 + 16;         // z rows: 288 bytes (an odd number of 32-byte units)
+constexpr int DW_PG = DW_WB + 16;       // dG rows: 288 bytes
 
 template <int R, int ACT>
 __device__ __forceinline__ void gate_dw_body(const GateDwArgs& a, uint16_t* __restrict__ sZm, uint16_t* __restrict__ sGm) {
   typedef uint16_t TC;
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  constexpr int WB = DW_WB, TB = DW_TB, PZ = DW_PZ, PG = DW_PG;
+  constexpr int WB = DW_WB, TB = DW_TB, PZ = DW_PZ, PG = DW_PG, WPW = DW_WPW;
   constexpr int RW = R / 8;                 // 16-byte words per z row of the gate
+  constexpr int GWR = WB / 8;               // 16-byte words per dG row
   constexpr int ZW = TB * RW / 256;         // 16-byte z words per thread and block
-  constexpr int GW = TB * WB / 8 / 256;     // 16-byte dG words per thread and block
+  constexpr int GW = TB * GWR / 256;        // 16-byte dG words per thread and block
   constexpr int KS = R / 32, RT = R / 16;
-  static_assert(ZW * 256 == TB * RW && GW * 256 == TB * WB / 8, "block layout");
+  static_assert(ZW * 256 == TB * RW && GW * 256 == TB * GWR, "block layout");
 
   const int gi = blockIdx.y;
   const int W = a.W[gi];
-  const int nwt = W / WB;
+  const int nwt = (W + WB - 1) / WB;  // (W is a multiple of 64: the last group may be half)
   const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
   const int wt = j % nwt;
   const int split = (j / nwt) * 8 + xcd;
@@ -673,17 +676,22 @@ __device__ __forceinline__ void gate_dw_body(const GateDwArgs& a, uint16_t* __re
   const int nblk = kend > kbeg ? (kend - kbeg + TB - 1) / TB : 0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int wcol = w0 + 16 * wave + c16;
+  const int wl = 16 * WPW * wave;  // the wave's first column within the workgroup's
   const TC* __restrict__ z = a.z + a.zoff[gi];
   const TC* __restrict__ U = a.U + a.woff[gi];
   const TC* __restrict__ dG = a.dG[gi];
 
-  // the lane's column of U as the right operand of the pre product (k = r)
-  bf16x8 ub[KS];
+  // the lane's columns of U as right operands of the pre product (k = r)
+  bf16x8 ub[WPW][KS];
+  float cb[WPW];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    ub[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(U + static_cast<size_t>(wcol) * R + 32 * ks + 8 * g));
-  const float cb = bf16_to_f32(a.bias[a.boff[gi] + wcol]);
+  for (int u = 0; u < WPW; ++u) {
+    const int wcol = min(w0 + wl + 16 * u + c16, W - 1);  // columns past W: zero dG, not stored
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      ub[u][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(U + static_cast<size_t>(wcol) * R + 32 * ks + 8 * g));
+    cb[u] = bf16_to_f32(a.bias[a.boff[gi] + wcol]);
+  }
 
   // Rows past the split's end are read at its last row (no branch around the
   // loads); their dG words are then zeroed, which makes their dpre zero.
@@ -699,10 +707,10 @@ __device__ __forceinline__ void gate_dw_body(const GateDwArgs& a, uint16_t* __re
 #pragma unroll
     for (int u = 0; u < GW; ++u) {
       const int idx = tid + 256 * u;
-      const int row = t0 + (idx >> 3), c = idx & 7;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(dG + static_cast<size_t>(min(row, kend - 1)) * W + w0 + 8 * c);
+      const int row = t0 + idx / GWR, col = w0 + 8 * (idx % GWR);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(dG + static_cast<size_t>(min(row, kend - 1)) * W + (col < W ? col : w0));
       const u32x4 zero = {0u, 0u, 0u, 0u};
-      gr[u] = row < kend ? v : zero;
+      gr[u] = row < kend && col < W ? v : zero;
     }
   };
   auto store_block = [&](int buf) __attribute__((always_inline)) {
@@ -714,13 +722,15 @@ __device__ __forceinline__ void gate_dw_body(const GateDwArgs& a, uint16_t* __re
 #pragma unroll
     for (int u = 0; u < GW; ++u) {
       const int idx = tid + 256 * u;
-      *reinterpret_cast<u32x4*>(&sGm[buf * TB * PG + (idx >> 3) * PG + 8 * (idx & 7)]) = gr[u];
+      *reinterpret_cast<u32x4*>(&sGm[buf * TB * PG + (idx / GWR) * PG + 8 * (idx % GWR)]) = gr[u];
     }
   };
 
-  f32x4 du[RT];
+  f32x4 du[RT][WPW];
 #pragma unroll
-  for (int s2 = 0; s2 < RT; ++s2) du[s2] = zero4();
+  for (int s2 = 0; s2 < RT; ++s2)
+#pragma unroll
+    for (int u = 0; u < WPW; ++u) du[s2][u] = zero4();
 
   if (nblk > 0) {
     load_block(0);
@@ -733,24 +743,28 @@ __device__ __forceinline__ void gate_dw_body(const GateDwArgs& a, uint16_t* __re
     if (b + 1 < nblk) load_block(b + 1);
     const TC* zb = sZm + buf * TB * PZ;
     const TC* gb = sGm + buf * TB * PG;
-    i16x4 dpf[TB / 16];
+    i16x4 dpf[TB / 16][WPW];
 #pragma unroll
     for (int tt = 0; tt < TB / 16; ++tt) {
-      f32x4 acc = {cb, cb, cb, cb};
+      bf16x8 za[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&zb[(16 * tt + c16) * PZ + 32 * ks + 8 * g])),
-            ub[ks], acc, 0, 0, 0);
-      // dG at (tokens 16tt + 4g .. + 3, column 16 wave + c16)
-      const i16x4 gq = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(gb + (16 * tt + 4 * g + (c16 >> 2)) * PG + 16 * wave + 4 * (c16 & 3)));
-      f32x4 dv;
+        za[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&zb[(16 * tt + c16) * PZ + 32 * ks + 8 * g]));
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dv[q] = bf16_to_f32(static_cast<uint16_t>(gq[q])) * act_grad_t<ACT>(acc[q]);
-      dpf[tt] = pack4(dv);
+      for (int u = 0; u < WPW; ++u) {
+        f32x4 acc = {cb[u], cb[u], cb[u], cb[u]};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(za[ks], ub[u][ks], acc, 0, 0, 0);
+        // dG at (tokens 16tt + 4g .. + 3, the lane's column)
+        const i16x4 gq = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(gb + (16 * tt + 4 * g + (c16 >> 2)) * PG + wl + 16 * u + 4 * (c16 & 3)));
+        f32x4 dv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dv[q] = bf16_to_f32(static_cast<uint16_t>(gq[q])) * act_grad_t<ACT>(acc[q]);
+        dpf[tt][u] = pack4(dv);
+      }
     }
-    // dU^T[16s + 4g .., column] += z^T dpre over the block's tokens
+    // dU^T[16s + 4g .., columns] += z^T dpre over the block's tokens
     const TC* zt = zb + (4 * g + (c16 >> 2)) * PZ + 4 * (c16 & 3);
 #pragma unroll
     for (int s2 = 0; s2 < RT; ++s2) {
@@ -758,7 +772,8 @@ __device__ __forceinline__ void gate_dw_body(const GateDwArgs& a, uint16_t* __re
       for (int tt = 0; tt < TB / 16; tt += 2) {
         const i16x4 z0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(zt + 16 * tt * PZ + 16 * s2));
         const i16x4 z1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(zt + (16 * tt + 16) * PZ + 16 * s2));
-        du[s2] = mma32_bf16(z0, dpf[tt], z1, dpf[tt + 1], du[s2]);
+#pragma unroll
+        for (int u = 0; u < WPW; ++u) du[s2][u] = mma32_bf16(z0, dpf[tt][u], z1, dpf[tt + 1][u], du[s2][u]);
       }
     }
     // the next block into the other buffer: every wave finished reading it
@@ -766,10 +781,15 @@ __device__ __forceinline__ void gate_dw_body(const GateDwArgs& a, uint16_t* __re
     if (b + 1 < nblk) store_block(buf ^ 1);
     __syncthreads();
   }
-  // lane: dU[column wcol][16s + 4g .. + 3]
-  float* out = a.part + static_cast<size_t>(split) * a.split_stride + a.woff[gi] + static_cast<size_t>(wcol) * R + 4 * g;
+  // lane: dU[column][16s + 4g .. + 3]
 #pragma unroll
-  for (int s2 = 0; s2 < RT; ++s2) *reinterpret_cast<f32x4*>(out + 16 * s2) = du[s2];
+  for (int u = 0; u < WPW; ++u) {
+    const int wcol = w0 + wl + 16 * u + c16;
+    if (w0 + wl + 16 * u >= W) continue;
+    float* out = a.part + static_cast<size_t>(split) * a.split_stride + a.woff[gi] + static_cast<size_t>(wcol) * R + 4 * g;
+#pragma unroll
+    for (int s2 = 0; s2 < RT; ++s2) *reinterpret_cast<f32x4*>(out + 16 * s2) = du[s2][u];
+  }
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gate_dw_kernel(GateDwArgs a) {
@@ -1139,7 +1159,7 @@ hipError_t gate_bwd_typed(const GateShape& s, const void* x, const void* W_down,
         d.act[i] = kActs[i];
         d.woff[i] = L.woff[i];
         d.boff[i] = L.boff[i];
-        nwt = std::max(nwt, L.W[i] / 64);
+        nwt = std::max(nwt, (L.W[i] + DW_WB - 1) / DW_WB);
       }
       const int gx = 8 * nwt * ((W.ksplit + 7) / 8);
       hipLaunchKernelGGL(gate_dw_kernel, dim3(gx, 5), dim3(256), 0, stream, d);
