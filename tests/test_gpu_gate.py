@@ -38,6 +38,9 @@ CASES = [
     ("bf16_M129_d64_H1_dk64_dv128", 129, 64, 1, 64, 128, "bf16"),
     ("f32_M9000_d128_H1_d64_splits", 9000, 128, 1, 64, 64, "f32"),
     ("bf16_M9000_d256_H2_d128_splits", 9000, 256, 2, 128, 128, "bf16"),
+    # key widths of 192 columns (a half group of 128 in the weight-gradient
+    # kernel) with the tokens split 3 ways
+    ("bf16_M9000_d128_H3_dk64_dv128_splits", 9000, 128, 3, 64, 128, "bf16"),
 ]
 
 
