@@ -142,6 +142,40 @@ __device__ __forceinline__ void transpose_block(const uint4 (&in)[4], uint4 (&ou
     for (int r = 0; r < 4; ++r) o[4 * c + r] = w[4 * r + c];
 }
 
+// GEMM epilogue, from registers: acc[i][j][r] = C[mw + 16i + fr][nw + 16j + 4g
+// + r] (g = lane / 16, fr = lane % 16), stored in the compute type or as
+// split s's fp32 partial.
+template <typename TC, int TM, int TN, int EPI>
+__device__ __forceinline__ void gemm_store(const f32x4 (&acc)[TM][TN], const GemmProblem& P, const GemmBatch& batch,
+                                           int split, int mw, int nw, int lane) {
+  const int fr = lane & 15, g4 = 4 * (lane >> 4);
+  if constexpr (EPI == EPI_PARTIAL) {
+    float* out = static_cast<float*>(P.C) + static_cast<size_t>(split) * batch.split_stride;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int gm = mw + 16 * i + fr;
+      if (gm >= P.M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int gn = nw + 16 * j + g4;
+        if (gn < P.N) *reinterpret_cast<f32x4*>(out + static_cast<size_t>(gm) * P.ldc + gn) = acc[i][j];
+      }
+    }
+  } else {
+    TC* out = static_cast<TC*>(P.C);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int gm = mw + 16 * i + fr;
+      if (gm >= P.M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int gn = nw + 16 * j + g4;
+        if (gn < P.N) store4(out + static_cast<size_t>(gm) * P.ldc + gn, acc[i][j]);
+      }
+    }
+  }
+}
+
 // Grouped GEMM, C_g = A_g B_g for the problems of `batch` (blockIdx.y picks
 // problem and contraction split).  128 x BN tile on four waves (2 x 2), each
 // wave 64 x BN/2 as 16 x 16 MFMA tiles.  The MFMA is issued with the B tile
@@ -292,34 +326,141 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmBatch batch) {
     __syncthreads();
   }
 
-  // ---- epilogue, from registers ------------------------------------------------
-  // acc[i][j][r] = C[m0 + wm + 16i + fr][n0 + wn + 16j + 4g + r], g = lane / 16
-  const int g4 = 4 * (lane >> 4);
-  if constexpr (EPI == EPI_PARTIAL) {
-    float* out = static_cast<float*>(P.C) + static_cast<size_t>(split) * batch.split_stride;
+  gemm_store<TC, TM, TN, EPI>(acc, P, batch, split, m0 + wm, n0 + wn, lane);
+}
+
+// The bf16 grouped GEMM with its operand tiles moved straight from global
+// memory into LDS (global_load_lds_dwordx4): no register staging and no
+// transposes.  Tile, waves and epilogue as gemm_kernel (128 x 128 on four
+// waves, 64-deep steps).  Two LDS stages, each its own __shared__ array: the
+// compiler then sees that one step's loads into one stage do not write what
+// the step reads from the other (it would otherwise wait for those loads
+// before every LDS read), and the loop is unrolled by two so that each
+// step names its stages statically.  A step waits for its own stage's loads
+// (vmcnt 0) and meets the other waves at a barrier, issues the next step's
+// loads into the other stage (which every wave finished reading in the
+// previous step), then forms its products.
+// Stage layouts, with each row's 16-byte words permuted so that both the
+// direct writes (1 KB contiguous per wave instruction) and the fragment
+// reads are free of bank conflicts:
+//   k-contiguous operand: [128 rows][64 k], 128-byte rows; word w of row r
+//     at position w ^ ((r >> 1) & 7); fragments by ds_read_b128;
+//   k-strided operand: [64 k][128 columns], 256-byte rows; word w of row r
+//     at position w ^ 2 ((r & 3) + 4 ((r >> 3) & 1)); fragments by two
+//     transposing reads (ds_read_b64_tr_b16) of four k rows each.
+// Every split's contraction range is whole 64-deep steps (the launcher
+// checks; other shapes take gemm_kernel).  Rows and columns past M and N
+// read the last valid ones and are not stored.
+template <bool A_KC, bool B_KC, int EPI>
+__global__ __launch_bounds__(GEMM_THREADS) void gemm_lds_kernel(GemmBatch batch) {
+  typedef uint16_t TC;
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  typedef __attribute__((address_space(3))) void lds_void;
+  constexpr int BM = 128, BN = 128, BK = 64, TM = BM / 32, TN = BN / 32;
+  constexpr int TILE = 128 * BK;
+  __shared__ __align__(16) TC sA0[TILE];
+  __shared__ __align__(16) TC sA1[TILE];
+  __shared__ __align__(16) TC sB0[TILE];
+  __shared__ __align__(16) TC sB1[TILE];
+
+  const int grp = blockIdx.y / batch.ksplit;
+  const int split = blockIdx.y - grp * batch.ksplit;
+  const GemmProblem& P = batch.p[grp];
+  const int mt = (P.M + BM - 1) / BM, nt = (P.N + BN - 1) / BN;
+  const int ntile = mt * nt;
+  const int per_xcd = (ntile + 7) / 8;
+  const int t = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (static_cast<int>(blockIdx.x / 8) >= per_xcd || t >= ntile) return;
+  const int m0 = (t / nt) * BM;
+  const int n0 = (t % nt) * BN;
+  const int kbeg = split * batch.kchunk;
+  const int kend = min(P.K, kbeg + batch.kchunk);
+  const int nk = kend > kbeg ? (kend - kbeg) / BK : 0;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = (wave >> 1) * (BM / 2);
+  const int wn = (wave & 1) * (BN / 2);
+  const TC* __restrict__ gA = static_cast<const TC*>(P.A);
+  const TC* __restrict__ gB = static_cast<const TC*>(P.B);
+
+  // one operand tile into a stage: k-contiguous rows r0.. (k along the row)
+  auto load_kc = [&](TC* dst, const TC* g, int ld, int rows_valid, int r0, int k0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int gm = m0 + wm + 16 * i + fr;
-      if (gm >= P.M) continue;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int gn = n0 + wn + 16 * j + g4;
-        if (gn < P.N) *reinterpret_cast<f32x4*>(out + static_cast<size_t>(gm) * P.ldc + gn) = acc[i][j];
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int row = 32 * wave + 8 * j + (lane >> 3);
+      const int w = (lane & 7) ^ ((row >> 1) & 7);
+      const TC* src = g + static_cast<size_t>(min(r0 + row, rows_valid - 1)) * ld + k0 + 8 * w;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + (32 * wave + 8 * j) * BK), 16, 0, 0);
     }
-  } else {
-    TC* out = static_cast<TC*>(P.C);
+  };
+  // ... or k-strided: k rows k0 .., columns c0 .. c0 + 127
+  auto load_ks = [&](TC* dst, const TC* g, int ld, int cols_valid, int c0, int k0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int gm = m0 + wm + 16 * i + fr;
-      if (gm >= P.M) continue;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int gn = n0 + wn + 16 * j + g4;
-        if (gn < P.N) store4(out + static_cast<size_t>(gm) * P.ldc + gn, acc[i][j]);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * wave + 4 * j + (lane >> 4);
+      const int w = (lane & 15) ^ (2 * ((row & 3) + 4 * ((row >> 3) & 1)));
+      const TC* src = g + static_cast<size_t>(k0 + row) * ld + min(c0 + 8 * w, cols_valid - 8);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + (16 * wave + 4 * j) * 128), 16, 0, 0);
     }
+  };
+  auto load_step = [&](TC* a, TC* b, int k0) __attribute__((always_inline)) {
+    if constexpr (A_KC) load_kc(a, gA, P.lda, P.M, m0, k0);
+    else load_ks(a, gA, P.lda, P.M, m0, k0);
+    if constexpr (B_KC) load_kc(b, gB, P.ldb, P.N, n0, k0);
+    else load_ks(b, gB, P.ldb, P.N, n0, k0);
+  };
+  // fragment of row / column `rc` of a stage, k = 32 ks + 8 (lane / 16) .. + 7
+  auto frag = [&](const TC* st, int rc, int ks, auto kc_tag) __attribute__((always_inline)) -> bf16x8 {
+    constexpr bool KC = decltype(kc_tag)::value;
+    const int g = lane >> 4;
+    if constexpr (KC) {
+      const int r = rc + (lane & 15);
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + r * BK + 8 * ((4 * ks + g) ^ ((r >> 1) & 7))));
+    } else {
+      const int l = lane & 15;
+      const int w = (rc >> 3) + ((l & 3) >> 1);
+      i16x4 h[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int rr = 32 * ks + 8 * g + 4 * hh + (l >> 2);
+        h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(st + rr * 128 + 8 * (w ^ (2 * ((rr & 3) + 4 * ((rr >> 3) & 1)))) + 4 * (l & 1)));
+      }
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = zero4();
+
+  auto step = [&](const TC* a, const TC* b, TC* an, TC* bn, int kt) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of this stage are in LDS
+    __syncthreads();                      // and every wave's
+    if (kt + 1 < nk) load_step(an, bn, kbeg + (kt + 1) * BK);
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      bf16x8 fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[i] = frag(a, wm + 16 * i, ks, std::integral_constant<bool, A_KC>{});
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[j] = frag(b, wn + 16 * j, ks, std::integral_constant<bool, B_KC>{});
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    }
+  };
+  if (nk > 0) load_step(sA0, sB0, kbeg);
+#pragma unroll 1
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(sA0, sB0, sA1, sB1, kt);
+    if (kt + 1 < nk) step(sA1, sB1, sA0, sB0, kt + 1);
   }
+  gemm_store<TC, TM, TN, EPI>(acc, P, batch, split, m0 + wm, n0 + wn, lane);
 }
 
 // Activation as a template argument (one instance per gate form).
@@ -966,6 +1107,18 @@ hipError_t run_gemm(const GemmBatch& b, hipStream_t stream) {
   for (int i = 0; i < b.n; ++i) tiles = std::max(tiles, ((b.p[i].M + BM - 1) / BM) * ((b.p[i].N + BN - 1) / BN));
   if (tiles == 0) return hipSuccess;
   const int grid = (tiles + 7) / 8 * 8;  // whole rounds of the 8 XCDs
+  if constexpr (sizeof(TC) == 2 && BM == 128 && BN == 128 && BK == 64) {
+    // whole 64-deep steps in every split, 16-byte rows: the LDS-direct kernel
+    bool whole = b.kchunk % BK == 0;
+    for (int i = 0; i < b.n; ++i)
+      whole = whole && b.p[i].K % BK == 0 && b.p[i].lda % 8 == 0 && b.p[i].ldb % 8 == 0 && b.p[i].M >= 8 &&
+              b.p[i].N >= 8;
+    if (whole) {
+      hipLaunchKernelGGL((gemm_lds_kernel<A_KC, B_KC, EPI>), dim3(grid, b.n * b.ksplit), dim3(GEMM_THREADS), 0, stream,
+                         b);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((gemm_kernel<TC, BM, BN, A_KC, B_KC, EPI, BK>), dim3(grid, b.n * b.ksplit), dim3(GEMM_THREADS), 0,
                      stream, b);
   return hipGetLastError();
