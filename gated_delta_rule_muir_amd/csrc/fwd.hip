@@ -137,7 +137,10 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
   // formed while block I's are read)
   __shared__ __attribute__((aligned(16))) TC sT[NBUF][16][20];
   __shared__ __attribute__((aligned(16))) TC sP[NBUF][16][20];
-  __shared__ __attribute__((aligned(16))) TC sStage[16][2 * DK + 8];
+  // W and Q' rows of a block on their way to the summary; in bf16 one buffer
+  // per block parity, so a block's copy-out needs no closing barrier (the
+  // buffer is written again two blocks later, after two barriers)
+  __shared__ __attribute__((aligned(16))) TC sStage[NBUF][16][2 * DK + 8];
 
   // ---- the next block's inputs are loaded one block ahead (4 tokens of
   // channel ej), kept raw until used (a conversion at the load would wait
@@ -426,8 +429,8 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
         const f32x4 qv = load4(&sQh[bb][j][4 * g]) - op;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          sStage[4 * g + i][j] = M::cvt(uw[i]);
-          sStage[4 * g + i][DK + j] = M::cvt(qv[i]);
+          sStage[tb][4 * g + i][j] = M::cvt(uw[i]);
+          sStage[tb][4 * g + i][DK + j] = M::cvt(qv[i]);
         }
       }
     }
@@ -451,11 +454,11 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
         const int j4 = (idx - r * (DK / 4)) * 4;
         typedef typename Raw4<TC>::type R4;
         *reinterpret_cast<R4*>(out.W + static_cast<size_t>(r0 + r) * DK + j4) =
-            *reinterpret_cast<const R4*>(&sStage[r][j4]);
+            *reinterpret_cast<const R4*>(&sStage[tb][r][j4]);
         *reinterpret_cast<R4*>(out.Qp + static_cast<size_t>(r0 + r) * DK + j4) =
-            *reinterpret_cast<const R4*>(&sStage[r][DK + j4]);
+            *reinterpret_cast<const R4*>(&sStage[tb][r][DK + j4]);
       }
-      __syncthreads();
+      if (!PIPE) __syncthreads();
     }
   }
 }
