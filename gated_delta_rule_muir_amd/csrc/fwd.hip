@@ -148,6 +148,10 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
   // block's are issued before the prologue's own loads, so that both wait
   // on one round trip ----
   Tin pk[4], pe[4], pq[4], pg[4], pv[4], pw[4], pl[4];
+  // 64-token chunks (bf16): the block sums' log_a words are kept and used by
+  // the blocks' elementwise work instead of a second read
+  constexpr bool KEEPL = PIPE && NB == 4;
+  i16x4 lk0, lk1, lk2, lk3;  // (named, not an array: a private array would be placed in LDS)
   auto prefetch = [&](int I) {
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -158,7 +162,7 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
       pg[rr] = *at(gsel, static_cast<uint32_t>(16 * I + 4 * part + rr) * gts + static_cast<uint32_t>(ej));
       pv[rr] = *at(vb, o);
       pw[rr] = *at(wb, o);
-      pl[rr] = *at(lb, o);
+      if constexpr (!KEEPL) pl[rr] = *at(lb, o);
     }
   };
 
@@ -171,7 +175,17 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
   for (int I = 0; I < NB; ++I) {
     float sacc = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) sacc += ldv(lb, gi(16 * I + 4 * part + rr, ej));
+    for (int rr = 0; rr < 4; ++rr) {
+      const Tin raw = *at(lb, gi(16 * I + 4 * part + rr, ej));
+      if constexpr (KEEPL) {
+        const short w = static_cast<short>(raw);
+        if (I == 0) lk0[rr] = w;
+        else if (I == 1) lk1[rr] = w;
+        else if (I == 2) lk2[rr] = w;
+        else lk3[rr] = w;
+      }
+      sacc += M::to_f32(raw);
+    }
     sPart[I][part][ej] = sacc;
   }
   __syncthreads();
@@ -225,7 +239,13 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
       gv[rr] = gmode == GAMMA_NONE ? 1.f : M::to_f32(pg[rr]);
       vv[rr] = M::to_f32(pv[rr]);
       wv[rr] = M::to_f32(pw[rr]);
-      lv[rr] = M::to_f32(pl[rr]);
+      if constexpr (KEEPL) {
+        // block I's words by selects (no run-time index into the register array)
+        const short x = I == 0 ? lk0[rr] : I == 1 ? lk1[rr] : I == 2 ? lk2[rr] : lk3[rr];
+        lv[rr] = M::to_f32(static_cast<Tin>(x));
+      } else {
+        lv[rr] = M::to_f32(pl[rr]);
+      }
     }
     prefetch(I + 1 < NB ? I + 1 : I);
     // direct partial sums (never differences of cumulative sums): prefix of
