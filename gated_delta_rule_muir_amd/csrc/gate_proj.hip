@@ -6,16 +6,21 @@
 //
 // The gates' up-projections run in gate_up_kernel (the rank-64/128
 // contraction with the activation, or its gradient and the bias sums, fused
-// into the epilogue).  Every other product runs through one grouped GEMM
-// kernel: up to five independent problems per launch, 128 x BN tiles on four
-// waves, bf16 (v_mfma_f32_16x16x32_bf16) or fp32 (v_mfma_f32_16x16x4_f32)
-// with fp32 accumulation, and an epilogue chosen at compile time:
+// into the epilogue; in the bf16 backward also dz = dpre U).  The bf16
+// backward forms dU = dpre^T z in gate_dw_kernel, with dpre recomputed from z,
+// so dpre is never stored.  Every other product runs through a grouped GEMM:
+// up to five independent problems per launch, 128 x 128 tiles on four waves,
+// bf16 (v_mfma_f32_16x16x32_bf16) or fp32 (v_mfma_f32_16x16x4_f32) with fp32
+// accumulation, and an epilogue chosen at compile time:
 //   EPI_STORE     C = acc, in the compute type
 //   EPI_PARTIAL   fp32 partial of one split of the contraction
 // Operands are read either along their contiguous axis (k contiguous: rows of
-// A, columns of B^T) or across it (k strided), the latter transposed on the
-// way into LDS, so every product here -- x W_down^T, dpre U, dz W_down,
-// dz^T x, dpre^T z -- runs without an explicit transpose.
+// A, columns of B^T) or across it (k strided), so every product here --
+// x W_down^T, dz W_down, dz^T x, and in fp32 dpre U and dpre^T z -- runs
+// without an explicit transpose: bf16 tiles go straight from global memory
+// into LDS (gemm_lds_kernel) and k-strided ones are read with transposing LDS
+// reads; the register-staged gemm_kernel (fp32, and bf16 shapes that are not
+// whole 64-deep steps) transposes them on the way into LDS.
 #include <algorithm>
 #include <type_traits>
 
