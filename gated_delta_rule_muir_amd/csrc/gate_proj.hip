@@ -6,9 +6,10 @@
 //
 // The gates' up-projections run in gate_up_kernel (the rank-64/128
 // contraction with the activation, or its gradient and the bias sums, fused
-// into the epilogue; in the bf16 backward also dz = dpre U).  The bf16
-// backward forms dU = dpre^T z in gate_dw_kernel, with dpre recomputed from z,
-// so dpre is never stored.  Every other product runs through a grouped GEMM:
+// into the epilogue).  The bf16 backward runs two bodies in one launch
+// (gate_bwd_up_kernel): dpre with dz = dpre U, and dU = dpre^T z with the
+// bias sums, each recomputing dpre from z, so dpre is never stored.  Every
+// other product runs through a grouped GEMM:
 // up to five independent problems per launch, 128 x 128 tiles on four waves,
 // bf16 (v_mfma_f32_16x16x32_bf16) or fp32 (v_mfma_f32_16x16x4_f32) with fp32
 // accumulation, and an epilogue chosen at compile time:
@@ -42,7 +43,7 @@ enum Epi {
   EPI_GATE = 1,      // up-projection: gate = act(acc + bias)
   EPI_GATE_BWD = 2,  // up-projection: dpre = dG * act'(acc + bias), with per-tile column sums
   EPI_PARTIAL = 3,   // general GEMM: fp32 partial of one split of the contraction
-  EPI_GATE_DZ = 4    // up-projection: as EPI_GATE_BWD, and dz = dpre U accumulated over the whole width
+  EPI_GATE_DZ = 4    // up-projection: dpre as EPI_GATE_BWD (no column sums), and dz = dpre U over the whole width
 };
 
 // Per-compute-type GEMM fragment: bf16 contracts 32 per MFMA (8 values per
@@ -509,12 +510,15 @@ template <typename TC, int EPI> struct UpShape {
 };
 
 template <typename TC, int EPI, int R, int ACT>
-__device__ __forceinline__ void gate_up_body(const GateUpArgs<TC>& a, TC* __restrict__ sBm, TC* __restrict__ sS,
+__device__ __forceinline__ void gate_up_body(const GateUpArgs<TC>& a, int gi, TC* __restrict__ sBm, TC* __restrict__ sS,
                                              float* __restrict__ redm) {
   typedef GF<TC> F;
   typedef UpShape<TC, EPI> S;
   constexpr bool DZ = EPI == EPI_GATE_DZ;
   constexpr bool BWD = EPI == EPI_GATE_BWD || DZ;
+  // per-tile column sums of dpre (the bias gradient); with EPI_GATE_DZ the
+  // weight-gradient kernel forms them instead
+  constexpr bool CS = BWD && !DZ;
   static_assert(!DZ || sizeof(TC) == 2, "the fused dz product is bf16");
   constexpr int E = 16 / sizeof(TC);
   constexpr int LDK = S::LDK, LDS_ = S::LDS_;
@@ -526,7 +530,6 @@ __device__ __forceinline__ void gate_up_body(const GateUpArgs<TC>& a, TC* __rest
   constexpr int SW = BM * WPR / UP_THREADS;    // staged words per thread
   static_assert(MAXW * UP_THREADS == BN * WPU && SW * UP_THREADS == BM * WPR && R <= S::RMAX, "tile layout");
 
-  const int gi = blockIdx.y;
   const int W = a.W[gi];
   const int mt = (a.M + BM - 1) / BM;
   const int ntiles = W / BN;
@@ -623,7 +626,7 @@ __device__ __forceinline__ void gate_up_body(const GateUpArgs<TC>& a, TC* __rest
     // tile t's U block is in buffer buf (and its dG words in sS); every wave is
     // done with tile t - 1, so the other buffers are free once read
     __syncthreads();
-    if constexpr (BWD) {
+    if constexpr (CS) {
       if (t > t0) put_colsum(t - 1, redm + (buf ^ 1) * 4 * BN);
     }
     // the next tile's operands, in flight during this one
@@ -666,13 +669,13 @@ __device__ __forceinline__ void gate_up_body(const GateUpArgs<TC>& a, TC* __rest
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             v[q] = gv[q] * act_grad_t<ACT>(v[q]);
-            cs[q] += row_ok ? v[q] : 0.f;
+            if constexpr (CS) cs[q] += row_ok ? v[q] : 0.f;
           }
           if constexpr (DZ) dp[i][j] = MM<TC>::from_f32(v);
         }
         if constexpr (!DZ) store4(&sS[row * LDS_ + c], v);
       }
-      if constexpr (BWD) {
+      if constexpr (CS) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float sm = sum16(cs[q]);
@@ -714,7 +717,7 @@ __device__ __forceinline__ void gate_up_body(const GateUpArgs<TC>& a, TC* __rest
     // words go to this wave's own staging rows after its reads of them above
     if (t + 1 < t1) put_tile(sBm + (buf ^ 1) * BN * LDK);
   }
-  if constexpr (BWD) {
+  if constexpr (CS) {
     __syncthreads();
     put_colsum(t1 - 1, redm + ((t1 - 1 - t0) & 1) * 4 * BN);
   }
@@ -758,7 +761,7 @@ gate_up_kernel(GateUpArgs<TC> a) {
   __shared__ float red[2 * 4 * UP_BN];
   const int gi = blockIdx.y;
   const int r = a.r[gi];
-#define MUIR_UP_BODY(RR, AA) gate_up_body<TC, EPI, RR, AA>(a, sB, sS, red)
+#define MUIR_UP_BODY(RR, AA) gate_up_body<TC, EPI, RR, AA>(a, gi, sB, sS, red)
   MUIR_GATE_FORMS(MUIR_UP_BODY)
 #undef MUIR_UP_BODY
 }
@@ -771,6 +774,9 @@ struct GateDwArgs {
   const uint16_t* dG[5];  // the gates' gradients, [M, W_i]
   float* part;            // fp32 partials, split s at part + s * split_stride, gate i at woff[i]
   size_t split_stride;
+  float* colsum;          // the bias gradient's partials: split s, gate i at colsum + s * colsum_ld + csoff[i]
+  int colsum_ld;
+  int csoff[5];
   int M, ksplit, kchunk;
   int r[5], W[5], zoff[5], act[5];
   size_t woff[5], boff[5];
@@ -789,16 +795,21 @@ struct GateDwArgs {
 //     four consecutive tokens per lane, two token tiles per 32-deep product.
 // The next block's z and dG rows are loaded while this block computes and
 // stored into the other LDS buffer after it: one barrier per block.  Tokens
-// past M are zero (dG = 0 gives dpre = 0).  Workgroups of one split sit on
+// past M are zero (dG = 0 gives dpre = 0).  The lane's four dpre values of
+// each token tile are also summed in place, for the bias gradient's partial
+// sum over the split (in-lane adds; the four token groups meet at the end).
+// Workgroups of one split sit on
 // one XCD, so its z rows are fetched into that XCD's L2 once.  The rank and
 // activation are template arguments of the body.
 constexpr int DW_WPW = 2;               // 16-column tiles per wave
 constexpr int DW_WB = 64 * DW_WPW, DW_TB = 64;
 constexpr int DW_PZ = 128 + 16;         // z rows: 288 bytes (an odd number of 32-byte units)
 constexpr int DW_PG = DW_WB + 16;       // dG rows: 288 bytes
+constexpr int DW_SPLIT_TOKENS = 2048;   // tokens per split of the weight-gradient kernel
 
 template <int R, int ACT>
-__device__ __forceinline__ void gate_dw_body(const GateDwArgs& a, uint16_t* __restrict__ sZm, uint16_t* __restrict__ sGm) {
+__device__ __forceinline__ void gate_dw_body(const GateDwArgs& a, int gi, uint16_t* __restrict__ sZm,
+                                             uint16_t* __restrict__ sGm) {
   typedef uint16_t TC;
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   constexpr int WB = DW_WB, TB = DW_TB, PZ = DW_PZ, PG = DW_PG, WPW = DW_WPW;
@@ -809,7 +820,6 @@ __device__ __forceinline__ void gate_dw_body(const GateDwArgs& a, uint16_t* __re
   constexpr int KS = R / 32, RT = R / 16;
   static_assert(ZW * 256 == TB * RW && GW * 256 == TB * GWR, "block layout");
 
-  const int gi = blockIdx.y;
   const int W = a.W[gi];
   const int nwt = (W + WB - 1) / WB;  // (W is a multiple of 64: the last group may be half)
   const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
@@ -877,6 +887,9 @@ __device__ __forceinline__ void gate_dw_body(const GateDwArgs& a, uint16_t* __re
   for (int s2 = 0; s2 < RT; ++s2)
 #pragma unroll
     for (int u = 0; u < WPW; ++u) du[s2][u] = zero4();
+  float csum[WPW];  // sum of dpre over the lane's tokens, the lane's column
+#pragma unroll
+  for (int u = 0; u < WPW; ++u) csum[u] = 0.f;
 
   if (nblk > 0) {
     load_block(0);
@@ -908,6 +921,7 @@ __device__ __forceinline__ void gate_dw_body(const GateDwArgs& a, uint16_t* __re
 #pragma unroll
         for (int q = 0; q < 4; ++q) dv[q] = bf16_to_f32(static_cast<uint16_t>(gq[q])) * act_grad_t<ACT>(acc[q]);
         dpf[tt][u] = pack4(dv);
+        csum[u] += (dv[0] + dv[1]) + (dv[2] + dv[3]);
       }
     }
     // dU^T[16s + 4g .., columns] += z^T dpre over the block's tokens
@@ -927,25 +941,58 @@ __device__ __forceinline__ void gate_dw_body(const GateDwArgs& a, uint16_t* __re
     if (b + 1 < nblk) store_block(buf ^ 1);
     __syncthreads();
   }
-  // lane: dU[column][16s + 4g .. + 3]
+  // lane: dU[column][16s + 4g .. + 3]; the bias partial from the lanes of
+  // the column's four token groups (c16 + 16g)
 #pragma unroll
   for (int u = 0; u < WPW; ++u) {
     const int wcol = w0 + wl + 16 * u + c16;
+    float cg = csum[u] + __shfl_xor(csum[u], 16, 64);
+    cg += __shfl_xor(cg, 32, 64);
     if (w0 + wl + 16 * u >= W) continue;
+    if (g == 0) a.colsum[static_cast<size_t>(split) * a.colsum_ld + a.csoff[gi] + wcol] = cg;
     float* out = a.part + static_cast<size_t>(split) * a.split_stride + a.woff[gi] + static_cast<size_t>(wcol) * R + 4 * g;
 #pragma unroll
     for (int s2 = 0; s2 < RT; ++s2) *reinterpret_cast<f32x4*>(out + 16 * s2) = du[s2][u];
   }
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gate_dw_kernel(GateDwArgs a) {
-  __shared__ __align__(16) uint16_t sZ[2 * DW_TB * DW_PZ];
-  __shared__ __align__(16) uint16_t sG[2 * DW_TB * DW_PG];
-  const int gi = blockIdx.y;
-  const int r = a.r[gi];
-#define MUIR_DW_BODY(RR, AA) gate_dw_body<RR, AA>(a, sZ, sG)
-  MUIR_GATE_FORMS(MUIR_DW_BODY)
+// The bf16 backward of the up-projections in one launch: blockIdx.y < 5 runs
+// the fused dpre / dz body (EPI_GATE_DZ) of gate y, blockIdx.y >= 5 the
+// weight-gradient body of gate y - 5.  The two parts are independent (both
+// recompute dpre from z; one writes dz, the other the split partials of dU
+// and of the bias gradient).  Either alone ends in a partly filled round of
+// the CUs' workgroup slots (1,280 workgroups each at the 4K layer, two per
+// CU); in one launch the second part's workgroups fill the slots the first
+// part's last round leaves free.  The LDS is one buffer, laid out per part.
+constexpr int BWDUP_LDS_UP =
+    (2 * UP_BN * UpShape<uint16_t, EPI_GATE_DZ>::LDK + UpShape<uint16_t, EPI_GATE_DZ>::BM * UpShape<uint16_t, EPI_GATE_DZ>::LDS_) * 2 +
+    2 * 4 * UP_BN * 4;
+constexpr int BWDUP_LDS_DW = 2 * DW_TB * (DW_PZ + DW_PG) * 2;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gate_bwd_up_kernel(GateUpArgs<uint16_t> ua,
+                                                                                               GateDwArgs da) {
+  typedef UpShape<uint16_t, EPI_GATE_DZ> S;
+  static_assert(UP_THREADS == 256, "one block size for both parts");
+  __shared__ __align__(16) char smem[BWDUP_LDS_UP > BWDUP_LDS_DW ? BWDUP_LDS_UP : BWDUP_LDS_DW];
+  if (blockIdx.y < 5) {
+    const GateUpArgs<uint16_t>& a = ua;
+    const int gi = blockIdx.y;
+    const int r = a.r[gi];
+    uint16_t* sB = reinterpret_cast<uint16_t*>(smem);
+    uint16_t* sS = sB + 2 * UP_BN * S::LDK;
+    float* red = reinterpret_cast<float*>(sS + S::BM * S::LDS_);
+#define MUIR_UP_BODY(RR, AA) gate_up_body<uint16_t, EPI_GATE_DZ, RR, AA>(a, gi, sB, sS, red)
+    MUIR_GATE_FORMS(MUIR_UP_BODY)
+#undef MUIR_UP_BODY
+  } else {
+    const GateDwArgs& a = da;
+    const int gi = blockIdx.y - 5;
+    const int r = a.r[gi];
+    uint16_t* sZ = reinterpret_cast<uint16_t*>(smem);
+    uint16_t* sG = sZ + 2 * DW_TB * DW_PZ;
+#define MUIR_DW_BODY(RR, AA) gate_dw_body<RR, AA>(a, gi, sZ, sG)
+    MUIR_GATE_FORMS(MUIR_DW_BODY)
 #undef MUIR_DW_BODY
+  }
 }
 
 // Column sums of a [rows][ncols] fp32 array (the bias gradient from the
@@ -1241,11 +1288,12 @@ hipError_t gate_bwd_typed(const GateShape& s, const void* x, const void* W_down,
     dpo[i] = acc;
     acc += static_cast<size_t>(s.M) * L.W[i];
   }
-  // 1. dpre_i = dG_i * act'(z_i U_i + c_i), with per-tile column sums
-  {
+  // 1. dpre_i = dG_i * act'(z_i U_i + c_i), and its column sums (the bias
+  // gradient) per token tile (fp32) or per split (bf16)
   GateUpArgs<TC> u = gate_up_args<TC>(L, zr, Wu, bs);
-    u.colsum = csum;
-    u.colsum_ld = W.colsum_ld;
+  u.colsum = csum;
+  u.colsum_ld = W.colsum_ld;
+  {
     int coff = 0;
     for (int i = 0; i < 5; ++i) {
       u.out[i] = dpre + dpo[i];
@@ -1253,25 +1301,51 @@ hipError_t gate_bwd_typed(const GateShape& s, const void* x, const void* W_down,
       u.csoff[i] = coff;
       coff += L.W[i];
     }
-    if constexpr (sizeof(TC) == 2) {
-      // with 2. fused: dz[:, slice_i] = dpre_i U_i; dpre itself is not kept
-      // (the weight gradient recomputes it)
-      u.dz = dz;
-      if ((e = run_gate_up<TC, EPI_GATE_DZ>(u, stream)) != hipSuccess) return e;
-    } else {
-      if ((e = run_gate_up<TC, EPI_GATE_BWD>(u, stream)) != hipSuccess) return e;
-    }
   }
-  // 2. dz[:, slice_i] = dpre_i U_i
-  if constexpr (sizeof(TC) == 4) {
-    GemmBatch u = {};
-    u.n = 5;
-    u.ksplit = 1;
-    u.kchunk = std::max(L.W[0], L.W[2]);
+  if constexpr (sizeof(TC) == 2) {
+    // bf16, one launch: dz[:, slice_i] = dpre_i U_i (2.) with dpre kept in
+    // registers, and dU_i = dpre_i^T z_i (5.) with dpre recomputed from z;
+    // dpre itself is never stored
+    u.dz = dz;
+    GateDwArgs d = {};
+    d.z = zr;
+    d.U = Wu;
+    d.bias = bs;
+    d.part = part + static_cast<size_t>(W.ksplit) * W.part_stride;  // after dW_down's partials
+    d.split_stride = W.part_stride;
+    d.colsum = csum;
+    d.colsum_ld = W.colsum_ld;
+    d.M = s.M;
+    d.ksplit = W.dw_ksplit;
+    d.kchunk = W.dw_kchunk;
+    int nwt = 0;
+    for (int i = 0; i < 5; ++i) {
+      d.dG[i] = static_cast<const TC*>(dgates[i]);
+      d.r[i] = L.r[i];
+      d.W[i] = L.W[i];
+      d.zoff[i] = L.zoff[i];
+      d.act[i] = kActs[i];
+      d.woff[i] = L.woff[i];
+      d.boff[i] = L.boff[i];
+      d.csoff[i] = u.csoff[i];
+      nwt = std::max(nwt, (L.W[i] + DW_WB - 1) / DW_WB);
+    }
+    // x: the row blocks of the dz part (one workgroup takes all of a gate's
+    // column tiles), or the weight-gradient part's column groups x splits
+    const int gx = std::max((s.M + 127) / 128, 8 * nwt * ((W.dw_ksplit + 7) / 8));
+    hipLaunchKernelGGL(gate_bwd_up_kernel, dim3(gx, 10), dim3(256), 0, stream, u, d);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  } else {
+    if ((e = run_gate_up<TC, EPI_GATE_BWD>(u, stream)) != hipSuccess) return e;
+    // 2. dz[:, slice_i] = dpre_i U_i
+    GemmBatch g = {};
+    g.n = 5;
+    g.ksplit = 1;
+    g.kchunk = std::max(L.W[0], L.W[2]);
     for (int i = 0; i < 5; ++i)
-      u.p[i] = GemmProblem{dpre + dpo[i], Wu + L.woff[i], dz + L.zoff[i], s.M, L.r[i], L.W[i], L.W[i], L.r[i],
+      g.p[i] = GemmProblem{dpre + dpo[i], Wu + L.woff[i], dz + L.zoff[i], s.M, L.r[i], L.W[i], L.W[i], L.r[i],
                            GATE_RTOT};
-    if ((e = run_gemm<TC, 128, 128, true, false, EPI_STORE>(u, stream)) != hipSuccess) return e;
+    if ((e = run_gemm<TC, 128, 128, true, false, EPI_STORE>(g, stream)) != hipSuccess) return e;
   }
   // 3. dx = dz W_down
   {
@@ -1282,7 +1356,7 @@ hipError_t gate_bwd_typed(const GateShape& s, const void* x, const void* W_down,
     b.p[0] = GemmProblem{dz, W_down, dx, s.M, s.d, GATE_RTOT, GATE_RTOT, s.d, s.d};
     if ((e = run_gemm<TC, 128, 128, true, false, EPI_STORE>(b, stream)) != hipSuccess) return e;
   }
-  // 4. dW_down = dz^T x (split over tokens), 5. dW_up_i = dpre_i^T z_i (split over tokens)
+  // 4. dW_down = dz^T x (split over tokens)
   {
     GemmBatch b = {};
     b.n = 1;
@@ -1296,52 +1370,33 @@ hipError_t gate_bwd_typed(const GateShape& s, const void* x, const void* W_down,
                        0, stream, part, W.ksplit, W.part_stride, n, dW_down);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  // 5. dW_up_i = dpre_i^T z_i (split over tokens; bf16: formed in 1.)
   {
+    const float* upart = part;
+    int upk = W.ksplit;
     if constexpr (sizeof(TC) == 2) {
-      // dpre recomputed from z (never stored)
-      GateDwArgs d = {};
-      d.z = zr;
-      d.U = Wu;
-      d.bias = bs;
-      d.part = part;
-      d.split_stride = W.part_stride;
-      d.M = s.M;
-      d.ksplit = W.ksplit;
-      d.kchunk = W.kchunk;
-      int nwt = 0;
-      for (int i = 0; i < 5; ++i) {
-        d.dG[i] = static_cast<const TC*>(dgates[i]);
-        d.r[i] = L.r[i];
-        d.W[i] = L.W[i];
-        d.zoff[i] = L.zoff[i];
-        d.act[i] = kActs[i];
-        d.woff[i] = L.woff[i];
-        d.boff[i] = L.boff[i];
-        nwt = std::max(nwt, (L.W[i] + DW_WB - 1) / DW_WB);
-      }
-      const int gx = 8 * nwt * ((W.ksplit + 7) / 8);
-      hipLaunchKernelGGL(gate_dw_kernel, dim3(gx, 5), dim3(256), 0, stream, d);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+      upart = part + static_cast<size_t>(W.ksplit) * W.part_stride;
+      upk = W.dw_ksplit;
     } else {
-      GemmBatch u = {};
-      u.n = 5;
-      u.ksplit = W.ksplit;
-      u.kchunk = W.kchunk;
-      u.split_stride = W.part_stride;
+      GemmBatch g = {};
+      g.n = 5;
+      g.ksplit = W.ksplit;
+      g.kchunk = W.kchunk;
+      g.split_stride = W.part_stride;
       for (int i = 0; i < 5; ++i)
-        u.p[i] = GemmProblem{dpre + dpo[i], zr + L.zoff[i], part + L.woff[i], L.W[i], L.r[i], s.M, L.W[i], GATE_RTOT,
+        g.p[i] = GemmProblem{dpre + dpo[i], zr + L.zoff[i], part + L.woff[i], L.W[i], L.r[i], s.M, L.W[i], GATE_RTOT,
                              L.r[i]};
-      if ((e = run_gemm<TC, 128, 128, false, false, EPI_PARTIAL>(u, stream)) != hipSuccess) return e;
+      if ((e = run_gemm<TC, 128, 128, false, false, EPI_PARTIAL>(g, stream)) != hipSuccess) return e;
     }
     const size_t n = L.woff[4] + static_cast<size_t>(L.r[4]) * L.W[4];
     hipLaunchKernelGGL(split_sum_kernel, dim3(static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 4096))), dim3(256),
-                       0, stream, part, W.ksplit, W.part_stride, n, dW_up);
+                       0, stream, upart, upk, W.part_stride, n, dW_up);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // 6. dbias = column sums over the token tiles
+  // 6. dbias = column sums over the token tiles (fp32) or the splits (bf16)
   {
     hipLaunchKernelGGL(colsum_kernel, dim3(static_cast<unsigned>((W.colsum_ld + 31) / 32)), dim3(256), 0, stream,
-                       csum, W.mtiles, W.colsum_ld, dbias);
+                       csum, sizeof(TC) == 2 ? W.dw_ksplit : W.mtiles, W.colsum_ld, dbias);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -1373,15 +1428,20 @@ GateWorkspace gate_workspace(const GateShape& s) {
   // launches fill the chip: about 4096 tokens per split, at most 16 splits
   w.ksplit = std::max(1, std::min(16, (s.M + 4095) / 4096));
   w.kchunk = ((s.M + w.ksplit - 1) / w.ksplit + 63) / 64 * 64;  // whole main-loop steps
+  // the up-projections' weight-gradient kernel (bf16) has a split of its own
+  w.dw_ksplit = s.bf16 ? std::max(1, std::min(64, (s.M + DW_SPLIT_TOKENS - 1) / DW_SPLIT_TOKENS)) : w.ksplit;
+  w.dw_kchunk = ((s.M + w.dw_ksplit - 1) / w.dw_ksplit + 63) / 64 * 64;
   const size_t up = L.woff[4] + static_cast<size_t>(L.r[4]) * L.W[4];
   w.part_stride = r256(std::max(static_cast<size_t>(s.d) * GATE_RTOT, up) * 4) / 4;
   w.part_off = off;
-  off += static_cast<size_t>(w.ksplit) * w.part_stride * 4;
+  // dW_down's split partials, then (bf16) the up-projections' own, which the
+  // combined kernel writes before dW_down's are formed
+  off += static_cast<size_t>(w.ksplit + (s.bf16 ? w.dw_ksplit : 0)) * w.part_stride * 4;
   w.mtiles = (s.M + 127) / 128;
   w.colsum_ld = 0;
   for (int i = 0; i < 5; ++i) w.colsum_ld += L.W[i];
   w.colsum_off = off;
-  off += r256(static_cast<size_t>(w.mtiles) * w.colsum_ld * 4);
+  off += r256(static_cast<size_t>(std::max(w.mtiles, w.dw_ksplit)) * w.colsum_ld * 4);
   w.bytes = off;
   return w;
 }

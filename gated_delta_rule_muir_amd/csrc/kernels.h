@@ -177,11 +177,13 @@ struct GateShape {
   bool bf16;
 };
 // Backward workspace: recomputed z, dpre of the five gates (fp32 only), dz, split
-// partials of the weight gradients and the per-tile column sums.
+// partials of the weight gradients and the bias gradient's partial column sums
+// (per 128-token tile for fp32, per split for bf16).
 struct GateWorkspace {
   size_t z_off, dpre_off, dz_off, part_off, colsum_off, bytes;
   size_t part_stride;
   int ksplit, kchunk, mtiles, colsum_ld;
+  int dw_ksplit, dw_kchunk;  // the split of the bf16 weight-gradient kernel
 };
 GateWorkspace gate_workspace(const GateShape& s);
 // Elements of the packed up-projection weights (sum of rank x width).
