@@ -32,8 +32,10 @@
  *    [B, H, dk, dv] row-major (dv contiguous).
  *  - The caller owns every buffer, including the workspace; the library
  *    never allocates, frees or synchronises, and keeps no state between
- *    calls.  Calls are asynchronous on `stream` (a hipStream_t; NULL is the
- *    default stream).  Calls on different streams with disjoint buffers may
+ *    calls, with two exceptions stated where they apply: the no-allocation
+ *    forward's fixed scratch array, and the hipBLASLt handle and plans of
+ *    the bf16 gate projection.  Calls are asynchronous on `stream` (a
+ *    hipStream_t; NULL is the default stream).  Calls on different streams with disjoint buffers may
  *    run concurrently.
  *  - Outputs must not alias inputs (muir_step's S is updated in place by
  *    design).
@@ -351,6 +353,17 @@ typedef struct {
 /*
  * Forward: writes z (kept for the backward) and the five gates.  All
  * pointers are required.  M == 0 launches nothing.
+ *
+ * For bf16, the two plain products z = x W_down^T (here, and in the
+ * backward when z is NULL) and dx = dz W_down run through hipBLASLt.  The
+ * first such call on a device creates that device's hipBLASLt handle, and
+ * the first call of each shape its plan (descriptors and the algorithm the
+ * library's heuristic picks); both are kept until the process ends, and
+ * hipBLASLt makes its own host allocations and loads its kernels for them.
+ * Later calls of a known shape allocate nothing, so a caller that captures
+ * these calls into a graph makes one call of each shape first.  A shape
+ * for which hipBLASLt has no algorithm needing no workspace runs this
+ * library's own GEMM kernel.
  */
 muir_status_t muir_gate_proj_fwd(const muir_gate_dims_t* dims, const void* x, const void* W_down,
                                  const void* W_up, const void* bias, void* z, void* log_a,
