@@ -962,14 +962,19 @@ __device__ __forceinline__ void gate_dw_body(const GateDwArgs& a, int gi, uint16
   }
 }
 
-// The bf16 backward of the up-projections in one launch: blockIdx.y < 5 runs
-// the fused dpre / dz body (EPI_GATE_DZ) of gate y, blockIdx.y >= 5 the
-// weight-gradient body of gate y - 5.  The two parts are independent (both
+// The bf16 backward of the up-projections in one launch: blockIdx.y = 2 i
+// runs the fused dpre / dz body (EPI_GATE_DZ) of gate i, blockIdx.y = 2 i + 1
+// the weight-gradient body of gate i.  The two parts are independent (both
 // recompute dpre from z; one writes dz, the other the split partials of dU
 // and of the bias gradient).  Either alone ends in a partly filled round of
 // the CUs' workgroup slots (1,280 workgroups each at the 4K layer, two per
 // CU); in one launch the second part's workgroups fill the slots the first
-// part's last round leaves free.  The LDS is one buffer, laid out per part.
+// part's last round leaves free.  Workgroups are dispatched in blockIdx.y
+// order, so both parts of one gate run one after the other: the second
+// part's reads of the gate's gradient (134 MB at the 4K layer) then find it
+// in the 256 MB Infinity Cache instead of HBM, which the order gate by gate
+// and part by part did not allow (the four other gates' gradients passed
+// between the two reads).  The LDS is one buffer, laid out per part.
 constexpr int BWDUP_LDS_UP =
     (2 * UP_BN * UpShape<uint16_t, EPI_GATE_DZ>::LDK + UpShape<uint16_t, EPI_GATE_DZ>::BM * UpShape<uint16_t, EPI_GATE_DZ>::LDS_) * 2 +
     2 * 4 * UP_BN * 4;
@@ -979,9 +984,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   typedef UpShape<uint16_t, EPI_GATE_DZ> S;
   static_assert(UP_THREADS == 256, "one block size for both parts");
   __shared__ __align__(16) char smem[BWDUP_LDS_UP > BWDUP_LDS_DW ? BWDUP_LDS_UP : BWDUP_LDS_DW];
-  if (blockIdx.y < 5) {
+  if ((blockIdx.y & 1) == 0) {
     const GateUpArgs<uint16_t>& a = ua;
-    const int gi = blockIdx.y;
+    const int gi = blockIdx.y >> 1;
     const int r = a.r[gi];
     uint16_t* sB = reinterpret_cast<uint16_t*>(smem);
     uint16_t* sS = sB + 2 * UP_BN * S::LDK;
@@ -991,7 +996,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
 #undef MUIR_UP_BODY
   } else {
     const GateDwArgs& a = da;
-    const int gi = blockIdx.y - 5;
+    const int gi = blockIdx.y >> 1;
     const int r = a.r[gi];
     uint16_t* sZ = reinterpret_cast<uint16_t*>(smem);
     uint16_t* sG = sZ + 2 * DW_TB * DW_PZ;
