@@ -19,7 +19,8 @@ Beside it the line carries:
   step_model    the whole step's algorithmic bytes and flops over its time
   cpu_baseline  the fp64 sequential oracle on the host cores, on a bounded
                 sample of the same workload (4 batch rows: 64 heads x 4096)
-  secondary     the same step with bf16 gradients, long-context fwd+bwd
+  secondary     the same step with bf16 gradients, the forward alone on the
+                same inputs (without and with saved chunk states), long-context fwd+bwd
                 (T=32768, chunk 128 and 256), one 1M-token stream (chunked
                 prefill chained through the state, then decode), the gate
                 prologue at the layer's shape (fused low-rank gate projection
@@ -196,6 +197,68 @@ def time_fwdbwd(m, dv, C, steps, warmup, torch, hiprt, names, profile=True, grad
         kern = {k: v / steps for k, v in acc.items()}
         pool.close()
     return (t1 - t0) * 1e3 / steps, kern
+
+
+def time_fwd(m, dv, C, steps, warmup, torch, hiprt, names, save_states):
+    """Warmup + timed forward calls alone (with or without saving the chunk
+    states); returns (ms_per_call, per-kernel avg ms)."""
+    B, T, H, d = dv["q"].shape
+    fws = torch.empty(m.muir_chunk_fwd_workspace(B, T, H, d, d, C), dtype=torch.uint8, device=dv["q"].device)
+    args = [dv[n] for n in names]
+    o = torch.empty_like(dv["q"])
+
+    def call():
+        m.muir_chunk_fwd(*args, chunk=C, save_states=save_states, workspace=fws, out=o)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    per = 3  # events: before, prep, scan
+    pool = hiprt.EventPool(per * steps)
+    m.muir_set_profile_events(pool.arr, pool.n)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rec = m.muir_profile_events_recorded()
+    m.muir_set_profile_events(None)
+    if rec != per * steps:
+        raise RuntimeError(f"expected {per * steps} profile events, got {rec}")
+    acc = {"fwd_prep": 0.0, "fwd_scan": 0.0}
+    for s_ in range(steps):
+        acc["fwd_prep"] += pool.elapsed_ms(s_ * per, s_ * per + 1)
+        acc["fwd_scan"] += pool.elapsed_ms(s_ * per + 1, s_ * per + 2)
+    pool.close()
+    return (t1 - t0) * 1e3 / steps, {k: v / steps for k, v in acc.items()}
+
+
+def fwd_report(kern, ms, d, C, nth, save_states, e=2, es=2):
+    """The forward alone: per-kernel algorithmic bytes (kernel_bytes; the
+    scan's saved states only when it saves them), the dominant kernel's
+    roofline, and the forward's bytes and flops (step_bytes, step_flops)
+    over its time."""
+    st = d * d * es / C if save_states else 0.0
+    kb = {"fwd_prep": 7 * d * e, "fwd_scan": d * e + st}
+    kernels = {}
+    for kn, t in kern.items():
+        byt = kb[kn] * nth
+        kernels[kn] = {"avg_us": t * 1e3, "alg_bytes": byt, "GBs": byt / (t * 1e-3) / 1e9,
+                       "hbm_frac": byt / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    dom = max(kern, key=lambda k: kern[k])
+    roof = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GBs"], "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": kernels[dom]["GBs"] / HBM_PEAK_GBS,
+            "alg_bytes_per_launch": kb[dom] * nth, "avg_launch_us": kernels[dom]["avg_us"]}
+    fb = (8 * d * e + st) * nth
+    ff = step_flops(d, C)[0] * nth
+    t = ms * 1e-3
+    model = {"alg_bytes": fb, "alg_GBs": fb / t / 1e9, "alg_flops": ff,
+             "hbm_floor_us": fb / (HBM_PEAK_GBS * 1e9) * 1e6,
+             "mfma_floor_us": ff / (BF16_PEAK_TFLOPS * 1e12) * 1e6,
+             "frac": max(fb / (HBM_PEAK_GBS * 1e9), ff / (BF16_PEAK_TFLOPS * 1e12)) / t,
+             "mfma_util_alg": ff / t / (BF16_PEAK_TFLOPS * 1e12)}
+    return kernels, roof, model
 
 
 def roofline_report(kern, ms, d, C, nth, workload, eg):
@@ -509,6 +572,23 @@ def main():
                                                  "gradients": "bf16", "kernels": kern2, "roofline": roof2,
                                                  "step_model": sm2}
             log(f"[bench]   {ntok / (ms2 * 1e-3):.4g} tokens/s")
+        if want("layer_fwd_4k"):
+            # the forward alone at the same shape and inputs: as a prefill or
+            # inference pass (no chunk states kept), and as a training forward
+            log("[bench] secondary: the forward alone (without and with saved chunk states)")
+            line = {"workload": "layer_fwd_4k: B=8 T=4096 H=16 d=128 chunk 64, bf16 inputs, fp32 state; "
+                                "muir_chunk_fwd alone on the step's inputs"}
+            # one untimed round of both forms first: the first timed round after
+            # the step measured up to 10% slower, in both orders
+            for save in (False, True):
+                time_fwd(m, dv, C, 10, 3, torch, hiprt, names, save)
+            for key, save in (("no_saved_states", False), ("saved_states", True)):
+                ms3, k3 = time_fwd(m, dv, C, max(10, args.steps), 3, torch, hiprt, names, save)
+                kern3, roof3, fm3 = fwd_report(k3, ms3, d, C, nth, save)
+                line[key] = {"tokens_per_s": ntok / (ms3 * 1e-3), "ms_per_call": ms3, "kernels": kern3,
+                             "roofline": roof3, "fwd_model": fm3}
+                log(f"[bench]   {key}: {ntok / (ms3 * 1e-3):.4g} tokens/s ({ms3:.3f} ms)")
+            sec["layer_fwd_4k"] = line
         del dv
         torch.cuda.empty_cache()
         for name in ("long_32k_c128", "long_32k_c256"):
