@@ -20,8 +20,10 @@ Beside it the line carries:
   cpu_baseline  the fp64 sequential oracle on the host cores, on a bounded
                 sample of the same workload (4 batch rows: 64 heads x 4096)
   secondary     the same step with bf16 gradients, the forward alone on the
-                same inputs (without and with saved chunk states), long-context fwd+bwd
-                (T=32768, chunk 128 and 256), one 1M-token stream (chunked
+                same inputs (without and with saved chunk states), the step with a
+                static readout gate and with none, long-context fwd+bwd
+                (T=32768, chunk 128 and 256), packed documents of mixed length
+                (about 32K tokens, fwd+bwd), one 1M-token stream (chunked
                 prefill chained through the state, then decode), the gate
                 prologue at the layer's shape (fused low-rank gate projection
                 and q / k SiLU + L2, fwd + bwd), and the streaming decode step
@@ -62,24 +64,26 @@ def log(*a):
 # summaries, deltas, state gradients) are not counted: they appear only in
 # the measured traffic, whose ratio to these bytes shows what the
 # decomposition into kernels costs.
-def step_bytes(d: int, C: int, e: int = 2, es: int = 2, eg: int = 4):
-    """(forward, backward) algorithmic bytes per token-head: inputs 7de, o de
-    and the saved states d^2 es / C; inputs, dO, saved states and the
-    gradients 7d eg."""
-    fwd = 7 * d * e + d * e + d * d * es / C
-    bwd = 7 * d * e + d * e + d * d * es / C + 7 * d * eg
+def step_bytes(d: int, C: int, e: int = 2, es: int = 2, eg: int = 4, ni: int = 7):
+    """(forward, backward) algorithmic bytes per token-head: inputs ni d e, o
+    d e and the saved states d^2 es / C; inputs, dO, saved states and the
+    gradients ni d eg.  ni = 7 per-token inputs, or 6 when the readout gate is
+    static or absent (it is then not a per-token input, nor its gradient a
+    per-token output)."""
+    fwd = ni * d * e + d * e + d * d * es / C
+    bwd = ni * d * e + d * e + d * d * es / C + ni * d * eg
     return fwd, bwd
 
 
-def kernel_bytes(d: int, C: int, e: int = 2, es: int = 2, eg: int = 4):
+def kernel_bytes(d: int, C: int, e: int = 2, es: int = 2, eg: int = 4, ni: int = 7):
     """Algorithmic bytes per token-head that each kernel of the step itself
     moves: the prep kernel reads the inputs, the forward scan writes o and
     the chunk-start states, the reverse scan reads dO, and the chunk
     gradient kernel reads the inputs, dO and the states and writes the seven
     gradients (dO is counted by both backward kernels, which both read it)."""
     st = d * d * es / C
-    return {"fwd_prep": 7 * d * e, "fwd_scan": d * e + st, "bwd_scan": d * e,
-            "bwd_chunk": 7 * d * e + d * e + st + 7 * d * eg}
+    return {"fwd_prep": ni * d * e, "fwd_scan": d * e + st, "bwd_scan": d * e,
+            "bwd_chunk": ni * d * e + d * e + st + ni * d * eg}
 
 
 def step_flops(d: int, C: int):
@@ -156,9 +160,11 @@ def time_fwdbwd(m, dv, C, steps, warmup, torch, hiprt, names, profile=True, grad
     B, T, H, d = dv["q"].shape
     dev = dv["q"].device
     gcode = m.MUIR_BF16 if grad_dtype == torch.bfloat16 else m.MUIR_F32
-    fws = torch.empty(m.muir_chunk_fwd_workspace(B, T, H, d, d, C), dtype=torch.uint8, device=dev)
-    bws = torch.empty(m.muir_chunk_bwd_workspace(B, T, H, d, d, C, grad_dtype=gcode), dtype=torch.uint8,
-                      device=dev)
+    gam = dv["gamma"]
+    gm = m.MUIR_GAMMA_NONE if gam is None else m.MUIR_GAMMA_STATIC if gam.dim() == 2 else m.MUIR_GAMMA_TOKEN
+    fws = torch.empty(m.muir_chunk_fwd_workspace(B, T, H, d, d, C, gamma_mode=gm), dtype=torch.uint8, device=dev)
+    bws = torch.empty(m.muir_chunk_bwd_workspace(B, T, H, d, d, C, gamma_mode=gm, grad_dtype=gcode),
+                      dtype=torch.uint8, device=dev)
     args = [dv[n] for n in names]
 
     def step():
@@ -261,26 +267,26 @@ def fwd_report(kern, ms, d, C, nth, save_states, e=2, es=2):
     return kernels, roof, model
 
 
-def roofline_report(kern, ms, d, C, nth, workload, eg):
+def roofline_report(kern, ms, d, C, nth, workload, eg, ni=7):
     """Per-kernel and whole-step figures from the algorithmic bytes (step_bytes,
     kernel_bytes; gradients of eg bytes) of nth token-heads.  `roofline` is
     the dominant (longest) kernel's: its algorithmic bytes per launch over its
     average launch time, against the HBM peak (every kernel and the step are
     below the bf16 MFMA ridge, see step_model), plus its measured HBM traffic
     per launch when the counter record matches its sources."""
-    kb = kernel_bytes(d, C, eg=eg)
+    kb = kernel_bytes(d, C, eg=eg, ni=ni)
     kernels = {}
     for kn, t in kern.items():
         byt = kb[kn] * nth
         kernels[kn] = {"avg_us": t * 1e3, "alg_bytes": byt, "GBs": byt / (t * 1e-3) / 1e9,
                        "hbm_frac": byt / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
     dom = max(kern, key=lambda k: kern[k])
-    traffic = measured_traffic(dom, workload) if eg == 4 else None
+    traffic = measured_traffic(dom, workload) if eg == 4 and ni == 7 else None
     roof = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["GBs"], "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": kernels[dom]["GBs"] / HBM_PEAK_GBS, "traffic": traffic,
             "traffic_over_alg": None if traffic is None else traffic / (kb[dom] * nth),
             "alg_bytes_per_launch": kb[dom] * nth, "avg_launch_us": kernels[dom]["avg_us"]}
-    fb, bb = step_bytes(d, C, eg=eg)
+    fb, bb = step_bytes(d, C, eg=eg, ni=ni)
     fwd_f, bwd_f = step_flops(d, C)
     sb, sf = (fb + bb) * nth, (fwd_f + bwd_f) * nth
     t = ms * 1e-3
@@ -426,6 +432,56 @@ def stream_bench(m, torch, muir_inputs):
             "prefill_tokens_per_s": w.T / (t1 - t0), "decode_us_per_token": (t2 - t1) * 1e6 / steps,
             "parity": "same inputs as tests/test_gpu_stream.py::test_stream_1m_prefill_then_decode, which checks "
                       f"heads 0 and {H - 1} against the fp64 oracle over every token"}
+
+
+def varlen_bench(m, torch, muir_inputs, steps=10, warmup=3):
+    """The varlen_32k workload: packed documents of mixed length (an empty
+    one, one token, exact chunk multiples, one past a chunk, uniform draws up
+    to 4,096 tokens), forward then backward (the backward recomputes the chunk
+    states; fp32 gradients), timed around whole steps.  The inputs are the
+    ones tests/test_gpu_fullsize.py::test_varlen_full_layer checks against the
+    oracle on every document and head."""
+    w = muir_inputs.WORKLOADS["varlen_32k"]
+    lens = muir_inputs.varlen_lengths(w.B, w.T, w.chunk, seed=w.extra["lengths_seed"])
+    inp = muir_inputs.varlen_inputs(lens, w.H, w.dk, w.dv, dtype=w.dtype, decay=w.decay, seed=w.extra["seed"])
+    dv = {n: (t.to("cuda") if t is not None else None) for n, t in inp.items()}
+    names = ("q", "k", "v", "log_a", "erase", "write", "gamma")
+    args = [dv[n] for n in names]
+    cu, L = dv["cu_seqlens"], int(lens.max())
+    fws = torch.empty(m.muir_chunk_varlen_fwd_workspace(w.B, L, w.H, w.dk, w.dv, w.chunk), dtype=torch.uint8,
+                      device="cuda")
+    bws = torch.empty(m.muir_chunk_varlen_bwd_workspace(w.B, L, w.H, w.dk, w.dv, w.chunk), dtype=torch.uint8,
+                      device="cuda")
+    o = torch.empty_like(dv["v"])
+
+    def step():
+        m.muir_chunk_varlen_fwd(*args, cu, chunk=w.chunk, max_len=L, workspace=fws, out=o, final_state=False)
+        m.muir_chunk_varlen_bwd(*args, dv["dO"], cu, chunk=w.chunk, max_len=L, workspace=bws, want_dS0=False)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    total = int(lens.sum())
+    nth = total * w.H
+    fb, bb = step_bytes(w.dk, w.chunk)
+    fwd_f, bwd_f = step_flops(w.dk, w.chunk)
+    # the backward recomputes the chunk states instead of reading saved ones:
+    # its bytes are the step's without the states' write and read
+    sb = (fb + bb - 2 * w.dk * w.dk * 2 / w.chunk) * nth
+    t = ms * 1e-3
+    return {"workload": f"varlen_32k: {w.B} packed documents of lengths {lens.tolist()} ({total} tokens), "
+                        f"H={w.H} d={w.dk} chunk {w.chunk}, bf16 inputs, fp32 gradients",
+            "tokens_per_s": total / t, "ms_per_step": ms,
+            "step_model": {"alg_bytes": sb, "alg_GBs": sb / t / 1e9, "hbm_floor_us": sb / (HBM_PEAK_GBS * 1e9) * 1e6,
+                           "frac": sb / (HBM_PEAK_GBS * 1e9) / t,
+                           "mfma_util_alg": (fwd_f + bwd_f) * nth / t / (BF16_PEAK_TFLOPS * 1e12)},
+            "parity": "same inputs as tests/test_gpu_fullsize.py::test_varlen_full_layer (every document and "
+                      "head against the fp64 oracle)"}
 
 
 def gate_bench(m, torch, hiprt, M=32768, d=2048, H=16, dk=128, dv=128, steps=10, warmup=2, seed=0):
@@ -589,6 +645,21 @@ def main():
                              "roofline": roof3, "fwd_model": fm3}
                 log(f"[bench]   {key}: {ntok / (ms3 * 1e-3):.4g} tokens/s ({ms3:.3f} ms)")
             sec["layer_fwd_4k"] = line
+        if want("gamma_forms_4k"):
+            # the step with a static readout gate (one [H, dk] vector) and with
+            # none, on the same inputs otherwise
+            log("[bench] secondary: the step with a static readout gate and with none")
+            line = {"workload": "gamma_forms_4k: the layer_fwdbwd_4k step with the readout gate static "
+                                "(gamma of token 0 of batch row 0, [H, dk]) or absent; fp32 gradients"}
+            for key, gam in (("static", dv["gamma"][0, 0].contiguous()), ("none", None)):
+                dvg = dict(dv)
+                dvg["gamma"] = gam
+                ms4, k4 = time_fwdbwd(m, dvg, C, max(10, args.steps // 2), 3, torch, hiprt, names)
+                kern4, roof4, sm4 = roofline_report(k4, ms4, d, C, nth, f"gamma_{key}_4k", eg=4, ni=6)
+                line[key] = {"tokens_per_s": ntok / (ms4 * 1e-3), "ms_per_step": ms4, "kernels": kern4,
+                             "roofline": roof4, "step_model": sm4}
+                log(f"[bench]   {key}: {ntok / (ms4 * 1e-3):.4g} tokens/s ({ms4:.3f} ms)")
+            sec["gamma_forms_4k"] = line
         del dv
         torch.cuda.empty_cache()
         for name in ("long_32k_c128", "long_32k_c256"):
@@ -603,6 +674,11 @@ def main():
                          "kernels": kern2, "roofline": roof2, "step_model": sm2}
             log(f"[bench]   {sec[name]['tokens_per_s']:.4g} tokens/s")
             del dv2
+            torch.cuda.empty_cache()
+        if want("varlen_32k"):
+            log("[bench] secondary varlen_32k (packed documents of mixed length, fwd+bwd)")
+            sec["varlen_32k"] = varlen_bench(m, torch, muir_inputs)
+            log(f"[bench]   {sec['varlen_32k']['tokens_per_s']:.4g} tokens/s ({sec['varlen_32k']['ms_per_step']:.3f} ms)")
             torch.cuda.empty_cache()
         if want("stream_1m"):
             log("[bench] secondary stream (1M-token prefill, then decode)")

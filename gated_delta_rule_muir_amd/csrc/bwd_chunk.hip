@@ -189,6 +189,20 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     const float x = ldv(gst, static_cast<uint32_t>(j));
     return gmode == GAMMA_NONE ? 1.f : x;
   };
+  // the static gate's values this thread uses (channels colv(n) and ej; none:
+  // 1), read once here, ahead of the prologue's own reads: a read per block
+  // sat in the sweep's critical path (1,229 against 1,038 us per launch at
+  // the 4K layer, static against per-token gate)
+  float gsc[NT], gse = 1.f;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) gsc[n] = 1.f;
+  if constexpr (!GTOK) {
+    if (gmode != GAMMA_NONE) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) gsc[n] = ldv(gst, static_cast<uint32_t>(colv(n)));
+      gse = ldv(gst, static_cast<uint32_t>(ej));
+    }
+  }
   TC* gDel = reinterpret_cast<TC*>(scratch + static_cast<size_t>(chunk) * bwd_scratch_bytes_tc<TC, FORM>(C, DK, DV));
   TC* gS = gDel + static_cast<size_t>(C) * DV;  // form 0: [NB][DK][DV]
   TC* gSub = gDel;                              // form 2: [NSUB - 1] states as 16 x 16 tiles
@@ -399,7 +413,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
         xk[rr] = ldv(kb, o);
         xe[rr] = ldv(eb, o);
         xq[rr] = ldv(qb, o);
-        xg[rr] = gam(r0 + RPT * part + rr, ej);
+        xg[rr] = GTOK ? gam(r0 + RPT * part + rr, ej) : gse;
       }
     }
 #pragma unroll
@@ -427,7 +441,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
       for (int ii = 0; ii < 4; ++ii) {
         const uint32_t o = gi(r0 + 4 * g + ii, colv(n));
         oq[n][ii] = ldv(qb, o);
-        og[n][ii] = gam(r0 + 4 * g + ii, colv(n));
+        og[n][ii] = GTOK ? gam(r0 + 4 * g + ii, colv(n)) : gsc[n];
         ov[n][ii] = ldv(vb, o);
         ow[n][ii] = ldv(wb, o);
         ok[n][ii] = ldv(kb, o);
@@ -505,7 +519,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     if constexpr (DIRECT) {
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        const float gs = GTOK ? 0.f : gam_static(colv(n));
+        const float gs = GTOK ? 0.f : gsc[n];
         // tokens 4g .. 4g+3 of channel colv(n)
         const i16x4 fq = tr_in(0, 4 * g, col0(n)), fk = tr_in(1, 4 * g, col0(n)), fv = tr_in(2, 4 * g, col0(n)),
                     fw = tr_in(3, 4 * g, col0(n)), fe = tr_in(4, 4 * g, col0(n)), fl = tr_in(5, 4 * g, col0(n));
@@ -562,7 +576,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   auto commit_r = [&](int J) -> int {
     const int safe = !((sUnsafe >> J) & 1);
     if constexpr (DIRECT) {
-      const float gs = GTOK ? 0.f : gam_static(ej);
+      const float gs = GTOK ? 0.f : gse;
       // tokens RPT part .. + 3 of channel ej (the lane's channel within its
       // 16-lane group: ej % 16 == lane % 16)
       static_assert(RPT == 4 && DK % 64 == 0, "elementwise mapping of the transposing reads");
@@ -1416,27 +1430,54 @@ hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, c
 
 namespace {
 // dgamma of a static readout gate: per (head, key channel), the sum of the
-// per-chunk partial sums over the batch and the chunks (fixed order).
+// per-chunk partial sums over the batch and the chunks, in a fixed order.  A
+// block takes 32 consecutive (head, channel) columns; the B*NC partials of
+// each are split over 8 thread groups (rows r = grp, grp + 8, ...), each
+// summing into four interleaved accumulators so that its loads stay in
+// flight together, and the groups' sums are added in LDS in group order.
+// (One thread per column summing its partials in sequence took about 150 us
+// at the 4K layer: 512 dependent steps on 8 workgroups.)
 __global__ __launch_bounds__(256) void gamma_sum_kernel(int B, int H, int NC, int DK,
                                                         const float* __restrict__ part,
                                                         float* __restrict__ dgamma) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= H * DK) return;
-  const int h = idx / DK;
-  const int j = idx - h * DK;
-  float acc = 0.f;
-  for (int b = 0; b < B; ++b) {
-    const float* p = part + (static_cast<size_t>(b) * H + h) * NC * DK + j;
-    for (int c = 0; c < NC; ++c) acc += p[static_cast<size_t>(c) * DK];
+  __shared__ float red[8][32];
+  const int jl = threadIdx.x & 31, grp = threadIdx.x >> 5;
+  const int col = blockIdx.x * 32 + jl;
+  const bool ok = col < H * DK;
+  const int h = ok ? col / DK : 0;
+  const int j = ok ? col - h * DK : 0;
+  const int n = B * NC;  // partial row r = b NC + c at part[((b H + h) NC + c) DK + j]
+  auto P = [&](int r) -> float {
+    const int b = r / NC;
+    const int c = r - b * NC;
+    return part[((static_cast<size_t>(b) * H + h) * NC + c) * DK + j];
+  };
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  int r = grp;
+  if (ok) {
+    for (; r + 24 < n; r += 32) {
+      a0 += P(r);
+      a1 += P(r + 8);
+      a2 += P(r + 16);
+      a3 += P(r + 24);
+    }
+    for (; r < n; r += 8) a0 += P(r);
   }
-  dgamma[idx] = acc;
+  red[grp][jl] = (a0 + a1) + (a2 + a3);
+  __syncthreads();
+  if (grp == 0 && ok) {
+    float acc = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < 8; ++g2) acc += red[g2][jl];
+    dgamma[col] = acc;
+  }
 }
 }  // namespace
 
 hipError_t launch_gamma_sum(const ChunkShape& s, const float* part, float* dgamma, hipStream_t stream) {
   const int n = s.H * s.DK;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(gamma_sum_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, s.B, s.H, s.NC(), s.DK, part,
+  hipLaunchKernelGGL(gamma_sum_kernel, dim3((n + 31) / 32), dim3(256), 0, stream, s.B, s.H, s.NC(), s.DK, part,
                      dgamma);
   return hipGetLastError();
 }

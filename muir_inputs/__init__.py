@@ -282,4 +282,9 @@ WORKLOADS = {
                           extra={"segment": 32768, "decode_steps": 64, "seed": 31}),
     "decode_64x16": Workload("decode_64x16", 64, 4096, 16, 128, 128, 1, "bf16", "channel",
                              extra={"steps": 4096}),
+    # packed documents of mixed length at the layer's width: N = 16 documents
+    # of up to 4,096 tokens (varlen_lengths), about 32K tokens in all; B = N,
+    # T = the longest length
+    "varlen_32k": Workload("varlen_32k", 16, 4096, 16, 128, 128, 64, "bf16", "channel", backward=True,
+                           extra={"lengths_seed": 41, "seed": 43}),
 }
