@@ -100,7 +100,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     const Tin* __restrict__ dS_chunks, const Tin* __restrict__ dO, Tg* __restrict__ dq,
     Tg* __restrict__ dk, Tg* __restrict__ dv, Tg* __restrict__ dlog_a,
     Tg* __restrict__ derase, Tg* __restrict__ dwrite, Tg* __restrict__ dgamma,
-    char* __restrict__ scratch, int gmode, float* __restrict__ dgam_part) {
+    char* __restrict__ scratch, int gmode, float* __restrict__ dgam_part, const int32_t* __restrict__ ncu) {
   typedef Tin TC;
   typedef MM<TC> M;
   typedef typename M::frag frag;
@@ -142,6 +142,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   const int chunk = blockIdx.x;
   const int bh = chunk / NC;
   const int c = chunk - bh * NC;
+  if (ncu && c >= *ncu) {
+    // packed documents: a chunk past those in use adds nothing to a static
+    // gate's gradient
+    if (gmode == GAMMA_STATIC)
+      for (int j = threadIdx.x; j < DK; j += NTH) dgam_part[static_cast<size_t>(chunk) * DK + j] = 0.f;
+    return;
+  }
   const int b = bh / H;
   const int h = bh - b * H;
   const int tid = threadIdx.x;
@@ -1397,7 +1404,7 @@ hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, c
                      (const TT*)write, (const TT*)gamma, (const char*)summ, s.summary_bytes(), s.tp_offset(),    \
                      s.dl_offset(), (const TT*)S_chunks, (const TT*)dS_chunks, (const TT*)dO, (TG*)dq, (TG*)dk,  \
                      (TG*)dv, (TG*)dlog_a, (TG*)derase, (TG*)dwrite, (TG*)dgamma, (char*)scratch, s.gmode,       \
-                     dgam_part)
+                     dgam_part, s.ncu)
 #define MUIR_BCH1(TT, TG, DD, CC, NW, FORM)                              \
   do {                                                                   \
     if (s.gmode == GAMMA_TOKEN) MUIR_BCH2(TT, TG, DD, CC, NW, FORM, true); \

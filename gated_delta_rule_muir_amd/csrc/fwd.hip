@@ -66,7 +66,7 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
     int T, int H, const Tin* __restrict__ q, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ log_a, const Tin* __restrict__ erase,
     const Tin* __restrict__ write, const Tin* __restrict__ gamma, char* __restrict__ summ,
-    size_t summ_bytes, int gmode) {
+    size_t summ_bytes, int gmode, const int32_t* __restrict__ ncu) {
   typedef Tin TC;
   typedef MM<TC> M;
   typedef typename M::frag frag;
@@ -85,6 +85,7 @@ __global__ __launch_bounds__((2 * DK / 32) * 64) void fwd_prep_kernel(
   const int chunk = blockIdx.x;
   const int bh = chunk / NC;
   const int c = chunk - bh * NC;
+  if (ncu && c >= *ncu) return;  // packed documents: a chunk past those in use
   const int b = bh / H;
   const int h = bh - b * H;
   const int tid = threadIdx.x;
@@ -494,7 +495,7 @@ hipError_t launch_fwd_prep(const ChunkShape& s, const void* q, const void* k, co
   hipLaunchKernelGGL((fwd_prep_kernel<TT, DD, CC>), dim3(grid), dim3((2 * DD / 32) * 64), 0,         \
                      stream, s.T, s.H, (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, \
                      (const TT*)erase, (const TT*)write, (const TT*)gamma, (char*)summ,            \
-                     s.summary_bytes(), s.gmode)
+                     s.summary_bytes(), s.gmode, s.ncu)
 #define MUIR_PREP(TT, DD)                         \
   do {                                            \
     if (s.C == 64) MUIR_PREP1(TT, DD, 64);        \

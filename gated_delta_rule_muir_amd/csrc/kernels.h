@@ -44,12 +44,29 @@ __host__ __device__ constexpr uint32_t stile_index(int r, int j, int DV) {
 // [H, dk]; none (gamma = 1, no pointer).
 enum GammaMode { GAMMA_TOKEN = 0, GAMMA_STATIC = 1, GAMMA_NONE = 2 };
 
+// Packed documents (variable-length calls) run as one sequence (B = 1) in
+// which each document starts at a chunk boundary.  Per chunk of that
+// sequence, cinfo holds the document's index (CI_DOC bits) and whether the
+// chunk is the document's first (CI_START: the scans start the state from
+// the document's S0, and the reverse scan cuts the gradient flowing into the
+// chunk before it) or last (CI_END: the forward scan writes the document's
+// S_T there, and the reverse scan starts the gradient from its dS_T).
+constexpr int32_t CI_DOC = (1 << 29) - 1;
+constexpr int32_t CI_START = 1 << 29;
+constexpr int32_t CI_END = 1 << 30;
+
 // Sizes and derived quantities of one chunkwise call, validated by the API.
 struct ChunkShape {
   int B, T, H, DK, DV, C;
   bool bf16;
   bool gbf16;  // per-token gradients in bf16 (else fp32)
   int gmode;   // GammaMode
+  // Packed documents only (else NULL): the per-chunk document table above,
+  // and the number of chunks in use (device memory; the chunks past it, which
+  // the launch sizes still count, are skipped by every kernel).  S0, S_T,
+  // dS_T and dS0 are then per document, [N, H, dk, dv].
+  const int32_t* cinfo = nullptr;
+  const int32_t* ncu = nullptr;
   // chunks per sequence, a partial last one included (the kernels only ever
   // run on shapes whose T is a multiple of C)
   int NC() const { return (T + C - 1) / C; }

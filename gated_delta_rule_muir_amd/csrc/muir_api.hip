@@ -8,6 +8,9 @@
 #include "kernels.h"
 
 using muir::ChunkShape;
+using muir::CI_DOC;
+using muir::CI_END;
+using muir::CI_START;
 
 // Workspace of the no-allocation forward (muir_chunk_fwd_noalloc): one array
 // per GPU, in the library's code object.  Host code never uses this name as
@@ -399,6 +402,212 @@ muir_status_t bwd_staged(const ChunkShape& s, const int32_t* cu, const Inputs& i
   return MUIR_OK;
 }
 
+// ---- Packed documents (variable-length calls) ----
+// The documents run as one sequence (B = 1) in which document n starts at
+// chunk c0(n) = the chunks of the documents before it (ceil(L / C) each), so
+// the kernels see the documents' own chunks and nothing more; the scans start
+// each document from its S0 and end it at its S_T (ChunkShape::cinfo).  The
+// launch sizes count N ceil(L_max / C) chunks, the most the documents can
+// fill (the padded layout's count, so the workspace is no larger); the
+// chunks in use are counted on the device and every kernel skips the rest.
+
+// The packed sequence's shape: s has B = N documents and T = the longest length.
+ChunkShape packed_shape(const ChunkShape& s) {
+  ChunkShape p = s;
+  p.B = 1;
+  p.T = s.B * ((s.T + s.C - 1) / s.C) * s.C;
+  return p;
+}
+// Whether a call fits the packed form's 32-bit row and document indices
+// (else it takes the padded form).
+bool packable(const ChunkShape& s) {
+  const long long rows = static_cast<long long>(s.B) * ((s.T + s.C - 1) / s.C) * s.C;
+  return s.B < CI_DOC && rows < (1LL << 31) - 256;
+}
+// The plan: the chunk table (one int32 per chunk), the chunk count and each
+// document's first row (int32 each).
+size_t plan_bytes(const ChunkShape& p, int N) {
+  return round256(static_cast<size_t>(p.NC()) * 4) + 256 + round256(static_cast<size_t>(N) * 4);
+}
+struct Plan {
+  int32_t* cinfo;
+  int32_t* ncu;
+  int32_t* docoff;
+};
+Plan carve_plan(char* at, const ChunkShape& p) {
+  Plan r;
+  r.cinfo = reinterpret_cast<int32_t*>(at);
+  r.ncu = reinterpret_cast<int32_t*>(at + round256(static_cast<size_t>(p.NC()) * 4));
+  r.docoff = reinterpret_cast<int32_t*>(at + round256(static_cast<size_t>(p.NC()) * 4) + 256);
+  return r;
+}
+
+// One workgroup: each thread takes a run of consecutive documents, the runs'
+// chunk counts are scanned in LDS, and each thread then writes its
+// documents' first rows and chunk-table entries.  Nothing is written past
+// the NCmax chunks the launch sizes count: a document longer than the
+// call's max_len (which must bound every length) is cut there, as the
+// padded form would cut it.
+__global__ __launch_bounds__(256) void plan_kernel(const int32_t* __restrict__ cu, int N, int C, int NCmax,
+                                                   int32_t* __restrict__ cinfo, int32_t* __restrict__ ncu,
+                                                   int32_t* __restrict__ docoff) {
+  __shared__ int run[256];
+  const int t = threadIdx.x;
+  const int per = (N + 255) / 256;
+  const int d0 = min(N, t * per), d1 = min(N, d0 + per);
+  int sum = 0;
+  for (int d = d0; d < d1; ++d) sum += (cu[d + 1] - cu[d] + C - 1) / C;
+  run[t] = sum;
+  __syncthreads();
+  if (t == 0) {
+    int acc = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int v = run[i];
+      run[i] = acc;
+      acc += v;
+    }
+    *ncu = min(acc, NCmax);
+  }
+  __syncthreads();
+  int c0 = run[t];
+  for (int d = d0; d < d1; ++d) {
+    const int n = (cu[d + 1] - cu[d] + C - 1) / C;
+    docoff[d] = c0 * C;
+    for (int k = 0; k < n && c0 + k < NCmax; ++k)
+      cinfo[c0 + k] = d | (k == 0 ? CI_START : 0) | (k == n - 1 ? CI_END : 0);
+    c0 += n;
+  }
+}
+
+// Sequence tensors between the caller's packed [T_total, H, D] layout and the
+// chunk-aligned one, in 16-byte words (WW per token): document d's tokens
+// from row docoff[d], zero rows after them to its last chunk's end.  Rows
+// past the chunks in use are neither written nor read.
+__global__ void pack_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int WW, int C,
+                            const int32_t* __restrict__ cu, const int32_t* __restrict__ cinfo,
+                            const int32_t* __restrict__ ncu, const int32_t* __restrict__ docoff, int to_packed) {
+  const size_t used = static_cast<size_t>(*ncu) * C * WW;
+  for (size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < used;
+       idx += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const size_t row = idx / WW;
+    const int w = static_cast<int>(idx - row * WW);
+    const int d = cinfo[row / C] & CI_DOC;
+    const int t = static_cast<int>(row) - docoff[d];
+    const int len = cu[d + 1] - cu[d];
+    const size_t crow = static_cast<size_t>(cu[d]) + t;
+    if (to_packed) {
+      const uint4 z = {0u, 0u, 0u, 0u};
+      dst[idx] = t < len ? src[crow * WW + w] : z;
+    } else if (t < len) {
+      dst[crow * WW + w] = src[idx];
+    }
+  }
+}
+
+hipError_t pack(const void* src, void* dst, const ChunkShape& p, int D, size_t esize, const int32_t* cu,
+                const Plan& pl, bool to_packed, hipStream_t s) {
+  const int WW = static_cast<int>(static_cast<size_t>(p.H) * D * esize / 16);
+  const size_t total = static_cast<size_t>(p.T) * WW;  // the most the chunks in use can hold
+  if (total == 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>(total / 256 + 1 < 8192 ? total / 256 + 1 : 8192);
+  hipLaunchKernelGGL(pack_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const uint4*>(src),
+                     static_cast<uint4*>(dst), WW, p.C, cu, pl.cinfo, pl.ncu, pl.docoff, to_packed ? 1 : 0);
+  return hipGetLastError();
+}
+
+// Documents without tokens: the final state is the initial state (zero
+// without one), and the initial state's gradient is the final state's.  16
+// blocks per document, n floats each.
+__global__ void empty_docs_kernel(const int32_t* __restrict__ cu, size_t n, const float* __restrict__ src,
+                                  float* __restrict__ dst) {
+  const int d = blockIdx.x / 16;
+  if (cu[d + 1] != cu[d]) return;
+  const size_t base = static_cast<size_t>(d) * n;
+  for (size_t i = static_cast<size_t>(blockIdx.x % 16) * blockDim.x + threadIdx.x; i < n; i += 16 * blockDim.x)
+    dst[base + i] = src ? src[base + i] : 0.f;
+}
+hipError_t empty_docs(const int32_t* cu, int N, const ChunkShape& s, const float* src, float* dst, hipStream_t hs) {
+  if (!dst || N == 0) return hipSuccess;
+  hipLaunchKernelGGL(empty_docs_kernel, dim3(static_cast<unsigned>(N) * 16), dim3(256), 0, hs, cu,
+                     static_cast<size_t>(s.H) * s.DK * s.DV, src, dst);
+  return hipGetLastError();
+}
+
+muir_status_t pack_inputs(const ChunkShape& p, const int32_t* cu, const Plan& pl, const Inputs& in, Inputs* out,
+                          StageCursor* cur, hipStream_t hs) {
+  for (int i = 0; i < 7; ++i) {
+    if (i == 6 && p.gmode != MUIR_GAMMA_TOKEN) {
+      out->x[6] = in.x[6];  // a static gate is [H, dk] and needs no staging; an absent one is not read
+      continue;
+    }
+    const int D = kIsDk[i] ? p.DK : p.DV;
+    void* dst = cur->take(p, D, p.tc_bytes());
+    if (pack(in.x[i], dst, p, D, p.tc_bytes(), cu, pl, true, hs) != hipSuccess) return MUIR_ERR_HIP;
+    out->x[i] = dst;
+  }
+  return MUIR_OK;
+}
+
+size_t packed_fwd_need(const ChunkShape& s) {
+  const ChunkShape p = packed_shape(s);
+  return fwd_ws(p) + fwd_stage_bytes(p) + plan_bytes(p, s.B);
+}
+size_t packed_bwd_need(const ChunkShape& s) {
+  const ChunkShape p = packed_shape(s);
+  return bwd_ws(p) + bwd_stage_bytes(p) + plan_bytes(p, s.B);
+}
+
+muir_status_t fwd_packed(const ChunkShape& s, const int32_t* cu, const Inputs& in, const float* S0, void* o,
+                         float* S_T, void* workspace, hipStream_t hs) {
+  ChunkShape p = packed_shape(s);
+  char* w = static_cast<char*>(workspace);
+  const Plan pl = carve_plan(w + fwd_ws(p) + fwd_stage_bytes(p), p);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, hs, cu, s.B, s.C, p.NC(), pl.cinfo, pl.ncu, pl.docoff);
+  if (hipGetLastError() != hipSuccess) return MUIR_ERR_HIP;
+  p.cinfo = pl.cinfo;
+  p.ncu = pl.ncu;
+  StageCursor cur{w + fwd_ws(p)};
+  Inputs sin;
+  muir_status_t st = pack_inputs(p, cu, pl, in, &sin, &cur, hs);
+  if (st != MUIR_OK) return st;
+  void* po = cur.take(p, p.DV, p.tc_bytes());
+  if ((st = fwd_core(p, sin, S0, po, S_T, nullptr, workspace, hs)) != MUIR_OK) return st;
+  if (pack(po, o, p, p.DV, p.tc_bytes(), cu, pl, false, hs) != hipSuccess) return MUIR_ERR_HIP;
+  return empty_docs(cu, s.B, s, S0, S_T, hs) == hipSuccess ? MUIR_OK : MUIR_ERR_HIP;
+}
+
+muir_status_t bwd_packed(const ChunkShape& s, const int32_t* cu, const Inputs& in, const float* S0, const void* dO,
+                         const float* dS_T, const Grads& gr, float* dS0, void* workspace, hipStream_t hs) {
+  ChunkShape p = packed_shape(s);
+  char* w = static_cast<char*>(workspace);
+  const Plan pl = carve_plan(w + bwd_ws(p) + bwd_stage_bytes(p), p);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, hs, cu, s.B, s.C, p.NC(), pl.cinfo, pl.ncu, pl.docoff);
+  if (hipGetLastError() != hipSuccess) return MUIR_ERR_HIP;
+  p.cinfo = pl.cinfo;
+  p.ncu = pl.ncu;
+  StageCursor cur{w + bwd_ws(p)};
+  Inputs sin;
+  muir_status_t st = pack_inputs(p, cu, pl, in, &sin, &cur, hs);
+  if (st != MUIR_OK) return st;
+  void* pdO = cur.take(p, p.DV, p.tc_bytes());
+  if (pack(dO, pdO, p, p.DV, p.tc_bytes(), cu, pl, true, hs) != hipSuccess) return MUIR_ERR_HIP;
+  Grads sg;
+  for (int i = 0; i < 7; ++i) {
+    if (i == 6 && p.gmode != MUIR_GAMMA_TOKEN) {
+      sg.x[6] = gr.x[6];  // a static gate's gradient is [H, dk] fp32; an absent gate has none
+      continue;
+    }
+    sg.x[i] = cur.take(p, kIsDk[i] ? p.DK : p.DV, p.tg_bytes());
+  }
+  if ((st = bwd_core(p, sin, S0, nullptr, nullptr, pdO, dS_T, sg, dS0, workspace, hs)) != MUIR_OK) return st;
+  for (int i = 0; i < 7; ++i) {
+    if (i == 6 && p.gmode != MUIR_GAMMA_TOKEN) continue;
+    if (pack(sg.x[i], gr.x[i], p, kIsDk[i] ? p.DK : p.DV, p.tg_bytes(), cu, pl, false, hs) != hipSuccess)
+      return MUIR_ERR_HIP;
+  }
+  return empty_docs(cu, s.B, s, dS_T, dS0, hs) == hipSuccess ? MUIR_OK : MUIR_ERR_HIP;
+}
+
 size_t fwd_need(const ChunkShape& s) {
   return s.T % s.C == 0 ? fwd_ws(s) : fwd_ws(padded(s)) + fwd_stage_bytes(padded(s));
 }
@@ -482,8 +691,12 @@ __global__ __launch_bounds__(256) void check_values_kernel(int64_t n, const T* _
   }
 }
 
-size_t varlen_fwd_need(const ChunkShape& s) { return fwd_ws(padded(s)) + fwd_stage_bytes(padded(s)); }
-size_t varlen_bwd_need(const ChunkShape& s) { return bwd_ws(padded(s)) + bwd_stage_bytes(padded(s)); }
+size_t varlen_fwd_need(const ChunkShape& s) {
+  return packable(s) ? packed_fwd_need(s) : fwd_ws(padded(s)) + fwd_stage_bytes(padded(s));
+}
+size_t varlen_bwd_need(const ChunkShape& s) {
+  return packable(s) ? packed_bwd_need(s) : bwd_ws(padded(s)) + bwd_stage_bytes(padded(s));
+}
 
 }  // namespace
 
@@ -631,6 +844,7 @@ muir_status_t muir_chunk_varlen_fwd(const muir_dims_t* dims, const int32_t* cu_s
   if (s.nchunks() != 0 && !cu_seqlens) return MUIR_ERR_NULL;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (s.nchunks() == 0) return fwd_empty(s, S0, S_T, hs);
+  if (packable(s)) return fwd_packed(s, cu_seqlens, in, S0, o, S_T, workspace, hs);
   return fwd_staged(s, cu_seqlens, in, S0, o, S_T, nullptr, workspace, hs);
 }
 
@@ -651,6 +865,7 @@ muir_status_t muir_chunk_varlen_bwd(const muir_dims_t* dims, const int32_t* cu_s
   if (s.nchunks() != 0 && !cu_seqlens) return MUIR_ERR_NULL;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (s.nchunks() == 0) return bwd_empty(s, dS_T, dgamma, dS0, hs);
+  if (packable(s)) return bwd_packed(s, cu_seqlens, in, S0, dO, dS_T, gr, dS0, workspace, hs);
   return bwd_staged(s, cu_seqlens, in, S0, nullptr, nullptr, dO, dS_T, gr, dS0, workspace, hs);
 }
 

@@ -134,7 +134,8 @@ __global__ __launch_bounds__(64 * NW * RS) __attribute__((amdgpu_waves_per_eu(TR
     int T, int H, int C, const char* __restrict__ summ, size_t summ_bytes,
     const float* __restrict__ S0, Tin* __restrict__ o, Tin* __restrict__ S_chunks,
     float* __restrict__ S_T, char* __restrict__ dsumm, size_t dl_offset, int nseg,
-    const float* __restrict__ S_seg, float* __restrict__ trans) {
+    const float* __restrict__ S_seg, float* __restrict__ trans, const int32_t* __restrict__ cinfo,
+    const int32_t* __restrict__ ncu) {
   typedef Tin TC;
   typedef MM<TC> M;
   typedef typename M::frag frag;
@@ -163,15 +164,16 @@ __global__ __launch_bounds__(64 * NW * RS) __attribute__((amdgpu_waves_per_eu(TR
   static_assert(RTW % 2 == 0 && (RS == 1 || RS == 2), "row split");
 
   const int NC = T / C;
+  const int NCU = ncu ? min(*ncu, NC) : NC;  // chunks in use (packed documents: see ChunkShape)
   const int NSB = C / SB;
   const int nvb = NCOL / NV;
   const int2 gm = xcd_group(blockIdx.x, nvb, static_cast<int>(gridDim.x) / nvb);
   const int bh = gm.x / nseg;
   const int seg = gm.x - bh * nseg;
   const int vb = gm.y;
-  const int L = (NC + nseg - 1) / nseg;  // chunks per segment
-  const int cbeg = min(NC, seg * L);
-  const int cend = min(NC, cbeg + L);
+  const int L = (NCU + nseg - 1) / nseg;  // chunks per segment
+  const int cbeg = min(NCU, seg * L);
+  const int cend = min(NCU, cbeg + L);
   const bool pcols = TRANS && vb * NV >= DV;  // transition columns: no U~ (their loads read tile 0)
   const int vbu = pcols ? 0 : vb;
   const int b = bh / H;
@@ -287,10 +289,30 @@ __global__ __launch_bounds__(64 * NW * RS) __attribute__((amdgpu_waves_per_eu(TR
 
   const int U0 = cbeg * NSB, U1 = cend * NSB;
   if (U0 < U1) prefetch(U0);
+  // packed documents: this chunk's table entry, and the next chunk's, loaded
+  // a chunk ahead
+  int cinf = 0, cinf_next = (cinfo && cbeg < cend) ? cinfo[cbeg] : 0;
 #pragma unroll 1
   for (int u = U0; u < U1; ++u) {
     const int c = u / NSB;
     const int sb = u - c * NSB;
+    if (cinfo && sb == 0) {
+      cinf = cinf_next;
+      cinf_next = c + 1 < cend ? cinfo[c + 1] : 0;
+      if (cinf & CI_START) {
+        // a document's first chunk: its S0 (zero without one); in the
+        // transition pass [S | P] = [S0 | 0], since no earlier state reaches
+        // past this chunk
+        const float* src = S0 ? S0 + (static_cast<size_t>(cinf & CI_DOC) * H + h) * DK * DV : nullptr;
+#pragma unroll
+        for (int s = 0; s < RTW; ++s)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 16 * (s0 + s) + 4 * g + i;
+            S[s][i] = (src && !pcols) ? src[static_cast<size_t>(row) * DV + colg] : 0.f;
+          }
+      }
+    }
     // The chunk-start state is stored first, ahead of this unit's commit and
     // the next unit's loads: vector memory instructions issue in order, so
     // stores queued behind a unit of loads wait for them.  (Measured at B = 8,
@@ -428,6 +450,14 @@ __global__ __launch_bounds__(64 * NW * RS) __attribute__((amdgpu_waves_per_eu(TR
       for (int s = 0; s < RTW; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[s][i] = sgC[16 * (s0 + s) + 4 * g + i] * S[s][i] + dS[s][i];
+      if (!TRANS && (cinf & CI_END) && S_T) {
+        // a document's last chunk: its final state
+        float* dst = S_T + (static_cast<size_t>(cinf & CI_DOC) * H + h) * DK * DV;
+#pragma unroll
+        for (int s = 0; s < RTW; ++s)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * (s0 + s) + 4 * g + i) * DV + colg] = S[s][i];
+      }
     }
   }
   if constexpr (TRANS) {
@@ -436,7 +466,7 @@ __global__ __launch_bounds__(64 * NW * RS) __attribute__((amdgpu_waves_per_eu(TR
     for (int s = 0; s < RTW; ++s)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * (s0 + s) + 4 * g + i) * NCOL + colg] = S[s][i];
-  } else if (S_T && seg == nseg - 1) {
+  } else if (S_T && seg == nseg - 1 && !cinfo) {
 #pragma unroll
     for (int s = 0; s < RTW; ++s)
 #pragma unroll
@@ -464,7 +494,8 @@ template <typename Tin, int DK, int NW, bool TRANS, int RS>
 __global__ __launch_bounds__(64 * NW * RS) void bwd_scan_kernel(
     int T, int H, int C, const char* __restrict__ summ, size_t summ_bytes,
     const Tin* __restrict__ dO, const float* __restrict__ dS_T, Tin* __restrict__ dS_chunks,
-    float* __restrict__ dS0, int nseg, const float* __restrict__ dS_seg, float* __restrict__ trans) {
+    float* __restrict__ dS0, int nseg, const float* __restrict__ dS_seg, float* __restrict__ trans,
+    const int32_t* __restrict__ cinfo, const int32_t* __restrict__ ncu) {
   typedef Tin TC;
   typedef MM<TC> M;
   typedef typename M::frag frag;
@@ -497,15 +528,16 @@ __global__ __launch_bounds__(64 * NW * RS) void bwd_scan_kernel(
   static_assert(RTW % 2 == 0 && (RS == 1 || RS == 2), "row split");
 
   const int NC = T / C;
+  const int NCU = ncu ? min(*ncu, NC) : NC;  // chunks in use (packed documents: see ChunkShape)
   const int NSB = C / SB;
   const int nvb = DV / NV;
   const int2 gm = xcd_group(blockIdx.x, nvb, static_cast<int>(gridDim.x) / nvb);
   const int bh = gm.x / nseg;
   const int seg = gm.x - bh * nseg;
   const int vb = gm.y;
-  const int L = (NC + nseg - 1) / nseg;  // chunks per segment
-  const int cbeg = min(NC, seg * L);
-  const int cend = min(NC, cbeg + L);
+  const int L = (NCU + nseg - 1) / nseg;  // chunks per segment
+  const int cbeg = min(NCU, seg * L);
+  const int cend = min(NCU, cbeg + L);
   const int b = bh / H;
   const int h = bh - b * H;
   const int tid = threadIdx.x;
@@ -598,7 +630,7 @@ __global__ __launch_bounds__(64 * NW * RS) void bwd_scan_kernel(
   {
     // the segment's end: zero with TRANS, else dS_T or the segment state
     const float* src = TRANS ? nullptr
-                       : seg == nseg - 1 ? (dS_T ? dS_T + sbase : nullptr)
+                       : seg == nseg - 1 ? ((dS_T && !cinfo) ? dS_T + sbase : nullptr)
                                          : dS_seg + (static_cast<size_t>(bh) * nseg + seg) * DK * DV;
 #pragma unroll
     for (int s = 0; s < RTW; ++s)
@@ -611,10 +643,27 @@ __global__ __launch_bounds__(64 * NW * RS) void bwd_scan_kernel(
 
   const int U = (cend - cbeg) * NSB;
   if (U > 0) prefetch(0);
+  // packed documents: this chunk's table entry, and the next one's (the chunk
+  // before it), loaded a chunk ahead
+  int cinf = 0, cinf_next = (cinfo && U > 0) ? cinfo[cend - 1] : 0;
 #pragma unroll 1
   for (int u = 0; u < U; ++u) {
     const int c = unit_c(u);
     const int sb = unit_sb(u);
+    if (cinfo && sb == NSB - 1) {
+      cinf = cinf_next;
+      cinf_next = c - 1 >= cbeg ? cinfo[c - 1] : 0;
+      if (cinf & CI_END) {
+        // a document's last chunk: the gradient at its end is the document's
+        // dS_T (zero without one)
+        const float* src = dS_T ? dS_T + (static_cast<size_t>(cinf & CI_DOC) * H + h) * DK * DV : nullptr;
+#pragma unroll
+        for (int s = 0; s < RTW; ++s)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            dS[s][i] = src ? src[static_cast<size_t>(16 * (s0 + s) + 4 * g + i) * DV + colg] : 0.f;
+      }
+    }
     __syncthreads();
     commit();
     // The chunk-end gradient is stored after the commit, before the next
@@ -706,6 +755,20 @@ __global__ __launch_bounds__(64 * NW * RS) void bwd_scan_kernel(
       for (int s = 0; s < RTW; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i) dS[s][i] = sgC[16 * (s0 + s) + 4 * g + i] * dS[s][i] + Z[s][i];
+      if (cinf & CI_START) {
+        // a document's first chunk: the gradient at its start is the
+        // document's dS0; none of it reaches the chunk before (another
+        // document's), so the flow is cut there
+        if (!TRANS && dS0) {
+          float* dst = dS0 + (static_cast<size_t>(cinf & CI_DOC) * H + h) * DK * DV;
+#pragma unroll
+          for (int s = 0; s < RTW; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * (s0 + s) + 4 * g + i) * DV + colg] = dS[s][i];
+        }
+#pragma unroll
+        for (int s = 0; s < RTW; ++s) dS[s] = zero4();
+      }
     }
   }
   if constexpr (TRANS) {
@@ -714,7 +777,7 @@ __global__ __launch_bounds__(64 * NW * RS) void bwd_scan_kernel(
     for (int s = 0; s < RTW; ++s)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * (s0 + s) + 4 * g + i) * TS + colg] = dS[s][i];
-  } else if (dS0 && seg == 0) {
+  } else if (dS0 && seg == 0 && !cinfo) {
 #pragma unroll
     for (int s = 0; s < RTW; ++s)
 #pragma unroll
@@ -820,13 +883,15 @@ __global__ __launch_bounds__(4 * DK) void seg_combine_kernel(int nseg, const flo
 // recurrence, then every segment's scan from its start -- else one wave (16
 // columns) per workgroup.
 // Each segment's offset and transition, [E_g | P_g], into trans.
+// (S0 is read only at the first chunks of packed documents.)
 template <typename TT, int DD>
-void fwd_trans_typed(const ChunkShape& s, const void* summ, float* trans, hipStream_t stream) {
+void fwd_trans_typed(const ChunkShape& s, const void* summ, const float* S0, float* trans, hipStream_t stream) {
   const int heads = s.B * s.H;
   const int nseg = s.scan_segments();
   hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, true, 1>), dim3(heads * nseg * (2 * DD / 64)), dim3(256), 0, stream,
-                     s.T, s.H, s.C, (const char*)summ, s.summary_bytes(), (const float*)nullptr, (TT*)nullptr,
-                     (TT*)nullptr, (float*)nullptr, (char*)nullptr, size_t(0), nseg, (const float*)nullptr, trans);
+                     s.T, s.H, s.C, (const char*)summ, s.summary_bytes(), s.cinfo ? S0 : (const float*)nullptr,
+                     (TT*)nullptr, (TT*)nullptr, (float*)nullptr, (char*)nullptr, size_t(0), nseg,
+                     (const float*)nullptr, trans, s.cinfo, s.ncu);
 }
 
 template <typename TT, int DD>
@@ -839,20 +904,22 @@ hipError_t fwd_scan_typed(const ChunkShape& s, const void* summ, const float* S0
   if (nseg > 1) {
     float* trans = split;
     float* sseg = split + static_cast<size_t>(heads) * nseg * DD * (2 * DD);
-    fwd_trans_typed<TT, DD>(s, summ, trans, stream);
-    hipLaunchKernelGGL((seg_combine_kernel<DD, false>), dim3(heads * (DD / 16)), dim3(4 * DD), 0, stream, nseg, S0,
-                       (const float*)trans, (const float*)trans, sseg);
+    fwd_trans_typed<TT, DD>(s, summ, S0, trans, stream);
+    // (packed documents: the first chunk starts a document, whose own S0 the
+    // scan takes there)
+    hipLaunchKernelGGL((seg_combine_kernel<DD, false>), dim3(heads * (DD / 16)), dim3(4 * DD), 0, stream, nseg,
+                       s.cinfo ? (const float*)nullptr : S0, (const float*)trans, (const float*)trans, sseg);
     hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, false, 2>), dim3(heads * nseg * (DD / 64)), dim3(512), 0, stream,
                        s.T, s.H, s.C, (const char*)summ, sb, S0, (TT*)o, S_chunks, S_T, (char*)deltas,
-                       s.dl_offset(), nseg, (const float*)sseg, (float*)nullptr);
+                       s.dl_offset(), nseg, (const float*)sseg, (float*)nullptr, s.cinfo, s.ncu);
   } else if (static_cast<long long>(heads) * (DD / 64) >= 256) {
     hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, false, 2>), dim3(heads * (DD / 64)), dim3(512), 0, stream, s.T,
                        s.H, s.C, (const char*)summ, sb, S0, (TT*)o, S_chunks, S_T, (char*)deltas, s.dl_offset(), 1,
-                       (const float*)nullptr, (float*)nullptr);
+                       (const float*)nullptr, (float*)nullptr, s.cinfo, s.ncu);
   } else {
     hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 1, false, 1>), dim3(heads * (DD / 16)), dim3(64), 0, stream, s.T,
                        s.H, s.C, (const char*)summ, sb, S0, (TT*)o, S_chunks, S_T, (char*)deltas, s.dl_offset(), 1,
-                       (const float*)nullptr, (float*)nullptr);
+                       (const float*)nullptr, (float*)nullptr, s.cinfo, s.ncu);
   }
   return hipGetLastError();
 }
@@ -868,22 +935,23 @@ hipError_t bwd_scan_typed(const ChunkShape& s, const void* summ, const void* dO,
     // the transposes of the forward's, read from ftrans
     float* trans = split;
     float* sseg = split + static_cast<size_t>(heads) * nseg * DD * (2 * DD);
+    // (the transition pass takes each packed document's dS_T at its last chunk)
     hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, true, 2>), dim3(heads * nseg * (DD / 64)), dim3(512), 0, stream,
                        s.T, s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks, (float*)nullptr,
-                       nseg, (const float*)nullptr, trans);
-    hipLaunchKernelGGL((seg_combine_kernel<DD, true>), dim3(heads * (DD / 16)), dim3(4 * DD), 0, stream, nseg, dS_T,
-                       (const float*)trans, ftrans, sseg);
+                       nseg, (const float*)nullptr, trans, s.cinfo, s.ncu);
+    hipLaunchKernelGGL((seg_combine_kernel<DD, true>), dim3(heads * (DD / 16)), dim3(4 * DD), 0, stream, nseg,
+                       s.cinfo ? (const float*)nullptr : dS_T, (const float*)trans, ftrans, sseg);
     hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, false, 2>), dim3(heads * nseg * (DD / 64)), dim3(512), 0, stream,
                        s.T, s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks, dS0, nseg,
-                       (const float*)sseg, (float*)nullptr);
+                       (const float*)sseg, (float*)nullptr, s.cinfo, s.ncu);
   } else if (static_cast<long long>(heads) * (DD / 64) >= 256) {
     hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, false, 2>), dim3(heads * (DD / 64)), dim3(512), 0, stream, s.T,
                        s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks, dS0, 1,
-                       (const float*)nullptr, (float*)nullptr);
+                       (const float*)nullptr, (float*)nullptr, s.cinfo, s.ncu);
   } else {
     hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 1, false, 1>), dim3(heads * (DD / 16)), dim3(64), 0, stream, s.T,
                        s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks, dS0, 1,
-                       (const float*)nullptr, (float*)nullptr);
+                       (const float*)nullptr, (float*)nullptr, s.cinfo, s.ncu);
   }
   return hipGetLastError();
 }
@@ -901,12 +969,13 @@ hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S
 
 hipError_t launch_fwd_trans(const ChunkShape& s, const void* summ, float* split, hipStream_t stream) {
   if (s.B * s.H == 0 || s.scan_segments() < 2) return hipSuccess;
+  if (s.cinfo) return hipErrorInvalidValue;  // packed documents need their S0 here: launch_fwd_scan forms these
   if (s.bf16) {
-    if (s.DK == 128) fwd_trans_typed<uint16_t, 128>(s, summ, split, stream);
-    else fwd_trans_typed<uint16_t, 64>(s, summ, split, stream);
+    if (s.DK == 128) fwd_trans_typed<uint16_t, 128>(s, summ, nullptr, split, stream);
+    else fwd_trans_typed<uint16_t, 64>(s, summ, nullptr, split, stream);
   } else {
-    if (s.DK == 128) fwd_trans_typed<float, 128>(s, summ, split, stream);
-    else fwd_trans_typed<float, 64>(s, summ, split, stream);
+    if (s.DK == 128) fwd_trans_typed<float, 128>(s, summ, nullptr, split, stream);
+    else fwd_trans_typed<float, 64>(s, summ, nullptr, split, stream);
   }
   return hipGetLastError();
 }

@@ -261,15 +261,20 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims,
  *                for muir_chunk_fwd.  The workspace size depends on B * T.
  *   cu_seqlens : [B + 1] int32 DEVICE array, cu_seqlens[0] = 0 and
  *                non-decreasing.  Precondition (not checked, as the array is
- *                on the device): every length is <= dims->T; tokens of a
- *                longer sequence past dims->T are neither read nor written.
+ *                on the device): every length is <= dims->T.  If one is
+ *                longer, the call still reads and writes only the given
+ *                tensors and its workspace, but its results are unspecified.
  *   q, k, log_a, erase, (per-token) gamma : [T_total, H, dk] dtype
  *   v, write, o                           : [T_total, H, dv] dtype
  *   S0, S_T    : [B, H, dk, dv] fp32 per sequence, as in muir_chunk_fwd
- * The call copies the sequences into zero-padded [B, T_pad, H, D] tensors in
- * its workspace (T_pad = T rounded up to the chunk), runs the chunkwise
- * kernels there, and copies the real tokens' results back.  Chunk states and
- * summaries are not exported: the backward recomputes them.
+ * The call copies the sequences into one sequence in its workspace, each
+ * starting at a chunk boundary and zero-padded to its last chunk's end; the
+ * scans start each sequence from its own S0 and end it at its own S_T, and
+ * the chunk kernels see only the sequences' own chunks.  It then copies the
+ * real tokens' results back.  (Shapes whose B * T_pad reaches 2^31 rows, with
+ * T_pad = T rounded up to the chunk, run on zero-padded [B, T_pad, H, D]
+ * copies instead.)  Chunk states and summaries are not exported: the
+ * backward recomputes them.
  */
 size_t muir_chunk_varlen_fwd_workspace(const muir_dims_t* dims);
 

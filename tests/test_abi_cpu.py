@@ -239,11 +239,15 @@ def test_partial_chunk_needs_a_staging_area():
     d = _dims(m, T=100)
     need = L.muir_chunk_fwd_workspace(ctypes.byref(d))
     assert _fwd(m, L, d, ws_bytes=need - 1) == ERR_WORKSPACE
-    # the packed entry points size for dims.T as the longest sequence, padded
+    # the packed entry points size for B documents of at most dims.T tokens
+    # each, as one packed sequence of B ceil(T / C) chunks with a staging copy
+    # of every sequence tensor: the size depends on T only through ceil(T / C),
+    # holds a staging area even for whole chunks, and grows with B
     for fv, fd in ((L.muir_chunk_varlen_fwd_workspace, L.muir_chunk_fwd_workspace),
                    (L.muir_chunk_varlen_bwd_workspace, L.muir_chunk_bwd_workspace)):
-        assert fv(ctypes.byref(_dims(m, B=3, T=100))) == fd(ctypes.byref(_dims(m, B=3, T=100)))
+        assert fv(ctypes.byref(_dims(m, B=3, T=100))) == fv(ctypes.byref(_dims(m, B=3, T=128)))
         assert fv(ctypes.byref(_dims(m, B=3, T=128))) > fd(ctypes.byref(_dims(m, B=3, T=128)))
+        assert fv(ctypes.byref(_dims(m, B=4, T=128))) > fv(ctypes.byref(_dims(m, B=3, T=128)))
         assert fv(ctypes.byref(_dims(m, chunk=48))) == 0
 
 
