@@ -92,9 +92,9 @@ def lib():
         L.muir_chunk_varlen_fwd_workspace.restype = SZ
         L.muir_chunk_varlen_bwd_workspace.argtypes = [D]
         L.muir_chunk_varlen_bwd_workspace.restype = SZ
-        L.muir_chunk_varlen_fwd.argtypes = [D, P] + [P] * 7 + [P, P, P] + [P, SZ, P]
+        L.muir_chunk_varlen_fwd.argtypes = [D, P] + [P] * 7 + [P, P, P] + [I32] + [P, SZ, P]
         L.muir_chunk_varlen_fwd.restype = ctypes.c_int
-        L.muir_chunk_varlen_bwd.argtypes = [D, P] + [P] * 7 + [P, P, P] + [P] * 8 + [P, SZ, P]
+        L.muir_chunk_varlen_bwd.argtypes = [D, P] + [P] * 7 + [P, P, P] + [P] * 8 + [P] + [P, SZ, P]
         L.muir_chunk_varlen_bwd.restype = ctypes.c_int
         GD = ctypes.POINTER(_GateDims)
         L.muir_gate_proj_bwd_workspace.argtypes = [GD]
@@ -404,14 +404,18 @@ def _check_cu(cu_seqlens, dev, total: int, max_len: Optional[int]) -> Tuple[int,
 
 
 def muir_chunk_varlen_fwd(q, k, v, log_a, erase, write, gamma, cu_seqlens, S0=None, *, chunk: int = 64,
-                          max_len: Optional[int] = None, final_state: bool = True,
+                          max_len: Optional[int] = None, final_state: bool = True, keep: bool = False,
                           workspace: Optional[torch.Tensor] = None, out=None
                           ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Forward of packed variable-length sequences: inputs [T_total, H, D]
     with sequence n in rows cu_seqlens[n] .. cu_seqlens[n+1]-1 (cu_seqlens an
     int32 GPU tensor [N + 1]); gamma [T_total, H, dk], [H, dk] or None; S0
     [N, H, dk, dv] fp32 or None.  Returns (o [T_total, H, dv], S_T [N, H, dk,
-    dv] fp32 or None)."""
+    dv] fp32 or None).  keep: leave the chunk states, summaries and packed
+    inputs in `workspace` (which must then be given) for
+    muir_chunk_varlen_bwd(fwd_workspace=workspace)."""
+    if keep and workspace is None:
+        raise ValueError("keep: pass the workspace that the backward will take")
     Tt, H, dk = q.shape
     dv = v.shape[2]
     dev, dt = q.device, q.dtype
@@ -430,8 +434,8 @@ def muir_chunk_varlen_fwd(q, k, v, log_a, erase, write, gamma, cu_seqlens, S0=No
     ws = _workspace(int(lib().muir_chunk_varlen_fwd_workspace(ctypes.byref(d))), dev, workspace)
     rc = lib().muir_chunk_varlen_fwd(ctypes.byref(d), _ptr(cu_seqlens),
                                      *(_ptr(t) for t in (q, k, v, log_a, erase, write, gamma)),
-                                     _ptr(S0), _ptr(o), _ptr(S_T), _ptr(ws), ctypes.c_size_t(ws.numel()),
-                                     _stream(dev))
+                                     _ptr(S0), _ptr(o), _ptr(S_T), 1 if keep else 0, _ptr(ws),
+                                     ctypes.c_size_t(ws.numel()), _stream(dev))
     if rc != 0:
         raise MuirError(rc, "muir_chunk_varlen_fwd")
     return o, S_T
@@ -440,10 +444,11 @@ def muir_chunk_varlen_fwd(q, k, v, log_a, erase, write, gamma, cu_seqlens, S0=No
 def muir_chunk_varlen_bwd(q, k, v, log_a, erase, write, gamma, dO, cu_seqlens, S0=None, dS_T=None, *,
                           chunk: int = 64, max_len: Optional[int] = None,
                           workspace: Optional[torch.Tensor] = None, want_dS0: bool = True,
-                          grad_dtype: Optional[torch.dtype] = None):
+                          grad_dtype: Optional[torch.dtype] = None, fwd_workspace: Optional[torch.Tensor] = None):
     """Backward of muir_chunk_varlen_fwd.  Returns the gradients as
     muir_chunk_bwd does (per-token ones [T_total, H, D] in `grad_dtype`, fp32
-    by default) and dS0 [N, H, dk, dv]."""
+    by default) and dS0 [N, H, dk, dv].  fwd_workspace: the workspace of a
+    keep=True forward on the same sequences, reused instead of recomputing."""
     Tt, H, dk = q.shape
     dv = v.shape[2]
     dev, dt = q.device, q.dtype
@@ -472,7 +477,7 @@ def muir_chunk_varlen_bwd(q, k, v, log_a, erase, write, gamma, dO, cu_seqlens, S
                                      _ptr(S0), _ptr(dO), _ptr(dS_T),
                                      *(_ptr(g[n]) for n in ("dq", "dk", "dv", "dlog_a", "derase", "dwrite",
                                                             "dgamma", "dS0")),
-                                     _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
+                                     _ptr(fwd_workspace), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
     if rc != 0:
         raise MuirError(rc, "muir_chunk_varlen_bwd")
     return g

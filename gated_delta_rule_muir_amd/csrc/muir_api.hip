@@ -558,47 +558,95 @@ muir_status_t pack_inputs(const ChunkShape& p, const int32_t* cu, const Plan& pl
   return MUIR_OK;
 }
 
+// The chunk-start states a packed forward keeps for its backward (keep), in
+// the compute type, after the plan; always reserved.
+size_t packed_states_bytes(const ChunkShape& p) {
+  return round256(p.nchunks() * static_cast<size_t>(p.DK) * p.DV * p.tc_bytes());
+}
 size_t packed_fwd_need(const ChunkShape& s) {
   const ChunkShape p = packed_shape(s);
-  return fwd_ws(p) + fwd_stage_bytes(p) + plan_bytes(p, s.B);
+  return fwd_ws(p) + fwd_stage_bytes(p) + plan_bytes(p, s.B) + packed_states_bytes(p);
+}
+// The packed forward's workspace: its kernels' workspace (the chunk
+// summaries, then the split scans' area), the packed inputs and o, the plan,
+// the kept chunk-start states.
+struct PackedFwd {
+  char* ws;
+  Plan pl;
+  char* staging;
+  void* S_chunks;
+};
+PackedFwd packed_fwd_parts(void* workspace, const ChunkShape& p, int N) {
+  char* w = static_cast<char*>(workspace);
+  PackedFwd r;
+  r.ws = w;
+  r.staging = w + fwd_ws(p);
+  r.pl = carve_plan(r.staging + fwd_stage_bytes(p), p);
+  r.S_chunks = r.staging + fwd_stage_bytes(p) + plan_bytes(p, N);
+  return r;
 }
 size_t packed_bwd_need(const ChunkShape& s) {
   const ChunkShape p = packed_shape(s);
   return bwd_ws(p) + bwd_stage_bytes(p) + plan_bytes(p, s.B);
 }
 
+// keep: the chunk-start states (and with them the deltas, in the summaries)
+// are saved, and the summaries, packed inputs and plan stay in the workspace
+// for muir_chunk_varlen_bwd to reuse.
 muir_status_t fwd_packed(const ChunkShape& s, const int32_t* cu, const Inputs& in, const float* S0, void* o,
-                         float* S_T, void* workspace, hipStream_t hs) {
+                         float* S_T, bool keep, void* workspace, hipStream_t hs) {
   ChunkShape p = packed_shape(s);
-  char* w = static_cast<char*>(workspace);
-  const Plan pl = carve_plan(w + fwd_ws(p) + fwd_stage_bytes(p), p);
+  const PackedFwd f = packed_fwd_parts(workspace, p, s.B);
+  const Plan pl = f.pl;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, hs, cu, s.B, s.C, p.NC(), pl.cinfo, pl.ncu, pl.docoff);
   if (hipGetLastError() != hipSuccess) return MUIR_ERR_HIP;
   p.cinfo = pl.cinfo;
   p.ncu = pl.ncu;
-  StageCursor cur{w + fwd_ws(p)};
+  StageCursor cur{f.staging};
   Inputs sin;
   muir_status_t st = pack_inputs(p, cu, pl, in, &sin, &cur, hs);
   if (st != MUIR_OK) return st;
   void* po = cur.take(p, p.DV, p.tc_bytes());
-  if ((st = fwd_core(p, sin, S0, po, S_T, nullptr, workspace, hs)) != MUIR_OK) return st;
+  if ((st = fwd_core(p, sin, S0, po, S_T, keep ? f.S_chunks : nullptr, workspace, hs)) != MUIR_OK) return st;
   if (pack(po, o, p, p.DV, p.tc_bytes(), cu, pl, false, hs) != hipSuccess) return MUIR_ERR_HIP;
   return empty_docs(cu, s.B, s, S0, S_T, hs) == hipSuccess ? MUIR_OK : MUIR_ERR_HIP;
 }
 
+// fwd_workspace: a keeping forward's workspace, whose plan, packed inputs,
+// summaries and chunk-start states are reused (else all are formed here).
 muir_status_t bwd_packed(const ChunkShape& s, const int32_t* cu, const Inputs& in, const float* S0, const void* dO,
-                         const float* dS_T, const Grads& gr, float* dS0, void* workspace, hipStream_t hs) {
+                         const float* dS_T, const Grads& gr, float* dS0, const void* fwd_workspace, void* workspace,
+                         hipStream_t hs) {
   ChunkShape p = packed_shape(s);
   char* w = static_cast<char*>(workspace);
-  const Plan pl = carve_plan(w + bwd_ws(p) + bwd_stage_bytes(p), p);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, hs, cu, s.B, s.C, p.NC(), pl.cinfo, pl.ncu, pl.docoff);
-  if (hipGetLastError() != hipSuccess) return MUIR_ERR_HIP;
-  p.cinfo = pl.cinfo;
-  p.ncu = pl.ncu;
   StageCursor cur{w + bwd_ws(p)};
   Inputs sin;
-  muir_status_t st = pack_inputs(p, cu, pl, in, &sin, &cur, hs);
-  if (st != MUIR_OK) return st;
+  Plan pl;
+  const void* summ = nullptr;
+  const void* Sc = nullptr;
+  muir_status_t st;
+  if (fwd_workspace) {
+    // the forward's parts, carved as the forward carved them
+    const PackedFwd f = packed_fwd_parts(const_cast<void*>(fwd_workspace), p, s.B);
+    pl = f.pl;
+    StageCursor fc{f.staging};
+    for (int i = 0; i < 7; ++i) {
+      if (i == 6 && p.gmode != MUIR_GAMMA_TOKEN) {
+        sin.x[6] = in.x[6];
+        continue;
+      }
+      sin.x[i] = fc.take(p, kIsDk[i] ? p.DK : p.DV, p.tc_bytes());
+    }
+    summ = f.ws;
+    Sc = f.S_chunks;  // (this call's own input copies are not needed: dO and the gradients take the staging area)
+  } else {
+    pl = carve_plan(w + bwd_ws(p) + bwd_stage_bytes(p), p);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, hs, cu, s.B, s.C, p.NC(), pl.cinfo, pl.ncu, pl.docoff);
+    if (hipGetLastError() != hipSuccess) return MUIR_ERR_HIP;
+  }
+  p.cinfo = pl.cinfo;
+  p.ncu = pl.ncu;
+  if (!fwd_workspace && (st = pack_inputs(p, cu, pl, in, &sin, &cur, hs)) != MUIR_OK) return st;
   void* pdO = cur.take(p, p.DV, p.tc_bytes());
   if (pack(dO, pdO, p, p.DV, p.tc_bytes(), cu, pl, true, hs) != hipSuccess) return MUIR_ERR_HIP;
   Grads sg;
@@ -609,7 +657,7 @@ muir_status_t bwd_packed(const ChunkShape& s, const int32_t* cu, const Inputs& i
     }
     sg.x[i] = cur.take(p, kIsDk[i] ? p.DK : p.DV, p.tg_bytes());
   }
-  if ((st = bwd_core(p, sin, S0, nullptr, nullptr, pdO, dS_T, sg, dS0, workspace, hs)) != MUIR_OK) return st;
+  if ((st = bwd_core(p, sin, S0, Sc, summ, pdO, dS_T, sg, dS0, workspace, hs)) != MUIR_OK) return st;
   for (int i = 0; i < 7; ++i) {
     if (i == 6 && p.gmode != MUIR_GAMMA_TOKEN) continue;
     if (pack(sg.x[i], gr.x[i], p, kIsDk[i] ? p.DK : p.DV, p.tg_bytes(), cu, pl, false, hs) != hipSuccess)
@@ -712,7 +760,7 @@ size_t varlen_bwd_need(const ChunkShape& s) {
 
 extern "C" {
 
-int32_t muir_abi_version(void) { return 9; }
+int32_t muir_abi_version(void) { return 10; }
 
 int32_t muir_set_profile_events(void** events, int32_t count) {
   if (count < 0 || (count > 0 && !events)) return MUIR_ERR_NULL;
@@ -843,7 +891,8 @@ size_t muir_chunk_varlen_bwd_workspace(const muir_dims_t* dims) {
 muir_status_t muir_chunk_varlen_fwd(const muir_dims_t* dims, const int32_t* cu_seqlens, const void* q,
                                     const void* k, const void* v, const void* log_a, const void* erase,
                                     const void* write, const void* gamma, const float* S0, void* o,
-                                    float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
+                                    float* S_T, int32_t keep, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
   ChunkShape s;
   muir_status_t st = check_dims(dims, &s);
   if (st != MUIR_OK) return st;
@@ -854,7 +903,7 @@ muir_status_t muir_chunk_varlen_fwd(const muir_dims_t* dims, const int32_t* cu_s
   if (s.nchunks() != 0 && !cu_seqlens) return MUIR_ERR_NULL;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (s.nchunks() == 0) return fwd_empty(s, S0, S_T, hs);
-  if (packable(s)) return fwd_packed(s, cu_seqlens, in, S0, o, S_T, workspace, hs);
+  if (packable(s)) return fwd_packed(s, cu_seqlens, in, S0, o, S_T, keep != 0, workspace, hs);
   return fwd_staged(s, cu_seqlens, in, S0, o, S_T, nullptr, workspace, hs);
 }
 
@@ -862,8 +911,8 @@ muir_status_t muir_chunk_varlen_bwd(const muir_dims_t* dims, const int32_t* cu_s
                                     const void* k, const void* v, const void* log_a, const void* erase,
                                     const void* write, const void* gamma, const float* S0, const void* dO,
                                     const float* dS_T, void* dq, void* dk, void* dv, void* dlog_a, void* derase,
-                                    void* dwrite, void* dgamma, float* dS0, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
+                                    void* dwrite, void* dgamma, float* dS0, const void* fwd_workspace,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
   ChunkShape s;
   muir_status_t st = check_dims(dims, &s, true);
   if (st != MUIR_OK) return st;
@@ -875,7 +924,8 @@ muir_status_t muir_chunk_varlen_bwd(const muir_dims_t* dims, const int32_t* cu_s
   if (s.nchunks() != 0 && !cu_seqlens) return MUIR_ERR_NULL;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (s.nchunks() == 0) return bwd_empty(s, dS_T, dgamma, dS0, hs);
-  if (packable(s)) return bwd_packed(s, cu_seqlens, in, S0, dO, dS_T, gr, dS0, workspace, hs);
+  if (fwd_workspace && !aligned16(fwd_workspace)) return MUIR_ERR_ALIGN;
+  if (packable(s)) return bwd_packed(s, cu_seqlens, in, S0, dO, dS_T, gr, dS0, fwd_workspace, workspace, hs);
   return bwd_staged(s, cu_seqlens, in, S0, nullptr, nullptr, dO, dS_T, gr, dS0, workspace, hs);
 }
 

@@ -273,8 +273,13 @@ muir_status_t muir_chunk_bwd(const muir_dims_t* dims,
  * the chunk kernels see only the sequences' own chunks.  It then copies the
  * real tokens' results back.  (Shapes whose B * T_pad reaches 2^31 rows, with
  * T_pad = T rounded up to the chunk, run on zero-padded [B, T_pad, H, D]
- * copies instead.)  Chunk states and summaries are not exported: the
- * backward recomputes them.
+ * copies instead.)
+ *   keep       : nonzero: the chunk-start states are saved and, with the
+ *                chunk summaries, the packed inputs and the packing plan,
+ *                left in the workspace, which the backward of the same
+ *                sequences may then take as fwd_workspace instead of
+ *                recomputing them; 0: not saved.  (The padded form ignores
+ *                it.)  The workspace size does not depend on it.
  */
 size_t muir_chunk_varlen_fwd_workspace(const muir_dims_t* dims);
 
@@ -282,7 +287,7 @@ muir_status_t muir_chunk_varlen_fwd(const muir_dims_t* dims, const int32_t* cu_s
                                     const void* q, const void* k, const void* v,
                                     const void* log_a, const void* erase,
                                     const void* write, const void* gamma,
-                                    const float* S0, void* o, float* S_T,
+                                    const float* S0, void* o, float* S_T, int32_t keep,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -292,6 +297,12 @@ muir_status_t muir_chunk_varlen_fwd(const muir_dims_t* dims, const int32_t* cu_s
  * grad_dtype).  dS_T and dS0 are
  * [B, H, dk, dv] per sequence; a static gate's gradient is [H, dk] fp32,
  * summed over every sequence's tokens.
+ *   fwd_workspace : NULL, or the workspace of a muir_chunk_varlen_fwd call
+ *                   with keep != 0 on the same dims, cu_seqlens, inputs and
+ *                   S0, left unchanged since: its packed inputs, summaries and
+ *                   chunk-start states are read instead of formed again
+ *                   (results equal bit for bit).  16-byte aligned.  (The
+ *                   padded form ignores it.)
  */
 size_t muir_chunk_varlen_bwd_workspace(const muir_dims_t* dims);
 
@@ -302,6 +313,7 @@ muir_status_t muir_chunk_varlen_bwd(const muir_dims_t* dims, const int32_t* cu_s
                                     const float* S0, const void* dO, const float* dS_T,
                                     void* dq, void* dk, void* dv, void* dlog_a,
                                     void* derase, void* dwrite, void* dgamma, float* dS0,
+                                    const void* fwd_workspace,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*

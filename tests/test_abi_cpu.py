@@ -50,7 +50,7 @@ def test_status_strings_cover_every_code():
         seen.add(s)
     assert len(seen) == 10
     assert L.muir_status_string(99).decode() == "unknown status"
-    assert L.muir_abi_version() == 9
+    assert L.muir_abi_version() == 10
 
 
 def _dims(m, B=1, T=128, H=2, dk=64, dv=64, chunk=64, dtype=1, gamma_mode=0, grad_dtype=0):
@@ -260,11 +260,11 @@ def test_varlen_rejects_bad_arguments():
     def fwd(dd, cu=FAKE[13], ptrs=None, ws_bytes=1 << 40):
         p = list(FAKE[:7]) if ptrs is None else ptrs
         return L.muir_chunk_varlen_fwd(ctypes.byref(dd) if dd is not None else None, cu, *p, None, FAKE[7],
-                                       None, FAKE[12], ctypes.c_size_t(ws_bytes), None)
+                                       None, 0, FAKE[12], ctypes.c_size_t(ws_bytes), None)
 
-    def bwd(dd, cu=FAKE[13], grads=None, ws_bytes=1 << 40):
+    def bwd(dd, cu=FAKE[13], grads=None, ws_bytes=1 << 40, fws=None):
         g = list(FAKE[:7]) if grads is None else grads
-        return L.muir_chunk_varlen_bwd(ctypes.byref(dd), cu, *FAKE[:7], None, FAKE[8], None, *g, None,
+        return L.muir_chunk_varlen_bwd(ctypes.byref(dd), cu, *FAKE[:7], None, FAKE[8], None, *g, None, fws,
                                        FAKE[12], ctypes.c_size_t(ws_bytes), None)
     assert fwd(None) == ERR_NULL
     assert fwd(d, cu=None) == ERR_NULL
@@ -280,6 +280,8 @@ def test_varlen_rejects_bad_arguments():
     g = list(FAKE[:7])
     g[0] = None
     assert bwd(d, grads=g) == ERR_NULL
+    # a forward workspace to reuse must be 16-byte aligned like the others
+    assert bwd(d, fws=ctypes.c_void_p(0x10004)) == ERR_ALIGN
 
 
 def _gdims(m, M=256, d=128, H=2, dk=64, dv=64, dtype=1):

@@ -116,7 +116,7 @@ def test_long_32k_fwd_bwd_all_heads(name):
 def test_varlen_full_layer():
     """varlen_32k as bench.py runs it: 16 packed documents of mixed length
     (about 32K tokens, H=16, d=128, chunk 64, bf16 inputs, fp32 gradients),
-    the forward then the backward recomputing the chunk states.  Every
+    the forward keeping its chunk states, then the backward reusing them.  Every
     document's outputs, final state and gradients against the oracle on that
     document alone, over every head; the worst (document, head) slice of each
     packed tensor is asserted too, over the documents of at least one chunk."""
@@ -127,14 +127,17 @@ def test_varlen_full_layer():
     inp = muir_inputs.varlen_inputs(lens, w.H, w.dk, w.dv, dtype=w.dtype, decay=w.decay, seed=w.extra["seed"])
     dv = {n: (t.to("cuda") if t is not None else None) for n, t in inp.items()}
     args = [dv[n] for n in NAMES]
-    o, S_T = m.muir_chunk_varlen_fwd(*args, dv["cu_seqlens"], chunk=w.chunk)
-    g = m.muir_chunk_varlen_bwd(*args, dv["dO"], dv["cu_seqlens"], chunk=w.chunk)
+    L = int(lens.max())
+    fws = torch.empty(m.muir_chunk_varlen_fwd_workspace(w.B, L, w.H, w.dk, w.dv, w.chunk), dtype=torch.uint8,
+                      device="cuda")
+    o, S_T = m.muir_chunk_varlen_fwd(*args, dv["cu_seqlens"], chunk=w.chunk, max_len=L, keep=True, workspace=fws)
+    g = m.muir_chunk_varlen_bwd(*args, dv["dO"], dv["cu_seqlens"], chunk=w.chunk, max_len=L, fwd_workspace=fws)
     torch.cuda.synchronize()
     for n in GRADS:
         assert g[n].dtype == torch.float32, n
     o, S_T = o.cpu(), S_T.cpu()
     g = {n: t.cpu() for n, t in g.items()}
-    del dv
+    del dv, fws
     torch.cuda.empty_cache()
     _say("  oracle fwd+bwd on every document ...")
     cu = np.concatenate([[0], np.cumsum(lens)])

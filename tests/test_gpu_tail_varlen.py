@@ -178,6 +178,37 @@ def test_varlen_matches_per_sequence_oracle(case):
         assert e <= TOL[dtype], (n, e)
 
 
+@pytest.mark.parametrize("form", ["token", "static"])
+def test_varlen_backward_reuses_the_forward(form):
+    """A keeping forward leaves its packed inputs, summaries and chunk states
+    in its workspace; the backward that takes it gives the recomputing
+    backward's results bit for bit (the same kernels on the same data), and
+    the keeping forward the plain forward's."""
+    m = _lib()
+    N, max_len, H, d, C = 6, 300, 2, 128, 64
+    lens = muir_inputs.varlen_lengths(N, max_len, C, seed=9)
+    _say(f"varlen reuse form={form} lens={lens.tolist()}")
+    inp = muir_inputs.varlen_inputs(lens, H, d, d, dtype="bf16", decay="channel", seed=29, S0_scale=0.1,
+                                    with_dST=True)
+    inp["gamma_static"] = inp["gamma"][0].clone()
+    dv = to_dev(inp)
+    gam = dv["gamma"] if form == "token" else dv["gamma_static"]
+    args = [dv["q"], dv["k"], dv["v"], dv["log_a"], dv["erase"], dv["write"], gam]
+    cu = dv["cu_seqlens"]
+    gm = m.MUIR_GAMMA_TOKEN if form == "token" else m.MUIR_GAMMA_STATIC
+    ws = torch.empty(m.muir_chunk_varlen_fwd_workspace(N, max_len, H, d, d, C, gamma_mode=gm), dtype=torch.uint8,
+                     device="cuda")
+    o1, S1 = m.muir_chunk_varlen_fwd(*args, cu, dv["S0"], chunk=C, max_len=max_len, keep=True, workspace=ws)
+    o2, S2 = m.muir_chunk_varlen_fwd(*args, cu, dv["S0"], chunk=C, max_len=max_len)
+    kw = dict(S0=dv["S0"], dS_T=dv["dS_T"], chunk=C, max_len=max_len)
+    g1 = m.muir_chunk_varlen_bwd(*args, dv["dO"], cu, fwd_workspace=ws, **kw)
+    g2 = m.muir_chunk_varlen_bwd(*args, dv["dO"], cu, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    for n in GRADS:
+        assert torch.equal(g1[n], g2[n]), n
+
+
 def test_varlen_equal_lengths_equal_batched_call():
     """Packed sequences that all have the same whole-chunk length give
     exactly the batched call's results (the same kernels on the same data)."""
