@@ -129,7 +129,9 @@ template <typename TC> __device__ __forceinline__ typename MM<TC>::frag identity
 // the segment's offset E and transition P into trans[head][seg] ([dk][DV + DK]
 // fp32); without it, segment seg > 0 starts from S_seg[head][seg] ([dk][dv]
 // fp32, formed from those by seg_combine_kernel) and segment 0 from S0.
-template <typename Tin, int DK, int NW, bool TRANS, int RS>
+// DOCS: packed documents (cinfo, ncu given; see ChunkShape).  A separate
+// instance, so that the fixed-length scans carry none of its registers.
+template <typename Tin, int DK, int NW, bool TRANS, int RS, bool DOCS>
 __global__ __launch_bounds__(64 * NW * RS) __attribute__((amdgpu_waves_per_eu(TRANS ? 2 : 1))) void fwd_scan_kernel(
     int T, int H, int C, const char* __restrict__ summ, size_t summ_bytes,
     const float* __restrict__ S0, Tin* __restrict__ o, Tin* __restrict__ S_chunks,
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(64 * NW * RS) __attribute__((amdgpu_waves_per_eu(TR
   static_assert(RTW % 2 == 0 && (RS == 1 || RS == 2), "row split");
 
   const int NC = T / C;
-  const int NCU = ncu ? min(*ncu, NC) : NC;  // chunks in use (packed documents: see ChunkShape)
+  const int NCU = DOCS ? min(*ncu, NC) : NC;  // chunks in use (packed documents: see ChunkShape)
   const int NSB = C / SB;
   const int nvb = NCOL / NV;
   const int2 gm = xcd_group(blockIdx.x, nvb, static_cast<int>(gridDim.x) / nvb);
@@ -291,12 +293,13 @@ __global__ __launch_bounds__(64 * NW * RS) __attribute__((amdgpu_waves_per_eu(TR
   if (U0 < U1) prefetch(U0);
   // packed documents: this chunk's table entry, and the next chunk's, loaded
   // a chunk ahead
-  int cinf = 0, cinf_next = (cinfo && cbeg < cend) ? cinfo[cbeg] : 0;
+  int cinf = 0, cinf_next = 0;
+  if constexpr (DOCS) cinf_next = cbeg < cend ? cinfo[cbeg] : 0;
 #pragma unroll 1
   for (int u = U0; u < U1; ++u) {
     const int c = u / NSB;
     const int sb = u - c * NSB;
-    if (cinfo && sb == 0) {
+    if (DOCS && sb == 0) {
       cinf = cinf_next;
       cinf_next = c + 1 < cend ? cinfo[c + 1] : 0;
       if (cinf & CI_START) {
@@ -450,7 +453,7 @@ __global__ __launch_bounds__(64 * NW * RS) __attribute__((amdgpu_waves_per_eu(TR
       for (int s = 0; s < RTW; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[s][i] = sgC[16 * (s0 + s) + 4 * g + i] * S[s][i] + dS[s][i];
-      if (!TRANS && (cinf & CI_END) && S_T) {
+      if (DOCS && !TRANS && (cinf & CI_END) && S_T) {
         // a document's last chunk: its final state
         float* dst = S_T + (static_cast<size_t>(cinf & CI_DOC) * H + h) * DK * DV;
 #pragma unroll
@@ -466,7 +469,7 @@ __global__ __launch_bounds__(64 * NW * RS) __attribute__((amdgpu_waves_per_eu(TR
     for (int s = 0; s < RTW; ++s)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * (s0 + s) + 4 * g + i) * NCOL + colg] = S[s][i];
-  } else if (S_T && seg == nseg - 1 && !cinfo) {
+  } else if (S_T && seg == nseg - 1 && !DOCS) {
 #pragma unroll
     for (int s = 0; s < RTW; ++s)
 #pragma unroll
@@ -490,7 +493,7 @@ __global__ __launch_bounds__(64 * NW * RS) __attribute__((amdgpu_waves_per_eu(TR
 // forward's trans.  Without TRANS, the last segment starts from dS_T and
 // segment seg from dS_seg[head][seg] (the gradient at the segment's end), and
 // segment 0 writes dS0.
-template <typename Tin, int DK, int NW, bool TRANS, int RS>
+template <typename Tin, int DK, int NW, bool TRANS, int RS, bool DOCS>
 __global__ __launch_bounds__(64 * NW * RS) void bwd_scan_kernel(
     int T, int H, int C, const char* __restrict__ summ, size_t summ_bytes,
     const Tin* __restrict__ dO, const float* __restrict__ dS_T, Tin* __restrict__ dS_chunks,
@@ -528,7 +531,7 @@ __global__ __launch_bounds__(64 * NW * RS) void bwd_scan_kernel(
   static_assert(RTW % 2 == 0 && (RS == 1 || RS == 2), "row split");
 
   const int NC = T / C;
-  const int NCU = ncu ? min(*ncu, NC) : NC;  // chunks in use (packed documents: see ChunkShape)
+  const int NCU = DOCS ? min(*ncu, NC) : NC;  // chunks in use (packed documents: see ChunkShape)
   const int NSB = C / SB;
   const int nvb = DV / NV;
   const int2 gm = xcd_group(blockIdx.x, nvb, static_cast<int>(gridDim.x) / nvb);
@@ -630,7 +633,7 @@ __global__ __launch_bounds__(64 * NW * RS) void bwd_scan_kernel(
   {
     // the segment's end: zero with TRANS, else dS_T or the segment state
     const float* src = TRANS ? nullptr
-                       : seg == nseg - 1 ? ((dS_T && !cinfo) ? dS_T + sbase : nullptr)
+                       : seg == nseg - 1 ? ((dS_T && !DOCS) ? dS_T + sbase : nullptr)
                                          : dS_seg + (static_cast<size_t>(bh) * nseg + seg) * DK * DV;
 #pragma unroll
     for (int s = 0; s < RTW; ++s)
@@ -645,12 +648,13 @@ __global__ __launch_bounds__(64 * NW * RS) void bwd_scan_kernel(
   if (U > 0) prefetch(0);
   // packed documents: this chunk's table entry, and the next one's (the chunk
   // before it), loaded a chunk ahead
-  int cinf = 0, cinf_next = (cinfo && U > 0) ? cinfo[cend - 1] : 0;
+  int cinf = 0, cinf_next = 0;
+  if constexpr (DOCS) cinf_next = U > 0 ? cinfo[cend - 1] : 0;
 #pragma unroll 1
   for (int u = 0; u < U; ++u) {
     const int c = unit_c(u);
     const int sb = unit_sb(u);
-    if (cinfo && sb == NSB - 1) {
+    if (DOCS && sb == NSB - 1) {
       cinf = cinf_next;
       cinf_next = c - 1 >= cbeg ? cinfo[c - 1] : 0;
       if (cinf & CI_END) {
@@ -755,7 +759,7 @@ __global__ __launch_bounds__(64 * NW * RS) void bwd_scan_kernel(
       for (int s = 0; s < RTW; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i) dS[s][i] = sgC[16 * (s0 + s) + 4 * g + i] * dS[s][i] + Z[s][i];
-      if (cinf & CI_START) {
+      if (DOCS && (cinf & CI_START)) {
         // a document's first chunk: the gradient at its start is the
         // document's dS0; none of it reaches the chunk before (another
         // document's), so the flow is cut there
@@ -777,7 +781,7 @@ __global__ __launch_bounds__(64 * NW * RS) void bwd_scan_kernel(
     for (int s = 0; s < RTW; ++s)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[static_cast<size_t>(16 * (s0 + s) + 4 * g + i) * TS + colg] = dS[s][i];
-  } else if (dS0 && seg == 0 && !cinfo) {
+  } else if (dS0 && seg == 0 && !DOCS) {
 #pragma unroll
     for (int s = 0; s < RTW; ++s)
 #pragma unroll
@@ -884,17 +888,17 @@ __global__ __launch_bounds__(4 * DK) void seg_combine_kernel(int nseg, const flo
 // columns) per workgroup.
 // Each segment's offset and transition, [E_g | P_g], into trans.
 // (S0 is read only at the first chunks of packed documents.)
-template <typename TT, int DD>
+template <typename TT, int DD, bool DOCS>
 void fwd_trans_typed(const ChunkShape& s, const void* summ, const float* S0, float* trans, hipStream_t stream) {
   const int heads = s.B * s.H;
   const int nseg = s.scan_segments();
-  hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, true, 1>), dim3(heads * nseg * (2 * DD / 64)), dim3(256), 0, stream,
+  hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, true, 1, DOCS>), dim3(heads * nseg * (2 * DD / 64)), dim3(256), 0, stream,
                      s.T, s.H, s.C, (const char*)summ, s.summary_bytes(), s.cinfo ? S0 : (const float*)nullptr,
                      (TT*)nullptr, (TT*)nullptr, (float*)nullptr, (char*)nullptr, size_t(0), nseg,
                      (const float*)nullptr, trans, s.cinfo, s.ncu);
 }
 
-template <typename TT, int DD>
+template <typename TT, int DD, bool DOCS>
 hipError_t fwd_scan_typed(const ChunkShape& s, const void* summ, const float* S0, void* o,
                           void* S_chunks_v, float* S_T, void* deltas, float* split, hipStream_t stream) {
   TT* S_chunks = static_cast<TT*>(S_chunks_v);
@@ -904,27 +908,27 @@ hipError_t fwd_scan_typed(const ChunkShape& s, const void* summ, const float* S0
   if (nseg > 1) {
     float* trans = split;
     float* sseg = split + static_cast<size_t>(heads) * nseg * DD * (2 * DD);
-    fwd_trans_typed<TT, DD>(s, summ, S0, trans, stream);
+    fwd_trans_typed<TT, DD, DOCS>(s, summ, S0, trans, stream);
     // (packed documents: the first chunk starts a document, whose own S0 the
     // scan takes there)
     hipLaunchKernelGGL((seg_combine_kernel<DD, false>), dim3(heads * (DD / 16)), dim3(4 * DD), 0, stream, nseg,
                        s.cinfo ? (const float*)nullptr : S0, (const float*)trans, (const float*)trans, sseg);
-    hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, false, 2>), dim3(heads * nseg * (DD / 64)), dim3(512), 0, stream,
+    hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, false, 2, DOCS>), dim3(heads * nseg * (DD / 64)), dim3(512), 0, stream,
                        s.T, s.H, s.C, (const char*)summ, sb, S0, (TT*)o, S_chunks, S_T, (char*)deltas,
                        s.dl_offset(), nseg, (const float*)sseg, (float*)nullptr, s.cinfo, s.ncu);
   } else if (static_cast<long long>(heads) * (DD / 64) >= 256) {
-    hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, false, 2>), dim3(heads * (DD / 64)), dim3(512), 0, stream, s.T,
+    hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 4, false, 2, DOCS>), dim3(heads * (DD / 64)), dim3(512), 0, stream, s.T,
                        s.H, s.C, (const char*)summ, sb, S0, (TT*)o, S_chunks, S_T, (char*)deltas, s.dl_offset(), 1,
                        (const float*)nullptr, (float*)nullptr, s.cinfo, s.ncu);
   } else {
-    hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 1, false, 1>), dim3(heads * (DD / 16)), dim3(64), 0, stream, s.T,
+    hipLaunchKernelGGL((fwd_scan_kernel<TT, DD, 1, false, 1, DOCS>), dim3(heads * (DD / 16)), dim3(64), 0, stream, s.T,
                        s.H, s.C, (const char*)summ, sb, S0, (TT*)o, S_chunks, S_T, (char*)deltas, s.dl_offset(), 1,
                        (const float*)nullptr, (float*)nullptr, s.cinfo, s.ncu);
   }
   return hipGetLastError();
 }
 
-template <typename TT, int DD>
+template <typename TT, int DD, bool DOCS>
 hipError_t bwd_scan_typed(const ChunkShape& s, const void* summ, const void* dO, const float* dS_T,
                           void* dS_chunks, float* dS0, float* split, const float* ftrans, hipStream_t stream) {
   const int heads = s.B * s.H;
@@ -936,59 +940,73 @@ hipError_t bwd_scan_typed(const ChunkShape& s, const void* summ, const void* dO,
     float* trans = split;
     float* sseg = split + static_cast<size_t>(heads) * nseg * DD * (2 * DD);
     // (the transition pass takes each packed document's dS_T at its last chunk)
-    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, true, 2>), dim3(heads * nseg * (DD / 64)), dim3(512), 0, stream,
+    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, true, 2, DOCS>), dim3(heads * nseg * (DD / 64)), dim3(512), 0, stream,
                        s.T, s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks, (float*)nullptr,
                        nseg, (const float*)nullptr, trans, s.cinfo, s.ncu);
     hipLaunchKernelGGL((seg_combine_kernel<DD, true>), dim3(heads * (DD / 16)), dim3(4 * DD), 0, stream, nseg,
                        s.cinfo ? (const float*)nullptr : dS_T, (const float*)trans, ftrans, sseg);
-    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, false, 2>), dim3(heads * nseg * (DD / 64)), dim3(512), 0, stream,
+    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, false, 2, DOCS>), dim3(heads * nseg * (DD / 64)), dim3(512), 0, stream,
                        s.T, s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks, dS0, nseg,
                        (const float*)sseg, (float*)nullptr, s.cinfo, s.ncu);
   } else if (static_cast<long long>(heads) * (DD / 64) >= 256) {
-    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, false, 2>), dim3(heads * (DD / 64)), dim3(512), 0, stream, s.T,
+    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 4, false, 2, DOCS>), dim3(heads * (DD / 64)), dim3(512), 0, stream, s.T,
                        s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks, dS0, 1,
                        (const float*)nullptr, (float*)nullptr, s.cinfo, s.ncu);
   } else {
-    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 1, false, 1>), dim3(heads * (DD / 16)), dim3(64), 0, stream, s.T,
+    hipLaunchKernelGGL((bwd_scan_kernel<TT, DD, 1, false, 1, DOCS>), dim3(heads * (DD / 16)), dim3(64), 0, stream, s.T,
                        s.H, s.C, (const char*)summ, sb, (const TT*)dO, dS_T, (TT*)dS_chunks, dS0, 1,
                        (const float*)nullptr, (float*)nullptr, s.cinfo, s.ncu);
   }
   return hipGetLastError();
 }
 
+template <bool DOCS>
+hipError_t fwd_scan_any(const ChunkShape& s, const void* summ, const float* S0, void* o, void* S_chunks,
+                        float* S_T, void* deltas, float* split, hipStream_t stream) {
+  if (s.bf16) {
+    return s.DK == 128 ? fwd_scan_typed<uint16_t, 128, DOCS>(s, summ, S0, o, S_chunks, S_T, deltas, split, stream)
+                       : fwd_scan_typed<uint16_t, 64, DOCS>(s, summ, S0, o, S_chunks, S_T, deltas, split, stream);
+  }
+  return s.DK == 128 ? fwd_scan_typed<float, 128, DOCS>(s, summ, S0, o, S_chunks, S_T, deltas, split, stream)
+                     : fwd_scan_typed<float, 64, DOCS>(s, summ, S0, o, S_chunks, S_T, deltas, split, stream);
+}
+
 hipError_t launch_fwd_scan(const ChunkShape& s, const void* summ, const float* S0, void* o,
                            void* S_chunks, float* S_T, void* deltas, float* split, hipStream_t stream) {
   if (s.B * s.H == 0) return hipSuccess;
-  if (s.bf16) {
-    return s.DK == 128 ? fwd_scan_typed<uint16_t, 128>(s, summ, S0, o, S_chunks, S_T, deltas, split, stream)
-                       : fwd_scan_typed<uint16_t, 64>(s, summ, S0, o, S_chunks, S_T, deltas, split, stream);
-  }
-  return s.DK == 128 ? fwd_scan_typed<float, 128>(s, summ, S0, o, S_chunks, S_T, deltas, split, stream)
-                     : fwd_scan_typed<float, 64>(s, summ, S0, o, S_chunks, S_T, deltas, split, stream);
+  return s.cinfo ? fwd_scan_any<true>(s, summ, S0, o, S_chunks, S_T, deltas, split, stream)
+                 : fwd_scan_any<false>(s, summ, S0, o, S_chunks, S_T, deltas, split, stream);
 }
 
 hipError_t launch_fwd_trans(const ChunkShape& s, const void* summ, float* split, hipStream_t stream) {
   if (s.B * s.H == 0 || s.scan_segments() < 2) return hipSuccess;
   if (s.cinfo) return hipErrorInvalidValue;  // packed documents need their S0 here: launch_fwd_scan forms these
   if (s.bf16) {
-    if (s.DK == 128) fwd_trans_typed<uint16_t, 128>(s, summ, nullptr, split, stream);
-    else fwd_trans_typed<uint16_t, 64>(s, summ, nullptr, split, stream);
+    if (s.DK == 128) fwd_trans_typed<uint16_t, 128, false>(s, summ, nullptr, split, stream);
+    else fwd_trans_typed<uint16_t, 64, false>(s, summ, nullptr, split, stream);
   } else {
-    if (s.DK == 128) fwd_trans_typed<float, 128>(s, summ, nullptr, split, stream);
-    else fwd_trans_typed<float, 64>(s, summ, nullptr, split, stream);
+    if (s.DK == 128) fwd_trans_typed<float, 128, false>(s, summ, nullptr, split, stream);
+    else fwd_trans_typed<float, 64, false>(s, summ, nullptr, split, stream);
   }
   return hipGetLastError();
+}
+
+template <bool DOCS>
+hipError_t bwd_scan_any(const ChunkShape& s, const void* summ, const void* dO, const float* dS_T, void* dS_chunks,
+                        float* dS0, float* split, const float* ftrans, hipStream_t stream) {
+  if (s.bf16) {
+    return s.DK == 128 ? bwd_scan_typed<uint16_t, 128, DOCS>(s, summ, dO, dS_T, dS_chunks, dS0, split, ftrans, stream)
+                       : bwd_scan_typed<uint16_t, 64, DOCS>(s, summ, dO, dS_T, dS_chunks, dS0, split, ftrans, stream);
+  }
+  return s.DK == 128 ? bwd_scan_typed<float, 128, DOCS>(s, summ, dO, dS_T, dS_chunks, dS0, split, ftrans, stream)
+                     : bwd_scan_typed<float, 64, DOCS>(s, summ, dO, dS_T, dS_chunks, dS0, split, ftrans, stream);
 }
 
 hipError_t launch_bwd_scan(const ChunkShape& s, const void* summ, const void* dO, const float* dS_T,
                            void* dS_chunks, float* dS0, float* split, const float* ftrans, hipStream_t stream) {
   if (s.B * s.H == 0) return hipSuccess;
-  if (s.bf16) {
-    return s.DK == 128 ? bwd_scan_typed<uint16_t, 128>(s, summ, dO, dS_T, dS_chunks, dS0, split, ftrans, stream)
-                       : bwd_scan_typed<uint16_t, 64>(s, summ, dO, dS_T, dS_chunks, dS0, split, ftrans, stream);
-  }
-  return s.DK == 128 ? bwd_scan_typed<float, 128>(s, summ, dO, dS_T, dS_chunks, dS0, split, ftrans, stream)
-                     : bwd_scan_typed<float, 64>(s, summ, dO, dS_T, dS_chunks, dS0, split, ftrans, stream);
+  return s.cinfo ? bwd_scan_any<true>(s, summ, dO, dS_T, dS_chunks, dS0, split, ftrans, stream)
+                 : bwd_scan_any<false>(s, summ, dO, dS_T, dS_chunks, dS0, split, ftrans, stream);
 }
 
 }  // namespace muir
