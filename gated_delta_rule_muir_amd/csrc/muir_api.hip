@@ -138,24 +138,32 @@ hipError_t copy_or_zero(float* dst, const float* src, size_t n, hipStream_t s) {
 // else rows n*Tsrc .. n*Tsrc + Tsrc-1 of a [N, Tsrc, H, D] tensor; in the
 // padded [N, Tp, H, D] copy, rows past a sequence's end are zero.  to_padded:
 // caller -> padded (every padded row written); else padded -> caller (the
-// real rows only).
-__global__ void stage_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int N, int Tsrc, int Tp,
-                             int WW, const int32_t* __restrict__ cu, int to_padded) {
-  const size_t total = static_cast<size_t>(N) * Tp * WW;
-  for (size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
-       idx += static_cast<size_t>(gridDim.x) * blockDim.x) {
-    const size_t row = idx / WW;
-    const int w = static_cast<int>(idx - row * WW);
+// real rows only).  A block takes whole rows (grid-stride) and copies each
+// row's words with consecutive threads, as pack_kernel does.
+__global__ __launch_bounds__(256) void stage_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int N,
+                                                    int Tsrc, int Tp, int WW, const int32_t* __restrict__ cu,
+                                                    int to_padded) {
+  const long long rows = static_cast<long long>(N) * Tp;
+  for (long long row = blockIdx.x; row < rows; row += gridDim.x) {
     const int n = static_cast<int>(row / Tp);
-    const int t = static_cast<int>(row - static_cast<size_t>(n) * Tp);
+    const int t = static_cast<int>(row - static_cast<long long>(n) * Tp);
     const long long start = cu ? cu[n] : static_cast<long long>(n) * Tsrc;
     const int len = cu ? cu[n + 1] - cu[n] : Tsrc;
+    const bool real = t < len;
     const size_t crow = static_cast<size_t>(start + t);
     if (to_padded) {
-      const uint4 z = {0u, 0u, 0u, 0u};
-      dst[idx] = t < len ? src[crow * WW + w] : z;
-    } else if (t < len) {
-      dst[crow * WW + w] = src[idx];
+      uint4* o = dst + static_cast<size_t>(row) * WW;
+      if (real) {
+        const uint4* s = src + crow * WW;
+        for (int w = threadIdx.x; w < WW; w += blockDim.x) o[w] = s[w];
+      } else {
+        const uint4 z = {0u, 0u, 0u, 0u};
+        for (int w = threadIdx.x; w < WW; w += blockDim.x) o[w] = z;
+      }
+    } else if (real) {
+      const uint4* s = src + static_cast<size_t>(row) * WW;
+      uint4* o = dst + crow * WW;
+      for (int w = threadIdx.x; w < WW; w += blockDim.x) o[w] = s[w];
     }
   }
 }
@@ -163,9 +171,9 @@ __global__ void stage_kernel(const uint4* __restrict__ src, uint4* __restrict__ 
 hipError_t stage(const void* src, void* dst, const ChunkShape& p, int Tsrc, int D, size_t esize, const int32_t* cu,
                  bool to_padded, hipStream_t s) {
   const int WW = static_cast<int>(static_cast<size_t>(p.H) * D * esize / 16);
-  const size_t total = static_cast<size_t>(p.B) * p.T * WW;
-  if (total == 0) return hipSuccess;
-  const unsigned blocks = static_cast<unsigned>(total / 256 + 1 < 8192 ? total / 256 + 1 : 8192);
+  const long long rows = static_cast<long long>(p.B) * p.T;
+  if (rows == 0 || WW == 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>(rows < 8192 ? rows : 8192);
   hipLaunchKernelGGL(stage_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const uint4*>(src),
                      static_cast<uint4*>(dst), p.B, Tsrc, p.T, WW, cu, to_padded ? 1 : 0);
   return hipGetLastError();
