@@ -90,8 +90,12 @@ template <typename TC, int DK, int C> constexpr int stage_split() {
 
 // Tin: element type of the inputs, dO, the chunk states and the MFMA
 // operands; Tg: element type of the per-token gradients (Tin, or fp32 for
-// bf16 inputs); FORM: BwdForm.
-template <typename Tin, typename Tg, int DK, int C, int NW, int FORM, bool GTOK>
+// bf16 inputs); FORM: BwdForm.  PKO (packed documents, ChunkShape::docoff):
+// the per-token gradients go straight to the caller's packed [T_total, H, D]
+// tensors -- the chunk's rows from row cu[d] + (its first row - docoff[d]) of
+// document d, the rows past the document's end not stored -- instead of to
+// a chunk-aligned copy.
+template <typename Tin, typename Tg, int DK, int C, int NW, int FORM, bool GTOK, bool PKO>
 __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     int T, int H, const Tin* __restrict__ q, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ log_a, const Tin* __restrict__ erase,
@@ -100,7 +104,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
     const Tin* __restrict__ dS_chunks, const Tin* __restrict__ dO, Tg* __restrict__ dq,
     Tg* __restrict__ dk, Tg* __restrict__ dv, Tg* __restrict__ dlog_a,
     Tg* __restrict__ derase, Tg* __restrict__ dwrite, Tg* __restrict__ dgamma,
-    char* __restrict__ scratch, int gmode, float* __restrict__ dgam_part, const int32_t* __restrict__ ncu) {
+    char* __restrict__ scratch, int gmode, float* __restrict__ dgam_part, const int32_t* __restrict__ ncu,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ docoff, const int32_t* __restrict__ cinfo) {
   typedef Tin TC;
   typedef MM<TC> M;
   typedef typename M::frag frag;
@@ -180,13 +185,22 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   const Tin* gb = gbase + ebase;
   const Tin* gst = gbase + static_cast<size_t>(h) * DK;
   const Tin* dOb = dO + ebase;
-  Tg* dqb = dq + ebase;
-  Tg* dkb = dk + ebase;
-  Tg* dvb = dv + ebase;
-  Tg* dlb = dlog_a + ebase;
-  Tg* deb = derase + ebase;
-  Tg* dwb = dwrite + ebase;
-  Tg* dgb = dgamma + ebase;
+  // the gradients' chunk base, and the chunk's rows that are stored
+  size_t obase = ebase;
+  int vrows = C;
+  if constexpr (PKO) {
+    const int d = cinfo[c] & CI_DOC;
+    const int t0 = c * C - docoff[d];  // the chunk's first token within document d (B = 1)
+    vrows = min(C, cu[d + 1] - cu[d] - t0);
+    obase = ((static_cast<size_t>(cu[d]) + t0) * H + h) * DK;
+  }
+  Tg* dqb = dq + obase;
+  Tg* dkb = dk + obase;
+  Tg* dvb = dv + obase;
+  Tg* dlb = dlog_a + obase;
+  Tg* deb = derase + obase;
+  Tg* dwb = dwrite + obase;
+  Tg* dgb = dgamma + obase;
   auto gi = [&](int t, int j) -> uint32_t { return static_cast<uint32_t>(t) * HD + static_cast<uint32_t>(j); };
   // the readout gate of element (t, j) of the chunk (GTOK: per token, as the
   // other inputs; else static or none, chosen at run time)
@@ -349,10 +363,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_chunk_kernel(
   // turning the tile with an fp32 identity product for 16-byte stores)
   auto store_grad = [&](Tg* base, int r0, int n, f32x4 tile) {
     if constexpr (sizeof(Tg) == 2) {
-      store4(at(base, gi(r0 + c16, col0(n) + 4 * g)), turn(tile));
+      const f32x4 tt = turn(tile);
+      if (!PKO || r0 + c16 < vrows) store4(at(base, gi(r0 + c16, col0(n) + 4 * g)), tt);
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *at(base, gi(r0 + 4 * g + i, colv(n))) = tile[i];
+      for (int i = 0; i < 4; ++i)
+        if (!PKO || r0 + 4 * g + i < vrows) *at(base, gi(r0 + 4 * g + i, colv(n))) = tile[i];
     }
   };
 
@@ -1398,36 +1414,41 @@ hipError_t launch_bwd_chunk(const ChunkShape& s, const void* q, const void* k, c
                             hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(s.nchunks());
   if (grid == 0) return hipSuccess;
-#define MUIR_BCH2(TT, TG, DD, CC, NW, FORM, GT)                                                              \
-  hipLaunchKernelGGL((bwd_chunk_kernel<TT, TG, DD, CC, NW, FORM, GT>), dim3(grid), dim3(64 * NW), 0, stream, s.T, \
+#define MUIR_BCH2(TT, TG, DD, CC, NW, FORM, GT, PK)                                                          \
+  hipLaunchKernelGGL((bwd_chunk_kernel<TT, TG, DD, CC, NW, FORM, GT, PK>), dim3(grid), dim3(64 * NW), 0, stream, s.T, \
                      s.H, (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)log_a, (const TT*)erase,        \
                      (const TT*)write, (const TT*)gamma, (const char*)summ, s.summary_bytes(), s.tp_offset(),    \
                      s.dl_offset(), (const TT*)S_chunks, (const TT*)dS_chunks, (const TT*)dO, (TG*)dq, (TG*)dk,  \
                      (TG*)dv, (TG*)dlog_a, (TG*)derase, (TG*)dwrite, (TG*)dgamma, (char*)scratch, s.gmode,       \
-                     dgam_part, s.ncu)
-#define MUIR_BCH1(TT, TG, DD, CC, NW, FORM)                              \
-  do {                                                                   \
-    if (s.gmode == GAMMA_TOKEN) MUIR_BCH2(TT, TG, DD, CC, NW, FORM, true); \
-    else MUIR_BCH2(TT, TG, DD, CC, NW, FORM, false);                     \
+                     dgam_part, s.ncu, s.cu, s.docoff, s.cinfo)
+#define MUIR_BCH1(TT, TG, DD, CC, NW, FORM, PK)                              \
+  do {                                                                       \
+    if (s.gmode == GAMMA_TOKEN) MUIR_BCH2(TT, TG, DD, CC, NW, FORM, true, PK); \
+    else MUIR_BCH2(TT, TG, DD, CC, NW, FORM, false, PK);                     \
   } while (0)
-#define MUIR_BCH(TT, TG, DD, NW, F64, FL)                    \
-  do {                                                       \
-    if (s.C == 64) MUIR_BCH1(TT, TG, DD, 64, NW, F64);       \
-    else if (s.C == 128) MUIR_BCH1(TT, TG, DD, 128, NW, FL); \
-    else MUIR_BCH1(TT, TG, DD, 256, NW, FL);                 \
+#define MUIR_BCH(TT, TG, DD, NW, F64, FL, PK)                    \
+  do {                                                           \
+    if (s.C == 64) MUIR_BCH1(TT, TG, DD, 64, NW, F64, PK);       \
+    else if (s.C == 128) MUIR_BCH1(TT, TG, DD, 128, NW, FL, PK); \
+    else MUIR_BCH1(TT, TG, DD, 256, NW, FL, PK);                 \
   } while (0)
   // one 16-column tile per wave: 8 waves at d = 128, 4 at d = 64; bf16 inputs
   // take the direct forms (their chunk deltas are kept by the forward scan,
   // ChunkShape::bwd_direct), fp32 inputs the two sweeps
+  // (packed-document output straight to the caller's tensors: bf16 inputs
+  // at d = 128 only; packed_output() tells the caller)
+  const bool pko = s.docoff && s.bf16 && s.DK == 128;
   if (s.bf16 && s.gbf16) {
-    if (s.DK == 128) MUIR_BCH(uint16_t, uint16_t, 128, 8, BWD_DIRECT, BWD_SUB);
-    else MUIR_BCH(uint16_t, uint16_t, 64, 4, BWD_DIRECT, BWD_SUB);
+    if (s.DK == 128 && pko) MUIR_BCH(uint16_t, uint16_t, 128, 8, BWD_DIRECT, BWD_SUB, true);
+    else if (s.DK == 128) MUIR_BCH(uint16_t, uint16_t, 128, 8, BWD_DIRECT, BWD_SUB, false);
+    else MUIR_BCH(uint16_t, uint16_t, 64, 4, BWD_DIRECT, BWD_SUB, false);
   } else if (s.bf16) {
-    if (s.DK == 128) MUIR_BCH(uint16_t, float, 128, 8, BWD_DIRECT, BWD_SUB);
-    else MUIR_BCH(uint16_t, float, 64, 4, BWD_DIRECT, BWD_SUB);
+    if (s.DK == 128 && pko) MUIR_BCH(uint16_t, float, 128, 8, BWD_DIRECT, BWD_SUB, true);
+    else if (s.DK == 128) MUIR_BCH(uint16_t, float, 128, 8, BWD_DIRECT, BWD_SUB, false);
+    else MUIR_BCH(uint16_t, float, 64, 4, BWD_DIRECT, BWD_SUB, false);
   } else {
-    if (s.DK == 128) MUIR_BCH(float, float, 128, 8, BWD_TWO_SWEEP, BWD_TWO_SWEEP);
-    else MUIR_BCH(float, float, 64, 4, BWD_TWO_SWEEP, BWD_TWO_SWEEP);
+    if (s.DK == 128) MUIR_BCH(float, float, 128, 8, BWD_TWO_SWEEP, BWD_TWO_SWEEP, false);
+    else MUIR_BCH(float, float, 64, 4, BWD_TWO_SWEEP, BWD_TWO_SWEEP, false);
   }
 #undef MUIR_BCH
 #undef MUIR_BCH1

@@ -67,6 +67,12 @@ struct ChunkShape {
   // dS_T and dS0 are then per document, [N, H, dk, dv].
   const int32_t* cinfo = nullptr;
   const int32_t* ncu = nullptr;
+  // Packed documents whose per-token gradients the chunk kernel writes
+  // straight to the caller's packed tensors (packed_output()): the caller's
+  // cu_seqlens and each document's first row in the packed sequence.
+  const int32_t* cu = nullptr;
+  const int32_t* docoff = nullptr;
+  bool packed_output() const { return cinfo && bf16 && DK == 128; }
   // chunks per sequence, a partial last one included (the kernels only ever
   // run on shapes whose T is a multiple of C)
   int NC() const { return (T + C - 1) / C; }

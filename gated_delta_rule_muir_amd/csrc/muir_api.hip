@@ -657,16 +657,23 @@ muir_status_t bwd_packed(const ChunkShape& s, const int32_t* cu, const Inputs& i
   if (!fwd_workspace && (st = pack_inputs(p, cu, pl, in, &sin, &cur, hs)) != MUIR_OK) return st;
   void* pdO = cur.take(p, p.DV, p.tc_bytes());
   if (pack(dO, pdO, p, p.DV, p.tc_bytes(), cu, pl, true, hs) != hipSuccess) return MUIR_ERR_HIP;
+  // the chunk kernel writes the per-token gradients straight to the caller's
+  // tensors when it can (ChunkShape::packed_output), else to copies here
+  const bool direct = p.packed_output();
+  if (direct) {
+    p.cu = cu;
+    p.docoff = pl.docoff;
+  }
   Grads sg;
   for (int i = 0; i < 7; ++i) {
-    if (i == 6 && p.gmode != MUIR_GAMMA_TOKEN) {
-      sg.x[6] = gr.x[6];  // a static gate's gradient is [H, dk] fp32; an absent gate has none
+    if ((i == 6 && p.gmode != MUIR_GAMMA_TOKEN) || direct) {
+      sg.x[i] = gr.x[i];  // (a static gate's gradient is [H, dk] fp32; an absent gate has none)
       continue;
     }
     sg.x[i] = cur.take(p, kIsDk[i] ? p.DK : p.DV, p.tg_bytes());
   }
   if ((st = bwd_core(p, sin, S0, Sc, summ, pdO, dS_T, sg, dS0, workspace, hs)) != MUIR_OK) return st;
-  for (int i = 0; i < 7; ++i) {
+  for (int i = 0; i < 7 && !direct; ++i) {
     if (i == 6 && p.gmode != MUIR_GAMMA_TOKEN) continue;
     if (pack(sg.x[i], gr.x[i], p, kIsDk[i] ? p.DK : p.DV, p.tg_bytes(), cu, pl, false, hs) != hipSuccess)
       return MUIR_ERR_HIP;
